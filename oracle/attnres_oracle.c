@@ -1,0 +1,256 @@
+/*
+ * Block / Full Attention Residuals -- reference oracle, fp64, plain C.
+ * TEST INFRASTRUCTURE ONLY (see attnres_oracle.h for the sources followed and
+ * the readings taken where the pages are silent).
+ *
+ * Everything here is the plain definition computed per token and per
+ * aggregation site, in the order the pages state it: RMSNorm each key,
+ * score it against the site's pseudo-query, softmax over depth, weight the
+ * unnormalised sources, then apply the consuming sublayer's PreNorm.
+ * There is no blocking, no fusion and no two-phase evaluation in the forward
+ * functions.
+ */
+#include "attnres_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* "Attention Residuals 阅读补充", RMSNorm section: mean square over the d
+ * features of one token, eps inside the root. */
+double oracle_rms(int64_t d, const double* x, double eps) {
+    double s = 0.0;
+    for (int64_t k = 0; k < d; ++k) s += x[k] * x[k];
+    return sqrt(s / (double)d + eps);
+}
+
+int oracle_rmsnorm(int64_t d, const double* x, const double* gain, double eps, double* y) {
+    if (d <= 0 || !x || !y) return -1;
+    double r = oracle_rms(d, x, eps);
+    for (int64_t k = 0; k < d; ++k) y[k] = (gain ? gain[k] : 1.0) * (x[k] / r);
+    return 0;
+}
+
+/* "Attention Residuals" notes, section 7: z_i = w^T RMSNorm_g(src_i);
+ * alpha = softmax(z); h = sum_i alpha_i src_i (values are the raw sources). */
+int oracle_depth_softmax(int64_t n, int64_t d, const double* const* src,
+                         const double* w, const double* g, double eps,
+                         double* z, double* alpha, double* h, double* m, double* lse) {
+    if (n <= 0 || d <= 0 || !src || !w) return -1;
+    double* zz = (double*)malloc(sizeof(double) * (size_t)n * 2);
+    double* key = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!zz || !key) { free(zz); free(key); return -2; }
+    double* aa = zz + n;
+    for (int64_t i = 0; i < n; ++i) {
+        oracle_rmsnorm(d, src[i], g, eps, key);          /* key = RMSNorm_g(v_i) */
+        double s = 0.0;
+        for (int64_t k = 0; k < d; ++k) s += w[k] * key[k];
+        zz[i] = s;                                         /* z_i = w^T key */
+    }
+    double mx = zz[0];
+    for (int64_t i = 1; i < n; ++i) if (zz[i] > mx) mx = zz[i];
+    double sum = 0.0;
+    for (int64_t i = 0; i < n; ++i) { aa[i] = exp(zz[i] - mx); sum += aa[i]; }
+    for (int64_t i = 0; i < n; ++i) aa[i] /= sum;
+    if (h) {
+        for (int64_t k = 0; k < d; ++k) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < n; ++i) acc += aa[i] * src[i][k];
+            h[k] = acc;
+        }
+    }
+    if (z) memcpy(z, zz, sizeof(double) * (size_t)n);
+    if (alpha) memcpy(alpha, aa, sizeof(double) * (size_t)n);
+    if (m) *m = mx;
+    if (lse) *lse = mx + log(sum);
+    free(zz);
+    free(key);
+    return 0;
+}
+
+/* "Attention Residuals" notes, section 10: per-partition (m, ell, o). */
+int oracle_partition_stats(int64_t n, int64_t d, const double* const* src,
+                           const double* w, const double* g, double eps,
+                           double* m, double* ell, double* o) {
+    if (n <= 0 || d <= 0 || !m || !ell || !o) return -1;
+    double* z = (double*)malloc(sizeof(double) * (size_t)n);
+    if (!z) return -2;
+    int rc = oracle_depth_softmax(n, d, src, w, g, eps, z, NULL, NULL, NULL, NULL);
+    if (rc) { free(z); return rc; }
+    double mx = z[0];
+    for (int64_t i = 1; i < n; ++i) if (z[i] > mx) mx = z[i];
+    double l = 0.0;
+    for (int64_t k = 0; k < d; ++k) o[k] = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double e = exp(z[i] - mx);
+        l += e;
+        for (int64_t k = 0; k < d; ++k) o[k] += e * src[i][k];
+    }
+    *m = mx;
+    *ell = l;
+    free(z);
+    return 0;
+}
+
+/* "Attention Residuals 阅读补充", two-phase section: merge of two disjoint
+ * partitions under their common maximum. */
+int oracle_merge_two(int64_t d, double mA, double lA, const double* oA,
+                     double mB, double lB, const double* oB, double* h) {
+    if (d <= 0 || !oA || !oB || !h) return -1;
+    double M = mA > mB ? mA : mB;
+    double a = exp(mA - M), b = exp(mB - M);
+    double den = a * lA + b * lB;
+    for (int64_t k = 0; k < d; ++k) h[k] = (a * oA[k] + b * oB[k]) / den;
+    return 0;
+}
+
+static void widen(int64_t d, const float* x, double* y) {
+    for (int64_t k = 0; k < d; ++k) y[k] = (double)x[k];
+}
+
+int oracle_block_forward(int64_t n_tok, int64_t d, int64_t n_blocks, const int64_t* blocks,
+                         int64_t n_given, const float* emb, const float* given, const float* v,
+                         const float* w, const float* g, const float* gamma, double eps,
+                         int final_site,
+                         double* x_out, double* h_out, double* o1_out, double* m1_out,
+                         double* lse1_out, double* lse_out, double* hfinal_out, double* reps_out) {
+    if (n_tok < 0 || d <= 0 || n_blocks < 0 || n_given < 0 || !emb || !w) return -1;
+    if (n_given > 0 && !given) return -1;
+    int64_t L = 0;
+    for (int64_t b = 0; b < n_blocks; ++b) {
+        if (blocks[b] <= 0) return -1;
+        L += blocks[b];
+    }
+    if (L > 0 && !v) return -1;
+    const int64_t R = 1 + n_given + n_blocks;   /* b_0 .. b_N */
+    int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < n_tok; ++t) {
+        double* reps = (double*)malloc(sizeof(double) * (size_t)(R * d));
+        double* partial = (double*)malloc(sizeof(double) * (size_t)d);
+        double* wq = (double*)malloc(sizeof(double) * (size_t)(2 * d));
+        double* gam = (double*)malloc(sizeof(double) * (size_t)d);
+        double* h = (double*)malloc(sizeof(double) * (size_t)d);
+        double* x = (double*)malloc(sizeof(double) * (size_t)d);
+        const double** srcs = (const double**)malloc(sizeof(double*) * (size_t)(R + 1));
+        if (!reps || !partial || !wq || !gam || !h || !x || !srcs) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            double* gk = wq + d;
+            /* b_0 is the token embedding; b_1..b_{n_given} are supplied. */
+            widen(d, emb + t * d, reps);
+            for (int64_t n = 0; n < n_given; ++n)
+                widen(d, given + (n * n_tok + t) * d, reps + (1 + n) * d);
+            int64_t have = 1 + n_given;   /* completed sources so far */
+            int64_t l = 0;                /* 0-based sublayer index */
+            for (int64_t b = 0; b < n_blocks; ++b) {
+                for (int64_t j = 0; j < blocks[b]; ++j, ++l) {
+                    /* Sources: [b_0..b_{n-1}] and, after the block's first
+                     * sublayer, the partial sum of the block so far. */
+                    int64_t ns = 0;
+                    for (int64_t i = 0; i < have; ++i) srcs[ns++] = reps + i * d;
+                    if (j > 0) srcs[ns++] = partial;
+                    widen(d, w + l * d, wq);
+                    if (g) widen(d, g + l * d, gk);
+                    double lse_full = 0.0;
+                    oracle_depth_softmax(ns, d, srcs, wq, g ? gk : NULL, eps,
+                                         NULL, NULL, h, NULL, &lse_full);
+                    if (gamma) widen(d, gamma + l * d, gam);
+                    oracle_rmsnorm(d, h, gamma ? gam : NULL, eps, x);
+                    const int64_t row = (l * n_tok + t) * d;
+                    if (x_out) memcpy(x_out + row, x, sizeof(double) * (size_t)d);
+                    if (h_out) memcpy(h_out + row, h, sizeof(double) * (size_t)d);
+                    if (lse_out) lse_out[l * n_tok + t] = lse_full;
+                    if (o1_out || m1_out || lse1_out) {
+                        /* The same site restricted to the completed blocks. */
+                        double m1 = 0.0, lse1 = 0.0;
+                        oracle_depth_softmax(have, d, srcs, wq, g ? gk : NULL, eps,
+                                             NULL, NULL, h, &m1, &lse1);
+                        if (o1_out) memcpy(o1_out + row, h, sizeof(double) * (size_t)d);
+                        if (m1_out) m1_out[l * n_tok + t] = m1;
+                        if (lse1_out) lse1_out[l * n_tok + t] = lse1;
+                    }
+                    /* The sublayer's output joins the block's running sum. */
+                    const float* vl = v + (l * n_tok + t) * d;
+                    for (int64_t k = 0; k < d; ++k)
+                        partial[k] = (j == 0 ? 0.0 : partial[k]) + (double)vl[k];
+                }
+                memcpy(reps + have * d, partial, sizeof(double) * (size_t)d);
+                ++have;
+            }
+            if (final_site && hfinal_out) {
+                for (int64_t i = 0; i < have; ++i) srcs[i] = reps + i * d;
+                widen(d, w + L * d, wq);
+                if (g) widen(d, g + L * d, gk);
+                oracle_depth_softmax(have, d, srcs, wq, g ? gk : NULL, eps,
+                                     NULL, NULL, hfinal_out + t * d, NULL, NULL);
+            }
+            if (reps_out)
+                for (int64_t i = 0; i < have; ++i)
+                    memcpy(reps_out + (i * n_tok + t) * d, reps + i * d, sizeof(double) * (size_t)d);
+        }
+        free(reps); free(partial); free(wq); free(gam); free(h); free(x); free((void*)srcs);
+    }
+    return bad ? -2 : 0;
+}
+
+int oracle_full_forward(int64_t n_tok, int64_t d, int64_t L, const float* emb, const float* v,
+                        const float* w, const float* g, const float* gamma, double eps,
+                        int final_site, double* x_out, double* h_out, double* lse_out,
+                        double* hfinal_out) {
+    if (n_tok < 0 || d <= 0 || L < 0 || !emb || !w || (L > 0 && !v)) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < n_tok; ++t) {
+        /* v_0 = embedding, v_i = output of sublayer i: every one kept. */
+        double* hist = (double*)malloc(sizeof(double) * (size_t)((L + 1) * d));
+        double* wq = (double*)malloc(sizeof(double) * (size_t)(2 * d));
+        double* gam = (double*)malloc(sizeof(double) * (size_t)d);
+        double* h = (double*)malloc(sizeof(double) * (size_t)d);
+        double* x = (double*)malloc(sizeof(double) * (size_t)d);
+        const double** srcs = (const double**)malloc(sizeof(double*) * (size_t)(L + 1));
+        if (!hist || !wq || !gam || !h || !x || !srcs) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            double* gk = wq + d;
+            widen(d, emb + t * d, hist);
+            for (int64_t i = 0; i <= L; ++i) srcs[i] = hist + i * d;
+            for (int64_t l = 0; l < L; ++l) {
+                /* sublayer l+1 attends over v_0..v_l */
+                widen(d, w + l * d, wq);
+                if (g) widen(d, g + l * d, gk);
+                double lse = 0.0;
+                oracle_depth_softmax(l + 1, d, srcs, wq, g ? gk : NULL, eps, NULL, NULL, h, NULL, &lse);
+                if (gamma) widen(d, gamma + l * d, gam);
+                oracle_rmsnorm(d, h, gamma ? gam : NULL, eps, x);
+                const int64_t row = (l * n_tok + t) * d;
+                if (x_out) memcpy(x_out + row, x, sizeof(double) * (size_t)d);
+                if (h_out) memcpy(h_out + row, h, sizeof(double) * (size_t)d);
+                if (lse_out) lse_out[l * n_tok + t] = lse;
+                widen(d, v + (l * n_tok + t) * d, hist + (l + 1) * d);
+            }
+            if (final_site && hfinal_out) {
+                widen(d, w + L * d, wq);
+                if (g) widen(d, g + L * d, gk);
+                oracle_depth_softmax(L + 1, d, srcs, wq, g ? gk : NULL, eps, NULL, NULL,
+                                     hfinal_out + t * d, NULL, NULL);
+            }
+        }
+        free(hist); free(wq); free(gam); free(h); free(x); free((void*)srcs);
+    }
+    return bad ? -2 : 0;
+}

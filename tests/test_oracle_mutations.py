@@ -1,0 +1,58 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake into a copy of the oracle's C source (on the
+CPU, in a temporary directory), builds it, and runs the pin suite against
+the broken copy in a subprocess; the suite must fail.  The real oracle is
+never modified.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "attnres_oracle.c")
+
+MUTATIONS = {
+    "eps_dropped": ("return sqrt(s / (double)d + eps);", "return sqrt(s / (double)d);"),
+    "eps_outside_mean": ("return sqrt(s / (double)d + eps);", "return sqrt((s + eps) / (double)d);"),
+    "norm_not_rms": ("return sqrt(s / (double)d + eps);", "return sqrt(s + eps);"),
+    "score_sign": ("zz[i] = s;                                         /* z_i = w^T key */",
+                   "zz[i] = -s;"),
+    "temperature_sqrt_d": ("zz[i] = s;                                         /* z_i = w^T key */",
+                           "zz[i] = s / sqrt((double)d);"),
+    "normalised_values": ("for (int64_t i = 0; i < n; ++i) acc += aa[i] * src[i][k];",
+                          "for (int64_t i = 0; i < n; ++i) acc += aa[i] * src[i][k] / oracle_rms(d, src[i], eps);"),
+    "gain_ignored": ("oracle_rmsnorm(d, src[i], g, eps, key);", "oracle_rmsnorm(d, src[i], NULL, eps, key);"),
+    "empty_partial_is_source": ("if (j > 0) srcs[ns++] = partial;",
+                                "if (j == 0) for (int64_t k = 0; k < d; ++k) partial[k] = 0.0;\n                    srcs[ns++] = partial;"),
+    "partial_missing": ("if (j > 0) srcs[ns++] = partial;", ""),
+    "next_sites_query": ("widen(d, w + l * d, wq);\n                    if (g) widen(d, g + l * d, gk);",
+                         "widen(d, w + (l + 1) * d, wq);\n                    if (g) widen(d, g + (l + 1) * d, gk);"),
+    "full_next_query": ("/* sublayer l+1 attends over v_0..v_l */\n                widen(d, w + l * d, wq);",
+                        "widen(d, w + (l + 1 < L ? l + 1 : l) * d, wq);"),
+    "prenorm_gain_ignored": ("oracle_rmsnorm(d, h, gamma ? gam : NULL, eps, x);\n                    const int64_t row = (l * n_tok + t) * d;\n                    if (x_out)",
+                             "oracle_rmsnorm(d, h, NULL, eps, x);\n                    const int64_t row = (l * n_tok + t) * d;\n                    if (x_out)"),
+    "lse_without_max": ("if (lse) *lse = mx + log(sum);", "if (lse) *lse = log(sum);"),
+    "merge_unweighted": ("double den = a * lA + b * lB;", "double den = lA + lB;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor not unique: " + name
+    mutated = tmp_path / "attnres_oracle.c"
+    mutated.write_text(src.replace(old, new))
+    hdr = os.path.join(ROOT, "oracle", "attnres_oracle.h")
+    (tmp_path / "attnres_oracle.h").write_text(open(hdr).read())
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", str(lib),
+                    str(mutated), "-lm"], check=True)
+    env = dict(os.environ, ATTNRES_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, "pins did not catch mutation %s:\n%s" % (name, r.stdout[-2000:])
