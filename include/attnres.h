@@ -1,0 +1,155 @@
+/*
+ * attnres.h -- C ABI of the MI355X (gfx950) Block / Full Attention Residuals
+ * depth-aggregation library (libattnres.so).
+ *
+ * What it computes.  For every token t and every target sublayer l, a learned,
+ * input-independent pseudo-query w_l scores each depth source u as
+ *     z(u) = w_l^T ( g_l (.) u / r(u) ),   r(u) = sqrt(mean_k u_k^2 + eps),
+ * the scores are softmaxed over the site's sources and weight the raw sources:
+ *     h_l = sum_u softmax(z)_u * u.
+ * Sources: "Attention Residuals" (structured notes on arXiv 2603.15031),
+ * section 7 "Full AttnRes" for the score/softmax/aggregation, and
+ * "Attention Residuals 阅读补充", section "RMSNorm 的数学原理" for RMSNorm.
+ * In Block AttnRes (same notes, section 8) the sources of a sublayer in block
+ * n are the embedding b_0, the completed block sums b_1..b_{n-1} and, after
+ * the block's first sublayer, the running partial sum of block n.
+ *
+ * The work is split as in the notes' section 10 (two-phase inference) and the
+ * reading notes' section on static queries and two-phase computation:
+ *   - attnres_phase1: one batched pass per block; each completed-block source
+ *     row is read once and serves all S pseudo-queries of the block.  Returns
+ *     the normalised partial outputs and their softmax statistics.
+ *   - attnres_phase2_merge: one call per sublayer; adds the previous
+ *     sublayer's output to the partial sum, scores the partial sum, merges it
+ *     with the phase-1 partition exactly (online softmax), and applies the
+ *     consuming sublayer's PreNorm RMSNorm in the same pass.
+ *   - attnres_block_accumulate: b_n = partial + last output of the block.
+ *   - attnres_full: one-shot aggregation of n sources with one query (Full
+ *     AttnRes, or the final aggregation over b_0..b_N), optional PreNorm.
+ *
+ * Conventions for every entry point:
+ *  - Storage dtype `dt` (fp32 or bf16) for rows of sources and outputs; all
+ *    arithmetic is fp32; bf16 results are rounded to nearest even.
+ *    Parameters (w, key_gain, prenorm_gain) are fp32 [.., d] rows.
+ *  - Layout: row-major, token-major rows of d channels.  A row set [T][d] is
+ *    contiguous.  Multi-source inputs are slabs src + i*src_stride (elements).
+ *  - d must be a multiple of 8 and at most 16384; strides multiples of 8;
+ *    row and parameter pointers 16-byte aligned, statistics ([T] / [S][T]
+ *    fp32) pointers 4-byte aligned.
+ *  - All pointers except `stream` are device pointers owned by the caller.
+ *    The library allocates nothing and keeps no state beyond loaded kernels.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Calls
+ *    are asynchronous; argument errors are reported synchronously before any
+ *    launch; a failed launch reports ATTNRES_EHIP.
+ *  - T == 0 is valid and launches nothing.
+ *  - Kernels use no atomics: results are bitwise reproducible run to run and
+ *    independent of how tokens are split over calls.
+ */
+#ifndef ATTNRES_H
+#define ATTNRES_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTNRES_OK = 0,
+    ATTNRES_EINVAL = 1,  /* null pointer, bad size, unsupported size combination */
+    ATTNRES_EDTYPE = 2,  /* unknown dtype */
+    ATTNRES_EALIGN = 3,  /* d or a stride not a multiple of 8, pointer not 16-byte aligned */
+    ATTNRES_EALIAS = 4,  /* an output overlaps an input (other than the allowed in-place case) */
+    ATTNRES_EHIP = 5     /* the HIP runtime reported an error at launch */
+} attnres_status_t;
+
+typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1 } attnres_dtype_t;
+
+/* Largest supported values. */
+#define ATTNRES_MAX_D 16384
+#define ATTNRES_MAX_SOURCES 32          /* attnres_full / phase 1 with S == 1 */
+#define ATTNRES_MAX_SOURCES_MULTI 16    /* phase 1 with S >= 2 */
+
+/*
+ * Phase 1 of a block ("Attention Residuals" notes, section 10, first phase;
+ * "Attention Residuals 阅读补充", static-query batching Q K^T).
+ * For each token t and each query s < S, over the n_src completed sources
+ * u_i = src + i*src_stride (each [T][d], dtype dt):
+ *     z_si = w_s^T (key_gain_s (.) u_i / r(u_i)),  m_s = max_i z_si,
+ *     lse_s = m_s + ln sum_i e^{z_si - m_s},
+ *     out[s][t][:] = sum_i e^{z_si - lse_s} u_i        (normalised)
+ *   w, key_gain: [S][d] fp32 (key_gain NULL = ones).
+ *   out: [S][T][d] dtype dt.  m_out, lse_out: [S][T] fp32 (m_out may be NULL).
+ * Limits: 1 <= n_src <= ATTNRES_MAX_SOURCES_MULTI when S >= 2, <=
+ * ATTNRES_MAX_SOURCES when S == 1; S >= 1 (queries are processed 32 at a
+ * time; each group of 32 reads the sources once).
+ * out must not overlap src; m_out/lse_out must not overlap anything.
+ */
+attnres_status_t attnres_phase1(attnres_dtype_t dt,
+                                const void* src, int64_t n_src, int64_t src_stride,
+                                int64_t T, int64_t d,
+                                const float* w, const float* key_gain, int64_t S, float eps,
+                                void* out, float* m_out, float* lse_out, void* stream);
+
+/*
+ * Phase 2 for one sublayer j of a block ("Attention Residuals" notes,
+ * section 10, second phase; "Attention Residuals 阅读补充", merge of two
+ * disjoint partitions; PreNorm fusion as in "ML 研究者的三层基本功", system
+ * layer, and the CSDN summary section 4.2 on kernel fusion).
+ *   o = p1_out [T][d] (dt), lse = p1_lse [T] fp32: this sublayer's phase-1
+ *   partition (output normalised, lse = its log-sum-exp).
+ *   If sublayer_prev == NULL (first sublayer of the block): h = o.
+ *   Otherwise the partial sum is
+ *       p = (partial_in or 0) + sublayer_prev        (fp32 arithmetic)
+ *   partial_in: [T][d] of dtype partial_dt (NULL = zero);
+ *   sublayer_prev: [T][d] of dtype dt (the previous sublayer's output).
+ *   p is written to partial_out ([T][d] fp32, NULL = not stored; it may be
+ *   the same pointer as partial_in when partial_dt == ATTNRES_F32).
+ *   Merge: zc = w^T(key_gain (.) p / r(p)), M = max(lse, zc),
+ *       h = (e^{lse-M} o + e^{zc-M} p) / (e^{lse-M} + e^{zc-M}).
+ *   PreNorm: x = prenorm_gain (.) h / r(h)  (prenorm_gain NULL = ones).
+ *   h_out, x_out: [T][d] dtype dt, either may be NULL but not both.
+ *   w, key_gain, prenorm_gain: [d] fp32 (key_gain NULL = ones).
+ * Passing partial_in or partial_out without sublayer_prev is ATTNRES_EINVAL.
+ */
+attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d,
+                                      const void* p1_out, const float* p1_lse,
+                                      attnres_dtype_t partial_dt, const void* partial_in,
+                                      const void* sublayer_prev, float* partial_out,
+                                      const float* w, const float* key_gain,
+                                      const float* prenorm_gain, float eps,
+                                      void* h_out, void* x_out, void* stream);
+
+/*
+ * One-shot depth aggregation with a single query ("Attention Residuals"
+ * notes, section 7, Full AttnRes; also the final aggregation over
+ * b_0..b_N of section 8).  Sources u_i = src + i*src_stride, i < n_src.
+ *   h = sum_i softmax_i(z) u_i,  x = prenorm_gain (.) h / r(h).
+ *   h_out, x_out: [T][d] dtype dt, either may be NULL but not both (x_out
+ *   NULL: no PreNorm).  lse_out: [T] fp32 or NULL.
+ *   w, key_gain, prenorm_gain: [d] fp32 (gains NULL = ones).
+ * Limits: 1 <= n_src <= ATTNRES_MAX_SOURCES.  Outputs must not overlap src.
+ */
+attnres_status_t attnres_full(attnres_dtype_t dt,
+                              const void* src, int64_t n_src, int64_t src_stride,
+                              int64_t T, int64_t d,
+                              const float* w, const float* key_gain,
+                              const float* prenorm_gain, float eps,
+                              void* h_out, void* x_out, float* lse_out, void* stream);
+
+/*
+ * Block completion ("Attention Residuals" notes, section 8: b_n is the sum of
+ * the block's sublayer outputs):  out = (partial_in or 0) + v.
+ *   partial_in: [T][d] dtype partial_dt (NULL = zero); v, out: [T][d] dtype dt.
+ *   out may be the same pointer as partial_in when partial_dt == dt.
+ */
+attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t d,
+                                          attnres_dtype_t partial_dt, const void* partial_in,
+                                          const void* v, void* out, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* attnres_status_string(attnres_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTNRES_H */

@@ -1,0 +1,134 @@
+"""Parity harness: run a workload through the HIP path, capture sampled rows at
+every aggregation site, and compare them with the fp64 oracle.
+
+Metric (per output row): max_k |gpu_k - ref_k| / max_k |ref_k|.  Bars: 2e-2
+for bf16 storage, 1e-5 for fp32 storage.  Statistics (lse) are compared as
+|gpu - ref| / max(1, |ref|) against the same bar.
+"""
+from __future__ import annotations
+
+import time
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from transformer_depth_wise_amd import BlockAttnRes, FullAttnRes
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def row_rel_err(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-row max-abs-rel error over the last axis."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.max(np.abs(gpu - ref), axis=-1)
+    den = np.max(np.abs(ref), axis=-1)
+    return num / np.maximum(den, 1e-300)
+
+
+def stat_err(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return np.abs(gpu - ref) / np.maximum(1.0, np.abs(ref))
+
+
+def _host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+class Capture:
+    """Collect sampled rows of every site's outputs on the device."""
+
+    def __init__(self, idx: torch.Tensor):
+        self.idx = idx
+        self.rows: Dict[str, List[torch.Tensor]] = {}
+
+    def __call__(self, site, **tensors):
+        for k, t in tensors.items():
+            if t is None:
+                continue
+            self.rows.setdefault(k, []).append(t.index_select(0, self.idx).clone())
+
+    def stacked(self, k) -> np.ndarray:
+        return _host(torch.stack(self.rows[k]))
+
+
+def block_inputs(w: synth.Workload, device, t0: int = 0, t1: Optional[int] = None):
+    t1 = w.T if t1 is None else t1
+    scales = synth.sublayer_scales(w)
+    emb = synth.embedding(w, t0, t1, device)
+    given = [synth.given_block(w, n + 1, t0, t1, device) for n in range(w.n_given)]
+    v = [synth.sublayer_output(w, l + 1, t0, t1, device, scales) for l in range(w.L)]
+    return emb, given, v
+
+
+def run_block_parity(w: synth.Workload, samples: Optional[Sequence[int]] = None, device="cuda",
+                     keep_h: bool = True, x_ring: int = 4) -> Dict[str, float]:
+    """Block AttnRes on the GPU vs the oracle on sampled tokens.  Returns the
+    worst error per output kind (already asserted against the bar)."""
+    dev = torch.device(device)
+    emb, given, v = block_inputs(w, dev)
+    prm = synth.params(w, dev)
+    st = BlockAttnRes(w.T, w.d, w.block_sizes, w.torch_dtype, n_given=w.n_given, eps=w.eps, device=dev,
+                      keep_h=keep_h, x_ring=x_ring, final_site=w.final_site)
+    st.reps[0].copy_(emb)
+    for n, b in enumerate(given):
+        st.reps[1 + n].copy_(b)
+    samples = list(range(w.T)) if samples is None else list(samples)
+    idx = torch.tensor(samples, dtype=torch.long, device=dev)
+    cap = Capture(idx)
+    st.forward(prm, lambda l, x: v[l], hook=cap)
+    torch.cuda.synchronize()
+
+    # oracle on the sampled tokens, from the very values the GPU saw
+    o = oracle.block_forward(
+        emb.index_select(0, idx), torch.stack([t.index_select(0, idx) for t in v]), prm["w"], prm["g"],
+        prm["gamma"], w.block_sizes, w.eps,
+        given=torch.stack([t.index_select(0, idx) for t in given]) if given else None,
+        final_site=w.final_site)
+    tol = TOL[w.dtype]
+    worst = {}
+    worst["x"] = float(row_rel_err(cap.stacked("x"), o["x"]).max())
+    if keep_h:
+        worst["h"] = float(row_rel_err(cap.stacked("h"), o["h"]).max())
+    worst["o1"] = float(row_rel_err(cap.stacked("o1"), o["o1"]).max())
+    worst["lse1"] = float(stat_err(cap.stacked("lse1"), o["lse1"]).max())
+    worst["m1"] = float(stat_err(cap.stacked("m1"), o["m1"]).max())
+    reps_gpu = _host(st.reps.index_select(1, idx))
+    worst["reps"] = float(row_rel_err(reps_gpu, o["reps"]).max())
+    if w.final_site:
+        worst["hfinal"] = float(row_rel_err(_host(st.h_final.index_select(0, idx)), o["hfinal"]).max())
+    for k, e in worst.items():
+        assert e <= tol, "%s: %s max-abs-rel %.3e exceeds %.1e" % (w.name, k, e, tol)
+    return worst
+
+
+def run_full_parity(w: synth.Workload, samples: Optional[Sequence[int]] = None, device="cuda"):
+    dev = torch.device(device)
+    scales = synth.sublayer_scales(w)
+    prm = synth.params(w, dev)
+    st = FullAttnRes(w.T, w.d, w.L, w.torch_dtype, eps=w.eps, device=dev, keep_h=True, final_site=w.final_site)
+    st.hist[0].copy_(synth.embedding(w, 0, w.T, dev))
+    for l in range(w.L):
+        st.hist[l + 1].copy_(synth.sublayer_output(w, l + 1, 0, w.T, dev, scales))
+    samples = list(range(w.T)) if samples is None else list(samples)
+    idx = torch.tensor(samples, dtype=torch.long, device=dev)
+    cap = Capture(idx)
+    st.forward(prm, lambda l, x: None, hook=cap)
+    torch.cuda.synchronize()
+    hist = st.hist.index_select(1, idx)
+    o = oracle.full_forward(hist[0], hist[1:], prm["w"], prm["g"], prm["gamma"], w.eps, final_site=w.final_site)
+    tol = TOL[w.dtype]
+    worst = {
+        "x": float(row_rel_err(cap.stacked("x"), o["x"]).max()),
+        "h": float(row_rel_err(cap.stacked("h"), o["h"]).max()),
+        "lse": float(stat_err(cap.stacked("lse"), o["lse"]).max()),
+    }
+    if w.final_site:
+        worst["hfinal"] = float(row_rel_err(_host(st.h_final.index_select(0, idx)), o["hfinal"]).max())
+    for k, e in worst.items():
+        assert e <= tol, "%s: %s max-abs-rel %.3e exceeds %.1e" % (w.name, k, e, tol)
+    return worst

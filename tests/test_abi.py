@@ -1,0 +1,122 @@
+"""The C-ABI library: it loads, exports every declared symbol, and rejects bad
+arguments before any launch.  Runs without a GPU: every call here fails
+validation (or has T == 0) and returns before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnres.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from transformer_depth_wise_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from transformer_depth_wise_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attnres_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("attnres_phase1", "attnres_phase2_merge", "attnres_full", "attnres_block_accumulate",
+              "attnres_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_uses_the_same_names():
+    import transformer_depth_wise_amd as tdw
+    for name in declared_functions():
+        if name != "attnres_status_string":
+            assert callable(getattr(tdw, name)), name
+
+
+A = 1 << 20  # a 16-byte aligned fake device address; never dereferenced here
+EINVAL, EDTYPE, EALIGN, EALIAS = 1, 2, 3, 4
+
+
+def p(x):
+    return ctypes.c_void_p(x)
+
+
+def phase1(lib, dt=1, src=A, n=3, stride=4096 * 64, T=4096, d=64, w=8 * A, kg=None, S=4, eps=1e-6,
+           out=16 * A, m=None, lse=24 * A):
+    return lib.attnres_phase1(dt, p(src), n, stride, T, d, p(w), p(kg), S, eps, p(out), p(m), p(lse), None)
+
+
+def test_phase1_validation(lib):
+    assert phase1(lib, dt=7) == EDTYPE
+    assert phase1(lib, d=12) == EALIGN
+    assert phase1(lib, d=0) == EINVAL
+    assert phase1(lib, d=16392) == EINVAL
+    assert phase1(lib, n=0) == EINVAL
+    assert phase1(lib, S=0) == EINVAL
+    assert phase1(lib, n=17) == EINVAL            # more than 16 sources with S >= 2
+    assert phase1(lib, n=33, S=1) == EINVAL
+    assert phase1(lib, src=None) == EINVAL
+    assert phase1(lib, lse=None) == EINVAL
+    assert phase1(lib, stride=100) == EINVAL      # slabs would overlap
+    assert phase1(lib, stride=4096 * 64 + 4) == EALIGN
+    assert phase1(lib, src=A + 4) == EALIGN
+    assert phase1(lib, out=A + 4096 * 64) == EALIAS   # output inside the source slabs
+    assert phase1(lib, lse=16 * A + 8) == EALIAS      # stats inside the output
+    assert phase1(lib, lse=24 * A + 2) == EALIGN
+    assert phase1(lib, eps=-1.0) == EINVAL
+    assert phase1(lib, T=0) == 0                      # nothing to do, nothing launched
+
+
+def merge(lib, dt=1, T=1024, d=64, o=A, lse=2 * A, pdt=0, pin=None, v=None, pout=None, w=3 * A, kg=None,
+          gm=None, h=None, x=4 * A):
+    return lib.attnres_phase2_merge(dt, T, d, p(o), p(lse), pdt, p(pin), p(v), p(pout), p(w), p(kg), p(gm),
+                                    1e-6, p(h), p(x), None)
+
+
+def test_merge_validation(lib):
+    assert merge(lib, x=None) == EINVAL                    # no output at all
+    assert merge(lib, pin=5 * A) == EINVAL                 # partial without the previous output
+    assert merge(lib, pout=5 * A) == EINVAL
+    assert merge(lib, pdt=9) == EDTYPE
+    assert merge(lib, d=20) == EALIGN
+    assert merge(lib, x=A + 64) == EALIAS                  # output over the phase-1 input
+    assert merge(lib, v=6 * A, pin=5 * A, pout=5 * A + 16) == EALIAS   # shifted in-place
+    assert merge(lib, v=6 * A, pin=5 * A, pout=5 * A, pdt=1) == EALIAS  # in place needs fp32
+    assert merge(lib, T=0, v=6 * A, pin=5 * A, pout=5 * A) == 0         # exact in-place fp32 is allowed
+    assert merge(lib, T=0) == 0
+
+
+def test_full_and_accumulate_validation(lib):
+    f = lambda **k: lib.attnres_full(k.get("dt", 1), p(k.get("src", A)), k.get("n", 2), k.get("stride", 64 * 64),
+                                     k.get("T", 64), k.get("d", 64), p(k.get("w", 2 * A)), None, None, 1e-6,
+                                     p(k.get("h", 3 * A)), p(k.get("x")), p(k.get("lse")), None)
+    assert f(n=0) == EINVAL
+    assert f(n=33) == EINVAL
+    assert f(h=None) == EINVAL
+    assert f(h=A + 128) == EALIAS
+    assert f(d=4) == EALIGN
+    assert f(T=0) == 0
+    acc = lambda **k: lib.attnres_block_accumulate(k.get("dt", 1), k.get("T", 64), k.get("d", 64), k.get("pdt", 0),
+                                                   p(k.get("pin")), p(k.get("v", A)), p(k.get("out", 2 * A)), None)
+    assert acc(v=None) == EINVAL
+    assert acc(out=A) == EALIAS
+    assert acc(pin=2 * A, pdt=0) == EALIAS          # in place only with the same dtype
+    assert acc(pin=2 * A, pdt=1, T=0) == 0
+    assert acc(dt=3) == EDTYPE
+
+
+def test_status_strings(lib):
+    from transformer_depth_wise_amd import _lib
+    for code in range(6):
+        assert _lib.status_string(code).startswith("ATTNRES_")

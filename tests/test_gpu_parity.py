@@ -1,0 +1,178 @@
+"""GPU parity of the HIP path against the fp64 oracle (needs an MI355X).
+
+Every workload runs through the C ABI in the launch configuration the
+benchmark uses.  Each test prints the case it is about to run before any GPU
+work, so a failure can be attributed from the log alone.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from harness import TOL, row_rel_err, run_block_parity, run_full_parity, stat_err, _host
+import transformer_depth_wise_amd as tdw
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    tdw.load()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ full workloads
+def test_tiny_block_f32_all_tokens():
+    w = synth.WORKLOADS["tiny_block_f32"]
+    _say("case tiny_block_f32 T=%d d=%d blocks=%s" % (w.T, w.d, w.block_sizes))
+    worst = run_block_parity(w)
+    _say("worst", worst)
+
+
+def test_full_bf16_all_sites():
+    w = synth.WORKLOADS["full_bf16"]
+    _say("case full_bf16 T=%d d=%d L=%d (sampled 512 tokens)" % (w.T, w.d, w.L))
+    worst = run_full_parity(w, samples=synth.sample_tokens(w.T, 512))
+    _say("worst", worst)
+
+
+def test_decode_block_bf16_all_tokens():
+    w = synth.WORKLOADS["decode_block_bf16"]
+    _say("case decode_block_bf16 T=%d d=%d S=24 given=%d" % (w.T, w.d, w.n_given))
+    worst = run_block_parity(w)
+    _say("worst", worst)
+
+
+def test_prefill_chunk_bf16_sampled():
+    w = synth.WORKLOADS["prefill_chunk_bf16"]
+    _say("case prefill_chunk_bf16 T=%d d=%d blocks=%s (64 sampled tokens)" % (w.T, w.d, w.block_sizes))
+    worst = run_block_parity(w, samples=synth.sample_tokens(w.T, 64), keep_h=True)
+    _say("worst", worst)
+
+
+# -------------------------------------------------- ragged and edge shapes
+EDGE = [
+    # (T, d, blocks, n_given, dtype)
+    (1, 8, (3, 2), 0, "f32"),
+    (17, 24, (1, 4), 1, "f32"),
+    (33, 136, (2, 3, 5), 0, "bf16"),
+    (40, 1032, (5, 1, 2), 2, "bf16"),
+    (19, 7168, (3,), 7, "bf16"),
+    (50, 256, (33,), 0, "bf16"),          # S > 32: two query tiles in one phase-1 call
+    (16, 64, (17, 2), 0, "f32"),           # S = 17: second query tile of 16 partly used
+    (23, 512, (1,) * 15, 0, "bf16"),      # 16 completed sources at the last blocks
+    (31, 16384, (4,), 0, "bf16"),          # widest supported row
+]
+
+
+@pytest.mark.parametrize("T,d,blocks,n_given,dt", EDGE)
+def test_block_edge_shapes(T, d, blocks, n_given, dt):
+    base = synth.WORKLOADS["tiny_block_f32"]
+    w = synth.scaled(base, name="edge", T=T, d=d, block_sizes=tuple(blocks), n_given=n_given, dtype=dt,
+                     unit_gains=False, seed=4242 + T + d)
+    _say("case edge T=%d d=%d blocks=%s given=%d %s" % (T, d, blocks, n_given, dt))
+    worst = run_block_parity(w)
+    _say("worst", worst)
+
+
+@pytest.mark.parametrize("T,d,L", [(5, 8, 3), (18, 200, 31), (64, 1024, 9)])
+def test_full_edge_shapes(T, d, L):
+    base = synth.WORKLOADS["full_bf16"]
+    w = synth.scaled(base, name="full_edge", T=T, d=d, block_sizes=(1,) * L, seed=777 + L)
+    _say("case full_edge T=%d d=%d L=%d" % (T, d, L))
+    run_full_parity(w)
+
+
+def test_empty_token_set_is_a_noop():
+    _say("case T=0")
+    dev = torch.device("cuda")
+    z = torch.empty((3, 0, 64), dtype=torch.bfloat16, device=dev)
+    w = torch.zeros((2, 64), dtype=torch.float32, device=dev)
+    out = torch.empty((2, 0, 64), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((2, 0), dtype=torch.float32, device=dev)
+    tdw.attnres_phase1(z, 3, w, None, 1e-6, out, None, lse)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------- special cases
+def test_zero_query_gives_mean_and_identical_sources_give_source():
+    _say("case special: zero query / identical sources")
+    dev = torch.device("cuda")
+    T, d, n = 37, 7168, 9
+    src = (torch.randn((n, T, d), device=dev) * 3).to(torch.bfloat16)
+    h = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T,), dtype=torch.float32, device=dev)
+    tdw.attnres_full(src, n, torch.zeros(d, device=dev), None, None, 1e-6, h, None, lse)
+    mean = src.double().mean(0)
+    assert row_rel_err(_host(h), mean.cpu().numpy()).max() <= 1e-2
+    assert np.allclose(lse.cpu().numpy(), math.log(n), rtol=1e-6)
+    same = src[:1].expand(n, T, d).contiguous()
+    tdw.attnres_full(same, n, torch.randn(d, device=dev), None, None, 1e-6, h, None, lse)
+    assert torch.equal(h, same[0])
+
+
+def test_phase1_single_query_equals_full():
+    _say("case phase1(S=1) vs full")
+    dev = torch.device("cuda")
+    T, d, n = 50, 1024, 6
+    src = (torch.randn((n, T, d), device=dev)).to(torch.bfloat16)
+    wq = torch.randn((1, d), device=dev) * 0.02
+    g = torch.rand((1, d), device=dev) * 0.4 + 0.8
+    out = torch.empty((1, T, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, T), dtype=torch.float32, device=dev)
+    tdw.attnres_phase1(src, n, wq, g, 1e-6, out, None, lse)
+    h = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    lse2 = torch.empty((T,), dtype=torch.float32, device=dev)
+    tdw.attnres_full(src, n, wq[0], g[0], None, 1e-6, h, None, lse2)
+    assert torch.equal(out[0], h)
+    assert torch.equal(lse[0], lse2)
+
+
+def test_block_runs_are_bitwise_deterministic():
+    w = synth.scaled(synth.WORKLOADS["prefill_chunk_bf16"], T=2048, name="det")
+    _say("case determinism T=%d" % w.T)
+    dev = torch.device("cuda")
+    from harness import block_inputs
+    emb, given, v = block_inputs(w, dev)
+    prm = synth.params(w, dev)
+    outs = []
+    for _ in range(2):
+        st = tdw.BlockAttnRes(w.T, w.d, w.block_sizes, w.torch_dtype, device=dev, x_ring=1, keep_h=False)
+        st.reps[0].copy_(emb)
+        xs = []
+        st.forward(prm, lambda l, x: v[l], hook=lambda site, x, **k: xs.append(x[::97].clone()))
+        torch.cuda.synchronize()
+        outs.append((st.h_final.clone(), st.reps.clone(), torch.stack(xs)))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
+def test_token_split_invariance():
+    """Tokens never interact: one call over T tokens equals calls over slices."""
+    _say("case token split invariance")
+    dev = torch.device("cuda")
+    w = synth.scaled(synth.WORKLOADS["prefill_chunk_bf16"], T=1000, block_sizes=(5, 7), name="split")
+    from harness import block_inputs
+    emb, given, v = block_inputs(w, dev)
+    prm = synth.params(w, dev)
+    st = tdw.BlockAttnRes(w.T, w.d, w.block_sizes, w.torch_dtype, device=dev)
+    st.reps[0].copy_(emb)
+    st.forward(prm, lambda l, x: v[l])
+    whole = st.h_final.clone()
+    for a, b in ((0, 333), (333, 1000)):
+        s2 = tdw.BlockAttnRes(b - a, w.d, w.block_sizes, w.torch_dtype, device=dev)
+        s2.reps[0].copy_(emb[a:b])
+        s2.forward(prm, lambda l, x: v[l][a:b].contiguous())
+        assert torch.equal(s2.h_final, whole[a:b])

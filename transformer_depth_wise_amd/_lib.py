@@ -1,0 +1,136 @@
+"""ctypes binding of libattnres.so: the four C-ABI entry points, same names.
+
+Argument marshalling only.  Tensors are passed by device pointer together with
+the current HIP stream; every computation happens in the library's gfx950
+kernels.  There is no fallback: if the library is missing or a tensor is not
+on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattnres.so")
+
+F32, BF16 = 0, 1
+ATTNRES_MAX_D = 16384
+ATTNRES_MAX_SOURCES = 32
+ATTNRES_MAX_SOURCES_MULTI = 16
+
+EXPORTED = ("attnres_phase1", "attnres_phase2_merge", "attnres_full",
+            "attnres_block_accumulate", "attnres_status_string")
+
+
+class AttnResError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__("%s failed: %s (status %d)" % (fn, msg, code))
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libattnres.so not found at %s: build it with "
+                           "`python -m transformer_depth_wise_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    V, I, F, E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    lib.attnres_phase1.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V]
+    lib.attnres_phase2_merge.argtypes = [E, I, I, V, V, E, V, V, V, V, V, V, F, V, V, V]
+    lib.attnres_full.argtypes = [E, V, I, I, I, I, V, V, V, F, V, V, V, V]
+    lib.attnres_block_accumulate.argtypes = [E, I, I, E, V, V, V, V]
+    for fn in ("attnres_phase1", "attnres_phase2_merge", "attnres_full", "attnres_block_accumulate"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.attnres_status_string.argtypes = [ctypes.c_int]
+    lib.attnres_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().attnres_status_string(int(code)).decode()
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError("unsupported storage dtype %s (float32 or bfloat16)" % t)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor is not on a GPU; the AttnRes library computes on the GPU only")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise AttnResError(fn, rc, status_string(rc))
+
+
+def attnres_phase1(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],
+                   eps: float, out: torch.Tensor, m_out: Optional[torch.Tensor], lse_out: torch.Tensor,
+                   stream=None) -> None:
+    """src: [>=n_src, T, d] slabs (sources 0..n_src-1 at stride src.stride(0));
+    w, key_gain: [S, d] fp32; out: [S, T, d]; m_out, lse_out: [S, T] fp32."""
+    S, T, d = out.shape
+    stride = src.stride(0) if src.dim() == 3 else T * d
+    rc = load().attnres_phase1(dtype_code(src.dtype), _ptr(src), n_src, stride, T, d, _ptr(w), _ptr(key_gain),
+                               S, eps, _ptr(out), _ptr(m_out), _ptr(lse_out), _stream(stream))
+    _check("attnres_phase1", rc)
+
+
+def attnres_phase2_merge(p1_out: torch.Tensor, p1_lse: torch.Tensor, partial_in: Optional[torch.Tensor],
+                         sublayer_prev: Optional[torch.Tensor], partial_out: Optional[torch.Tensor],
+                         w: torch.Tensor, key_gain: Optional[torch.Tensor], prenorm_gain: Optional[torch.Tensor],
+                         eps: float, h_out: Optional[torch.Tensor], x_out: Optional[torch.Tensor],
+                         stream=None) -> None:
+    """p1_out: [T, d]; p1_lse: [T]; partial_in: [T, d] fp32 or storage dtype;
+    sublayer_prev: [T, d]; partial_out: [T, d] fp32; w, key_gain, prenorm_gain: [d]."""
+    T, d = p1_out.shape
+    pdt = dtype_code(partial_in.dtype) if partial_in is not None else F32
+    rc = load().attnres_phase2_merge(dtype_code(p1_out.dtype), T, d, _ptr(p1_out), _ptr(p1_lse), pdt,
+                                     _ptr(partial_in), _ptr(sublayer_prev), _ptr(partial_out), _ptr(w),
+                                     _ptr(key_gain), _ptr(prenorm_gain), eps, _ptr(h_out), _ptr(x_out),
+                                     _stream(stream))
+    _check("attnres_phase2_merge", rc)
+
+
+def attnres_full(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],
+                 prenorm_gain: Optional[torch.Tensor], eps: float, h_out: Optional[torch.Tensor],
+                 x_out: Optional[torch.Tensor], lse_out: Optional[torch.Tensor], stream=None) -> None:
+    """src: [>=n_src, T, d]; w, gains: [d] fp32; h_out/x_out: [T, d]; lse_out: [T]."""
+    T, d = src.shape[-2], src.shape[-1]
+    stride = src.stride(0) if src.dim() == 3 else T * d
+    rc = load().attnres_full(dtype_code(src.dtype), _ptr(src), n_src, stride, T, d, _ptr(w), _ptr(key_gain),
+                             _ptr(prenorm_gain), eps, _ptr(h_out), _ptr(x_out), _ptr(lse_out), _stream(stream))
+    _check("attnres_full", rc)
+
+
+def attnres_block_accumulate(partial_in: Optional[torch.Tensor], v: torch.Tensor, out: torch.Tensor,
+                             stream=None) -> None:
+    """out = (partial_in or 0) + v; all [T, d]."""
+    T, d = v.shape
+    pdt = dtype_code(partial_in.dtype) if partial_in is not None else F32
+    rc = load().attnres_block_accumulate(dtype_code(v.dtype), T, d, pdt, _ptr(partial_in), _ptr(v), _ptr(out),
+                                         _stream(stream))
+    _check("attnres_block_accumulate", rc)

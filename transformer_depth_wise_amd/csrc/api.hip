@@ -1,0 +1,220 @@
+// C ABI of libattnres: argument validation and dispatch to the gfx950
+// kernels.  Every check runs on the host before anything is launched; see
+// include/attnres.h for the contract of each entry point.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/attnres.h"
+#include "attnres_launch.h"
+
+namespace attnres {
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace attnres
+
+namespace {
+
+using attnres::Dtype;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int64_t esize(attnres_dtype_t dt) { return dt == ATTNRES_F32 ? 4 : 2; }
+
+bool dtype_ok(attnres_dtype_t dt) { return dt == ATTNRES_F32 || dt == ATTNRES_BF16; }
+
+attnres_status_t check_d(int64_t d) {
+  if (d <= 0 || d > ATTNRES_MAX_D) return ATTNRES_EINVAL;
+  if (d % 8 != 0) return ATTNRES_EALIGN;
+  return ATTNRES_OK;
+}
+
+attnres_status_t hip_status(hipError_t e) { return e == hipSuccess ? ATTNRES_OK : ATTNRES_EHIP; }
+
+// all non-null row pointers 16-byte aligned, statistics pointers 4-byte aligned
+attnres_status_t check_align(std::initializer_list<const void*> rows,
+                             std::initializer_list<const void*> stats = {}) {
+  for (const void* p : rows)
+    if (p && !aligned16(p)) return ATTNRES_EALIGN;
+  for (const void* p : stats)
+    if (p && !aligned4(p)) return ATTNRES_EALIGN;
+  return ATTNRES_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attnres_status_string(attnres_status_t status) {
+  switch (status) {
+    case ATTNRES_OK: return "ATTNRES_OK";
+    case ATTNRES_EINVAL: return "ATTNRES_EINVAL: null pointer, bad size or unsupported size combination";
+    case ATTNRES_EDTYPE: return "ATTNRES_EDTYPE: unknown dtype";
+    case ATTNRES_EALIGN: return "ATTNRES_EALIGN: d or a stride not a multiple of 8, or pointer not 16-byte aligned";
+    case ATTNRES_EALIAS: return "ATTNRES_EALIAS: an output overlaps an input";
+    case ATTNRES_EHIP: return "ATTNRES_EHIP: the HIP runtime reported an error";
+  }
+  return "ATTNRES_UNKNOWN_STATUS";
+}
+
+attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
+                                int64_t T, int64_t d, const float* w, const float* key_gain, int64_t S,
+                                float eps, void* out, float* m_out, float* lse_out, void* stream) {
+  if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
+  attnres_status_t st = check_d(d);
+  if (st != ATTNRES_OK) return st;
+  if (T < 0 || S < 1 || n_src < 1) return ATTNRES_EINVAL;
+  if (n_src > (S == 1 ? ATTNRES_MAX_SOURCES : ATTNRES_MAX_SOURCES_MULTI)) return ATTNRES_EINVAL;
+  if (T > (int64_t)1 << 40 || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (!src || !w || !out || !lse_out) return ATTNRES_EINVAL;
+  if (n_src > 1 && (src_stride < T * d)) return ATTNRES_EINVAL;
+  if (src_stride % 8 != 0) return ATTNRES_EALIGN;
+  st = check_align({src, w, key_gain, out}, {m_out, lse_out});
+  if (st != ATTNRES_OK) return st;
+  const int64_t es = esize(dt);
+  const Range rs = range_of(src, ((n_src - 1) * src_stride + T * d) * es);
+  const Range ro = range_of(out, S * T * d * es);
+  const Range rl = range_of(lse_out, S * T * 4);
+  const Range rm = m_out ? range_of(m_out, S * T * 4) : Range{0, 0};
+  const Range rw = range_of(w, S * d * 4);
+  const Range rg = key_gain ? range_of(key_gain, S * d * 4) : Range{0, 0};
+  for (Range o : {ro, rl, rm})
+    for (Range i : {rs, rw, rg})
+      if (overlaps(o, i)) return ATTNRES_EALIAS;
+  if (overlaps(ro, rl) || overlaps(ro, rm) || overlaps(rl, rm)) return ATTNRES_EALIAS;
+  if (T == 0) return ATTNRES_OK;
+
+  const Dtype kdt = dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (S == 1)
+    return hip_status(attnres::launch_phase1_single(kdt, src, (int)n_src, src_stride, T, (int)d, w, key_gain,
+                                                    nullptr, eps, out, nullptr, m_out, lse_out, s));
+  for (int64_t s0 = 0; s0 < S; s0 += 32) {
+    const int64_t sn = (S - s0) < 32 ? (S - s0) : 32;
+    char* o = static_cast<char*>(out) + s0 * T * d * es;
+    hipError_t e = attnres::launch_phase1_multi(kdt, src, (int)n_src, src_stride, T, (int)d, w + s0 * d,
+                                                key_gain ? key_gain + s0 * d : nullptr, (int)sn, eps, o,
+                                                m_out ? m_out + s0 * T : nullptr, lse_out + s0 * T, s);
+    if (e != hipSuccess) return ATTNRES_EHIP;
+  }
+  return ATTNRES_OK;
+}
+
+attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, const void* p1_out,
+                                      const float* p1_lse, attnres_dtype_t partial_dt, const void* partial_in,
+                                      const void* sublayer_prev, float* partial_out, const float* w,
+                                      const float* key_gain, const float* prenorm_gain, float eps, void* h_out,
+                                      void* x_out, void* stream) {
+  if (!dtype_ok(dt) || !dtype_ok(partial_dt)) return ATTNRES_EDTYPE;
+  attnres_status_t st = check_d(d);
+  if (st != ATTNRES_OK) return st;
+  if (T < 0 || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (!p1_out || !p1_lse || (!h_out && !x_out)) return ATTNRES_EINVAL;
+  if (!sublayer_prev && (partial_in || partial_out)) return ATTNRES_EINVAL;
+  if (sublayer_prev && !w) return ATTNRES_EINVAL;
+  st = check_align({p1_out, partial_in, sublayer_prev, partial_out, w, key_gain, prenorm_gain, h_out, x_out}, {p1_lse});
+  if (st != ATTNRES_OK) return st;
+  const int64_t es = esize(dt);
+  const int64_t rows = T * d;
+  const Range r_o = range_of(p1_out, rows * es), r_l = range_of(p1_lse, T * 4);
+  const Range r_pi = partial_in ? range_of(partial_in, rows * esize(partial_dt)) : Range{0, 0};
+  const Range r_v = sublayer_prev ? range_of(sublayer_prev, rows * es) : Range{0, 0};
+  const Range r_po = partial_out ? range_of(partial_out, rows * 4) : Range{0, 0};
+  const Range r_w = w ? range_of(w, d * 4) : Range{0, 0};
+  const Range r_g = key_gain ? range_of(key_gain, d * 4) : Range{0, 0};
+  const Range r_gm = prenorm_gain ? range_of(prenorm_gain, d * 4) : Range{0, 0};
+  const Range r_h = h_out ? range_of(h_out, rows * es) : Range{0, 0};
+  const Range r_x = x_out ? range_of(x_out, rows * es) : Range{0, 0};
+  // partial_out may be exactly partial_in (fp32, element-wise in place); no other overlap
+  const bool in_place = partial_out && partial_in == static_cast<const void*>(partial_out) && partial_dt == ATTNRES_F32;
+  for (Range o : {r_h, r_x, r_po})
+    for (Range i : {r_o, r_l, r_pi, r_v, r_w, r_g, r_gm}) {
+      if (in_place && o.lo == r_po.lo && o.hi == r_po.hi && i.lo == r_pi.lo && i.hi == r_pi.hi) continue;
+      if (overlaps(o, i)) return ATTNRES_EALIAS;
+    }
+  if (overlaps(r_h, r_x) || overlaps(r_h, r_po) || overlaps(r_x, r_po)) return ATTNRES_EALIAS;
+  if (T == 0) return ATTNRES_OK;
+  const Dtype kdt = dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
+  const Dtype kpdt = partial_dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
+  return hip_status(attnres::launch_merge(kdt, T, (int)d, p1_out, p1_lse, kpdt, partial_in, sublayer_prev,
+                                          partial_out, w, key_gain, x_out ? prenorm_gain : nullptr, eps, h_out,
+                                          x_out, static_cast<hipStream_t>(stream)));
+}
+
+attnres_status_t attnres_full(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride, int64_t T,
+                              int64_t d, const float* w, const float* key_gain, const float* prenorm_gain,
+                              float eps, void* h_out, void* x_out, float* lse_out, void* stream) {
+  if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
+  attnres_status_t st = check_d(d);
+  if (st != ATTNRES_OK) return st;
+  if (T < 0 || n_src < 1 || n_src > ATTNRES_MAX_SOURCES || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (!src || !w || (!h_out && !x_out)) return ATTNRES_EINVAL;
+  if (n_src > 1 && src_stride < T * d) return ATTNRES_EINVAL;
+  if (src_stride % 8 != 0) return ATTNRES_EALIGN;
+  st = check_align({src, w, key_gain, prenorm_gain, h_out, x_out}, {lse_out});
+  if (st != ATTNRES_OK) return st;
+  const int64_t es = esize(dt);
+  const Range rs = range_of(src, ((n_src - 1) * src_stride + T * d) * es);
+  const Range rh = h_out ? range_of(h_out, T * d * es) : Range{0, 0};
+  const Range rx = x_out ? range_of(x_out, T * d * es) : Range{0, 0};
+  const Range rl = lse_out ? range_of(lse_out, T * 4) : Range{0, 0};
+  const Range rw = range_of(w, d * 4);
+  const Range rg = key_gain ? range_of(key_gain, d * 4) : Range{0, 0};
+  const Range rgm = prenorm_gain ? range_of(prenorm_gain, d * 4) : Range{0, 0};
+  for (Range o : {rh, rx, rl})
+    for (Range i : {rs, rw, rg, rgm})
+      if (overlaps(o, i)) return ATTNRES_EALIAS;
+  if (overlaps(rh, rx) || overlaps(rh, rl) || overlaps(rx, rl)) return ATTNRES_EALIAS;
+  if (T == 0) return ATTNRES_OK;
+  const Dtype kdt = dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
+  return hip_status(attnres::launch_phase1_single(kdt, src, (int)n_src, src_stride, T, (int)d, w, key_gain,
+                                                  prenorm_gain, eps, h_out, x_out, nullptr, lse_out,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t d, attnres_dtype_t partial_dt,
+                                          const void* partial_in, const void* v, void* out, void* stream) {
+  if (!dtype_ok(dt) || !dtype_ok(partial_dt)) return ATTNRES_EDTYPE;
+  attnres_status_t st = check_d(d);
+  if (st != ATTNRES_OK) return st;
+  if (T < 0 || !v || !out) return ATTNRES_EINVAL;
+  st = check_align({partial_in, v, out});
+  if (st != ATTNRES_OK) return st;
+  const int64_t rows = T * d;
+  const Range ro = range_of(out, rows * esize(dt));
+  const Range rv = range_of(v, rows * esize(dt));
+  const Range rp = partial_in ? range_of(partial_in, rows * esize(partial_dt)) : Range{0, 0};
+  if (overlaps(ro, rv)) return ATTNRES_EALIAS;
+  const bool in_place = partial_in == out && partial_dt == dt;
+  if (!in_place && overlaps(ro, rp)) return ATTNRES_EALIAS;
+  if (T == 0) return ATTNRES_OK;
+  const Dtype kdt = dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
+  const Dtype kpdt = partial_dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
+  return hip_status(attnres::launch_accumulate(kdt, T, (int)d, kpdt, partial_in, v, out,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Device-side building blocks shared by the gfx950 AttnRes kernels.
+// Private to libattnres: storage-type traits, 16-byte row-chunk loads and
+// stores, and wave / workgroup reductions.  Compiled for gfx950 only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnres {
+
+// Storage tag for bf16 rows (raw bits).  All arithmetic is fp32.
+struct bf16_t {
+  unsigned short bits;
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---- 8-element row chunks ----------------------------------------------
+// A "chunk" is 8 consecutive channels of one row: 16 bytes of bf16 or 32
+// bytes of fp32.  d is a multiple of 8, rows are 16-byte aligned.
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4 u, float (&v)[8]) {
+  v[0] = __uint_as_float(u.x << 16);
+  v[1] = __uint_as_float(u.x & 0xffff0000u);
+  v[2] = __uint_as_float(u.y << 16);
+  v[3] = __uint_as_float(u.y & 0xffff0000u);
+  v[4] = __uint_as_float(u.z << 16);
+  v[5] = __uint_as_float(u.z & 0xffff0000u);
+  v[6] = __uint_as_float(u.w << 16);
+  v[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+// Round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  bf16x2_t p;
+  p.x = (__bf16)a;
+  p.y = (__bf16)b;
+  return __builtin_bit_cast(unsigned, p);
+}
+
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void load8(const bf16_t* p, float (&v)[8]) {
+  unpack_bf16x8(*reinterpret_cast<const uint4*>(p), v);
+}
+
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+__device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
+  uint4 u;
+  u.x = pack_bf16x2(v[0], v[1]);
+  u.y = pack_bf16x2(v[2], v[3]);
+  u.z = pack_bf16x2(v[4], v[5]);
+  u.w = pack_bf16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(p) = u;
+}
+
+__device__ __forceinline__ void zero8(float (&v)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 0.f;
+}
+
+// ---- reductions ------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// Sum of (a, b) over the 256 threads of a workgroup, in a fixed order (the
+// result is identical in every thread and from run to run).  `lds` holds 8
+// floats; callers alternate between two such buffers so that one barrier per
+// reduction suffices.
+__device__ __forceinline__ float2 block_sum2_256(float a, float b, float* lds) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    lds[2 * wave + 0] = a;
+    lds[2 * wave + 1] = b;
+  }
+  __syncthreads();
+  float2 r;
+  r.x = (lds[0] + lds[2]) + (lds[4] + lds[6]);
+  r.y = (lds[1] + lds[3]) + (lds[5] + lds[7]);
+  return r;
+}
+
+}  // namespace attnres

@@ -1,0 +1,32 @@
+// Host-side launchers of the gfx950 AttnRes kernels (private to libattnres).
+// Arguments are validated by the C ABI layer before these are called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnres {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+int device_cu_count();
+
+// Phase 1 of a block, one tile of at most 32 queries (S >= 2, n <= 16), or
+// S == 1 with optional PreNorm (n <= 32).  Returns a hipError_t.
+hipError_t launch_phase1_multi(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
+                               const float* w, const float* kg, int S, float eps, void* out,
+                               float* m_out, float* lse_out, hipStream_t stream);
+
+hipError_t launch_phase1_single(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
+                                const float* w, const float* kg, const float* gamma, float eps,
+                                void* h_out, void* x_out, float* m_out, float* lse_out,
+                                hipStream_t stream);
+
+hipError_t launch_merge(Dtype dt, int64_t T, int d, const void* o1, const float* lse1,
+                        Dtype pdt, const void* pin, const void* vprev, float* pout,
+                        const float* w, const float* kg, const float* gamma, float eps,
+                        void* h_out, void* x_out, hipStream_t stream);
+
+hipError_t launch_accumulate(Dtype dt, int64_t T, int d, Dtype pdt, const void* pin, const void* v,
+                             void* out, hipStream_t stream);
+
+}  // namespace attnres

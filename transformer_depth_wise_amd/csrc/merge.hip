@@ -1,0 +1,233 @@
+// Phase 2 of Block AttnRes on gfx950 and the block-completion sum.
+//
+// Phase 2 runs once per sublayer ("Attention Residuals" notes, section 10,
+// second phase): the first sublayer of a block takes the phase-1 result as
+// is; every later one scores the block's running partial sum and merges it
+// with the phase-1 partition exactly.  With the phase-1 output o already
+// normalised and lse its log-sum-exp, the two-partition merge of the reading
+// notes' two-phase section reduces to
+//     h = o + beta (p - o),   beta = 1 / (1 + e^{lse - z(p)}).
+// The merge is element-wise, so it is fused with the consuming sublayer's
+// PreNorm RMSNorm (CSDN summary, section 4.2; "ML 研究者的三层基本功",
+// system layer) and with the partial-sum update p = partial + v_prev.
+//
+// Each token row is processed by one team of threads (a wave for d <= 2048,
+// the whole 256-thread workgroup above that).  A thread owns CPL chunks of 8
+// channels; the row's two reductions (|p|^2 with w.p, then |h|^2) use wave
+// shuffles and, for 256-thread teams, one LDS exchange each.  The per-channel
+// parameters (w (.) g and gamma) stay in registers while the workgroup walks
+// over tokens with a grid stride.
+#include "attnres_device.h"
+#include "attnres_launch.h"
+
+namespace attnres {
+
+template <typename St, typename Pt, int TEAM, int CPL>
+__global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __restrict__ o1,
+                                               const float* __restrict__ lse1, const Pt* __restrict__ pin,
+                                               const St* __restrict__ vprev, float* __restrict__ pout,
+                                               const float* __restrict__ w, const float* __restrict__ kg,
+                                               const float* __restrict__ gamma, float eps,
+                                               St* __restrict__ h_out, St* __restrict__ x_out) {
+  constexpr int TPW = 256 / TEAM;  // tokens in flight per workgroup
+  __shared__ float red[2][8];
+  const int team = threadIdx.x / TEAM;
+  const int tl = threadIdx.x % TEAM;
+  const int C = d >> 3;
+  const float inv_d = 1.0f / (float)d;
+
+  float wq[CPL][8], gm[CPL][8];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const int c = tl + TEAM * k;
+    if (c < C) {
+      if (vprev) {
+        load8(w + c * 8, wq[k]);
+        if (kg) {
+          float g[8];
+          load8(kg + c * 8, g);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wq[k][e] *= g[e];
+        }
+      } else {
+        zero8(wq[k]);
+      }
+      if (gamma) {
+        load8(gamma + c * 8, gm[k]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gm[k][e] = 1.f;
+      }
+    } else {
+      zero8(wq[k]);
+      zero8(gm[k]);
+    }
+  }
+
+  int parity = 0;
+  const int64_t step = (int64_t)gridDim.x * TPW;
+  for (int64_t tok = (int64_t)blockIdx.x * TPW + team; tok - team < T; tok += step) {
+    const bool live = tok < T;  // uniform per team; whole-workgroup teams are always live here
+    float h[CPL][8], p[CPL][8];
+    float ss = 0.f, dot = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int c = tl + TEAM * k;
+      zero8(h[k]);
+      zero8(p[k]);
+      if (live && c < C) {
+        const int64_t off = tok * d + c * 8;
+        load8(o1 + off, h[k]);
+        if (vprev) {
+          load8(vprev + off, p[k]);
+          if (pin) {
+            float q[8];
+            load8(pin + off, q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[k][e] = q[e] + p[k][e];
+          }
+          if (pout) store8(pout + off, p[k]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ss = fmaf(p[k][e], p[k][e], ss);
+            dot = fmaf(wq[k][e], p[k][e], dot);
+          }
+        }
+      }
+    }
+    if (vprev) {
+      float2 r;
+      if (TEAM == 256) {
+        r = block_sum2_256(ss, dot, red[parity]);
+        parity ^= 1;
+      } else {
+        r.x = wave_sum(ss);
+        r.y = wave_sum(dot);
+      }
+      const float zc = r.y / sqrtf(r.x * inv_d + eps);
+      const float lse = live ? lse1[tok] : 0.f;
+      const float beta = 1.0f / (1.0f + expf(lse - zc));
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[k][e] = fmaf(beta, p[k][e] - h[k][e], h[k][e]);
+    }
+    float sh = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sh = fmaf(h[k][e], h[k][e], sh);
+    float r2 = 0.f;
+    if (x_out) {
+      if (TEAM == 256) {
+        r2 = block_sum2_256(sh, 0.f, red[parity]).x;
+        parity ^= 1;
+      } else {
+        r2 = wave_sum(sh);
+      }
+    }
+    if (live) {
+      const float rinv = x_out ? 1.0f / sqrtf(r2 * inv_d + eps) : 1.f;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        const int c = tl + TEAM * k;
+        if (c < C) {
+          const int64_t off = tok * d + c * 8;
+          if (h_out) store8(h_out + off, h[k]);
+          if (x_out) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = gm[k][e] * (h[k][e] * rinv);
+            store8(x_out + off, x);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <typename St, typename Pt>
+__global__ __launch_bounds__(256) void k_accumulate(int64_t nchunks, const Pt* __restrict__ pin,
+                                                    const St* __restrict__ v, St* __restrict__ out) {
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks; c += step) {
+    float a[8];
+    load8(v + c * 8, a);
+    if (pin) {
+      float b[8];
+      load8(pin + c * 8, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = b[e] + a[e];
+    }
+    store8(out + c * 8, a);
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+template <typename St, typename Pt, int TEAM, int CPL>
+static hipError_t run_merge(int64_t T, int d, const void* o1, const float* lse1, const void* pin,
+                            const void* vprev, float* pout, const float* w, const float* kg,
+                            const float* gamma, float eps, void* h_out, void* x_out, hipStream_t stream) {
+  constexpr int TPW = 256 / TEAM;
+  const int64_t tiles = (T + TPW - 1) / TPW;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const dim3 grid((unsigned)(tiles < cap ? tiles : cap));
+  hipLaunchKernelGGL((k_merge<St, Pt, TEAM, CPL>), grid, dim3(256), 0, stream, T, d,
+                     static_cast<const St*>(o1), lse1, static_cast<const Pt*>(pin),
+                     static_cast<const St*>(vprev), pout, w, kg, gamma, eps, static_cast<St*>(h_out),
+                     static_cast<St*>(x_out));
+  return hipGetLastError();
+}
+
+template <typename St, typename Pt>
+static hipError_t pick_team(int64_t T, int d, const void* o1, const float* lse1, const void* pin,
+                            const void* vprev, float* pout, const float* w, const float* kg,
+                            const float* gamma, float eps, void* h_out, void* x_out, hipStream_t stream) {
+  const int C = d >> 3;
+#define ATTNRES_RUN_MERGE(TEAM_, CPL_) \
+  return run_merge<St, Pt, TEAM_, CPL_>(T, d, o1, lse1, pin, vprev, pout, w, kg, gamma, eps, h_out, x_out, stream)
+  if (C <= 64) ATTNRES_RUN_MERGE(64, 1);
+  if (C <= 128) ATTNRES_RUN_MERGE(64, 2);
+  if (C <= 256) ATTNRES_RUN_MERGE(64, 4);
+  if (C <= 512) ATTNRES_RUN_MERGE(256, 2);
+  if (C <= 1024) ATTNRES_RUN_MERGE(256, 4);
+  ATTNRES_RUN_MERGE(256, 8);
+#undef ATTNRES_RUN_MERGE
+}
+
+hipError_t launch_merge(Dtype dt, int64_t T, int d, const void* o1, const float* lse1, Dtype pdt,
+                        const void* pin, const void* vprev, float* pout, const float* w, const float* kg,
+                        const float* gamma, float eps, void* h_out, void* x_out, hipStream_t stream) {
+  if (dt == kBF16) {
+    if (pdt == kBF16)
+      return pick_team<bf16_t, bf16_t>(T, d, o1, lse1, pin, vprev, pout, w, kg, gamma, eps, h_out, x_out, stream);
+    return pick_team<bf16_t, float>(T, d, o1, lse1, pin, vprev, pout, w, kg, gamma, eps, h_out, x_out, stream);
+  }
+  if (pdt == kBF16)
+    return pick_team<float, bf16_t>(T, d, o1, lse1, pin, vprev, pout, w, kg, gamma, eps, h_out, x_out, stream);
+  return pick_team<float, float>(T, d, o1, lse1, pin, vprev, pout, w, kg, gamma, eps, h_out, x_out, stream);
+}
+
+template <typename St, typename Pt>
+static hipError_t run_acc(int64_t T, int d, const void* pin, const void* v, void* out, hipStream_t stream) {
+  const int64_t nchunks = T * (int64_t)(d >> 3);
+  const int64_t blocks = (nchunks + 255) / 256;
+  const int64_t cap = (int64_t)device_cu_count() * 16;
+  const dim3 grid((unsigned)(blocks < cap ? blocks : cap));
+  hipLaunchKernelGGL((k_accumulate<St, Pt>), grid, dim3(256), 0, stream, nchunks,
+                     static_cast<const Pt*>(pin), static_cast<const St*>(v), static_cast<St*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_accumulate(Dtype dt, int64_t T, int d, Dtype pdt, const void* pin, const void* v,
+                             void* out, hipStream_t stream) {
+  if (dt == kBF16) {
+    if (pdt == kBF16) return run_acc<bf16_t, bf16_t>(T, d, pin, v, out, stream);
+    return run_acc<bf16_t, float>(T, d, pin, v, out, stream);
+  }
+  if (pdt == kBF16) return run_acc<float, bf16_t>(T, d, pin, v, out, stream);
+  return run_acc<float, float>(T, d, pin, v, out, stream);
+}
+
+}  // namespace attnres

@@ -1,0 +1,251 @@
+"""Drivers of the Block / Full AttnRes depth aggregation on one GPU.
+
+The schedule follows the two-phase inference of "Attention Residuals" (notes,
+section 10) for every block of sublayers:
+
+    phase 1   attnres_phase1      sources b_0..b_{n-1}, all S queries of the block
+    phase 2   attnres_phase2_merge  x S, sequentially; sublayer j's output is
+              produced between two calls (here by a synthetic sublayer)
+    block end attnres_block_accumulate  b_n = partial + v_S
+    final     attnres_full        b_0..b_N with the final query (no PreNorm)
+
+Buffers live in HBM for the whole pass: the block representations
+``reps [1 + n_given + N, T, d]`` (slot 0 is the embedding b_0), the phase-1
+outputs ``o1 [S_max, T, d]`` with their ``lse/m [S_max, T]`` (fp32), the
+running intra-block partial sum ``partial [T, d]`` in fp32, and a small ring of
+PreNorm outputs ``x``.  The partial sum is kept in fp32 because a bf16 running
+sum over a 24-sublayer block drifts by several percent of the row maximum;
+block sums are rounded once, when they are complete.
+
+``plan()`` lists every launch of a pass with its algorithmic bytes (each row
+the method must read or write, counted once).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Dict, List, Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import (attnres_block_accumulate, attnres_full, attnres_phase1, attnres_phase2_merge)
+
+SiteHook = Callable[..., None]
+Sublayer = Callable[[int, torch.Tensor], torch.Tensor]
+
+
+@dataclasses.dataclass
+class Launch:
+    kind: str       # "phase1", "phase2", "accumulate", "final", "full"
+    bytes: int      # algorithmic bytes moved by this launch
+
+
+def _esize(dt: torch.dtype) -> int:
+    return 4 if dt == torch.float32 else 2
+
+
+class BlockAttnRes:
+    """Block AttnRes forward over T tokens of width d on the current GPU.
+
+    ``block_sizes``: sublayers per block computed in this pass.
+    ``n_given``: completed block sums supplied as inputs (a decode-shaped step
+    starts at block n_given + 1).  ``x_ring``: number of PreNorm output
+    buffers cycled through (a real model consumes x_l immediately).
+    """
+
+    def __init__(self, T: int, d: int, block_sizes: Sequence[int], dtype: torch.dtype, n_given: int = 0,
+                 eps: float = 1e-6, device=None, x_ring: int = 4, keep_h: bool = False,
+                 final_site: bool = True):
+        self.T, self.d, self.dtype = int(T), int(d), dtype
+        self.block_sizes = [int(s) for s in block_sizes]
+        self.n_given, self.eps = int(n_given), float(eps)
+        self.L = sum(self.block_sizes)
+        self.final_site = final_site
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.device = dev
+        n_reps = 1 + self.n_given + len(self.block_sizes)
+        if n_reps > _lib.ATTNRES_MAX_SOURCES:
+            raise ValueError("too many sources for one aggregation site: %d" % n_reps)
+        if any(s > 1 for s in self.block_sizes) and 1 + self.n_given + len(self.block_sizes) - 1 > \
+                _lib.ATTNRES_MAX_SOURCES_MULTI:
+            raise ValueError("phase 1 with S >= 2 supports at most %d completed sources"
+                             % _lib.ATTNRES_MAX_SOURCES_MULTI)
+        smax = max(self.block_sizes) if self.block_sizes else 1
+        self.reps = torch.empty((n_reps, T, d), dtype=dtype, device=dev)
+        self.o1 = torch.empty((smax, T, d), dtype=dtype, device=dev)
+        self.m1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
+        self.lse1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
+        self.partial = torch.empty((T, d), dtype=torch.float32, device=dev)
+        self.x = torch.empty((max(1, x_ring), T, d), dtype=dtype, device=dev)
+        self.h = torch.empty((T, d), dtype=dtype, device=dev) if keep_h else None
+        self.h_final = torch.empty((T, d), dtype=dtype, device=dev)
+        self.lse_final = torch.empty((T,), dtype=torch.float32, device=dev)
+
+    # ------------------------------------------------------------------ bytes
+    def _row(self, dt=None) -> int:
+        return self.T * self.d * _esize(self.dtype if dt is None else dt)
+
+    def plan(self) -> List[Launch]:
+        """Algorithmic bytes of every launch of one pass, in launch order."""
+        r, r32 = self._row(), self._row(torch.float32)
+        stat = self.T * 4
+        out: List[Launch] = []
+        n_done = 1 + self.n_given
+        for S in self.block_sizes:
+            out.append(Launch("phase1", n_done * r + S * (r + 2 * stat)))
+            for j in range(S):
+                if j == 0:
+                    b = 2 * r + stat
+                elif j == 1:
+                    b = 3 * r + stat
+                elif j == 2:
+                    b = 4 * r + r32 + stat
+                else:
+                    b = 3 * r + 2 * r32 + stat
+                out.append(Launch("phase2", b))
+            if S == 1:
+                out.append(Launch("accumulate", 2 * r))
+            elif S == 2:
+                out.append(Launch("accumulate", 3 * r))
+            else:
+                out.append(Launch("accumulate", 2 * r + r32))
+            n_done += 1
+        if self.final_site:
+            out.append(Launch("final", (n_done + 1) * r + stat))
+        return out
+
+    # ---------------------------------------------------------------- forward
+    def forward(self, params: Dict[str, torch.Tensor], sublayer: Sublayer,
+                hook: Optional[SiteHook] = None, stream=None,
+                instrument: Optional[Callable[[str, bool], None]] = None) -> torch.Tensor:
+        """One pass over the whole depth.  ``self.reps[0]`` must hold b_0 and
+        ``self.reps[1:1+n_given]`` the supplied block sums.  ``params`` holds
+        fp32 ``w``, ``g`` [L+1, d] and ``gamma`` [L, d] (``g``/``gamma`` may be
+        None for unit gains).  ``sublayer(l, x_l)`` returns the output v_l of
+        sublayer l (0-based), a [T, d] tensor that stays valid for the rest of
+        the block.  ``hook(site, x=, h=, o1=, lse1=, m1=)`` is called after
+        each phase-2 launch.  ``instrument(kind, begin)`` is called just
+        before (begin=True) and after (begin=False) every launch."""
+        w, g, gam = params["w"], params.get("g"), params.get("gamma")
+        eps = self.eps
+        n_done = 1 + self.n_given
+        mark = instrument if instrument is not None else (lambda kind, begin: None)
+        l0 = 0
+        nx = self.x.shape[0]
+        for S in self.block_sizes:
+            mark("phase1", True)
+            attnres_phase1(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S], eps,
+                           self.o1[:S], self.m1[:S], self.lse1[:S], stream=stream)
+            mark("phase1", False)
+            # outputs of the block kept alive: the first two (for the first
+            # fp32 partial sum) and the previous one
+            first = second = prev = None
+            for j in range(S):
+                site = l0 + j
+                x = self.x[site % nx]
+                kg = None if g is None else g[site]
+                pg = None if gam is None else gam[site]
+                if j == 0:
+                    pin, pout = None, None
+                elif j == 1:
+                    pin, pout = None, None
+                elif j == 2:
+                    pin, pout = first, self.partial
+                else:
+                    pin, pout = self.partial, self.partial
+                mark("phase2", True)
+                attnres_phase2_merge(self.o1[j], self.lse1[j], pin, prev, pout, w[site], kg, pg, eps,
+                                     self.h, x, stream=stream)
+                mark("phase2", False)
+                if hook is not None:
+                    hook(site, x=x, h=self.h, o1=self.o1[j], lse1=self.lse1[j], m1=self.m1[j])
+                prev = sublayer(site, x)
+                if j == 0:
+                    first = prev
+                elif j == 1:
+                    second = prev
+                if j >= 2:
+                    first = second = None
+            mark("accumulate", True)
+            if S == 1:
+                attnres_block_accumulate(None, prev, self.reps[n_done], stream=stream)
+            elif S == 2:
+                attnres_block_accumulate(first, prev, self.reps[n_done], stream=stream)
+            else:
+                attnres_block_accumulate(self.partial, prev, self.reps[n_done], stream=stream)
+            mark("accumulate", False)
+            n_done += 1
+            l0 += S
+        if self.final_site:
+            mark("final", True)
+            attnres_full(self.reps, n_done, w[self.L], None if g is None else g[self.L], None, eps,
+                         self.h_final, None, self.lse_final, stream=stream)
+            mark("final", False)
+        return self.h_final
+
+
+class FullAttnRes:
+    """Full AttnRes (every sublayer output its own source), one-shot per site:
+    sublayer l aggregates hist[0..l-1] with attnres_full and PreNorm."""
+
+    def __init__(self, T: int, d: int, L: int, dtype: torch.dtype, eps: float = 1e-6, device=None,
+                 keep_h: bool = False, final_site: bool = True):
+        self.T, self.d, self.L, self.dtype, self.eps = int(T), int(d), int(L), dtype, float(eps)
+        if L + 1 > _lib.ATTNRES_MAX_SOURCES:
+            raise ValueError("Full AttnRes supports at most %d sources" % _lib.ATTNRES_MAX_SOURCES)
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.final_site = final_site
+        self.hist = torch.empty((L + 1, T, d), dtype=dtype, device=dev)  # v_0 = embedding, v_1..v_L
+        self.x = torch.empty((2, T, d), dtype=dtype, device=dev)
+        self.h = torch.empty((T, d), dtype=dtype, device=dev) if keep_h else None
+        self.lse = torch.empty((T,), dtype=torch.float32, device=dev)
+        self.h_final = torch.empty((T, d), dtype=dtype, device=dev)
+
+    def plan(self) -> List[Launch]:
+        r = self.T * self.d * _esize(self.dtype)
+        out = [Launch("full", (l + 1) * r + r + self.T * 4) for l in range(1, self.L + 1)]
+        if self.final_site:
+            out.append(Launch("final", (self.L + 2) * r + self.T * 4))
+        return out
+
+    def forward(self, params: Dict[str, torch.Tensor], sublayer: Callable[[int, torch.Tensor], None],
+                hook: Optional[SiteHook] = None, stream=None) -> torch.Tensor:
+        """``hist[0]`` must hold the embedding; ``sublayer(l, x_l)`` writes the
+        output of sublayer l (0-based) into ``hist[l + 1]``."""
+        w, g, gam = params["w"], params.get("g"), params.get("gamma")
+        for l in range(self.L):
+            x = self.x[l % 2]
+            attnres_full(self.hist, l + 1, w[l], None if g is None else g[l], None if gam is None else gam[l],
+                         self.eps, self.h, x, self.lse, stream=stream)
+            if hook is not None:
+                hook(l, x=x, h=self.h, lse=self.lse)
+            sublayer(l, x)
+        if self.final_site:
+            attnres_full(self.hist, self.L + 1, w[self.L], None if g is None else g[self.L], None, self.eps,
+                         self.h_final, None, None, stream=stream)
+        return self.h_final
+
+
+def prefill_chunked(T_total: int, chunk: int, d: int, block_sizes: Sequence[int], dtype: torch.dtype,
+                    params: Dict[str, torch.Tensor], fill_embedding: Callable[[int, int, torch.Tensor], None],
+                    sublayer_for_chunk: Callable[[int, int], Sublayer],
+                    on_chunk: Optional[Callable[[int, int, BlockAttnRes], None]] = None,
+                    eps: float = 1e-6, hook_for_chunk=None) -> BlockAttnRes:
+    """Long-context prefill on one GPU, streamed in chunks of ``chunk`` tokens
+    ("Attention Residuals 阅读补充", Block AttnRes memory section; the notes'
+    section 10 on sequence sharding and chunked prefill).  Depth attention
+    never mixes tokens, so each chunk is an independent pass; the per-chunk
+    buffers (block representations, phase-1 outputs, partial sum) are
+    allocated once and reused, which bounds the resident block cache by the
+    chunk length instead of the context length."""
+    st = BlockAttnRes(min(chunk, T_total), d, block_sizes, dtype, eps=eps)
+    for c0 in range(0, T_total, chunk):
+        c1 = min(T_total, c0 + chunk)
+        if c1 - c0 != st.T:  # ragged last chunk
+            st = BlockAttnRes(c1 - c0, d, block_sizes, dtype, eps=eps)
+        fill_embedding(c0, c1, st.reps[0])
+        hook = hook_for_chunk(c0, c1) if hook_for_chunk is not None else None
+        st.forward(params, sublayer_for_chunk(c0, c1), hook=hook)
+        if on_chunk is not None:
+            on_chunk(c0, c1, st)
+    return st
