@@ -28,37 +28,37 @@ METRIC = "AttnRes token-sublayers/s + achieved HBM GB/s (% of MI355X peak)"
 
 
 def cpu_baseline(w, emb, v, prm, target_s: float):
-    """Time the fp64 oracle on a bounded, evenly spaced token sample."""
-    import numpy as np
+    """Time the fp64 oracle, as it stands, on a bounded token sample: batches
+    of evenly spaced tokens (full depth each) until about ``target_s``
+    seconds of oracle time have run."""
     import torch
     import oracle
     import synth
 
     oracle.build(force=False)
-
-    def run(tokens):
+    w_h, g_h, gm_h = oracle._f32(prm["w"]), oracle._f32(prm["g"]), oracle._f32(prm["gamma"])
+    order = synth.sample_tokens(w.T, w.T)  # every token, visited in a strided order below
+    batch = 256
+    stride = max(1, w.T // batch)
+    done, spent, start = 0, 0.0, 0
+    while spent < target_s and start < stride:
+        tokens = order[start::stride][:batch]
+        start += 1
         idx = torch.tensor(tokens, dtype=torch.long, device=emb.device)
-        e = emb.index_select(0, idx)
-        vv = torch.stack([t.index_select(0, idx) for t in v])
-        e_h, v_h = oracle._f32(e), oracle._f32(vv)
-        w_h, g_h, gm_h = oracle._f32(prm["w"]), oracle._f32(prm["g"]), oracle._f32(prm["gamma"])
+        e_h = oracle._f32(emb.index_select(0, idx))
+        v_h = oracle._f32(torch.stack([t.index_select(0, idx) for t in v]))
         t0 = time.perf_counter()
         oracle.block_forward(e_h, v_h, w_h, g_h, gm_h, w.block_sizes, w.eps, final_site=w.final_site,
                              want=("hfinal",))
-        return time.perf_counter() - t0
-
-    probe = synth.sample_tokens(w.T, 16)
-    dt = run(probe)
-    n = int(max(16, min(512, round(len(probe) * target_s / max(dt, 1e-3)))))
-    tokens = synth.sample_tokens(w.T, n)
-    dt = run(tokens)
+        spent += time.perf_counter() - t0
+        done += len(tokens)
     return {
-        "value": len(tokens) * w.L / dt,
+        "value": round(done * w.L / spent, 1),
         "unit": "token-sublayers/s",
         "cores": oracle.threads(),
         "kind": "oracle",
-        "sample": "%d evenly spaced tokens of the %d-token chunk, all %d sublayers + final site, fp64, "
-                  "%.1f s wall" % (len(tokens), w.T, w.L, dt),
+        "sample": "%d tokens (batches of %d evenly spaced tokens) of the %d-token chunk, all %d sublayers "
+                  "+ final site, fp64, %.1f s of oracle time" % (done, batch, w.T, w.L, spent),
     }
 
 

@@ -41,7 +41,9 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Calls
  *    are asynchronous; argument errors are reported synchronously before any
  *    launch; a failed launch reports ATTNRES_EHIP.
- *  - T == 0 is valid and launches nothing.
+ *  - T == 0 is valid and launches nothing; it returns ATTNRES_OK once the
+ *    scalar arguments (dtype, d, counts, eps) are valid, whatever the
+ *    pointers are (empty tensors may have null data pointers).
  *  - Kernels use no atomics: results are bitwise reproducible run to run and
  *    independent of how tokens are split over calls.
  */
@@ -81,14 +83,25 @@ typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1 } attnres_dtype_t;
  *   out: [S][T][d] dtype dt.  m_out, lse_out: [S][T] fp32 (m_out may be NULL).
  * Limits: 1 <= n_src <= ATTNRES_MAX_SOURCES_MULTI when S >= 2, <=
  * ATTNRES_MAX_SOURCES when S == 1; S >= 1 (queries are processed 32 at a
- * time; each group of 32 reads the sources once).
- * out must not overlap src; m_out/lse_out must not overlap anything.
+ * time; each group of 32 reads the sources once for the scores and once for
+ * the outputs).
+ * workspace: caller-owned device memory of at least
+ * attnres_phase1_workspace_bytes(T, n_src, S) bytes, 16-byte aligned, used
+ * for the softmax weights between the scoring and output kernels (its
+ * contents afterwards are unspecified); NULL allowed when that size is 0.
+ * out must not overlap src; m_out, lse_out and workspace must not overlap
+ * anything.
  */
 attnres_status_t attnres_phase1(attnres_dtype_t dt,
                                 const void* src, int64_t n_src, int64_t src_stride,
                                 int64_t T, int64_t d,
                                 const float* w, const float* key_gain, int64_t S, float eps,
-                                void* out, float* m_out, float* lse_out, void* stream);
+                                void* out, float* m_out, float* lse_out,
+                                void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes attnres_phase1 needs: T * n_src * min(S, 32) * 4 when
+ * S >= 2, 0 when S == 1; -1 for invalid sizes. */
+int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t n_src, int64_t S);
 
 /*
  * Phase 2 for one sublayer j of a block ("Attention Residuals" notes,

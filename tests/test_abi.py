@@ -53,8 +53,11 @@ def p(x):
 
 
 def phase1(lib, dt=1, src=A, n=3, stride=4096 * 64, T=4096, d=64, w=8 * A, kg=None, S=4, eps=1e-6,
-           out=16 * A, m=None, lse=24 * A):
-    return lib.attnres_phase1(dt, p(src), n, stride, T, d, p(w), p(kg), S, eps, p(out), p(m), p(lse), None)
+           out=16 * A, m=None, lse=24 * A, ws=32 * A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attnres_phase1_workspace_bytes(T, n, S)
+    return lib.attnres_phase1(dt, p(src), n, stride, T, d, p(w), p(kg), S, eps, p(out), p(m), p(lse), p(ws),
+                              ws_bytes, None)
 
 
 def test_phase1_validation(lib):
@@ -75,7 +78,14 @@ def test_phase1_validation(lib):
     assert phase1(lib, lse=16 * A + 8) == EALIAS      # stats inside the output
     assert phase1(lib, lse=24 * A + 2) == EALIGN
     assert phase1(lib, eps=-1.0) == EINVAL
+    assert phase1(lib, ws=None) == EINVAL                # S >= 2 needs the workspace
+    assert phase1(lib, ws_bytes=100) == EINVAL           # too small
+    assert phase1(lib, ws=16 * A + 64) == EALIAS         # workspace inside the output
+    assert lib.attnres_phase1_workspace_bytes(4096, 3, 4) == 4096 * 3 * 4 * 4
+    assert lib.attnres_phase1_workspace_bytes(4096, 3, 40) == 4096 * 3 * 32 * 4
+    assert lib.attnres_phase1_workspace_bytes(4096, 3, 1) == 0
     assert phase1(lib, T=0) == 0                      # nothing to do, nothing launched
+    assert phase1(lib, T=0, src=None, out=None, lse=None) == 0
 
 
 def merge(lib, dt=1, T=1024, d=64, o=A, lse=2 * A, pdt=0, pin=None, v=None, pout=None, w=3 * A, kg=None,
@@ -93,8 +103,8 @@ def test_merge_validation(lib):
     assert merge(lib, x=A + 64) == EALIAS                  # output over the phase-1 input
     assert merge(lib, v=6 * A, pin=5 * A, pout=5 * A + 16) == EALIAS   # shifted in-place
     assert merge(lib, v=6 * A, pin=5 * A, pout=5 * A, pdt=1) == EALIAS  # in place needs fp32
-    assert merge(lib, T=0, v=6 * A, pin=5 * A, pout=5 * A) == 0         # exact in-place fp32 is allowed
     assert merge(lib, T=0) == 0
+    assert merge(lib, T=0, o=None, lse=None, x=None) == 0               # empty: pointers unused
 
 
 def test_full_and_accumulate_validation(lib):
@@ -112,7 +122,7 @@ def test_full_and_accumulate_validation(lib):
     assert acc(v=None) == EINVAL
     assert acc(out=A) == EALIAS
     assert acc(pin=2 * A, pdt=0) == EALIAS          # in place only with the same dtype
-    assert acc(pin=2 * A, pdt=1, T=0) == 0
+    assert acc(T=0, v=None, out=None) == 0
     assert acc(dt=3) == EDTYPE
 
 

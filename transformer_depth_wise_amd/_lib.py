@@ -21,7 +21,7 @@ ATTNRES_MAX_D = 16384
 ATTNRES_MAX_SOURCES = 32
 ATTNRES_MAX_SOURCES_MULTI = 16
 
-EXPORTED = ("attnres_phase1", "attnres_phase2_merge", "attnres_full",
+EXPORTED = ("attnres_phase1", "attnres_phase1_workspace_bytes", "attnres_phase2_merge", "attnres_full",
             "attnres_block_accumulate", "attnres_status_string")
 
 
@@ -45,7 +45,9 @@ def load(path: Optional[str] = None):
                            "`python -m transformer_depth_wise_amd.build`" % p)
     lib = ctypes.CDLL(p)
     V, I, F, E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
-    lib.attnres_phase1.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V]
+    lib.attnres_phase1.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V, I, V]
+    lib.attnres_phase1_workspace_bytes.argtypes = [I, I, I]
+    lib.attnres_phase1_workspace_bytes.restype = ctypes.c_int64
     lib.attnres_phase2_merge.argtypes = [E, I, I, V, V, E, V, V, V, V, V, V, F, V, V, V]
     lib.attnres_full.argtypes = [E, V, I, I, I, I, V, V, V, F, V, V, V, V]
     lib.attnres_block_accumulate.argtypes = [E, I, I, E, V, V, V, V]
@@ -87,15 +89,22 @@ def _check(fn: str, rc: int):
         raise AttnResError(fn, rc, status_string(rc))
 
 
+def attnres_phase1_workspace_bytes(T: int, n_src: int, S: int) -> int:
+    return int(load().attnres_phase1_workspace_bytes(T, n_src, S))
+
+
 def attnres_phase1(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],
                    eps: float, out: torch.Tensor, m_out: Optional[torch.Tensor], lse_out: torch.Tensor,
-                   stream=None) -> None:
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """src: [>=n_src, T, d] slabs (sources 0..n_src-1 at stride src.stride(0));
-    w, key_gain: [S, d] fp32; out: [S, T, d]; m_out, lse_out: [S, T] fp32."""
+    w, key_gain: [S, d] fp32; out: [S, T, d]; m_out, lse_out: [S, T] fp32;
+    workspace: device tensor of at least attnres_phase1_workspace_bytes bytes."""
     S, T, d = out.shape
     stride = src.stride(0) if src.dim() == 3 else T * d
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load().attnres_phase1(dtype_code(src.dtype), _ptr(src), n_src, stride, T, d, _ptr(w), _ptr(key_gain),
-                               S, eps, _ptr(out), _ptr(m_out), _ptr(lse_out), _stream(stream))
+                               S, eps, _ptr(out), _ptr(m_out), _ptr(lse_out), _ptr(workspace), ws_bytes,
+                               _stream(stream))
     _check("attnres_phase1", rc)
 
 

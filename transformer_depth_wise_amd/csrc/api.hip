@@ -80,19 +80,29 @@ const char* attnres_status_string(attnres_status_t status) {
   return "ATTNRES_UNKNOWN_STATUS";
 }
 
+int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t n_src, int64_t S) {
+  if (T < 0 || n_src < 1 || S < 1) return -1;
+  if (S == 1) return 0;
+  return T * n_src * (S < 32 ? S : 32) * (int64_t)sizeof(float);
+}
+
 attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
                                 int64_t T, int64_t d, const float* w, const float* key_gain, int64_t S,
-                                float eps, void* out, float* m_out, float* lse_out, void* stream) {
+                                float eps, void* out, float* m_out, float* lse_out, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
   if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
   if (T < 0 || S < 1 || n_src < 1) return ATTNRES_EINVAL;
   if (n_src > (S == 1 ? ATTNRES_MAX_SOURCES : ATTNRES_MAX_SOURCES_MULTI)) return ATTNRES_EINVAL;
   if (T > (int64_t)1 << 40 || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!src || !w || !out || !lse_out) return ATTNRES_EINVAL;
   if (n_src > 1 && (src_stride < T * d)) return ATTNRES_EINVAL;
   if (src_stride % 8 != 0) return ATTNRES_EALIGN;
-  st = check_align({src, w, key_gain, out}, {m_out, lse_out});
+  const int64_t ws_need = attnres_phase1_workspace_bytes(T, n_src, S);
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return ATTNRES_EINVAL;
+  st = check_align({src, w, key_gain, out, ws_need > 0 ? workspace : nullptr}, {m_out, lse_out});
   if (st != ATTNRES_OK) return st;
   const int64_t es = esize(dt);
   const Range rs = range_of(src, ((n_src - 1) * src_stride + T * d) * es);
@@ -101,11 +111,12 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_s
   const Range rm = m_out ? range_of(m_out, S * T * 4) : Range{0, 0};
   const Range rw = range_of(w, S * d * 4);
   const Range rg = key_gain ? range_of(key_gain, S * d * 4) : Range{0, 0};
-  for (Range o : {ro, rl, rm})
+  const Range rws = ws_need > 0 ? range_of(workspace, ws_need) : Range{0, 0};
+  for (Range o : {ro, rl, rm, rws})
     for (Range i : {rs, rw, rg})
       if (overlaps(o, i)) return ATTNRES_EALIAS;
   if (overlaps(ro, rl) || overlaps(ro, rm) || overlaps(rl, rm)) return ATTNRES_EALIAS;
-  if (T == 0) return ATTNRES_OK;
+  if (overlaps(rws, ro) || overlaps(rws, rl) || overlaps(rws, rm)) return ATTNRES_EALIAS;
 
   const Dtype kdt = dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -117,7 +128,8 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_s
     char* o = static_cast<char*>(out) + s0 * T * d * es;
     hipError_t e = attnres::launch_phase1_multi(kdt, src, (int)n_src, src_stride, T, (int)d, w + s0 * d,
                                                 key_gain ? key_gain + s0 * d : nullptr, (int)sn, eps, o,
-                                                m_out ? m_out + s0 * T : nullptr, lse_out + s0 * T, s);
+                                                m_out ? m_out + s0 * T : nullptr, lse_out + s0 * T,
+                                                static_cast<float*>(workspace), s);
     if (e != hipSuccess) return ATTNRES_EHIP;
   }
   return ATTNRES_OK;
@@ -132,8 +144,9 @@ attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, 
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
   if (T < 0 || !(eps >= 0.f)) return ATTNRES_EINVAL;
-  if (!p1_out || !p1_lse || (!h_out && !x_out)) return ATTNRES_EINVAL;
   if (!sublayer_prev && (partial_in || partial_out)) return ATTNRES_EINVAL;
+  if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
+  if (!p1_out || !p1_lse || (!h_out && !x_out)) return ATTNRES_EINVAL;
   if (sublayer_prev && !w) return ATTNRES_EINVAL;
   st = check_align({p1_out, partial_in, sublayer_prev, partial_out, w, key_gain, prenorm_gain, h_out, x_out}, {p1_lse});
   if (st != ATTNRES_OK) return st;
@@ -156,7 +169,6 @@ attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, 
       if (overlaps(o, i)) return ATTNRES_EALIAS;
     }
   if (overlaps(r_h, r_x) || overlaps(r_h, r_po) || overlaps(r_x, r_po)) return ATTNRES_EALIAS;
-  if (T == 0) return ATTNRES_OK;
   const Dtype kdt = dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
   const Dtype kpdt = partial_dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
   return hip_status(attnres::launch_merge(kdt, T, (int)d, p1_out, p1_lse, kpdt, partial_in, sublayer_prev,
@@ -171,6 +183,7 @@ attnres_status_t attnres_full(attnres_dtype_t dt, const void* src, int64_t n_src
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
   if (T < 0 || n_src < 1 || n_src > ATTNRES_MAX_SOURCES || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!src || !w || (!h_out && !x_out)) return ATTNRES_EINVAL;
   if (n_src > 1 && src_stride < T * d) return ATTNRES_EINVAL;
   if (src_stride % 8 != 0) return ATTNRES_EALIGN;
@@ -188,7 +201,6 @@ attnres_status_t attnres_full(attnres_dtype_t dt, const void* src, int64_t n_src
     for (Range i : {rs, rw, rg, rgm})
       if (overlaps(o, i)) return ATTNRES_EALIAS;
   if (overlaps(rh, rx) || overlaps(rh, rl) || overlaps(rx, rl)) return ATTNRES_EALIAS;
-  if (T == 0) return ATTNRES_OK;
   const Dtype kdt = dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
   return hip_status(attnres::launch_phase1_single(kdt, src, (int)n_src, src_stride, T, (int)d, w, key_gain,
                                                   prenorm_gain, eps, h_out, x_out, nullptr, lse_out,
@@ -200,7 +212,9 @@ attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t
   if (!dtype_ok(dt) || !dtype_ok(partial_dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
-  if (T < 0 || !v || !out) return ATTNRES_EINVAL;
+  if (T < 0) return ATTNRES_EINVAL;
+  if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
+  if (!v || !out) return ATTNRES_EINVAL;
   st = check_align({partial_in, v, out});
   if (st != ATTNRES_OK) return st;
   const int64_t rows = T * d;
@@ -210,7 +224,6 @@ attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t
   if (overlaps(ro, rv)) return ATTNRES_EALIAS;
   const bool in_place = partial_in == out && partial_dt == dt;
   if (!in_place && overlaps(ro, rp)) return ATTNRES_EALIAS;
-  if (T == 0) return ATTNRES_OK;
   const Dtype kdt = dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
   const Dtype kpdt = partial_dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
   return hip_status(attnres::launch_accumulate(kdt, T, (int)d, kpdt, partial_in, v, out,

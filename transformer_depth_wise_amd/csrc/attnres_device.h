@@ -71,6 +71,39 @@ __device__ __forceinline__ void zero8(float (&v)[8]) {
   for (int e = 0; e < 8; ++e) v[e] = 0.f;
 }
 
+// ---- raw 16-byte chunks held in registers between load and use ------------
+// Chunk<T> keeps 8 elements in their storage format so that loads for the
+// next token or row chunk can be in flight while the current one is used.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+template <typename T> struct Chunk;
+template <> struct Chunk<bf16_t> {
+  u32x4_t r;
+  __device__ __forceinline__ void load(const bf16_t* p) { r = ld16(p); }
+  __device__ __forceinline__ void zero() { r = u32x4_t{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ void unpack(float (&v)[8]) const {
+    unpack_bf16x8(make_uint4(r.x, r.y, r.z, r.w), v);
+  }
+};
+template <> struct Chunk<float> {
+  u32x4_t a, b;
+  __device__ __forceinline__ void load(const float* p) { a = ld16(p); b = ld16(p + 4); }
+  __device__ __forceinline__ void zero() { a = u32x4_t{0u, 0u, 0u, 0u}; b = a; }
+  __device__ __forceinline__ void unpack(float (&v)[8]) const {
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  }
+};
+__device__ __forceinline__ void out8(float* p, const float (&v)[8]) {
+  st16(p, u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+  st16(p + 4, u32x4_t{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
+}
+__device__ __forceinline__ void out8(bf16_t* p, const float (&v)[8]) {
+  st16(p, u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
+}
+
 // ---- reductions ------------------------------------------------------------
 
 __device__ __forceinline__ float wave_sum(float x) {

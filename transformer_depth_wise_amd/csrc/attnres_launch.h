@@ -10,11 +10,12 @@ enum Dtype { kF32 = 0, kBF16 = 1 };
 
 int device_cu_count();
 
-// Phase 1 of a block, one tile of at most 32 queries (S >= 2, n <= 16), or
-// S == 1 with optional PreNorm (n <= 32).  Returns a hipError_t.
+// Phase 1 of a block, one tile of at most 32 queries (S >= 2, n <= 16);
+// `alpha` is workspace for T * S * n fp32 softmax weights.  Or S == 1 with
+// optional PreNorm (n <= 32).  Return a hipError_t.
 hipError_t launch_phase1_multi(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
                                const float* w, const float* kg, int S, float eps, void* out,
-                               float* m_out, float* lse_out, hipStream_t stream);
+                               float* m_out, float* lse_out, float* alpha, hipStream_t stream);
 
 hipError_t launch_phase1_single(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
                                 const float* w, const float* kg, const float* gamma, float eps,

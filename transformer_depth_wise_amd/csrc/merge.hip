@@ -15,12 +15,108 @@
 // the whole 256-thread workgroup above that).  A thread owns CPL chunks of 8
 // channels; the row's two reductions (|p|^2 with w.p, then |h|^2) use wave
 // shuffles and, for 256-thread teams, one LDS exchange each.  The per-channel
-// parameters (w (.) g and gamma) stay in registers while the workgroup walks
-// over tokens with a grid stride.
+// parameters (w (.) g and gamma) stay in registers while a persistent grid of
+// two workgroups per CU walks over the tokens; the raw rows of the team's next
+// token are loaded before the current token is reduced, merged and stored, so
+// HBM traffic continues through the reductions and barriers (the loop is
+// unrolled twice over two register stages).
 #include "attnres_device.h"
 #include "attnres_launch.h"
 
 namespace attnres {
+
+
+template <typename St, typename Pt, int CPL>
+struct Stage {
+  Chunk<St> o[CPL], v[CPL];
+  Chunk<Pt> q[CPL];
+};
+
+template <typename St, typename Pt, int TEAM, int CPL>
+__device__ __forceinline__ void issue(Stage<St, Pt, CPL>& s, int64_t tok, int64_t T, int d, int C, int tl,
+                                      const St* o1, const Pt* pin, const St* vprev) {
+  const bool live = tok < T;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const int c = tl + TEAM * k;
+    if (live && c < C) {
+      const int64_t off = tok * d + c * 8;
+      s.o[k].load(o1 + off);
+      if (vprev) {
+        s.v[k].load(vprev + off);
+        if (pin) s.q[k].load(pin + off); else s.q[k].zero();
+      } else { s.v[k].zero(); s.q[k].zero(); }
+    } else {
+      s.o[k].zero(); s.v[k].zero(); s.q[k].zero();
+    }
+  }
+}
+
+template <typename St, typename Pt, int TEAM, int CPL>
+__device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok, int64_t T, int d, int C, int tl,
+                                        const float* lse1, const St* vprev, float* pout,
+                                        const float (&wq)[CPL][8], const float (&gm)[CPL][8], float eps, float inv_d,
+                                        St* h_out, St* x_out, float (*red)[8], int& parity) {
+  const bool live = tok < T;
+  float h[CPL][8], p[CPL][8];
+  float ss = 0.f, dot = 0.f;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    s.o[k].unpack(h[k]);
+    if (vprev) {
+      float q[8];
+      s.v[k].unpack(p[k]);
+      s.q[k].unpack(q);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[k][e] = q[e] + p[k][e];
+      const int c = tl + TEAM * k;
+      if (pout && live && c < C) out8(pout + tok * d + c * 8, p[k]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { ss = fmaf(p[k][e], p[k][e], ss); dot = fmaf(wq[k][e], p[k][e], dot); }
+    } else {
+      zero8(p[k]);
+    }
+  }
+  if (vprev) {
+    float2 r;
+    if (TEAM == 256) { r = block_sum2_256(ss, dot, red[parity]); parity ^= 1; }
+    else { r.x = wave_sum(ss); r.y = wave_sum(dot); }
+    const float zc = r.y / sqrtf(r.x * inv_d + eps);
+    const float lse = live ? lse1[tok] : 0.f;
+    const float beta = 1.0f / (1.0f + expf(lse - zc));
+#pragma unroll
+    for (int k = 0; k < CPL; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[k][e] = fmaf(beta, p[k][e] - h[k][e], h[k][e]);
+  }
+  float sh = 0.f;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sh = fmaf(h[k][e], h[k][e], sh);
+  float r2 = 0.f;
+  if (x_out) {
+    if (TEAM == 256) { r2 = block_sum2_256(sh, 0.f, red[parity]).x; parity ^= 1; }
+    else r2 = wave_sum(sh);
+  }
+  if (live) {
+    const float rinv = x_out ? 1.0f / sqrtf(r2 * inv_d + eps) : 1.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int c = tl + TEAM * k;
+      if (c < C) {
+        const int64_t off = tok * d + c * 8;
+        if (h_out) out8(h_out + off, h[k]);
+        if (x_out) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = gm[k][e] * (h[k][e] * rinv);
+          out8(x_out + off, x);
+        }
+      }
+    }
+  }
+}
 
 template <typename St, typename Pt, int TEAM, int CPL>
 __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __restrict__ o1,
@@ -29,13 +125,12 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
                                                const float* __restrict__ w, const float* __restrict__ kg,
                                                const float* __restrict__ gamma, float eps,
                                                St* __restrict__ h_out, St* __restrict__ x_out) {
-  constexpr int TPW = 256 / TEAM;  // tokens in flight per workgroup
+  constexpr int TPW = 256 / TEAM;
   __shared__ float red[2][8];
   const int team = threadIdx.x / TEAM;
   const int tl = threadIdx.x % TEAM;
   const int C = d >> 3;
   const float inv_d = 1.0f / (float)d;
-
   float wq[CPL][8], gm[CPL][8];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
@@ -43,106 +138,30 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
     if (c < C) {
       if (vprev) {
         load8(w + c * 8, wq[k]);
-        if (kg) {
-          float g[8];
-          load8(kg + c * 8, g);
+        if (kg) { float g[8]; load8(kg + c * 8, g);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) wq[k][e] *= g[e];
-        }
-      } else {
-        zero8(wq[k]);
-      }
-      if (gamma) {
-        load8(gamma + c * 8, gm[k]);
-      } else {
+          for (int e = 0; e < 8; ++e) wq[k][e] *= g[e]; }
+      } else zero8(wq[k]);
+      if (gamma) load8(gamma + c * 8, gm[k]);
+      else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) gm[k][e] = 1.f;
       }
-    } else {
-      zero8(wq[k]);
-      zero8(gm[k]);
-    }
+    } else { zero8(wq[k]); zero8(gm[k]); }
   }
-
   int parity = 0;
   const int64_t step = (int64_t)gridDim.x * TPW;
-  for (int64_t tok = (int64_t)blockIdx.x * TPW + team; tok - team < T; tok += step) {
-    const bool live = tok < T;  // uniform per team; whole-workgroup teams are always live here
-    float h[CPL][8], p[CPL][8];
-    float ss = 0.f, dot = 0.f;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      const int c = tl + TEAM * k;
-      zero8(h[k]);
-      zero8(p[k]);
-      if (live && c < C) {
-        const int64_t off = tok * d + c * 8;
-        load8(o1 + off, h[k]);
-        if (vprev) {
-          load8(vprev + off, p[k]);
-          if (pin) {
-            float q[8];
-            load8(pin + off, q);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) p[k][e] = q[e] + p[k][e];
-          }
-          if (pout) store8(pout + off, p[k]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ss = fmaf(p[k][e], p[k][e], ss);
-            dot = fmaf(wq[k][e], p[k][e], dot);
-          }
-        }
-      }
-    }
-    if (vprev) {
-      float2 r;
-      if (TEAM == 256) {
-        r = block_sum2_256(ss, dot, red[parity]);
-        parity ^= 1;
-      } else {
-        r.x = wave_sum(ss);
-        r.y = wave_sum(dot);
-      }
-      const float zc = r.y / sqrtf(r.x * inv_d + eps);
-      const float lse = live ? lse1[tok] : 0.f;
-      const float beta = 1.0f / (1.0f + expf(lse - zc));
-#pragma unroll
-      for (int k = 0; k < CPL; ++k)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[k][e] = fmaf(beta, p[k][e] - h[k][e], h[k][e]);
-    }
-    float sh = 0.f;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sh = fmaf(h[k][e], h[k][e], sh);
-    float r2 = 0.f;
-    if (x_out) {
-      if (TEAM == 256) {
-        r2 = block_sum2_256(sh, 0.f, red[parity]).x;
-        parity ^= 1;
-      } else {
-        r2 = wave_sum(sh);
-      }
-    }
-    if (live) {
-      const float rinv = x_out ? 1.0f / sqrtf(r2 * inv_d + eps) : 1.f;
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        const int c = tl + TEAM * k;
-        if (c < C) {
-          const int64_t off = tok * d + c * 8;
-          if (h_out) store8(h_out + off, h[k]);
-          if (x_out) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = gm[k][e] * (h[k][e] * rinv);
-            store8(x_out + off, x);
-          }
-        }
-      }
-    }
+  int64_t tok = (int64_t)blockIdx.x * TPW + team;
+  Stage<St, Pt, CPL> A, B;
+  issue<St, Pt, TEAM, CPL>(A, tok, T, d, C, tl, o1, pin, vprev);
+  while (tok - team < T) {
+    issue<St, Pt, TEAM, CPL>(B, tok + step, T, d, C, tl, o1, pin, vprev);
+    process<St, Pt, TEAM, CPL>(A, tok, T, d, C, tl, lse1, vprev, pout, wq, gm, eps, inv_d, h_out, x_out, red, parity);
+    tok += step;
+    if (tok - team >= T) break;
+    issue<St, Pt, TEAM, CPL>(A, tok + step, T, d, C, tl, o1, pin, vprev);
+    process<St, Pt, TEAM, CPL>(B, tok, T, d, C, tl, lse1, vprev, pout, wq, gm, eps, inv_d, h_out, x_out, red, parity);
+    tok += step;
   }
 }
 
@@ -171,7 +190,7 @@ static hipError_t run_merge(int64_t T, int d, const void* o1, const float* lse1,
                             const float* gamma, float eps, void* h_out, void* x_out, hipStream_t stream) {
   constexpr int TPW = 256 / TEAM;
   const int64_t tiles = (T + TPW - 1) / TPW;
-  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int64_t cap = (int64_t)device_cu_count() * 2;  // persistent: 2 workgroups per CU
   const dim3 grid((unsigned)(tiles < cap ? tiles : cap));
   hipLaunchKernelGGL((k_merge<St, Pt, TEAM, CPL>), grid, dim3(256), 0, stream, T, d,
                      static_cast<const St*>(o1), lse1, static_cast<const Pt*>(pin),

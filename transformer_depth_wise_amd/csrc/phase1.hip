@@ -6,8 +6,9 @@
 // products into one Q K^T product, and each source row is read once per
 // block instead of once per sublayer).
 //
-// Work decomposition (one workgroup = 4 waves = a tile of 16 tokens):
-//  part A  scores.  Z[q][t][i] = sum_k (w_q g_q)[k] * u_i[t][k] is a dense
+// Work decomposition.  S >= 2 uses two kernels; S == 1 (Full AttnRes sites and
+// the final aggregation) uses one kernel that does both parts per tile.
+//  part A  scores (one workgroup = 4 waves = a tile of 16 tokens).  Z[q][t][i] = sum_k (w_q g_q)[k] * u_i[t][k] is a dense
 //          contraction over d, computed on the matrix cores with
 //          v_mfma_f32_16x16x32_bf16 (bf16 rows; the fp32 query is split into
 //          bf16 hi + lo parts, so the product keeps ~16 mantissa bits of the
@@ -18,9 +19,10 @@
 //          accumulated on the vector ALUs from the same registers.  The four
 //          waves' partial sums are added in a fixed order through LDS, then
 //          z = Z / r(u) and the softmax over sources is taken in LDS.
-//  part B  outputs.  out[s][t] = sum_i alpha[t][s][i] u_i[t]: the tile's
-//          source rows are streamed again (16-byte loads, a wave reads 1 KiB
-//          of one row) and each row chunk serves all S queries.
+//          For S >= 2 the softmax weights go to a caller-provided workspace.
+//  part B  outputs.  out[s][t] = sum_i alpha[t][s][i] u_i[t]: the source rows
+//          are streamed again (16-byte loads, a wave reads 1 KiB of one row)
+//          and each row chunk serves all S queries.
 #include "attnres_device.h"
 #include "attnres_launch.h"
 
@@ -218,13 +220,15 @@ struct Red {
 };
 
 // ---------------------------------------------------------------------------
-// S >= 2 (or any S <= 32 with n <= 16): all queries of a tile of 32.
+// S >= 2, first kernel: scores and softmax weights of a 16-token tile for up
+// to 32 queries.  The weights go to the workspace as alpha[t][q][i]
+// (i fastest), the statistics to m_out / lse_out.
 template <typename St, int MT, int NB>
-__global__ __launch_bounds__(256) void k_phase1_multi(const St* __restrict__ src, int n, int64_t stride,
-                                                      int64_t T, int d, const float* __restrict__ w,
-                                                      const float* __restrict__ kg, int S, float eps,
-                                                      St* __restrict__ out, float* __restrict__ m_out,
-                                                      float* __restrict__ lse_out) {
+__global__ __launch_bounds__(256) void k_p1_scores(const St* __restrict__ src, int n, int64_t stride,
+                                                   int64_t T, int d, const float* __restrict__ w,
+                                                   const float* __restrict__ kg, int S, float eps,
+                                                   float* __restrict__ alpha, float* __restrict__ m_out,
+                                                   float* __restrict__ lse_out) {
   constexpr int G = NB < 8 ? NB : 8;
   constexpr int QP = 16 * MT;
   constexpr int NP = NB < 4 ? 4 : NB;
@@ -265,60 +269,88 @@ __global__ __launch_bounds__(256) void k_phase1_multi(const St* __restrict__ src
 
   // softmax over the n sources of every (token, query) pair
   for (int pidx = threadIdx.x; pidx < 16 * QP; pidx += 256) {
-    float* row = zb + pidx * NP;
+    const int t = pidx / QP, q = pidx - t * QP;
+    const int64_t tok = tok0 + t;
+    if (q >= S || tok >= T) continue;
+    const float* row = zb + pidx * NP;
     float mx = row[0];
     for (int i = 1; i < n; ++i) mx = fmaxf(mx, row[i]);
     float l = 0.f;
-    for (int i = 0; i < n; ++i) {
-      const float e = expf(row[i] - mx);
-      row[i] = e;
-      l += e;
-    }
-    for (int i = 0; i < n; ++i) row[i] = row[i] / l;
-    for (int i = n; i < NP; ++i) row[i] = 0.f;
-    const int t = pidx / QP, q = pidx - t * QP;
-    const int64_t tok = tok0 + t;
-    if (q < S && tok < T) {
-      if (m_out) m_out[(int64_t)q * T + tok] = mx;
-      lse_out[(int64_t)q * T + tok] = mx + logf(l);
+    for (int i = 0; i < n; ++i) l += expf(row[i] - mx);
+    float* a = alpha + (tok * S + q) * n;
+    for (int i = 0; i < n; ++i) a[i] = expf(row[i] - mx) / l;
+    if (m_out) m_out[(int64_t)q * T + tok] = mx;
+    lse_out[(int64_t)q * T + tok] = mx + logf(l);
+  }
+}
+
+// S >= 2, second kernel: out[q][t] = sum_i alpha[t][q][i] u_i[t].  A wave owns
+// one (token, group of 64 chunks) item at a time, so the weights are
+// wave-uniform and come in through scalar loads; every source chunk is used
+// by all S queries; the next item's source chunks are loaded before the
+// current item is computed.
+template <typename St, int NB>
+__device__ __forceinline__ void p1_issue(Chunk<St> (&s)[NB], int64_t item, int64_t items, int ngroups,
+                                         const St* __restrict__ src, int n, int64_t stride, int d, int C,
+                                         int lane) {
+  const int64_t t = item / ngroups;
+  const int c = (int)(item - t * ngroups) * 64 + lane;
+  const bool ok = item < items && c < C;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    if (ok && i < n) {
+      s[i].load(src + (int64_t)i * stride + t * d + c * 8);
+    } else {
+      s[i].zero();
     }
   }
-  __syncthreads();
+}
 
-  // part B: each 8-channel chunk of the n source rows serves all S queries
-  const int C = d >> 3;
-  const int ntile = (int)((T - tok0) < 16 ? (T - tok0) : 16);
-  for (int item = threadIdx.x; item < ntile * C; item += 256) {
-    const int t = item / C;
-    const int c = item - t * C;
-    const int64_t tok = tok0 + t;
-    float b[NB][8];
+template <typename St, int NB>
+__device__ __forceinline__ void p1_emit(const Chunk<St> (&s)[NB], int64_t item, int ngroups, int n, int64_t T,
+                                        int d, int C, int lane, const float* __restrict__ alpha, int S,
+                                        St* __restrict__ out) {
+  const int64_t t = item / ngroups;
+  const int c = (int)(item - t * ngroups) * 64 + lane;
+  float b[NB][8];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) s[i].unpack(b[i]);
+  const float* al = alpha + t * S * n;
+  for (int q = 0; q < S; ++q) {
+    float o[8];
+    zero8(o);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (i < n) {
-        load8(src + (int64_t)i * stride + tok * d + c * 8, b[i]);
-      } else {
-        zero8(b[i]);
+        const float a = al[q * n + i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(a, b[i][e], o[e]);
       }
     }
-    for (int s = 0; s < S; ++s) {
-      const float* al = zb + (t * QP + s) * NP;
-      float o[8];
-      zero8(o);
-#pragma unroll
-      for (int i4 = 0; i4 < NP / 4; ++i4) {
-        const float4 a4 = *reinterpret_cast<const float4*>(al + 4 * i4);
-        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (4 * i4 + j < NB) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = fmaf(av[j], b[4 * i4 + j][e], o[e]);
-          }
-        }
-      }
-      store8(out + ((int64_t)s * T + tok) * d + c * 8, o);
-    }
+    if (c < C) out8(out + ((int64_t)q * T + t) * d + c * 8, o);
+  }
+}
+
+template <typename St, int NB>
+__global__ __launch_bounds__(256) void k_p1_out(const St* __restrict__ src, int n, int64_t stride, int64_t T,
+                                                int d, const float* __restrict__ alpha, int S,
+                                                St* __restrict__ out) {
+  const int C = d >> 3;
+  const int ngroups = (C + 63) >> 6;
+  const int64_t items = T * ngroups;
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  int64_t item = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Chunk<St> A[NB], B[NB];
+  p1_issue<St, NB>(A, item, items, ngroups, src, n, stride, d, C, lane);
+  while (item < items) {
+    p1_issue<St, NB>(B, item + nw, items, ngroups, src, n, stride, d, C, lane);
+    p1_emit<St, NB>(A, item, ngroups, n, T, d, C, lane, alpha, S, out);
+    item += nw;
+    if (item >= items) break;
+    p1_issue<St, NB>(A, item + nw, items, ngroups, src, n, stride, d, C, lane);
+    p1_emit<St, NB>(B, item, ngroups, n, T, d, C, lane, alpha, S, out);
+    item += nw;
   }
 }
 
@@ -460,39 +492,46 @@ static hipError_t set_lds(Kern k, size_t bytes) {
 template <typename St, int MT, int NB>
 static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, int d, const float* w,
                             const float* kg, int S, float eps, void* out, float* m_out, float* lse_out,
-                            hipStream_t stream) {
+                            float* alpha, hipStream_t stream) {
   constexpr int G = NB < 8 ? NB : 8;
   constexpr int NP = NB < 4 ? 4 : NB;
   const size_t lds = sizeof(float) * (2 * Red<MT, G>::kSlot + 16 * 16 * MT * NP);
-  auto kern = k_phase1_multi<St, MT, NB>;
-  hipError_t e = set_lds(kern, lds);
+  auto ks = k_p1_scores<St, MT, NB>;
+  hipError_t e = set_lds(ks, lds);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((T + 15) / 16));
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, static_cast<const St*>(src), n, stride, T, d, w,
-                     kg, S, eps, static_cast<St*>(out), m_out, lse_out);
+  hipLaunchKernelGGL(ks, dim3((unsigned)((T + 15) / 16)), dim3(256), lds, stream, static_cast<const St*>(src),
+                     n, stride, T, d, w, kg, S, eps, alpha, m_out, lse_out);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t items = T * (int64_t)(((d >> 3) + 63) >> 6);
+  const int64_t wgs = (items + 3) / 4;
+  const int64_t cap = (int64_t)device_cu_count() * 4;
+  hipLaunchKernelGGL((k_p1_out<St, NB>), dim3((unsigned)(wgs < cap ? wgs : cap)), dim3(256), 0, stream,
+                     static_cast<const St*>(src), n, stride, T, d, alpha, S, static_cast<St*>(out));
   return hipGetLastError();
 }
 
 template <typename St, int MT>
 static hipError_t pick_nb(const void* src, int n, int64_t stride, int64_t T, int d, const float* w,
                           const float* kg, int S, float eps, void* out, float* m_out, float* lse_out,
-                          hipStream_t stream) {
-  if (n <= 1) return run_multi<St, MT, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, stream);
-  if (n <= 2) return run_multi<St, MT, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, stream);
-  if (n <= 4) return run_multi<St, MT, 4>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, stream);
-  if (n <= 8) return run_multi<St, MT, 8>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, stream);
-  return run_multi<St, MT, 16>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, stream);
+                          float* alpha, hipStream_t stream) {
+  if (n <= 1) return run_multi<St, MT, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
+  if (n <= 2) return run_multi<St, MT, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
+  if (n <= 4) return run_multi<St, MT, 4>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
+  if (n <= 8) return run_multi<St, MT, 8>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
+  return run_multi<St, MT, 16>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
 }
 
 hipError_t launch_phase1_multi(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
                                const float* w, const float* kg, int S, float eps, void* out,
-                               float* m_out, float* lse_out, hipStream_t stream) {
+                               float* m_out, float* lse_out, float* alpha, hipStream_t stream) {
   if (dt == kBF16) {
-    if (S <= 16) return pick_nb<bf16_t, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, stream);
-    return pick_nb<bf16_t, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, stream);
+    if (S <= 16)
+      return pick_nb<bf16_t, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
+    return pick_nb<bf16_t, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
   }
-  if (S <= 16) return pick_nb<float, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, stream);
-  return pick_nb<float, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, stream);
+  if (S <= 16) return pick_nb<float, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
+  return pick_nb<float, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
 }
 
 template <typename St, int G>

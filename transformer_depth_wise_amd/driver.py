@@ -11,7 +11,8 @@ section 10) for every block of sublayers:
 
 Buffers live in HBM for the whole pass: the block representations
 ``reps [1 + n_given + N, T, d]`` (slot 0 is the embedding b_0), the phase-1
-outputs ``o1 [S_max, T, d]`` with their ``lse/m [S_max, T]`` (fp32), the
+outputs ``o1 [S_max, T, d]`` with their ``lse/m [S_max, T]`` (fp32) and the
+phase-1 workspace (softmax weights, ``T * n * S_max`` fp32), the
 running intra-block partial sum ``partial [T, d]`` in fp32, and a small ring of
 PreNorm outputs ``x``.  The partial sum is kept in fp32 because a bf16 running
 sum over a 24-sublayer block drifts by several percent of the row maximum;
@@ -75,6 +76,9 @@ class BlockAttnRes:
         self.o1 = torch.empty((smax, T, d), dtype=dtype, device=dev)
         self.m1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
         self.lse1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
+        n_max = 1 + self.n_given + max(0, len(self.block_sizes) - 1)
+        ws = _lib.attnres_phase1_workspace_bytes(T, n_max, smax) if T > 0 else 0
+        self.workspace = torch.empty((max(ws, 16) // 4,), dtype=torch.float32, device=dev)
         self.partial = torch.empty((T, d), dtype=torch.float32, device=dev)
         self.x = torch.empty((max(1, x_ring), T, d), dtype=dtype, device=dev)
         self.h = torch.empty((T, d), dtype=dtype, device=dev) if keep_h else None
@@ -135,7 +139,7 @@ class BlockAttnRes:
         for S in self.block_sizes:
             mark("phase1", True)
             attnres_phase1(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S], eps,
-                           self.o1[:S], self.m1[:S], self.lse1[:S], stream=stream)
+                           self.o1[:S], self.m1[:S], self.lse1[:S], self.workspace, stream=stream)
             mark("phase1", False)
             # outputs of the block kept alive: the first two (for the first
             # fp32 partial sum) and the previous one
