@@ -62,6 +62,73 @@ def cpu_baseline(w, emb, v, prm, target_s: float):
     }
 
 
+def measured_traffic(path, kind, workload):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when there is none or
+    the kernel's sources changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(path):
+        return None
+    try:
+        tr = json.load(open(path))
+    except ValueError:
+        return None
+    if tr.get("kind") != kind or tr.get("workload") != workload:
+        return None
+    h = hashlib.sha256()
+    for f in tr.get("sources", []):
+        fp = os.path.join(ROOT, f)
+        if not os.path.exists(fp):
+            return None
+        h.update(open(fp, "rb").read())
+    if h.hexdigest()[:16] != tr.get("source_sha256_16"):
+        return None
+    return tr.get("bytes_per_launch")
+
+
+def long_prefill_report(w, dev):
+    """Peak device memory and throughput of the long-context prefill, streamed
+    in chunks vs one unchunked pass.  Sublayer outputs are generated for the
+    tokens at hand between phase-2 launches (the full context's outputs would
+    not fit), so the times include that generation; the memory split reports
+    the AttnRes buffers separately from the total peak."""
+    import torch
+    import synth
+    import transformer_depth_wise_amd as tdw
+
+    scales = synth.sublayer_scales(w)
+    prm = synth.params(w, dev)
+    res = {"metric": "long-context prefill peak device memory, chunked vs unchunked", "config": {
+        "workload": w.name, "T": w.T, "chunk": w.chunk, "d": w.d, "sublayers": w.L,
+        "blocks": list(w.block_sizes)}}
+    for label, chunk in (("chunked", w.chunk), ("unchunked", w.T)):
+        ledger = {}
+
+        def fill(c0, c1, dst):
+            dst.copy_(synth.embedding(w, c0, c1, dev))
+
+        def sub_for(c0, c1):
+            return lambda l, x: synth.sublayer_output(w, l + 1, c0, c1, dev, scales)
+
+        def on_chunk(c0, c1, st):
+            ledger.update(st.buffer_bytes())
+
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        t0 = time.perf_counter()
+        tdw.prefill_chunked(w.T, chunk, w.d, w.block_sizes, w.torch_dtype, prm, fill, sub_for,
+                            on_chunk=on_chunk, eps=w.eps)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        res[label] = {"peak_gb": round((torch.cuda.max_memory_allocated() - base) / 1e9, 3),
+                      "attnres_buffers_gb": round(ledger["total"] / 1e9, 3),
+                      "block_reps_gb": round(ledger["block_reps"] / 1e9, 3),
+                      "seconds_incl_generation": round(el, 3)}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -70,6 +137,8 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill_chunk_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", choices=["copy"], default=None,
+                    help="run only a plain device copy of known size (counter calibration)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="rocprofv3 FETCH_SIZE/WRITE_SIZE summary for the dominant kernel")
     args = ap.parse_args()
@@ -89,8 +158,21 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.probe == "copy":
+        # 1 GiB read + 1 GiB written per dispatch, 4 dispatches
+        a = torch.ones((1 << 29,), dtype=torch.bfloat16, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"probe": "copy", "bytes_read_per_dispatch": a.numel() * 2,
+                          "bytes_written_per_dispatch": b.numel() * 2, "dispatches": 4}), flush=True)
+        return 0
     w = synth.WORKLOADS[args.workload]
-    if w.full or w.chunk:
+    if w.chunk:
+        print(json.dumps(long_prefill_report(w, dev)), flush=True)
+        return 0
+    if w.full:
         raise SystemExit("bench.py times the block workloads only")
 
     # ---- inputs resident in HBM (untimed)
@@ -139,6 +221,32 @@ def main() -> int:
     kind_ms = {}
     for kind, a, b in recs:
         kind_ms[kind] = kind_ms.get(kind, 0.0) + a.elapsed_time(b)
+
+    # ---- cold-cache pass: a 512 MiB scratch write between consecutive
+    # launches evicts the 256 MB last-level cache (MALL), as the sublayers of
+    # a model would; only the AttnRes launches are timed (events around each).
+    scratch = torch.empty((1 << 28,), dtype=torch.float16, device=dev)
+    crecs = []
+
+    def instrument_cold(kind, begin):
+        if begin:
+            scratch.fill_(1.0)
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        if begin:
+            crecs.append([kind, e, None])
+        else:
+            crecs[-1][2] = e
+
+    cold_steps = max(1, min(3, args.steps))
+    for _ in range(cold_steps):
+        st.forward(prm, sub, instrument=instrument_cold)
+    torch.cuda.synchronize()
+    cold_kind = {}
+    for kind, a, b in crecs:
+        cold_kind[kind] = cold_kind.get(kind, 0.0) + a.elapsed_time(b) / cold_steps
+    del scratch
+    cold_ms = sum(cold_kind.values())
     steps = args.steps
     ms_per_step = elapsed * 1e3 / steps
     units = w.T * w.L
@@ -154,14 +262,7 @@ def main() -> int:
     avg_launch_s = kind_ms[dom] / steps / launches * 1e-3
     avg_bytes = kind_bytes[dom] / launches
     achieved = avg_bytes / avg_launch_s / 1e9
-    traffic = None
-    if os.path.exists(args.traffic):
-        try:
-            tr = json.load(open(args.traffic))
-            if tr.get("kind") == dom and tr.get("workload") == w.name:
-                traffic = tr.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = measured_traffic(args.traffic, dom, w.name)
     out = {
         "metric": METRIC,
         "value": round(units * steps / elapsed, 1),
@@ -186,6 +287,13 @@ def main() -> int:
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "avg_launch_us": round(avg_launch_s * 1e6, 2), "algorithmic_bytes_per_launch": int(avg_bytes)},
+        "cold_cache": {
+            "note": "512 MiB scratch write between launches (MALL evicted), AttnRes kernels only",
+            "ms_per_step": round(cold_ms, 4),
+            "value": round(units / (cold_ms * 1e-3), 1),
+            "hbm_gbps": round(step_bytes / (cold_ms * 1e-3) / 1e9, 1),
+            "kernels_gbps": {k: round(kind_bytes[k] / (cold_kind[k] * 1e-3) / 1e9, 1) for k in cold_kind},
+            "dominant_frac": round(kind_bytes[dom] / (cold_kind[dom] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, emb, v, prm, args.cpu_seconds)

@@ -86,9 +86,10 @@ typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1 } attnres_dtype_t;
  * time; each group of 32 reads the sources once for the scores and once for
  * the outputs).
  * workspace: caller-owned device memory of at least
- * attnres_phase1_workspace_bytes(T, n_src, S) bytes, 16-byte aligned, used
- * for the softmax weights between the scoring and output kernels (its
- * contents afterwards are unspecified); NULL allowed when that size is 0.
+ * attnres_phase1_workspace_bytes(T, d, n_src, S) bytes, 16-byte aligned,
+ * used for the queries packed as matrix-core operands and for the softmax
+ * weights between the scoring and output kernels (its contents afterwards are
+ * unspecified); NULL allowed when that size is 0.
  * out must not overlap src; m_out, lse_out and workspace must not overlap
  * anything.
  */
@@ -99,9 +100,9 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt,
                                 void* out, float* m_out, float* lse_out,
                                 void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes attnres_phase1 needs: T * n_src * min(S, 32) * 4 when
- * S >= 2, 0 when S == 1; -1 for invalid sizes. */
-int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t n_src, int64_t S);
+/* Workspace bytes attnres_phase1 needs: 32 * d * 4 + T * n_src * min(S, 32)
+ * * 4 when S >= 2, 0 when S == 1; -1 for invalid sizes. */
+int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int64_t S);
 
 /*
  * Phase 2 for one sublayer j of a block ("Attention Residuals" notes,

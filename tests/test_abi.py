@@ -55,7 +55,7 @@ def p(x):
 def phase1(lib, dt=1, src=A, n=3, stride=4096 * 64, T=4096, d=64, w=8 * A, kg=None, S=4, eps=1e-6,
            out=16 * A, m=None, lse=24 * A, ws=32 * A, ws_bytes=None):
     if ws_bytes is None:
-        ws_bytes = lib.attnres_phase1_workspace_bytes(T, n, S)
+        ws_bytes = lib.attnres_phase1_workspace_bytes(T, d, n, S)
     return lib.attnres_phase1(dt, p(src), n, stride, T, d, p(w), p(kg), S, eps, p(out), p(m), p(lse), p(ws),
                               ws_bytes, None)
 
@@ -81,9 +81,10 @@ def test_phase1_validation(lib):
     assert phase1(lib, ws=None) == EINVAL                # S >= 2 needs the workspace
     assert phase1(lib, ws_bytes=100) == EINVAL           # too small
     assert phase1(lib, ws=16 * A + 64) == EALIAS         # workspace inside the output
-    assert lib.attnres_phase1_workspace_bytes(4096, 3, 4) == 4096 * 3 * 4 * 4
-    assert lib.attnres_phase1_workspace_bytes(4096, 3, 40) == 4096 * 3 * 32 * 4
-    assert lib.attnres_phase1_workspace_bytes(4096, 3, 1) == 0
+    assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 4) == 32 * 64 * 4 + 4096 * 3 * 4 * 4
+    assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 40) == 32 * 64 * 4 + 4096 * 3 * 32 * 4
+    assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 1) == 0
+    assert lib.attnres_phase1_workspace_bytes(4096, 12, 3, 4) == -1
     assert phase1(lib, T=0) == 0                      # nothing to do, nothing launched
     assert phase1(lib, T=0, src=None, out=None, lse=None) == 0
 

@@ -176,3 +176,76 @@ def test_token_split_invariance():
         s2.reps[0].copy_(emb[a:b])
         s2.forward(prm, lambda l, x: v[l][a:b].contiguous())
         assert torch.equal(s2.h_final, whole[a:b])
+
+
+# --------------------------------------------- long context, chunked prefill
+def _long_prefill(w, chunked: bool, samples, dev):
+    """Run the whole depth over T tokens, streamed in 16K chunks or in one
+    pass; sublayer outputs are produced on the fly for the tokens at hand
+    (as a model's sublayers would), never for the whole context at once."""
+    from harness import Capture
+    scales = synth.sublayer_scales(w)
+    prm = synth.params(w, dev)
+    h_final = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
+    caps = {}
+
+    def fill(c0, c1, dst):
+        dst.copy_(synth.embedding(w, c0, c1, dev))
+
+    def sub_for(c0, c1):
+        return lambda l, x: synth.sublayer_output(w, l + 1, c0, c1, dev, scales)
+
+    def hook_for(c0, c1):
+        local = [t - c0 for t in samples if c0 <= t < c1]
+        if not local:
+            return None
+        cap = Capture(torch.tensor(local, dtype=torch.long, device=dev))
+        caps[c0] = (local, cap)
+        return cap
+
+    def on_chunk(c0, c1, st):
+        h_final[c0:c1].copy_(st.h_final)
+
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    tdw.prefill_chunked(w.T, w.chunk if chunked else w.T, w.d, w.block_sizes, w.torch_dtype, prm, fill, sub_for,
+                        on_chunk=on_chunk, eps=w.eps, hook_for_chunk=hook_for)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    xs = {}
+    for c0, (local, cap) in caps.items():
+        x = torch.stack(cap.rows["x"])  # [L, k, d]
+        for j, t in enumerate(local):
+            xs[c0 + t] = x[:, j].clone()
+    return h_final, xs, peak
+
+
+def test_long_prefill_chunked_equals_unchunked_and_oracle():
+    w = synth.WORKLOADS["long_prefill_bf16"]
+    dev = torch.device("cuda")
+    samples = synth.sample_tokens(w.T, 24)
+    _say("case long_prefill T=%d chunk=%d chunked pass" % (w.T, w.chunk))
+    hc, xc, peak_c = _long_prefill(w, True, samples, dev)
+    _say("case long_prefill unchunked pass")
+    hu, xu, peak_u = _long_prefill(w, False, samples, dev)
+    _say("peak AttnRes device memory: chunked %.2f GB, unchunked %.2f GB" % (peak_c / 1e9, peak_u / 1e9))
+    # tokens never interact, so the chunking cannot change any bit
+    assert torch.equal(hc, hu)
+    for t in samples:
+        assert torch.equal(xc[t], xu[t]), t
+    assert peak_c * 4 < peak_u
+    # oracle on the sampled tokens, from the generated inputs
+    idx = torch.tensor(samples, dtype=torch.long, device=dev)
+    scales = synth.sublayer_scales(w)
+    emb = torch.cat([synth.embedding(w, t, t + 1, dev) for t in samples])
+    v = torch.stack([torch.cat([synth.sublayer_output(w, l + 1, t, t + 1, dev, scales) for t in samples])
+                     for l in range(w.L)])
+    prm = synth.params(w, dev)
+    o = oracle.block_forward(emb, v, prm["w"], prm["g"], prm["gamma"], w.block_sizes, w.eps,
+                             want=("x", "hfinal"))
+    gx = torch.stack([xc[t] for t in samples], dim=1)  # [L, k, d]
+    ex = row_rel_err(_host(gx), o["x"]).max()
+    eh = row_rel_err(_host(hc.index_select(0, idx)), o["hfinal"]).max()
+    _say("worst x %.3e hfinal %.3e" % (ex, eh))
+    assert ex <= TOL["bf16"] and eh <= TOL["bf16"]

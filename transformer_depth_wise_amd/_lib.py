@@ -46,7 +46,7 @@ def load(path: Optional[str] = None):
     lib = ctypes.CDLL(p)
     V, I, F, E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
     lib.attnres_phase1.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V, I, V]
-    lib.attnres_phase1_workspace_bytes.argtypes = [I, I, I]
+    lib.attnres_phase1_workspace_bytes.argtypes = [I, I, I, I]
     lib.attnres_phase1_workspace_bytes.restype = ctypes.c_int64
     lib.attnres_phase2_merge.argtypes = [E, I, I, V, V, E, V, V, V, V, V, V, F, V, V, V]
     lib.attnres_full.argtypes = [E, V, I, I, I, I, V, V, V, F, V, V, V, V]
@@ -89,8 +89,8 @@ def _check(fn: str, rc: int):
         raise AttnResError(fn, rc, status_string(rc))
 
 
-def attnres_phase1_workspace_bytes(T: int, n_src: int, S: int) -> int:
-    return int(load().attnres_phase1_workspace_bytes(T, n_src, S))
+def attnres_phase1_workspace_bytes(T: int, d: int, n_src: int, S: int) -> int:
+    return int(load().attnres_phase1_workspace_bytes(T, d, n_src, S))
 
 
 def attnres_phase1(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],

@@ -80,10 +80,12 @@ const char* attnres_status_string(attnres_status_t status) {
   return "ATTNRES_UNKNOWN_STATUS";
 }
 
-int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t n_src, int64_t S) {
-  if (T < 0 || n_src < 1 || S < 1) return -1;
+int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int64_t S) {
+  if (T < 0 || n_src < 1 || S < 1 || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
   if (S == 1) return 0;
-  return T * n_src * (S < 32 ? S : 32) * (int64_t)sizeof(float);
+  // packed queries (32 rows x d x 4 bytes) + softmax weights (T x n x 32 x 4 bytes)
+  const int64_t sq = S < 32 ? S : 32;
+  return 32 * d * 4 + T * n_src * sq * (int64_t)sizeof(float);
 }
 
 attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
@@ -100,7 +102,7 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_s
   if (!src || !w || !out || !lse_out) return ATTNRES_EINVAL;
   if (n_src > 1 && (src_stride < T * d)) return ATTNRES_EINVAL;
   if (src_stride % 8 != 0) return ATTNRES_EALIGN;
-  const int64_t ws_need = attnres_phase1_workspace_bytes(T, n_src, S);
+  const int64_t ws_need = attnres_phase1_workspace_bytes(T, d, n_src, S);
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return ATTNRES_EINVAL;
   st = check_align({src, w, key_gain, out, ws_need > 0 ? workspace : nullptr}, {m_out, lse_out});
   if (st != ATTNRES_OK) return st;

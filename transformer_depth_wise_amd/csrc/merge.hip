@@ -30,31 +30,32 @@ template <typename St, typename Pt, int CPL>
 struct Stage {
   Chunk<St> o[CPL], v[CPL];
   Chunk<Pt> q[CPL];
+  bool ok[CPL];
 };
 
-template <typename St, typename Pt, int TEAM, int CPL>
+// Loads of one token for the team.  Every load is unconditional (an
+// out-of-range token or chunk reads a clamped valid address and is zeroed
+// when used), so the loads of a stage issue back to back.
+template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN>
 __device__ __forceinline__ void issue(Stage<St, Pt, CPL>& s, int64_t tok, int64_t T, int d, int C, int tl,
                                       const St* o1, const Pt* pin, const St* vprev) {
   const bool live = tok < T;
+  const int64_t tc = live ? tok : T - 1;
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
-    const int c = tl + TEAM * k;
-    if (live && c < C) {
-      const int64_t off = tok * d + c * 8;
-      s.o[k].load(o1 + off);
-      if (vprev) {
-        s.v[k].load(vprev + off);
-        if (pin) s.q[k].load(pin + off); else s.q[k].zero();
-      } else { s.v[k].zero(); s.q[k].zero(); }
-    } else {
-      s.o[k].zero(); s.v[k].zero(); s.q[k].zero();
-    }
+    const int c0 = tl + TEAM * k;
+    s.ok[k] = live && c0 < C;
+    const int c = c0 < C ? c0 : C - 1;
+    const int64_t off = tc * d + c * 8;
+    s.o[k].load(o1 + off);
+    if (HAS_V) s.v[k].load(vprev + off);
+    if (HAS_PIN) s.q[k].load(pin + off);
   }
 }
 
-template <typename St, typename Pt, int TEAM, int CPL>
+template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN>
 __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok, int64_t T, int d, int C, int tl,
-                                        const float* lse1, const St* vprev, float* pout,
+                                        const float* lse1, float* pout,
                                         const float (&wq)[CPL][8], const float (&gm)[CPL][8], float eps, float inv_d,
                                         St* h_out, St* x_out, float (*red)[8], int& parity) {
   const bool live = tok < T;
@@ -63,26 +64,43 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
     s.o[k].unpack(h[k]);
-    if (vprev) {
-      float q[8];
+    if (HAS_V) {
       s.v[k].unpack(p[k]);
-      s.q[k].unpack(q);
+      if (HAS_PIN) {
+        float q[8];
+        s.q[k].unpack(q);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[k][e] = q[e] + p[k][e];
-      const int c = tl + TEAM * k;
-      if (pout && live && c < C) out8(pout + tok * d + c * 8, p[k]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { ss = fmaf(p[k][e], p[k][e], ss); dot = fmaf(wq[k][e], p[k][e], dot); }
+        for (int e = 0; e < 8; ++e) p[k][e] = q[e] + p[k][e];
+      }
     } else {
       zero8(p[k]);
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h[k][e] = s.ok[k] ? h[k][e] : 0.f;
+      p[k][e] = s.ok[k] ? p[k][e] : 0.f;
+    }
+    if (HAS_V) {
+      const int c = tl + TEAM * k;
+      if (pout && s.ok[k]) out8(pout + tok * d + c * 8, p[k]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ss = fmaf(p[k][e], p[k][e], ss);
+        dot = fmaf(wq[k][e], p[k][e], dot);
+      }
+    }
   }
-  if (vprev) {
+  if (HAS_V) {
     float2 r;
-    if (TEAM == 256) { r = block_sum2_256(ss, dot, red[parity]); parity ^= 1; }
-    else { r.x = wave_sum(ss); r.y = wave_sum(dot); }
+    if (TEAM == 256) {
+      r = block_sum2_256(ss, dot, red[parity]);
+      parity ^= 1;
+    } else {
+      r.x = wave_sum(ss);
+      r.y = wave_sum(dot);
+    }
     const float zc = r.y / sqrtf(r.x * inv_d + eps);
-    const float lse = live ? lse1[tok] : 0.f;
+    const float lse = lse1[live ? tok : T - 1];
     const float beta = 1.0f / (1.0f + expf(lse - zc));
 #pragma unroll
     for (int k = 0; k < CPL; ++k)
@@ -96,29 +114,30 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
     for (int e = 0; e < 8; ++e) sh = fmaf(h[k][e], h[k][e], sh);
   float r2 = 0.f;
   if (x_out) {
-    if (TEAM == 256) { r2 = block_sum2_256(sh, 0.f, red[parity]).x; parity ^= 1; }
-    else r2 = wave_sum(sh);
+    if (TEAM == 256) {
+      r2 = block_sum2_256(sh, 0.f, red[parity]).x;
+      parity ^= 1;
+    } else {
+      r2 = wave_sum(sh);
+    }
   }
-  if (live) {
-    const float rinv = x_out ? 1.0f / sqrtf(r2 * inv_d + eps) : 1.f;
+  const float rinv = x_out ? 1.0f / sqrtf(r2 * inv_d + eps) : 1.f;
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      const int c = tl + TEAM * k;
-      if (c < C) {
-        const int64_t off = tok * d + c * 8;
-        if (h_out) out8(h_out + off, h[k]);
-        if (x_out) {
-          float x[8];
+  for (int k = 0; k < CPL; ++k) {
+    if (s.ok[k]) {
+      const int64_t off = tok * d + (tl + TEAM * k) * 8;
+      if (h_out) out8(h_out + off, h[k]);
+      if (x_out) {
+        float x[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = gm[k][e] * (h[k][e] * rinv);
-          out8(x_out + off, x);
-        }
+        for (int e = 0; e < 8; ++e) x[e] = gm[k][e] * (h[k][e] * rinv);
+        out8(x_out + off, x);
       }
     }
   }
 }
 
-template <typename St, typename Pt, int TEAM, int CPL>
+template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN>
 __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __restrict__ o1,
                                                const float* __restrict__ lse1, const Pt* __restrict__ pin,
                                                const St* __restrict__ vprev, float* __restrict__ pout,
@@ -136,31 +155,42 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
   for (int k = 0; k < CPL; ++k) {
     const int c = tl + TEAM * k;
     if (c < C) {
-      if (vprev) {
+      if (HAS_V) {
         load8(w + c * 8, wq[k]);
-        if (kg) { float g[8]; load8(kg + c * 8, g);
+        if (kg) {
+          float g[8];
+          load8(kg + c * 8, g);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) wq[k][e] *= g[e]; }
-      } else zero8(wq[k]);
-      if (gamma) load8(gamma + c * 8, gm[k]);
-      else {
+          for (int e = 0; e < 8; ++e) wq[k][e] *= g[e];
+        }
+      } else {
+        zero8(wq[k]);
+      }
+      if (gamma) {
+        load8(gamma + c * 8, gm[k]);
+      } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) gm[k][e] = 1.f;
       }
-    } else { zero8(wq[k]); zero8(gm[k]); }
+    } else {
+      zero8(wq[k]);
+      zero8(gm[k]);
+    }
   }
   int parity = 0;
   const int64_t step = (int64_t)gridDim.x * TPW;
   int64_t tok = (int64_t)blockIdx.x * TPW + team;
   Stage<St, Pt, CPL> A, B;
-  issue<St, Pt, TEAM, CPL>(A, tok, T, d, C, tl, o1, pin, vprev);
+  issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(A, tok, T, d, C, tl, o1, pin, vprev);
   while (tok - team < T) {
-    issue<St, Pt, TEAM, CPL>(B, tok + step, T, d, C, tl, o1, pin, vprev);
-    process<St, Pt, TEAM, CPL>(A, tok, T, d, C, tl, lse1, vprev, pout, wq, gm, eps, inv_d, h_out, x_out, red, parity);
+    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(B, tok + step, T, d, C, tl, o1, pin, vprev);
+    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(A, tok, T, d, C, tl, lse1, pout, wq, gm, eps, inv_d, h_out, x_out,
+                                              red, parity);
     tok += step;
     if (tok - team >= T) break;
-    issue<St, Pt, TEAM, CPL>(A, tok + step, T, d, C, tl, o1, pin, vprev);
-    process<St, Pt, TEAM, CPL>(B, tok, T, d, C, tl, lse1, vprev, pout, wq, gm, eps, inv_d, h_out, x_out, red, parity);
+    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(A, tok + step, T, d, C, tl, o1, pin, vprev);
+    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(B, tok, T, d, C, tl, lse1, pout, wq, gm, eps, inv_d, h_out, x_out,
+                                              red, parity);
     tok += step;
   }
 }
@@ -192,10 +222,21 @@ static hipError_t run_merge(int64_t T, int d, const void* o1, const float* lse1,
   const int64_t tiles = (T + TPW - 1) / TPW;
   const int64_t cap = (int64_t)device_cu_count() * 2;  // persistent: 2 workgroups per CU
   const dim3 grid((unsigned)(tiles < cap ? tiles : cap));
-  hipLaunchKernelGGL((k_merge<St, Pt, TEAM, CPL>), grid, dim3(256), 0, stream, T, d,
-                     static_cast<const St*>(o1), lse1, static_cast<const Pt*>(pin),
-                     static_cast<const St*>(vprev), pout, w, kg, gamma, eps, static_cast<St*>(h_out),
-                     static_cast<St*>(x_out));
+  const St* o = static_cast<const St*>(o1);
+  const Pt* pi = static_cast<const Pt*>(pin);
+  const St* v = static_cast<const St*>(vprev);
+  St* h = static_cast<St*>(h_out);
+  St* x = static_cast<St*>(x_out);
+  if (!vprev) {
+    hipLaunchKernelGGL((k_merge<St, Pt, TEAM, CPL, false, false>), grid, dim3(256), 0, stream, T, d, o, lse1, pi, v,
+                       pout, w, kg, gamma, eps, h, x);
+  } else if (!pin) {
+    hipLaunchKernelGGL((k_merge<St, Pt, TEAM, CPL, true, false>), grid, dim3(256), 0, stream, T, d, o, lse1, pi, v,
+                       pout, w, kg, gamma, eps, h, x);
+  } else {
+    hipLaunchKernelGGL((k_merge<St, Pt, TEAM, CPL, true, true>), grid, dim3(256), 0, stream, T, d, o, lse1, pi, v,
+                       pout, w, kg, gamma, eps, h, x);
+  }
   return hipGetLastError();
 }
 

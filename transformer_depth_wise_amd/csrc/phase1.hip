@@ -6,27 +6,40 @@
 // products into one Q K^T product, and each source row is read once per
 // block instead of once per sublayer).
 //
-// Work decomposition.  S >= 2 uses two kernels; S == 1 (Full AttnRes sites and
-// the final aggregation) uses one kernel that does both parts per tile.
-//  part A  scores (one workgroup = 4 waves = a tile of 16 tokens).  Z[q][t][i] = sum_k (w_q g_q)[k] * u_i[t][k] is a dense
-//          contraction over d, computed on the matrix cores with
-//          v_mfma_f32_16x16x32_bf16 (bf16 rows; the fp32 query is split into
-//          bf16 hi + lo parts, so the product keeps ~16 mantissa bits of the
-//          query and accumulates in fp32) or v_mfma_f32_16x16x4_f32 (fp32
-//          rows).  A lane supplies query (lane&15) of the A operand and token
-//          (lane&15) of the B operand; the 4 lane groups and the 4 waves split
-//          the channels.  Sum of squares of every source row (for its RMS) is
-//          accumulated on the vector ALUs from the same registers.  The four
-//          waves' partial sums are added in a fixed order through LDS, then
-//          z = Z / r(u) and the softmax over sources is taken in LDS.
-//          For S >= 2 the softmax weights go to a caller-provided workspace.
+// Work decomposition.  S >= 2 uses three launches (pack, score, output);
+// S == 1 (Full AttnRes sites and the final aggregation) uses one kernel that
+// does both parts per 16-token tile.
+//  part A  scores (one workgroup = 4 waves = a tile of 16 tokens).
+//          Z[q][t][i] = sum_k (w_q g_q)[k] * u_i[t][k] is a dense contraction
+//          over d, computed on the matrix cores with v_mfma_f32_16x16x32_bf16
+//          (bf16 rows; the fp32 query is split into bf16 hi + lo parts, so the
+//          product keeps ~16 mantissa bits of the query and accumulates in
+//          fp32) or v_mfma_f32_16x16x4_f32 (fp32 rows).  A lane supplies query
+//          (lane&15) of the A operand and token (lane&15) of the B operand;
+//          the 4 lane groups and the 4 waves split the channels.  The sum of
+//          squares of every source row (for its RMS) is accumulated on the
+//          vector ALUs from the same registers.  The four waves' partial sums
+//          are added in a fixed order through LDS, then z = Z / r(u) and the
+//          softmax over sources is taken in LDS.  For S >= 2 the queries are
+//          packed once per call into MFMA operand chunks and the softmax
+//          weights go to a caller-provided workspace.
 //  part B  outputs.  out[s][t] = sum_i alpha[t][s][i] u_i[t]: the source rows
 //          are streamed again (16-byte loads, a wave reads 1 KiB of one row)
 //          and each row chunk serves all S queries.
+//
+// Every global load is unconditional: an out-of-range token or chunk loads a
+// clamped, valid address and the value is replaced by zero afterwards.  This
+// keeps loads free of exec-mask branches, so the compiler issues a whole
+// K-block (or the next item) of loads before the first wait.
 #include "attnres_device.h"
 #include "attnres_launch.h"
 
 namespace attnres {
+
+__device__ __forceinline__ u32x4_t sel16(bool ok, u32x4_t v) {
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  return ok ? v : z;
+}
 
 template <typename St>
 struct Mfma;
@@ -57,14 +70,30 @@ struct Mfma<bf16_t> {
     return a;
   }
 
-  static __device__ __forceinline__ B load_b(const bf16_t* p, bool ok, float& ss) {
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (ok) u = *reinterpret_cast<const uint4*>(p);
+  // Packed query chunk: 8 bf16 hi parts then 8 bf16 lo parts (32 bytes).
+  static __device__ __forceinline__ A load_packed(const u32x4_t* p, bool ok) {
+    A a;
+    a.hi = __builtin_bit_cast(bf16x8_t, sel16(ok, ld16(p)));
+    a.lo = __builtin_bit_cast(bf16x8_t, sel16(ok, ld16(p + 1)));
+    return a;
+  }
+
+  static __device__ __forceinline__ void pack(const float (&q)[8], u32x4_t* p) {
+    const A a = make_a(q);
+    st16(p, __builtin_bit_cast(u32x4_t, a.hi));
+    st16(p + 1, __builtin_bit_cast(u32x4_t, a.lo));
+  }
+
+  static __device__ __forceinline__ B load_b(const bf16_t* p, bool ok) {
+    return __builtin_bit_cast(bf16x8_t, sel16(ok, ld16(p)));
+  }
+
+  static __device__ __forceinline__ void sumsq(const B& b, float& ss) {
+    const u32x4_t u = __builtin_bit_cast(u32x4_t, b);
     float f[8];
-    unpack_bf16x8(u, f);
+    unpack_bf16x8(make_uint4(u.x, u.y, u.z, u.w), f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
-    return __builtin_bit_cast(bf16x8_t, u);
   }
 
   static __device__ __forceinline__ void mma(f32x4_t& acc, const A& a, const B& b) {
@@ -89,16 +118,33 @@ struct Mfma<float> {
     return a;
   }
 
-  static __device__ __forceinline__ B load_b(const float* p, bool ok, float& ss) {
+  // Packed query chunk: the 8 folded fp32 values (32 bytes).
+  static __device__ __forceinline__ A load_packed(const u32x4_t* p, bool ok) {
+    const u32x4_t x = sel16(ok, ld16(p)), y = sel16(ok, ld16(p + 1));
+    A a;
+    a.v[0] = __uint_as_float(x.x); a.v[1] = __uint_as_float(x.y); a.v[2] = __uint_as_float(x.z);
+    a.v[3] = __uint_as_float(x.w); a.v[4] = __uint_as_float(y.x); a.v[5] = __uint_as_float(y.y);
+    a.v[6] = __uint_as_float(y.z); a.v[7] = __uint_as_float(y.w);
+    return a;
+  }
+
+  static __device__ __forceinline__ void pack(const float (&q)[8], u32x4_t* p) {
+    st16(p, u32x4_t{__float_as_uint(q[0]), __float_as_uint(q[1]), __float_as_uint(q[2]), __float_as_uint(q[3])});
+    st16(p + 1, u32x4_t{__float_as_uint(q[4]), __float_as_uint(q[5]), __float_as_uint(q[6]), __float_as_uint(q[7])});
+  }
+
+  static __device__ __forceinline__ B load_b(const float* p, bool ok) {
+    const u32x4_t x = sel16(ok, ld16(p)), y = sel16(ok, ld16(p + 4));
     B b;
-    if (ok) {
-      load8(p, b.v);
-    } else {
-      zero8(b.v);
-    }
+    b.v[0] = __uint_as_float(x.x); b.v[1] = __uint_as_float(x.y); b.v[2] = __uint_as_float(x.z);
+    b.v[3] = __uint_as_float(x.w); b.v[4] = __uint_as_float(y.x); b.v[5] = __uint_as_float(y.y);
+    b.v[6] = __uint_as_float(y.z); b.v[7] = __uint_as_float(y.w);
+    return b;
+  }
+
+  static __device__ __forceinline__ void sumsq(const B& b, float& ss) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(b.v[e], b.v[e], ss);
-    return b;
   }
 
   // One channel per lane group per instruction: channel e of the lane's chunk.
@@ -109,23 +155,29 @@ struct Mfma<float> {
 };
 
 // Per-wave partial scores of the 16-token tile starting at tok0 against
-// queries [0, 16*MT) for sources [g0, g0+G).  Channel chunks (8 channels)
-// are visited in K-blocks of 16 chunks; wave w takes K-blocks w, w+4, ...;
-// within a K-block, step s4 reads chunk 4*s4 + grp, so the 4 lane groups read
-// 64 contiguous bytes of each token row per instruction.
-template <typename St, int MT, int G>
-__device__ __forceinline__ void score_pass(const St* __restrict__ src, int n, int64_t stride,
-                                           int64_t T, int d, const float* __restrict__ w,
-                                           const float* __restrict__ kg, int S, int64_t tok0,
-                                           int g0, f32x4_t (&acc)[MT][G], float (&ss)[G]) {
+// queries [0, 16*MT) for sources [g0, g0+G) (all valid).  Channel chunks (8
+// channels) are visited in K-blocks of 16 chunks; wave w takes K-blocks w,
+// w+4, ...; within a K-block, step s4 reads chunk 4*s4 + grp, so the 4 lane
+// groups read 64 contiguous bytes of each token row per instruction.
+// With PACKED, the queries come from `pk` ([16*MT][C] chunks of 32 bytes,
+// rows >= S zero) written by k_pack_queries; otherwise w (.) g is formed and
+// split per chunk from the fp32 parameters.
+template <typename St, int MT, int G, bool PACKED>
+__device__ __forceinline__ void score_pass(const St* __restrict__ src, int64_t stride, int64_t T, int d,
+                                           const float* __restrict__ w, const float* __restrict__ kg,
+                                           const u32x4_t* __restrict__ pk, int S, int64_t tok0, int g0,
+                                           f32x4_t (&acc)[MT][G], float (&ss)[G]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int64_t tok = tok0 + col;
-  const bool tok_ok = tok < T;
+  const bool tok_ok = tok0 + col < T;
+  const int64_t tok = tok_ok ? tok0 + col : T - 1;  // clamped: always a valid row
   const int C = d >> 3;
   const int nkb = (C + 15) >> 4;
+  const St* base[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) base[i] = src + (int64_t)(g0 + i) * stride + tok * d;
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -134,38 +186,54 @@ __device__ __forceinline__ void score_pass(const St* __restrict__ src, int n, in
   for (int i = 0; i < G; ++i) ss[i] = 0.f;
 
   for (int kb = wave; kb < nkb; kb += 4) {
+    // All loads of the K-block first (queries and sources of the 4 steps),
+    // then the matrix-core work: the scheduling barrier keeps the compiler
+    // from sinking loads next to their first use, so a wave keeps 4 * (2*MT
+    // + G) 16-byte loads in flight instead of one step's worth.
+    typename Mfma<St>::A a[4][MT];
+    typename Mfma<St>::B b[4][G];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const int c = kb * 16 + s4 * 4 + grp;
-      const bool cok = c < C;
-      typename Mfma<St>::A a[MT];
+      const int c0 = kb * 16 + s4 * 4 + grp;
+      const bool cok = c0 < C;
+      const int c = cok ? c0 : C - 1;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const int q = m * 16 + col;
-        float qv[8];
-        if (cok && q < S) {
-          load8(w + (int64_t)q * d + c * 8, qv);
-          if (kg) {
-            float gv[8];
-            load8(kg + (int64_t)q * d + c * 8, gv);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qv[e] *= gv[e];
-          }
+        if (PACKED) {
+          a[s4][m] = Mfma<St>::load_packed(pk + ((int64_t)q * C + c) * 2, cok);
         } else {
-          zero8(qv);
+          const bool qok = cok && q < S;
+          const int qc = q < S ? q : 0;
+          float qv[8];
+          const u32x4_t w0 = sel16(qok, ld16(w + (int64_t)qc * d + c * 8));
+          const u32x4_t w1 = sel16(qok, ld16(w + (int64_t)qc * d + c * 8 + 4));
+          qv[0] = __uint_as_float(w0.x); qv[1] = __uint_as_float(w0.y); qv[2] = __uint_as_float(w0.z);
+          qv[3] = __uint_as_float(w0.w); qv[4] = __uint_as_float(w1.x); qv[5] = __uint_as_float(w1.y);
+          qv[6] = __uint_as_float(w1.z); qv[7] = __uint_as_float(w1.w);
+          if (kg) {
+            const u32x4_t g0v = ld16(kg + (int64_t)qc * d + c * 8);
+            const u32x4_t g1v = ld16(kg + (int64_t)qc * d + c * 8 + 4);
+            qv[0] *= __uint_as_float(g0v.x); qv[1] *= __uint_as_float(g0v.y);
+            qv[2] *= __uint_as_float(g0v.z); qv[3] *= __uint_as_float(g0v.w);
+            qv[4] *= __uint_as_float(g1v.x); qv[5] *= __uint_as_float(g1v.y);
+            qv[6] *= __uint_as_float(g1v.z); qv[7] *= __uint_as_float(g1v.w);
+          }
+          a[s4][m] = Mfma<St>::make_a(qv);
         }
-        a[m] = Mfma<St>::make_a(qv);
       }
+#pragma unroll
+      for (int i = 0; i < G; ++i) b[s4][i] = Mfma<St>::load_b(base[i] + c * 8, cok && tok_ok);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
       for (int i = 0; i < G; ++i) {
-        const int si = g0 + i;
-        const bool ok = cok && tok_ok && si < n;
-        const St* p = src + (int64_t)si * stride + tok * d + c * 8;
-        typename Mfma<St>::B b = Mfma<St>::load_b(p, ok, ss[i]);
+        Mfma<St>::sumsq(b[s4][i], ss[i]);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) Mfma<St>::mma(acc[m][i], a[m], b);
+        for (int m = 0; m < MT; ++m) Mfma<St>::mma(acc[m][i], a[s4][m], b[s4][i]);
       }
-    }
   }
   // every lane group saw different channels of the same (token, source)
 #pragma unroll
@@ -219,52 +287,95 @@ struct Red {
   }
 };
 
-// ---------------------------------------------------------------------------
-// S >= 2, first kernel: scores and softmax weights of a 16-token tile for up
-// to 32 queries.  The weights go to the workspace as alpha[t][q][i]
-// (i fastest), the statistics to m_out / lse_out.
-template <typename St, int MT, int NB>
-__global__ __launch_bounds__(256) void k_p1_scores(const St* __restrict__ src, int n, int64_t stride,
-                                                   int64_t T, int d, const float* __restrict__ w,
-                                                   const float* __restrict__ kg, int S, float eps,
-                                                   float* __restrict__ alpha, float* __restrict__ m_out,
-                                                   float* __restrict__ lse_out) {
-  constexpr int G = NB < 8 ? NB : 8;
-  constexpr int QP = 16 * MT;
-  constexpr int NP = NB < 4 ? 4 : NB;
-  typedef Red<MT, G> R;
-  extern __shared__ float lds[];
-  float* red = lds;
-  float* zb = lds + 2 * R::kSlot;  // [16 tokens][QP queries][NP sources]
+constexpr int kGroup = 4;  // sources scored per pass over the channels
 
+// One pass of part A for sources [g0, g0+G) followed by the fixed-order
+// reduction; wave 0 then stores z = Z / r(u) into zb[(t * QP + q) * np + i]
+// (ONEQ: only query 0, zb[t * np + i]).
+template <typename St, int MT, int G, bool PACKED, bool ONEQ>
+__device__ __forceinline__ void score_group(const St* src, int64_t stride, int64_t T, int d, const float* w,
+                                            const float* kg, const u32x4_t* pk, int S, float eps, int64_t tok0,
+                                            int g0, float* red, float* zb, int np) {
+  constexpr int QP = 16 * MT;
+  f32x4_t acc[MT][G];
+  float ss[G];
+  score_pass<St, MT, G, PACKED>(src, stride, T, d, w, kg, pk, S, tok0, g0, acc, ss);
+  Red<MT, G>::reduce(red, acc, ss);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int64_t tok0 = (int64_t)blockIdx.x * 16;
-
-  for (int g0 = 0; g0 < n; g0 += G) {
-    f32x4_t acc[MT][G];
-    float ss[G];
-    score_pass<St, MT, G>(src, n, stride, T, d, w, kg, S, tok0, g0, acc, ss);
-    R::reduce(red, acc, ss);
-    if (wave == 0) {
+  if ((threadIdx.x >> 6) == 0) {
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const int si = g0 + i;
-        if (si < n) {
-          const float r = sqrtf(ss[i] / (float)d + eps);
+    for (int i = 0; i < G; ++i) {
+      const float r = sqrtf(ss[i] / (float)d + eps);
+      if (ONEQ) {
+        if (grp == 0) zb[col * np + g0 + i] = acc[0][i][0] / r;  // row 0 of the MFMA output
+      } else {
 #pragma unroll
-          for (int m = 0; m < MT; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int q = m * 16 + grp * 4 + rr;
-              zb[(col * QP + q) * NP + si] = acc[m][i][rr] / r;
-            }
-        }
+          for (int rr = 0; rr < 4; ++rr) {
+            const int q = m * 16 + grp * 4 + rr;
+            zb[(col * QP + q) * np + g0 + i] = acc[m][i][rr] / r;
+          }
       }
     }
   }
+}
+
+// All n sources: full groups of kGroup, then one remainder group.
+template <typename St, int MT, bool PACKED, bool ONEQ>
+__device__ __forceinline__ void score_all(const St* src, int n, int64_t stride, int64_t T, int d, const float* w,
+                                          const float* kg, const u32x4_t* pk, int S, float eps, int64_t tok0,
+                                          float* red, float* zb, int np) {
+  int g0 = 0;
+  for (; g0 + kGroup <= n; g0 += kGroup)
+    score_group<St, MT, kGroup, PACKED, ONEQ>(src, stride, T, d, w, kg, pk, S, eps, tok0, g0, red, zb, np);
+  const int r = n - g0;
+  if (r == 1) score_group<St, MT, 1, PACKED, ONEQ>(src, stride, T, d, w, kg, pk, S, eps, tok0, g0, red, zb, np);
+  if (r == 2) score_group<St, MT, 2, PACKED, ONEQ>(src, stride, T, d, w, kg, pk, S, eps, tok0, g0, red, zb, np);
+  if (r == 3) score_group<St, MT, 3, PACKED, ONEQ>(src, stride, T, d, w, kg, pk, S, eps, tok0, g0, red, zb, np);
+}
+
+// ---------------------------------------------------------------------------
+// S >= 2, prologue: pack the tile's queries w (.) g once per call into MFMA
+// operand chunks ([16*MT][C] x 32 bytes, rows >= S zero).
+template <typename St, int MT>
+__global__ __launch_bounds__(256) void k_pack_queries(const float* __restrict__ w, const float* __restrict__ kg,
+                                                      int S, int d, u32x4_t* __restrict__ pk) {
+  const int C = d >> 3;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= 16 * MT * C) return;
+  const int q = idx / C, c = idx - q * C;
+  float qv[8];
+  if (q < S) {
+    load8(w + (int64_t)q * d + c * 8, qv);
+    if (kg) {
+      float gv[8];
+      load8(kg + (int64_t)q * d + c * 8, gv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] *= gv[e];
+    }
+  } else {
+    zero8(qv);
+  }
+  Mfma<St>::pack(qv, pk + (int64_t)idx * 2);
+}
+
+// S >= 2, first kernel: scores and softmax weights of a 16-token tile for up
+// to 32 queries.  The weights go to the workspace as alpha[t][q][i]
+// (i fastest), the statistics to m_out / lse_out.
+template <typename St, int MT>
+__global__ __launch_bounds__(256) void k_p1_scores(const St* __restrict__ src, int n, int64_t stride,
+                                                   int64_t T, int d, const u32x4_t* __restrict__ pk, int S,
+                                                   float eps, float* __restrict__ alpha,
+                                                   float* __restrict__ m_out, float* __restrict__ lse_out) {
+  constexpr int QP = 16 * MT;
+  extern __shared__ float lds[];
+  float* red = lds;
+  float* zb = lds + 2 * Red<MT, kGroup>::kSlot;  // [16 tokens][QP queries][n sources]
+  const int64_t tok0 = (int64_t)blockIdx.x * 16;
+  score_all<St, MT, true, false>(src, n, stride, T, d, nullptr, nullptr, pk, S, eps, tok0, red, zb, n);
   __syncthreads();
 
   // softmax over the n sources of every (token, query) pair
@@ -272,7 +383,7 @@ __global__ __launch_bounds__(256) void k_p1_scores(const St* __restrict__ src, i
     const int t = pidx / QP, q = pidx - t * QP;
     const int64_t tok = tok0 + t;
     if (q >= S || tok >= T) continue;
-    const float* row = zb + pidx * NP;
+    const float* row = zb + pidx * n;
     float mx = row[0];
     for (int i = 1; i < n; ++i) mx = fmaxf(mx, row[i]);
     float l = 0.f;
@@ -288,78 +399,72 @@ __global__ __launch_bounds__(256) void k_p1_scores(const St* __restrict__ src, i
 // one (token, group of 64 chunks) item at a time, so the weights are
 // wave-uniform and come in through scalar loads; every source chunk is used
 // by all S queries; the next item's source chunks are loaded before the
-// current item is computed.
-template <typename St, int NB>
-__device__ __forceinline__ void p1_issue(Chunk<St> (&s)[NB], int64_t item, int64_t items, int ngroups,
-                                         const St* __restrict__ src, int n, int64_t stride, int d, int C,
-                                         int lane) {
-  const int64_t t = item / ngroups;
-  const int c = (int)(item - t * ngroups) * 64 + lane;
-  const bool ok = item < items && c < C;
+// current item is computed.  N is the exact number of sources.
+template <typename St, int N>
+__device__ __forceinline__ void p1_issue(Chunk<St> (&s)[N], bool& ok, int64_t item, int64_t items, int ngroups,
+                                         const St* __restrict__ src, int64_t stride, int d, int C, int lane) {
+  const int64_t it = item < items ? item : items - 1;
+  const int64_t t = it / ngroups;
+  const int c0 = (int)(it - t * ngroups) * 64 + lane;
+  ok = c0 < C;
+  const int c = ok ? c0 : C - 1;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    if (ok && i < n) {
-      s[i].load(src + (int64_t)i * stride + t * d + c * 8);
-    } else {
-      s[i].zero();
-    }
-  }
+  for (int i = 0; i < N; ++i) s[i].load(src + (int64_t)i * stride + t * d + c * 8);
 }
 
-template <typename St, int NB>
-__device__ __forceinline__ void p1_emit(const Chunk<St> (&s)[NB], int64_t item, int ngroups, int n, int64_t T,
-                                        int d, int C, int lane, const float* __restrict__ alpha, int S,
+template <typename St, int N>
+__device__ __forceinline__ void p1_emit(const Chunk<St> (&s)[N], bool ok, int64_t item, int ngroups, int64_t T,
+                                        int d, int lane, const float* __restrict__ alpha, int S,
                                         St* __restrict__ out) {
   const int64_t t = item / ngroups;
   const int c = (int)(item - t * ngroups) * 64 + lane;
-  float b[NB][8];
+  float b[N][8];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) s[i].unpack(b[i]);
-  const float* al = alpha + t * S * n;
+  for (int i = 0; i < N; ++i) s[i].unpack(b[i]);
+  const float* al = alpha + t * S * N;
   for (int q = 0; q < S; ++q) {
     float o[8];
     zero8(o);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (i < n) {
-        const float a = al[q * n + i];
+    for (int i = 0; i < N; ++i) {
+      const float a = al[q * N + i];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = fmaf(a, b[i][e], o[e]);
-      }
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(a, b[i][e], o[e]);
     }
-    if (c < C) out8(out + ((int64_t)q * T + t) * d + c * 8, o);
+    if (ok) out8(out + ((int64_t)q * T + t) * d + c * 8, o);
   }
 }
 
-template <typename St, int NB>
-__global__ __launch_bounds__(256) void k_p1_out(const St* __restrict__ src, int n, int64_t stride, int64_t T,
-                                                int d, const float* __restrict__ alpha, int S,
-                                                St* __restrict__ out) {
+template <typename St, int N>
+__global__ __launch_bounds__(256) void k_p1_out(const St* __restrict__ src, int64_t stride, int64_t T, int d,
+                                                const float* __restrict__ alpha, int S, St* __restrict__ out) {
   const int C = d >> 3;
   const int ngroups = (C + 63) >> 6;
   const int64_t items = T * ngroups;
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * 4;
   int64_t item = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  Chunk<St> A[NB], B[NB];
-  p1_issue<St, NB>(A, item, items, ngroups, src, n, stride, d, C, lane);
+  Chunk<St> A[N], B[N];
+  bool okA, okB;
+  p1_issue<St, N>(A, okA, item, items, ngroups, src, stride, d, C, lane);
   while (item < items) {
-    p1_issue<St, NB>(B, item + nw, items, ngroups, src, n, stride, d, C, lane);
-    p1_emit<St, NB>(A, item, ngroups, n, T, d, C, lane, alpha, S, out);
+    p1_issue<St, N>(B, okB, item + nw, items, ngroups, src, stride, d, C, lane);
+    p1_emit<St, N>(A, okA, item, ngroups, T, d, lane, alpha, S, out);
     item += nw;
     if (item >= items) break;
-    p1_issue<St, NB>(A, item + nw, items, ngroups, src, n, stride, d, C, lane);
-    p1_emit<St, NB>(B, item, ngroups, n, T, d, C, lane, alpha, S, out);
+    p1_issue<St, N>(A, okA, item + nw, items, ngroups, src, stride, d, C, lane);
+    p1_emit<St, N>(B, okB, item, ngroups, T, d, lane, alpha, S, out);
     item += nw;
   }
 }
 
 // ---------------------------------------------------------------------------
-// S == 1: one query, up to 32 sources in groups of G, optional PreNorm of
-// the output (Full AttnRes sites and the final aggregation).
+// S == 1: one query, up to 32 sources, optional PreNorm of the output (Full
+// AttnRes sites and the final aggregation).  Part B walks the tile's tokens
+// with the whole workgroup (the PreNorm needs each token's full row).
 constexpr int kSingleNP = 32;
 
-template <typename St, int G>
+template <typename St>
 __global__ __launch_bounds__(256) void k_phase1_single(const St* __restrict__ src, int n, int64_t stride,
                                                        int64_t T, int d, const float* __restrict__ w,
                                                        const float* __restrict__ kg,
@@ -367,31 +472,12 @@ __global__ __launch_bounds__(256) void k_phase1_single(const St* __restrict__ sr
                                                        St* __restrict__ h_out, St* __restrict__ x_out,
                                                        float* __restrict__ m_out,
                                                        float* __restrict__ lse_out) {
-  typedef Red<1, G> R;
   extern __shared__ float lds[];
   float* red = lds;
-  float* zb = lds + 2 * R::kSlot;         // [16 tokens][kSingleNP sources]
-  float* red2 = zb + 16 * kSingleNP;      // 2 x 8 floats for the PreNorm reduction
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;
-  const int grp = lane >> 4;
+  float* zb = lds + 2 * Red<1, kGroup>::kSlot;  // [16 tokens][kSingleNP sources]
+  float* red2 = zb + 16 * kSingleNP;             // 2 x 8 floats for the PreNorm reduction
   const int64_t tok0 = (int64_t)blockIdx.x * 16;
-
-  for (int g0 = 0; g0 < n; g0 += G) {
-    f32x4_t acc[1][G];
-    float ss[G];
-    score_pass<St, 1, G>(src, n, stride, T, d, w, kg, 1, tok0, g0, acc, ss);
-    R::reduce(red, acc, ss);
-    if (wave == 0 && grp == 0) {  // row 0 of the MFMA output = query 0
-#pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const int si = g0 + i;
-        if (si < n) zb[col * kSingleNP + si] = acc[0][i][0] / sqrtf(ss[i] / (float)d + eps);
-      }
-    }
-  }
+  score_all<St, 1, false, true>(src, n, stride, T, d, w, kg, nullptr, 1, eps, tok0, red, zb, kSingleNP);
   __syncthreads();
   if (threadIdx.x < 16) {
     float* row = zb + threadIdx.x * kSingleNP;
@@ -489,57 +575,72 @@ static hipError_t set_lds(Kern k, size_t bytes) {
                              (int)bytes);
 }
 
-template <typename St, int MT, int NB>
-static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, int d, const float* w,
-                            const float* kg, int S, float eps, void* out, float* m_out, float* lse_out,
-                            float* alpha, hipStream_t stream) {
-  constexpr int G = NB < 8 ? NB : 8;
-  constexpr int NP = NB < 4 ? 4 : NB;
-  const size_t lds = sizeof(float) * (2 * Red<MT, G>::kSlot + 16 * 16 * MT * NP);
-  auto ks = k_p1_scores<St, MT, NB>;
-  hipError_t e = set_lds(ks, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ks, dim3((unsigned)((T + 15) / 16)), dim3(256), lds, stream, static_cast<const St*>(src),
-                     n, stride, T, d, w, kg, S, eps, alpha, m_out, lse_out);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+template <typename St, int N>
+static hipError_t run_out(const void* src, int64_t stride, int64_t T, int d, const float* al, int S, void* out,
+                          hipStream_t stream) {
   const int64_t items = T * (int64_t)(((d >> 3) + 63) >> 6);
   const int64_t wgs = (items + 3) / 4;
   const int64_t cap = (int64_t)device_cu_count() * 4;
-  hipLaunchKernelGGL((k_p1_out<St, NB>), dim3((unsigned)(wgs < cap ? wgs : cap)), dim3(256), 0, stream,
-                     static_cast<const St*>(src), n, stride, T, d, alpha, S, static_cast<St*>(out));
+  hipLaunchKernelGGL((k_p1_out<St, N>), dim3((unsigned)(wgs < cap ? wgs : cap)), dim3(256), 0, stream,
+                     static_cast<const St*>(src), stride, T, d, al, S, static_cast<St*>(out));
   return hipGetLastError();
 }
 
+template <typename St>
+static hipError_t pick_out(int n, const void* src, int64_t stride, int64_t T, int d, const float* al, int S,
+                           void* out, hipStream_t stream) {
+  switch (n) {
+#define ATTNRES_CASE(N_) \
+  case N_:               \
+    return run_out<St, N_>(src, stride, T, d, al, S, out, stream);
+    ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4) ATTNRES_CASE(5) ATTNRES_CASE(6)
+    ATTNRES_CASE(7) ATTNRES_CASE(8) ATTNRES_CASE(9) ATTNRES_CASE(10) ATTNRES_CASE(11) ATTNRES_CASE(12)
+    ATTNRES_CASE(13) ATTNRES_CASE(14) ATTNRES_CASE(15) ATTNRES_CASE(16)
+#undef ATTNRES_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename St, int MT>
-static hipError_t pick_nb(const void* src, int n, int64_t stride, int64_t T, int d, const float* w,
-                          const float* kg, int S, float eps, void* out, float* m_out, float* lse_out,
-                          float* alpha, hipStream_t stream) {
-  if (n <= 1) return run_multi<St, MT, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
-  if (n <= 2) return run_multi<St, MT, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
-  if (n <= 4) return run_multi<St, MT, 4>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
-  if (n <= 8) return run_multi<St, MT, 8>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
-  return run_multi<St, MT, 16>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
+static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, int d, const float* w,
+                            const float* kg, int S, float eps, void* out, float* m_out, float* lse_out,
+                            float* ws, hipStream_t stream) {
+  // workspace: packed queries first, then the softmax weights
+  u32x4_t* pk = reinterpret_cast<u32x4_t*>(ws);
+  float* al = ws + (int64_t)16 * MT * (d >> 3) * 8;
+  const int npk = 16 * MT * (d >> 3);
+  hipLaunchKernelGGL((k_pack_queries<St, MT>), dim3((unsigned)((npk + 255) / 256)), dim3(256), 0, stream, w, kg,
+                     S, d, pk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = sizeof(float) * (2 * Red<MT, kGroup>::kSlot + 16 * 16 * MT * n);
+  auto ks = k_p1_scores<St, MT>;
+  e = set_lds(ks, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ks, dim3((unsigned)((T + 15) / 16)), dim3(256), lds, stream, static_cast<const St*>(src),
+                     n, stride, T, d, pk, S, eps, al, m_out, lse_out);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return pick_out<St>(n, src, stride, T, d, al, S, out, stream);
 }
 
 hipError_t launch_phase1_multi(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
                                const float* w, const float* kg, int S, float eps, void* out,
-                               float* m_out, float* lse_out, float* alpha, hipStream_t stream) {
+                               float* m_out, float* lse_out, float* ws, hipStream_t stream) {
   if (dt == kBF16) {
-    if (S <= 16)
-      return pick_nb<bf16_t, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
-    return pick_nb<bf16_t, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
+    if (S <= 16) return run_multi<bf16_t, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, ws, stream);
+    return run_multi<bf16_t, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, ws, stream);
   }
-  if (S <= 16) return pick_nb<float, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
-  return pick_nb<float, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, alpha, stream);
+  if (S <= 16) return run_multi<float, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, ws, stream);
+  return run_multi<float, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, ws, stream);
 }
 
-template <typename St, int G>
+template <typename St>
 static hipError_t run_single(const void* src, int n, int64_t stride, int64_t T, int d, const float* w,
                              const float* kg, const float* gamma, float eps, void* h_out, void* x_out,
                              float* m_out, float* lse_out, hipStream_t stream) {
-  const size_t lds = sizeof(float) * (2 * Red<1, G>::kSlot + 16 * kSingleNP + 16);
-  auto kern = k_phase1_single<St, G>;
+  const size_t lds = sizeof(float) * (2 * Red<1, kGroup>::kSlot + 16 * kSingleNP + 16);
+  auto kern = k_phase1_single<St>;
   hipError_t e = set_lds(kern, lds);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((T + 15) / 16));
@@ -548,23 +649,13 @@ static hipError_t run_single(const void* src, int n, int64_t stride, int64_t T, 
   return hipGetLastError();
 }
 
-template <typename St>
-static hipError_t pick_g(const void* src, int n, int64_t stride, int64_t T, int d, const float* w,
-                         const float* kg, const float* gamma, float eps, void* h_out, void* x_out,
-                         float* m_out, float* lse_out, hipStream_t stream) {
-  if (n <= 1) return run_single<St, 1>(src, n, stride, T, d, w, kg, gamma, eps, h_out, x_out, m_out, lse_out, stream);
-  if (n <= 2) return run_single<St, 2>(src, n, stride, T, d, w, kg, gamma, eps, h_out, x_out, m_out, lse_out, stream);
-  if (n <= 4) return run_single<St, 4>(src, n, stride, T, d, w, kg, gamma, eps, h_out, x_out, m_out, lse_out, stream);
-  return run_single<St, 8>(src, n, stride, T, d, w, kg, gamma, eps, h_out, x_out, m_out, lse_out, stream);
-}
-
 hipError_t launch_phase1_single(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
                                 const float* w, const float* kg, const float* gamma, float eps,
                                 void* h_out, void* x_out, float* m_out, float* lse_out,
                                 hipStream_t stream) {
   if (dt == kBF16)
-    return pick_g<bf16_t>(src, n, stride, T, d, w, kg, gamma, eps, h_out, x_out, m_out, lse_out, stream);
-  return pick_g<float>(src, n, stride, T, d, w, kg, gamma, eps, h_out, x_out, m_out, lse_out, stream);
+    return run_single<bf16_t>(src, n, stride, T, d, w, kg, gamma, eps, h_out, x_out, m_out, lse_out, stream);
+  return run_single<float>(src, n, stride, T, d, w, kg, gamma, eps, h_out, x_out, m_out, lse_out, stream);
 }
 
 }  // namespace attnres

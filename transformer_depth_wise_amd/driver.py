@@ -77,7 +77,7 @@ class BlockAttnRes:
         self.m1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
         self.lse1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
         n_max = 1 + self.n_given + max(0, len(self.block_sizes) - 1)
-        ws = _lib.attnres_phase1_workspace_bytes(T, n_max, smax) if T > 0 else 0
+        ws = _lib.attnres_phase1_workspace_bytes(T, d, n_max, smax) if T > 0 else 0
         self.workspace = torch.empty((max(ws, 16) // 4,), dtype=torch.float32, device=dev)
         self.partial = torch.empty((T, d), dtype=torch.float32, device=dev)
         self.x = torch.empty((max(1, x_ring), T, d), dtype=dtype, device=dev)
@@ -86,6 +86,20 @@ class BlockAttnRes:
         self.lse_final = torch.empty((T,), dtype=torch.float32, device=dev)
 
     # ------------------------------------------------------------------ bytes
+    def buffer_bytes(self) -> Dict[str, int]:
+        """Device memory held by this pass's buffers (the AttnRes working set)."""
+        out = {"block_reps": self.reps.numel() * self.reps.element_size(),
+               "phase1_out": self.o1.numel() * self.o1.element_size(),
+               "phase1_stats": 2 * self.m1.numel() * 4,
+               "phase1_workspace": self.workspace.numel() * 4,
+               "partial_sum": self.partial.numel() * 4,
+               "prenorm_out": self.x.numel() * self.x.element_size(),
+               "final": self.h_final.numel() * self.h_final.element_size() + self.lse_final.numel() * 4}
+        if self.h is not None:
+            out["h"] = self.h.numel() * self.h.element_size()
+        out["total"] = sum(out.values())
+        return out
+
     def _row(self, dt=None) -> int:
         return self.T * self.d * _esize(self.dtype if dt is None else dt)
 
