@@ -277,7 +277,7 @@ def main() -> int:
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "sublayers": w.L,
-                   "blocks": list(w.block_sizes), "storage": w.dtype, "partial_sum": "f32",
+                   "blocks": list(w.block_sizes), "storage": w.dtype, "partial_sum": st.partial_format,
                    "parallelism": "single GPU"},
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),

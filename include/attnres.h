@@ -64,7 +64,12 @@ typedef enum {
     ATTNRES_EHIP = 5     /* the HIP runtime reported an error at launch */
 } attnres_status_t;
 
-typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1 } attnres_dtype_t;
+/* Storage formats.  ATTNRES_P24 is only valid for the running partial sum
+ * of a block (partial_in / partial_out): the fp32 value rounded to nearest
+ * even at bit 8 of its encoding and kept as its upper 24 bits, stored as two
+ * planes -- T*d 16-bit upper halves followed by T*d bytes holding bits 8..15
+ * (3 bytes per element; full fp32 range, relative step 2^-16). */
+typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1, ATTNRES_P24 = 2 } attnres_dtype_t;
 
 /* Largest supported values. */
 #define ATTNRES_MAX_D 16384
@@ -114,10 +119,11 @@ int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int6
  *   If sublayer_prev == NULL (first sublayer of the block): h = o.
  *   Otherwise the partial sum is
  *       p = (partial_in or 0) + sublayer_prev        (fp32 arithmetic)
- *   partial_in: [T][d] of dtype partial_dt (NULL = zero);
- *   sublayer_prev: [T][d] of dtype dt (the previous sublayer's output).
- *   p is written to partial_out ([T][d] fp32, NULL = not stored; it may be
- *   the same pointer as partial_in when partial_dt == ATTNRES_F32).
+ *   partial_in: [T][d] in format partial_dt (F32, P24, or dt itself for a
+ *   sublayer output; NULL = zero); sublayer_prev: [T][d] of dtype dt (the
+ *   previous sublayer's output).  p is written to partial_out in format
+ *   partial_out_dt (F32 or P24; NULL = not stored); partial_out may be the
+ *   same pointer as partial_in when both formats are the same (in place).
  *   Merge: zc = w^T(key_gain (.) p / r(p)), M = max(lse, zc),
  *       h = (e^{lse-M} o + e^{zc-M} p) / (e^{lse-M} + e^{zc-M}).
  *   PreNorm: x = prenorm_gain (.) h / r(h)  (prenorm_gain NULL = ones).
@@ -128,7 +134,8 @@ int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int6
 attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d,
                                       const void* p1_out, const float* p1_lse,
                                       attnres_dtype_t partial_dt, const void* partial_in,
-                                      const void* sublayer_prev, float* partial_out,
+                                      const void* sublayer_prev,
+                                      attnres_dtype_t partial_out_dt, void* partial_out,
                                       const float* w, const float* key_gain,
                                       const float* prenorm_gain, float eps,
                                       void* h_out, void* x_out, void* stream);
@@ -153,8 +160,9 @@ attnres_status_t attnres_full(attnres_dtype_t dt,
 /*
  * Block completion ("Attention Residuals" notes, section 8: b_n is the sum of
  * the block's sublayer outputs):  out = (partial_in or 0) + v.
- *   partial_in: [T][d] dtype partial_dt (NULL = zero); v, out: [T][d] dtype dt.
- *   out may be the same pointer as partial_in when partial_dt == dt.
+ *   partial_in: [T][d] in format partial_dt (F32, P24 or dt; NULL = zero);
+ *   v, out: [T][d] dtype dt.  out may be the same pointer as partial_in when
+ *   partial_dt == dt.
  */
 attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t d,
                                           attnres_dtype_t partial_dt, const void* partial_in,

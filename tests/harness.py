@@ -66,14 +66,14 @@ def block_inputs(w: synth.Workload, device, t0: int = 0, t1: Optional[int] = Non
 
 
 def run_block_parity(w: synth.Workload, samples: Optional[Sequence[int]] = None, device="cuda",
-                     keep_h: bool = True, x_ring: int = 4) -> Dict[str, float]:
+                     keep_h: bool = True, x_ring: int = 4, partial: Optional[str] = None) -> Dict[str, float]:
     """Block AttnRes on the GPU vs the oracle on sampled tokens.  Returns the
     worst error per output kind (already asserted against the bar)."""
     dev = torch.device(device)
     emb, given, v = block_inputs(w, dev)
     prm = synth.params(w, dev)
     st = BlockAttnRes(w.T, w.d, w.block_sizes, w.torch_dtype, n_given=w.n_given, eps=w.eps, device=dev,
-                      keep_h=keep_h, x_ring=x_ring, final_site=w.final_site)
+                      keep_h=keep_h, x_ring=x_ring, final_site=w.final_site, partial=partial)
     st.reps[0].copy_(emb)
     for n, b in enumerate(given):
         st.reps[1 + n].copy_(b)

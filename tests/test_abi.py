@@ -45,6 +45,8 @@ def test_binding_uses_the_same_names():
 
 
 A = 1 << 20  # a 16-byte aligned fake device address; never dereferenced here
+# Every call below must fail validation or have T == 0: a call that passed
+# validation with these fake pointers would launch a kernel on them.
 EINVAL, EDTYPE, EALIGN, EALIAS = 1, 2, 3, 4
 
 
@@ -52,12 +54,18 @@ def p(x):
     return ctypes.c_void_p(x)
 
 
+def checked(rc):
+    # ATTNRES_EHIP here means validation let fake pointers through to a launch
+    assert rc != 5, "validation passed fake pointers to a kernel launch"
+    return rc
+
+
 def phase1(lib, dt=1, src=A, n=3, stride=4096 * 64, T=4096, d=64, w=8 * A, kg=None, S=4, eps=1e-6,
            out=16 * A, m=None, lse=24 * A, ws=32 * A, ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = lib.attnres_phase1_workspace_bytes(T, d, n, S)
-    return lib.attnres_phase1(dt, p(src), n, stride, T, d, p(w), p(kg), S, eps, p(out), p(m), p(lse), p(ws),
-                              ws_bytes, None)
+    return checked(lib.attnres_phase1(dt, p(src), n, stride, T, d, p(w), p(kg), S, eps, p(out), p(m), p(lse),
+                                      p(ws), ws_bytes, None))
 
 
 def test_phase1_validation(lib):
@@ -89,10 +97,10 @@ def test_phase1_validation(lib):
     assert phase1(lib, T=0, src=None, out=None, lse=None) == 0
 
 
-def merge(lib, dt=1, T=1024, d=64, o=A, lse=2 * A, pdt=0, pin=None, v=None, pout=None, w=3 * A, kg=None,
-          gm=None, h=None, x=4 * A):
-    return lib.attnres_phase2_merge(dt, T, d, p(o), p(lse), pdt, p(pin), p(v), p(pout), p(w), p(kg), p(gm),
-                                    1e-6, p(h), p(x), None)
+def merge(lib, dt=1, T=1024, d=64, o=A, lse=2 * A, pdt=0, pin=None, v=None, podt=0, pout=None, w=3 * A,
+          kg=None, gm=None, h=None, x=4 * A):
+    return checked(lib.attnres_phase2_merge(dt, T, d, p(o), p(lse), pdt, p(pin), p(v), podt, p(pout), p(w),
+                                            p(kg), p(gm), 1e-6, p(h), p(x), None))
 
 
 def test_merge_validation(lib):
@@ -103,28 +111,37 @@ def test_merge_validation(lib):
     assert merge(lib, d=20) == EALIGN
     assert merge(lib, x=A + 64) == EALIAS                  # output over the phase-1 input
     assert merge(lib, v=6 * A, pin=5 * A, pout=5 * A + 16) == EALIAS   # shifted in-place
-    assert merge(lib, v=6 * A, pin=5 * A, pout=5 * A, pdt=1) == EALIAS  # in place needs fp32
+    assert merge(lib, v=6 * A, pin=5 * A, pout=5 * A, pdt=1) == EALIAS  # in place needs one format
+    assert merge(lib, v=6 * A, pin=5 * A, pout=5 * A, pdt=2, podt=0) == EALIAS
+    assert merge(lib, T=0, v=6 * A, pin=5 * A, pout=5 * A, pdt=2, podt=2) == 0  # P24 in place
+    assert merge(lib, v=6 * A, pin=5 * A, podt=1, pout=7 * A) == EDTYPE  # partial_out is F32 or P24
+    assert merge(lib, dt=2) == EDTYPE                                  # P24 is not a row format
+    assert merge(lib, dt=0, pdt=1, v=6 * A, pin=5 * A) == EDTYPE        # bf16 partial with fp32 rows
+    # a P24 partial spans 3 bytes per element: the low-byte plane starts 1024 x 64 x 2 bytes in
+    assert merge(lib, v=7 * A + 1024 * 64 * 2, pin=5 * A, pdt=2, pout=7 * A, podt=2) == EALIAS
     assert merge(lib, T=0) == 0
     assert merge(lib, T=0, o=None, lse=None, x=None) == 0               # empty: pointers unused
 
 
 def test_full_and_accumulate_validation(lib):
-    f = lambda **k: lib.attnres_full(k.get("dt", 1), p(k.get("src", A)), k.get("n", 2), k.get("stride", 64 * 64),
+    f = lambda **k: checked(lib.attnres_full(k.get("dt", 1), p(k.get("src", A)), k.get("n", 2), k.get("stride", 64 * 64),
                                      k.get("T", 64), k.get("d", 64), p(k.get("w", 2 * A)), None, None, 1e-6,
-                                     p(k.get("h", 3 * A)), p(k.get("x")), p(k.get("lse")), None)
+                                     p(k.get("h", 3 * A)), p(k.get("x")), p(k.get("lse")), None))
     assert f(n=0) == EINVAL
     assert f(n=33) == EINVAL
     assert f(h=None) == EINVAL
     assert f(h=A + 128) == EALIAS
     assert f(d=4) == EALIGN
     assert f(T=0) == 0
-    acc = lambda **k: lib.attnres_block_accumulate(k.get("dt", 1), k.get("T", 64), k.get("d", 64), k.get("pdt", 0),
-                                                   p(k.get("pin")), p(k.get("v", A)), p(k.get("out", 2 * A)), None)
+    acc = lambda **k: checked(lib.attnres_block_accumulate(k.get("dt", 1), k.get("T", 64), k.get("d", 64), k.get("pdt", 0),
+                                                   p(k.get("pin")), p(k.get("v", A)), p(k.get("out", 2 * A)), None))
     assert acc(v=None) == EINVAL
     assert acc(out=A) == EALIAS
     assert acc(pin=2 * A, pdt=0) == EALIAS          # in place only with the same dtype
     assert acc(T=0, v=None, out=None) == 0
     assert acc(dt=3) == EDTYPE
+    assert acc(dt=2) == EDTYPE                      # P24 only for the partial
+    assert acc(T=0, pin=5 * A, pdt=2) == 0
 
 
 def test_status_strings(lib):

@@ -55,11 +55,46 @@ def test_decode_block_bf16_all_tokens():
     _say("worst", worst)
 
 
-def test_prefill_chunk_bf16_sampled():
+@pytest.mark.parametrize("partial", ["p24", "f32"])
+def test_prefill_chunk_bf16_sampled(partial):
     w = synth.WORKLOADS["prefill_chunk_bf16"]
-    _say("case prefill_chunk_bf16 T=%d d=%d blocks=%s (64 sampled tokens)" % (w.T, w.d, w.block_sizes))
-    worst = run_block_parity(w, samples=synth.sample_tokens(w.T, 64), keep_h=True)
+    _say("case prefill_chunk_bf16 T=%d d=%d blocks=%s partial=%s (64 sampled tokens)"
+         % (w.T, w.d, w.block_sizes, partial))
+    worst = run_block_parity(w, samples=synth.sample_tokens(w.T, 64), keep_h=True, partial=partial)
     _say("worst", worst)
+
+
+def _p24_emulate(x: np.ndarray) -> np.ndarray:
+    """The 24-bit split format's value of fp32 x: round to nearest even at
+    bit 8 of the encoding, keep the upper 24 bits."""
+    u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7F + ((u >> 8) & 1)) & 0xFFFFFF00
+    return r.astype(np.uint32).view(np.float32)
+
+
+def test_p24_partial_roundtrip_is_exact():
+    _say("case P24 partial round trip")
+    dev = torch.device("cuda")
+    T, d = 37, 1032
+    pin = (torch.randn((T, d), device=dev) * torch.logspace(-3, 3, d, device=dev)).float()
+    pin[0, :8] = torch.tensor([0.0, -0.0, 1.0, -1.0, 1.0 + 2 ** -16, 1.0 + 3 * 2 ** -17, 3e-38, -65504.0])
+    zeros = torch.zeros((T, d), dtype=torch.float32, device=dev)
+    o = torch.randn((T, d), device=dev)
+    lse = torch.zeros((T,), device=dev)
+    p24 = tdw._lib.p24_partial(T, d, dev)
+    x = torch.empty((T, d), device=dev)
+    # p = pin + 0, stored as P24
+    tdw.attnres_phase2_merge(o, lse, pin, zeros, p24, torch.zeros(d, device=dev), None, None, 1e-6, None, x)
+    back = torch.empty((T, d), device=dev)
+    tdw.attnres_block_accumulate(p24, zeros, back)  # P24 -> fp32 + 0
+    torch.cuda.synchronize()
+    got, want = back.cpu().numpy(), _p24_emulate(pin.cpu().numpy())
+    # value comparison: the kernels compute pin + 0.0, which turns -0.0 into +0.0
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "P24 mismatch at %s: got %r want %r (input %r)" % (
+        bad[:4].tolist(), got[tuple(bad[0])], want[tuple(bad[0])], pin.cpu().numpy()[tuple(bad[0])])
+    rel = np.abs(back.cpu().numpy() - pin.cpu().numpy()) / np.maximum(np.abs(pin.cpu().numpy()), 1e-30)
+    assert rel.max() <= 2.0 ** -16
 
 
 # -------------------------------------------------- ragged and edge shapes

@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattnres.so")
 
-F32, BF16 = 0, 1
+F32, BF16, P24 = 0, 1, 2
 ATTNRES_MAX_D = 16384
 ATTNRES_MAX_SOURCES = 32
 ATTNRES_MAX_SOURCES_MULTI = 16
@@ -48,7 +48,7 @@ def load(path: Optional[str] = None):
     lib.attnres_phase1.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V, I, V]
     lib.attnres_phase1_workspace_bytes.argtypes = [I, I, I, I]
     lib.attnres_phase1_workspace_bytes.restype = ctypes.c_int64
-    lib.attnres_phase2_merge.argtypes = [E, I, I, V, V, E, V, V, V, V, V, V, F, V, V, V]
+    lib.attnres_phase2_merge.argtypes = [E, I, I, V, V, E, V, V, E, V, V, V, V, F, V, V, V]
     lib.attnres_full.argtypes = [E, V, I, I, I, I, V, V, V, F, V, V, V, V]
     lib.attnres_block_accumulate.argtypes = [E, I, I, E, V, V, V, V]
     for fn in ("attnres_phase1", "attnres_phase2_merge", "attnres_full", "attnres_block_accumulate"):
@@ -64,11 +64,20 @@ def status_string(code: int) -> str:
 
 
 def dtype_code(t: torch.dtype) -> int:
+    """float32 -> F32, bfloat16 -> BF16; a uint8 tensor holds a partial sum in
+    the 24-bit split format (P24, 3 bytes per element)."""
     if t == torch.float32:
         return F32
     if t == torch.bfloat16:
         return BF16
-    raise TypeError("unsupported storage dtype %s (float32 or bfloat16)" % t)
+    if t == torch.uint8:
+        return P24
+    raise TypeError("unsupported storage dtype %s (float32, bfloat16, or uint8 for a P24 partial)" % t)
+
+
+def p24_partial(T: int, d: int, device) -> torch.Tensor:
+    """An uninitialised partial-sum buffer in the P24 format."""
+    return torch.empty((3 * T * d,), dtype=torch.uint8, device=device)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -113,12 +122,14 @@ def attnres_phase2_merge(p1_out: torch.Tensor, p1_lse: torch.Tensor, partial_in:
                          w: torch.Tensor, key_gain: Optional[torch.Tensor], prenorm_gain: Optional[torch.Tensor],
                          eps: float, h_out: Optional[torch.Tensor], x_out: Optional[torch.Tensor],
                          stream=None) -> None:
-    """p1_out: [T, d]; p1_lse: [T]; partial_in: [T, d] fp32 or storage dtype;
-    sublayer_prev: [T, d]; partial_out: [T, d] fp32; w, key_gain, prenorm_gain: [d]."""
+    """p1_out: [T, d]; p1_lse: [T]; partial_in: [T, d] fp32 / storage dtype, or
+    a P24 buffer; sublayer_prev: [T, d]; partial_out: [T, d] fp32 or a P24
+    buffer; w, key_gain, prenorm_gain: [d]."""
     T, d = p1_out.shape
     pdt = dtype_code(partial_in.dtype) if partial_in is not None else F32
+    podt = dtype_code(partial_out.dtype) if partial_out is not None else F32
     rc = load().attnres_phase2_merge(dtype_code(p1_out.dtype), T, d, _ptr(p1_out), _ptr(p1_lse), pdt,
-                                     _ptr(partial_in), _ptr(sublayer_prev), _ptr(partial_out), _ptr(w),
+                                     _ptr(partial_in), _ptr(sublayer_prev), podt, _ptr(partial_out), _ptr(w),
                                      _ptr(key_gain), _ptr(prenorm_gain), eps, _ptr(h_out), _ptr(x_out),
                                      _stream(stream))
     _check("attnres_phase2_merge", rc)
@@ -137,7 +148,7 @@ def attnres_full(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optio
 
 def attnres_block_accumulate(partial_in: Optional[torch.Tensor], v: torch.Tensor, out: torch.Tensor,
                              stream=None) -> None:
-    """out = (partial_in or 0) + v; all [T, d]."""
+    """out = (partial_in or 0) + v; all [T, d] (partial_in may be a P24 buffer)."""
     T, d = v.shape
     pdt = dtype_code(partial_in.dtype) if partial_in is not None else F32
     rc = load().attnres_block_accumulate(dtype_code(v.dtype), T, d, pdt, _ptr(partial_in), _ptr(v), _ptr(out),

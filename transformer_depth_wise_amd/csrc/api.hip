@@ -42,9 +42,17 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-int64_t esize(attnres_dtype_t dt) { return dt == ATTNRES_F32 ? 4 : 2; }
+int64_t esize(attnres_dtype_t dt) { return dt == ATTNRES_F32 ? 4 : dt == ATTNRES_P24 ? 3 : 2; }
 
+// row storage: F32 or BF16; a partial sum may also be P24
 bool dtype_ok(attnres_dtype_t dt) { return dt == ATTNRES_F32 || dt == ATTNRES_BF16; }
+bool partial_ok(attnres_dtype_t pdt, attnres_dtype_t dt) {
+  return pdt == ATTNRES_F32 || pdt == ATTNRES_P24 || pdt == dt;
+}
+
+Dtype kind_of(attnres_dtype_t dt) {
+  return dt == ATTNRES_F32 ? attnres::kF32 : dt == ATTNRES_P24 ? attnres::kP24 : attnres::kBF16;
+}
 
 attnres_status_t check_d(int64_t d) {
   if (d <= 0 || d > ATTNRES_MAX_D) return ATTNRES_EINVAL;
@@ -120,7 +128,7 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_s
   if (overlaps(ro, rl) || overlaps(ro, rm) || overlaps(rl, rm)) return ATTNRES_EALIAS;
   if (overlaps(rws, ro) || overlaps(rws, rl) || overlaps(rws, rm)) return ATTNRES_EALIAS;
 
-  const Dtype kdt = dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
+  const Dtype kdt = kind_of(dt);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (S == 1)
     return hip_status(attnres::launch_phase1_single(kdt, src, (int)n_src, src_stride, T, (int)d, w, key_gain,
@@ -139,10 +147,11 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_s
 
 attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, const void* p1_out,
                                       const float* p1_lse, attnres_dtype_t partial_dt, const void* partial_in,
-                                      const void* sublayer_prev, float* partial_out, const float* w,
-                                      const float* key_gain, const float* prenorm_gain, float eps, void* h_out,
-                                      void* x_out, void* stream) {
-  if (!dtype_ok(dt) || !dtype_ok(partial_dt)) return ATTNRES_EDTYPE;
+                                      const void* sublayer_prev, attnres_dtype_t partial_out_dt, void* partial_out,
+                                      const float* w, const float* key_gain, const float* prenorm_gain, float eps,
+                                      void* h_out, void* x_out, void* stream) {
+  if (!dtype_ok(dt) || !partial_ok(partial_dt, dt)) return ATTNRES_EDTYPE;
+  if (partial_out_dt != ATTNRES_F32 && partial_out_dt != ATTNRES_P24) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
   if (T < 0 || !(eps >= 0.f)) return ATTNRES_EINVAL;
@@ -157,25 +166,25 @@ attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, 
   const Range r_o = range_of(p1_out, rows * es), r_l = range_of(p1_lse, T * 4);
   const Range r_pi = partial_in ? range_of(partial_in, rows * esize(partial_dt)) : Range{0, 0};
   const Range r_v = sublayer_prev ? range_of(sublayer_prev, rows * es) : Range{0, 0};
-  const Range r_po = partial_out ? range_of(partial_out, rows * 4) : Range{0, 0};
+  const Range r_po = partial_out ? range_of(partial_out, rows * esize(partial_out_dt)) : Range{0, 0};
   const Range r_w = w ? range_of(w, d * 4) : Range{0, 0};
   const Range r_g = key_gain ? range_of(key_gain, d * 4) : Range{0, 0};
   const Range r_gm = prenorm_gain ? range_of(prenorm_gain, d * 4) : Range{0, 0};
   const Range r_h = h_out ? range_of(h_out, rows * es) : Range{0, 0};
   const Range r_x = x_out ? range_of(x_out, rows * es) : Range{0, 0};
-  // partial_out may be exactly partial_in (fp32, element-wise in place); no other overlap
-  const bool in_place = partial_out && partial_in == static_cast<const void*>(partial_out) && partial_dt == ATTNRES_F32;
+  // partial_out may be exactly partial_in (same format, element-wise in place); no other overlap
+  const bool in_place = partial_out && partial_in == static_cast<const void*>(partial_out) &&
+                        partial_dt == partial_out_dt;
   for (Range o : {r_h, r_x, r_po})
     for (Range i : {r_o, r_l, r_pi, r_v, r_w, r_g, r_gm}) {
       if (in_place && o.lo == r_po.lo && o.hi == r_po.hi && i.lo == r_pi.lo && i.hi == r_pi.hi) continue;
       if (overlaps(o, i)) return ATTNRES_EALIAS;
     }
   if (overlaps(r_h, r_x) || overlaps(r_h, r_po) || overlaps(r_x, r_po)) return ATTNRES_EALIAS;
-  const Dtype kdt = dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
-  const Dtype kpdt = partial_dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
-  return hip_status(attnres::launch_merge(kdt, T, (int)d, p1_out, p1_lse, kpdt, partial_in, sublayer_prev,
-                                          partial_out, w, key_gain, x_out ? prenorm_gain : nullptr, eps, h_out,
-                                          x_out, static_cast<hipStream_t>(stream)));
+  return hip_status(attnres::launch_merge(kind_of(dt), T, (int)d, p1_out, p1_lse, kind_of(partial_dt), partial_in,
+                                          sublayer_prev, kind_of(partial_out_dt), partial_out, w, key_gain,
+                                          x_out ? prenorm_gain : nullptr, eps, h_out, x_out,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 attnres_status_t attnres_full(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride, int64_t T,
@@ -203,7 +212,7 @@ attnres_status_t attnres_full(attnres_dtype_t dt, const void* src, int64_t n_src
     for (Range i : {rs, rw, rg, rgm})
       if (overlaps(o, i)) return ATTNRES_EALIAS;
   if (overlaps(rh, rx) || overlaps(rh, rl) || overlaps(rx, rl)) return ATTNRES_EALIAS;
-  const Dtype kdt = dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
+  const Dtype kdt = kind_of(dt);
   return hip_status(attnres::launch_phase1_single(kdt, src, (int)n_src, src_stride, T, (int)d, w, key_gain,
                                                   prenorm_gain, eps, h_out, x_out, nullptr, lse_out,
                                                   static_cast<hipStream_t>(stream)));
@@ -211,7 +220,7 @@ attnres_status_t attnres_full(attnres_dtype_t dt, const void* src, int64_t n_src
 
 attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t d, attnres_dtype_t partial_dt,
                                           const void* partial_in, const void* v, void* out, void* stream) {
-  if (!dtype_ok(dt) || !dtype_ok(partial_dt)) return ATTNRES_EDTYPE;
+  if (!dtype_ok(dt) || !partial_ok(partial_dt, dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
   if (T < 0) return ATTNRES_EINVAL;
@@ -226,9 +235,7 @@ attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t
   if (overlaps(ro, rv)) return ATTNRES_EALIAS;
   const bool in_place = partial_in == out && partial_dt == dt;
   if (!in_place && overlaps(ro, rp)) return ATTNRES_EALIAS;
-  const Dtype kdt = dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
-  const Dtype kpdt = partial_dt == ATTNRES_F32 ? attnres::kF32 : attnres::kBF16;
-  return hip_status(attnres::launch_accumulate(kdt, T, (int)d, kpdt, partial_in, v, out,
+  return hip_status(attnres::launch_accumulate(kind_of(dt), T, (int)d, kind_of(partial_dt), partial_in, v, out,
                                                static_cast<hipStream_t>(stream)));
 }
 

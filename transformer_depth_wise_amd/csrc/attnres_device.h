@@ -12,6 +12,13 @@ struct bf16_t {
   unsigned short bits;
 };
 
+// Storage tag for the 24-bit split format of a block's running partial sum:
+// a plane of T*d 16-bit upper halves, then a plane of T*d bytes with bits
+// 8..15 of the fp32 encoding rounded to nearest even at bit 8.
+struct p24_t {
+  unsigned char byte;
+};
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -75,13 +82,20 @@ __device__ __forceinline__ void zero8(float (&v)[8]) {
 // Chunk<T> keeps 8 elements in their storage format so that loads for the
 // next token or row chunk can be in flight while the current one is used.
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+__device__ __forceinline__ u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+__device__ __forceinline__ void st8(void* p, u32x2_t v) { *reinterpret_cast<u32x2_t*>(p) = v; }
+
+// load_at(base, off, plane): the 8 elements at element offset `off` of a
+// [T][d] buffer; `plane` = T*d is used by split formats only.
 template <typename T> struct Chunk;
 template <> struct Chunk<bf16_t> {
   u32x4_t r;
   __device__ __forceinline__ void load(const bf16_t* p) { r = ld16(p); }
+  __device__ __forceinline__ void load_at(const bf16_t* b, int64_t off, int64_t) { r = ld16(b + off); }
   __device__ __forceinline__ void zero() { r = u32x4_t{0u, 0u, 0u, 0u}; }
   __device__ __forceinline__ void unpack(float (&v)[8]) const {
     unpack_bf16x8(make_uint4(r.x, r.y, r.z, r.w), v);
@@ -90,12 +104,57 @@ template <> struct Chunk<bf16_t> {
 template <> struct Chunk<float> {
   u32x4_t a, b;
   __device__ __forceinline__ void load(const float* p) { a = ld16(p); b = ld16(p + 4); }
+  __device__ __forceinline__ void load_at(const float* p, int64_t off, int64_t) { load(p + off); }
   __device__ __forceinline__ void zero() { a = u32x4_t{0u, 0u, 0u, 0u}; b = a; }
   __device__ __forceinline__ void unpack(float (&v)[8]) const {
     v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
     v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
   }
 };
+template <> struct Chunk<p24_t> {
+  u32x4_t hi;  // 8 x 16-bit upper halves
+  u32x2_t lo;  // 8 x 8-bit next bits
+  __device__ __forceinline__ void load_at(const p24_t* b, int64_t off, int64_t plane) {
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(b);
+    hi = ld16(base + off * 2);
+    lo = ld8(base + plane * 2 + off);
+  }
+  __device__ __forceinline__ void zero() {
+    hi = u32x4_t{0u, 0u, 0u, 0u};
+    lo = u32x2_t{0u, 0u};
+  }
+  __device__ __forceinline__ void unpack(float (&v)[8]) const {
+    const unsigned h[4] = {hi.x, hi.y, hi.z, hi.w};
+    const unsigned l[2] = {lo.x, lo.y};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const unsigned h16 = (h[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      const unsigned l8 = (l[e >> 2] >> (8 * (e & 3))) & 0xffu;
+      v[e] = __uint_as_float((h16 << 16) | (l8 << 8));
+    }
+  }
+};
+
+// fp32 -> upper 24 bits, round to nearest even at bit 8 (finite values).
+__device__ __forceinline__ unsigned round24(float x) {
+  const unsigned u = __float_as_uint(x);
+  return u + 0x7fu + ((u >> 8) & 1u);
+}
+
+__device__ __forceinline__ void out24(p24_t* b, int64_t off, int64_t plane, const float (&v)[8]) {
+  unsigned r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = round24(v[e]);
+  unsigned char* base = reinterpret_cast<unsigned char*>(b);
+  st16(base + off * 2, u32x4_t{(r[0] >> 16) | (r[1] & 0xffff0000u), (r[2] >> 16) | (r[3] & 0xffff0000u),
+                               (r[4] >> 16) | (r[5] & 0xffff0000u), (r[6] >> 16) | (r[7] & 0xffff0000u)});
+  st8(base + plane * 2 + off,
+      u32x2_t{((r[0] >> 8) & 0xffu) | (((r[1] >> 8) & 0xffu) << 8) | (((r[2] >> 8) & 0xffu) << 16) |
+                  (((r[3] >> 8) & 0xffu) << 24),
+              ((r[4] >> 8) & 0xffu) | (((r[5] >> 8) & 0xffu) << 8) | (((r[6] >> 8) & 0xffu) << 16) |
+                  (((r[7] >> 8) & 0xffu) << 24)});
+}
+
 __device__ __forceinline__ void out8(float* p, const float (&v)[8]) {
   st16(p, u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
   st16(p + 4, u32x4_t{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});

@@ -6,7 +6,7 @@
 
 namespace attnres {
 
-enum Dtype { kF32 = 0, kBF16 = 1 };
+enum Dtype { kF32 = 0, kBF16 = 1, kP24 = 2 };
 
 int device_cu_count();
 
@@ -23,7 +23,7 @@ hipError_t launch_phase1_single(Dtype dt, const void* src, int n, int64_t stride
                                 hipStream_t stream);
 
 hipError_t launch_merge(Dtype dt, int64_t T, int d, const void* o1, const float* lse1,
-                        Dtype pdt, const void* pin, const void* vprev, float* pout,
+                        Dtype pdt, const void* pin, const void* vprev, Dtype podt, void* pout,
                         const float* w, const float* kg, const float* gamma, float eps,
                         void* h_out, void* x_out, hipStream_t stream);
 

@@ -38,7 +38,7 @@ struct Stage {
 // when used), so the loads of a stage issue back to back.
 template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN>
 __device__ __forceinline__ void issue(Stage<St, Pt, CPL>& s, int64_t tok, int64_t T, int d, int C, int tl,
-                                      const St* o1, const Pt* pin, const St* vprev) {
+                                      const St* o1, const Pt* pin, const St* vprev, int64_t plane) {
   const bool live = tok < T;
   const int64_t tc = live ? tok : T - 1;
 #pragma unroll
@@ -49,13 +49,13 @@ __device__ __forceinline__ void issue(Stage<St, Pt, CPL>& s, int64_t tok, int64_
     const int64_t off = tc * d + c * 8;
     s.o[k].load(o1 + off);
     if (HAS_V) s.v[k].load(vprev + off);
-    if (HAS_PIN) s.q[k].load(pin + off);
+    if (HAS_PIN) s.q[k].load_at(pin, off, plane);
   }
 }
 
 template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN>
 __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok, int64_t T, int d, int C, int tl,
-                                        const float* lse1, float* pout,
+                                        const float* lse1, void* pout, bool pout24, int64_t plane,
                                         const float (&wq)[CPL][8], const float (&gm)[CPL][8], float eps, float inv_d,
                                         St* h_out, St* x_out, float (*red)[8], int& parity) {
   const bool live = tok < T;
@@ -82,7 +82,14 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
     }
     if (HAS_V) {
       const int c = tl + TEAM * k;
-      if (pout && s.ok[k]) out8(pout + tok * d + c * 8, p[k]);
+      if (pout && s.ok[k]) {
+        const int64_t off = tok * d + c * 8;
+        if (pout24) {
+          out24(static_cast<p24_t*>(pout), off, plane, p[k]);
+        } else {
+          out8(static_cast<float*>(pout) + off, p[k]);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         ss = fmaf(p[k][e], p[k][e], ss);
@@ -140,11 +147,12 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
 template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN>
 __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __restrict__ o1,
                                                const float* __restrict__ lse1, const Pt* __restrict__ pin,
-                                               const St* __restrict__ vprev, float* __restrict__ pout,
+                                               const St* __restrict__ vprev, void* __restrict__ pout, int pout24,
                                                const float* __restrict__ w, const float* __restrict__ kg,
                                                const float* __restrict__ gamma, float eps,
                                                St* __restrict__ h_out, St* __restrict__ x_out) {
   constexpr int TPW = 256 / TEAM;
+  const int64_t plane = T * (int64_t)d;
   __shared__ float red[2][8];
   const int team = threadIdx.x / TEAM;
   const int tl = threadIdx.x % TEAM;
@@ -181,15 +189,17 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
   const int64_t step = (int64_t)gridDim.x * TPW;
   int64_t tok = (int64_t)blockIdx.x * TPW + team;
   Stage<St, Pt, CPL> A, B;
-  issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(A, tok, T, d, C, tl, o1, pin, vprev);
+  issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(A, tok, T, d, C, tl, o1, pin, vprev, plane);
   while (tok - team < T) {
-    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(B, tok + step, T, d, C, tl, o1, pin, vprev);
-    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(A, tok, T, d, C, tl, lse1, pout, wq, gm, eps, inv_d, h_out, x_out,
+    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(B, tok + step, T, d, C, tl, o1, pin, vprev, plane);
+    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(A, tok, T, d, C, tl, lse1, pout, pout24 != 0, plane, wq, gm, eps,
+                                              inv_d, h_out, x_out,
                                               red, parity);
     tok += step;
     if (tok - team >= T) break;
-    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(A, tok + step, T, d, C, tl, o1, pin, vprev);
-    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(B, tok, T, d, C, tl, lse1, pout, wq, gm, eps, inv_d, h_out, x_out,
+    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(A, tok + step, T, d, C, tl, o1, pin, vprev, plane);
+    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN>(B, tok, T, d, C, tl, lse1, pout, pout24 != 0, plane, wq, gm, eps,
+                                              inv_d, h_out, x_out,
                                               red, parity);
     tok += step;
   }
@@ -199,12 +209,15 @@ template <typename St, typename Pt>
 __global__ __launch_bounds__(256) void k_accumulate(int64_t nchunks, const Pt* __restrict__ pin,
                                                     const St* __restrict__ v, St* __restrict__ out) {
   const int64_t step = (int64_t)gridDim.x * 256;
+  const int64_t plane = nchunks * 8;
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks; c += step) {
     float a[8];
     load8(v + c * 8, a);
     if (pin) {
+      Chunk<Pt> q;
+      q.load_at(pin, c * 8, plane);
       float b[8];
-      load8(pin + c * 8, b);
+      q.unpack(b);
 #pragma unroll
       for (int e = 0; e < 8; ++e) a[e] = b[e] + a[e];
     }
@@ -216,7 +229,7 @@ __global__ __launch_bounds__(256) void k_accumulate(int64_t nchunks, const Pt* _
 
 template <typename St, typename Pt, int TEAM, int CPL>
 static hipError_t run_merge(int64_t T, int d, const void* o1, const float* lse1, const void* pin,
-                            const void* vprev, float* pout, const float* w, const float* kg,
+                            const void* vprev, void* pout, int pout24, const float* w, const float* kg,
                             const float* gamma, float eps, void* h_out, void* x_out, hipStream_t stream) {
   constexpr int TPW = 256 / TEAM;
   const int64_t tiles = (T + TPW - 1) / TPW;
@@ -229,24 +242,25 @@ static hipError_t run_merge(int64_t T, int d, const void* o1, const float* lse1,
   St* x = static_cast<St*>(x_out);
   if (!vprev) {
     hipLaunchKernelGGL((k_merge<St, Pt, TEAM, CPL, false, false>), grid, dim3(256), 0, stream, T, d, o, lse1, pi, v,
-                       pout, w, kg, gamma, eps, h, x);
+                       pout, pout24, w, kg, gamma, eps, h, x);
   } else if (!pin) {
     hipLaunchKernelGGL((k_merge<St, Pt, TEAM, CPL, true, false>), grid, dim3(256), 0, stream, T, d, o, lse1, pi, v,
-                       pout, w, kg, gamma, eps, h, x);
+                       pout, pout24, w, kg, gamma, eps, h, x);
   } else {
     hipLaunchKernelGGL((k_merge<St, Pt, TEAM, CPL, true, true>), grid, dim3(256), 0, stream, T, d, o, lse1, pi, v,
-                       pout, w, kg, gamma, eps, h, x);
+                       pout, pout24, w, kg, gamma, eps, h, x);
   }
   return hipGetLastError();
 }
 
 template <typename St, typename Pt>
 static hipError_t pick_team(int64_t T, int d, const void* o1, const float* lse1, const void* pin,
-                            const void* vprev, float* pout, const float* w, const float* kg,
+                            const void* vprev, void* pout, int pout24, const float* w, const float* kg,
                             const float* gamma, float eps, void* h_out, void* x_out, hipStream_t stream) {
   const int C = d >> 3;
-#define ATTNRES_RUN_MERGE(TEAM_, CPL_) \
-  return run_merge<St, Pt, TEAM_, CPL_>(T, d, o1, lse1, pin, vprev, pout, w, kg, gamma, eps, h_out, x_out, stream)
+#define ATTNRES_RUN_MERGE(TEAM_, CPL_)                                                                          \
+  return run_merge<St, Pt, TEAM_, CPL_>(T, d, o1, lse1, pin, vprev, pout, pout24, w, kg, gamma, eps, h_out, x_out, \
+                                        stream)
   if (C <= 64) ATTNRES_RUN_MERGE(64, 1);
   if (C <= 128) ATTNRES_RUN_MERGE(64, 2);
   if (C <= 256) ATTNRES_RUN_MERGE(64, 4);
@@ -256,17 +270,25 @@ static hipError_t pick_team(int64_t T, int d, const void* o1, const float* lse1,
 #undef ATTNRES_RUN_MERGE
 }
 
+template <typename St>
+static hipError_t pick_pin(Dtype pdt, int64_t T, int d, const void* o1, const float* lse1, const void* pin,
+                           const void* vprev, void* pout, int pout24, const float* w, const float* kg,
+                           const float* gamma, float eps, void* h_out, void* x_out, hipStream_t stream) {
+  // without a partial input the partial type is irrelevant: one instance
+  if (!pin || pdt == kF32)
+    return pick_team<St, float>(T, d, o1, lse1, pin, vprev, pout, pout24, w, kg, gamma, eps, h_out, x_out, stream);
+  if (pdt == kP24)
+    return pick_team<St, p24_t>(T, d, o1, lse1, pin, vprev, pout, pout24, w, kg, gamma, eps, h_out, x_out, stream);
+  return pick_team<St, St>(T, d, o1, lse1, pin, vprev, pout, pout24, w, kg, gamma, eps, h_out, x_out, stream);
+}
+
 hipError_t launch_merge(Dtype dt, int64_t T, int d, const void* o1, const float* lse1, Dtype pdt,
-                        const void* pin, const void* vprev, float* pout, const float* w, const float* kg,
+                        const void* pin, const void* vprev, Dtype podt, void* pout, const float* w, const float* kg,
                         const float* gamma, float eps, void* h_out, void* x_out, hipStream_t stream) {
-  if (dt == kBF16) {
-    if (pdt == kBF16)
-      return pick_team<bf16_t, bf16_t>(T, d, o1, lse1, pin, vprev, pout, w, kg, gamma, eps, h_out, x_out, stream);
-    return pick_team<bf16_t, float>(T, d, o1, lse1, pin, vprev, pout, w, kg, gamma, eps, h_out, x_out, stream);
-  }
-  if (pdt == kBF16)
-    return pick_team<float, bf16_t>(T, d, o1, lse1, pin, vprev, pout, w, kg, gamma, eps, h_out, x_out, stream);
-  return pick_team<float, float>(T, d, o1, lse1, pin, vprev, pout, w, kg, gamma, eps, h_out, x_out, stream);
+  const int pout24 = podt == kP24 ? 1 : 0;
+  if (dt == kBF16)
+    return pick_pin<bf16_t>(pdt, T, d, o1, lse1, pin, vprev, pout, pout24, w, kg, gamma, eps, h_out, x_out, stream);
+  return pick_pin<float>(pdt, T, d, o1, lse1, pin, vprev, pout, pout24, w, kg, gamma, eps, h_out, x_out, stream);
 }
 
 template <typename St, typename Pt>
@@ -280,14 +302,18 @@ static hipError_t run_acc(int64_t T, int d, const void* pin, const void* v, void
   return hipGetLastError();
 }
 
+template <typename St>
+static hipError_t acc_pin(Dtype pdt, int64_t T, int d, const void* pin, const void* v, void* out,
+                          hipStream_t stream) {
+  if (!pin || pdt == kF32) return run_acc<St, float>(T, d, pin, v, out, stream);
+  if (pdt == kP24) return run_acc<St, p24_t>(T, d, pin, v, out, stream);
+  return run_acc<St, St>(T, d, pin, v, out, stream);
+}
+
 hipError_t launch_accumulate(Dtype dt, int64_t T, int d, Dtype pdt, const void* pin, const void* v,
                              void* out, hipStream_t stream) {
-  if (dt == kBF16) {
-    if (pdt == kBF16) return run_acc<bf16_t, bf16_t>(T, d, pin, v, out, stream);
-    return run_acc<bf16_t, float>(T, d, pin, v, out, stream);
-  }
-  if (pdt == kBF16) return run_acc<float, bf16_t>(T, d, pin, v, out, stream);
-  return run_acc<float, float>(T, d, pin, v, out, stream);
+  if (dt == kBF16) return acc_pin<bf16_t>(pdt, T, d, pin, v, out, stream);
+  return acc_pin<float>(pdt, T, d, pin, v, out, stream);
 }
 
 }  // namespace attnres

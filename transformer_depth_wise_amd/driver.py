@@ -12,11 +12,13 @@ section 10) for every block of sublayers:
 Buffers live in HBM for the whole pass: the block representations
 ``reps [1 + n_given + N, T, d]`` (slot 0 is the embedding b_0), the phase-1
 outputs ``o1 [S_max, T, d]`` with their ``lse/m [S_max, T]`` (fp32) and the
-phase-1 workspace (softmax weights, ``T * n * S_max`` fp32), the
-running intra-block partial sum ``partial [T, d]`` in fp32, and a small ring of
-PreNorm outputs ``x``.  The partial sum is kept in fp32 because a bf16 running
-sum over a 24-sublayer block drifts by several percent of the row maximum;
-block sums are rounded once, when they are complete.
+phase-1 workspace (packed queries and softmax weights), the running
+intra-block partial sum ``partial``, and a small ring of PreNorm outputs
+``x``.  The partial sum is never stored in bf16: a bf16 running sum over a
+24-sublayer block drifts by several percent of the row maximum.  It is kept in
+the 24-bit split format (P24, 3 bytes per element, relative step 2^-16) for
+bf16 rows and in fp32 for fp32 rows; block sums are rounded to the storage
+dtype once, when they are complete.
 
 ``plan()`` lists every launch of a pass with its algorithmic bytes (each row
 the method must read or write, counted once).
@@ -56,7 +58,7 @@ class BlockAttnRes:
 
     def __init__(self, T: int, d: int, block_sizes: Sequence[int], dtype: torch.dtype, n_given: int = 0,
                  eps: float = 1e-6, device=None, x_ring: int = 4, keep_h: bool = False,
-                 final_site: bool = True):
+                 final_site: bool = True, partial: Optional[str] = None):
         self.T, self.d, self.dtype = int(T), int(d), dtype
         self.block_sizes = [int(s) for s in block_sizes]
         self.n_given, self.eps = int(n_given), float(eps)
@@ -79,7 +81,14 @@ class BlockAttnRes:
         n_max = 1 + self.n_given + max(0, len(self.block_sizes) - 1)
         ws = _lib.attnres_phase1_workspace_bytes(T, d, n_max, smax) if T > 0 else 0
         self.workspace = torch.empty((max(ws, 16) // 4,), dtype=torch.float32, device=dev)
-        self.partial = torch.empty((T, d), dtype=torch.float32, device=dev)
+        # running partial sum: P24 (24-bit split) for bf16 rows, fp32 for fp32 rows
+        self.partial_format = partial or ("p24" if dtype == torch.bfloat16 else "f32")
+        if self.partial_format == "p24":
+            self.partial = _lib.p24_partial(T, d, dev)
+        elif self.partial_format == "f32":
+            self.partial = torch.empty((T, d), dtype=torch.float32, device=dev)
+        else:
+            raise ValueError("partial format must be 'p24' or 'f32'")
         self.x = torch.empty((max(1, x_ring), T, d), dtype=dtype, device=dev)
         self.h = torch.empty((T, d), dtype=dtype, device=dev) if keep_h else None
         self.h_final = torch.empty((T, d), dtype=dtype, device=dev)
@@ -92,7 +101,7 @@ class BlockAttnRes:
                "phase1_out": self.o1.numel() * self.o1.element_size(),
                "phase1_stats": 2 * self.m1.numel() * 4,
                "phase1_workspace": self.workspace.numel() * 4,
-               "partial_sum": self.partial.numel() * 4,
+               "partial_sum": self.partial.numel() * self.partial.element_size(),
                "prenorm_out": self.x.numel() * self.x.element_size(),
                "final": self.h_final.numel() * self.h_final.element_size() + self.lse_final.numel() * 4}
         if self.h is not None:
@@ -105,7 +114,8 @@ class BlockAttnRes:
 
     def plan(self) -> List[Launch]:
         """Algorithmic bytes of every launch of one pass, in launch order."""
-        r, r32 = self._row(), self._row(torch.float32)
+        r = self._row()
+        r32 = self.T * self.d * (3 if self.partial_format == "p24" else 4)
         stat = self.T * 4
         out: List[Launch] = []
         n_done = 1 + self.n_given
