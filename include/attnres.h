@@ -85,7 +85,10 @@ typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1, ATTNRES_P24 = 2 } attnres_dtyp
  *     lse_s = m_s + ln sum_i e^{z_si - m_s},
  *     out[s][t][:] = sum_i e^{z_si - lse_s} u_i        (normalised)
  *   w, key_gain: [S][d] fp32 (key_gain NULL = ones).
- *   out: [S][T][d] dtype dt.  m_out, lse_out: [S][T] fp32 (m_out may be NULL).
+ *   out: [S][T][d] dtype dt, or NULL to compute the statistics only (with a
+ *   single source every output equals that source, so a caller can use the
+ *   source row itself in phase 2).  m_out, lse_out: [S][T] fp32 (m_out may
+ *   be NULL).
  * Limits: 1 <= n_src <= ATTNRES_MAX_SOURCES_MULTI when S >= 2, <=
  * ATTNRES_MAX_SOURCES when S == 1; S >= 1 (queries are processed 32 at a
  * time; each group of 32 reads the sources once for the scores and once for
@@ -94,7 +97,9 @@ typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1, ATTNRES_P24 = 2 } attnres_dtyp
  * attnres_phase1_workspace_bytes(T, d, n_src, S) bytes, 16-byte aligned,
  * used for the queries packed as matrix-core operands and for the softmax
  * weights between the scoring and output kernels (its contents afterwards are
- * unspecified); NULL allowed when that size is 0.
+ * unspecified).  Required for S >= 2.  For S == 1 it is optional: without it
+ * (or when it is too small) one fused kernel computes the site instead of the
+ * streaming pair.
  * out must not overlap src; m_out, lse_out and workspace must not overlap
  * anything.
  */
@@ -105,8 +110,9 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt,
                                 void* out, float* m_out, float* lse_out,
                                 void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes attnres_phase1 needs: 32 * d * 4 + T * n_src * min(S, 32)
- * * 4 when S >= 2, 0 when S == 1; -1 for invalid sizes. */
+/* Workspace bytes attnres_phase1 uses: 32 * d * 4 + T * n_src * min(S, 32)
+ * * 4 (0 for S == 1 with more than ATTNRES_MAX_SOURCES_MULTI sources); -1
+ * for invalid sizes. */
 int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int64_t S);
 
 /*

@@ -91,7 +91,9 @@ def test_phase1_validation(lib):
     assert phase1(lib, ws=16 * A + 64) == EALIAS         # workspace inside the output
     assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 4) == 32 * 64 * 4 + 4096 * 3 * 4 * 4
     assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 40) == 32 * 64 * 4 + 4096 * 3 * 32 * 4
-    assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 1) == 0
+    assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 1) == 32 * 64 * 4 + 4096 * 3 * 4
+    assert lib.attnres_phase1_workspace_bytes(4096, 64, 20, 1) == 0     # > 16 sources: fused path only
+    assert lib.attnres_phase1_workspace_bytes(4096, 64, 20, 2) == -1
     assert lib.attnres_phase1_workspace_bytes(4096, 12, 3, 4) == -1
     assert phase1(lib, T=0) == 0                      # nothing to do, nothing launched
     assert phase1(lib, T=0, src=None, out=None, lse=None) == 0

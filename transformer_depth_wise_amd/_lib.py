@@ -103,12 +103,14 @@ def attnres_phase1_workspace_bytes(T: int, d: int, n_src: int, S: int) -> int:
 
 
 def attnres_phase1(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],
-                   eps: float, out: torch.Tensor, m_out: Optional[torch.Tensor], lse_out: torch.Tensor,
+                   eps: float, out: Optional[torch.Tensor], m_out: Optional[torch.Tensor], lse_out: torch.Tensor,
                    workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """src: [>=n_src, T, d] slabs (sources 0..n_src-1 at stride src.stride(0));
-    w, key_gain: [S, d] fp32; out: [S, T, d]; m_out, lse_out: [S, T] fp32;
-    workspace: device tensor of at least attnres_phase1_workspace_bytes bytes."""
-    S, T, d = out.shape
+    w, key_gain: [S, d] fp32; out: [S, T, d] or None (statistics only);
+    m_out, lse_out: [S, T] fp32; workspace: device tensor of at least
+    attnres_phase1_workspace_bytes bytes."""
+    S, T = lse_out.shape
+    d = src.shape[-1]
     stride = src.stride(0) if src.dim() == 3 else T * d
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load().attnres_phase1(dtype_code(src.dtype), _ptr(src), n_src, stride, T, d, _ptr(w), _ptr(key_gain),

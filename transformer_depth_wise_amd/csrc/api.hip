@@ -90,7 +90,7 @@ const char* attnres_status_string(attnres_status_t status) {
 
 int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int64_t S) {
   if (T < 0 || n_src < 1 || S < 1 || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
-  if (S == 1) return 0;
+  if (n_src > ATTNRES_MAX_SOURCES_MULTI) return S == 1 ? 0 : -1;
   // packed queries (32 rows x d x 4 bytes) + softmax weights (T x n x 32 x 4 bytes)
   const int64_t sq = S < 32 ? S : 32;
   return 32 * d * 4 + T * n_src * sq * (int64_t)sizeof(float);
@@ -107,16 +107,18 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_s
   if (n_src > (S == 1 ? ATTNRES_MAX_SOURCES : ATTNRES_MAX_SOURCES_MULTI)) return ATTNRES_EINVAL;
   if (T > (int64_t)1 << 40 || !(eps >= 0.f)) return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
-  if (!src || !w || !out || !lse_out) return ATTNRES_EINVAL;
+  if (!src || !w || !lse_out) return ATTNRES_EINVAL;
   if (n_src > 1 && (src_stride < T * d)) return ATTNRES_EINVAL;
   if (src_stride % 8 != 0) return ATTNRES_EALIGN;
-  const int64_t ws_need = attnres_phase1_workspace_bytes(T, d, n_src, S);
+  int64_t ws_need = attnres_phase1_workspace_bytes(T, d, n_src, S);
+  // S == 1: the workspace is optional (without it, one fused kernel runs)
+  if (S == 1 && (!workspace || workspace_bytes < ws_need)) ws_need = 0;
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return ATTNRES_EINVAL;
   st = check_align({src, w, key_gain, out, ws_need > 0 ? workspace : nullptr}, {m_out, lse_out});
   if (st != ATTNRES_OK) return st;
   const int64_t es = esize(dt);
   const Range rs = range_of(src, ((n_src - 1) * src_stride + T * d) * es);
-  const Range ro = range_of(out, S * T * d * es);
+  const Range ro = out ? range_of(out, S * T * d * es) : Range{0, 0};
   const Range rl = range_of(lse_out, S * T * 4);
   const Range rm = m_out ? range_of(m_out, S * T * 4) : Range{0, 0};
   const Range rw = range_of(w, S * d * 4);
@@ -130,12 +132,12 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_s
 
   const Dtype kdt = kind_of(dt);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (S == 1)
+  if (S == 1 && ws_need == 0)
     return hip_status(attnres::launch_phase1_single(kdt, src, (int)n_src, src_stride, T, (int)d, w, key_gain,
                                                     nullptr, eps, out, nullptr, m_out, lse_out, s));
   for (int64_t s0 = 0; s0 < S; s0 += 32) {
     const int64_t sn = (S - s0) < 32 ? (S - s0) : 32;
-    char* o = static_cast<char*>(out) + s0 * T * d * es;
+    char* o = out ? static_cast<char*>(out) + s0 * T * d * es : nullptr;
     hipError_t e = attnres::launch_phase1_multi(kdt, src, (int)n_src, src_stride, T, (int)d, w + s0 * d,
                                                 key_gain ? key_gain + s0 * d : nullptr, (int)sn, eps, o,
                                                 m_out ? m_out + s0 * T : nullptr, lse_out + s0 * T,

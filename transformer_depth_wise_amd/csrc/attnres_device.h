@@ -155,6 +155,19 @@ __device__ __forceinline__ void out24(p24_t* b, int64_t off, int64_t plane, cons
                   (((r[7] >> 8) & 0xffu) << 24)});
 }
 
+// Non-temporal 16-byte store: for outputs that are not read again soon, so
+// they do not displace reusable lines from the caches.
+__device__ __forceinline__ void st16_nt(void* p, u32x4_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void out8_nt(bf16_t* p, const float (&v)[8]) {
+  st16_nt(p, u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
+}
+__device__ __forceinline__ void out8_nt(float* p, const float (&v)[8]) {
+  st16_nt(p, u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+  st16_nt(p + 4, u32x4_t{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
+}
+
 __device__ __forceinline__ void out8(float* p, const float (&v)[8]) {
   st16(p, u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
   st16(p + 4, u32x4_t{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});

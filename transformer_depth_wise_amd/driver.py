@@ -80,6 +80,8 @@ class BlockAttnRes:
         self.lse1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
         n_max = 1 + self.n_given + max(0, len(self.block_sizes) - 1)
         ws = _lib.attnres_phase1_workspace_bytes(T, d, n_max, smax) if T > 0 else 0
+        if final_site and T > 0:  # the final site runs as a one-query phase 1
+            ws = max(ws, _lib.attnres_phase1_workspace_bytes(T, d, n_reps, 1))
         self.workspace = torch.empty((max(ws, 16) // 4,), dtype=torch.float32, device=dev)
         # running partial sum: P24 (24-bit split) for bf16 rows, fp32 for fp32 rows
         self.partial_format = partial or ("p24" if dtype == torch.bfloat16 else "f32")
@@ -120,7 +122,10 @@ class BlockAttnRes:
         out: List[Launch] = []
         n_done = 1 + self.n_given
         for S in self.block_sizes:
-            out.append(Launch("phase1", n_done * r + S * (r + 2 * stat)))
+            if n_done == 1:  # statistics only; phase 2 reads b_0 as its phase-1 output
+                out.append(Launch("phase1", r + S * 2 * stat))
+            else:
+                out.append(Launch("phase1", n_done * r + S * (r + 2 * stat)))
             for j in range(S):
                 if j == 0:
                     b = 2 * r + stat
@@ -161,9 +166,14 @@ class BlockAttnRes:
         l0 = 0
         nx = self.x.shape[0]
         for S in self.block_sizes:
+            # with a single completed source (the embedding) every phase-1
+            # output is that source: compute the statistics only and let
+            # phase 2 read b_0 itself
+            single = n_done == 1
             mark("phase1", True)
             attnres_phase1(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S], eps,
-                           self.o1[:S], self.m1[:S], self.lse1[:S], self.workspace, stream=stream)
+                           None if single else self.o1[:S], self.m1[:S], self.lse1[:S], self.workspace,
+                           stream=stream)
             mark("phase1", False)
             # outputs of the block kept alive: the first two (for the first
             # fp32 partial sum) and the previous one
@@ -182,11 +192,12 @@ class BlockAttnRes:
                 else:
                     pin, pout = self.partial, self.partial
                 mark("phase2", True)
-                attnres_phase2_merge(self.o1[j], self.lse1[j], pin, prev, pout, w[site], kg, pg, eps,
+                o = self.reps[0] if single else self.o1[j]
+                attnres_phase2_merge(o, self.lse1[j], pin, prev, pout, w[site], kg, pg, eps,
                                      self.h, x, stream=stream)
                 mark("phase2", False)
                 if hook is not None:
-                    hook(site, x=x, h=self.h, o1=self.o1[j], lse1=self.lse1[j], m1=self.m1[j])
+                    hook(site, x=x, h=self.h, o1=o, lse1=self.lse1[j], m1=self.m1[j])
                 prev = sublayer(site, x)
                 if j == 0:
                     first = prev
@@ -206,8 +217,9 @@ class BlockAttnRes:
             l0 += S
         if self.final_site:
             mark("final", True)
-            attnres_full(self.reps, n_done, w[self.L], None if g is None else g[self.L], None, eps,
-                         self.h_final, None, self.lse_final, stream=stream)
+            attnres_phase1(self.reps, n_done, w[self.L:self.L + 1], None if g is None else g[self.L:self.L + 1],
+                           eps, self.h_final.unsqueeze(0), None, self.lse_final.unsqueeze(0), self.workspace,
+                           stream=stream)
             mark("final", False)
         return self.h_final
 
