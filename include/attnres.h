@@ -110,9 +110,9 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt,
                                 void* out, float* m_out, float* lse_out,
                                 void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes attnres_phase1 uses: 32 * d * 4 + T * n_src * min(S, 32)
- * * 4 (0 for S == 1 with more than ATTNRES_MAX_SOURCES_MULTI sources); -1
- * for invalid sizes. */
+/* Workspace bytes attnres_phase1 uses: 16384 * ceil(d / 128) (packed
+ * queries) + T * n_src * min(S, 32) * 4 (softmax weights); 0 for S == 1 with
+ * more than ATTNRES_MAX_SOURCES_MULTI sources; -1 for invalid sizes. */
 int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int64_t S);
 
 /*

@@ -89,9 +89,12 @@ def test_phase1_validation(lib):
     assert phase1(lib, ws=None) == EINVAL                # S >= 2 needs the workspace
     assert phase1(lib, ws_bytes=100) == EINVAL           # too small
     assert phase1(lib, ws=16 * A + 64) == EALIAS         # workspace inside the output
-    assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 4) == 32 * 64 * 4 + 4096 * 3 * 4 * 4
-    assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 40) == 32 * 64 * 4 + 4096 * 3 * 32 * 4
-    assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 1) == 32 * 64 * 4 + 4096 * 3 * 4
+    # packed queries: 32 rows x 4 bytes per channel, d rounded up to 128
+    assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 4) == 16384 + 4096 * 3 * 4 * 4
+    assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 40) == 16384 + 4096 * 3 * 32 * 4
+    assert lib.attnres_phase1_workspace_bytes(4096, 64, 3, 1) == 16384 + 4096 * 3 * 4
+    assert lib.attnres_phase1_workspace_bytes(16384, 7168, 8, 24) == 56 * 16384 + 16384 * 8 * 24 * 4
+    assert lib.attnres_phase1_workspace_bytes(10, 136, 2, 2) == 2 * 16384 + 10 * 2 * 2 * 4
     assert lib.attnres_phase1_workspace_bytes(4096, 64, 20, 1) == 0     # > 16 sources: fused path only
     assert lib.attnres_phase1_workspace_bytes(4096, 64, 20, 2) == -1
     assert lib.attnres_phase1_workspace_bytes(4096, 12, 3, 4) == -1

@@ -213,6 +213,58 @@ def test_token_split_invariance():
         assert torch.equal(s2.h_final, whole[a:b])
 
 
+# ------------------------- phase 1 over long token ranges (wide-tile scoring)
+WIDE = [
+    # (dtype, d, n_src, S): ragged last K-block, single query, fp32, largest LDS use
+    ("bf16", 7104, 8, 24),
+    ("bf16", 7168, 9, 1),
+    ("f32", 1032, 3, 20),
+    ("bf16", 1024, 16, 32),
+]
+
+
+@pytest.mark.parametrize("dt,d,n,S", WIDE)
+def test_phase1_long_range_equals_slices_and_oracle(dt, d, n, S):
+    """Phase 1 over a token range long enough for the wide scoring kernel (64
+    tokens per workgroup, one workgroup per compute unit) gives, bit for bit,
+    what calls over shorter slices (16-token tiles) give, and matches the
+    oracle on sampled tokens."""
+    dev = torch.device("cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    T = 64 * cus + 40                   # ragged last workgroup
+    cut = 64 * cus // 2                 # both slices stay below 64 * cus tokens
+    _say("case phase1 long range %s T=%d d=%d n=%d S=%d" % (dt, T, d, n, S))
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    g = torch.Generator(device=dev).manual_seed(9000 + d + n + S)
+    src = torch.randn((n, T, d), generator=g, device=dev).to(tdt)
+    w = torch.randn((S, d), generator=g, device=dev) * 0.02
+    kg = torch.rand((S, d), generator=g, device=dev) * 0.4 + 0.8
+    ws = torch.empty(tdw.attnres_phase1_workspace_bytes(T, d, n, S) // 4 + 4, device=dev)
+
+    def call(t0, t1):
+        out = torch.empty((S, t1 - t0, d), dtype=tdt, device=dev)
+        m = torch.empty((S, t1 - t0), device=dev)
+        lse = torch.empty((S, t1 - t0), device=dev)
+        tdw.attnres_phase1(src[:, t0:t1], n, w, kg, 1e-6, out, m, lse, workspace=ws)
+        return out, m, lse
+
+    whole = call(0, T)
+    parts = [call(0, cut), call(cut, T)]
+    torch.cuda.synchronize()
+    for k in range(3):
+        assert torch.equal(whole[k], torch.cat([parts[0][k], parts[1][k]], dim=-2 if k == 0 else -1)), k
+    tol = TOL[dt]
+    for t in synth.sample_tokens(T, 6):
+        rows = [src[i, t].double().cpu().numpy() for i in range(n)]
+        for q in (0, S - 1):
+            # the oracle's partition statistics: max m, sum ell of e^{z - m}, and
+            # the unnormalised sum o of e^{z_i - m} u_i
+            m_ref, ell, o_ref = oracle.partition_stats(rows, w[q].cpu().numpy(), kg[q].cpu().numpy(), 1e-6)
+            assert stat_err(np.array([whole[1][q, t].item()]), np.array([m_ref])).max() <= tol
+            assert stat_err(np.array([whole[2][q, t].item()]), np.array([m_ref + math.log(ell)])).max() <= tol
+            assert row_rel_err(_host(whole[0][q, t]), o_ref / ell) <= tol
+
+
 # --------------------------------------------- long context, chunked prefill
 def _long_prefill(w, chunked: bool, samples, dev):
     """Run the whole depth over T tokens, streamed in 16K chunks or in one

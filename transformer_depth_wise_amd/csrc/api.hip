@@ -91,9 +91,11 @@ const char* attnres_status_string(attnres_status_t status) {
 int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int64_t S) {
   if (T < 0 || n_src < 1 || S < 1 || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
   if (n_src > ATTNRES_MAX_SOURCES_MULTI) return S == 1 ? 0 : -1;
-  // packed queries (32 rows x d x 4 bytes) + softmax weights (T x n x 32 x 4 bytes)
+  // packed queries (32 rows x 4 bytes x d rounded up to 128) + softmax
+  // weights (T x n x min(S, 32) x 4 bytes)
   const int64_t sq = S < 32 ? S : 32;
-  return 32 * d * 4 + T * n_src * sq * (int64_t)sizeof(float);
+  const int64_t kblocks = (d + 127) / 128;
+  return 32 * 4 * 128 * kblocks + T * n_src * sq * (int64_t)sizeof(float);
 }
 
 attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,

@@ -188,6 +188,16 @@ __device__ __forceinline__ float wave_sum(float x) {
 // result is identical in every thread and from run to run).  `lds` holds 8
 // floats; callers alternate between two such buffers so that one barrier per
 // reduction suffices.
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// orders global memory, which makes every wave wait for all of its global
+// loads and stores in flight (the prefetched next item included); here those
+// stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float2 block_sum2_256(float a, float b, float* lds) {
   a = wave_sum(a);
   b = wave_sum(b);
@@ -197,7 +207,7 @@ __device__ __forceinline__ float2 block_sum2_256(float a, float b, float* lds) {
     lds[2 * wave + 0] = a;
     lds[2 * wave + 1] = b;
   }
-  __syncthreads();
+  lds_barrier();
   float2 r;
   r.x = (lds[0] + lds[2]) + (lds[4] + lds[6]);
   r.y = (lds[1] + lds[3]) + (lds[5] + lds[7]);

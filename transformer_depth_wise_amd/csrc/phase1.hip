@@ -70,23 +70,26 @@ struct Mfma<bf16_t> {
     return a;
   }
 
-  // Packed query chunk: 8 bf16 hi parts then 8 bf16 lo parts (32 bytes).
-  static __device__ __forceinline__ A load_packed(const u32x4_t* p, bool ok) {
+  // Packed query chunk: 8 bf16 hi parts in the first half, the 8 lo parts
+  // in the second.
+  static __device__ __forceinline__ A from_halves(u32x4_t h, u32x4_t l) {
     A a;
-    a.hi = __builtin_bit_cast(bf16x8_t, sel16(ok, ld16(p)));
-    a.lo = __builtin_bit_cast(bf16x8_t, sel16(ok, ld16(p + 1)));
+    a.hi = __builtin_bit_cast(bf16x8_t, h);
+    a.lo = __builtin_bit_cast(bf16x8_t, l);
     return a;
   }
 
-  static __device__ __forceinline__ void pack(const float (&q)[8], u32x4_t* p) {
+  static __device__ __forceinline__ void pack(const float (&q)[8], u32x4_t* h, u32x4_t* l) {
     const A a = make_a(q);
-    st16(p, __builtin_bit_cast(u32x4_t, a.hi));
-    st16(p + 1, __builtin_bit_cast(u32x4_t, a.lo));
+    st16(h, __builtin_bit_cast(u32x4_t, a.hi));
+    st16(l, __builtin_bit_cast(u32x4_t, a.lo));
   }
 
   static __device__ __forceinline__ B load_b(const bf16_t* p, bool ok) {
     return __builtin_bit_cast(bf16x8_t, sel16(ok, ld16(p)));
   }
+
+  static __device__ __forceinline__ B zero_b() { return __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u}); }
 
   static __device__ __forceinline__ void sumsq(const B& b, float& ss) {
     const u32x4_t u = __builtin_bit_cast(u32x4_t, b);
@@ -118,9 +121,8 @@ struct Mfma<float> {
     return a;
   }
 
-  // Packed query chunk: the 8 folded fp32 values (32 bytes).
-  static __device__ __forceinline__ A load_packed(const u32x4_t* p, bool ok) {
-    const u32x4_t x = sel16(ok, ld16(p)), y = sel16(ok, ld16(p + 1));
+  // Packed query chunk: the 8 folded fp32 values, 4 in each half.
+  static __device__ __forceinline__ A from_halves(u32x4_t x, u32x4_t y) {
     A a;
     a.v[0] = __uint_as_float(x.x); a.v[1] = __uint_as_float(x.y); a.v[2] = __uint_as_float(x.z);
     a.v[3] = __uint_as_float(x.w); a.v[4] = __uint_as_float(y.x); a.v[5] = __uint_as_float(y.y);
@@ -128,9 +130,9 @@ struct Mfma<float> {
     return a;
   }
 
-  static __device__ __forceinline__ void pack(const float (&q)[8], u32x4_t* p) {
-    st16(p, u32x4_t{__float_as_uint(q[0]), __float_as_uint(q[1]), __float_as_uint(q[2]), __float_as_uint(q[3])});
-    st16(p + 1, u32x4_t{__float_as_uint(q[4]), __float_as_uint(q[5]), __float_as_uint(q[6]), __float_as_uint(q[7])});
+  static __device__ __forceinline__ void pack(const float (&q)[8], u32x4_t* h, u32x4_t* l) {
+    st16(h, u32x4_t{__float_as_uint(q[0]), __float_as_uint(q[1]), __float_as_uint(q[2]), __float_as_uint(q[3])});
+    st16(l, u32x4_t{__float_as_uint(q[4]), __float_as_uint(q[5]), __float_as_uint(q[6]), __float_as_uint(q[7])});
   }
 
   static __device__ __forceinline__ B load_b(const float* p, bool ok) {
@@ -139,6 +141,13 @@ struct Mfma<float> {
     b.v[0] = __uint_as_float(x.x); b.v[1] = __uint_as_float(x.y); b.v[2] = __uint_as_float(x.z);
     b.v[3] = __uint_as_float(x.w); b.v[4] = __uint_as_float(y.x); b.v[5] = __uint_as_float(y.y);
     b.v[6] = __uint_as_float(y.z); b.v[7] = __uint_as_float(y.w);
+    return b;
+  }
+
+  static __device__ __forceinline__ B zero_b() {
+    B b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b.v[e] = 0.f;
     return b;
   }
 
@@ -154,14 +163,30 @@ struct Mfma<float> {
   }
 };
 
+// Packed query operands.  Channels are grouped into K-blocks of 128 (16
+// chunks of 8); K-block kb of a tile of 16*MT queries is a contiguous run of
+// MT*4*2*64 16-byte words ordered [m][step][half][lane], where lane
+// (grp*16 + col) holds query m*16+col, chunk kb*16 + step*4 + grp, half 0 =
+// bf16 hi parts (fp32: values 0..3), half 1 = lo parts (values 4..7).  Rows
+// >= S and chunks past the end of d are zero, so no load needs a guard and
+// one wave reads 1 KiB of consecutive bytes per instruction.
+constexpr int kKBlock = 16;          // chunks per K-block
+constexpr int kPackedKBlockWords = 2 * 512;  // 16-byte words per K-block, room for 32 queries
+template <int MT>
+__device__ __forceinline__ int64_t packed_index(int kb, int m, int s4, int lane) {
+  return (int64_t)kb * (MT * 512) + ((m * 4 + s4) * 2) * 64 + lane;
+}
+
 // Per-wave partial scores of the 16-token tile starting at tok0 against
 // queries [0, 16*MT) for sources [g0, g0+G) (all valid).  Channel chunks (8
-// channels) are visited in K-blocks of 16 chunks; wave w takes K-blocks w,
-// w+4, ...; within a K-block, step s4 reads chunk 4*s4 + grp, so the 4 lane
-// groups read 64 contiguous bytes of each token row per instruction.
-// With PACKED, the queries come from `pk` ([16*MT][C] chunks of 32 bytes,
-// rows >= S zero) written by k_pack_queries; otherwise w (.) g is formed and
-// split per chunk from the fp32 parameters.
+// channels) are visited in K-blocks of 16 chunks; wave w takes the w-th
+// contiguous quarter [w*nkb/4, (w+1)*nkb/4) of the K-blocks, in order, so each
+// wave streams through its part of every row; within a K-block, step s4 reads
+// chunk 4*s4 + grp, so the 4 lane groups read 64 contiguous bytes of each
+// token row per instruction.
+// With PACKED, the queries come from `pk` (packed layout above) written by
+// k_pack_queries; otherwise w (.) g is formed and split per chunk from the
+// fp32 parameters.
 template <typename St, int MT, int G, bool PACKED>
 __device__ __forceinline__ void score_pass(const St* __restrict__ src, int64_t stride, int64_t T, int d,
                                            const float* __restrict__ w, const float* __restrict__ kg,
@@ -174,7 +199,7 @@ __device__ __forceinline__ void score_pass(const St* __restrict__ src, int64_t s
   const bool tok_ok = tok0 + col < T;
   const int64_t tok = tok_ok ? tok0 + col : T - 1;  // clamped: always a valid row
   const int C = d >> 3;
-  const int nkb = (C + 15) >> 4;
+  const int nkb = (C + kKBlock - 1) / kKBlock;
   const St* base[G];
 #pragma unroll
   for (int i = 0; i < G; ++i) base[i] = src + (int64_t)(g0 + i) * stride + tok * d;
@@ -185,7 +210,8 @@ __device__ __forceinline__ void score_pass(const St* __restrict__ src, int64_t s
 #pragma unroll
   for (int i = 0; i < G; ++i) ss[i] = 0.f;
 
-  for (int kb = wave; kb < nkb; kb += 4) {
+  const int kb_end = ((wave + 1) * nkb) >> 2;
+  for (int kb = (wave * nkb) >> 2; kb < kb_end; ++kb) {
     // All loads of the K-block first (queries and sources of the 4 steps),
     // then the matrix-core work: the scheduling barrier keeps the compiler
     // from sinking loads next to their first use, so a wave keeps 4 * (2*MT
@@ -201,7 +227,8 @@ __device__ __forceinline__ void score_pass(const St* __restrict__ src, int64_t s
       for (int m = 0; m < MT; ++m) {
         const int q = m * 16 + col;
         if (PACKED) {
-          a[s4][m] = Mfma<St>::load_packed(pk + ((int64_t)q * C + c) * 2, cok);
+          const u32x4_t* qp = pk + packed_index<MT>(kb, m, s4, lane);
+          a[s4][m] = Mfma<St>::from_halves(ld16(qp), ld16(qp + 64));
         } else {
           const bool qok = cok && q < S;
           const int qc = q < S ? q : 0;
@@ -276,13 +303,13 @@ struct Red {
   static __device__ __forceinline__ void reduce(float* red, f32x4_t (&acc)[MT][G], float (&ss)[G]) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    __syncthreads();  // previous readers of the slots are done
+    lds_barrier();  // previous readers of the slots are done
     if (wave >= 2) put(red + (wave - 2) * kSlot, acc, ss, lane);
-    __syncthreads();
+    lds_barrier();
     if (wave < 2) add(red + wave * kSlot, acc, ss, lane);
-    __syncthreads();
+    lds_barrier();
     if (wave == 1) put(red, acc, ss, lane);
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) add(red, acc, ss, lane);
   }
 };
@@ -338,17 +365,24 @@ __device__ __forceinline__ void score_all(const St* src, int n, int64_t stride, 
 }
 
 // ---------------------------------------------------------------------------
-// S >= 2, prologue: pack the tile's queries w (.) g once per call into MFMA
-// operand chunks ([16*MT][C] x 32 bytes, rows >= S zero).
+// Prologue of the streaming pair: pack the tile's queries w (.) g once per
+// call into matrix-core operands (layout above).  One thread per (K-block,
+// m, step, lane).
 template <typename St, int MT>
 __global__ __launch_bounds__(256) void k_pack_queries(const float* __restrict__ w, const float* __restrict__ kg,
                                                       int S, int d, u32x4_t* __restrict__ pk) {
   const int C = d >> 3;
+  const int nkb = (C + kKBlock - 1) / kKBlock;
   const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= 16 * MT * C) return;
-  const int q = idx / C, c = idx - q * C;
+  if (idx >= nkb * MT * 4 * 64) return;
+  const int lane = idx & 63;
+  const int s4 = (idx >> 6) & 3;
+  const int m = (idx >> 8) % MT;
+  const int kb = (idx >> 8) / MT;
+  const int q = m * 16 + (lane & 15);
+  const int c = kb * kKBlock + s4 * 4 + (lane >> 4);
   float qv[8];
-  if (q < S) {
+  if (q < S && c < C) {
     load8(w + (int64_t)q * d + c * 8, qv);
     if (kg) {
       float gv[8];
@@ -359,7 +393,8 @@ __global__ __launch_bounds__(256) void k_pack_queries(const float* __restrict__ 
   } else {
     zero8(qv);
   }
-  Mfma<St>::pack(qv, pk + (int64_t)idx * 2);
+  u32x4_t* dst = pk + packed_index<MT>(kb, m, s4, lane);
+  Mfma<St>::pack(qv, dst, dst + 64);
 }
 
 // S >= 2, first kernel: scores and softmax weights of a 16-token tile for up
@@ -376,7 +411,7 @@ __global__ __launch_bounds__(256) void k_p1_scores(const St* __restrict__ src, i
   float* zb = lds + 2 * Red<MT, kGroup>::kSlot;  // [16 tokens][QP queries][n sources]
   const int64_t tok0 = (int64_t)blockIdx.x * 16;
   score_all<St, MT, true, false>(src, n, stride, T, d, nullptr, nullptr, pk, S, eps, tok0, red, zb, n);
-  __syncthreads();
+  lds_barrier();
 
   // softmax over the n sources of every (token, query) pair
   for (int pidx = threadIdx.x; pidx < 16 * QP; pidx += 256) {
@@ -392,6 +427,231 @@ __global__ __launch_bounds__(256) void k_p1_scores(const St* __restrict__ src, i
     for (int i = 0; i < n; ++i) a[i] = expf(row[i] - mx) / l;
     if (m_out) m_out[(int64_t)q * T + tok] = mx;
     lse_out[(int64_t)q * T + tok] = mx + logf(l);
+  }
+}
+
+// Wide-tile variant of the scoring kernel for long token ranges, with the
+// same results bit for bit.  A workgroup holds kWideWaves compute waves, each
+// owning a 16-token tile over all of d, plus one loader wave.  A compute wave
+// streams its source rows through a ring of D register stages (one K-block of
+// one source per stage), so D-1 K-blocks are in flight while the matrix cores
+// work on the oldest.  The loader wave copies the packed queries of each
+// K-block into one of two LDS slots one K-block ahead; the workgroup meets at
+// one barrier per K-block.  The loader waits only on its own query loads, so
+// the source stream never waits behind a query load, and every packed query
+// byte leaves L2 once per 64 tokens instead of once per 16.
+//
+// Summation order.  Per source, the K-blocks are visited in order; they form
+// four contiguous classes [w*nkb/4, (w+1)*nkb/4), each summed from zero, the
+// sum of squares of each class is reduced over the lane groups, and the
+// classes are combined as (c0 + c2) + (c1 + c3): exactly what k_p1_scores
+// gets from its four waves (one class each) and its fixed-order reduction.
+struct KOrder {
+  int nkb;
+  __device__ __forceinline__ explicit KOrder(int n) : nkb(n) {}
+  // K-block kb -> its class w; `last` marks the final K-block of the class
+  __device__ __forceinline__ void at(int kb, int& w, bool& last) const {
+    w = 0;
+    while (w < 3 && (((w + 1) * nkb) >> 2) <= kb) ++w;
+    last = kb + 1 == (((w + 1) * nkb) >> 2);
+  }
+};
+
+constexpr int kWideWaves = 4;  // compute waves (16 tokens each) per workgroup
+
+// Ring depth (stages of one K-block): 16 VGPRs per bf16 stage, 32 per fp32
+// stage, within the 256 VGPRs a wave may hold (two waves share one SIMD).
+template <typename St, int MT>
+struct WideDepth {
+  static constexpr int value = MT == 1 ? 6 : 4;
+};
+template <int MT>
+struct WideDepth<float, MT> {
+  static constexpr int value = 2;
+};
+
+template <typename St, int MT>
+__global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
+    const St* __restrict__ src, int n, int64_t stride, int64_t T, int d, const u32x4_t* __restrict__ pk, int S,
+    float eps, float* __restrict__ alpha, float* __restrict__ m_out, float* __restrict__ lse_out) {
+  constexpr int D = WideDepth<St, MT>::value;
+  constexpr int QW = MT * 512;  // 16-byte words per packed K-block
+  static_assert(D % 2 == 0, "the LDS slot of a ring stage must be a constant");
+  __shared__ u32x4_t qs[2][QW];
+  extern __shared__ float zs[];  // per compute wave: z[16 tokens][S][n]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int C = d >> 3;
+  const int nkb = (C + kKBlock - 1) / kKBlock;
+  const int nit = n * nkb;  // (source, K-block) iterations, source-major
+  const KOrder ko(nkb);
+  // Global memory is touched only by loads until the last loop ends, and
+  // every load below is unconditional (indices clamped), so the compiler
+  // counts the loads in flight exactly and never waits for a younger stage.
+
+  if (wave == kWideWaves) {
+    // loader: the queries of iteration `it` go to slot it & 1
+    u32x4_t r0[MT * 8], r1[MT * 8];
+    auto fetch = [&](u32x4_t(&r)[MT * 8], int it) {
+      const int kb = (it < nit ? it : nit - 1) % nkb;
+      const u32x4_t* p = pk + (int64_t)kb * QW + lane;
+#pragma unroll
+      for (int j = 0; j < MT * 8; ++j) r[j] = ld16(p + j * 64);
+    };
+    fetch(r0, 0);
+    fetch(r1, 1);
+    int it = 0;
+    for (; it + 2 <= nit; it += 2) {
+#pragma unroll
+      for (int j = 0; j < MT * 8; ++j) qs[0][j * 64 + lane] = r0[j];
+      fetch(r0, it + 2);
+      lds_barrier();
+#pragma unroll
+      for (int j = 0; j < MT * 8; ++j) qs[1][j * 64 + lane] = r1[j];
+      fetch(r1, it + 3);
+      lds_barrier();
+    }
+    if (it < nit) {
+#pragma unroll
+      for (int j = 0; j < MT * 8; ++j) qs[0][j * 64 + lane] = r0[j];
+      lds_barrier();
+    }
+    return;
+  }
+
+  typedef typename Mfma<St>::B B;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t tok0 = (int64_t)blockIdx.x * (16 * kWideWaves) + wave * 16;
+  const int64_t tokc = tok0 + col < T ? tok0 + col : T - 1;  // clamped row; results of such lanes are dropped
+  const St* row = src + tokc * d;
+  float* zw = zs + wave * (16 * S * n);
+  B b[D][4];
+  auto issue = [&](B(&bs)[4], int it) {
+    it = it < nit ? it : nit - 1;
+    const int i = it / nkb;
+    const int kb = it - i * nkb;
+    const St* base = row + (int64_t)i * stride;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      // raw load: chunks past the end of d are zeroed when the stage is used,
+      // so that nothing here waits for the data
+      const int c0 = kb * kKBlock + s4 * 4 + grp;
+      bs[s4] = Mfma<St>::load_b(base + (c0 < C ? c0 : C - 1) * 8, true);
+    }
+  };
+
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[MT], P[MT], Q[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = P[m] = Q[m] = zero4;
+  float ss = 0.f, PS = 0.f, QS = 0.f;
+
+  // one iteration: wait for the queries, then the matrix-core work on the
+  // oldest ring stage, then the per-class / per-source bookkeeping
+  auto step = [&](B(&bs)[4], const u32x4_t* slot, int it) {
+    const int i = it / nkb;
+    const int kb = it - i * nkb;
+    int w;
+    bool last;
+    ko.at(kb, w, last);
+    if ((kb + 1) * kKBlock > C) {  // the K-block runs past the end of d
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        if (kb * kKBlock + s4 * 4 + grp >= C) bs[s4] = Mfma<St>::zero_b();
+    }
+    // all query fragments of the K-block first: the LDS latency is paid once
+    // per K-block, not once per matrix-core step
+    typename Mfma<St>::A a[4][MT];
+    const u32x4_t* q = slot + lane;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const u32x4_t* qp = q + ((m * 4 + s4) * 2) * 64;
+        a[s4][m] = Mfma<St>::from_halves(qp[0], qp[64]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      Mfma<St>::sumsq(bs[s4], ss);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) Mfma<St>::mma(acc[m], a[s4][m], bs[s4]);
+    }
+    if (last) {
+      float sw = ss;
+      sw += __shfl_xor(sw, 16, 64);
+      sw += __shfl_xor(sw, 32, 64);
+      if (w == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) P[m] = acc[m];
+        PS = sw;
+      } else if (w == 1) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) Q[m] = acc[m];
+        QS = sw;
+      } else if (w == 2) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) P[m] += acc[m];
+        PS += sw;
+      } else {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) Q[m] += acc[m];
+        QS += sw;
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = zero4;
+      ss = 0.f;
+    }
+    if (kb == nkb - 1) {
+      // source i done: z = Z / r(u_i), kept in LDS until the softmax
+      const float r = sqrtf((PS + QS) / (float)d + eps);
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int qi = m * 16 + grp * 4 + rr;
+          if (qi < S) zw[(col * S + qi) * n + i] = (P[m][rr] + Q[m][rr]) / r;
+        }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) P[m] = Q[m] = zero4;
+      PS = QS = 0.f;
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < D - 1; ++s) issue(b[s], s);
+  int it0 = 0;
+  for (; it0 + D <= nit; it0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      issue(b[(s + D - 1) % D], it0 + s + D - 1);
+      lds_barrier();  // the queries of this K-block are in slot s & 1
+      step(b[s], qs[s & 1], it0 + s);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < D - 1; ++s)  // tail: every stage is already loaded
+    if (it0 + s < nit) {
+      lds_barrier();
+      step(b[s], qs[s & 1], it0 + s);
+    }
+
+  // softmax over the n sources of every (token, query) pair of the tile (the
+  // wave reads back only what it wrote, in program order)
+  for (int pidx = lane; pidx < 16 * S; pidx += 64) {
+    const int t = pidx / S, qi = pidx - t * S;
+    const int64_t tok = tok0 + t;
+    if (tok >= T) continue;
+    const float* z = zw + pidx * n;
+    float mx = z[0];
+    for (int i = 1; i < n; ++i) mx = fmaxf(mx, z[i]);
+    float l = 0.f;
+    for (int i = 0; i < n; ++i) l += expf(z[i] - mx);
+    float* a = alpha + (tok * S + qi) * n;
+    for (int i = 0; i < n; ++i) a[i] = expf(z[i] - mx) / l;
+    if (m_out) m_out[(int64_t)qi * T + tok] = mx;
+    lse_out[(int64_t)qi * T + tok] = mx + logf(l);
   }
 }
 
@@ -480,7 +740,7 @@ __global__ __launch_bounds__(256) void k_phase1_single(const St* __restrict__ sr
   float* red2 = zb + 16 * kSingleNP;             // 2 x 8 floats for the PreNorm reduction
   const int64_t tok0 = (int64_t)blockIdx.x * 16;
   score_all<St, 1, false, true>(src, n, stride, T, d, w, kg, nullptr, 1, eps, tok0, red, zb, kSingleNP);
-  __syncthreads();
+  lds_barrier();
   if (threadIdx.x < 16) {
     float* row = zb + threadIdx.x * kSingleNP;
     float mx = row[0];
@@ -498,7 +758,7 @@ __global__ __launch_bounds__(256) void k_phase1_single(const St* __restrict__ sr
       if (lse_out) lse_out[tok] = mx + logf(l);
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (!h_out && !x_out) return;  // statistics only (uniform)
 
   const int C = d >> 3;
@@ -571,11 +831,17 @@ __global__ __launch_bounds__(256) void k_phase1_single(const St* __restrict__ sr
 // ---------------------------------------------------------------------------
 // launchers
 
+// Allow `dynamic` bytes of dynamic LDS when a launch needs more than 64 KiB
+// in total (static + dynamic).
+template <typename Kern>
+static hipError_t set_lds(Kern k, size_t dynamic, size_t total) {
+  if (total <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)dynamic);
+}
 template <typename Kern>
 static hipError_t set_lds(Kern k, size_t bytes) {
-  if (bytes <= 65536) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)bytes);
+  return set_lds(k, bytes, bytes);
 }
 
 template <typename St, int N>
@@ -608,20 +874,33 @@ template <typename St, int MT>
 static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, int d, const float* w,
                             const float* kg, int S, float eps, void* out, float* m_out, float* lse_out,
                             float* ws, hipStream_t stream) {
-  // workspace: packed queries first, then the softmax weights
+  // workspace: packed queries first (room for 32 queries), then the softmax
+  // weights
+  const int nkb = ((d >> 3) + kKBlock - 1) / kKBlock;
   u32x4_t* pk = reinterpret_cast<u32x4_t*>(ws);
-  float* al = ws + (int64_t)16 * MT * (d >> 3) * 8;
-  const int npk = 16 * MT * (d >> 3);
+  float* al = ws + (int64_t)nkb * kPackedKBlockWords * 4;
+  const int npk = nkb * MT * 4 * 64;
   hipLaunchKernelGGL((k_pack_queries<St, MT>), dim3((unsigned)((npk + 255) / 256)), dim3(256), 0, stream, w, kg,
                      S, d, pk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = sizeof(float) * (2 * Red<MT, kGroup>::kSlot + 16 * 16 * MT * n);
-  auto ks = k_p1_scores<St, MT>;
-  e = set_lds(ks, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ks, dim3((unsigned)((T + 15) / 16)), dim3(256), lds, stream, static_cast<const St*>(src),
-                     n, stride, T, d, pk, S, eps, al, m_out, lse_out);
+  const int64_t wide_groups = (T + 16 * kWideWaves - 1) / (16 * kWideWaves);
+  if (wide_groups >= device_cu_count()) {
+    // enough 64-token tiles for one workgroup per compute unit
+    const size_t zl = sizeof(float) * kWideWaves * 16 * S * n;
+    auto kw = k_p1_scores_wide<St, MT>;
+    e = set_lds(kw, zl, zl + sizeof(u32x4_t) * 2 * MT * 512);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kw, dim3((unsigned)wide_groups), dim3(64 * (kWideWaves + 1)), zl, stream,
+                       static_cast<const St*>(src), n, stride, T, d, pk, S, eps, al, m_out, lse_out);
+  } else {
+    const size_t lds = sizeof(float) * (2 * Red<MT, kGroup>::kSlot + 16 * 16 * MT * n);
+    auto ks = k_p1_scores<St, MT>;
+    e = set_lds(ks, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ks, dim3((unsigned)((T + 15) / 16)), dim3(256), lds, stream, static_cast<const St*>(src),
+                       n, stride, T, d, pk, S, eps, al, m_out, lse_out);
+  }
   e = hipGetLastError();
   if (e != hipSuccess || out == nullptr) return e;  // statistics only
   return pick_out<St>(n, src, stride, T, d, al, S, out, stream);
