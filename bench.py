@@ -129,6 +129,109 @@ def long_prefill_report(w, dev):
     return res
 
 
+def _time(fn, steps: int) -> float:
+    """Seconds per call of ``fn`` over ``steps`` calls, GPU-synchronised."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        fn(k)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def other_workloads(dev, steps: int):
+    """Shorter measurements of the other hot-path shapes, each pass over
+    resident inputs: the decode-shaped block step (eager launches and one
+    HIP-graph replay per pass), Full AttnRes one-shot sites, and one GPU's
+    token share (2048 tokens) of the 16K chunk.  Working sets that fit the
+    256 MB last-level cache rotate over 4 input replicas so that every pass
+    reads from HBM."""
+    import torch
+    import synth
+    import transformer_depth_wise_amd as tdw
+
+    res = {}
+
+    def block_states(w, replicas):
+        sts, subs = [], []
+        prm = synth.params(w, dev)
+        scales = synth.sublayer_scales(w)
+        for r in range(replicas):
+            st = tdw.BlockAttnRes(w.T, w.d, w.block_sizes, w.torch_dtype, n_given=w.n_given, eps=w.eps,
+                                  device=dev, final_site=w.final_site)
+            st.reps[0].copy_(synth.embedding(w, 0, w.T, dev))
+            for n in range(w.n_given):
+                st.reps[1 + n].copy_(synth.given_block(w, n + 1, 0, w.T, dev))
+            v = [synth.sublayer_output(w, l + 1, 0, w.T, dev, scales) for l in range(w.L)]
+            sts.append(st)
+            subs.append(lambda l, x, v=v: v[l])
+        return sts, subs, prm
+
+    def summary(w, st, sec):
+        b = sum(x.bytes for x in st.plan())
+        return {"config": {"T": w.T, "d": w.d, "blocks": list(w.block_sizes), "given_blocks": w.n_given},
+                "ms_per_step": round(sec * 1e3, 4), "value": round(w.T * w.L / sec, 1),
+                "unit": "token-sublayers/s", "hbm_gbps": round(b / sec / 1e9, 1),
+                "bytes_per_step": b}
+
+    # decode-shaped block step: T=256, one block of 24, 7 given block sums
+    w = synth.WORKLOADS["decode_block_bf16"]
+    sts, subs, prm = block_states(w, 4)
+    for k in range(4):
+        sts[k].forward(prm, subs[k])
+    eager = _time(lambda k: sts[k % 4].forward(prm, subs[k % 4]), max(steps, 20))
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for k in range(4):
+            sts[k].forward(prm, subs[k])
+    torch.cuda.current_stream().wait_stream(side)
+    for k in range(4):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sts[k].forward(prm, subs[k])
+        graphs.append(g)
+    replay = _time(lambda k: graphs[k % 4].replay(), max(steps, 20))
+    res[w.name] = summary(w, sts[0], eager)
+    res[w.name]["launches_per_step"] = len(sts[0].plan())
+    res[w.name]["graph_replay"] = {"ms_per_step": round(replay * 1e3, 4),
+                                   "value": round(w.T * w.L / replay, 1),
+                                   "hbm_gbps": round(res[w.name]["bytes_per_step"] / replay / 1e9, 1)}
+    del graphs, sts, subs
+
+    # Full AttnRes: every sublayer output its own source, one-shot per site
+    w = synth.WORKLOADS["full_bf16"]
+    prm = synth.params(w, dev)
+    scales = synth.sublayer_scales(w)
+    fulls = []
+    for r in range(4):
+        f = tdw.FullAttnRes(w.T, w.d, w.L, w.torch_dtype, eps=w.eps, device=dev, final_site=w.final_site)
+        f.hist[0].copy_(synth.embedding(w, 0, w.T, dev))
+        for l in range(w.L):
+            f.hist[l + 1].copy_(synth.sublayer_output(w, l + 1, 0, w.T, dev, scales))
+        fulls.append(f)
+    noop = lambda l, x: None  # noqa: E731  (outputs are resident in hist)
+    for f in fulls:
+        f.forward(prm, noop)
+    sec = _time(lambda k: fulls[k % 4].forward(prm, noop), max(steps, 20))
+    b = sum(x.bytes for x in fulls[0].plan())
+    res[w.name] = {"config": {"T": w.T, "d": w.d, "sublayers": w.L}, "ms_per_step": round(sec * 1e3, 4),
+                   "value": round(w.T * w.L / sec, 1), "unit": "token-sublayers/s",
+                   "hbm_gbps": round(b / sec / 1e9, 1), "bytes_per_step": b,
+                   "note": "one-shot sites re-read earlier outputs; those re-reads partly hit the last-level cache"}
+    del fulls
+
+    # one GPU's share (16384 / 8 tokens) of the 16K chunk
+    w = synth.scaled(synth.WORKLOADS["prefill_chunk_bf16"], T=2048, name="prefill_share_2048")
+    sts, subs, prm = block_states(w, 1)
+    sts[0].forward(prm, subs[0])
+    sec = _time(lambda k: sts[0].forward(prm, subs[0]), steps)
+    res[w.name] = summary(w, sts[0], sec)
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +240,7 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill_chunk_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the decode / Full / per-GPU-share workloads")
     ap.add_argument("--probe", choices=["copy"], default=None,
                     help="run only a plain device copy of known size (counter calibration)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -297,6 +401,10 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, emb, v, prm, args.cpu_seconds)
+    if not args.no_other:
+        del v, st, emb, sub, given
+        torch.cuda.empty_cache()
+        out["other_workloads"] = other_workloads(dev, args.steps)
     print(json.dumps(out), flush=True)
     return 0
 

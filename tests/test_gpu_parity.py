@@ -213,6 +213,51 @@ def test_token_split_invariance():
         assert torch.equal(s2.h_final, whole[a:b])
 
 
+# ------------------------------------------------ decode step as a HIP graph
+def test_decode_step_graph_replay_matches_eager():
+    """The decode-shaped block step (T=256, one block of 24, 7 given block
+    sums) captured once as a HIP graph: every replay, with eager work in
+    between that overwrites all outputs, reproduces the eager pass bit for bit."""
+    w = synth.WORKLOADS["decode_block_bf16"]
+    _say("case decode step graph replay T=%d" % w.T)
+    dev = torch.device("cuda")
+    from harness import block_inputs
+    emb, given, v = block_inputs(w, dev)
+    prm = synth.params(w, dev)
+    st = tdw.BlockAttnRes(w.T, w.d, w.block_sizes, w.torch_dtype, n_given=w.n_given, eps=w.eps, device=dev,
+                          x_ring=w.L, final_site=w.final_site)
+    st.reps[0].copy_(emb)
+    for n, b in enumerate(given):
+        st.reps[1 + n].copy_(b)
+    sub = lambda l, x: v[l]  # noqa: E731
+    st.forward(prm, sub)
+    torch.cuda.synchronize()
+    # outputs of the pass (the decode step has no final aggregation site)
+    outs = lambda: [st.reps, st.x] + ([st.h_final] if w.final_site else [])  # noqa: E731
+    ref = [t.clone() for t in outs()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.forward(prm, sub)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.forward(prm, sub)
+    for k in range(3):
+        st.h_final.fill_(float(k + 1))
+        st.x.fill_(-1.0 - k)
+        st.reps[1 + w.n_given:].fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("reps", "x", "h_final"), ref, outs()):
+            if not torch.equal(a, b):
+                bad = (a != b).nonzero()
+                raise AssertionError("replay %d: %s differs at %d places, first %s: %r vs %r (max |diff| %.3e)"
+                                     % (k, name, bad.shape[0], bad[0].tolist(), a[tuple(bad[0])].item(),
+                                        b[tuple(bad[0])].item(), (a.float() - b.float()).abs().max().item()))
+
+
 # ------------------------- phase 1 over long token ranges (wide-tile scoring)
 WIDE = [
     # (dtype, d, n_src, S): ragged last K-block, single query, fp32, largest LDS use
