@@ -124,10 +124,13 @@ int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int6
  *   partition (output normalised, lse = its log-sum-exp).
  *   If sublayer_prev == NULL (first sublayer of the block): h = o.
  *   Otherwise the partial sum is
- *       p = (partial_in or 0) + sublayer_prev        (fp32 arithmetic)
- *   partial_in: [T][d] in format partial_dt (F32, P24, or dt itself for a
- *   sublayer output; NULL = zero); sublayer_prev: [T][d] of dtype dt (the
- *   previous sublayer's output).  p is written to partial_out in format
+ *       p = ((partial_in or 0) + (sublayer_prev2 or 0)) + sublayer_prev
+ *   in fp32 arithmetic, in that order.  partial_in: [T][d] in format
+ *   partial_dt (F32, P24, or dt itself for a sublayer output; NULL = zero);
+ *   sublayer_prev, sublayer_prev2: [T][d] of dtype dt (the outputs of the
+ *   previous and the one-before-previous sublayer; sublayer_prev2 NULL =
+ *   zero).  With sublayer_prev2 a caller can store the running partial only
+ *   at every second sublayer.  p is written to partial_out in format
  *   partial_out_dt (F32 or P24; NULL = not stored); partial_out may be the
  *   same pointer as partial_in when both formats are the same (in place).
  *   Merge: zc = w^T(key_gain (.) p / r(p)), M = max(lse, zc),
@@ -135,12 +138,13 @@ int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int6
  *   PreNorm: x = prenorm_gain (.) h / r(h)  (prenorm_gain NULL = ones).
  *   h_out, x_out: [T][d] dtype dt, either may be NULL but not both.
  *   w, key_gain, prenorm_gain: [d] fp32 (key_gain NULL = ones).
- * Passing partial_in or partial_out without sublayer_prev is ATTNRES_EINVAL.
+ * Passing partial_in, sublayer_prev2 or partial_out without sublayer_prev
+ * is ATTNRES_EINVAL.
  */
 attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d,
                                       const void* p1_out, const float* p1_lse,
                                       attnres_dtype_t partial_dt, const void* partial_in,
-                                      const void* sublayer_prev,
+                                      const void* sublayer_prev2, const void* sublayer_prev,
                                       attnres_dtype_t partial_out_dt, void* partial_out,
                                       const float* w, const float* key_gain,
                                       const float* prenorm_gain, float eps,
@@ -165,14 +169,15 @@ attnres_status_t attnres_full(attnres_dtype_t dt,
 
 /*
  * Block completion ("Attention Residuals" notes, section 8: b_n is the sum of
- * the block's sublayer outputs):  out = (partial_in or 0) + v.
+ * the block's sublayer outputs):
+ *     out = ((partial_in or 0) + (v2 or 0)) + v      (fp32, in that order)
  *   partial_in: [T][d] in format partial_dt (F32, P24 or dt; NULL = zero);
- *   v, out: [T][d] dtype dt.  out may be the same pointer as partial_in when
- *   partial_dt == dt.
+ *   v2 (NULL = zero), v, out: [T][d] dtype dt.  out may be the same pointer
+ *   as partial_in when partial_dt == dt; out must not overlap v or v2.
  */
 attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t d,
                                           attnres_dtype_t partial_dt, const void* partial_in,
-                                          const void* v, void* out, void* stream);
+                                          const void* v2, const void* v, void* out, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* attnres_status_string(attnres_status_t status);

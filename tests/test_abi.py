@@ -102,9 +102,9 @@ def test_phase1_validation(lib):
     assert phase1(lib, T=0, src=None, out=None, lse=None) == 0
 
 
-def merge(lib, dt=1, T=1024, d=64, o=A, lse=2 * A, pdt=0, pin=None, v=None, podt=0, pout=None, w=3 * A,
+def merge(lib, dt=1, T=1024, d=64, o=A, lse=2 * A, pdt=0, pin=None, v2=None, v=None, podt=0, pout=None, w=3 * A,
           kg=None, gm=None, h=None, x=4 * A):
-    return checked(lib.attnres_phase2_merge(dt, T, d, p(o), p(lse), pdt, p(pin), p(v), podt, p(pout), p(w),
+    return checked(lib.attnres_phase2_merge(dt, T, d, p(o), p(lse), pdt, p(pin), p(v2), p(v), podt, p(pout), p(w),
                                             p(kg), p(gm), 1e-6, p(h), p(x), None))
 
 
@@ -112,6 +112,11 @@ def test_merge_validation(lib):
     assert merge(lib, x=None) == EINVAL                    # no output at all
     assert merge(lib, pin=5 * A) == EINVAL                 # partial without the previous output
     assert merge(lib, pout=5 * A) == EINVAL
+    assert merge(lib, v2=6 * A) == EINVAL                  # two-before-previous output without the previous
+    assert merge(lib, v=6 * A, v2=7 * A, pin=5 * A, pout=5 * A, pdt=2, podt=2, x=6 * A + 64) == EALIAS
+    assert merge(lib, v=6 * A, v2=7 * A + 8) == EALIGN     # every row pointer 16-byte aligned
+    assert merge(lib, v=6 * A, v2=7 * A, x=7 * A + 1024 * 64) == EALIAS  # output over the end of v2
+    assert merge(lib, T=0, v=6 * A, v2=7 * A, pin=5 * A, pout=5 * A, pdt=2, podt=2) == 0
     assert merge(lib, pdt=9) == EDTYPE
     assert merge(lib, d=20) == EALIGN
     assert merge(lib, x=A + 64) == EALIAS                  # output over the phase-1 input
@@ -139,7 +144,8 @@ def test_full_and_accumulate_validation(lib):
     assert f(d=4) == EALIGN
     assert f(T=0) == 0
     acc = lambda **k: checked(lib.attnres_block_accumulate(k.get("dt", 1), k.get("T", 64), k.get("d", 64), k.get("pdt", 0),
-                                                   p(k.get("pin")), p(k.get("v", A)), p(k.get("out", 2 * A)), None))
+                                                   p(k.get("pin")), p(k.get("v2")), p(k.get("v", A)),
+                                                   p(k.get("out", 2 * A)), None))
     assert acc(v=None) == EINVAL
     assert acc(out=A) == EALIAS
     assert acc(pin=2 * A, pdt=0) == EALIAS          # in place only with the same dtype
@@ -147,6 +153,9 @@ def test_full_and_accumulate_validation(lib):
     assert acc(dt=3) == EDTYPE
     assert acc(dt=2) == EDTYPE                      # P24 only for the partial
     assert acc(T=0, pin=5 * A, pdt=2) == 0
+    assert acc(v2=2 * A + 64) == EALIAS             # out over v2
+    assert acc(v2=3 * A + 4) == EALIGN
+    assert acc(T=0, pin=5 * A, pdt=2, v2=3 * A) == 0
 
 
 def test_status_strings(lib):

@@ -48,9 +48,9 @@ def load(path: Optional[str] = None):
     lib.attnres_phase1.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V, I, V]
     lib.attnres_phase1_workspace_bytes.argtypes = [I, I, I, I]
     lib.attnres_phase1_workspace_bytes.restype = ctypes.c_int64
-    lib.attnres_phase2_merge.argtypes = [E, I, I, V, V, E, V, V, E, V, V, V, V, F, V, V, V]
+    lib.attnres_phase2_merge.argtypes = [E, I, I, V, V, E, V, V, V, E, V, V, V, V, F, V, V, V]
     lib.attnres_full.argtypes = [E, V, I, I, I, I, V, V, V, F, V, V, V, V]
-    lib.attnres_block_accumulate.argtypes = [E, I, I, E, V, V, V, V]
+    lib.attnres_block_accumulate.argtypes = [E, I, I, E, V, V, V, V, V]
     for fn in ("attnres_phase1", "attnres_phase2_merge", "attnres_full", "attnres_block_accumulate"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.attnres_status_string.argtypes = [ctypes.c_int]
@@ -123,17 +123,18 @@ def attnres_phase2_merge(p1_out: torch.Tensor, p1_lse: torch.Tensor, partial_in:
                          sublayer_prev: Optional[torch.Tensor], partial_out: Optional[torch.Tensor],
                          w: torch.Tensor, key_gain: Optional[torch.Tensor], prenorm_gain: Optional[torch.Tensor],
                          eps: float, h_out: Optional[torch.Tensor], x_out: Optional[torch.Tensor],
-                         stream=None) -> None:
+                         stream=None, sublayer_prev2: Optional[torch.Tensor] = None) -> None:
     """p1_out: [T, d]; p1_lse: [T]; partial_in: [T, d] fp32 / storage dtype, or
-    a P24 buffer; sublayer_prev: [T, d]; partial_out: [T, d] fp32 or a P24
-    buffer; w, key_gain, prenorm_gain: [d]."""
+    a P24 buffer; sublayer_prev, sublayer_prev2: [T, d] (partial sum
+    p = partial_in + sublayer_prev2 + sublayer_prev, absent terms zero);
+    partial_out: [T, d] fp32 or a P24 buffer; w, key_gain, prenorm_gain: [d]."""
     T, d = p1_out.shape
     pdt = dtype_code(partial_in.dtype) if partial_in is not None else F32
     podt = dtype_code(partial_out.dtype) if partial_out is not None else F32
     rc = load().attnres_phase2_merge(dtype_code(p1_out.dtype), T, d, _ptr(p1_out), _ptr(p1_lse), pdt,
-                                     _ptr(partial_in), _ptr(sublayer_prev), podt, _ptr(partial_out), _ptr(w),
-                                     _ptr(key_gain), _ptr(prenorm_gain), eps, _ptr(h_out), _ptr(x_out),
-                                     _stream(stream))
+                                     _ptr(partial_in), _ptr(sublayer_prev2), _ptr(sublayer_prev), podt,
+                                     _ptr(partial_out), _ptr(w), _ptr(key_gain), _ptr(prenorm_gain), eps,
+                                     _ptr(h_out), _ptr(x_out), _stream(stream))
     _check("attnres_phase2_merge", rc)
 
 
@@ -149,10 +150,11 @@ def attnres_full(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optio
 
 
 def attnres_block_accumulate(partial_in: Optional[torch.Tensor], v: torch.Tensor, out: torch.Tensor,
-                             stream=None) -> None:
-    """out = (partial_in or 0) + v; all [T, d] (partial_in may be a P24 buffer)."""
+                             stream=None, v2: Optional[torch.Tensor] = None) -> None:
+    """out = (partial_in or 0) + (v2 or 0) + v; all [T, d] (partial_in may be
+    a P24 buffer)."""
     T, d = v.shape
     pdt = dtype_code(partial_in.dtype) if partial_in is not None else F32
-    rc = load().attnres_block_accumulate(dtype_code(v.dtype), T, d, pdt, _ptr(partial_in), _ptr(v), _ptr(out),
-                                         _stream(stream))
+    rc = load().attnres_block_accumulate(dtype_code(v.dtype), T, d, pdt, _ptr(partial_in), _ptr(v2), _ptr(v),
+                                         _ptr(out), _stream(stream))
     _check("attnres_block_accumulate", rc)

@@ -151,7 +151,8 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_s
 
 attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, const void* p1_out,
                                       const float* p1_lse, attnres_dtype_t partial_dt, const void* partial_in,
-                                      const void* sublayer_prev, attnres_dtype_t partial_out_dt, void* partial_out,
+                                      const void* sublayer_prev2, const void* sublayer_prev,
+                                      attnres_dtype_t partial_out_dt, void* partial_out,
                                       const float* w, const float* key_gain, const float* prenorm_gain, float eps,
                                       void* h_out, void* x_out, void* stream) {
   if (!dtype_ok(dt) || !partial_ok(partial_dt, dt)) return ATTNRES_EDTYPE;
@@ -159,17 +160,20 @@ attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, 
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
   if (T < 0 || !(eps >= 0.f)) return ATTNRES_EINVAL;
-  if (!sublayer_prev && (partial_in || partial_out)) return ATTNRES_EINVAL;
+  if (!sublayer_prev && (partial_in || partial_out || sublayer_prev2)) return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!p1_out || !p1_lse || (!h_out && !x_out)) return ATTNRES_EINVAL;
   if (sublayer_prev && !w) return ATTNRES_EINVAL;
-  st = check_align({p1_out, partial_in, sublayer_prev, partial_out, w, key_gain, prenorm_gain, h_out, x_out}, {p1_lse});
+  st = check_align({p1_out, partial_in, sublayer_prev2, sublayer_prev, partial_out, w, key_gain, prenorm_gain, h_out,
+                    x_out},
+                   {p1_lse});
   if (st != ATTNRES_OK) return st;
   const int64_t es = esize(dt);
   const int64_t rows = T * d;
   const Range r_o = range_of(p1_out, rows * es), r_l = range_of(p1_lse, T * 4);
   const Range r_pi = partial_in ? range_of(partial_in, rows * esize(partial_dt)) : Range{0, 0};
   const Range r_v = sublayer_prev ? range_of(sublayer_prev, rows * es) : Range{0, 0};
+  const Range r_v2 = sublayer_prev2 ? range_of(sublayer_prev2, rows * es) : Range{0, 0};
   const Range r_po = partial_out ? range_of(partial_out, rows * esize(partial_out_dt)) : Range{0, 0};
   const Range r_w = w ? range_of(w, d * 4) : Range{0, 0};
   const Range r_g = key_gain ? range_of(key_gain, d * 4) : Range{0, 0};
@@ -180,13 +184,14 @@ attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, 
   const bool in_place = partial_out && partial_in == static_cast<const void*>(partial_out) &&
                         partial_dt == partial_out_dt;
   for (Range o : {r_h, r_x, r_po})
-    for (Range i : {r_o, r_l, r_pi, r_v, r_w, r_g, r_gm}) {
+    for (Range i : {r_o, r_l, r_pi, r_v, r_v2, r_w, r_g, r_gm}) {
       if (in_place && o.lo == r_po.lo && o.hi == r_po.hi && i.lo == r_pi.lo && i.hi == r_pi.hi) continue;
       if (overlaps(o, i)) return ATTNRES_EALIAS;
     }
   if (overlaps(r_h, r_x) || overlaps(r_h, r_po) || overlaps(r_x, r_po)) return ATTNRES_EALIAS;
   return hip_status(attnres::launch_merge(kind_of(dt), T, (int)d, p1_out, p1_lse, kind_of(partial_dt), partial_in,
-                                          sublayer_prev, kind_of(partial_out_dt), partial_out, w, key_gain,
+                                          sublayer_prev2, sublayer_prev, kind_of(partial_out_dt), partial_out, w,
+                                          key_gain,
                                           x_out ? prenorm_gain : nullptr, eps, h_out, x_out,
                                           static_cast<hipStream_t>(stream)));
 }
@@ -223,23 +228,25 @@ attnres_status_t attnres_full(attnres_dtype_t dt, const void* src, int64_t n_src
 }
 
 attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t d, attnres_dtype_t partial_dt,
-                                          const void* partial_in, const void* v, void* out, void* stream) {
+                                          const void* partial_in, const void* v2, const void* v, void* out,
+                                          void* stream) {
   if (!dtype_ok(dt) || !partial_ok(partial_dt, dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
   if (T < 0) return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!v || !out) return ATTNRES_EINVAL;
-  st = check_align({partial_in, v, out});
+  st = check_align({partial_in, v2, v, out});
   if (st != ATTNRES_OK) return st;
   const int64_t rows = T * d;
   const Range ro = range_of(out, rows * esize(dt));
   const Range rv = range_of(v, rows * esize(dt));
   const Range rp = partial_in ? range_of(partial_in, rows * esize(partial_dt)) : Range{0, 0};
-  if (overlaps(ro, rv)) return ATTNRES_EALIAS;
+  const Range rv2 = v2 ? range_of(v2, rows * esize(dt)) : Range{0, 0};
+  if (overlaps(ro, rv) || overlaps(ro, rv2)) return ATTNRES_EALIAS;
   const bool in_place = partial_in == out && partial_dt == dt;
   if (!in_place && overlaps(ro, rp)) return ATTNRES_EALIAS;
-  return hip_status(attnres::launch_accumulate(kind_of(dt), T, (int)d, kind_of(partial_dt), partial_in, v, out,
+  return hip_status(attnres::launch_accumulate(kind_of(dt), T, (int)d, kind_of(partial_dt), partial_in, v2, v, out,
                                                static_cast<hipStream_t>(stream)));
 }
 

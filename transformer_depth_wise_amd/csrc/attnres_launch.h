@@ -23,11 +23,11 @@ hipError_t launch_phase1_single(Dtype dt, const void* src, int n, int64_t stride
                                 hipStream_t stream);
 
 hipError_t launch_merge(Dtype dt, int64_t T, int d, const void* o1, const float* lse1,
-                        Dtype pdt, const void* pin, const void* vprev, Dtype podt, void* pout,
+                        Dtype pdt, const void* pin, const void* vprev2, const void* vprev, Dtype podt, void* pout,
                         const float* w, const float* kg, const float* gamma, float eps,
                         void* h_out, void* x_out, hipStream_t stream);
 
-hipError_t launch_accumulate(Dtype dt, int64_t T, int d, Dtype pdt, const void* pin, const void* v,
-                             void* out, hipStream_t stream);
+hipError_t launch_accumulate(Dtype dt, int64_t T, int d, Dtype pdt, const void* pin, const void* v2,
+                             const void* v, void* out, hipStream_t stream);
 
 }  // namespace attnres

@@ -18,7 +18,10 @@ intra-block partial sum ``partial``, and a small ring of PreNorm outputs
 24-sublayer block drifts by several percent of the row maximum.  It is kept in
 the 24-bit split format (P24, 3 bytes per element, relative step 2^-16) for
 bf16 rows and in fp32 for fp32 rows; block sums are rounded to the storage
-dtype once, when they are complete.
+dtype once, when they are complete.  The partial is stored only at the even
+positions j = 2, 4, ... of a block: sublayer j + 1 reads it with v_j and
+writes nothing, sublayer j + 2 reads it with v_j and v_{j+1} and stores the
+next one, so the two latest sublayer outputs must stay valid.
 
 ``plan()`` lists every launch of a pass with its algorithmic bytes (each row
 the method must read or write, counted once).
@@ -128,20 +131,24 @@ class BlockAttnRes:
                 out.append(Launch("phase1", n_done * r + S * (r + 2 * stat)))
             for j in range(S):
                 if j == 0:
-                    b = 2 * r + stat
+                    b = 2 * r + stat                  # o; x
                 elif j == 1:
-                    b = 3 * r + stat
+                    b = 3 * r + stat                  # o, v0; x
                 elif j == 2:
-                    b = 4 * r + r32 + stat
+                    b = 4 * r + r32 + stat            # o, v0, v1; p, x
+                elif j % 2:
+                    b = 3 * r + r32 + stat            # o, p, v; x
                 else:
-                    b = 3 * r + 2 * r32 + stat
+                    b = 4 * r + 2 * r32 + stat        # o, p, v, v; p, x
                 out.append(Launch("phase2", b))
             if S == 1:
                 out.append(Launch("accumulate", 2 * r))
             elif S == 2:
                 out.append(Launch("accumulate", 3 * r))
+            elif S % 2:
+                out.append(Launch("accumulate", 2 * r + r32))   # p (stored at S-1), v; b
             else:
-                out.append(Launch("accumulate", 2 * r + r32))
+                out.append(Launch("accumulate", 3 * r + r32))   # p (stored at S-2), v, v; b
             n_done += 1
         if self.final_site:
             out.append(Launch("final", (n_done + 1) * r + stat))
@@ -175,43 +182,39 @@ class BlockAttnRes:
                            None if single else self.o1[:S], self.m1[:S], self.lse1[:S], self.workspace,
                            stream=stream)
             mark("phase1", False)
-            # outputs of the block kept alive: the first two (for the first
-            # fp32 partial sum) and the previous one
-            first = second = prev = None
+            # the two latest outputs of the block stay alive (prev2, prev)
+            prev2 = prev = None
             for j in range(S):
                 site = l0 + j
                 x = self.x[site % nx]
                 kg = None if g is None else g[site]
                 pg = None if gam is None else gam[site]
-                if j == 0:
-                    pin, pout = None, None
-                elif j == 1:
-                    pin, pout = None, None
+                # the partial p_j = v_0 + ... + v_{j-1} is stored at even j >= 2
+                if j <= 1:
+                    pin, v2, pout = None, None, None            # p = v_0 (j = 1) or none
                 elif j == 2:
-                    pin, pout = first, self.partial
+                    pin, v2, pout = None, prev2, self.partial   # p = v_0 + v_1, stored
+                elif j % 2:
+                    pin, v2, pout = self.partial, None, None    # p = p_{j-1} + v_{j-1}
                 else:
-                    pin, pout = self.partial, self.partial
+                    pin, v2, pout = self.partial, prev2, self.partial  # p_{j-2} + v_{j-2} + v_{j-1}
                 mark("phase2", True)
                 o = self.reps[0] if single else self.o1[j]
                 attnres_phase2_merge(o, self.lse1[j], pin, prev, pout, w[site], kg, pg, eps,
-                                     self.h, x, stream=stream)
+                                     self.h, x, stream=stream, sublayer_prev2=v2)
                 mark("phase2", False)
                 if hook is not None:
                     hook(site, x=x, h=self.h, o1=o, lse1=self.lse1[j], m1=self.m1[j])
-                prev = sublayer(site, x)
-                if j == 0:
-                    first = prev
-                elif j == 1:
-                    second = prev
-                if j >= 2:
-                    first = second = None
+                prev2, prev = prev, sublayer(site, x)
             mark("accumulate", True)
             if S == 1:
                 attnres_block_accumulate(None, prev, self.reps[n_done], stream=stream)
             elif S == 2:
-                attnres_block_accumulate(first, prev, self.reps[n_done], stream=stream)
-            else:
+                attnres_block_accumulate(None, prev, self.reps[n_done], stream=stream, v2=prev2)
+            elif S % 2:
                 attnres_block_accumulate(self.partial, prev, self.reps[n_done], stream=stream)
+            else:
+                attnres_block_accumulate(self.partial, prev, self.reps[n_done], stream=stream, v2=prev2)
             mark("accumulate", False)
             n_done += 1
             l0 += S
