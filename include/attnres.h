@@ -75,6 +75,7 @@ typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1, ATTNRES_P24 = 2 } attnres_dtyp
 #define ATTNRES_MAX_D 16384
 #define ATTNRES_MAX_SOURCES 32          /* attnres_full / phase 1 with S == 1 */
 #define ATTNRES_MAX_SOURCES_MULTI 16    /* phase 1 with S >= 2 */
+#define ATTNRES_MAX_GROUP_SOURCES 16    /* attnres_phase2_merge_multi */
 
 /*
  * Phase 1 of a block ("Attention Residuals" notes, section 10, first phase;
@@ -149,6 +150,29 @@ attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d,
                                       const float* w, const float* key_gain,
                                       const float* prenorm_gain, float eps,
                                       void* h_out, void* x_out, void* stream);
+
+/*
+ * Phase 2 of the grouped two-phase Full AttnRes ("Attention Residuals" notes,
+ * section 7 for the sources, section 10 for the two phases; "Attention
+ * Residuals 阅读补充", static queries and two-phase computation): the
+ * sublayer's phase-1 partition (o = p1_out [T][d], lse = p1_lse [T], over the
+ * sources completed before its group) is merged with the n_src outputs
+ * produced inside the group so far, each its own source:
+ *     u_i = src + i*src_stride ([T][d] dtype dt), i < n_src,
+ *     z_i = w^T(key_gain (.) u_i / r(u_i)),  M = max(lse, z_i),
+ *     h = (e^{lse-M} o + sum_i e^{z_i-M} u_i) / (e^{lse-M} + sum_i e^{z_i-M}),
+ *     x = prenorm_gain (.) h / r(h).
+ *   0 <= n_src <= ATTNRES_MAX_GROUP_SOURCES (n_src = 0: h = o; src and w may
+ *   then be NULL).  w, key_gain, prenorm_gain: [d] fp32 (gains NULL = ones).
+ *   h_out, x_out: [T][d] dtype dt, either may be NULL but not both (x_out
+ *   NULL: no PreNorm).  Outputs must not overlap any input or each other.
+ */
+attnres_status_t attnres_phase2_merge_multi(attnres_dtype_t dt, int64_t T, int64_t d,
+                                            const void* p1_out, const float* p1_lse,
+                                            const void* src, int64_t n_src, int64_t src_stride,
+                                            const float* w, const float* key_gain,
+                                            const float* prenorm_gain, float eps,
+                                            void* h_out, void* x_out, void* stream);
 
 /*
  * One-shot depth aggregation with a single query ("Attention Residuals"

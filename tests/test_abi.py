@@ -25,10 +25,10 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attnres_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_every_entry_point():
     names = declared_functions()
-    for n in ("attnres_phase1", "attnres_phase2_merge", "attnres_full", "attnres_block_accumulate",
-              "attnres_status_string"):
+    for n in ("attnres_phase1", "attnres_phase1_workspace_bytes", "attnres_phase2_merge",
+              "attnres_phase2_merge_multi", "attnres_full", "attnres_block_accumulate", "attnres_status_string"):
         assert n in names
 
 
@@ -156,6 +156,26 @@ def test_full_and_accumulate_validation(lib):
     assert acc(v2=2 * A + 64) == EALIAS             # out over v2
     assert acc(v2=3 * A + 4) == EALIGN
     assert acc(T=0, pin=5 * A, pdt=2, v2=3 * A) == 0
+
+
+def test_merge_multi_validation(lib):
+    mm = lambda **k: checked(lib.attnres_phase2_merge_multi(
+        k.get("dt", 1), k.get("T", 64), k.get("d", 64), p(k.get("o", A)), p(k.get("lse", 2 * A)),
+        p(k.get("src", 3 * A)), k.get("n", 2), k.get("stride", 64 * 64), p(k.get("w", 4 * A)), None, None, 1e-6,
+        p(k.get("h")), p(k.get("x", 5 * A)), None))
+    assert mm(n=17) == EINVAL                        # more than ATTNRES_MAX_GROUP_SOURCES
+    assert mm(n=-1) == EINVAL
+    assert mm(src=None) == EINVAL                    # sources announced but absent
+    assert mm(w=None) == EINVAL
+    assert mm(stride=64) == EINVAL                   # source slabs overlap
+    assert mm(stride=64 * 64 + 4) == EALIGN
+    assert mm(x=None) == EINVAL                      # no output
+    assert mm(x=3 * A + 64 * 64 * 2) == EALIAS       # output over the second source
+    assert mm(h=5 * A + 64) == EALIAS                # the two outputs overlap
+    assert mm(dt=2) == EDTYPE
+    assert mm(d=12) == EALIGN
+    assert mm(T=0) == 0
+    assert mm(T=0, n=0, src=None, w=None, o=None, lse=None, x=None) == 0
 
 
 def test_status_strings(lib):

@@ -130,6 +130,20 @@ def test_full_edge_shapes(T, d, L):
     run_full_parity(w)
 
 
+@pytest.mark.parametrize("T,d,L,group", [(4096, 1024, 16, 4), (5, 8, 3, 2), (18, 200, 19, 5), (64, 1024, 9, 4),
+                                         (33, 7168, 6, 6), (40, 16384, 4, 3)])
+def test_full_grouped_two_phase(T, d, L, group):
+    """Grouped two-phase Full AttnRes (phase 1 per group + multi-source merge)
+    against the oracle's one-shot sites."""
+    base = synth.WORKLOADS["full_bf16"]
+    w = base if (T, d, L) == (base.T, base.d, base.L) else synth.scaled(
+        base, name="full_grouped", T=T, d=d, block_sizes=(1,) * L, seed=991 + L + d)
+    _say("case full grouped T=%d d=%d L=%d group=%d" % (T, d, L, group))
+    samples = synth.sample_tokens(w.T, 256) if w.T > 256 else None
+    worst = run_full_parity(w, samples, group=group)
+    _say("worst", worst)
+
+
 def test_empty_token_set_is_a_noop():
     _say("case T=0")
     dev = torch.device("cuda")

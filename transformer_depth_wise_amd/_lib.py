@@ -20,9 +20,10 @@ F32, BF16, P24 = 0, 1, 2
 ATTNRES_MAX_D = 16384
 ATTNRES_MAX_SOURCES = 32
 ATTNRES_MAX_SOURCES_MULTI = 16
+ATTNRES_MAX_GROUP_SOURCES = 16
 
-EXPORTED = ("attnres_phase1", "attnres_phase1_workspace_bytes", "attnres_phase2_merge", "attnres_full",
-            "attnres_block_accumulate", "attnres_status_string")
+EXPORTED = ("attnres_phase1", "attnres_phase1_workspace_bytes", "attnres_phase2_merge", "attnres_phase2_merge_multi",
+            "attnres_full", "attnres_block_accumulate", "attnres_status_string")
 
 
 class AttnResError(RuntimeError):
@@ -49,9 +50,11 @@ def load(path: Optional[str] = None):
     lib.attnres_phase1_workspace_bytes.argtypes = [I, I, I, I]
     lib.attnres_phase1_workspace_bytes.restype = ctypes.c_int64
     lib.attnres_phase2_merge.argtypes = [E, I, I, V, V, E, V, V, V, E, V, V, V, V, F, V, V, V]
+    lib.attnres_phase2_merge_multi.argtypes = [E, I, I, V, V, V, I, I, V, V, V, F, V, V, V]
     lib.attnres_full.argtypes = [E, V, I, I, I, I, V, V, V, F, V, V, V, V]
     lib.attnres_block_accumulate.argtypes = [E, I, I, E, V, V, V, V, V]
-    for fn in ("attnres_phase1", "attnres_phase2_merge", "attnres_full", "attnres_block_accumulate"):
+    for fn in ("attnres_phase1", "attnres_phase2_merge", "attnres_phase2_merge_multi", "attnres_full",
+               "attnres_block_accumulate"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.attnres_status_string.argtypes = [ctypes.c_int]
     lib.attnres_status_string.restype = ctypes.c_char_p
@@ -136,6 +139,20 @@ def attnres_phase2_merge(p1_out: torch.Tensor, p1_lse: torch.Tensor, partial_in:
                                      _ptr(partial_out), _ptr(w), _ptr(key_gain), _ptr(prenorm_gain), eps,
                                      _ptr(h_out), _ptr(x_out), _stream(stream))
     _check("attnres_phase2_merge", rc)
+
+
+def attnres_phase2_merge_multi(p1_out: torch.Tensor, p1_lse: torch.Tensor, src: Optional[torch.Tensor], n_src: int,
+                               w: Optional[torch.Tensor], key_gain: Optional[torch.Tensor],
+                               prenorm_gain: Optional[torch.Tensor], eps: float, h_out: Optional[torch.Tensor],
+                               x_out: Optional[torch.Tensor], stream=None) -> None:
+    """p1_out: [T, d]; p1_lse: [T]; src: [>=n_src, T, d] slabs (the group's
+    outputs so far, each its own source; None when n_src == 0); w, gains: [d]."""
+    T, d = p1_out.shape
+    stride = 0 if src is None else (src.stride(0) if src.dim() == 3 else T * d)
+    rc = load().attnres_phase2_merge_multi(dtype_code(p1_out.dtype), T, d, _ptr(p1_out), _ptr(p1_lse), _ptr(src),
+                                           n_src, stride, _ptr(w), _ptr(key_gain), _ptr(prenorm_gain), eps,
+                                           _ptr(h_out), _ptr(x_out), _stream(stream))
+    _check("attnres_phase2_merge_multi", rc)
 
 
 def attnres_full(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],

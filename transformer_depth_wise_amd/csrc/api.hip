@@ -196,6 +196,39 @@ attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, 
                                           static_cast<hipStream_t>(stream)));
 }
 
+attnres_status_t attnres_phase2_merge_multi(attnres_dtype_t dt, int64_t T, int64_t d, const void* p1_out,
+                                            const float* p1_lse, const void* src, int64_t n_src,
+                                            int64_t src_stride, const float* w, const float* key_gain,
+                                            const float* prenorm_gain, float eps, void* h_out, void* x_out,
+                                            void* stream) {
+  if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
+  attnres_status_t st = check_d(d);
+  if (st != ATTNRES_OK) return st;
+  if (T < 0 || n_src < 0 || n_src > ATTNRES_MAX_GROUP_SOURCES || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
+  if (!p1_out || !p1_lse || (!h_out && !x_out)) return ATTNRES_EINVAL;
+  if (n_src > 0 && (!src || !w)) return ATTNRES_EINVAL;
+  if (n_src > 1 && src_stride < T * d) return ATTNRES_EINVAL;
+  if (n_src > 0 && src_stride % 8 != 0) return ATTNRES_EALIGN;
+  st = check_align({p1_out, n_src > 0 ? src : nullptr, w, key_gain, prenorm_gain, h_out, x_out}, {p1_lse});
+  if (st != ATTNRES_OK) return st;
+  const int64_t es = esize(dt);
+  const Range r_o = range_of(p1_out, T * d * es), r_l = range_of(p1_lse, T * 4);
+  const Range r_s = n_src > 0 ? range_of(src, ((n_src - 1) * src_stride + T * d) * es) : Range{0, 0};
+  const Range r_w = w ? range_of(w, d * 4) : Range{0, 0};
+  const Range r_g = key_gain ? range_of(key_gain, d * 4) : Range{0, 0};
+  const Range r_gm = prenorm_gain ? range_of(prenorm_gain, d * 4) : Range{0, 0};
+  const Range r_h = h_out ? range_of(h_out, T * d * es) : Range{0, 0};
+  const Range r_x = x_out ? range_of(x_out, T * d * es) : Range{0, 0};
+  for (Range o : {r_h, r_x})
+    for (Range i : {r_o, r_l, r_s, r_w, r_g, r_gm})
+      if (overlaps(o, i)) return ATTNRES_EALIAS;
+  if (overlaps(r_h, r_x)) return ATTNRES_EALIAS;
+  return hip_status(attnres::launch_merge_multi(kind_of(dt), T, (int)d, p1_out, p1_lse, n_src > 0 ? src : nullptr,
+                                                (int)n_src, src_stride, w, key_gain, x_out ? prenorm_gain : nullptr,
+                                                eps, h_out, x_out, static_cast<hipStream_t>(stream)));
+}
+
 attnres_status_t attnres_full(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride, int64_t T,
                               int64_t d, const float* w, const float* key_gain, const float* prenorm_gain,
                               float eps, void* h_out, void* x_out, float* lse_out, void* stream) {

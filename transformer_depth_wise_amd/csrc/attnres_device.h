@@ -184,10 +184,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Sum of (a, b) over the 256 threads of a workgroup, in a fixed order (the
-// result is identical in every thread and from run to run).  `lds` holds 8
-// floats; callers alternate between two such buffers so that one barrier per
-// reduction suffices.
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // orders global memory, which makes every wave wait for all of its global
 // loads and stores in flight (the prefetched next item included); here those
@@ -198,6 +194,10 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Sum of (a, b) over the 256 threads of a workgroup, in a fixed order (the
+// result is identical in every thread and from run to run).  `lds` holds 8
+// floats; callers alternate between two such buffers so that one barrier per
+// reduction suffices.
 __device__ __forceinline__ float2 block_sum2_256(float a, float b, float* lds) {
   a = wave_sum(a);
   b = wave_sum(b);

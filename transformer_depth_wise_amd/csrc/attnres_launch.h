@@ -27,6 +27,10 @@ hipError_t launch_merge(Dtype dt, int64_t T, int d, const void* o1, const float*
                         const float* w, const float* kg, const float* gamma, float eps,
                         void* h_out, void* x_out, hipStream_t stream);
 
+hipError_t launch_merge_multi(Dtype dt, int64_t T, int d, const void* o1, const float* lse1, const void* src,
+                              int k, int64_t stride, const float* w, const float* kg, const float* gamma, float eps,
+                              void* h_out, void* x_out, hipStream_t stream);
+
 hipError_t launch_accumulate(Dtype dt, int64_t T, int d, Dtype pdt, const void* pin, const void* v2,
                              const void* v, void* out, hipStream_t stream);
 

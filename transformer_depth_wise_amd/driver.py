@@ -34,7 +34,8 @@ from typing import Callable, Dict, List, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import (attnres_block_accumulate, attnres_full, attnres_phase1, attnres_phase2_merge)
+from ._lib import (attnres_block_accumulate, attnres_full, attnres_phase1, attnres_phase2_merge,
+                   attnres_phase2_merge_multi)
 
 SiteHook = Callable[..., None]
 Sublayer = Callable[[int, torch.Tensor], torch.Tensor]
@@ -228,44 +229,106 @@ class BlockAttnRes:
 
 
 class FullAttnRes:
-    """Full AttnRes (every sublayer output its own source), one-shot per site:
-    sublayer l aggregates hist[0..l-1] with attnres_full and PreNorm."""
+    """Full AttnRes: every sublayer output is its own depth source ("Attention
+    Residuals" notes, section 7).
+
+    ``group=None``: one-shot per site, sublayer l aggregates hist[0..l] with
+    attnres_full and PreNorm.  ``group=G``: the grouped two-phase schedule
+    (reading notes, static queries and two-phase computation; notes section
+    10): for each group of G consecutive sublayers, phase 1 scores the
+    sources completed before the group for all G queries at once, then each
+    sublayer merges that partition with the outputs produced inside the group
+    so far (attnres_phase2_merge_multi).  The phase-1 call of a group reads
+    at most ATTNRES_MAX_SOURCES_MULTI completed sources."""
 
     def __init__(self, T: int, d: int, L: int, dtype: torch.dtype, eps: float = 1e-6, device=None,
-                 keep_h: bool = False, final_site: bool = True):
+                 keep_h: bool = False, final_site: bool = True, group: Optional[int] = None):
         self.T, self.d, self.L, self.dtype, self.eps = int(T), int(d), int(L), dtype, float(eps)
         if L + 1 > _lib.ATTNRES_MAX_SOURCES:
             raise ValueError("Full AttnRes supports at most %d sources" % _lib.ATTNRES_MAX_SOURCES)
         dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
         self.final_site = final_site
+        self.group = None if group is None else int(group)
         self.hist = torch.empty((L + 1, T, d), dtype=dtype, device=dev)  # v_0 = embedding, v_1..v_L
         self.x = torch.empty((2, T, d), dtype=dtype, device=dev)
         self.h = torch.empty((T, d), dtype=dtype, device=dev) if keep_h else None
         self.lse = torch.empty((T,), dtype=torch.float32, device=dev)
         self.h_final = torch.empty((T, d), dtype=dtype, device=dev)
+        if self.group is not None:
+            G = self.group
+            if not 1 <= G <= _lib.ATTNRES_MAX_GROUP_SOURCES:
+                raise ValueError("group size must be in [1, %d]" % _lib.ATTNRES_MAX_GROUP_SOURCES)
+            n_max = max(g0 + 1 for g0 in range(0, L, G))
+            if n_max > _lib.ATTNRES_MAX_SOURCES_MULTI:
+                raise ValueError("the last group's phase 1 would read %d sources (at most %d): use larger groups"
+                                 % (n_max, _lib.ATTNRES_MAX_SOURCES_MULTI))
+            self.o1 = torch.empty((G, T, d), dtype=dtype, device=dev)
+            self.m1 = torch.empty((G, T), dtype=torch.float32, device=dev)
+            self.lse1 = torch.empty((G, T), dtype=torch.float32, device=dev)
+            ws = _lib.attnres_phase1_workspace_bytes(T, d, n_max, G)
+            self.workspace = torch.empty((max(ws, 16) + 3) // 4, dtype=torch.float32, device=dev)
 
     def plan(self) -> List[Launch]:
         r = self.T * self.d * _esize(self.dtype)
-        out = [Launch("full", (l + 1) * r + r + self.T * 4) for l in range(1, self.L + 1)]
+        stat = self.T * 4
+        if self.group is None:
+            out = [Launch("full", (l + 1) * r + r + stat) for l in range(1, self.L + 1)]
+        else:
+            out = []
+            for g0 in range(0, self.L, self.group):
+                S = min(self.group, self.L - g0)
+                n = g0 + 1
+                out.append(Launch("phase1", (r if n == 1 else n * r + S * r) + 2 * S * stat))
+                for j in range(S):
+                    out.append(Launch("phase2", (2 + j) * r + stat))   # o, j group outputs; x
         if self.final_site:
-            out.append(Launch("final", (self.L + 2) * r + self.T * 4))
+            out.append(Launch("final", (self.L + 2) * r + stat))
         return out
 
     def forward(self, params: Dict[str, torch.Tensor], sublayer: Callable[[int, torch.Tensor], None],
-                hook: Optional[SiteHook] = None, stream=None) -> torch.Tensor:
+                hook: Optional[SiteHook] = None, stream=None,
+                instrument: Optional[Callable[[str, bool], None]] = None) -> torch.Tensor:
         """``hist[0]`` must hold the embedding; ``sublayer(l, x_l)`` writes the
         output of sublayer l (0-based) into ``hist[l + 1]``."""
         w, g, gam = params["w"], params.get("g"), params.get("gamma")
-        for l in range(self.L):
-            x = self.x[l % 2]
-            attnres_full(self.hist, l + 1, w[l], None if g is None else g[l], None if gam is None else gam[l],
-                         self.eps, self.h, x, self.lse, stream=stream)
-            if hook is not None:
-                hook(l, x=x, h=self.h, lse=self.lse)
-            sublayer(l, x)
+        mark = instrument if instrument is not None else (lambda kind, begin: None)
+        if self.group is None:
+            for l in range(self.L):
+                x = self.x[l % 2]
+                mark("full", True)
+                attnres_full(self.hist, l + 1, w[l], None if g is None else g[l],
+                             None if gam is None else gam[l], self.eps, self.h, x, self.lse, stream=stream)
+                mark("full", False)
+                if hook is not None:
+                    hook(l, x=x, h=self.h, lse=self.lse)
+                sublayer(l, x)
+        else:
+            for g0 in range(0, self.L, self.group):
+                S = min(self.group, self.L - g0)
+                n = g0 + 1
+                single = n == 1  # only the embedding: every phase-1 output is hist[0]
+                mark("phase1", True)
+                attnres_phase1(self.hist, n, w[g0:g0 + S], None if g is None else g[g0:g0 + S], self.eps,
+                               None if single else self.o1[:S], self.m1[:S], self.lse1[:S], self.workspace,
+                               stream=stream)
+                mark("phase1", False)
+                for j in range(S):
+                    l = g0 + j
+                    x = self.x[l % 2]
+                    o = self.hist[0] if single else self.o1[j]
+                    mark("phase2", True)
+                    attnres_phase2_merge_multi(o, self.lse1[j], self.hist[g0 + 1:g0 + 1 + j] if j else None, j,
+                                               w[l], None if g is None else g[l], None if gam is None else gam[l],
+                                               self.eps, self.h, x, stream=stream)
+                    mark("phase2", False)
+                    if hook is not None:
+                        hook(l, x=x, h=self.h, lse=None)
+                    sublayer(l, x)
         if self.final_site:
+            mark("final", True)
             attnres_full(self.hist, self.L + 1, w[self.L], None if g is None else g[self.L], None, self.eps,
                          self.h_final, None, None, stream=stream)
+            mark("final", False)
         return self.h_final
 
 
