@@ -6,23 +6,26 @@
 // products into one Q K^T product, and each source row is read once per
 // block instead of once per sublayer).
 //
-// Work decomposition.  S >= 2 uses three launches (pack, score, output);
-// S == 1 (Full AttnRes sites and the final aggregation) uses one kernel that
-// does both parts per 16-token tile.
-//  part A  scores (one workgroup = 4 waves = a tile of 16 tokens).
-//          Z[q][t][i] = sum_k (w_q g_q)[k] * u_i[t][k] is a dense contraction
-//          over d, computed on the matrix cores with v_mfma_f32_16x16x32_bf16
-//          (bf16 rows; the fp32 query is split into bf16 hi + lo parts, so the
-//          product keeps ~16 mantissa bits of the query and accumulates in
-//          fp32) or v_mfma_f32_16x16x4_f32 (fp32 rows).  A lane supplies query
-//          (lane&15) of the A operand and token (lane&15) of the B operand;
-//          the 4 lane groups and the 4 waves split the channels.  The sum of
-//          squares of every source row (for its RMS) is accumulated on the
-//          vector ALUs from the same registers.  The four waves' partial sums
-//          are added in a fixed order through LDS, then z = Z / r(u) and the
-//          softmax over sources is taken in LDS.  For S >= 2 the queries are
-//          packed once per call into MFMA operand chunks and the softmax
-//          weights go to a caller-provided workspace.
+// Work decomposition.  With a workspace (always for S >= 2, and for the
+// final aggregation) phase 1 is a streaming pair: pack the queries, score,
+// then stream the outputs.  Without one (S == 1: Full AttnRes one-shot sites)
+// a single kernel does both parts per 16-token tile.
+//  part A  scores.  Z[q][t][i] = sum_k (w_q g_q)[k] * u_i[t][k] is a dense
+//          contraction over d, computed on the matrix cores with
+//          v_mfma_f32_16x16x32_bf16 (bf16 rows; the fp32 query is split into
+//          bf16 hi + lo parts, so the product keeps ~16 mantissa bits of the
+//          query and accumulates in fp32) or v_mfma_f32_16x16x4_f32 (fp32
+//          rows).  A lane supplies query (lane&15) of the A operand and token
+//          (lane&15) of the B operand; the 4 lane groups split each K-block's
+//          channels.  The sum of squares of every source row (for its RMS) is
+//          accumulated on the vector ALUs from the same registers.  Two
+//          kernels with the same summation order (bitwise equal results):
+//          k_p1_scores gives each (16-token tile, source) pair a workgroup
+//          whose 4 waves take contiguous quarters of d (short token ranges);
+//          k_p1_scores_wide gives each wave 16 tokens over all of d and shares
+//          the queries of 4 waves through LDS (long token ranges).  The
+//          queries are packed once per call into MFMA operand blocks; scores,
+//          then softmax weights, go to the caller's workspace.
 //  part B  outputs.  out[s][t] = sum_i alpha[t][s][i] u_i[t]: the source rows
 //          are streamed again (16-byte loads, a wave reads 1 KiB of one row)
 //          and each row chunk serves all S queries.
@@ -187,7 +190,7 @@ __device__ __forceinline__ int64_t packed_index(int kb, int m, int s4, int lane)
 // With PACKED, the queries come from `pk` (packed layout above) written by
 // k_pack_queries; otherwise w (.) g is formed and split per chunk from the
 // fp32 parameters.
-template <typename St, int MT, int G, bool PACKED>
+template <typename St, int MT, int G, bool PACKED, int KB = 1>
 __device__ __forceinline__ void score_pass(const St* __restrict__ src, int64_t stride, int64_t T, int d,
                                            const float* __restrict__ w, const float* __restrict__ kg,
                                            const u32x4_t* __restrict__ pk, int S, int64_t tok0, int g0,
@@ -211,56 +214,66 @@ __device__ __forceinline__ void score_pass(const St* __restrict__ src, int64_t s
   for (int i = 0; i < G; ++i) ss[i] = 0.f;
 
   const int kb_end = ((wave + 1) * nkb) >> 2;
-  for (int kb = (wave * nkb) >> 2; kb < kb_end; ++kb) {
-    // All loads of the K-block first (queries and sources of the 4 steps),
-    // then the matrix-core work: the scheduling barrier keeps the compiler
-    // from sinking loads next to their first use, so a wave keeps 4 * (2*MT
-    // + G) 16-byte loads in flight instead of one step's worth.
-    typename Mfma<St>::A a[4][MT];
-    typename Mfma<St>::B b[4][G];
+  for (int kb0 = (wave * nkb) >> 2; kb0 < kb_end; kb0 += KB) {
+    // All loads of KB K-blocks first (queries and sources of their 4 steps
+    // each), then the matrix-core work in K-block order: the scheduling
+    // barrier keeps the compiler from sinking loads next to their first use,
+    // so a wave keeps KB * 4 * (2*MT + G) 16-byte loads in flight.  A K-block
+    // past the wave's range loads a valid one again and is skipped.
+    typename Mfma<St>::A a[KB][4][MT];
+    typename Mfma<St>::B b[KB][4][G];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int c0 = kb * 16 + s4 * 4 + grp;
-      const bool cok = c0 < C;
-      const int c = cok ? c0 : C - 1;
+    for (int u = 0; u < KB; ++u) {
+      const int kb = kb0 + u < kb_end ? kb0 + u : kb0;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int q = m * 16 + col;
-        if (PACKED) {
-          const u32x4_t* qp = pk + packed_index<MT>(kb, m, s4, lane);
-          a[s4][m] = Mfma<St>::from_halves(ld16(qp), ld16(qp + 64));
-        } else {
-          const bool qok = cok && q < S;
-          const int qc = q < S ? q : 0;
-          float qv[8];
-          const u32x4_t w0 = sel16(qok, ld16(w + (int64_t)qc * d + c * 8));
-          const u32x4_t w1 = sel16(qok, ld16(w + (int64_t)qc * d + c * 8 + 4));
-          qv[0] = __uint_as_float(w0.x); qv[1] = __uint_as_float(w0.y); qv[2] = __uint_as_float(w0.z);
-          qv[3] = __uint_as_float(w0.w); qv[4] = __uint_as_float(w1.x); qv[5] = __uint_as_float(w1.y);
-          qv[6] = __uint_as_float(w1.z); qv[7] = __uint_as_float(w1.w);
-          if (kg) {
-            const u32x4_t g0v = ld16(kg + (int64_t)qc * d + c * 8);
-            const u32x4_t g1v = ld16(kg + (int64_t)qc * d + c * 8 + 4);
-            qv[0] *= __uint_as_float(g0v.x); qv[1] *= __uint_as_float(g0v.y);
-            qv[2] *= __uint_as_float(g0v.z); qv[3] *= __uint_as_float(g0v.w);
-            qv[4] *= __uint_as_float(g1v.x); qv[5] *= __uint_as_float(g1v.y);
-            qv[6] *= __uint_as_float(g1v.z); qv[7] *= __uint_as_float(g1v.w);
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int c0 = kb * kKBlock + s4 * 4 + grp;
+        const bool cok = c0 < C;
+        const int c = cok ? c0 : C - 1;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const int q = m * 16 + col;
+          if (PACKED) {
+            const u32x4_t* qp = pk + packed_index<MT>(kb, m, s4, lane);
+            a[u][s4][m] = Mfma<St>::from_halves(ld16(qp), ld16(qp + 64));
+          } else {
+            const bool qok = cok && q < S;
+            const int qc = q < S ? q : 0;
+            float qv[8];
+            const u32x4_t w0 = sel16(qok, ld16(w + (int64_t)qc * d + c * 8));
+            const u32x4_t w1 = sel16(qok, ld16(w + (int64_t)qc * d + c * 8 + 4));
+            qv[0] = __uint_as_float(w0.x); qv[1] = __uint_as_float(w0.y); qv[2] = __uint_as_float(w0.z);
+            qv[3] = __uint_as_float(w0.w); qv[4] = __uint_as_float(w1.x); qv[5] = __uint_as_float(w1.y);
+            qv[6] = __uint_as_float(w1.z); qv[7] = __uint_as_float(w1.w);
+            if (kg) {
+              const u32x4_t g0v = ld16(kg + (int64_t)qc * d + c * 8);
+              const u32x4_t g1v = ld16(kg + (int64_t)qc * d + c * 8 + 4);
+              qv[0] *= __uint_as_float(g0v.x); qv[1] *= __uint_as_float(g0v.y);
+              qv[2] *= __uint_as_float(g0v.z); qv[3] *= __uint_as_float(g0v.w);
+              qv[4] *= __uint_as_float(g1v.x); qv[5] *= __uint_as_float(g1v.y);
+              qv[6] *= __uint_as_float(g1v.z); qv[7] *= __uint_as_float(g1v.w);
+            }
+            a[u][s4][m] = Mfma<St>::make_a(qv);
           }
-          a[s4][m] = Mfma<St>::make_a(qv);
         }
-      }
 #pragma unroll
-      for (int i = 0; i < G; ++i) b[s4][i] = Mfma<St>::load_b(base[i] + c * 8, cok && tok_ok);
+        for (int i = 0; i < G; ++i) b[u][s4][i] = Mfma<St>::load_b(base[i] + c * 8, cok && tok_ok);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
+    for (int u = 0; u < KB; ++u) {
+      if (kb0 + u < kb_end) {  // uniform
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        Mfma<St>::sumsq(b[s4][i], ss[i]);
+        for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) Mfma<St>::mma(acc[m][i], a[s4][m], b[s4][i]);
+          for (int i = 0; i < G; ++i) {
+            Mfma<St>::sumsq(b[u][s4][i], ss[i]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) Mfma<St>::mma(acc[m][i], a[u][s4][m], b[u][s4][i]);
+          }
       }
+    }
   }
   // every lane group saw different channels of the same (token, source)
 #pragma unroll
@@ -397,37 +410,78 @@ __global__ __launch_bounds__(256) void k_pack_queries(const float* __restrict__ 
   Mfma<St>::pack(qv, dst, dst + 64);
 }
 
-// S >= 2, first kernel: scores and softmax weights of a 16-token tile for up
-// to 32 queries.  The weights go to the workspace as alpha[t][q][i]
-// (i fastest), the statistics to m_out / lse_out.
-template <typename St, int MT>
+// First kernel of the streaming pair for short and mid-sized token ranges:
+// the scores of sources [G*blockIdx.y, +G) (fewer in the last group) for a
+// 16-token tile (blockIdx.x) and up to 32 queries.  The 4 waves take
+// contiguous quarters of d (several K-blocks of loads in flight per wave),
+// their partials are added in the fixed order (w0 + w2) + (w1 + w3) through
+// LDS, and z = Z / r(u) goes to the weight slots alpha[t][q][i] of the
+// workspace; k_p1_softmax turns them into weights.  G trades parallelism
+// (workgroups) against re-reading the packed queries once per group.
+template <typename St, int MT, int G>
+__device__ __forceinline__ void score_sources(const St* src, int n, int64_t stride, int64_t T, int d,
+                                              const u32x4_t* pk, int S, float eps, int64_t tok0, int g0,
+                                              float* red, float* alpha) {
+  constexpr int KB = G == 1 ? (MT == 1 ? 4 : 3) : (G == 2 ? 2 : 1);
+  f32x4_t acc[MT][G];
+  float ss[G];
+  score_pass<St, MT, G, true, KB>(src, stride, T, d, nullptr, nullptr, pk, S, tok0, g0, acc, ss);
+  Red<MT, G>::reduce(red, acc, ss);
+  if ((threadIdx.x >> 6) == 0) {
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const int64_t tok = tok0 + col;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float r = sqrtf(ss[i] / (float)d + eps);
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int q = m * 16 + grp * 4 + rr;
+          if (q < S && tok < T) alpha[(tok * S + q) * n + g0 + i] = acc[m][i][rr] / r;
+        }
+    }
+  }
+}
+
+template <typename St, int MT, int G>
 __global__ __launch_bounds__(256) void k_p1_scores(const St* __restrict__ src, int n, int64_t stride,
                                                    int64_t T, int d, const u32x4_t* __restrict__ pk, int S,
-                                                   float eps, float* __restrict__ alpha,
-                                                   float* __restrict__ m_out, float* __restrict__ lse_out) {
-  constexpr int QP = 16 * MT;
-  extern __shared__ float lds[];
-  float* red = lds;
-  float* zb = lds + 2 * Red<MT, kGroup>::kSlot;  // [16 tokens][QP queries][n sources]
+                                                   float eps, float* __restrict__ alpha) {
+  __shared__ float red[2 * Red<MT, G>::kSlot];
   const int64_t tok0 = (int64_t)blockIdx.x * 16;
-  score_all<St, MT, true, false>(src, n, stride, T, d, nullptr, nullptr, pk, S, eps, tok0, red, zb, n);
-  lds_barrier();
-
-  // softmax over the n sources of every (token, query) pair
-  for (int pidx = threadIdx.x; pidx < 16 * QP; pidx += 256) {
-    const int t = pidx / QP, q = pidx - t * QP;
-    const int64_t tok = tok0 + t;
-    if (q >= S || tok >= T) continue;
-    const float* row = zb + pidx * n;
-    float mx = row[0];
-    for (int i = 1; i < n; ++i) mx = fmaxf(mx, row[i]);
-    float l = 0.f;
-    for (int i = 0; i < n; ++i) l += expf(row[i] - mx);
-    float* a = alpha + (tok * S + q) * n;
-    for (int i = 0; i < n; ++i) a[i] = expf(row[i] - mx) / l;
-    if (m_out) m_out[(int64_t)q * T + tok] = mx;
-    lse_out[(int64_t)q * T + tok] = mx + logf(l);
+  const int g0 = blockIdx.y * G;
+  const int r = n - g0 < G ? n - g0 : G;  // uniform
+  if (r == G) {
+    score_sources<St, MT, G>(src, n, stride, T, d, pk, S, eps, tok0, g0, red, alpha);
+  } else if (G > 1 && r == 1) {
+    score_sources<St, MT, 1>(src, n, stride, T, d, pk, S, eps, tok0, g0, red, alpha);
+  } else if (G > 2 && r == 2) {
+    score_sources<St, MT, (G > 2 ? 2 : 1)>(src, n, stride, T, d, pk, S, eps, tok0, g0, red, alpha);
+  } else if (G > 3 && r == 3) {
+    score_sources<St, MT, (G > 3 ? 3 : 1)>(src, n, stride, T, d, pk, S, eps, tok0, g0, red, alpha);
   }
+}
+
+// Softmax over the n sources of every (token, query) pair, in place in the
+// weight slots; the statistics go to m_out / lse_out.
+__global__ __launch_bounds__(256) void k_p1_softmax(int64_t pairs, int n, int S, int64_t T,
+                                                    float* __restrict__ alpha, float* __restrict__ m_out,
+                                                    float* __restrict__ lse_out) {
+  const int64_t pidx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (pidx >= pairs) return;
+  const int64_t tok = pidx / S;
+  const int q = (int)(pidx - tok * S);
+  float* a = alpha + pidx * n;
+  float mx = a[0];
+  for (int i = 1; i < n; ++i) mx = fmaxf(mx, a[i]);
+  float l = 0.f;
+  for (int i = 0; i < n; ++i) l += expf(a[i] - mx);
+  for (int i = 0; i < n; ++i) a[i] = expf(a[i] - mx) / l;
+  if (m_out) m_out[(int64_t)q * T + tok] = mx;
+  lse_out[(int64_t)q * T + tok] = mx + logf(l);
 }
 
 // Wide-tile variant of the scoring kernel for long token ranges, with the
@@ -894,12 +948,26 @@ static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, i
     hipLaunchKernelGGL(kw, dim3((unsigned)wide_groups), dim3(64 * (kWideWaves + 1)), zl, stream,
                        static_cast<const St*>(src), n, stride, T, d, pk, S, eps, al, m_out, lse_out);
   } else {
-    const size_t lds = sizeof(float) * (2 * Red<MT, kGroup>::kSlot + 16 * 16 * MT * n);
-    auto ks = k_p1_scores<St, MT>;
-    e = set_lds(ks, lds);
+    // one workgroup per (16-token tile, group of G sources), then the
+    // softmax per pair; G is the largest of 4, 2, 1 that still gives two
+    // workgroups per compute unit
+    const int64_t tiles = (T + 15) / 16;
+    const int64_t want = 2 * (int64_t)device_cu_count();
+    const int G = tiles * ((n + 3) / 4) >= want ? 4 : (tiles * ((n + 1) / 2) >= want ? 2 : 1);
+    const dim3 grid((unsigned)tiles, (unsigned)((n + G - 1) / G));
+    const St* sp = static_cast<const St*>(src);
+    if (G == 4) {
+      hipLaunchKernelGGL((k_p1_scores<St, MT, 4>), grid, dim3(256), 0, stream, sp, n, stride, T, d, pk, S, eps, al);
+    } else if (G == 2) {
+      hipLaunchKernelGGL((k_p1_scores<St, MT, 2>), grid, dim3(256), 0, stream, sp, n, stride, T, d, pk, S, eps, al);
+    } else {
+      hipLaunchKernelGGL((k_p1_scores<St, MT, 1>), grid, dim3(256), 0, stream, sp, n, stride, T, d, pk, S, eps, al);
+    }
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ks, dim3((unsigned)((T + 15) / 16)), dim3(256), lds, stream, static_cast<const St*>(src),
-                       n, stride, T, d, pk, S, eps, al, m_out, lse_out);
+    const int64_t pairs = T * S;
+    hipLaunchKernelGGL(k_p1_softmax, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, stream, pairs, n, S, T,
+                       al, m_out, lse_out);
   }
   e = hipGetLastError();
   if (e != hipSuccess || out == nullptr) return e;  // statistics only
