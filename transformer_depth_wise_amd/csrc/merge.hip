@@ -184,45 +184,72 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
   const int tl = threadIdx.x % TEAM;
   const int C = d >> 3;
   const float inv_d = 1.0f / (float)d;
-  float wq[CPL][8];
+  // Prologue, ordered so that nothing waits before the first token's rows
+  // are in flight: the parameter loads (clamped, unconditional), then the
+  // first token's loads, then the LDS stores of gamma (which wait for gamma
+  // only) and one barrier.
+  constexpr int KG = (TEAM * CPL + 255) / 256;  // gamma chunks per thread
+  float wq[CPL][8], gk[CPL][8], gv[KG][8];
+  if (HAS_V) {
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) {
-    const int c = tl + TEAM * k;
-    if (c < C) {
-      if (HAS_V) {
-        load8(w + c * 8, wq[k]);
-        if (kg) {
-          float g[8];
-          load8(kg + c * 8, g);
+    for (int k = 0; k < CPL; ++k) {
+      const int c0 = tl + TEAM * k;
+      load8(w + (c0 < C ? c0 : C - 1) * 8, wq[k]);
+    }
+    if (kg) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) wq[k][e] *= g[e];
-        }
-      } else {
-        zero8(wq[k]);
+      for (int k = 0; k < CPL; ++k) {
+        const int c0 = tl + TEAM * k;
+        load8(kg + (c0 < C ? c0 : C - 1) * 8, gk[k]);
       }
     } else {
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gk[k][e] = 1.f;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
       zero8(wq[k]);
+      zero8(gk[k]);
     }
   }
   if (x_out) {
-    for (int c = threadIdx.x; c < C; c += 256) {
-      float gv[8];
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      const int c0 = (int)threadIdx.x + 256 * k;
       if (gamma) {
-        load8(gamma + c * 8, gv);
+        load8(gamma + (c0 < C ? c0 : C - 1) * 8, gv[k]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gv[e] = 1.f;
+        for (int e = 0; e < 8; ++e) gv[k][e] = 1.f;
       }
-      gm_lds[2 * c] = make_float4(gv[0], gv[1], gv[2], gv[3]);
-      gm_lds[2 * c + 1] = make_float4(gv[4], gv[5], gv[6], gv[7]);
     }
   }
-  lds_barrier();
   int parity = 0;
   const int64_t step = (int64_t)gridDim.x * TPW;
   int64_t tok = (int64_t)blockIdx.x * TPW + team;
   Stage<St, Pt, CPL> A, B;
   issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(A, tok, T, d, C, tl, o1, pin, vprev2, vprev, plane);
+  // w (.) g, with chunks past the end of d zeroed (x 1.0 exactly without g)
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const bool live = tl + TEAM * k < C;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wq[k][e] = live ? wq[k][e] * gk[k][e] : 0.f;
+  }
+  if (x_out) {
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      const int c = (int)threadIdx.x + 256 * k;
+      if (c < C) {
+        gm_lds[2 * c] = make_float4(gv[k][0], gv[k][1], gv[k][2], gv[k][3]);
+        gm_lds[2 * c + 1] = make_float4(gv[k][4], gv[k][5], gv[k][6], gv[k][7]);
+      }
+    }
+  }
+  lds_barrier();
   while (tok - team < T) {
     issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(B, tok + step, T, d, C, tl, o1, pin, vprev2, vprev, plane);
     process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(A, tok, T, d, C, tl, lse1, pout, pout24 != 0, plane, wq, gm_lds, eps,
