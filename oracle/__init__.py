@@ -54,6 +54,8 @@ def _load():
         lib.oracle_block_forward.argtypes = [I, I, I, P, I, P, P, P, P, P, P, D, ctypes.c_int,
                                              P, P, P, P, P, P, P, P]
         lib.oracle_full_forward.argtypes = [I, I, I, P, P, P, P, P, D, ctypes.c_int, P, P, P, P]
+        lib.oracle_site_backward.argtypes = [I, I, P, P, P, P, ctypes.c_int, D, P, P, P, P, P]
+        lib.oracle_site_backward_tokens.argtypes = [I, I, I, P, P, P, P, ctypes.c_int, D, P, P, P, P, P]
         lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -200,3 +202,23 @@ def full_forward(emb, v, w, g, gamma, eps: float, final_site: bool = True,
     if rc != 0:
         raise RuntimeError("oracle_full_forward failed: %d" % rc)
     return out
+
+
+def site_backward(src, w, g, gamma, eps: float, dx, prenorm: bool = True):
+    """Backward of one aggregation site over tokens ("Attention Residuals
+    阅读补充", gradients along the tangent; "Attention Residuals" notes,
+    section 7, logit gradient).  src [n, T, d], dx [T, d], w/g/gamma [d]
+    (g, gamma may be None: ones).  Returns dict(du [n, T, d], dw, dg, dgamma
+    [d]) in fp64; dw, dg, dgamma are sums over the tokens."""
+    s = _f32(src)
+    n, T, d = s.shape
+    dxa = _f32(dx)
+    du = np.empty((n, T, d))
+    dw = np.empty(d)
+    dg = np.empty(d)
+    dgm = np.empty(d)
+    rc = _load().oracle_site_backward_tokens(T, n, d, _p(s), _p(_f32(w)), _p(_f32(g)), _p(_f32(gamma)),
+                                             1 if prenorm else 0, eps, _p(dxa), _p(du), _p(dw), _p(dg),
+                                             _p(dgm) if prenorm else None)
+    assert rc == 0, rc
+    return {"du": du, "dw": dw, "dg": dg, "dgamma": dgm if prenorm else None}

@@ -254,3 +254,118 @@ int oracle_full_forward(int64_t n_tok, int64_t d, int64_t L, const float* emb, c
     }
     return bad ? -2 : 0;
 }
+
+/* "Attention Residuals 阅读补充", gradients along the tangent: for
+ * y = x / r_eps(x) and an upstream gradient G = dL/dy,
+ * dL/dx = (G - y (y^T G) / d) / r_eps(x). */
+static void rms_core_backward(int64_t d, const double* x, double eps, const double* G, double* dx_out) {
+    const double r = oracle_rms(d, x, eps);
+    double yg = 0.0;
+    for (int64_t k = 0; k < d; ++k) yg += (x[k] / r) * G[k];
+    for (int64_t k = 0; k < d; ++k) dx_out[k] = (G[k] - (x[k] / r) * yg / (double)d) / r;
+}
+
+int oracle_site_backward(int64_t n, int64_t d, const double* const* src, const double* w,
+                         const double* g, const double* gamma, int prenorm, double eps,
+                         const double* dx, double* const* du, double* dw, double* dg,
+                         double* dgamma) {
+    if (n <= 0 || d <= 0 || !src || !w || !dx || !du || !dw || !dg) return -1;
+    double* z = (double*)malloc(sizeof(double) * (size_t)n);
+    double* alpha = (double*)malloc(sizeof(double) * (size_t)n);
+    double* h = (double*)malloc(sizeof(double) * (size_t)d);
+    double* Gh = (double*)malloc(sizeof(double) * (size_t)d);
+    double* G = (double*)malloc(sizeof(double) * (size_t)d);
+    double* t = (double*)malloc(sizeof(double) * (size_t)d);
+    int rc = (!z || !alpha || !h || !Gh || !G || !t) ? -2 : 0;
+    /* forward of the site */
+    if (!rc) rc = oracle_depth_softmax(n, d, src, w, g, eps, z, alpha, h, NULL, NULL);
+    if (rc) {
+        free(z); free(alpha); free(h); free(Gh); free(G); free(t);
+        return rc;
+    }
+    /* PreNorm: x = gamma (.) y_h with y_h = h / r(h) */
+    if (prenorm) {
+        const double rh = oracle_rms(d, h, eps);
+        for (int64_t k = 0; k < d; ++k) {
+            G[k] = (gamma ? gamma[k] : 1.0) * dx[k];
+            if (dgamma) dgamma[k] += dx[k] * (h[k] / rh);
+        }
+        rms_core_backward(d, h, eps, G, Gh);
+    } else {
+        for (int64_t k = 0; k < d; ++k) Gh[k] = dx[k];
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        /* logit gradient: alpha_i G_h^T (u_i - h) */
+        double s = 0.0;
+        for (int64_t k = 0; k < d; ++k) s += Gh[k] * (src[i][k] - h[k]);
+        const double dz = alpha[i] * s;
+        /* score path: z_i = w^T (g (.) y_i) */
+        const double r = oracle_rms(d, src[i], eps);
+        for (int64_t k = 0; k < d; ++k) {
+            const double gk = g ? g[k] : 1.0;
+            const double y = src[i][k] / r;
+            G[k] = dz * w[k] * gk;       /* dL/dy_i */
+            dw[k] += dz * gk * y;
+            dg[k] += dz * w[k] * y;
+        }
+        rms_core_backward(d, src[i], eps, G, t);
+        /* value path + score path */
+        for (int64_t k = 0; k < d; ++k) du[i][k] = alpha[i] * Gh[k] + t[k];
+    }
+    free(z); free(alpha); free(h); free(Gh); free(G); free(t);
+    return 0;
+}
+
+int oracle_site_backward_tokens(int64_t n_tok, int64_t n, int64_t d, const float* src,
+                                const float* w, const float* g, const float* gamma, int prenorm,
+                                double eps, const float* dx, double* du, double* dw, double* dg,
+                                double* dgamma) {
+    if (n_tok < 0 || n <= 0 || d <= 0 || !src || !w || !dx || !du || !dw || !dg) return -1;
+    double* wd = (double*)malloc(sizeof(double) * (size_t)d);
+    double* gd = g ? (double*)malloc(sizeof(double) * (size_t)d) : NULL;
+    double* gmd = gamma ? (double*)malloc(sizeof(double) * (size_t)d) : NULL;
+    widen(d, w, wd);
+    if (gd) widen(d, g, gd);
+    if (gmd) widen(d, gamma, gmd);
+    for (int64_t k = 0; k < d; ++k) {
+        dw[k] = 0.0;
+        dg[k] = 0.0;
+        if (dgamma) dgamma[k] = 0.0;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* rows = (double*)malloc(sizeof(double) * (size_t)(n * d));
+        double* dxt = (double*)malloc(sizeof(double) * (size_t)d);
+        const double** sp = (const double**)malloc(sizeof(double*) * (size_t)n);
+        double** dp = (double**)malloc(sizeof(double*) * (size_t)n);
+        double* lw = (double*)calloc((size_t)d, sizeof(double));
+        double* lg = (double*)calloc((size_t)d, sizeof(double));
+        double* lgm = (double*)calloc((size_t)d, sizeof(double));
+        double* dut = (double*)malloc(sizeof(double) * (size_t)(n * d));
+#pragma omp for schedule(static)
+        for (int64_t tk = 0; tk < n_tok; ++tk) {
+            for (int64_t i = 0; i < n; ++i) {
+                widen(d, src + ((size_t)i * (size_t)n_tok + (size_t)tk) * (size_t)d, rows + i * d);
+                sp[i] = rows + i * d;
+                dp[i] = dut + i * d;
+            }
+            widen(d, dx + (size_t)tk * (size_t)d, dxt);
+            if (oracle_site_backward(n, d, sp, wd, gd, gmd, prenorm, eps, dxt, dp, lw, lg, lgm)) bad = 1;
+            for (int64_t i = 0; i < n; ++i)
+                memcpy(du + ((size_t)i * (size_t)n_tok + (size_t)tk) * (size_t)d, dut + i * d,
+                       sizeof(double) * (size_t)d);
+        }
+#pragma omp critical
+        {
+            for (int64_t k = 0; k < d; ++k) {
+                dw[k] += lw[k];
+                dg[k] += lg[k];
+                if (dgamma) dgamma[k] += lgm[k];
+            }
+        }
+        free(rows); free(dxt); free(sp); free(dp); free(lw); free(lg); free(lgm); free(dut);
+    }
+    free(wd); free(gd); free(gmd);
+    return bad ? -3 : 0;
+}

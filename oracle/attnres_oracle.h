@@ -106,6 +106,32 @@ int oracle_full_forward(int64_t n_tok, int64_t d, int64_t L, const float* emb, c
                         int final_site, double* x_out, double* h_out, double* lse_out,
                         double* hfinal_out);
 
+/* Backward of one aggregation site for one token.  Forward:
+ *   y_i = u_i / r_eps(u_i),  z_i = w^T (g (.) y_i),  alpha = softmax(z),
+ *   h = sum_i alpha_i u_i,   x = gamma (.) h / r_eps(h)  (prenorm != 0)
+ *                            x = h                        (prenorm == 0)
+ * Given dx = dL/dx, writes du[i] = dL/du_i (n rows of d) and ADDS this
+ * token's dL/dw, dL/dg, dL/dgamma to dw, dg, dgamma (dgamma may be NULL
+ * without PreNorm).  g, gamma NULL mean ones.  Steps, in the pages' order:
+ *   RMSNorm backward ("Attention Residuals 阅读补充", section on gradients
+ *   propagating along the tangent: the upstream gradient is multiplied by
+ *   gamma, then dL/dx = (G - y (y^T G)/d) / r), the logit gradient
+ *   dL/dz_i = alpha_i G_h^T (u_i - h) ("Attention Residuals" notes, section
+ *   7), the value path alpha_i G_h, and the score path through w, g and the
+ *   key RMSNorm (the same Jacobian). */
+int oracle_site_backward(int64_t n, int64_t d, const double* const* src, const double* w,
+                         const double* g, const double* gamma, int prenorm, double eps,
+                         const double* dx, double* const* du, double* dw, double* dg,
+                         double* dgamma);
+
+/* oracle_site_backward over n_tok tokens of fp32 inputs (src [n][n_tok][d],
+ * dx [n_tok][d]); du [n][n_tok][d]; dw, dg, dgamma [d] are the sums over the
+ * tokens (overwritten). */
+int oracle_site_backward_tokens(int64_t n_tok, int64_t n, int64_t d, const float* src,
+                                const float* w, const float* g, const float* gamma, int prenorm,
+                                double eps, const float* dx, double* du, double* dw, double* dg,
+                                double* dgamma);
+
 /* Number of OpenMP threads the forward functions use (1 without OpenMP). */
 int oracle_threads(void);
 

@@ -38,6 +38,19 @@ MUTATIONS = {
     "merge_unweighted": ("double den = a * lA + b * lB;", "double den = lA + lB;"),
 }
 
+# mistakes in the site backward, caught by its own pins
+BACKWARD_MUTATIONS = {
+    "bwd_logit_without_h": ("s += Gh[k] * (src[i][k] - h[k]);", "s += Gh[k] * src[i][k];"),
+    "bwd_rms_radial_term_dropped": ("dx_out[k] = (G[k] - (x[k] / r) * yg / (double)d) / r;",
+                                    "dx_out[k] = G[k] / r;"),
+    "bwd_prenorm_gain_ignored": ("G[k] = (gamma ? gamma[k] : 1.0) * dx[k];", "G[k] = dx[k];"),
+    "bwd_value_path_dropped": ("du[i][k] = alpha[i] * Gh[k] + t[k];", "du[i][k] = t[k];"),
+    "bwd_key_gain_missing_in_dw": ("dw[k] += dz * gk * y;", "dw[k] += dz * y;"),
+}
+PINS = {name: "test_oracle_pins.py" for name in MUTATIONS}
+PINS.update({name: "test_oracle_backward.py" for name in BACKWARD_MUTATIONS})
+MUTATIONS.update(BACKWARD_MUTATIONS)
+
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_catch_planted_mistake(name, tmp_path):
@@ -53,6 +66,6 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                     str(mutated), "-lm"], check=True)
     env = dict(os.environ, ATTNRES_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", PINS[name])],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, "pins did not catch mutation %s:\n%s" % (name, r.stdout[-2000:])

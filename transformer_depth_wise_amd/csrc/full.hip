@@ -45,20 +45,24 @@ __global__ __launch_bounds__(256) void k_merge_multi(int64_t T, int d, const St*
   const int lane = threadIdx.x & (kWave - 1);
   const int C = d >> 3;
   const float inv_d = 1.0f / (float)d;
-  float wq[CPL][8];
+  // w and g are loaded (clamped, unconditionally) and multiplied where the
+  // first row needs them, so no wait precedes the first token's loads
+  float wr[CPL][8], gk[CPL][8];
 #pragma unroll
   for (int c8 = 0; c8 < CPL; ++c8) {
-    const int c = tl + TEAM * c8;
-    if (c < C && k > 0) {
-      load8(w + c * 8, wq[c8]);
+    const int c0 = tl + TEAM * c8;
+    const int c = c0 < C ? c0 : C - 1;
+    if (k > 0) {
+      load8(w + c * 8, wr[c8]);
       if (kg) {
-        float g[8];
-        load8(kg + c * 8, g);
+        load8(kg + c * 8, gk[c8]);
+      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wq[c8][e] *= g[e];
+        for (int e = 0; e < 8; ++e) gk[c8][e] = 1.f;
       }
     } else {
-      zero8(wq[c8]);
+      zero8(wr[c8]);
+      zero8(gk[c8]);
     }
   }
   int parity = 0;
@@ -109,7 +113,7 @@ __global__ __launch_bounds__(256) void k_merge_multi(int64_t T, int d, const St*
             for (int e = 0; e < 8; ++e) {
               const float v = ok[c8] ? f[e] : 0.f;
               ss = fmaf(v, v, ss);
-              dot = fmaf(wq[c8][e], v, dot);
+              dot = fmaf(wr[c8][e] * gk[c8][e], v, dot);
             }
           }
           part[2 * (b0 + r)] = ss;
