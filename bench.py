@@ -239,6 +239,29 @@ def other_workloads(dev, steps: int):
                                  "bytes_per_step": b}
     del fulls, grouped
 
+    # backward of one aggregation site at the 16K chunk's final-site shape
+    # (9 sources), with and without the PreNorm
+    T, d, n = 16384, 7168, 9
+    gen = torch.Generator(device=dev).manual_seed(77)
+    src = torch.randn((n, T, d), generator=gen, device=dev).to(torch.bfloat16)
+    dx = torch.randn((T, d), generator=gen, device=dev).to(torch.bfloat16)
+    wq = torch.randn((d,), generator=gen, device=dev) * 0.02
+    kg = torch.rand((d,), generator=gen, device=dev) * 0.4 + 0.8
+    dsrc = torch.empty_like(src)
+    dw, dkg, dgm = (torch.empty((d,), device=dev) for _ in range(3))
+    ws = torch.empty(tdw.attnres_site_backward_workspace_bytes(T, d) // 4 + 4, device=dev)
+    for prenorm in (True, False):
+        f = lambda k: tdw.attnres_site_backward(src, n, wq, kg, kg if prenorm else None, prenorm, 1e-6, dx,  # noqa
+                                                dsrc, dw, dkg, dgm if prenorm else None, ws)
+        f(0)
+        sec = _time(f, max(steps, 10))
+        b = (2 * n + 1) * T * d * 2
+        res["site_backward_n9" + ("_prenorm" if prenorm else "")] = {
+            "config": {"T": T, "d": d, "sources": n, "prenorm": prenorm}, "ms_per_step": round(sec * 1e3, 4),
+            "value": round(T / sec, 1), "unit": "tokens/s", "hbm_gbps": round(b / sec / 1e9, 1),
+            "bytes_per_step": b, "note": "reads 9 source rows + dx, writes 9 gradient rows per token"}
+    del src, dx, dsrc, ws
+
     # one GPU's share (16384 / 8 tokens) of the 16K chunk
     w = synth.scaled(synth.WORKLOADS["prefill_chunk_bf16"], T=2048, name="prefill_share_2048")
     sts, subs, prm = block_states(w, 1)

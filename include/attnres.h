@@ -192,6 +192,36 @@ attnres_status_t attnres_full(attnres_dtype_t dt,
                               void* h_out, void* x_out, float* lse_out, void* stream);
 
 /*
+ * Backward of one depth-aggregation site, for training ("Attention
+ * Residuals" notes, section 7: the logit gradient dL/dz_i = alpha_i
+ * G_h^T (u_i - h); "Attention Residuals 阅读补充", gradients along the
+ * tangent: the RMSNorm Jacobian).  The site's forward over the sources
+ * u_i = src + i*src_stride (i < n_src, each [T][d] dtype dt) is
+ *     z_i = w^T(key_gain (.) u_i / r(u_i)),  alpha = softmax(z),
+ *     h = sum_i alpha_i u_i,  x = prenorm_gain (.) h / r(h)  (prenorm != 0;
+ *     x = h otherwise),
+ * recomputed here.  Given dx = dL/dx [T][d] (dtype dt), writes
+ *     dsrc + i*dsrc_stride = dL/du_i  ([T][d] dtype dt, i < n_src),
+ *     dw = dL/dw, dkey_gain = dL/dkey_gain (NULL: not computed),
+ *     dprenorm_gain = dL/dprenorm_gain (NULL or prenorm == 0: not computed),
+ * each [d] fp32, summed over the T tokens in a fixed order (bitwise
+ * reproducible).  key_gain, prenorm_gain NULL mean ones.
+ * Limits: 1 <= n_src <= ATTNRES_MAX_SOURCES_MULTI.  The dsrc rows must not
+ * overlap any input; the [d] outputs must not overlap anything.
+ * workspace: at least attnres_site_backward_workspace_bytes(T, d) bytes of
+ * caller-owned device memory, 16-byte aligned (per-team partial sums).
+ */
+int64_t attnres_site_backward_workspace_bytes(int64_t T, int64_t d);
+attnres_status_t attnres_site_backward(attnres_dtype_t dt,
+                                       const void* src, int64_t n_src, int64_t src_stride,
+                                       int64_t T, int64_t d,
+                                       const float* w, const float* key_gain,
+                                       const float* prenorm_gain, int prenorm, float eps,
+                                       const void* dx, void* dsrc, int64_t dsrc_stride,
+                                       float* dw, float* dkey_gain, float* dprenorm_gain,
+                                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * Block completion ("Attention Residuals" notes, section 8: b_n is the sum of
  * the block's sublayer outputs):
  *     out = ((partial_in or 0) + (v2 or 0)) + v      (fp32, in that order)

@@ -324,6 +324,59 @@ def test_phase1_long_range_equals_slices_and_oracle(dt, d, n, S):
             assert row_rel_err(_host(whole[0][q, t]), o_ref / ell) <= tol
 
 
+# ------------------------------------------------ backward of one site
+BWD = [
+    # (T, d, n, prenorm, dtype, query scale)
+    (300, 1024, 5, True, "bf16", 0.02),
+    (97, 7168, 9, True, "bf16", 0.02),
+    (64, 7168, 9, False, "bf16", 0.2),      # peaked softmax
+    (64, 256, 3, False, "f32", 0.1),
+    (33, 136, 16, True, "f32", 0.05),       # most sources, ragged d
+    (5, 8, 1, True, "f32", 1.0),            # one source: no score gradient
+    (40, 16384, 2, True, "bf16", 0.02),     # widest row
+    (2100, 2048, 4, True, "bf16", 0.02),    # many tokens per team
+]
+
+
+@pytest.mark.parametrize("T,d,n,prenorm,dt,qs", BWD)
+def test_site_backward_matches_oracle(T, d, n, prenorm, dt, qs):
+    """dL/du_i, dL/dw, dL/dg and dL/dgamma of one aggregation site against
+    the oracle's fp64 backward (itself pinned to finite differences)."""
+    _say("case site backward T=%d d=%d n=%d prenorm=%s %s" % (T, d, n, prenorm, dt))
+    dev = torch.device("cuda")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    g = torch.Generator(device=dev).manual_seed(5000 + T + d + n)
+    scales = torch.exp(torch.rand((n, 1, 1), generator=g, device=dev) * 2.0)
+    src = (torch.randn((n, T, d), generator=g, device=dev) * scales).to(tdt)
+    w = torch.randn((d,), generator=g, device=dev) * qs
+    kg = torch.rand((d,), generator=g, device=dev) * 0.4 + 0.8
+    gm = torch.rand((d,), generator=g, device=dev) * 0.4 + 0.8
+    dx = torch.randn((T, d), generator=g, device=dev).to(tdt)
+    dsrc = torch.empty_like(src)
+    dw = torch.empty((d,), device=dev)
+    dkg = torch.empty((d,), device=dev)
+    dgm = torch.empty((d,), device=dev)
+    ws = torch.empty(tdw.attnres_site_backward_workspace_bytes(T, d) // 4 + 4, device=dev)
+    tdw.attnres_site_backward(src, n, w, kg, gm if prenorm else None, prenorm, 1e-6, dx, dsrc, dw, dkg,
+                              dgm if prenorm else None, ws)
+    torch.cuda.synchronize()
+    ref = oracle.site_backward(src, w, kg, gm if prenorm else None, 1e-6, dx, prenorm=prenorm)
+    tol = TOL[dt]
+    err = row_rel_err(_host(dsrc).reshape(n * T, d), ref["du"].reshape(n * T, d)).max()
+    _say("worst du %.3e" % err)
+    assert err <= tol
+    for name, got in (("dw", dw), ("dg", dkg)) + ((("dgamma", dgm),) if prenorm else ()):
+        e = float(row_rel_err(_host(got), ref[name if name != "dg" else "dg"]))
+        _say("worst %s %.3e" % (name, e))
+        assert e <= tol, name
+    # a second run gives the same bits (fixed-order reductions, no atomics)
+    d2 = torch.empty_like(dsrc)
+    dw2 = torch.empty_like(dw)
+    tdw.attnres_site_backward(src, n, w, kg, gm if prenorm else None, prenorm, 1e-6, dx, d2, dw2, None, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(d2, dsrc) and torch.equal(dw2, dw)
+
+
 # --------------------------------------------- long context, chunked prefill
 def _long_prefill(w, chunked: bool, samples, dev):
     """Run the whole depth over T tokens, streamed in 16K chunks or in one

@@ -23,7 +23,8 @@ ATTNRES_MAX_SOURCES_MULTI = 16
 ATTNRES_MAX_GROUP_SOURCES = 16
 
 EXPORTED = ("attnres_phase1", "attnres_phase1_workspace_bytes", "attnres_phase2_merge", "attnres_phase2_merge_multi",
-            "attnres_full", "attnres_block_accumulate", "attnres_status_string")
+            "attnres_full", "attnres_block_accumulate", "attnres_site_backward", "attnres_site_backward_workspace_bytes",
+            "attnres_status_string")
 
 
 class AttnResError(RuntimeError):
@@ -52,9 +53,12 @@ def load(path: Optional[str] = None):
     lib.attnres_phase2_merge.argtypes = [E, I, I, V, V, E, V, V, V, E, V, V, V, V, F, V, V, V]
     lib.attnres_phase2_merge_multi.argtypes = [E, I, I, V, V, V, I, I, V, V, V, F, V, V, V]
     lib.attnres_full.argtypes = [E, V, I, I, I, I, V, V, V, F, V, V, V, V]
+    lib.attnres_site_backward.argtypes = [E, V, I, I, I, I, V, V, V, E, F, V, V, I, V, V, V, V, I, V]
+    lib.attnres_site_backward_workspace_bytes.argtypes = [I, I]
+    lib.attnres_site_backward_workspace_bytes.restype = ctypes.c_int64
     lib.attnres_block_accumulate.argtypes = [E, I, I, E, V, V, V, V, V]
     for fn in ("attnres_phase1", "attnres_phase2_merge", "attnres_phase2_merge_multi", "attnres_full",
-               "attnres_block_accumulate"):
+               "attnres_block_accumulate", "attnres_site_backward"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.attnres_status_string.argtypes = [ctypes.c_int]
     lib.attnres_status_string.restype = ctypes.c_char_p
@@ -164,6 +168,28 @@ def attnres_full(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optio
     rc = load().attnres_full(dtype_code(src.dtype), _ptr(src), n_src, stride, T, d, _ptr(w), _ptr(key_gain),
                              _ptr(prenorm_gain), eps, _ptr(h_out), _ptr(x_out), _ptr(lse_out), _stream(stream))
     _check("attnres_full", rc)
+
+
+def attnres_site_backward_workspace_bytes(T: int, d: int) -> int:
+    return int(load().attnres_site_backward_workspace_bytes(T, d))
+
+
+def attnres_site_backward(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],
+                          prenorm_gain: Optional[torch.Tensor], prenorm: bool, eps: float, dx: torch.Tensor,
+                          dsrc: torch.Tensor, dw: torch.Tensor, dkey_gain: Optional[torch.Tensor],
+                          dprenorm_gain: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
+    """src, dsrc: [>=n_src, T, d] slabs; dx: [T, d]; w, gains and their
+    gradients: [d] fp32; workspace: device tensor of at least
+    attnres_site_backward_workspace_bytes(T, d) bytes."""
+    T, d = dx.shape
+    stride = src.stride(0) if src.dim() == 3 else T * d
+    dstride = dsrc.stride(0) if dsrc.dim() == 3 else T * d
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = load().attnres_site_backward(dtype_code(src.dtype), _ptr(src), n_src, stride, T, d, _ptr(w), _ptr(key_gain),
+                                      _ptr(prenorm_gain), 1 if prenorm else 0, eps, _ptr(dx), _ptr(dsrc), dstride,
+                                      _ptr(dw), _ptr(dkey_gain), _ptr(dprenorm_gain), _ptr(workspace), ws_bytes,
+                                      _stream(stream))
+    _check("attnres_site_backward", rc)
 
 
 def attnres_block_accumulate(partial_in: Optional[torch.Tensor], v: torch.Tensor, out: torch.Tensor,

@@ -229,6 +229,55 @@ attnres_status_t attnres_phase2_merge_multi(attnres_dtype_t dt, int64_t T, int64
                                                 eps, h_out, x_out, static_cast<hipStream_t>(stream)));
 }
 
+int64_t attnres_site_backward_workspace_bytes(int64_t T, int64_t d) {
+  if (T < 0 || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
+  if (T == 0) return 0;
+  return attnres::backward_slots(T, (int)d) * 2 * d * (int64_t)sizeof(float);
+}
+
+attnres_status_t attnres_site_backward(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
+                                       int64_t T, int64_t d, const float* w, const float* key_gain,
+                                       const float* prenorm_gain, int prenorm, float eps, const void* dx,
+                                       void* dsrc, int64_t dsrc_stride, float* dw, float* dkey_gain,
+                                       float* dprenorm_gain, void* workspace, int64_t workspace_bytes,
+                                       void* stream) {
+  if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
+  attnres_status_t st = check_d(d);
+  if (st != ATTNRES_OK) return st;
+  if (T < 0 || n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
+  if (!src || !w || !dx || !dsrc || !dw) return ATTNRES_EINVAL;
+  if (n_src > 1 && (src_stride < T * d || dsrc_stride < T * d)) return ATTNRES_EINVAL;
+  if (src_stride % 8 != 0 || dsrc_stride % 8 != 0) return ATTNRES_EALIGN;
+  const int64_t ws_need = attnres_site_backward_workspace_bytes(T, d);
+  if (!workspace || workspace_bytes < ws_need) return ATTNRES_EINVAL;
+  st = check_align({src, w, key_gain, prenorm_gain, dx, dsrc, workspace}, {dw, dkey_gain, dprenorm_gain});
+  if (st != ATTNRES_OK) return st;
+  const int64_t es = esize(dt);
+  const Range rs = range_of(src, ((n_src - 1) * src_stride + T * d) * es);
+  const Range rds = range_of(dsrc, ((n_src - 1) * dsrc_stride + T * d) * es);
+  const Range rdx = range_of(dx, T * d * es);
+  const Range rw = range_of(w, d * 4);
+  const Range rg = key_gain ? range_of(key_gain, d * 4) : Range{0, 0};
+  const Range rgm = prenorm_gain ? range_of(prenorm_gain, d * 4) : Range{0, 0};
+  const Range rws = range_of(workspace, ws_need);
+  const Range odw = range_of(dw, d * 4);
+  const Range odg = dkey_gain ? range_of(dkey_gain, d * 4) : Range{0, 0};
+  const Range odm = (prenorm && dprenorm_gain) ? range_of(dprenorm_gain, d * 4) : Range{0, 0};
+  const Range outs[] = {rds, odw, odg, odm, rws};
+  for (Range o : outs)
+    for (Range i : {rs, rdx, rw, rg, rgm})
+      if (overlaps(o, i)) return ATTNRES_EALIAS;
+  for (int a = 0; a < 5; ++a)
+    for (int b = a + 1; b < 5; ++b)
+      if (overlaps(outs[a], outs[b])) return ATTNRES_EALIAS;
+  return hip_status(attnres::launch_site_backward(kind_of(dt), T, (int)d, src, (int)n_src, src_stride, w, key_gain,
+                                                  prenorm ? prenorm_gain : nullptr, prenorm ? 1 : 0, eps, dx, dsrc,
+                                                  dsrc_stride, dw, dkey_gain, prenorm ? dprenorm_gain : nullptr,
+                                                  static_cast<float*>(workspace),
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 attnres_status_t attnres_full(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride, int64_t T,
                               int64_t d, const float* w, const float* key_gain, const float* prenorm_gain,
                               float eps, void* h_out, void* x_out, float* lse_out, void* stream) {

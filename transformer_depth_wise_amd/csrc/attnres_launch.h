@@ -31,6 +31,12 @@ hipError_t launch_merge_multi(Dtype dt, int64_t T, int d, const void* o1, const 
                               int k, int64_t stride, const float* w, const float* kg, const float* gamma, float eps,
                               void* h_out, void* x_out, hipStream_t stream);
 
+hipError_t launch_site_backward(Dtype dt, int64_t T, int d, const void* src, int n, int64_t stride, const float* w,
+                                const float* kg, const float* gamma, int prenorm, float eps, const void* dx,
+                                void* dsrc, int64_t dstride, float* dw, float* dkg, float* dgamma, float* part,
+                                hipStream_t stream);
+int64_t backward_slots(int64_t T, int d);
+
 hipError_t launch_accumulate(Dtype dt, int64_t T, int d, Dtype pdt, const void* pin, const void* v2,
                              const void* v, void* out, hipStream_t stream);
 

@@ -1,0 +1,404 @@
+// Backward of one depth-aggregation site on gfx950 (training).
+//
+// Forward of the site (one query over n sources, "Attention Residuals"
+// notes, section 7):  y_i = u_i / r(u_i),  z_i = (w (.) g)^T y_i,
+// alpha = softmax(z),  h = sum_i alpha_i u_i,  x = gamma (.) h / r(h)  (or
+// x = h without PreNorm).  Given dx = dL/dx per token:
+//   G_h  = (gamma (.) dx - y_h (y_h^T (gamma (.) dx)) / d) / r(h),  y_h = h/r(h)
+//          (the RMSNorm backward of "Attention Residuals 阅读补充", gradients
+//          along the tangent; G_h = dx without PreNorm),
+//   dz_i = alpha_i G_h^T (u_i - h)        (the notes' logit gradient),
+//   du_i = alpha_i G_h + (dz_i (w (.) g) - y_i z_i dz_i / d) / r(u_i)
+//          (value path + score path through the key RMSNorm; the radial term
+//          uses y_i^T (w (.) g) = z_i),
+//   dw = g (.) A,  dg = w (.) A,  A = sum_tokens sum_i dz_i y_i,
+//   dgamma = sum_tokens dx (.) y_h.
+//
+// One team of threads per token row, each thread owning one chunk of 8
+// channels (two for d <= 1024 or d > 8192; teams of 64 to 1024 threads by
+// d, so that the per-thread state stays in registers; the per-source values
+// of the current token sit in a small LDS table written by one thread).  Per token: pass 1 reads the n rows and reduces their
+// sums of squares and scores in one batch; pass 2 re-reads them for h (L2
+// hits), reads dx and reduces |h|^2 and (gamma dx) . h; pass 3 reduces
+// G_h . u_i and G_h . h; pass 4 writes du_i.  Every reduction is a fixed-order
+// team reduction (wave shuffles, then waves in index order through LDS).  A
+// and the dgamma sums are accumulated per thread over the team's tokens,
+// written per team to the workspace, and summed over teams in a fixed order
+// by a second kernel: no atomics, bitwise reproducible.
+#include "attnres_device.h"
+#include "attnres_launch.h"
+
+namespace attnres {
+
+constexpr int kBwdMax = 16;   // sources per site
+constexpr int kBwdBatch = 4;  // rows loaded per batch
+
+// Fixed-order sum of v[0..nv) over the team (NW waves); `buf` holds NW * NV
+// floats of LDS, alternated by the caller between consecutive reductions.
+template <int NW, int NV>
+__device__ __forceinline__ void team_reduce(float (&v)[NV], int nv, float* buf, int wv, int lane) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (i < nv) v[i] = wave_sum(v[i]);
+  if (NW > 1) {
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (i < nv) buf[wv * NV + i] = v[i];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (i < nv) {
+        float s = buf[i];
+#pragma unroll
+        for (int k = 1; k < NW; ++k) s += buf[k * NV + i];
+        v[i] = s;
+      }
+  }
+}
+
+template <typename St, int TEAM, int CPL>
+__global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
+    int64_t T, int d, const St* __restrict__ src, int n, int64_t stride, const float* __restrict__ w,
+    const float* __restrict__ kg, const float* __restrict__ gamma, int prenorm, float eps,
+    const St* __restrict__ dx, St* __restrict__ dsrc, int64_t dstride, float* __restrict__ part) {
+  constexpr int WG = TEAM < 256 ? 256 : TEAM;
+  constexpr int TPW = WG / TEAM;
+  constexpr int NW = TEAM / kWave;
+  constexpr int NV = 2 * kBwdMax + 2;
+  constexpr int kB = TEAM >= 1024 ? 2 : kBwdBatch;  // rows per load batch (registers of the widest teams)
+  __shared__ float red[2][TPW][NW * NV];
+  // per-source values of the team's current token: 1/r(u_i), z_i, alpha_i, dz_i
+  __shared__ float sv[TPW][4][kBwdMax];
+  const int team = threadIdx.x / TEAM;
+  const int tl = threadIdx.x % TEAM;
+  const int wv = tl / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int C = d >> 3;
+  const float inv_d = 1.0f / (float)d;
+  float* const s_ri = sv[team][0];
+  float* const s_z = sv[team][1];
+  float* const s_al = sv[team][2];
+  float* const s_dz = sv[team][3];
+  bool ok[CPL];
+  int cc[CPL];
+#pragma unroll
+  for (int c8 = 0; c8 < CPL; ++c8) {
+    const int c0 = tl + TEAM * c8;
+    ok[c8] = c0 < C;
+    cc[c8] = ok[c8] ? c0 : C - 1;
+  }
+  float wq[CPL][8], accA[CPL][8], accG[CPL][8];
+#pragma unroll
+  for (int c8 = 0; c8 < CPL; ++c8) {
+    float g8[8];
+    load8(w + cc[c8] * 8, wq[c8]);
+    if (kg) {
+      load8(kg + cc[c8] * 8, g8);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g8[e] = 1.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      wq[c8][e] = ok[c8] ? wq[c8][e] * g8[e] : 0.f;
+      accA[c8][e] = 0.f;
+      accG[c8][e] = 0.f;
+    }
+  }
+  int parity = 0;
+  const int64_t step = (int64_t)gridDim.x * TPW;
+  // every team of a workgroup runs the same number of iterations (the
+  // reductions synchronise the workgroup); tokens past T are clamped and
+  // neither stored nor accumulated
+  for (int64_t tok = (int64_t)blockIdx.x * TPW + team; tok - team < T; tok += step) {
+    const bool live = tok < T;
+    const int64_t tc = live ? tok : T - 1;
+    const St* base = src + tc * d;
+    // ---- pass 1: |u_i|^2 and (w (.) g) . u_i
+    {
+      float v[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) v[i] = 0.f;
+#pragma unroll
+      for (int b0 = 0; b0 < kBwdMax; b0 += kB) {
+        if (b0 < n) {
+          Chunk<St> u[kB][CPL];
+#pragma unroll
+          for (int r = 0; r < kB; ++r) {
+            const int i = b0 + r < n ? b0 + r : n - 1;
+#pragma unroll
+            for (int c8 = 0; c8 < CPL; ++c8) u[r][c8].load(base + (int64_t)i * stride + cc[c8] * 8);
+          }
+#pragma unroll
+          for (int r = 0; r < kB; ++r)
+#pragma unroll
+            for (int c8 = 0; c8 < CPL; ++c8) {
+              float f[8];
+              u[r][c8].unpack(f);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float x = ok[c8] ? f[e] : 0.f;
+                v[2 * (b0 + r)] = fmaf(x, x, v[2 * (b0 + r)]);
+                v[2 * (b0 + r) + 1] = fmaf(wq[c8][e], x, v[2 * (b0 + r) + 1]);
+              }
+            }
+        }
+      }
+      team_reduce<NW, NV>(v, 2 * n, &red[parity][team][0], wv, lane);
+      parity ^= 1;
+      if (tl == 0) {
+        float M = -INFINITY;
+        for (int i = 0; i < n; ++i) {
+          s_ri[i] = 1.0f / sqrtf(v[2 * i] * inv_d + eps);
+          s_z[i] = v[2 * i + 1] * s_ri[i];
+          M = fmaxf(M, s_z[i]);
+        }
+        float den = 0.f;
+        for (int i = 0; i < n; ++i) {
+          s_al[i] = expf(s_z[i] - M);
+          den += s_al[i];
+        }
+        for (int i = 0; i < n; ++i) s_al[i] = s_al[i] / den;
+      }
+      lds_barrier();
+    }
+    // ---- pass 2: h, dx, then G_h (PreNorm backward)
+    float h[CPL][8], gdx[CPL][8];
+#pragma unroll
+    for (int c8 = 0; c8 < CPL; ++c8) zero8(h[c8]);
+#pragma unroll
+    for (int b0 = 0; b0 < kBwdMax; b0 += kB) {
+      if (b0 < n) {
+        Chunk<St> u[kB][CPL];
+#pragma unroll
+        for (int r = 0; r < kB; ++r) {
+          const int i = b0 + r < n ? b0 + r : n - 1;
+#pragma unroll
+          for (int c8 = 0; c8 < CPL; ++c8) u[r][c8].load(base + (int64_t)i * stride + cc[c8] * 8);
+        }
+#pragma unroll
+        for (int r = 0; r < kB; ++r)
+          if (b0 + r < n) {
+            const float a = s_al[b0 + r];
+#pragma unroll
+            for (int c8 = 0; c8 < CPL; ++c8) {
+              float f[8];
+              u[r][c8].unpack(f);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) h[c8][e] = fmaf(a, f[e], h[c8][e]);
+            }
+          }
+      }
+    }
+#pragma unroll
+    for (int c8 = 0; c8 < CPL; ++c8) {
+      Chunk<St> ch;
+      ch.load(dx + tc * d + cc[c8] * 8);
+      ch.unpack(gdx[c8]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (!ok[c8]) h[c8][e] = 0.f;
+        gdx[c8][e] = ok[c8] ? gdx[c8][e] : 0.f;
+      }
+    }
+    if (prenorm) {
+      float gm[CPL][8];
+#pragma unroll
+      for (int c8 = 0; c8 < CPL; ++c8) {
+        if (gamma) {
+          load8(gamma + cc[c8] * 8, gm[c8]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gm[c8][e] = 1.f;
+        }
+      }
+      float p2[2] = {0.f, 0.f};
+#pragma unroll
+      for (int c8 = 0; c8 < CPL; ++c8)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p2[0] = fmaf(h[c8][e], h[c8][e], p2[0]);
+          p2[1] = fmaf(gm[c8][e] * gdx[c8][e], h[c8][e], p2[1]);
+        }
+      team_reduce<NW, 2>(p2, 2, &red[parity][team][0], wv, lane);
+      parity ^= 1;
+      const float rh = 1.0f / sqrtf(p2[0] * inv_d + eps);
+      const float cr = p2[1] * rh * rh * rh * inv_d;
+#pragma unroll
+      for (int c8 = 0; c8 < CPL; ++c8)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (live) accG[c8][e] = fmaf(gdx[c8][e], h[c8][e] * rh, accG[c8][e]);
+          gdx[c8][e] = gm[c8][e] * gdx[c8][e] * rh - h[c8][e] * cr;  // G_h
+        }
+    }
+    // ---- pass 3: G_h . u_i and G_h . h -> dz_i
+    {
+      float v[kBwdMax + 1];
+#pragma unroll
+      for (int i = 0; i <= kBwdMax; ++i) v[i] = 0.f;
+#pragma unroll
+      for (int c8 = 0; c8 < CPL; ++c8)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[kBwdMax] = fmaf(gdx[c8][e], h[c8][e], v[kBwdMax]);
+#pragma unroll
+      for (int b0 = 0; b0 < kBwdMax; b0 += kB) {
+        if (b0 < n) {
+          Chunk<St> u[kB][CPL];
+#pragma unroll
+          for (int r = 0; r < kB; ++r) {
+            const int i = b0 + r < n ? b0 + r : n - 1;
+#pragma unroll
+            for (int c8 = 0; c8 < CPL; ++c8) u[r][c8].load(base + (int64_t)i * stride + cc[c8] * 8);
+          }
+#pragma unroll
+          for (int r = 0; r < kB; ++r)
+#pragma unroll
+            for (int c8 = 0; c8 < CPL; ++c8) {
+              float f[8];
+              u[r][c8].unpack(f);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[b0 + r] = fmaf(gdx[c8][e], ok[c8] ? f[e] : 0.f, v[b0 + r]);
+            }
+        }
+      }
+      // G_h . h moves next to the n source sums for one reduction
+      v[n < kBwdMax ? n : kBwdMax] = v[kBwdMax];
+      team_reduce<NW, kBwdMax + 1>(v, n + 1, &red[parity][team][0], wv, lane);
+      parity ^= 1;
+      if (tl == 0) {
+        for (int i = 0; i < n; ++i) s_dz[i] = s_al[i] * (v[i] - v[n]);
+      }
+      lds_barrier();
+    }
+    // ---- pass 4: du_i and the A sums
+#pragma unroll
+    for (int b0 = 0; b0 < kBwdMax; b0 += kB) {
+      if (b0 < n) {
+        Chunk<St> u[kB][CPL];
+#pragma unroll
+        for (int r = 0; r < kB; ++r) {
+          const int i = b0 + r < n ? b0 + r : n - 1;
+#pragma unroll
+          for (int c8 = 0; c8 < CPL; ++c8) u[r][c8].load(base + (int64_t)i * stride + cc[c8] * 8);
+        }
+#pragma unroll
+        for (int r = 0; r < kB; ++r) {
+          const int i = b0 + r;
+          if (i < n) {
+            const float a = s_al[i], g = s_dz[i], ri = s_ri[i], zi = s_z[i];
+#pragma unroll
+            for (int c8 = 0; c8 < CPL; ++c8) {
+              float f[8], o[8];
+              u[r][c8].unpack(f);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float y = f[e] * ri;
+                o[e] = fmaf(a, gdx[c8][e], g * ri * (wq[c8][e] - y * zi * inv_d));
+                if (live && ok[c8]) accA[c8][e] = fmaf(g, y, accA[c8][e]);
+              }
+              if (live && ok[c8]) store8(dsrc + (int64_t)i * dstride + tok * d + cc[c8] * 8, o);
+            }
+          }
+        }
+      }
+    }
+    // the next token's pass 1 rewrites the per-source values only after its
+    // own reduction barrier, which every lane reaches after finishing here
+  }
+  // per-team partial sums: part[slot][0][d] = A, part[slot][1][d] = dgamma
+  const int64_t slot = (int64_t)blockIdx.x * TPW + team;
+  float* pa = part + slot * 2 * (int64_t)d;
+#pragma unroll
+  for (int c8 = 0; c8 < CPL; ++c8)
+    if (ok[c8]) {
+      out8(pa + cc[c8] * 8, accA[c8]);
+      out8(pa + d + cc[c8] * 8, accG[c8]);
+    }
+}
+
+// Sum the per-team partials in slot order; dw = g (.) A, dg = w (.) A,
+// dgamma = the dgamma sum.  One thread per channel.
+__global__ __launch_bounds__(256) void k_site_backward_reduce(int64_t slots, int d, const float* __restrict__ part,
+                                                              const float* __restrict__ w,
+                                                              const float* __restrict__ kg,
+                                                              float* __restrict__ dw, float* __restrict__ dkg,
+                                                              float* __restrict__ dgamma) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= d) return;
+  float A = 0.f, G = 0.f;
+  for (int64_t s = 0; s < slots; ++s) {
+    A += part[s * 2 * (int64_t)d + k];
+    G += part[s * 2 * (int64_t)d + d + k];
+  }
+  dw[k] = kg ? kg[k] * A : A;
+  if (dkg) dkg[k] = w[k] * A;
+  if (dgamma) dgamma[k] = G;
+}
+
+int backward_team(int d) {
+  const int C = d >> 3;
+  if (C <= 128) return 64;
+  if (C <= 256) return 256;
+  if (C <= 512) return 512;
+  return 1024;
+}
+
+int64_t backward_slots(int64_t T, int d) {
+  const int team = backward_team(d);
+  const int tpw = team < 256 ? 256 / team : 1;
+  const int64_t wgs = (T + tpw - 1) / tpw;
+  return (wgs < 1024 ? wgs : 1024) * tpw;
+}
+
+template <typename St, int TEAM, int CPL>
+static hipError_t run_bwd(int64_t T, int d, const void* src, int n, int64_t stride, const float* w,
+                          const float* kg, const float* gamma, int prenorm, float eps, const void* dx, void* dsrc,
+                          int64_t dstride, float* dw, float* dkg, float* dgamma, float* part, hipStream_t stream) {
+  constexpr int WG = TEAM < 256 ? 256 : TEAM;
+  constexpr int TPW = WG / TEAM;
+  int64_t wgs = (T + TPW - 1) / TPW;
+  const int64_t cap = (int64_t)device_cu_count() * (TEAM >= 512 ? 1 : 2);
+  if (wgs > cap) wgs = cap;
+  if (wgs > 1024) wgs = 1024;
+  hipLaunchKernelGGL((k_site_backward<St, TEAM, CPL>), dim3((unsigned)wgs), dim3(WG), 0, stream, T, d,
+                     static_cast<const St*>(src), n, stride, w, kg, gamma, prenorm, eps, static_cast<const St*>(dx),
+                     static_cast<St*>(dsrc), dstride, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_site_backward_reduce, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, stream, wgs * TPW, d,
+                     part, w, kg, dw, dkg, prenorm ? dgamma : nullptr);
+  return hipGetLastError();
+}
+
+template <typename St>
+static hipError_t pick_bwd(int64_t T, int d, const void* src, int n, int64_t stride, const float* w, const float* kg,
+                           const float* gamma, int prenorm, float eps, const void* dx, void* dsrc, int64_t dstride,
+                           float* dw, float* dkg, float* dgamma, float* part, hipStream_t stream) {
+  const int C = d >> 3;
+#define ATTNRES_BWD(TEAM_, CPL_)                                                                                  \
+  return run_bwd<St, TEAM_, CPL_>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, dstride, dw, dkg, \
+                                  dgamma, part, stream)
+  if (C <= 64) ATTNRES_BWD(64, 1);
+  if (C <= 128) ATTNRES_BWD(64, 2);
+  if (C <= 256) ATTNRES_BWD(256, 1);
+  if (C <= 512) ATTNRES_BWD(512, 1);
+  if (C <= 1024) ATTNRES_BWD(1024, 1);
+  ATTNRES_BWD(1024, 2);
+#undef ATTNRES_BWD
+}
+
+hipError_t launch_site_backward(Dtype dt, int64_t T, int d, const void* src, int n, int64_t stride, const float* w,
+                                const float* kg, const float* gamma, int prenorm, float eps, const void* dx,
+                                void* dsrc, int64_t dstride, float* dw, float* dkg, float* dgamma, float* part,
+                                hipStream_t stream) {
+  if (dt == kBF16)
+    return pick_bwd<bf16_t>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, dstride, dw, dkg, dgamma,
+                            part, stream);
+  return pick_bwd<float>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, dstride, dw, dkg, dgamma, part,
+                         stream);
+}
+
+}  // namespace attnres
