@@ -184,6 +184,27 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Sum over the 64 lanes of a wave without LDS: DPP butterflies inside each
+// 16-lane row (swap neighbours, swap pairs, mirror halves, mirror the row;
+// every step adds two equal-sized partial sums, so all lanes of a row hold
+// the same bits), then the four row sums read into scalars and added as
+// (r0 + r1) + (r2 + r3).  The result is the same in every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_step(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x = dpp_step<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_step<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_step<0x141>(x);  // row_half_mirror
+  x = dpp_step<0x140>(x);  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // orders global memory, which makes every wave wait for all of its global
 // loads and stores in flight (the prefetched next item included); here those

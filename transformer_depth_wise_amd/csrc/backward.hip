@@ -14,13 +14,14 @@
 //   dw = g (.) A,  dg = w (.) A,  A = sum_tokens sum_i dz_i y_i,
 //   dgamma = sum_tokens dx (.) y_h.
 //
-// One team of threads per token row, each thread owning one chunk of 8
-// channels (two for d <= 1024 or d > 8192; teams of 64 to 1024 threads by
-// d, so that the per-thread state stays in registers; the per-source values
-// of the current token sit in a small LDS table written by one thread).  Per token: pass 1 reads the n rows and reduces their
-// sums of squares and scores in one batch; pass 2 re-reads them for h (L2
-// hits), reads dx and reduces |h|^2 and (gamma dx) . h; pass 3 reduces
-// G_h . u_i and G_h . h; pass 4 writes du_i.  Every reduction is a fixed-order
+// One team of threads per token row, each thread owning one or two chunks of
+// 8 channels (teams of 64 to 1024 threads by d); the per-source values of
+// the current token sit in a small LDS table written by one thread.  For
+// d <= 8192 all n rows of a token are loaded once, together, into registers
+// (at most 16 rows x 2 chunks); wider rows are re-read by each pass (L2).
+// Per token: pass 1 reduces the rows' sums of squares and scores in one
+// batch; pass 2 forms h, reads dx and reduces |h|^2 and (gamma dx) . h;
+// pass 3 reduces G_h . u_i and G_h . h; pass 4 writes du_i.  Every reduction is a fixed-order
 // team reduction (wave shuffles, then waves in index order through LDS).  A
 // and the dgamma sums are accumulated per thread over the team's tokens,
 // written per team to the workspace, and summed over teams in a fixed order
@@ -33,32 +34,31 @@ namespace attnres {
 constexpr int kBwdMax = 16;   // sources per site
 constexpr int kBwdBatch = 4;  // rows loaded per batch
 
-// Fixed-order sum of v[0..nv) over the team (NW waves); `buf` holds NW * NV
-// floats of LDS, alternated by the caller between consecutive reductions.
+// Fixed-order sum of v[0..NV) over the team (NW waves): DPP wave sums, then
+// the waves in index order through LDS.  `buf` holds NW * NV floats of LDS,
+// alternated by the caller between consecutive reductions.  Unused entries
+// are zeros and cost a few instructions, not branches.
 template <int NW, int NV>
-__device__ __forceinline__ void team_reduce(float (&v)[NV], int nv, float* buf, int wv, int lane) {
+__device__ __forceinline__ void team_reduce(float (&v)[NV], float* buf, int wv, int lane) {
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if (i < nv) v[i] = wave_sum(v[i]);
+  for (int i = 0; i < NV; ++i) v[i] = wave_sum_dpp(v[i]);
   if (NW > 1) {
     if (lane == 0) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i)
-        if (i < nv) buf[wv * NV + i] = v[i];
+      for (int i = 0; i < NV; ++i) buf[wv * NV + i] = v[i];
     }
     lds_barrier();
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (i < nv) {
-        float s = buf[i];
+    for (int i = 0; i < NV; ++i) {
+      float s = buf[i];
 #pragma unroll
-        for (int k = 1; k < NW; ++k) s += buf[k * NV + i];
-        v[i] = s;
-      }
+      for (int k = 1; k < NW; ++k) s += buf[k * NV + i];
+      v[i] = s;
+    }
   }
 }
 
-template <typename St, int TEAM, int CPL>
+template <typename St, int TEAM, int CPL, bool HOLD, int NR>
 __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
     int64_t T, int d, const St* __restrict__ src, int n, int64_t stride, const float* __restrict__ w,
     const float* __restrict__ kg, const float* __restrict__ gamma, int prenorm, float eps,
@@ -66,11 +66,18 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
   constexpr int WG = TEAM < 256 ? 256 : TEAM;
   constexpr int TPW = WG / TEAM;
   constexpr int NW = TEAM / kWave;
-  constexpr int NV = 2 * kBwdMax + 2;
+  constexpr int NV = 2 * NR + 2;  // NR: rows this instance handles (n <= NR)
   constexpr int kB = TEAM >= 1024 ? 2 : kBwdBatch;  // rows per load batch (registers of the widest teams)
+  // HOLD: all n rows of the token are loaded once, together, and kept in
+  // registers for the four passes (the per-thread sums and w (.) g then live
+  // in LDS); otherwise every pass re-reads the rows (L2) and the sums and
+  // w (.) g stay in registers
+  Chunk<St> held[HOLD ? NR : 1][CPL];
   __shared__ float red[2][TPW][NW * NV];
   // per-source values of the team's current token: 1/r(u_i), z_i, alpha_i, dz_i
   __shared__ float sv[TPW][4][kBwdMax];
+  // HOLD: [2][CPL * 8][WG] per-thread sums (A, dgamma), then w (.) g [d]
+  extern __shared__ float dyn[];
   const int team = threadIdx.x / TEAM;
   const int tl = threadIdx.x % TEAM;
   const int wv = tl / kWave;
@@ -81,6 +88,10 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
   float* const s_z = sv[team][1];
   float* const s_al = sv[team][2];
   float* const s_dz = sv[team][3];
+  float* const wq_lds = dyn + 2 * CPL * 8 * WG;
+  auto acc = [&](int which, int c8, int e) -> float& {
+    return dyn[((which * CPL + c8) * 8 + e) * WG + threadIdx.x];
+  };
   bool ok[CPL];
   int cc[CPL];
 #pragma unroll
@@ -89,11 +100,11 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
     ok[c8] = c0 < C;
     cc[c8] = ok[c8] ? c0 : C - 1;
   }
-  float wq[CPL][8], accA[CPL][8], accG[CPL][8];
+  float wr[HOLD ? 1 : CPL][8], accA[HOLD ? 1 : CPL][8], accG[HOLD ? 1 : CPL][8];
 #pragma unroll
   for (int c8 = 0; c8 < CPL; ++c8) {
-    float g8[8];
-    load8(w + cc[c8] * 8, wq[c8]);
+    float wv8[8], g8[8];
+    load8(w + cc[c8] * 8, wv8);
     if (kg) {
       load8(kg + cc[c8] * 8, g8);
     } else {
@@ -102,11 +113,35 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      wq[c8][e] = ok[c8] ? wq[c8][e] * g8[e] : 0.f;
-      accA[c8][e] = 0.f;
-      accG[c8][e] = 0.f;
+      const float q = ok[c8] ? wv8[e] * g8[e] : 0.f;
+      if (HOLD) {
+        acc(0, c8, e) = 0.f;
+        acc(1, c8, e) = 0.f;
+      } else {
+        wr[c8][e] = q;
+        accA[c8][e] = 0.f;
+        accG[c8][e] = 0.f;
+      }
+    }
+    if (HOLD && ok[c8] && team == 0) {
+      float4* q4 = reinterpret_cast<float4*>(wq_lds + cc[c8] * 8);
+      q4[0] = make_float4(wv8[0] * g8[0], wv8[1] * g8[1], wv8[2] * g8[2], wv8[3] * g8[3]);
+      q4[1] = make_float4(wv8[4] * g8[4], wv8[5] * g8[5], wv8[6] * g8[6], wv8[7] * g8[7]);
     }
   }
+  if (HOLD) lds_barrier();
+  // w (.) g for chunk c8 of this thread
+  auto wq = [&](int c8, float (&q)[8]) {
+    if (HOLD) {
+      const float4* q4 = reinterpret_cast<const float4*>(wq_lds + cc[c8] * 8);
+      const float4 a = q4[0], b = q4[1];
+      q[0] = a.x; q[1] = a.y; q[2] = a.z; q[3] = a.w; q[4] = b.x; q[5] = b.y; q[6] = b.z; q[7] = b.w;
+      if (!ok[c8]) zero8(q);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = wr[HOLD ? 0 : c8][e];
+    }
+  };
   int parity = 0;
   const int64_t step = (int64_t)gridDim.x * TPW;
   // every team of a workgroup runs the same number of iterations (the
@@ -116,87 +151,110 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
     const bool live = tok < T;
     const int64_t tc = live ? tok : T - 1;
     const St* base = src + tc * d;
+    Chunk<St> dxc[CPL];
+#pragma unroll
+    for (int c8 = 0; c8 < CPL; ++c8) dxc[c8].load(dx + tc * d + cc[c8] * 8);
+    if (HOLD) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int ic = i < n ? i : n - 1;  // clamped: always a valid row
+#pragma unroll
+        for (int c8 = 0; c8 < CPL; ++c8) held[HOLD ? i : 0][c8].load(base + (int64_t)ic * stride + cc[c8] * 8);
+      }
+    }
+    // row i of the token, chunk c8 (held, or loaded now)
+    auto row = [&](int i, int c8) -> Chunk<St> {
+      Chunk<St> ch;
+      if (HOLD) {
+        ch = held[HOLD ? i : 0][c8];
+      } else {
+        ch.load(base + (int64_t)(i < n ? i : n - 1) * stride + cc[c8] * 8);
+      }
+      return ch;
+    };
     // ---- pass 1: |u_i|^2 and (w (.) g) . u_i
     {
       float v[NV];
 #pragma unroll
       for (int i = 0; i < NV; ++i) v[i] = 0.f;
 #pragma unroll
-      for (int b0 = 0; b0 < kBwdMax; b0 += kB) {
-        if (b0 < n) {
-          Chunk<St> u[kB][CPL];
+      for (int c8 = 0; c8 < CPL; ++c8) {
+        float q[8];
+        wq(c8, q);
 #pragma unroll
-          for (int r = 0; r < kB; ++r) {
-            const int i = b0 + r < n ? b0 + r : n - 1;
+        for (int b0 = 0; b0 < NR; b0 += kB) {
+          if (b0 < n) {
+            Chunk<St> u[kB];
 #pragma unroll
-            for (int c8 = 0; c8 < CPL; ++c8) u[r][c8].load(base + (int64_t)i * stride + cc[c8] * 8);
-          }
+            for (int r = 0; r < kB; ++r) u[r] = row(b0 + r, c8);
 #pragma unroll
-          for (int r = 0; r < kB; ++r)
+            for (int r = 0; r < kB; ++r) {
+              if (b0 + r < n) {  // uniform: padding rows of the batch are skipped
+                float f[8];
+                u[r].unpack(f);
 #pragma unroll
-            for (int c8 = 0; c8 < CPL; ++c8) {
-              float f[8];
-              u[r][c8].unpack(f);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const float x = ok[c8] ? f[e] : 0.f;
-                v[2 * (b0 + r)] = fmaf(x, x, v[2 * (b0 + r)]);
-                v[2 * (b0 + r) + 1] = fmaf(wq[c8][e], x, v[2 * (b0 + r) + 1]);
+                for (int e = 0; e < 8; ++e) {
+                  const float x = ok[c8] ? f[e] : 0.f;
+                  v[2 * (b0 + r)] = fmaf(x, x, v[2 * (b0 + r)]);
+                  v[2 * (b0 + r) + 1] = fmaf(q[e], x, v[2 * (b0 + r) + 1]);
+                }
               }
             }
+          }
         }
       }
-      team_reduce<NW, NV>(v, 2 * n, &red[parity][team][0], wv, lane);
+      team_reduce<NW, NV>(v, &red[parity][team][0], wv, lane);
       parity ^= 1;
-      if (tl == 0) {
-        float M = -INFINITY;
-        for (int i = 0; i < n; ++i) {
-          s_ri[i] = 1.0f / sqrtf(v[2 * i] * inv_d + eps);
-          s_z[i] = v[2 * i + 1] * s_ri[i];
-          M = fmaxf(M, s_z[i]);
+      // lane i of the team's first wave handles source i; max and sum over
+      // the n sources with DPP (lanes >= n contribute -inf / 0)
+      if (wv == 0) {
+        float ss = 0.f, dt = 0.f;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          ss = lane == i ? v[2 * i] : ss;
+          dt = lane == i ? v[2 * i + 1] : dt;
         }
-        float den = 0.f;
-        for (int i = 0; i < n; ++i) {
-          s_al[i] = expf(s_z[i] - M);
-          den += s_al[i];
+        const bool src_lane = lane < n;
+        const float ri = 1.0f / sqrtf(ss * inv_d + eps);
+        const float zi = src_lane ? dt * ri : -INFINITY;
+        float M = zi;
+        M = fmaxf(M, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(M), 0xB1, 0xF, 0xF, false)));
+        M = fmaxf(M, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(M), 0x4E, 0xF, 0xF, false)));
+        M = fmaxf(M, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(M), 0x141, 0xF, 0xF, false)));
+        M = fmaxf(M, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(M), 0x140, 0xF, 0xF, false)));
+        const float e = src_lane ? expf(zi - M) : 0.f;
+        const float den = wave_sum_dpp(e);  // lanes >= 16 hold zeros
+        if (src_lane) {
+          s_ri[lane] = ri;
+          s_z[lane] = zi;
+          s_al[lane] = e / den;
         }
-        for (int i = 0; i < n; ++i) s_al[i] = s_al[i] / den;
       }
       lds_barrier();
     }
     // ---- pass 2: h, dx, then G_h (PreNorm backward)
     float h[CPL][8], gdx[CPL][8];
 #pragma unroll
-    for (int c8 = 0; c8 < CPL; ++c8) zero8(h[c8]);
+    for (int c8 = 0; c8 < CPL; ++c8) {
+      zero8(h[c8]);
 #pragma unroll
-    for (int b0 = 0; b0 < kBwdMax; b0 += kB) {
-      if (b0 < n) {
-        Chunk<St> u[kB][CPL];
+      for (int b0 = 0; b0 < NR; b0 += kB) {
+        if (b0 < n) {
+          Chunk<St> u[kB];
 #pragma unroll
-        for (int r = 0; r < kB; ++r) {
-          const int i = b0 + r < n ? b0 + r : n - 1;
+          for (int r = 0; r < kB; ++r) u[r] = row(b0 + r, c8);
 #pragma unroll
-          for (int c8 = 0; c8 < CPL; ++c8) u[r][c8].load(base + (int64_t)i * stride + cc[c8] * 8);
-        }
-#pragma unroll
-        for (int r = 0; r < kB; ++r)
-          if (b0 + r < n) {
-            const float a = s_al[b0 + r];
-#pragma unroll
-            for (int c8 = 0; c8 < CPL; ++c8) {
+          for (int r = 0; r < kB; ++r)
+            if (b0 + r < n) {
+              const float a = s_al[b0 + r];
               float f[8];
-              u[r][c8].unpack(f);
+              u[r].unpack(f);
 #pragma unroll
               for (int e = 0; e < 8; ++e) h[c8][e] = fmaf(a, f[e], h[c8][e]);
             }
-          }
+        }
       }
-    }
-#pragma unroll
-    for (int c8 = 0; c8 < CPL; ++c8) {
-      Chunk<St> ch;
-      ch.load(dx + tc * d + cc[c8] * 8);
-      ch.unpack(gdx[c8]);
+      dxc[c8].unpack(gdx[c8]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (!ok[c8]) h[c8][e] = 0.f;
@@ -222,7 +280,7 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
           p2[0] = fmaf(h[c8][e], h[c8][e], p2[0]);
           p2[1] = fmaf(gm[c8][e] * gdx[c8][e], h[c8][e], p2[1]);
         }
-      team_reduce<NW, 2>(p2, 2, &red[parity][team][0], wv, lane);
+      team_reduce<NW, 2>(p2, &red[parity][team][0], wv, lane);
       parity ^= 1;
       const float rh = 1.0f / sqrtf(p2[0] * inv_d + eps);
       const float cr = p2[1] * rh * rh * rh * inv_d;
@@ -230,77 +288,91 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
       for (int c8 = 0; c8 < CPL; ++c8)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          if (live) accG[c8][e] = fmaf(gdx[c8][e], h[c8][e] * rh, accG[c8][e]);
+          if (live) {
+            if (HOLD) {
+              acc(1, c8, e) = fmaf(gdx[c8][e], h[c8][e] * rh, acc(1, c8, e));
+            } else {
+              accG[HOLD ? 0 : c8][e] = fmaf(gdx[c8][e], h[c8][e] * rh, accG[HOLD ? 0 : c8][e]);
+            }
+          }
           gdx[c8][e] = gm[c8][e] * gdx[c8][e] * rh - h[c8][e] * cr;  // G_h
         }
     }
     // ---- pass 3: G_h . u_i and G_h . h -> dz_i
     {
-      float v[kBwdMax + 1];
+      float v[NR + 1];
 #pragma unroll
-      for (int i = 0; i <= kBwdMax; ++i) v[i] = 0.f;
+      for (int i = 0; i <= NR; ++i) v[i] = 0.f;
 #pragma unroll
-      for (int c8 = 0; c8 < CPL; ++c8)
+      for (int c8 = 0; c8 < CPL; ++c8) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[kBwdMax] = fmaf(gdx[c8][e], h[c8][e], v[kBwdMax]);
+        for (int e = 0; e < 8; ++e) v[NR] = fmaf(gdx[c8][e], h[c8][e], v[NR]);
 #pragma unroll
-      for (int b0 = 0; b0 < kBwdMax; b0 += kB) {
-        if (b0 < n) {
-          Chunk<St> u[kB][CPL];
+        for (int b0 = 0; b0 < NR; b0 += kB) {
+          if (b0 < n) {
+            Chunk<St> u[kB];
 #pragma unroll
-          for (int r = 0; r < kB; ++r) {
-            const int i = b0 + r < n ? b0 + r : n - 1;
+            for (int r = 0; r < kB; ++r) u[r] = row(b0 + r, c8);
 #pragma unroll
-            for (int c8 = 0; c8 < CPL; ++c8) u[r][c8].load(base + (int64_t)i * stride + cc[c8] * 8);
-          }
+            for (int r = 0; r < kB; ++r) {
+              if (b0 + r < n) {
+                float f[8];
+                u[r].unpack(f);
 #pragma unroll
-          for (int r = 0; r < kB; ++r)
-#pragma unroll
-            for (int c8 = 0; c8 < CPL; ++c8) {
-              float f[8];
-              u[r][c8].unpack(f);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) v[b0 + r] = fmaf(gdx[c8][e], ok[c8] ? f[e] : 0.f, v[b0 + r]);
+                for (int e = 0; e < 8; ++e) v[b0 + r] = fmaf(gdx[c8][e], ok[c8] ? f[e] : 0.f, v[b0 + r]);
+              }
             }
+          }
         }
       }
-      // G_h . h moves next to the n source sums for one reduction
-      v[n < kBwdMax ? n : kBwdMax] = v[kBwdMax];
-      team_reduce<NW, kBwdMax + 1>(v, n + 1, &red[parity][team][0], wv, lane);
+      // the NR source sums and G_h . h (entry NR) in one reduction
+      team_reduce<NW, NR + 1>(v, &red[parity][team][0], wv, lane);
       parity ^= 1;
-      if (tl == 0) {
-        for (int i = 0; i < n; ++i) s_dz[i] = s_al[i] * (v[i] - v[n]);
+      if (wv == 0) {
+        float di = 0.f;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) di = lane == i ? v[i] : di;
+        if (lane < n) s_dz[lane] = s_al[lane] * (di - v[NR]);
       }
       lds_barrier();
     }
     // ---- pass 4: du_i and the A sums
 #pragma unroll
-    for (int b0 = 0; b0 < kBwdMax; b0 += kB) {
-      if (b0 < n) {
-        Chunk<St> u[kB][CPL];
+    for (int c8 = 0; c8 < CPL; ++c8) {
+      float q[8], tA[8];
+      wq(c8, q);
+      zero8(tA);
 #pragma unroll
-        for (int r = 0; r < kB; ++r) {
-          const int i = b0 + r < n ? b0 + r : n - 1;
+      for (int b0 = 0; b0 < NR; b0 += kB) {
+        if (b0 < n) {
+          Chunk<St> u[kB];
 #pragma unroll
-          for (int c8 = 0; c8 < CPL; ++c8) u[r][c8].load(base + (int64_t)i * stride + cc[c8] * 8);
-        }
+          for (int r = 0; r < kB; ++r) u[r] = row(b0 + r, c8);
 #pragma unroll
-        for (int r = 0; r < kB; ++r) {
-          const int i = b0 + r;
-          if (i < n) {
-            const float a = s_al[i], g = s_dz[i], ri = s_ri[i], zi = s_z[i];
-#pragma unroll
-            for (int c8 = 0; c8 < CPL; ++c8) {
+          for (int r = 0; r < kB; ++r) {
+            const int i = b0 + r;
+            if (i < n) {
+              const float a = s_al[i], g = s_dz[i], ri = s_ri[i], zi = s_z[i];
               float f[8], o[8];
-              u[r][c8].unpack(f);
+              u[r].unpack(f);
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
                 const float y = f[e] * ri;
-                o[e] = fmaf(a, gdx[c8][e], g * ri * (wq[c8][e] - y * zi * inv_d));
-                if (live && ok[c8]) accA[c8][e] = fmaf(g, y, accA[c8][e]);
+                o[e] = fmaf(a, gdx[c8][e], g * ri * (q[e] - y * zi * inv_d));
+                tA[e] = fmaf(g, y, tA[e]);
               }
               if (live && ok[c8]) store8(dsrc + (int64_t)i * dstride + tok * d + cc[c8] * 8, o);
             }
+          }
+        }
+      }
+      if (live && ok[c8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (HOLD) {
+            acc(0, c8, e) += tA[e];
+          } else {
+            accA[HOLD ? 0 : c8][e] += tA[e];
           }
         }
       }
@@ -314,8 +386,14 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
 #pragma unroll
   for (int c8 = 0; c8 < CPL; ++c8)
     if (ok[c8]) {
-      out8(pa + cc[c8] * 8, accA[c8]);
-      out8(pa + d + cc[c8] * 8, accG[c8]);
+      float A8[8], G8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        A8[e] = HOLD ? acc(0, c8, e) : accA[HOLD ? 0 : c8][e];
+        G8[e] = HOLD ? acc(1, c8, e) : accG[HOLD ? 0 : c8][e];
+      }
+      out8(pa + cc[c8] * 8, A8);
+      out8(pa + d + cc[c8] * 8, G8);
     }
 }
 
@@ -342,7 +420,7 @@ int backward_team(int d) {
   const int C = d >> 3;
   if (C <= 128) return 64;
   if (C <= 256) return 256;
-  if (C <= 512) return 512;
+  if (C <= 1024) return 512;
   return 1024;
 }
 
@@ -353,17 +431,23 @@ int64_t backward_slots(int64_t T, int d) {
   return (wgs < 1024 ? wgs : 1024) * tpw;
 }
 
-template <typename St, int TEAM, int CPL>
+template <typename St, int TEAM, int CPL, bool HOLD, int NR>
 static hipError_t run_bwd(int64_t T, int d, const void* src, int n, int64_t stride, const float* w,
                           const float* kg, const float* gamma, int prenorm, float eps, const void* dx, void* dsrc,
                           int64_t dstride, float* dw, float* dkg, float* dgamma, float* part, hipStream_t stream) {
   constexpr int WG = TEAM < 256 ? 256 : TEAM;
   constexpr int TPW = WG / TEAM;
   int64_t wgs = (T + TPW - 1) / TPW;
-  const int64_t cap = (int64_t)device_cu_count() * (TEAM >= 512 ? 1 : 2);
+  const int64_t cap = (int64_t)device_cu_count() * (TEAM >= 512 ? 1 : 2);  // one or two resident per CU
   if (wgs > cap) wgs = cap;
   if (wgs > 1024) wgs = 1024;
-  hipLaunchKernelGGL((k_site_backward<St, TEAM, CPL>), dim3((unsigned)wgs), dim3(WG), 0, stream, T, d,
+  const size_t lds = HOLD ? sizeof(float) * ((size_t)2 * CPL * 8 * WG + (size_t)d) : 0;
+  if (lds > 48 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_site_backward<St, TEAM, CPL, HOLD, NR>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_site_backward<St, TEAM, CPL, HOLD, NR>), dim3((unsigned)wgs), dim3(WG), lds, stream, T, d,
                      static_cast<const St*>(src), n, stride, w, kg, gamma, prenorm, eps, static_cast<const St*>(dx),
                      static_cast<St*>(dsrc), dstride, part);
   hipError_t e = hipGetLastError();
@@ -378,15 +462,22 @@ static hipError_t pick_bwd(int64_t T, int d, const void* src, int n, int64_t str
                            const float* gamma, int prenorm, float eps, const void* dx, void* dsrc, int64_t dstride,
                            float* dw, float* dkg, float* dgamma, float* part, hipStream_t stream) {
   const int C = d >> 3;
-#define ATTNRES_BWD(TEAM_, CPL_)                                                                                  \
-  return run_bwd<St, TEAM_, CPL_>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, dstride, dw, dkg, \
-                                  dgamma, part, stream)
-  if (C <= 64) ATTNRES_BWD(64, 1);
-  if (C <= 128) ATTNRES_BWD(64, 2);
-  if (C <= 256) ATTNRES_BWD(256, 1);
-  if (C <= 512) ATTNRES_BWD(512, 1);
-  if (C <= 1024) ATTNRES_BWD(1024, 1);
-  ATTNRES_BWD(1024, 2);
+#define ATTNRES_BWD(TEAM_, CPL_, HOLD_, NR_)                                                                     \
+  return run_bwd<St, TEAM_, CPL_, HOLD_, NR_>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, dstride, \
+                                              dw, dkg, dgamma, part, stream)
+#define ATTNRES_BWD_HOLD(TEAM_, CPL_)       \
+  do {                                      \
+    if (n <= 8) ATTNRES_BWD(TEAM_, CPL_, true, 8);   \
+    if (n <= 12) ATTNRES_BWD(TEAM_, CPL_, true, 12); \
+    ATTNRES_BWD(TEAM_, CPL_, true, 16);             \
+  } while (0)
+  if (C <= 64) ATTNRES_BWD_HOLD(64, 1);
+  if (C <= 128) ATTNRES_BWD_HOLD(64, 2);
+  if (C <= 256) ATTNRES_BWD_HOLD(256, 1);
+  if (C <= 512) ATTNRES_BWD_HOLD(512, 1);
+  if (C <= 1024) ATTNRES_BWD_HOLD(512, 2);
+  ATTNRES_BWD(1024, 2, false, 16);
+#undef ATTNRES_BWD_HOLD
 #undef ATTNRES_BWD
 }
 
