@@ -111,6 +111,35 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt,
                                 void* out, float* m_out, float* lse_out,
                                 void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * Phase 1 of a block with the first sublayer's input finished in the same
+ * pass ("Attention Residuals" notes, section 10: the block's first sublayer
+ * has no partial-sum source and takes the phase-1 result as is; its PreNorm,
+ * fused as in "ML 研究者的三层基本功", system layer).  Computes everything
+ * attnres_phase1 does, except that query 0's output o_0 is not written to
+ * out: instead
+ *     x_out[t][:] = prenorm_gain (.) h / r(h),   h = o_0 rounded to dt,
+ * i.e. exactly what attnres_phase2_merge with sublayer_prev == NULL gives
+ * from a stored o_0 (up to the order of the sum of squares).
+ *   prenorm_gain: [d] fp32 (NULL = ones).  x_out: [T][d] dtype dt, required.
+ *   h_out: [T][d] dtype dt or NULL; when given it receives o_0 (= h of the
+ *   first sublayer).
+ *   out: [S][T][d] as for attnres_phase1, slabs 1..S-1 hold queries
+ *   1..S-1; slab 0 is scratch (its contents afterwards are unspecified).
+ *   out may be NULL only when n_src == 1 (every query's output is then the
+ *   source row itself).  m_out, lse_out: [S][T] fp32 for every query.
+ * Limits and workspace as attnres_phase1 with S >= 2 (also required for
+ * S == 1; n_src <= ATTNRES_MAX_SOURCES_MULTI).  x_out and h_out must not
+ * overlap any input or other output.
+ */
+attnres_status_t attnres_phase1_first_prenorm(attnres_dtype_t dt,
+                                              const void* src, int64_t n_src, int64_t src_stride,
+                                              int64_t T, int64_t d,
+                                              const float* w, const float* key_gain, int64_t S, float eps,
+                                              void* out, float* m_out, float* lse_out,
+                                              const float* prenorm_gain, void* x_out, void* h_out,
+                                              void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Workspace bytes attnres_phase1 uses: 16384 * ceil(d / 128) (packed
  * queries) + T * n_src * min(S, 32) * 4 (softmax weights); 0 for S == 1 with
  * more than ATTNRES_MAX_SOURCES_MULTI sources; -1 for invalid sizes. */

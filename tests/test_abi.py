@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_every_entry_point():
     names = declared_functions()
-    for n in ("attnres_phase1", "attnres_phase1_workspace_bytes", "attnres_phase2_merge",
+    for n in ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_workspace_bytes", "attnres_phase2_merge",
               "attnres_phase2_merge_multi", "attnres_full", "attnres_block_accumulate", "attnres_status_string"):
         assert n in names
 
@@ -100,6 +100,33 @@ def test_phase1_validation(lib):
     assert lib.attnres_phase1_workspace_bytes(4096, 12, 3, 4) == -1
     assert phase1(lib, T=0) == 0                      # nothing to do, nothing launched
     assert phase1(lib, T=0, src=None, out=None, lse=None) == 0
+
+
+def first_prenorm(lib, dt=1, src=A, n=3, stride=4096 * 64, T=4096, d=64, w=8 * A, kg=None, S=4, out=16 * A,
+                  m=None, lse=24 * A, gm=None, x=40 * A, h=None, ws=32 * A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attnres_phase1_workspace_bytes(T, d, n, S)
+    return checked(lib.attnres_phase1_first_prenorm(dt, p(src), n, stride, T, d, p(w), p(kg), S, 1e-6, p(out),
+                                                    p(m), p(lse), p(gm), p(x), p(h), p(ws), ws_bytes, None))
+
+
+def test_phase1_first_prenorm_validation(lib):
+    assert first_prenorm(lib, x=None) == EINVAL               # x_out is the point of the call
+    assert first_prenorm(lib, out=None) == EINVAL             # several sources need the outputs
+    assert first_prenorm(lib, n=17) == EINVAL
+    assert first_prenorm(lib, n=20, S=1) == EINVAL            # S == 1 still runs the streaming pair
+    assert first_prenorm(lib, S=1, ws=None) == EINVAL         # ... which needs the workspace
+    assert first_prenorm(lib, x=A + 64) == EALIAS             # x_out inside the sources
+    assert first_prenorm(lib, h=16 * A + 64) == EALIAS        # h_out inside out
+    assert first_prenorm(lib, x=16 * A) == EALIAS             # x_out is out's slab 0
+    assert first_prenorm(lib, h=40 * A + 16) == EALIAS        # h_out overlaps x_out
+    assert first_prenorm(lib, gm=40 * A) == EALIAS            # an output over the PreNorm gain
+    assert first_prenorm(lib, x=40 * A + 4) == EALIGN
+    assert first_prenorm(lib, gm=48 * A + 2) == EALIGN
+    assert first_prenorm(lib, d=12) == EALIGN
+    assert first_prenorm(lib, dt=9) == EDTYPE
+    assert first_prenorm(lib, T=0) == 0
+    assert first_prenorm(lib, T=0, x=None) == EINVAL
 
 
 def merge(lib, dt=1, T=1024, d=64, o=A, lse=2 * A, pdt=0, pin=None, v2=None, v=None, podt=0, pout=None, w=3 * A,

@@ -324,6 +324,71 @@ def test_phase1_long_range_equals_slices_and_oracle(dt, d, n, S):
             assert row_rel_err(_host(whole[0][q, t]), o_ref / ell) <= tol
 
 
+# ------------------- phase 1 with the first sublayer's PreNorm in the same pass
+FIRST = [
+    # (T, d, n, S, dtype, h_out): T None = long enough for the token-order kernel
+    (None, 7168, 8, 24, "bf16", False),
+    (None, 1032, 3, 5, "bf16", True),      # ragged last chunk group
+    (None, 13312, 2, 3, "bf16", False),    # widest row whose copy fits in LDS
+    (None, 16384, 2, 2, "bf16", True),     # wider: phase 1 + a separate PreNorm launch
+    (None, 4096, 4, 3, "f32", True),
+    (None, 8192, 1, 4, "f32", False),      # one source: out may be NULL
+    (37, 1032, 3, 4, "bf16", True),        # short range: item-order kernel + PreNorm launch
+    (37, 64, 1, 3, "f32", True),           # short range, one source
+]
+
+
+@pytest.mark.parametrize("T,d,n,S,dt,with_h", FIRST)
+def test_phase1_first_prenorm(T, d, n, S, dt, with_h):
+    """attnres_phase1_first_prenorm gives the statistics and queries 1..S-1
+    of attnres_phase1 bit for bit, h = o_0 bit for bit, and x within one
+    storage ulp of the two-launch path (phase 1, then the first sublayer's
+    merge); x matches the oracle on sampled tokens."""
+    dev = torch.device("cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    T = 32 * cus + 40 if T is None else T
+    _say("case phase1 first prenorm %s T=%d d=%d n=%d S=%d h=%s" % (dt, T, d, n, S, with_h))
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    g = torch.Generator(device=dev).manual_seed(5100 + d + n + S)
+    scale = torch.exp(torch.rand((n, 1, 1), generator=g, device=dev) * 2.0)
+    src = (torch.randn((n, T, d), generator=g, device=dev) * scale).to(tdt)
+    w = torch.randn((S, d), generator=g, device=dev) * 0.02
+    kg = torch.rand((S, d), generator=g, device=dev) * 0.4 + 0.8
+    gamma = torch.rand((d,), generator=g, device=dev) * 0.4 + 0.8
+    ws = torch.empty(tdw.attnres_phase1_workspace_bytes(T, d, n, S) // 4 + 4, device=dev)
+    eps = 1e-6
+    outA = torch.empty((S, T, d), dtype=tdt, device=dev)
+    mA, lseA = torch.empty((S, T), device=dev), torch.empty((S, T), device=dev)
+    hA, xA = torch.empty((T, d), dtype=tdt, device=dev), torch.empty((T, d), dtype=tdt, device=dev)
+    tdw.attnres_phase1(src, n, w, kg, eps, outA, mA, lseA, workspace=ws)
+    tdw.attnres_phase2_merge(outA[0], lseA[0], None, None, None, w[0], kg[0], gamma, eps, hA, xA)
+    outB = None if n == 1 else torch.zeros((S, T, d), dtype=tdt, device=dev)
+    mB, lseB = torch.empty((S, T), device=dev), torch.empty((S, T), device=dev)
+    xB = torch.empty((T, d), dtype=tdt, device=dev)
+    hB = torch.empty((T, d), dtype=tdt, device=dev) if with_h else None
+    tdw.attnres_phase1_first_prenorm(src, n, w, kg, eps, outB, mB, lseB, gamma, xB, hB, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(mA, mB) and torch.equal(lseA, lseB)
+    if outB is not None:
+        assert torch.equal(outA[1:], outB[1:])
+    if with_h:
+        assert torch.equal(hB, outA[0])
+    # x: the sum of squares runs in another order, so a value may land one
+    # storage ulp away
+    # (fp32: a few ulps, as r(h) itself may differ in its last bits)
+    diff = (xA.float() - xB.float()).abs()
+    ulp = 2.0 ** -7 if dt == "bf16" else 2.0 ** -20
+    assert (diff <= ulp * xA.float().abs()).all(), diff.max().item()
+    if dt == "bf16":
+        assert (diff > 0).float().mean().item() < 0.01
+    tol = TOL[dt]
+    for t in synth.sample_tokens(T, 8):
+        rows = [src[i, t].double().cpu().numpy() for i in range(n)]
+        h = oracle.depth_softmax(rows, w[0].cpu().numpy(), kg[0].cpu().numpy(), eps)["h"]
+        x = oracle.rmsnorm(h, gamma.cpu().numpy(), eps)
+        assert row_rel_err(_host(xB[t]), x) <= tol, t
+
+
 # ------------------------------------------------ backward of one site
 BWD = [
     # (T, d, n, prenorm, dtype, query scale)

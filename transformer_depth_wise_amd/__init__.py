@@ -4,12 +4,13 @@ The compute lives in ``libattnres.so`` (hand-written gfx950 HIP kernels behind
 a C ABI declared in ``include/attnres.h``); ``_lib`` binds it with ctypes and
 ``driver`` schedules the two-phase computation over a model's depth.
 """
-from ._lib import (attnres_block_accumulate, attnres_full, attnres_phase1, attnres_phase1_workspace_bytes,
+from ._lib import (attnres_block_accumulate, attnres_full, attnres_phase1, attnres_phase1_first_prenorm,
+                   attnres_phase1_workspace_bytes,
                    attnres_phase2_merge, attnres_phase2_merge_multi, attnres_site_backward,
                    attnres_site_backward_workspace_bytes, AttnResError, load, status_string)
 from .driver import BlockAttnRes, FullAttnRes, prefill_chunked
 
-__all__ = ["attnres_phase1", "attnres_phase1_workspace_bytes", "attnres_phase2_merge", "attnres_phase2_merge_multi",
+__all__ = ["attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_workspace_bytes", "attnres_phase2_merge", "attnres_phase2_merge_multi",
            "attnres_full", "attnres_block_accumulate", "attnres_site_backward",
            "attnres_site_backward_workspace_bytes", "AttnResError", "load", "status_string", "BlockAttnRes",
            "FullAttnRes", "prefill_chunked"]

@@ -1,4 +1,4 @@
-"""ctypes binding of libattnres.so: the four C-ABI entry points, same names.
+"""ctypes binding of libattnres.so: its C-ABI entry points, same names.
 
 Argument marshalling only.  Tensors are passed by device pointer together with
 the current HIP stream; every computation happens in the library's gfx950
@@ -22,7 +22,7 @@ ATTNRES_MAX_SOURCES = 32
 ATTNRES_MAX_SOURCES_MULTI = 16
 ATTNRES_MAX_GROUP_SOURCES = 16
 
-EXPORTED = ("attnres_phase1", "attnres_phase1_workspace_bytes", "attnres_phase2_merge", "attnres_phase2_merge_multi",
+EXPORTED = ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_workspace_bytes", "attnres_phase2_merge", "attnres_phase2_merge_multi",
             "attnres_full", "attnres_block_accumulate", "attnres_site_backward", "attnres_site_backward_workspace_bytes",
             "attnres_status_string")
 
@@ -48,6 +48,7 @@ def load(path: Optional[str] = None):
     lib = ctypes.CDLL(p)
     V, I, F, E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
     lib.attnres_phase1.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V, I, V]
+    lib.attnres_phase1_first_prenorm.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V, V, V, V, I, V]
     lib.attnres_phase1_workspace_bytes.argtypes = [I, I, I, I]
     lib.attnres_phase1_workspace_bytes.restype = ctypes.c_int64
     lib.attnres_phase2_merge.argtypes = [E, I, I, V, V, E, V, V, V, E, V, V, V, V, F, V, V, V]
@@ -57,7 +58,7 @@ def load(path: Optional[str] = None):
     lib.attnres_site_backward_workspace_bytes.argtypes = [I, I]
     lib.attnres_site_backward_workspace_bytes.restype = ctypes.c_int64
     lib.attnres_block_accumulate.argtypes = [E, I, I, E, V, V, V, V, V]
-    for fn in ("attnres_phase1", "attnres_phase2_merge", "attnres_phase2_merge_multi", "attnres_full",
+    for fn in ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase2_merge", "attnres_phase2_merge_multi", "attnres_full",
                "attnres_block_accumulate", "attnres_site_backward"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.attnres_status_string.argtypes = [ctypes.c_int]
@@ -124,6 +125,25 @@ def attnres_phase1(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Opt
                                S, eps, _ptr(out), _ptr(m_out), _ptr(lse_out), _ptr(workspace), ws_bytes,
                                _stream(stream))
     _check("attnres_phase1", rc)
+
+
+def attnres_phase1_first_prenorm(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],
+                                 eps: float, out: Optional[torch.Tensor], m_out: Optional[torch.Tensor],
+                                 lse_out: torch.Tensor, prenorm_gain: Optional[torch.Tensor], x_out: torch.Tensor,
+                                 h_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                                 stream=None) -> None:
+    """As attnres_phase1, but query 0's output goes through the PreNorm into
+    x_out ([T, d]; and as is into h_out when given) instead of out[0], which
+    is scratch; out may be None only when n_src == 1."""
+    S, T = lse_out.shape
+    d = src.shape[-1]
+    stride = src.stride(0) if src.dim() == 3 else T * d
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().attnres_phase1_first_prenorm(dtype_code(src.dtype), _ptr(src), n_src, stride, T, d, _ptr(w),
+                                             _ptr(key_gain), S, eps, _ptr(out), _ptr(m_out), _ptr(lse_out),
+                                             _ptr(prenorm_gain), _ptr(x_out), _ptr(h_out), _ptr(workspace),
+                                             ws_bytes, _stream(stream))
+    _check("attnres_phase1_first_prenorm", rc)
 
 
 def attnres_phase2_merge(p1_out: torch.Tensor, p1_lse: torch.Tensor, partial_in: Optional[torch.Tensor],

@@ -98,25 +98,28 @@ int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int6
   return 32 * 4 * 128 * kblocks + T * n_src * sq * (int64_t)sizeof(float);
 }
 
-attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
-                                int64_t T, int64_t d, const float* w, const float* key_gain, int64_t S,
-                                float eps, void* out, float* m_out, float* lse_out, void* workspace,
-                                int64_t workspace_bytes, void* stream) {
+// Shared by attnres_phase1 and attnres_phase1_first_prenorm (x0 != null).
+static attnres_status_t phase1_impl(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
+                                    int64_t T, int64_t d, const float* w, const float* key_gain, int64_t S,
+                                    float eps, void* out, float* m_out, float* lse_out, const float* gamma0,
+                                    void* x0, void* h0, void* workspace, int64_t workspace_bytes, void* stream) {
   if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
   if (T < 0 || S < 1 || n_src < 1) return ATTNRES_EINVAL;
-  if (n_src > (S == 1 ? ATTNRES_MAX_SOURCES : ATTNRES_MAX_SOURCES_MULTI)) return ATTNRES_EINVAL;
+  if (n_src > (S == 1 && !x0 ? ATTNRES_MAX_SOURCES : ATTNRES_MAX_SOURCES_MULTI)) return ATTNRES_EINVAL;
   if (T > (int64_t)1 << 40 || !(eps >= 0.f)) return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!src || !w || !lse_out) return ATTNRES_EINVAL;
+  if (x0 && !out && n_src > 1) return ATTNRES_EINVAL;
   if (n_src > 1 && (src_stride < T * d)) return ATTNRES_EINVAL;
   if (src_stride % 8 != 0) return ATTNRES_EALIGN;
   int64_t ws_need = attnres_phase1_workspace_bytes(T, d, n_src, S);
-  // S == 1: the workspace is optional (without it, one fused kernel runs)
-  if (S == 1 && (!workspace || workspace_bytes < ws_need)) ws_need = 0;
+  // S == 1 without the first-query PreNorm: the workspace is optional
+  // (without it, one fused kernel runs)
+  if (S == 1 && !x0 && (!workspace || workspace_bytes < ws_need)) ws_need = 0;
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return ATTNRES_EINVAL;
-  st = check_align({src, w, key_gain, out, ws_need > 0 ? workspace : nullptr}, {m_out, lse_out});
+  st = check_align({src, w, key_gain, out, ws_need > 0 ? workspace : nullptr, gamma0, x0, h0}, {m_out, lse_out});
   if (st != ATTNRES_OK) return st;
   const int64_t es = esize(dt);
   const Range rs = range_of(src, ((n_src - 1) * src_stride + T * d) * es);
@@ -126,11 +129,18 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_s
   const Range rw = range_of(w, S * d * 4);
   const Range rg = key_gain ? range_of(key_gain, S * d * 4) : Range{0, 0};
   const Range rws = ws_need > 0 ? range_of(workspace, ws_need) : Range{0, 0};
-  for (Range o : {ro, rl, rm, rws})
-    for (Range i : {rs, rw, rg})
+  const Range rx = x0 ? range_of(x0, T * d * es) : Range{0, 0};
+  const Range rh = h0 ? range_of(h0, T * d * es) : Range{0, 0};
+  const Range rgm = gamma0 ? range_of(gamma0, d * 4) : Range{0, 0};
+  for (Range o : {ro, rl, rm, rws, rx, rh})
+    for (Range i : {rs, rw, rg, rgm})
       if (overlaps(o, i)) return ATTNRES_EALIAS;
-  if (overlaps(ro, rl) || overlaps(ro, rm) || overlaps(rl, rm)) return ATTNRES_EALIAS;
-  if (overlaps(rws, ro) || overlaps(rws, rl) || overlaps(rws, rm)) return ATTNRES_EALIAS;
+  {
+    const Range outs[] = {ro, rl, rm, rws, rx, rh};
+    for (int a = 0; a < 6; ++a)
+      for (int b = a + 1; b < 6; ++b)
+        if (overlaps(outs[a], outs[b])) return ATTNRES_EALIAS;
+  }
 
   const Dtype kdt = kind_of(dt);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -142,11 +152,31 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_s
     char* o = out ? static_cast<char*>(out) + s0 * T * d * es : nullptr;
     hipError_t e = attnres::launch_phase1_multi(kdt, src, (int)n_src, src_stride, T, (int)d, w + s0 * d,
                                                 key_gain ? key_gain + s0 * d : nullptr, (int)sn, eps, o,
-                                                m_out ? m_out + s0 * T : nullptr, lse_out + s0 * T,
+                                                m_out ? m_out + s0 * T : nullptr, lse_out + s0 * T, gamma0,
+                                                s0 == 0 ? x0 : nullptr, s0 == 0 ? h0 : nullptr,
                                                 static_cast<float*>(workspace), s);
     if (e != hipSuccess) return ATTNRES_EHIP;
   }
   return ATTNRES_OK;
+}
+
+attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
+                                int64_t T, int64_t d, const float* w, const float* key_gain, int64_t S,
+                                float eps, void* out, float* m_out, float* lse_out, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+  return phase1_impl(dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, nullptr, nullptr,
+                     nullptr, workspace, workspace_bytes, stream);
+}
+
+attnres_status_t attnres_phase1_first_prenorm(attnres_dtype_t dt, const void* src, int64_t n_src,
+                                              int64_t src_stride, int64_t T, int64_t d, const float* w,
+                                              const float* key_gain, int64_t S, float eps, void* out,
+                                              float* m_out, float* lse_out, const float* prenorm_gain,
+                                              void* x_out, void* h_out, void* workspace, int64_t workspace_bytes,
+                                              void* stream) {
+  if (!x_out) return ATTNRES_EINVAL;
+  return phase1_impl(dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, prenorm_gain,
+                     x_out, h_out, workspace, workspace_bytes, stream);
 }
 
 attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, const void* p1_out,

@@ -10,12 +10,16 @@ enum Dtype { kF32 = 0, kBF16 = 1, kP24 = 2 };
 
 int device_cu_count();
 
-// Phase 1 of a block, one tile of at most 32 queries (S >= 2, n <= 16);
-// `alpha` is workspace for T * S * n fp32 softmax weights.  Or S == 1 with
+// Phase 1 of a block, one tile of at most 32 queries (n <= 16); `alpha` is
+// workspace for the packed queries and T * S * n fp32 softmax weights.  With
+// x0 != null, query 0's output goes through the PreNorm with gain gamma0
+// into x0 (and as is into h0 when not null) instead of slab 0 of out, which
+// may be used as scratch; out may then be null when n == 1.  Or S == 1 with
 // optional PreNorm (n <= 32).  Return a hipError_t.
 hipError_t launch_phase1_multi(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
                                const float* w, const float* kg, int S, float eps, void* out,
-                               float* m_out, float* lse_out, float* alpha, hipStream_t stream);
+                               float* m_out, float* lse_out, const float* gamma0, void* x0, void* h0,
+                               float* alpha, hipStream_t stream);
 
 hipError_t launch_phase1_single(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
                                 const float* w, const float* kg, const float* gamma, float eps,

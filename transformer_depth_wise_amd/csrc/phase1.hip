@@ -709,7 +709,8 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
   }
 }
 
-// S >= 2, second kernel: out[q][t] = sum_i alpha[t][q][i] u_i[t].  A wave owns
+// S >= 2, second kernel: out[q][t] = sum_i alpha[t][q][i] u_i[t] (query 0 to
+// out0, which is out itself unless the first query is redirected).  A wave owns
 // one (token, group of 64 chunks) item at a time, so the weights are
 // wave-uniform and come in through scalar loads; every source chunk is used
 // by all S queries; the next item's source chunks are loaded before the
@@ -731,7 +732,7 @@ __device__ __forceinline__ void p1_issue(Chunk<St> (&s)[N], bool& ok, int64_t it
 template <typename St, int N>
 __device__ __forceinline__ void p1_emit(const Chunk<St> (&s)[N], bool ok, int64_t item, int ngroups, int64_t T,
                                         int d, int lane, const float* __restrict__ alpha, int S,
-                                        St* __restrict__ out) {
+                                        St* __restrict__ out, St* __restrict__ out0) {
   const int64_t t = item / ngroups;
   const int c = (int)(item - t * ngroups) * 64 + lane;
   float b[N][8];
@@ -747,13 +748,14 @@ __device__ __forceinline__ void p1_emit(const Chunk<St> (&s)[N], bool ok, int64_
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = fmaf(a, b[i][e], o[e]);
     }
-    if (ok) out8_nt(out + ((int64_t)q * T + t) * d + c * 8, o);
+    if (ok) out8_nt((q == 0 ? out0 : out + (int64_t)q * T * d) + t * d + c * 8, o);
   }
 }
 
 template <typename St, int N>
 __global__ __launch_bounds__(256) void k_p1_out(const St* __restrict__ src, int64_t stride, int64_t T, int d,
-                                                const float* __restrict__ alpha, int S, St* __restrict__ out) {
+                                                const float* __restrict__ alpha, int S, St* __restrict__ out,
+                                                St* __restrict__ out0) {
   const int C = d >> 3;
   const int ngroups = (C + 63) >> 6;
   const int64_t items = T * ngroups;
@@ -765,12 +767,185 @@ __global__ __launch_bounds__(256) void k_p1_out(const St* __restrict__ src, int6
   p1_issue<St, N>(A, okA, item, items, ngroups, src, stride, d, C, lane);
   while (item < items) {
     p1_issue<St, N>(B, okB, item + nw, items, ngroups, src, stride, d, C, lane);
-    p1_emit<St, N>(A, okA, item, ngroups, T, d, lane, alpha, S, out);
+    p1_emit<St, N>(A, okA, item, ngroups, T, d, lane, alpha, S, out, out0);
     item += nw;
     if (item >= items) break;
     p1_issue<St, N>(A, okA, item + nw, items, ngroups, src, stride, d, C, lane);
-    p1_emit<St, N>(B, okB, item, ngroups, T, d, lane, alpha, S, out);
+    p1_emit<St, N>(B, okB, item, ngroups, T, d, lane, alpha, S, out, out0);
     item += nw;
+  }
+}
+
+// The same outputs in token order, for long token ranges: each wave owns whole
+// tokens (w, w + W, w + 2W, ... for the W waves of the grid) and walks the
+// chunk groups of one token before the next, with the following group's
+// source chunks in flight.  Launched with one workgroup per compute unit:
+// fewer concurrent write streams keep HBM writes closer to their ceiling
+// than the interleaved item order does.
+//
+// FIRST: the first query's output is the whole input of the block's first
+// sublayer (it has no partial-sum source, "Attention Residuals" notes,
+// section 10), so its PreNorm is applied here and o_0 itself is not stored:
+// o_0 is rounded to the storage type (the value a store and a later load
+// would give), kept in the wave's slice of LDS and its squares summed; after
+// the token's last group the wave writes x_0 = gamma0 (.) o_0 / r(o_0)
+// (and o_0 to h0 when asked).  `out` may then be null (one source: every
+// query's output is the source row itself).
+template <typename St>
+struct FirstSlot;
+template <>
+struct FirstSlot<bf16_t> {
+  static constexpr int kWords = 1;  // u32x4 words per 8-channel chunk
+  __device__ static void put(u32x4_t* p, const float (&o)[8], float (&r)[8]) {
+    const u32x4_t u{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                    pack_bf16x2(o[6], o[7])};
+    p[0] = u;
+    Chunk<bf16_t> c;
+    c.r = u;
+    c.unpack(r);
+  }
+  __device__ static void get(const u32x4_t* p, float (&r)[8]) {
+    Chunk<bf16_t> c;
+    c.r = p[0];
+    c.unpack(r);
+  }
+};
+template <>
+struct FirstSlot<float> {
+  static constexpr int kWords = 2;
+  __device__ static void put(u32x4_t* p, const float (&o)[8], float (&r)[8]) {
+    p[0] = u32x4_t{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+    p[1] = u32x4_t{__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = o[e];
+  }
+  __device__ static void get(const u32x4_t* p, float (&r)[8]) {
+    const u32x4_t a = p[0], b = p[1];
+    r[0] = __uint_as_float(a.x), r[1] = __uint_as_float(a.y), r[2] = __uint_as_float(a.z), r[3] = __uint_as_float(a.w);
+    r[4] = __uint_as_float(b.x), r[5] = __uint_as_float(b.y), r[6] = __uint_as_float(b.z), r[7] = __uint_as_float(b.w);
+  }
+};
+
+// LDS bytes of the FIRST variant: four per-wave copies of o_0 plus gamma0.
+static inline size_t first_lds_bytes(int d, bool f32) {
+  const size_t padded = (size_t)((((d >> 3) + 63) >> 6) * 64) * 8;  // channels, whole groups
+  return 4 * padded * (f32 ? 4 : 2) + padded * 4;
+}
+
+template <typename St, int N>
+__device__ __forceinline__ void p1_issue_tok(Chunk<St> (&s)[N], int64_t t, int g, int64_t T,
+                                             const St* __restrict__ src, int64_t stride, int d, int C, int lane) {
+  const int64_t tc = t < T ? t : T - 1;
+  const int c0 = g * 64 + lane;
+  const int c = c0 < C ? c0 : C - 1;
+#pragma unroll
+  for (int i = 0; i < N; ++i) s[i].load(src + (int64_t)i * stride + tc * d + c * 8);
+}
+
+template <typename St, int N, bool FIRST>
+__global__ __launch_bounds__(256) void k_p1_out_tokens(const St* __restrict__ src, int64_t stride, int64_t T,
+                                                       int d, const float* __restrict__ alpha, int S,
+                                                       St* __restrict__ out, const float* __restrict__ gamma0,
+                                                       float eps, St* __restrict__ x0, St* __restrict__ h0) {
+  extern __shared__ u32x4_t first_lds[];
+  const int C = d >> 3;
+  const int ngroups = (C + 63) >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  constexpr int kW = FirstSlot<St>::kWords;
+  u32x4_t* mine = first_lds + (size_t)wave * ngroups * 64 * kW;  // this wave's o_0
+  const float* gl = reinterpret_cast<const float*>(first_lds + (size_t)4 * ngroups * 64 * kW);
+  if (FIRST) {
+    float* g = reinterpret_cast<float*>(first_lds + (size_t)4 * ngroups * 64 * kW);
+    for (int k = threadIdx.x; k < ngroups * 512; k += 256) g[k] = k < d ? (gamma0 ? gamma0[k] : 1.f) : 0.f;
+    lds_barrier();
+  }
+  int64_t t = (int64_t)blockIdx.x * 4 + wave;  // current item (t, g)
+  int g = 0;
+  int64_t tn = t;  // next item
+  int gn = g;
+  auto advance = [&](int64_t& tt, int& gg) {
+    if (++gg == ngroups) {
+      gg = 0;
+      tt += nw;
+    }
+  };
+  advance(tn, gn);
+  float ss = 0.f;
+
+  auto emit = [&](const Chunk<St>(&s)[N], int64_t tok, int grp) {
+    const int c = grp * 64 + lane;
+    const bool ok = c < C;
+    float b[N][8];
+#pragma unroll
+    for (int i = 0; i < N; ++i) s[i].unpack(b[i]);
+    const float* al = alpha + tok * S * N;
+    int q = 0;
+    if (FIRST) {
+      float o[8];
+      zero8(o);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const float a = al[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(a, b[i][e], o[e]);
+      }
+      float r[8];
+      FirstSlot<St>::put(mine + (size_t)c * kW, o, r);
+      if (ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(r[e], r[e], ss);
+        if (h0) out8(h0 + tok * d + c * 8, o);
+      }
+      q = 1;
+      if (!out) q = S;  // one source: nothing else to write
+    }
+    for (; q < S; ++q) {
+      float o[8];
+      zero8(o);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const float a = al[q * N + i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(a, b[i][e], o[e]);
+      }
+      if (ok) out8_nt(out + ((int64_t)q * T + tok) * d + c * 8, o);
+    }
+    if (FIRST && grp == ngroups - 1) {
+      // the token's last group: PreNorm of o_0 from the wave's LDS copy
+      const float tot = wave_sum_dpp(ss);
+      ss = 0.f;
+      const float rinv = 1.0f / sqrtf(tot * (1.0f / (float)d) + eps);
+#pragma unroll 2
+      for (int gg = 0; gg < ngroups; ++gg) {
+        const int cc = gg * 64 + lane;
+        if (cc < C) {
+          float o[8], x[8];
+          FirstSlot<St>::get(mine + (size_t)cc * kW, o);
+          const float4 g0 = *reinterpret_cast<const float4*>(gl + cc * 8);
+          const float4 g1 = *reinterpret_cast<const float4*>(gl + cc * 8 + 4);
+          const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = gm[e] * (o[e] * rinv);
+          out8(x0 + tok * d + cc * 8, x);
+        }
+      }
+    }
+  };
+
+  Chunk<St> A[N], B[N];
+  p1_issue_tok<St, N>(A, t, g, T, src, stride, d, C, lane);
+  while (t < T) {
+    p1_issue_tok<St, N>(B, tn, gn, T, src, stride, d, C, lane);
+    emit(A, t, g);
+    t = tn, g = gn;
+    advance(tn, gn);
+    if (t >= T) break;
+    p1_issue_tok<St, N>(A, tn, gn, T, src, stride, d, C, lane);
+    emit(B, t, g);
+    t = tn, g = gn;
+    advance(tn, gn);
   }
 }
 
@@ -898,24 +1073,63 @@ static hipError_t set_lds(Kern k, size_t bytes) {
   return set_lds(k, bytes, bytes);
 }
 
+// Token order pays off when every wave of a one-workgroup-per-CU grid gets
+// whole tokens and the last round of tokens leaves at most an eighth idle.
+static bool token_order(int64_t T) {
+  const int64_t W = 4 * (int64_t)device_cu_count();
+  if (T < W) return false;
+  return ((T + W - 1) / W) * W * 8 <= T * 9;
+}
+
+constexpr size_t kMaxLds = 160 * 1024;
+
 template <typename St, int N>
 static hipError_t run_out(const void* src, int64_t stride, int64_t T, int d, const float* al, int S, void* out,
-                          hipStream_t stream) {
-  const int64_t items = T * (int64_t)(((d >> 3) + 63) >> 6);
-  const int64_t wgs = (items + 3) / 4;
-  const int64_t cap = (int64_t)device_cu_count() * 8;
-  hipLaunchKernelGGL((k_p1_out<St, N>), dim3((unsigned)(wgs < cap ? wgs : cap)), dim3(256), 0, stream,
-                     static_cast<const St*>(src), stride, T, d, al, S, static_cast<St*>(out));
-  return hipGetLastError();
+                          const float* gamma0, float eps, void* x0, void* h0, hipStream_t stream) {
+  const St* sp = static_cast<const St*>(src);
+  St* op = static_cast<St*>(out);
+  const bool tok = token_order(T);
+  const dim3 tgrid((unsigned)device_cu_count());
+  if (x0 && tok && first_lds_bytes(d, sizeof(St) == 4) <= kMaxLds) {
+    const size_t lds = first_lds_bytes(d, sizeof(St) == 4);
+    auto k = k_p1_out_tokens<St, N, true>;
+    hipError_t e = set_lds(k, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, tgrid, dim3(256), lds, stream, sp, stride, T, d, al, S, op, gamma0, eps,
+                       static_cast<St*>(x0), static_cast<St*>(h0));
+    return hipGetLastError();
+  }
+  // query 0 goes to h0 when the first sublayer's PreNorm follows in a second
+  // launch and h0 is wanted (else to slab 0 of out, used as scratch)
+  St* op0 = (x0 && h0) ? static_cast<St*>(h0) : op;
+  if (op) {
+    if (tok && !x0) {
+      hipLaunchKernelGGL((k_p1_out_tokens<St, N, false>), tgrid, dim3(256), 0, stream, sp, stride, T, d, al, S, op,
+                         nullptr, eps, nullptr, nullptr);
+    } else {
+      const int64_t items = T * (int64_t)(((d >> 3) + 63) >> 6);
+      const int64_t wgs = (items + 3) / 4;
+      const int64_t cap = (int64_t)device_cu_count() * 8;
+      hipLaunchKernelGGL((k_p1_out<St, N>), dim3((unsigned)(wgs < cap ? wgs : cap)), dim3(256), 0, stream, sp,
+                         stride, T, d, al, S, op, op0);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !x0) return e;
+  }
+  // the first sublayer's input: h = o_0 (one source: the source row itself)
+  const void* o0 = op ? static_cast<const void*>(op0) : src;
+  void* hh = (h0 && o0 != h0) ? h0 : nullptr;
+  return launch_merge(sizeof(St) == 4 ? kF32 : kBF16, T, d, o0, nullptr, kF32, nullptr, nullptr, nullptr, kF32,
+                      nullptr, nullptr, nullptr, gamma0, eps, hh, x0, stream);
 }
 
 template <typename St>
 static hipError_t pick_out(int n, const void* src, int64_t stride, int64_t T, int d, const float* al, int S,
-                           void* out, hipStream_t stream) {
+                           void* out, const float* gamma0, float eps, void* x0, void* h0, hipStream_t stream) {
   switch (n) {
 #define ATTNRES_CASE(N_) \
   case N_:               \
-    return run_out<St, N_>(src, stride, T, d, al, S, out, stream);
+    return run_out<St, N_>(src, stride, T, d, al, S, out, gamma0, eps, x0, h0, stream);
     ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4) ATTNRES_CASE(5) ATTNRES_CASE(6)
     ATTNRES_CASE(7) ATTNRES_CASE(8) ATTNRES_CASE(9) ATTNRES_CASE(10) ATTNRES_CASE(11) ATTNRES_CASE(12)
     ATTNRES_CASE(13) ATTNRES_CASE(14) ATTNRES_CASE(15) ATTNRES_CASE(16)
@@ -927,7 +1141,7 @@ static hipError_t pick_out(int n, const void* src, int64_t stride, int64_t T, in
 template <typename St, int MT>
 static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, int d, const float* w,
                             const float* kg, int S, float eps, void* out, float* m_out, float* lse_out,
-                            float* ws, hipStream_t stream) {
+                            const float* gamma0, void* x0, void* h0, float* ws, hipStream_t stream) {
   // workspace: packed queries first (room for 32 queries), then the softmax
   // weights
   const int nkb = ((d >> 3) + kKBlock - 1) / kKBlock;
@@ -970,19 +1184,24 @@ static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, i
                        al, m_out, lse_out);
   }
   e = hipGetLastError();
-  if (e != hipSuccess || out == nullptr) return e;  // statistics only
-  return pick_out<St>(n, src, stride, T, d, al, S, out, stream);
+  if (e != hipSuccess || (out == nullptr && x0 == nullptr)) return e;  // statistics only
+  return pick_out<St>(n, src, stride, T, d, al, S, out, gamma0, eps, x0, h0, stream);
 }
 
 hipError_t launch_phase1_multi(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
                                const float* w, const float* kg, int S, float eps, void* out,
-                               float* m_out, float* lse_out, float* ws, hipStream_t stream) {
+                               float* m_out, float* lse_out, const float* gamma0, void* x0, void* h0, float* ws,
+                               hipStream_t stream) {
   if (dt == kBF16) {
-    if (S <= 16) return run_multi<bf16_t, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, ws, stream);
-    return run_multi<bf16_t, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, ws, stream);
+    if (S <= 16)
+      return run_multi<bf16_t, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, gamma0, x0, h0, ws,
+                                  stream);
+    return run_multi<bf16_t, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, gamma0, x0, h0, ws,
+                                stream);
   }
-  if (S <= 16) return run_multi<float, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, ws, stream);
-  return run_multi<float, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, ws, stream);
+  if (S <= 16)
+    return run_multi<float, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, gamma0, x0, h0, ws, stream);
+  return run_multi<float, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, gamma0, x0, h0, ws, stream);
 }
 
 template <typename St>

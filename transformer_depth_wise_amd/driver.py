@@ -3,9 +3,11 @@
 The schedule follows the two-phase inference of "Attention Residuals" (notes,
 section 10) for every block of sublayers:
 
-    phase 1   attnres_phase1      sources b_0..b_{n-1}, all S queries of the block
-    phase 2   attnres_phase2_merge  x S, sequentially; sublayer j's output is
-              produced between two calls (here by a synthetic sublayer)
+    phase 1   attnres_phase1_first_prenorm  sources b_0..b_{n-1}, all S queries
+              of the block; the first sublayer's PreNorm output x comes out
+              of this pass (that sublayer has no partial-sum source)
+    phase 2   attnres_phase2_merge  x (S - 1), sequentially; sublayer j's output
+              is produced between two calls (here by a synthetic sublayer)
     block end attnres_block_accumulate  b_n = partial + v_S
     final     attnres_full        b_0..b_N with the final query (no PreNorm)
 
@@ -34,8 +36,8 @@ from typing import Callable, Dict, List, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import (attnres_block_accumulate, attnres_full, attnres_phase1, attnres_phase2_merge,
-                   attnres_phase2_merge_multi)
+from ._lib import (attnres_block_accumulate, attnres_full, attnres_phase1, attnres_phase1_first_prenorm,
+                   attnres_phase2_merge, attnres_phase2_merge_multi)
 
 SiteHook = Callable[..., None]
 Sublayer = Callable[[int, torch.Tensor], torch.Tensor]
@@ -58,11 +60,14 @@ class BlockAttnRes:
     ``n_given``: completed block sums supplied as inputs (a decode-shaped step
     starts at block n_given + 1).  ``x_ring``: number of PreNorm output
     buffers cycled through (a real model consumes x_l immediately).
+    ``fuse_first``: the first sublayer of a block takes its PreNorm output
+    from the phase-1 pass (False: a separate phase-2 launch computes it).
     """
 
     def __init__(self, T: int, d: int, block_sizes: Sequence[int], dtype: torch.dtype, n_given: int = 0,
                  eps: float = 1e-6, device=None, x_ring: int = 4, keep_h: bool = False,
-                 final_site: bool = True, partial: Optional[str] = None):
+                 final_site: bool = True, partial: Optional[str] = None, fuse_first: bool = True):
+        self.fuse_first = bool(fuse_first)
         self.T, self.d, self.dtype = int(T), int(d), dtype
         self.block_sizes = [int(s) for s in block_sizes]
         self.n_given, self.eps = int(n_given), float(eps)
@@ -126,11 +131,16 @@ class BlockAttnRes:
         out: List[Launch] = []
         n_done = 1 + self.n_given
         for S in self.block_sizes:
-            if n_done == 1:  # statistics only; phase 2 reads b_0 as its phase-1 output
+            if self.fuse_first:  # + x of the first sublayer (phase 1 writes it instead of o_0)
+                out.append(Launch("phase1", n_done * r + S * r + S * 2 * stat if n_done > 1 else
+                                  2 * r + S * 2 * stat))
+            elif n_done == 1:  # statistics only; phase 2 reads b_0 as its phase-1 output
                 out.append(Launch("phase1", r + S * 2 * stat))
             else:
                 out.append(Launch("phase1", n_done * r + S * (r + 2 * stat)))
             for j in range(S):
+                if j == 0 and self.fuse_first:
+                    continue
                 if j == 0:
                     b = 2 * r + stat                  # o; x
                 elif j == 1:
@@ -179,9 +189,15 @@ class BlockAttnRes:
             # phase 2 read b_0 itself
             single = n_done == 1
             mark("phase1", True)
-            attnres_phase1(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S], eps,
-                           None if single else self.o1[:S], self.m1[:S], self.lse1[:S], self.workspace,
-                           stream=stream)
+            if self.fuse_first:
+                attnres_phase1_first_prenorm(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S],
+                                             eps, None if single else self.o1[:S], self.m1[:S], self.lse1[:S],
+                                             None if gam is None else gam[l0], self.x[l0 % nx], self.h,
+                                             self.workspace, stream=stream)
+            else:
+                attnres_phase1(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S], eps,
+                               None if single else self.o1[:S], self.m1[:S], self.lse1[:S], self.workspace,
+                               stream=stream)
             mark("phase1", False)
             # the two latest outputs of the block stay alive (prev2, prev)
             prev2 = prev = None
@@ -199,11 +215,15 @@ class BlockAttnRes:
                     pin, v2, pout = self.partial, None, None    # p = p_{j-1} + v_{j-1}
                 else:
                     pin, v2, pout = self.partial, prev2, self.partial  # p_{j-2} + v_{j-2} + v_{j-1}
-                mark("phase2", True)
                 o = self.reps[0] if single else self.o1[j]
-                attnres_phase2_merge(o, self.lse1[j], pin, prev, pout, w[site], kg, pg, eps,
-                                     self.h, x, stream=stream, sublayer_prev2=v2)
-                mark("phase2", False)
+                if j == 0 and self.fuse_first:
+                    # x (and h = o_0) came out of phase 1; slab 0 of o1 is scratch
+                    o = self.reps[0] if single else self.h
+                else:
+                    mark("phase2", True)
+                    attnres_phase2_merge(o, self.lse1[j], pin, prev, pout, w[site], kg, pg, eps,
+                                         self.h, x, stream=stream, sublayer_prev2=v2)
+                    mark("phase2", False)
                 if hook is not None:
                     hook(site, x=x, h=self.h, o1=o, lse1=self.lse1[j], m1=self.m1[j])
                 prev2, prev = prev, sublayer(site, x)
@@ -278,8 +298,9 @@ class FullAttnRes:
             for g0 in range(0, self.L, self.group):
                 S = min(self.group, self.L - g0)
                 n = g0 + 1
-                out.append(Launch("phase1", (r if n == 1 else n * r + S * r) + 2 * S * stat))
-                for j in range(S):
+                # + x of the group's first sublayer, written by phase 1
+                out.append(Launch("phase1", (2 * r if n == 1 else n * r + S * r) + 2 * S * stat))
+                for j in range(1, S):
                     out.append(Launch("phase2", (2 + j) * r + stat))   # o, j group outputs; x
         if self.final_site:
             out.append(Launch("final", (self.L + 2) * r + stat))
@@ -308,19 +329,23 @@ class FullAttnRes:
                 n = g0 + 1
                 single = n == 1  # only the embedding: every phase-1 output is hist[0]
                 mark("phase1", True)
-                attnres_phase1(self.hist, n, w[g0:g0 + S], None if g is None else g[g0:g0 + S], self.eps,
-                               None if single else self.o1[:S], self.m1[:S], self.lse1[:S], self.workspace,
-                               stream=stream)
+                # the group's first sublayer has no in-group source: its
+                # PreNorm output comes out of the phase-1 pass
+                attnres_phase1_first_prenorm(self.hist, n, w[g0:g0 + S], None if g is None else g[g0:g0 + S],
+                                             self.eps, None if single else self.o1[:S], self.m1[:S],
+                                             self.lse1[:S], None if gam is None else gam[g0],
+                                             self.x[g0 % 2], self.h, self.workspace, stream=stream)
                 mark("phase1", False)
                 for j in range(S):
                     l = g0 + j
                     x = self.x[l % 2]
                     o = self.hist[0] if single else self.o1[j]
-                    mark("phase2", True)
-                    attnres_phase2_merge_multi(o, self.lse1[j], self.hist[g0 + 1:g0 + 1 + j] if j else None, j,
-                                               w[l], None if g is None else g[l], None if gam is None else gam[l],
-                                               self.eps, self.h, x, stream=stream)
-                    mark("phase2", False)
+                    if j:
+                        mark("phase2", True)
+                        attnres_phase2_merge_multi(o, self.lse1[j], self.hist[g0 + 1:g0 + 1 + j], j, w[l],
+                                                   None if g is None else g[l], None if gam is None else gam[l],
+                                                   self.eps, self.h, x, stream=stream)
+                        mark("phase2", False)
                     if hook is not None:
                         hook(l, x=x, h=self.h, lse=None)
                     sublayer(l, x)
