@@ -56,6 +56,8 @@ def _load():
         lib.oracle_full_forward.argtypes = [I, I, I, P, P, P, P, P, D, ctypes.c_int, P, P, P, P]
         lib.oracle_site_backward.argtypes = [I, I, P, P, P, P, ctypes.c_int, D, P, P, P, P, P]
         lib.oracle_site_backward_tokens.argtypes = [I, I, I, P, P, P, P, ctypes.c_int, D, P, P, P, P, P]
+        lib.oracle_block_backward.argtypes = [I, I, I, P, I, P, P, P, P, P, P, D, ctypes.c_int, P, P,
+                                              P, P, P, P, P]
         lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -222,3 +224,34 @@ def site_backward(src, w, g, gamma, eps: float, dx, prenorm: bool = True):
                                              _p(dgm) if prenorm else None)
     assert rc == 0, rc
     return {"du": du, "dw": dw, "dg": dg, "dgamma": dgm if prenorm else None}
+
+
+def block_backward(emb, v, w, g, gamma, blocks: Sequence[int], eps: float, dx, dhf=None, given=None,
+                   final_site: bool = True):
+    """Backward of block_forward with the sublayer outputs as inputs, for the
+    loss sum_l dx_l . x_l + dhf . hfinal over the token rows of ``emb``.
+
+    dx [L, n_tok, d]; dhf [n_tok, d] or None.  Returns fp64 arrays dv [L,
+    n_tok, d], demb [n_tok, d], dgiven [n_given, n_tok, d], dw, dg [L+1, d]
+    and dgamma [L, d] (parameter gradients summed over the tokens)."""
+    emb = _f32(emb)
+    n_tok, d = emb.shape
+    L = int(sum(blocks))
+    v = _f32(v) if L > 0 else None
+    dx = _f32(dx) if L > 0 else None
+    w, g, gamma = _f32(w), _f32(g), _f32(gamma)
+    given = _f32(given)
+    dhf = _f32(dhf)
+    n_given = 0 if given is None else given.shape[0]
+    bl = np.ascontiguousarray(np.asarray(blocks, dtype=np.int64))
+    dv = np.empty((L, n_tok, d))
+    dreps = np.empty((1 + n_given, n_tok, d))
+    dw = np.empty((L + 1, d))
+    dg = np.empty((L + 1, d))
+    dgamma = np.empty((max(L, 1), d))
+    rc = _load().oracle_block_backward(n_tok, d, len(blocks), _p(bl), n_given, _p(emb), _p(given), _p(v), _p(w),
+                                       _p(g), _p(gamma), eps, 1 if final_site else 0, _p(dx), _p(dhf), _p(dv),
+                                       _p(dreps), _p(dw), _p(dg), _p(dgamma))
+    if rc != 0:
+        raise RuntimeError("oracle_block_backward failed: %d" % rc)
+    return {"dv": dv, "demb": dreps[0], "dgiven": dreps[1:], "dw": dw, "dg": dg, "dgamma": dgamma[:L]}

@@ -369,3 +369,121 @@ int oracle_site_backward_tokens(int64_t n_tok, int64_t n, int64_t d, const float
     free(wd); free(gd); free(gmd);
     return bad ? -3 : 0;
 }
+
+int oracle_block_backward(int64_t n_tok, int64_t d, int64_t n_blocks, const int64_t* blocks,
+                          int64_t n_given, const float* emb, const float* given, const float* v,
+                          const float* w, const float* g, const float* gamma, double eps,
+                          int final_site, const float* dx, const float* dhf, double* dv_out,
+                          double* dreps_out, double* dw_out, double* dg_out, double* dgamma_out) {
+    if (n_tok < 0 || d <= 0 || n_blocks < 0 || n_given < 0 || !emb || !w || !dv_out || !dreps_out ||
+        !dw_out || !dg_out || !dgamma_out)
+        return -1;
+    if (n_given > 0 && !given) return -1;
+    int64_t L = 0;
+    for (int64_t b = 0; b < n_blocks; ++b) {
+        if (blocks[b] <= 0) return -1;
+        L += blocks[b];
+    }
+    if (L > 0 && (!v || !dx)) return -1;
+    const int64_t R = 1 + n_given + n_blocks;   /* b_0 .. b_N */
+    for (int64_t k = 0; k < (L + 1) * d; ++k) dw_out[k] = dg_out[k] = 0.0;
+    for (int64_t k = 0; k < L * d; ++k) dgamma_out[k] = 0.0;
+    int bad = 0;
+
+#pragma omp parallel
+    {
+        double* reps = (double*)malloc(sizeof(double) * (size_t)(R * d));
+        double* parts = (double*)malloc(sizeof(double) * (size_t)((L > 0 ? L : 1) * d));
+        double* db = (double*)calloc((size_t)(R * d), sizeof(double));
+        double* du = (double*)malloc(sizeof(double) * (size_t)((R + 1) * d));
+        double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+        double* wq = (double*)malloc(sizeof(double) * (size_t)(3 * d));
+        double* dxt = (double*)malloc(sizeof(double) * (size_t)d);
+        double* lw = (double*)calloc((size_t)((L + 1) * d), sizeof(double));
+        double* lg = (double*)calloc((size_t)((L + 1) * d), sizeof(double));
+        double* lgm = (double*)calloc((size_t)((L > 0 ? L : 1) * d), sizeof(double));
+        const double** srcs = (const double**)malloc(sizeof(double*) * (size_t)(R + 1));
+        double** dus = (double**)malloc(sizeof(double*) * (size_t)(R + 1));
+        if (!reps || !parts || !db || !du || !acc || !wq || !dxt || !lw || !lg || !lgm || !srcs || !dus) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            double* gk = wq + d;
+            double* gm = wq + 2 * d;
+            for (int64_t i = 0; i <= R; ++i) dus[i] = du + i * d;
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t t = 0; t < n_tok; ++t) {
+                /* forward: block sums and the partial-sum source of every site */
+                widen(d, emb + t * d, reps);
+                for (int64_t n = 0; n < n_given; ++n)
+                    widen(d, given + (n * n_tok + t) * d, reps + (1 + n) * d);
+                int64_t l = 0;
+                for (int64_t b = 0; b < n_blocks; ++b) {
+                    double* bs = reps + (1 + n_given + b) * d;
+                    for (int64_t k = 0; k < d; ++k) bs[k] = 0.0;
+                    for (int64_t j = 0; j < blocks[b]; ++j, ++l) {
+                        /* parts[l] = v_{l0} + ... + v_{l-1} (the partial source of site l) */
+                        memcpy(parts + l * d, bs, sizeof(double) * (size_t)d);
+                        const float* vl = v + (l * n_tok + t) * d;
+                        for (int64_t k = 0; k < d; ++k) bs[k] += (double)vl[k];
+                    }
+                }
+                for (int64_t k = 0; k < R * d; ++k) db[k] = 0.0;
+                /* the final site reads b_0 .. b_N, no PreNorm */
+                if (final_site && dhf) {
+                    for (int64_t i = 0; i < R; ++i) srcs[i] = reps + i * d;
+                    widen(d, w + L * d, wq);
+                    if (g) widen(d, g + L * d, gk);
+                    widen(d, dhf + t * d, dxt);
+                    if (oracle_site_backward(R, d, srcs, wq, g ? gk : NULL, NULL, 0, eps, dxt, dus,
+                                             lw + L * d, lg + L * d, NULL))
+                        bad = 1;
+                    for (int64_t i = 0; i < R; ++i)
+                        for (int64_t k = 0; k < d; ++k) db[i * d + k] += du[i * d + k];
+                }
+                /* blocks in reverse; inside a block, sites in reverse */
+                int64_t l_end = L;
+                for (int64_t b = n_blocks - 1; b >= 0; --b) {
+                    const int64_t S = blocks[b];
+                    const int64_t l0 = l_end - S;
+                    const int64_t n = 1 + n_given + b;   /* sources before block b */
+                    /* dL/dv of the block's last output is dL/db_n; each site j
+                     * adds dL/dp_j for the outputs before it */
+                    memcpy(acc, db + n * d, sizeof(double) * (size_t)d);
+                    for (int64_t j = S - 1; j >= 0; --j) {
+                        const int64_t ll = l0 + j;
+                        memcpy(dv_out + (ll * n_tok + t) * d, acc, sizeof(double) * (size_t)d);
+                        int64_t ns = 0;
+                        for (int64_t i = 0; i < n; ++i) srcs[ns++] = reps + i * d;
+                        if (j > 0) srcs[ns++] = parts + ll * d;
+                        widen(d, w + ll * d, wq);
+                        if (g) widen(d, g + ll * d, gk);
+                        if (gamma) widen(d, gamma + ll * d, gm);
+                        widen(d, dx + (ll * n_tok + t) * d, dxt);
+                        if (oracle_site_backward(ns, d, srcs, wq, g ? gk : NULL, gamma ? gm : NULL, 1, eps, dxt,
+                                                 dus, lw + ll * d, lg + ll * d, lgm + ll * d))
+                            bad = 1;
+                        for (int64_t i = 0; i < n; ++i)
+                            for (int64_t k = 0; k < d; ++k) db[i * d + k] += du[i * d + k];
+                        if (j > 0)
+                            for (int64_t k = 0; k < d; ++k) acc[k] += du[n * d + k];
+                    }
+                    l_end = l0;
+                }
+                for (int64_t i = 0; i < 1 + n_given; ++i)
+                    memcpy(dreps_out + (i * n_tok + t) * d, db + i * d, sizeof(double) * (size_t)d);
+            }
+#pragma omp critical
+            {
+                for (int64_t k = 0; k < (L + 1) * d; ++k) {
+                    dw_out[k] += lw[k];
+                    dg_out[k] += lg[k];
+                }
+                for (int64_t k = 0; k < L * d; ++k) dgamma_out[k] += lgm[k];
+            }
+        }
+        free(reps); free(parts); free(db); free(du); free(acc); free(wq); free(dxt);
+        free(lw); free(lg); free(lgm); free((void*)srcs); free(dus);
+    }
+    return bad ? -2 : 0;
+}

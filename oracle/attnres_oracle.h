@@ -132,6 +132,25 @@ int oracle_site_backward_tokens(int64_t n_tok, int64_t n, int64_t d, const float
                                 double eps, const float* dx, double* du, double* dw, double* dg,
                                 double* dgamma);
 
+/* Backward of the whole Block AttnRes forward of oracle_block_forward, with
+ * the sublayer outputs v_l treated as inputs: the loss is
+ *   L = sum_l sum_t dx_l[t] . x_l[t]  +  sum_t dhf[t] . hfinal[t]
+ * (the second term only with final_site and dhf != NULL).  Every site's
+ * backward is oracle_site_backward over that site's own sources; the chain
+ * rule through the sums of the block structure ("Attention Residuals" notes,
+ * section 8: b_n is the sum of block n's sublayer outputs and the partial
+ * sum of a block is the sum of its outputs so far) gives
+ *   dL/dv_l = dL/db_n + sum over later sites j of the same block of dL/dp_j,
+ * where b_n is l's block sum and p_j the partial-sum source of site j.
+ * Outputs (fp64): dv [L][n_tok][d]; dreps [1 + n_given][n_tok][d] (the
+ * embedding, then the given block sums); dw, dg [L+1][d] and dgamma [L][d],
+ * summed over the tokens (overwritten).  dx [L][n_tok][d], dhf [n_tok][d]. */
+int oracle_block_backward(int64_t n_tok, int64_t d, int64_t n_blocks, const int64_t* blocks,
+                          int64_t n_given, const float* emb, const float* given, const float* v,
+                          const float* w, const float* g, const float* gamma, double eps,
+                          int final_site, const float* dx, const float* dhf, double* dv_out,
+                          double* dreps_out, double* dw_out, double* dg_out, double* dgamma_out);
+
 /* Number of OpenMP threads the forward functions use (1 without OpenMP). */
 int oracle_threads(void);
 

@@ -47,9 +47,27 @@ BACKWARD_MUTATIONS = {
     "bwd_value_path_dropped": ("du[i][k] = alpha[i] * Gh[k] + t[k];", "du[i][k] = t[k];"),
     "bwd_key_gain_missing_in_dw": ("dw[k] += dz * gk * y;", "dw[k] += dz * y;"),
 }
+# mistakes in the backward through the block structure
+BLOCK_BACKWARD_MUTATIONS = {
+    "bbwd_partial_grad_dropped": ("for (int64_t k = 0; k < d; ++k) acc[k] += du[n * d + k];", ";"),
+    "bbwd_block_sum_grad_dropped": ("memcpy(acc, db + n * d, sizeof(double) * (size_t)d);",
+                                    "for (int64_t k = 0; k < d; ++k) acc[k] = 0.0;"),
+    "bbwd_final_site_missing": ("if (final_site && dhf) {", "if (0) {"),
+    "bbwd_partial_includes_own_output": (
+        "memcpy(parts + l * d, bs, sizeof(double) * (size_t)d);\n"
+        "                        const float* vl = v + (l * n_tok + t) * d;\n"
+        "                        for (int64_t k = 0; k < d; ++k) bs[k] += (double)vl[k];",
+        "const float* vl = v + (l * n_tok + t) * d;\n"
+        "                        for (int64_t k = 0; k < d; ++k) bs[k] += (double)vl[k];\n"
+        "                        memcpy(parts + l * d, bs, sizeof(double) * (size_t)d);"),
+    "bbwd_prenorm_skipped": ("if (oracle_site_backward(ns, d, srcs, wq, g ? gk : NULL, gamma ? gm : NULL, 1, eps, dxt,",
+                             "if (oracle_site_backward(ns, d, srcs, wq, g ? gk : NULL, gamma ? gm : NULL, 0, eps, dxt,"),
+}
 PINS = {name: "test_oracle_pins.py" for name in MUTATIONS}
 PINS.update({name: "test_oracle_backward.py" for name in BACKWARD_MUTATIONS})
+PINS.update({name: "test_oracle_block_backward.py" for name in BLOCK_BACKWARD_MUTATIONS})
 MUTATIONS.update(BACKWARD_MUTATIONS)
+MUTATIONS.update(BLOCK_BACKWARD_MUTATIONS)
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
