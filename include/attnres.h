@@ -251,6 +251,80 @@ attnres_status_t attnres_site_backward(attnres_dtype_t dt,
                                        void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * Backward through the block structure, in the two phases of the forward
+ * (training).  Site j of a block reads the block sources u_i (b_0..b_{n-1})
+ * and, after the block's first sublayer, the partial sum p_j ("Attention
+ * Residuals" notes, section 8).  With the site's phase-1 partition (o_j
+ * normalised, lse_j) and beta_j the softmax weight of p_j, the forward is
+ * h_j = o_j + beta_j (p_j - o_j) ("Attention Residuals 阅读补充",
+ * two-phase merge).  The sites of a block run in reverse order, each through
+ * attnres_phase2_backward (the sublayer output gradients are complete only
+ * once every later site has run); the block sources' gradients of all S
+ * sites then come from one attnres_phase1_backward.  The logit gradient is
+ * the notes' (section 7) and the RMSNorm Jacobian the reading notes'
+ * (gradients along the tangent).
+ *
+ * attnres_phase2_backward: one site.
+ *   p1_out [T][d] (dt), p1_lse [T]: the site's phase-1 partition, as
+ *   attnres_phase1 returned it.  partial_in, sublayer_prev2, sublayer_prev:
+ *   the partial source, composed exactly as attnres_phase2_merge composes it
+ *   (sublayer_prev == NULL: the block's first sublayer, no partial source;
+ *   p1_lse and dpartial may then be NULL).  w, key_gain, prenorm_gain: [d]
+ *   fp32 (gains NULL = ones).  dx = dL/dx [T][d] (dt); prenorm == 0 means
+ *   x = h.  Writes
+ *     g_out = G = dL/dh [T][d] (dt),  c_out = 1 - beta, gh_out = G.h [T] fp32
+ *   (G.h from G as stored), and ADDS
+ *     dpartial += dL/dp [T][d] fp32 (the partial source's gradient: the
+ *       running gradient of the block's earlier sublayer outputs),
+ *     dw += dL/dw, dkey_gain += dL/dkey_gain of the partial source's score
+ *       (NULL: not computed; untouched without a partial source),
+ *     dprenorm_gain += dL/dprenorm_gain (NULL or prenorm == 0: not computed),
+ *   the [d] sums over the tokens in a fixed order.  dpartial is read and
+ *   written in place; every other output must not overlap anything.
+ *   workspace: attnres_phase2_backward_workspace_bytes(T, d) bytes, 16-byte
+ *   aligned (per-team sums).
+ *
+ * attnres_phase1_backward: the block sources' part of S sites at once.
+ *   src, n_src, src_stride: the block sources as for attnres_phase1.
+ *   w, key_gain: [S][d] fp32 (key_gain NULL = ones).  g_in + j*g_stride:
+ *   G_j [T][d] (dt) of site j.  c_in, gh_in: [S][T] fp32 from the sites'
+ *   attnres_phase2_backward (both NULL: each site is its phase-1 partition
+ *   alone, c = 1 and G.h derived here, e.g. the final aggregation with
+ *   G = dL/dh_final).  Recomputes the scores and alpha1 of every site, and
+ *     dsrc + i*dsrc_stride  [T][d] fp32: dL/du_i of the S sites, written
+ *       (accumulate == 0) or added (accumulate != 0),
+ *     dw += dL/dw, dkey_gain += dL/dkey_gain ([S][d] fp32) of the block
+ *       sources' scores (dkey_gain NULL: not computed),
+ *   the [S][d] sums over the tokens in a fixed order.  Limits: 1 <= n_src <=
+ *   ATTNRES_MAX_SOURCES_MULTI, 1 <= S <= 32.  Outputs must not overlap any
+ *   input or each other.  workspace:
+ *   attnres_phase1_backward_workspace_bytes(T, d, n_src, S) bytes, 16-byte
+ *   aligned (per-token coefficients, w (.) key_gain, per-range sums).
+ */
+int64_t attnres_phase2_backward_workspace_bytes(int64_t T, int64_t d);
+attnres_status_t attnres_phase2_backward(attnres_dtype_t dt, int64_t T, int64_t d,
+                                         const void* p1_out, const float* p1_lse,
+                                         attnres_dtype_t partial_dt, const void* partial_in,
+                                         const void* sublayer_prev2, const void* sublayer_prev,
+                                         const float* w, const float* key_gain,
+                                         const float* prenorm_gain, int prenorm, float eps,
+                                         const void* dx, float* dpartial,
+                                         void* g_out, float* c_out, float* gh_out,
+                                         float* dw, float* dkey_gain, float* dprenorm_gain,
+                                         void* workspace, int64_t workspace_bytes, void* stream);
+
+int64_t attnres_phase1_backward_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int64_t S);
+attnres_status_t attnres_phase1_backward(attnres_dtype_t dt,
+                                         const void* src, int64_t n_src, int64_t src_stride,
+                                         int64_t T, int64_t d,
+                                         const float* w, const float* key_gain, int64_t S, float eps,
+                                         const void* g_in, int64_t g_stride,
+                                         const float* c_in, const float* gh_in,
+                                         float* dsrc, int64_t dsrc_stride, int accumulate,
+                                         float* dw, float* dkey_gain,
+                                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * Block completion ("Attention Residuals" notes, section 8: b_n is the sum of
  * the block's sublayer outputs):
  *     out = ((partial_in or 0) + (v2 or 0)) + v      (fp32, in that order)

@@ -148,3 +148,57 @@ def run_full_parity(w: synth.Workload, samples: Optional[Sequence[int]] = None, 
     for k, e in worst.items():
         assert e <= tol, "%s: %s max-abs-rel %.3e exceeds %.1e" % (w.name, k, e, tol)
     return worst
+
+
+def run_block_backward_parity(w: synth.Workload, samples: Optional[Sequence[int]] = None, device="cuda",
+                              params_too: bool = True, dx_from_outputs: bool = False,
+                              tol: Optional[float] = None) -> Dict[str, float]:
+    """Block AttnRes training forward + backward on the GPU vs the oracle's
+    backward on sampled tokens: dL/dv_l of every site, dL/db_0 and the given
+    block sums; with ``params_too`` (all tokens sampled) also dw, dg, dgamma.
+    Upstream gradients dx_l, dh_final are seeded N(0,1) rows (or, with
+    ``dx_from_outputs``, the sublayer outputs themselves, to save memory)."""
+    dev = torch.device(device)
+    emb, given, v = block_inputs(w, dev)
+    prm = synth.params(w, dev)
+    st = BlockAttnRes(w.T, w.d, w.block_sizes, w.torch_dtype, n_given=w.n_given, eps=w.eps, device=dev,
+                      final_site=w.final_site, training=True)
+    st.reps[0].copy_(emb)
+    for n, b in enumerate(given):
+        st.reps[1 + n].copy_(b)
+    st.forward(prm, lambda l, x: v[l])
+    gen = torch.Generator(device=dev).manual_seed(7000 + w.T + w.d)
+    if dx_from_outputs:
+        dx = [v[(l + 1) % w.L] for l in range(w.L)]
+        dhf = v[0]
+    else:
+        dx = [torch.randn((w.T, w.d), generator=gen, device=dev).to(w.torch_dtype) for _ in range(w.L)]
+        dhf = torch.randn((w.T, w.d), generator=gen, device=dev).to(w.torch_dtype)
+    samples = list(range(w.T)) if samples is None else list(samples)
+    idx = torch.tensor(samples, dtype=torch.long, device=dev)
+    dv_rows = [None] * w.L
+
+    def dx_for(l, dv):
+        dv_rows[l] = dv.index_select(0, idx).clone()
+        return dx[l]
+
+    out = st.backward(prm, dx_for, dh_final=dhf if w.final_site else None)
+    torch.cuda.synchronize()
+    sel = lambda t: t.index_select(0, idx)  # noqa: E731
+    ref = oracle.block_backward(
+        sel(emb), torch.stack([sel(t) for t in v]), prm["w"], prm["g"], prm["gamma"], w.block_sizes, w.eps,
+        torch.stack([sel(t) for t in dx]), sel(dhf) if w.final_site else None,
+        given=torch.stack([sel(t) for t in given]) if given else None, final_site=w.final_site)
+    bar = TOL[w.dtype] if tol is None else tol
+    worst = {"dv": float(row_rel_err(_host(torch.stack(dv_rows)), ref["dv"]).max()),
+             "demb": float(row_rel_err(_host(sel(out["demb"])), ref["demb"]).max())}
+    if w.n_given:
+        worst["dgiven"] = float(row_rel_err(_host(out["dgiven"].index_select(1, idx)), ref["dgiven"]).max())
+    if params_too:
+        assert len(samples) == w.T, "parameter gradients are sums over every token"
+        worst["dw"] = float(row_rel_err(_host(out["dw"]), ref["dw"]).max())
+        worst["dg"] = float(row_rel_err(_host(out["dg"]), ref["dg"]).max())
+        worst["dgamma"] = float(row_rel_err(_host(out["dgamma"]), ref["dgamma"]).max())
+    for k, e in worst.items():
+        assert e <= bar, "%s: %s max-abs-rel %.3e exceeds %.1e" % (w.name, k, e, bar)
+    return worst

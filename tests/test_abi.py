@@ -28,6 +28,7 @@ def declared_functions():
 def test_header_declares_every_entry_point():
     names = declared_functions()
     for n in ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_workspace_bytes", "attnres_phase2_merge",
+              "attnres_phase2_backward", "attnres_phase1_backward",
               "attnres_phase2_merge_multi", "attnres_full", "attnres_block_accumulate", "attnres_status_string"):
         assert n in names
 
@@ -127,6 +128,75 @@ def test_phase1_first_prenorm_validation(lib):
     assert first_prenorm(lib, dt=9) == EDTYPE
     assert first_prenorm(lib, T=0) == 0
     assert first_prenorm(lib, T=0, x=None) == EINVAL
+
+
+def p2b(lib, dt=1, T=1024, d=64, o=A, lse=2 * A, pdt=0, pin=None, v2=None, v=3 * A, w=4 * A, kg=None, gm=None,
+        prenorm=1, dx=5 * A, dp=6 * A, g=7 * A, c=8 * A, gh=9 * A, dw=10 * A, dk=None, dgm=None, ws=11 * A,
+        ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attnres_phase2_backward_workspace_bytes(T, d)
+    return checked(lib.attnres_phase2_backward(dt, T, d, p(o), p(lse), pdt, p(pin), p(v2), p(v), p(w), p(kg), p(gm),
+                                               prenorm, 1e-6, p(dx), p(dp), p(g), p(c), p(gh), p(dw), p(dk), p(dgm),
+                                               p(ws), ws_bytes, None))
+
+
+def test_phase2_backward_validation(lib):
+    assert p2b(lib, dt=5) == EDTYPE
+    assert p2b(lib, pin=12 * A, pdt=9) == EDTYPE
+    assert p2b(lib, d=12) == EALIGN
+    assert p2b(lib, v=None, pin=12 * A) == EINVAL          # a partial input needs the previous output
+    assert p2b(lib, v=None, v2=12 * A) == EINVAL
+    assert p2b(lib, g=None) == EINVAL
+    assert p2b(lib, dp=None) == EINVAL                     # a partial source needs its gradient buffer
+    assert p2b(lib, lse=None) == EINVAL
+    assert p2b(lib, ws=None) == EINVAL
+    assert p2b(lib, ws_bytes=8) == EINVAL
+    assert p2b(lib, g=A + 64) == EALIAS                    # G over the phase-1 output
+    assert p2b(lib, dp=5 * A + 16) == EALIAS               # the partial gradient over dx
+    assert p2b(lib, c=9 * A) == EALIAS                     # the two per-token outputs overlap
+    assert p2b(lib, dw=11 * A) == EALIAS                   # dw inside the workspace
+    assert p2b(lib, g=7 * A + 8) == EALIGN
+    assert p2b(lib, c=8 * A + 2) == EALIGN
+    assert p2b(lib, T=0) == 0
+    assert p2b(lib, T=0, v=None, pin=12 * A) == EINVAL
+    assert lib.attnres_phase2_backward_workspace_bytes(0, 64) == 0
+    assert lib.attnres_phase2_backward_workspace_bytes(10, 12) == -1
+
+
+def p1b(lib, dt=1, src=A, n=3, stride=1024 * 64, T=1024, d=64, w=8 * A, kg=None, S=4, g=16 * A, gstride=1024 * 64,
+        c=None, gh=None, ds=24 * A, dstride=1024 * 64, dw=32 * A, dk=None, ws=40 * A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attnres_phase1_backward_workspace_bytes(T, d, n, S)
+    return checked(lib.attnres_phase1_backward(dt, p(src), n, stride, T, d, p(w), p(kg), S, 1e-6, p(g), gstride, p(c),
+                                               p(gh), p(ds), dstride, 1, p(dw), p(dk), p(ws), ws_bytes, None))
+
+
+def test_phase1_backward_validation(lib):
+    assert p1b(lib, dt=3) == EDTYPE
+    assert p1b(lib, d=12) == EALIGN
+    assert p1b(lib, n=0) == EINVAL
+    assert p1b(lib, n=17) == EINVAL
+    assert p1b(lib, S=33) == EINVAL
+    assert p1b(lib, c=48 * A) == EINVAL                    # c without G.h: G.h cannot be derived
+    assert p1b(lib, g=None) == EINVAL
+    assert p1b(lib, ds=None) == EINVAL
+    assert p1b(lib, dw=None) == EINVAL
+    assert p1b(lib, stride=100) == EINVAL
+    assert p1b(lib, gstride=100) == EINVAL
+    assert p1b(lib, dstride=100) == EINVAL
+    assert p1b(lib, gstride=1024 * 64 + 4) == EALIGN
+    assert p1b(lib, ws=None) == EINVAL
+    assert p1b(lib, ws_bytes=64) == EINVAL
+    assert p1b(lib, ds=A + 64) == EALIAS                   # gradients over the sources
+    assert p1b(lib, dw=16 * A + 64) == EALIAS              # dw over G
+    assert p1b(lib, dk=32 * A + 64, kg=48 * A) == EALIAS   # the two weight gradients overlap
+    assert p1b(lib, ws=24 * A + 64) == EALIAS
+    assert p1b(lib, T=0) == 0
+    # coefficients T x S x n, folded queries S x d, per-range sums (1024 waves over d / 512 groups)
+    assert lib.attnres_phase1_backward_workspace_bytes(1024, 64, 3, 4) == 4 * (1024 * 4 * 3 + 4 * 64 + 1024 * 4 * 64)
+    assert lib.attnres_phase1_backward_workspace_bytes(16384, 7168, 8, 24) == \
+        4 * (16384 * 24 * 8 + 24 * 7168 + 74 * 24 * 7168)
+    assert lib.attnres_phase1_backward_workspace_bytes(10, 64, 3, 33) == -1
 
 
 def merge(lib, dt=1, T=1024, d=64, o=A, lse=2 * A, pdt=0, pin=None, v2=None, v=None, podt=0, pout=None, w=3 * A,

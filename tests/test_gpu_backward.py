@@ -1,0 +1,55 @@
+"""GPU parity of the backward through the block structure (phase-2 backward
+per site, phase-1 backward per block) against the oracle's fp64 backward,
+itself pinned to finite differences (needs an MI355X)."""
+import sys
+
+import pytest
+import torch
+
+import synth
+from harness import run_block_backward_parity
+import transformer_depth_wise_amd as tdw
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    tdw.load()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+BWD_CASES = [
+    # (T, d, blocks, n_given, dtype, final_site)
+    (64, 256, (4, 4), 0, "f32", True),        # the tiny fp32 workload's shape
+    (5, 8, (1, 2, 3), 0, "f32", True),        # smallest rows, a block of one sublayer
+    (33, 64, (2, 3), 1, "f32", False),        # no final site
+    (200, 1032, (3, 5, 2), 1, "bf16", True),  # ragged chunk groups
+    (96, 2048, (6,), 3, "bf16", True),
+    (40, 7168, (5, 4), 2, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("T,d,blocks,n_given,dt,final_site", BWD_CASES)
+def test_block_backward_matches_oracle(T, d, blocks, n_given, dt, final_site):
+    base = synth.WORKLOADS["tiny_block_f32"]
+    w = synth.scaled(base, name="bwd", T=T, d=d, block_sizes=tuple(blocks), n_given=n_given, dtype=dt,
+                     unit_gains=False, seed=6100 + T + d, final_site=final_site)
+    _say("case block backward T=%d d=%d blocks=%s given=%d %s final=%s" % (T, d, blocks, n_given, dt, final_site))
+    worst = run_block_backward_parity(w)
+    _say("worst", worst)
+
+
+def test_block_backward_decode_shape():
+    w = synth.WORKLOADS["decode_block_bf16"]
+    _say("case block backward decode_block_bf16 T=%d d=%d S=24 given=%d" % (w.T, w.d, w.n_given))
+    worst = run_block_backward_parity(w, samples=synth.sample_tokens(w.T, 24), params_too=False)
+    _say("worst", worst)

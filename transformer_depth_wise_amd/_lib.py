@@ -24,7 +24,8 @@ ATTNRES_MAX_GROUP_SOURCES = 16
 
 EXPORTED = ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_workspace_bytes", "attnres_phase2_merge", "attnres_phase2_merge_multi",
             "attnres_full", "attnres_block_accumulate", "attnres_site_backward", "attnres_site_backward_workspace_bytes",
-            "attnres_status_string")
+            "attnres_phase2_backward", "attnres_phase2_backward_workspace_bytes", "attnres_phase1_backward",
+            "attnres_phase1_backward_workspace_bytes", "attnres_status_string")
 
 
 class AttnResError(RuntimeError):
@@ -58,8 +59,16 @@ def load(path: Optional[str] = None):
     lib.attnres_site_backward_workspace_bytes.argtypes = [I, I]
     lib.attnres_site_backward_workspace_bytes.restype = ctypes.c_int64
     lib.attnres_block_accumulate.argtypes = [E, I, I, E, V, V, V, V, V]
+    lib.attnres_phase2_backward.argtypes = [E, I, I, V, V, E, V, V, V, V, V, V, E, F, V, V, V, V, V, V, V, V, V, I,
+                                            V]
+    lib.attnres_phase2_backward_workspace_bytes.argtypes = [I, I]
+    lib.attnres_phase2_backward_workspace_bytes.restype = ctypes.c_int64
+    lib.attnres_phase1_backward.argtypes = [E, V, I, I, I, I, V, V, I, F, V, I, V, V, V, I, E, V, V, V, I, V]
+    lib.attnres_phase1_backward_workspace_bytes.argtypes = [I, I, I, I]
+    lib.attnres_phase1_backward_workspace_bytes.restype = ctypes.c_int64
     for fn in ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase2_merge", "attnres_phase2_merge_multi", "attnres_full",
-               "attnres_block_accumulate", "attnres_site_backward"):
+               "attnres_block_accumulate", "attnres_site_backward", "attnres_phase2_backward",
+               "attnres_phase1_backward"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.attnres_status_string.argtypes = [ctypes.c_int]
     lib.attnres_status_string.restype = ctypes.c_char_p
@@ -210,6 +219,58 @@ def attnres_site_backward(src: torch.Tensor, n_src: int, w: torch.Tensor, key_ga
                                       _ptr(dw), _ptr(dkey_gain), _ptr(dprenorm_gain), _ptr(workspace), ws_bytes,
                                       _stream(stream))
     _check("attnres_site_backward", rc)
+
+
+def attnres_phase2_backward_workspace_bytes(T: int, d: int) -> int:
+    return int(load().attnres_phase2_backward_workspace_bytes(T, d))
+
+
+def attnres_phase2_backward(p1_out: torch.Tensor, p1_lse: Optional[torch.Tensor], partial_in: Optional[torch.Tensor],
+                            sublayer_prev: Optional[torch.Tensor], w: torch.Tensor, key_gain: Optional[torch.Tensor],
+                            prenorm_gain: Optional[torch.Tensor], eps: float, dx: torch.Tensor,
+                            dpartial: Optional[torch.Tensor], g_out: torch.Tensor, c_out: torch.Tensor,
+                            gh_out: torch.Tensor, dw: Optional[torch.Tensor], dkey_gain: Optional[torch.Tensor],
+                            dprenorm_gain: Optional[torch.Tensor], workspace: torch.Tensor, prenorm: bool = True,
+                            sublayer_prev2: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One site's phase-2 backward: p1_out, dx, g_out: [T, d]; p1_lse, c_out,
+    gh_out: [T]; the partial source as for attnres_phase2_merge; dpartial:
+    [T, d] fp32, added to in place; dw, dkey_gain, dprenorm_gain: [d] fp32,
+    added to."""
+    T, d = p1_out.shape
+    pdt = dtype_code(partial_in.dtype) if partial_in is not None else F32
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = load().attnres_phase2_backward(dtype_code(p1_out.dtype), T, d, _ptr(p1_out), _ptr(p1_lse), pdt,
+                                        _ptr(partial_in), _ptr(sublayer_prev2), _ptr(sublayer_prev), _ptr(w),
+                                        _ptr(key_gain), _ptr(prenorm_gain), 1 if prenorm else 0, eps, _ptr(dx),
+                                        _ptr(dpartial), _ptr(g_out), _ptr(c_out), _ptr(gh_out), _ptr(dw),
+                                        _ptr(dkey_gain), _ptr(dprenorm_gain), _ptr(workspace), ws_bytes,
+                                        _stream(stream))
+    _check("attnres_phase2_backward", rc)
+
+
+def attnres_phase1_backward_workspace_bytes(T: int, d: int, n_src: int, S: int) -> int:
+    return int(load().attnres_phase1_backward_workspace_bytes(T, d, n_src, S))
+
+
+def attnres_phase1_backward(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],
+                            eps: float, g_in: torch.Tensor, c_in: Optional[torch.Tensor],
+                            gh_in: Optional[torch.Tensor], dsrc: torch.Tensor, dw: torch.Tensor,
+                            dkey_gain: Optional[torch.Tensor], workspace: torch.Tensor, accumulate: bool = False,
+                            stream=None) -> None:
+    """The block sources' part of S sites: src: [>=n_src, T, d]; w, key_gain,
+    dw, dkey_gain: [S, d] fp32; g_in: [S, T, d]; c_in, gh_in: [S, T] or None;
+    dsrc: [>=n_src, T, d] fp32, written or (accumulate) added to."""
+    S, d = w.shape
+    T = g_in.shape[-2]
+    stride = src.stride(0) if src.dim() == 3 else T * d
+    gstride = g_in.stride(0) if g_in.dim() == 3 else T * d
+    dstride = dsrc.stride(0) if dsrc.dim() == 3 else T * d
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = load().attnres_phase1_backward(dtype_code(src.dtype), _ptr(src), n_src, stride, T, d, _ptr(w), _ptr(key_gain),
+                                        S, eps, _ptr(g_in), gstride, _ptr(c_in), _ptr(gh_in), _ptr(dsrc), dstride,
+                                        1 if accumulate else 0, _ptr(dw), _ptr(dkey_gain), _ptr(workspace), ws_bytes,
+                                        _stream(stream))
+    _check("attnres_phase1_backward", rc)
 
 
 def attnres_block_accumulate(partial_in: Optional[torch.Tensor], v: torch.Tensor, out: torch.Tensor,

@@ -41,6 +41,27 @@ hipError_t launch_site_backward(Dtype dt, int64_t T, int d, const void* src, int
                                 hipStream_t stream);
 int64_t backward_slots(int64_t T, int d);
 
+// Backward through the block structure (training).  Phase-2 backward of one
+// site: G = dL/dh to g_out, c = 1 - beta and G.h per token, the partial
+// source's gradient added into dpart (fp32), and the site's partial-source
+// and PreNorm parameter gradients added into dw, dkg, dgamma (part: per-team
+// sums, p2_backward_slots(T, d) x 2 x d floats).
+hipError_t launch_p2_backward(Dtype dt, int64_t T, int d, const void* o1, const float* lse1, Dtype pdt,
+                              const void* pin, const void* vprev2, const void* vprev, const float* w, const float* kg,
+                              const float* gamma, int prenorm, float eps, const void* dx, float* dpart, void* g_out,
+                              float* c_out, float* gh_out, float* dw, float* dkg, float* dgamma, float* part,
+                              hipStream_t stream);
+int64_t p2_backward_slots(int64_t T, int d);
+
+// Phase-1 backward of a block: the block sources' gradients written or added
+// (accumulate) into dsrc (fp32), the block-source part of dw, dkg added.
+// ws: T * S * n coefficients + p1_backward_ranges(d) * S * d partial sums.
+hipError_t launch_p1_backward(Dtype dt, int64_t T, int d, const void* src, int n, int64_t stride, int S,
+                              const float* w, const float* kg, float eps, const void* gin, int64_t gstride,
+                              const float* c_in, const float* gh_in, float* dsrc, int64_t dstride, int accumulate,
+                              float* dw, float* dkg, float* ws, hipStream_t stream);
+int64_t p1_backward_ranges(int d);
+
 hipError_t launch_accumulate(Dtype dt, int64_t T, int d, Dtype pdt, const void* pin, const void* v2,
                              const void* v, void* out, hipStream_t stream);
 

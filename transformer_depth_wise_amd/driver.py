@@ -36,8 +36,9 @@ from typing import Callable, Dict, List, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import (attnres_block_accumulate, attnres_full, attnres_phase1, attnres_phase1_first_prenorm,
-                   attnres_phase2_merge, attnres_phase2_merge_multi)
+from ._lib import (attnres_block_accumulate, attnres_full, attnres_phase1, attnres_phase1_backward,
+                   attnres_phase1_first_prenorm, attnres_phase2_backward, attnres_phase2_merge,
+                   attnres_phase2_merge_multi)
 
 SiteHook = Callable[..., None]
 Sublayer = Callable[[int, torch.Tensor], torch.Tensor]
@@ -62,12 +63,18 @@ class BlockAttnRes:
     buffers cycled through (a real model consumes x_l immediately).
     ``fuse_first``: the first sublayer of a block takes its PreNorm output
     from the phase-1 pass (False: a separate phase-2 launch computes it).
+    ``training``: keep what ``backward`` needs -- every site's phase-1
+    output and statistics, and every stored partial sum (each in its own
+    buffer instead of in place); the first sublayer is then merged by a
+    phase-2 launch so that its phase-1 output is stored too.
     """
 
     def __init__(self, T: int, d: int, block_sizes: Sequence[int], dtype: torch.dtype, n_given: int = 0,
                  eps: float = 1e-6, device=None, x_ring: int = 4, keep_h: bool = False,
-                 final_site: bool = True, partial: Optional[str] = None, fuse_first: bool = True):
-        self.fuse_first = bool(fuse_first)
+                 final_site: bool = True, partial: Optional[str] = None, fuse_first: bool = True,
+                 training: bool = False):
+        self.training = bool(training)
+        self.fuse_first = bool(fuse_first) and not self.training
         self.T, self.d, self.dtype = int(T), int(d), dtype
         self.block_sizes = [int(s) for s in block_sizes]
         self.n_given, self.eps = int(n_given), float(eps)
@@ -100,10 +107,22 @@ class BlockAttnRes:
             self.partial = torch.empty((T, d), dtype=torch.float32, device=dev)
         else:
             raise ValueError("partial format must be 'p24' or 'f32'")
+        if self.training:
+            # per block: phase-1 outputs and statistics of every site, and the
+            # partial sums stored at positions j = 2, 4, ..., S - 1 (slot j // 2 - 1)
+            self.o_blocks = [torch.empty((S, T, d), dtype=dtype, device=dev) for S in self.block_sizes]
+            self.lse_blocks = [torch.empty((S, T), dtype=torch.float32, device=dev) for S in self.block_sizes]
+            self.p_slots = [[self._new_partial() for _ in range(max(0, (S - 1) // 2))] for S in self.block_sizes]
+            self.recipes: List[Optional[tuple]] = [None] * self.L
         self.x = torch.empty((max(1, x_ring), T, d), dtype=dtype, device=dev)
         self.h = torch.empty((T, d), dtype=dtype, device=dev) if keep_h else None
         self.h_final = torch.empty((T, d), dtype=dtype, device=dev)
         self.lse_final = torch.empty((T,), dtype=torch.float32, device=dev)
+
+    def _new_partial(self) -> torch.Tensor:
+        if self.partial_format == "p24":
+            return _lib.p24_partial(self.T, self.d, self.device)
+        return torch.empty((self.T, self.d), dtype=torch.float32, device=self.device)
 
     # ------------------------------------------------------------------ bytes
     def buffer_bytes(self) -> Dict[str, int]:
@@ -183,11 +202,14 @@ class BlockAttnRes:
         mark = instrument if instrument is not None else (lambda kind, begin: None)
         l0 = 0
         nx = self.x.shape[0]
-        for S in self.block_sizes:
+        for b, S in enumerate(self.block_sizes):
             # with a single completed source (the embedding) every phase-1
             # output is that source: compute the statistics only and let
             # phase 2 read b_0 itself
             single = n_done == 1
+            o1 = self.o_blocks[b] if self.training else self.o1[:S]
+            lse1 = self.lse_blocks[b] if self.training else self.lse1[:S]
+            slots = self.p_slots[b] if self.training else None
             mark("phase1", True)
             if self.fuse_first:
                 attnres_phase1_first_prenorm(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S],
@@ -196,8 +218,8 @@ class BlockAttnRes:
                                              self.workspace, stream=stream)
             else:
                 attnres_phase1(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S], eps,
-                               None if single else self.o1[:S], self.m1[:S], self.lse1[:S], self.workspace,
-                               stream=stream)
+                               o1 if (self.training or not single) else None, self.m1[:S], lse1,
+                               self.workspace, stream=stream)
             mark("phase1", False)
             # the two latest outputs of the block stay alive (prev2, prev)
             prev2 = prev = None
@@ -207,35 +229,44 @@ class BlockAttnRes:
                 kg = None if g is None else g[site]
                 pg = None if gam is None else gam[site]
                 # the partial p_j = v_0 + ... + v_{j-1} is stored at even j >= 2
+                # (training: each in its own slot, j // 2 - 1)
+                if slots is None:
+                    p_prev = p_new = self.partial
+                else:
+                    p_prev = slots[(j - 1) // 2 - 1] if j >= 3 else None
+                    p_new = slots[j // 2 - 1] if j >= 2 and j % 2 == 0 else None
                 if j <= 1:
                     pin, v2, pout = None, None, None            # p = v_0 (j = 1) or none
                 elif j == 2:
-                    pin, v2, pout = None, prev2, self.partial   # p = v_0 + v_1, stored
+                    pin, v2, pout = None, prev2, p_new          # p = v_0 + v_1, stored
                 elif j % 2:
-                    pin, v2, pout = self.partial, None, None    # p = p_{j-1} + v_{j-1}
+                    pin, v2, pout = p_prev, None, None          # p = p_{j-1} + v_{j-1}
                 else:
-                    pin, v2, pout = self.partial, prev2, self.partial  # p_{j-2} + v_{j-2} + v_{j-1}
-                o = self.reps[0] if single else self.o1[j]
+                    pin, v2, pout = p_prev, prev2, p_new        # p_{j-2} + v_{j-2} + v_{j-1}
+                if self.training:
+                    self.recipes[site] = (pin, v2, prev)
+                o = self.reps[0] if (single and not self.training) else o1[j]
                 if j == 0 and self.fuse_first:
                     # x (and h = o_0) came out of phase 1; slab 0 of o1 is scratch
                     o = self.reps[0] if single else self.h
                 else:
                     mark("phase2", True)
-                    attnres_phase2_merge(o, self.lse1[j], pin, prev, pout, w[site], kg, pg, eps,
+                    attnres_phase2_merge(o, lse1[j], pin, prev, pout, w[site], kg, pg, eps,
                                          self.h, x, stream=stream, sublayer_prev2=v2)
                     mark("phase2", False)
                 if hook is not None:
-                    hook(site, x=x, h=self.h, o1=o, lse1=self.lse1[j], m1=self.m1[j])
+                    hook(site, x=x, h=self.h, o1=o, lse1=lse1[j], m1=self.m1[j])
                 prev2, prev = prev, sublayer(site, x)
             mark("accumulate", True)
+            p_last = self.partial if slots is None else (slots[-1] if slots else None)
             if S == 1:
                 attnres_block_accumulate(None, prev, self.reps[n_done], stream=stream)
             elif S == 2:
                 attnres_block_accumulate(None, prev, self.reps[n_done], stream=stream, v2=prev2)
             elif S % 2:
-                attnres_block_accumulate(self.partial, prev, self.reps[n_done], stream=stream)
+                attnres_block_accumulate(p_last, prev, self.reps[n_done], stream=stream)
             else:
-                attnres_block_accumulate(self.partial, prev, self.reps[n_done], stream=stream, v2=prev2)
+                attnres_block_accumulate(p_last, prev, self.reps[n_done], stream=stream, v2=prev2)
             mark("accumulate", False)
             n_done += 1
             l0 += S
@@ -246,6 +277,73 @@ class BlockAttnRes:
                            stream=stream)
             mark("final", False)
         return self.h_final
+
+    # --------------------------------------------------------------- backward
+    def backward(self, params: Dict[str, torch.Tensor], dx_for: Callable[[int, torch.Tensor], torch.Tensor],
+                 dh_final: Optional[torch.Tensor] = None, stream=None,
+                 instrument: Optional[Callable[[str, bool], None]] = None) -> Dict[str, torch.Tensor]:
+        """Backward of the last ``forward`` (built with ``training=True``),
+        sites in reverse order.  ``dx_for(l, dv_l)`` is the sublayer's backward:
+        it receives dL/dv_l (fp32 [T, d], valid only during the call) and
+        returns dL/dx_l ([T, d], storage dtype).  ``dh_final``: dL/dh_final
+        (needed with the final site).  Returns fp32 ``demb`` [T, d],
+        ``dgiven`` [n_given, T, d], ``dw``, ``dg`` [L+1, d], ``dgamma`` [L, d]."""
+        if not self.training:
+            raise RuntimeError("backward needs a forward built with training=True")
+        if self.final_site and dh_final is None:
+            raise ValueError("dh_final is required with the final aggregation site")
+        w, g, gam = params["w"], params.get("g"), params.get("gamma")
+        T, d, eps, dev = self.T, self.d, self.eps, self.device
+        mark = instrument if instrument is not None else (lambda kind, begin: None)
+        n_reps = self.reps.shape[0]
+        smax = max(self.block_sizes) if self.block_sizes else 1
+        dw = torch.zeros((self.L + 1, d), dtype=torch.float32, device=dev)
+        dg = torch.zeros((self.L + 1, d), dtype=torch.float32, device=dev)
+        dgamma = torch.zeros((max(self.L, 1), d), dtype=torch.float32, device=dev)
+        G = torch.empty((smax, T, d), dtype=self.dtype, device=dev)
+        cg = torch.empty((2, smax, T), dtype=torch.float32, device=dev)  # 1 - beta, G.h
+        ws1 = max([_lib.attnres_phase1_backward_workspace_bytes(T, d, n_reps, 1) if self.final_site else 0] +
+                  [_lib.attnres_phase1_backward_workspace_bytes(T, d, 1 + self.n_given + b, S)
+                   for b, S in enumerate(self.block_sizes)])
+        ws = torch.empty((max(ws1, _lib.attnres_phase2_backward_workspace_bytes(T, d), 16) + 3) // 4,
+                         dtype=torch.float32, device=dev)
+        # dL/db_i for b_0 .. b_N: the final site writes them all first
+        if self.final_site:
+            dB = torch.empty((n_reps, T, d), dtype=torch.float32, device=dev)
+            mark("final", True)
+            attnres_phase1_backward(self.reps, n_reps, w[self.L:self.L + 1],
+                                    None if g is None else g[self.L:self.L + 1], eps, dh_final.unsqueeze(0), None,
+                                    None, dB, dw[self.L:self.L + 1], None if g is None else dg[self.L:self.L + 1],
+                                    ws, accumulate=False, stream=stream)
+            mark("final", False)
+        else:
+            dB = torch.zeros((n_reps, T, d), dtype=torch.float32, device=dev)
+        l_end = self.L
+        for b in range(len(self.block_sizes) - 1, -1, -1):
+            S = self.block_sizes[b]
+            l0 = l_end - S
+            n = 1 + self.n_given + b
+            # the running gradient of the block's outputs starts as dL/db_n
+            # (b_n is no source of this block) and gains dL/dp_j per site
+            R = dB[n]
+            for j in range(S - 1, -1, -1):
+                l = l0 + j
+                dx = dx_for(l, R)
+                pin, v2, v = self.recipes[l] if j > 0 else (None, None, None)
+                mark("phase2", True)
+                attnres_phase2_backward(self.o_blocks[b][j], self.lse_blocks[b][j], pin, v, w[l],
+                                        None if g is None else g[l], None if gam is None else gam[l], eps, dx,
+                                        R if j > 0 else None, G[j], cg[0, j], cg[1, j], dw[l],
+                                        None if g is None else dg[l], dgamma[l], ws, sublayer_prev2=v2,
+                                        stream=stream)
+                mark("phase2", False)
+            mark("phase1", True)
+            attnres_phase1_backward(self.reps, n, w[l0:l0 + S], None if g is None else g[l0:l0 + S], eps, G[:S],
+                                    cg[0, :S], cg[1, :S], dB, dw[l0:l0 + S], None if g is None else dg[l0:l0 + S],
+                                    ws, accumulate=True, stream=stream)
+            mark("phase1", False)
+            l_end = l0
+        return {"demb": dB[0], "dgiven": dB[1:1 + self.n_given], "dw": dw, "dg": dg, "dgamma": dgamma[:self.L]}
 
 
 class FullAttnRes:
