@@ -272,8 +272,8 @@ attnres_status_t attnres_site_backward(attnres_dtype_t dt,
  *   p1_lse and dpartial may then be NULL).  w, key_gain, prenorm_gain: [d]
  *   fp32 (gains NULL = ones).  dx = dL/dx [T][d] (dt); prenorm == 0 means
  *   x = h.  Writes
- *     g_out = G = dL/dh [T][d] (dt),  c_out = 1 - beta, gh_out = G.h [T] fp32
- *   (G.h from G as stored), and ADDS
+ *     g_out = G = dL/dh [T][d] (dt),  c_out = 1 - beta, gp_out = G.p [T] fp32
+ *   (G as stored; 0 without a partial source), and ADDS
  *     dpartial += dL/dp [T][d] fp32 (the partial source's gradient: the
  *       running gradient of the block's earlier sublayer outputs),
  *     dw += dL/dw, dkey_gain += dL/dkey_gain of the partial source's score
@@ -287,10 +287,13 @@ attnres_status_t attnres_site_backward(attnres_dtype_t dt,
  * attnres_phase1_backward: the block sources' part of S sites at once.
  *   src, n_src, src_stride: the block sources as for attnres_phase1.
  *   w, key_gain: [S][d] fp32 (key_gain NULL = ones).  g_in + j*g_stride:
- *   G_j [T][d] (dt) of site j.  c_in, gh_in: [S][T] fp32 from the sites'
+ *   G_j [T][d] (dt) of site j.  c_in, gp_in: [S][T] fp32 from the sites'
  *   attnres_phase2_backward (both NULL: each site is its phase-1 partition
- *   alone, c = 1 and G.h derived here, e.g. the final aggregation with
- *   G = dL/dh_final).  Recomputes the scores and alpha1 of every site, and
+ *   alone, c = 1, e.g. the final aggregation with G = dL/dh_final; c_in
+ *   without gp_in is EINVAL).  Recomputes the scores and alpha1 of every
+ *   site and G_j.h_j = c_j sum_i alpha1_ji G_j.u_i + (1 - c_j) G_j.p_j from
+ *   the same dot products (not from the stored phase-1 output, whose
+ *   rounding would dominate u_i - h_j when one source dominates), and
  *     dsrc + i*dsrc_stride  [T][d] fp32: dL/du_i of the S sites, written
  *       (accumulate == 0) or added (accumulate != 0),
  *     dw += dL/dw, dkey_gain += dL/dkey_gain ([S][d] fp32) of the block
@@ -309,7 +312,7 @@ attnres_status_t attnres_phase2_backward(attnres_dtype_t dt, int64_t T, int64_t 
                                          const float* w, const float* key_gain,
                                          const float* prenorm_gain, int prenorm, float eps,
                                          const void* dx, float* dpartial,
-                                         void* g_out, float* c_out, float* gh_out,
+                                         void* g_out, float* c_out, float* gp_out,
                                          float* dw, float* dkey_gain, float* dprenorm_gain,
                                          void* workspace, int64_t workspace_bytes, void* stream);
 
@@ -319,7 +322,7 @@ attnres_status_t attnres_phase1_backward(attnres_dtype_t dt,
                                          int64_t T, int64_t d,
                                          const float* w, const float* key_gain, int64_t S, float eps,
                                          const void* g_in, int64_t g_stride,
-                                         const float* c_in, const float* gh_in,
+                                         const float* c_in, const float* gp_in,
                                          float* dsrc, int64_t dsrc_stride, int accumulate,
                                          float* dw, float* dkey_gain,
                                          void* workspace, int64_t workspace_bytes, void* stream);

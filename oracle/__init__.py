@@ -56,8 +56,10 @@ def _load():
         lib.oracle_full_forward.argtypes = [I, I, I, P, P, P, P, P, D, ctypes.c_int, P, P, P, P]
         lib.oracle_site_backward.argtypes = [I, I, P, P, P, P, ctypes.c_int, D, P, P, P, P, P]
         lib.oracle_site_backward_tokens.argtypes = [I, I, I, P, P, P, P, ctypes.c_int, D, P, P, P, P, P]
-        lib.oracle_block_backward.argtypes = [I, I, I, P, I, P, P, P, P, P, P, D, ctypes.c_int, P, P,
-                                              P, P, P, P, P]
+        lib.oracle_block_backward.argtypes = [I, I, I, P, I, P, P, P, P, P, P, D, ctypes.c_int, ctypes.c_int,
+                                              P, P, P, P, P, P, P]
+        lib.oracle_round_bf16.argtypes = [D]
+        lib.oracle_round_bf16.restype = D
         lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -226,10 +228,17 @@ def site_backward(src, w, g, gamma, eps: float, dx, prenorm: bool = True):
     return {"du": du, "dw": dw, "dg": dg, "dgamma": dgm if prenorm else None}
 
 
+def round_bf16(x: float) -> float:
+    """x to fp32 (nearest even), then to bfloat16 (nearest even)."""
+    return float(_load().oracle_round_bf16(float(x)))
+
+
 def block_backward(emb, v, w, g, gamma, blocks: Sequence[int], eps: float, dx, dhf=None, given=None,
-                   final_site: bool = True):
+                   final_site: bool = True, bf16_sums: bool = False):
     """Backward of block_forward with the sublayer outputs as inputs, for the
     loss sum_l dx_l . x_l + dhf . hfinal over the token rows of ``emb``.
+    ``bf16_sums``: the block sums enter the later sites rounded to bfloat16
+    (their storage), gradients passing the rounding unchanged.
 
     dx [L, n_tok, d]; dhf [n_tok, d] or None.  Returns fp64 arrays dv [L,
     n_tok, d], demb [n_tok, d], dgiven [n_given, n_tok, d], dw, dg [L+1, d]
@@ -250,7 +259,8 @@ def block_backward(emb, v, w, g, gamma, blocks: Sequence[int], eps: float, dx, d
     dg = np.empty((L + 1, d))
     dgamma = np.empty((max(L, 1), d))
     rc = _load().oracle_block_backward(n_tok, d, len(blocks), _p(bl), n_given, _p(emb), _p(given), _p(v), _p(w),
-                                       _p(g), _p(gamma), eps, 1 if final_site else 0, _p(dx), _p(dhf), _p(dv),
+                                       _p(g), _p(gamma), eps, 1 if final_site else 0, 1 if bf16_sums else 0,
+                                       _p(dx), _p(dhf), _p(dv),
                                        _p(dreps), _p(dw), _p(dg), _p(dgamma))
     if rc != 0:
         raise RuntimeError("oracle_block_backward failed: %d" % rc)

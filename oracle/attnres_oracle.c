@@ -370,10 +370,23 @@ int oracle_site_backward_tokens(int64_t n_tok, int64_t n, int64_t d, const float
     return bad ? -3 : 0;
 }
 
+double oracle_round_bf16(double x) {
+    /* to fp32 (nearest), then to the upper 16 bits of fp32, nearest with
+     * ties to even: bfloat16 storage of a value summed in fp32 */
+    const float f = (float)x;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (double)f;   /* inf, nan */
+    u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
+    float r;
+    memcpy(&r, &u, sizeof r);
+    return (double)r;
+}
+
 int oracle_block_backward(int64_t n_tok, int64_t d, int64_t n_blocks, const int64_t* blocks,
                           int64_t n_given, const float* emb, const float* given, const float* v,
                           const float* w, const float* g, const float* gamma, double eps,
-                          int final_site, const float* dx, const float* dhf, double* dv_out,
+                          int final_site, int bf16_sums, const float* dx, const float* dhf, double* dv_out,
                           double* dreps_out, double* dw_out, double* dg_out, double* dgamma_out) {
     if (n_tok < 0 || d <= 0 || n_blocks < 0 || n_given < 0 || !emb || !w || !dv_out || !dreps_out ||
         !dw_out || !dg_out || !dgamma_out)
@@ -427,6 +440,10 @@ int oracle_block_backward(int64_t n_tok, int64_t d, int64_t n_blocks, const int6
                         const float* vl = v + (l * n_tok + t) * d;
                         for (int64_t k = 0; k < d; ++k) bs[k] += (double)vl[k];
                     }
+                    /* a block sum kept in bf16 storage enters the later sites
+                     * rounded; its gradient reaches the block's outputs as is */
+                    if (bf16_sums)
+                        for (int64_t k = 0; k < d; ++k) bs[k] = oracle_round_bf16(bs[k]);
                 }
                 for (int64_t k = 0; k < R * d; ++k) db[k] = 0.0;
                 /* the final site reads b_0 .. b_N, no PreNorm */

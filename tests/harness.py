@@ -157,7 +157,14 @@ def run_block_backward_parity(w: synth.Workload, samples: Optional[Sequence[int]
     backward on sampled tokens: dL/dv_l of every site, dL/db_0 and the given
     block sums; with ``params_too`` (all tokens sampled) also dw, dg, dgamma.
     Upstream gradients dx_l, dh_final are seeded N(0,1) rows (or, with
-    ``dx_from_outputs``, the sublayer outputs themselves, to save memory)."""
+    ``dx_from_outputs``, the sublayer outputs themselves, to save memory).
+
+    For bf16 storage the forward keeps the block sums in bf16, and the exact
+    gradient is sensitive to that rounding (the logit gradient weighs
+    u_i - h, a difference of nearly equal rows).  The GPU result is held to
+    the bar against the oracle whose block sums are rounded to bf16 the same
+    way (computed by the oracle itself), and against the exact oracle to the
+    bar plus the distance between the two oracle results."""
     dev = torch.device(device)
     emb, given, v = block_inputs(w, dev)
     prm = synth.params(w, dev)
@@ -185,20 +192,30 @@ def run_block_backward_parity(w: synth.Workload, samples: Optional[Sequence[int]
     out = st.backward(prm, dx_for, dh_final=dhf if w.final_site else None)
     torch.cuda.synchronize()
     sel = lambda t: t.index_select(0, idx)  # noqa: E731
-    ref = oracle.block_backward(
-        sel(emb), torch.stack([sel(t) for t in v]), prm["w"], prm["g"], prm["gamma"], w.block_sizes, w.eps,
-        torch.stack([sel(t) for t in dx]), sel(dhf) if w.final_site else None,
-        given=torch.stack([sel(t) for t in given]) if given else None, final_site=w.final_site)
-    bar = TOL[w.dtype] if tol is None else tol
-    worst = {"dv": float(row_rel_err(_host(torch.stack(dv_rows)), ref["dv"]).max()),
-             "demb": float(row_rel_err(_host(sel(out["demb"])), ref["demb"]).max())}
+    args = (sel(emb), torch.stack([sel(t) for t in v]), prm["w"], prm["g"], prm["gamma"], w.block_sizes, w.eps,
+            torch.stack([sel(t) for t in dx]), sel(dhf) if w.final_site else None)
+    kw = dict(given=torch.stack([sel(t) for t in given]) if given else None, final_site=w.final_site)
+    # two references: exact block sums, and (bf16 storage) the block sums
+    # rounded to bf16 as the forward stores them, gradients passing through
+    exact = oracle.block_backward(*args, **kw)
+    stored = oracle.block_backward(*args, bf16_sums=True, **kw) if w.dtype == "bf16" else exact
+    gpu = {"dv": _host(torch.stack(dv_rows)), "demb": _host(sel(out["demb"]))}
     if w.n_given:
-        worst["dgiven"] = float(row_rel_err(_host(out["dgiven"].index_select(1, idx)), ref["dgiven"]).max())
+        gpu["dgiven"] = _host(out["dgiven"].index_select(1, idx))
     if params_too:
         assert len(samples) == w.T, "parameter gradients are sums over every token"
-        worst["dw"] = float(row_rel_err(_host(out["dw"]), ref["dw"]).max())
-        worst["dg"] = float(row_rel_err(_host(out["dg"]), ref["dg"]).max())
-        worst["dgamma"] = float(row_rel_err(_host(out["dgamma"]), ref["dgamma"]).max())
-    for k, e in worst.items():
+        for k in ("dw", "dg", "dgamma"):
+            gpu[k] = _host(out[k])
+    bar = TOL[w.dtype] if tol is None else tol
+    worst = {}
+    for k, x in gpu.items():
+        e = float(row_rel_err(x, stored[k]).max())
+        # what bf16 storage of the block sums alone moves the exact gradient by
+        sens = float(row_rel_err(stored[k], exact[k]).max())
+        e_exact = float(row_rel_err(x, exact[k]).max())
+        worst[k] = e
+        worst[k + "_vs_exact"] = e_exact
         assert e <= bar, "%s: %s max-abs-rel %.3e exceeds %.1e" % (w.name, k, e, bar)
+        assert e_exact <= bar + sens, "%s: %s vs exact sums %.3e exceeds %.1e + %.3e" % (w.name, k, e_exact, bar,
+                                                                                          sens)
     return worst

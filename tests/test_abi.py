@@ -177,7 +177,7 @@ def test_phase1_backward_validation(lib):
     assert p1b(lib, n=0) == EINVAL
     assert p1b(lib, n=17) == EINVAL
     assert p1b(lib, S=33) == EINVAL
-    assert p1b(lib, c=48 * A) == EINVAL                    # c without G.h: G.h cannot be derived
+    assert p1b(lib, c=48 * A) == EINVAL                    # a partial weight without its G.p
     assert p1b(lib, g=None) == EINVAL
     assert p1b(lib, ds=None) == EINVAL
     assert p1b(lib, dw=None) == EINVAL

@@ -53,3 +53,13 @@ def test_block_backward_decode_shape():
     _say("case block backward decode_block_bf16 T=%d d=%d S=24 given=%d" % (w.T, w.d, w.n_given))
     worst = run_block_backward_parity(w, samples=synth.sample_tokens(w.T, 24), params_too=False)
     _say("worst", worst)
+
+
+def test_block_backward_prefill_chunk_sampled():
+    """The 16K-token chunk, 186 sublayers in 8 blocks, at full size: every
+    sampled token's dL/dv_l and dL/db_0 (upstream gradients are sublayer
+    output rows, so no extra 44 GB of synthetic gradients is needed)."""
+    w = synth.WORKLOADS["prefill_chunk_bf16"]
+    _say("case block backward prefill_chunk_bf16 T=%d d=%d blocks=%s (8 sampled tokens)" % (w.T, w.d, w.block_sizes))
+    worst = run_block_backward_parity(w, samples=synth.sample_tokens(w.T, 8), params_too=False, dx_from_outputs=True)
+    _say("worst", worst)

@@ -135,3 +135,45 @@ def test_last_output_of_the_last_block_without_final_site_gets_nothing():
                               final_site=False)
     assert np.all(b["dv"][-1] == 0.0)
     assert np.all(np.any(b["dv"][:-1] != 0.0, axis=-1))
+
+
+def test_round_bf16_matches_torch_conversion():
+    # bfloat16 storage rounding, checked against torch's own fp32 -> bf16
+    # conversion (nearest, ties to even) on random values, ties and extremes
+    import torch
+    rng = np.random.default_rng(11)
+    xs = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-30, 30, 2000),
+                         1.0 + np.arange(1, 64) * 2.0 ** -9, -(2.0 + np.arange(1, 64) * 2.0 ** -8),
+                         [0.0, -0.0, 1e-40, -3e-39, 3.38e38, 65504.0]]).astype(np.float32)
+    want = torch.from_numpy(xs).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.round_bf16(float(x)) for x in xs])
+    np.testing.assert_array_equal(got, want)
+
+
+def test_bf16_sums_change_nothing_when_sums_are_representable():
+    # integer outputs in [-3, 3] sum exactly in bfloat16 over these blocks
+    rng = np.random.default_rng(12)
+    T, d, blocks = 2, 6, (3, 4)
+    c = _case(13, T, d, blocks, 1, True)
+    v = rng.integers(-3, 4, size=(7, T, d)).astype(np.float64)
+    a = oracle.block_backward(c["emb"], v, c["w"], c["g"], c["gamma"], blocks, 1e-6, c["dx"], c["dhf"],
+                              given=c["given"])
+    b = oracle.block_backward(c["emb"], v, c["w"], c["g"], c["gamma"], blocks, 1e-6, c["dx"], c["dhf"],
+                              given=c["given"], bf16_sums=True)
+    for k in ("dv", "demb", "dgiven"):
+        np.testing.assert_array_equal(a[k], b[k])
+    for k in ("dw", "dg", "dgamma"):  # sums over threads: any order
+        np.testing.assert_allclose(a[k], b[k], rtol=1e-12, atol=1e-14)
+
+
+def test_bf16_sums_move_the_gradients_a_little():
+    # generic outputs: the rounded sums must be used (results differ), and
+    # the difference stays at the scale of bf16 rounding
+    c = _case(14, 3, 16, (3, 4), 0, True)
+    a = oracle.block_backward(c["emb"], c["v"], c["w"], c["g"], c["gamma"], (3, 4), 1e-6, c["dx"], c["dhf"])
+    b = oracle.block_backward(c["emb"], c["v"], c["w"], c["g"], c["gamma"], (3, 4), 1e-6, c["dx"], c["dhf"],
+                              bf16_sums=True)
+    diff = np.max(np.abs(a["demb"] - b["demb"])) / np.max(np.abs(a["demb"]))
+    assert 0.0 < diff < 0.05
+    # the last block's outputs reach only the final site through b_N
+    assert np.any(a["dv"] != b["dv"])

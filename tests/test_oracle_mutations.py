@@ -60,6 +60,8 @@ BLOCK_BACKWARD_MUTATIONS = {
         "const float* vl = v + (l * n_tok + t) * d;\n"
         "                        for (int64_t k = 0; k < d; ++k) bs[k] += (double)vl[k];\n"
         "                        memcpy(parts + l * d, bs, sizeof(double) * (size_t)d);"),
+    "bbwd_bf16_sums_not_rounded": ("if (bf16_sums)\n", "if (0)\n"),
+    "bbwd_bf16_ties_away": ("u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;", "u = (u + 0x8000u) & 0xffff0000u;"),
     "bbwd_prenorm_skipped": ("if (oracle_site_backward(ns, d, srcs, wq, g ? gk : NULL, gamma ? gm : NULL, 1, eps, dxt,",
                              "if (oracle_site_backward(ns, d, srcs, wq, g ? gk : NULL, gamma ? gm : NULL, 0, eps, dxt,"),
 }

@@ -229,11 +229,12 @@ def attnres_phase2_backward(p1_out: torch.Tensor, p1_lse: Optional[torch.Tensor]
                             sublayer_prev: Optional[torch.Tensor], w: torch.Tensor, key_gain: Optional[torch.Tensor],
                             prenorm_gain: Optional[torch.Tensor], eps: float, dx: torch.Tensor,
                             dpartial: Optional[torch.Tensor], g_out: torch.Tensor, c_out: torch.Tensor,
-                            gh_out: torch.Tensor, dw: Optional[torch.Tensor], dkey_gain: Optional[torch.Tensor],
+                            gp_out: torch.Tensor, dw: Optional[torch.Tensor], dkey_gain: Optional[torch.Tensor],
                             dprenorm_gain: Optional[torch.Tensor], workspace: torch.Tensor, prenorm: bool = True,
                             sublayer_prev2: Optional[torch.Tensor] = None, stream=None) -> None:
-    """One site's phase-2 backward: p1_out, dx, g_out: [T, d]; p1_lse, c_out,
-    gh_out: [T]; the partial source as for attnres_phase2_merge; dpartial:
+    """One site's phase-2 backward: p1_out, dx, g_out: [T, d]; p1_lse, c_out
+    (1 - beta), gp_out (G.p): [T]; the partial source as for
+    attnres_phase2_merge; dpartial:
     [T, d] fp32, added to in place; dw, dkey_gain, dprenorm_gain: [d] fp32,
     added to."""
     T, d = p1_out.shape
@@ -242,7 +243,7 @@ def attnres_phase2_backward(p1_out: torch.Tensor, p1_lse: Optional[torch.Tensor]
     rc = load().attnres_phase2_backward(dtype_code(p1_out.dtype), T, d, _ptr(p1_out), _ptr(p1_lse), pdt,
                                         _ptr(partial_in), _ptr(sublayer_prev2), _ptr(sublayer_prev), _ptr(w),
                                         _ptr(key_gain), _ptr(prenorm_gain), 1 if prenorm else 0, eps, _ptr(dx),
-                                        _ptr(dpartial), _ptr(g_out), _ptr(c_out), _ptr(gh_out), _ptr(dw),
+                                        _ptr(dpartial), _ptr(g_out), _ptr(c_out), _ptr(gp_out), _ptr(dw),
                                         _ptr(dkey_gain), _ptr(dprenorm_gain), _ptr(workspace), ws_bytes,
                                         _stream(stream))
     _check("attnres_phase2_backward", rc)
@@ -254,11 +255,11 @@ def attnres_phase1_backward_workspace_bytes(T: int, d: int, n_src: int, S: int) 
 
 def attnres_phase1_backward(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],
                             eps: float, g_in: torch.Tensor, c_in: Optional[torch.Tensor],
-                            gh_in: Optional[torch.Tensor], dsrc: torch.Tensor, dw: torch.Tensor,
+                            gp_in: Optional[torch.Tensor], dsrc: torch.Tensor, dw: torch.Tensor,
                             dkey_gain: Optional[torch.Tensor], workspace: torch.Tensor, accumulate: bool = False,
                             stream=None) -> None:
     """The block sources' part of S sites: src: [>=n_src, T, d]; w, key_gain,
-    dw, dkey_gain: [S, d] fp32; g_in: [S, T, d]; c_in, gh_in: [S, T] or None;
+    dw, dkey_gain: [S, d] fp32; g_in: [S, T, d]; c_in, gp_in: [S, T] or None;
     dsrc: [>=n_src, T, d] fp32, written or (accumulate) added to."""
     S, d = w.shape
     T = g_in.shape[-2]
@@ -267,7 +268,7 @@ def attnres_phase1_backward(src: torch.Tensor, n_src: int, w: torch.Tensor, key_
     dstride = dsrc.stride(0) if dsrc.dim() == 3 else T * d
     ws_bytes = workspace.numel() * workspace.element_size()
     rc = load().attnres_phase1_backward(dtype_code(src.dtype), _ptr(src), n_src, stride, T, d, _ptr(w), _ptr(key_gain),
-                                        S, eps, _ptr(g_in), gstride, _ptr(c_in), _ptr(gh_in), _ptr(dsrc), dstride,
+                                        S, eps, _ptr(g_in), gstride, _ptr(c_in), _ptr(gp_in), _ptr(dsrc), dstride,
                                         1 if accumulate else 0, _ptr(dw), _ptr(dkey_gain), _ptr(workspace), ws_bytes,
                                         _stream(stream))
     _check("attnres_phase1_backward", rc)

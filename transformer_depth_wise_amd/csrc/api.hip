@@ -318,7 +318,7 @@ attnres_status_t attnres_phase2_backward(attnres_dtype_t dt, int64_t T, int64_t 
                                          const float* p1_lse, attnres_dtype_t partial_dt, const void* partial_in,
                                          const void* sublayer_prev2, const void* sublayer_prev, const float* w,
                                          const float* key_gain, const float* prenorm_gain, int prenorm, float eps,
-                                         const void* dx, float* dpartial, void* g_out, float* c_out, float* gh_out,
+                                         const void* dx, float* dpartial, void* g_out, float* c_out, float* gp_out,
                                          float* dw, float* dkey_gain, float* dprenorm_gain, void* workspace,
                                          int64_t workspace_bytes, void* stream) {
   if (!dtype_ok(dt) || !partial_ok(partial_dt, dt)) return ATTNRES_EDTYPE;
@@ -327,13 +327,13 @@ attnres_status_t attnres_phase2_backward(attnres_dtype_t dt, int64_t T, int64_t 
   if (T < 0 || !(eps >= 0.f)) return ATTNRES_EINVAL;
   if (!sublayer_prev && (partial_in || sublayer_prev2)) return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
-  if (!p1_out || !dx || !g_out || !c_out || !gh_out || !w) return ATTNRES_EINVAL;
+  if (!p1_out || !dx || !g_out || !c_out || !gp_out || !w) return ATTNRES_EINVAL;
   if (sublayer_prev && (!p1_lse || !dpartial)) return ATTNRES_EINVAL;
   const int64_t ws_need = attnres_phase2_backward_workspace_bytes(T, d);
   if (!workspace || workspace_bytes < ws_need) return ATTNRES_EINVAL;
   st = check_align({p1_out, partial_in, sublayer_prev2, sublayer_prev, w, key_gain, prenorm_gain, dx, dpartial, g_out,
                     workspace},
-                   {p1_lse, c_out, gh_out, dw, dkey_gain, dprenorm_gain});
+                   {p1_lse, c_out, gp_out, dw, dkey_gain, dprenorm_gain});
   if (st != ATTNRES_OK) return st;
   const int64_t es = esize(dt), rows = T * d;
   const Range i_o = range_of(p1_out, rows * es), i_l = p1_lse ? range_of(p1_lse, T * 4) : Range{0, 0};
@@ -344,12 +344,12 @@ attnres_status_t attnres_phase2_backward(attnres_dtype_t dt, int64_t T, int64_t 
   const Range i_gm = prenorm_gain ? range_of(prenorm_gain, d * 4) : Range{0, 0};
   const Range i_dx = range_of(dx, rows * es);
   const Range o_dp = sublayer_prev ? range_of(dpartial, rows * 4) : Range{0, 0};
-  const Range o_g = range_of(g_out, rows * es), o_c = range_of(c_out, T * 4), o_gh = range_of(gh_out, T * 4);
+  const Range o_g = range_of(g_out, rows * es), o_c = range_of(c_out, T * 4), o_gp = range_of(gp_out, T * 4);
   const Range o_dw = (sublayer_prev && dw) ? range_of(dw, d * 4) : Range{0, 0};
   const Range o_dk = (sublayer_prev && dkey_gain) ? range_of(dkey_gain, d * 4) : Range{0, 0};
   const Range o_dm = (prenorm && dprenorm_gain) ? range_of(dprenorm_gain, d * 4) : Range{0, 0};
   const Range o_ws = range_of(workspace, ws_need);
-  const Range outs[] = {o_dp, o_g, o_c, o_gh, o_dw, o_dk, o_dm, o_ws};
+  const Range outs[] = {o_dp, o_g, o_c, o_gp, o_dw, o_dk, o_dm, o_ws};
   for (Range o : outs)
     for (Range i : {i_o, i_l, i_p, i_v2, i_v, i_w, i_g, i_gm, i_dx})
       if (overlaps(o, i)) return ATTNRES_EALIAS;
@@ -358,7 +358,7 @@ attnres_status_t attnres_phase2_backward(attnres_dtype_t dt, int64_t T, int64_t 
       if (overlaps(outs[a], outs[b])) return ATTNRES_EALIAS;
   return hip_status(attnres::launch_p2_backward(
       kind_of(dt), T, (int)d, p1_out, p1_lse, kind_of(partial_dt), partial_in, sublayer_prev2, sublayer_prev, w,
-      key_gain, prenorm ? prenorm_gain : nullptr, prenorm ? 1 : 0, eps, dx, dpartial, g_out, c_out, gh_out, dw,
+      key_gain, prenorm ? prenorm_gain : nullptr, prenorm ? 1 : 0, eps, dx, dpartial, g_out, c_out, gp_out, dw,
       dkey_gain, prenorm ? dprenorm_gain : nullptr, static_cast<float*>(workspace),
       static_cast<hipStream_t>(stream)));
 }
@@ -374,7 +374,7 @@ int64_t attnres_phase1_backward_workspace_bytes(int64_t T, int64_t d, int64_t n_
 attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
                                          int64_t T, int64_t d, const float* w, const float* key_gain, int64_t S,
                                          float eps, const void* g_in, int64_t g_stride, const float* c_in,
-                                         const float* gh_in, float* dsrc, int64_t dsrc_stride, int accumulate,
+                                         const float* gp_in, float* dsrc, int64_t dsrc_stride, int accumulate,
                                          float* dw, float* dkey_gain, void* workspace, int64_t workspace_bytes,
                                          void* stream) {
   if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
@@ -382,7 +382,7 @@ attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, const void* src, in
   if (st != ATTNRES_OK) return st;
   if (T < 0 || n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || S < 1 || S > 32 || !(eps >= 0.f))
     return ATTNRES_EINVAL;
-  if (gh_in == nullptr && c_in != nullptr) return ATTNRES_EINVAL;  // G.h is derived only for a whole site
+  if (gp_in == nullptr && c_in != nullptr) return ATTNRES_EINVAL;  // a partial weight needs its G.p
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!src || !w || !g_in || !dsrc || !dw) return ATTNRES_EINVAL;
   if ((n_src > 1 && (src_stride < T * d || dsrc_stride < T * d)) || (S > 1 && g_stride < T * d))
@@ -390,14 +390,14 @@ attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, const void* src, in
   if (src_stride % 8 != 0 || dsrc_stride % 8 != 0 || g_stride % 8 != 0) return ATTNRES_EALIGN;
   const int64_t ws_need = attnres_phase1_backward_workspace_bytes(T, d, n_src, S);
   if (!workspace || workspace_bytes < ws_need) return ATTNRES_EINVAL;
-  st = check_align({src, w, key_gain, g_in, dsrc, workspace}, {c_in, gh_in, dw, dkey_gain});
+  st = check_align({src, w, key_gain, g_in, dsrc, workspace}, {c_in, gp_in, dw, dkey_gain});
   if (st != ATTNRES_OK) return st;
   const int64_t es = esize(dt);
   const Range i_s = range_of(src, ((n_src - 1) * src_stride + T * d) * es);
   const Range i_w = range_of(w, S * d * 4), i_k = key_gain ? range_of(key_gain, S * d * 4) : Range{0, 0};
   const Range i_g = range_of(g_in, ((S - 1) * g_stride + T * d) * es);
   const Range i_c = c_in ? range_of(c_in, S * T * 4) : Range{0, 0};
-  const Range i_h = gh_in ? range_of(gh_in, S * T * 4) : Range{0, 0};
+  const Range i_h = gp_in ? range_of(gp_in, S * T * 4) : Range{0, 0};
   const Range o_ds = range_of(dsrc, ((n_src - 1) * dsrc_stride + T * d) * 4);
   const Range o_dw = range_of(dw, S * d * 4), o_dk = dkey_gain ? range_of(dkey_gain, S * d * 4) : Range{0, 0};
   const Range o_ws = range_of(workspace, ws_need);
@@ -409,7 +409,7 @@ attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, const void* src, in
     for (int b = a + 1; b < 4; ++b)
       if (overlaps(outs[a], outs[b])) return ATTNRES_EALIAS;
   return hip_status(attnres::launch_p1_backward(kind_of(dt), T, (int)d, src, (int)n_src, src_stride, (int)S, w,
-                                                key_gain, eps, g_in, g_stride, c_in, gh_in, dsrc, dsrc_stride,
+                                                key_gain, eps, g_in, g_stride, c_in, gp_in, dsrc, dsrc_stride,
                                                 accumulate ? 1 : 0, dw, dkey_gain, static_cast<float*>(workspace),
                                                 static_cast<hipStream_t>(stream)));
 }

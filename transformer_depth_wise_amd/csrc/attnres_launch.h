@@ -49,7 +49,7 @@ int64_t backward_slots(int64_t T, int d);
 hipError_t launch_p2_backward(Dtype dt, int64_t T, int d, const void* o1, const float* lse1, Dtype pdt,
                               const void* pin, const void* vprev2, const void* vprev, const float* w, const float* kg,
                               const float* gamma, int prenorm, float eps, const void* dx, float* dpart, void* g_out,
-                              float* c_out, float* gh_out, float* dw, float* dkg, float* dgamma, float* part,
+                              float* c_out, float* gp_out, float* dw, float* dkg, float* dgamma, float* part,
                               hipStream_t stream);
 int64_t p2_backward_slots(int64_t T, int d);
 
@@ -58,7 +58,7 @@ int64_t p2_backward_slots(int64_t T, int d);
 // ws: T * S * n coefficients + p1_backward_ranges(d) * S * d partial sums.
 hipError_t launch_p1_backward(Dtype dt, int64_t T, int d, const void* src, int n, int64_t stride, int S,
                               const float* w, const float* kg, float eps, const void* gin, int64_t gstride,
-                              const float* c_in, const float* gh_in, float* dsrc, int64_t dstride, int accumulate,
+                              const float* c_in, const float* gp_in, float* dsrc, int64_t dstride, int accumulate,
                               float* dw, float* dkg, float* ws, hipStream_t stream);
 int64_t p1_backward_ranges(int d);
 

@@ -506,7 +506,7 @@ hipError_t launch_site_backward(Dtype dt, int64_t T, int d, const void* src, int
 //
 //  phase-2 backward, one launch per site (k_p2_bwd): recompute p_j, beta_j
 //    and h_j, apply the PreNorm backward to get G_j = dL/dh_j, store G_j and
-//    the per-token scalars c_j = 1 - beta_j and G_j.h_j, and add the partial
+//    the per-token scalars c_j = 1 - beta_j and G_j.p_j, and add the partial
 //    source's gradient
 //        dp_j = beta_j G_j + dz_jp (w (.) g - y_p z_jp / d) / r(p_j),
 //        dz_jp = beta_j G_j.(p_j - h_j)
@@ -520,7 +520,11 @@ hipError_t launch_site_backward(Dtype dt, int64_t T, int d, const void* src, int
 //    G_j.h_j), and then, for all S sites at once,
 //        du_i = sum_j c_j alpha1_ji G_j + r_i^-1 (sum_j dz_ji (w_j (.) g_j)
 //               - y_i sum_j dz_ji z_ji / d),
-//    added into the fp32 gradients of the sources.  The weight gradients of
+//    added into the fp32 gradients of the sources.  G_j.h_j is formed there
+//    from the same dot products, c_j sum_k alpha1_jk G_j.u_k + (1 - c_j)
+//    G_j.p_j, not from the stored phase-1 output: when one source dominates,
+//    u_i - h_j is small and the storage rounding of o_j would be a large part
+//    of it.  The weight gradients of
 //    the block sources, sum over tokens and i of dz_ji y_i, are a contraction
 //    over rows: a separate channel-group-major pass (k_p1_bwd_wgrad) keeps
 //    per-lane sums for its channels over a range of tokens, and a fixed-order
@@ -598,7 +602,7 @@ template <typename St, int TEAM, int CPL, bool HAS_V, bool HAS_PIN, bool HAS_V2,
 __device__ __forceinline__ void bprocess(const BStage<St, Pt, CPL>& s, int64_t tok, int64_t T, int d, int C,
                                          int tl, int wv, int lane, const float* lse1, const float* wql,
                                          const float* gml, int prenorm, float eps, float inv_d, float* dpart,
-                                         St* g_out, float* c_out, float* gh_out, BAcc<CPL, ACC_LDS>& acc,
+                                         St* g_out, float* c_out, float* gp_out, BAcc<CPL, ACC_LDS>& acc,
                                          float* red, int& parity) {
   constexpr int NW = TEAM / kWave;
   const bool live = tok < T;
@@ -692,9 +696,9 @@ __device__ __forceinline__ void bprocess(const BStage<St, Pt, CPL>& s, int64_t t
       }
     }
   }
-  // G as stored (the phase-1 backward reads it back): G.h of the stored
+  // G as stored (the phase-1 backward reads it back): G.p of the stored
   // values keeps G.(u_i - h) consistent there
-  float r3[3] = {0.f, 0.f, 0.f};
+  float r3[2] = {0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
     float gr[8];
@@ -711,19 +715,20 @@ __device__ __forceinline__ void bprocess(const BStage<St, Pt, CPL>& s, int64_t t
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      r3[0] = fmaf(gr[e], h[k][e], r3[0]);
-      r3[1] = fmaf(G[k][e], p[k][e], r3[1]);
-      r3[2] = fmaf(G[k][e], h[k][e], r3[2]);
+      r3[0] = fmaf(gr[e], p[k][e], r3[0]);
+      r3[1] = fmaf(G[k][e], p[k][e] - h[k][e], r3[1]);
     }
   }
-  team_reduce<NW, 3>(r3, red + parity * NW * 4, wv, lane);
-  parity ^= 1;
+  if (HAS_V) {
+    team_reduce<NW, 2>(r3, red + parity * NW * 4, wv, lane);
+    parity ^= 1;
+  }
   if (tl == 0 && live) {
     c_out[tok] = 1.0f - beta;
-    gh_out[tok] = r3[0];
+    gp_out[tok] = HAS_V ? r3[0] : 0.f;
   }
   if (HAS_V) {
-    const float dz = beta * (r3[1] - r3[2]);
+    const float dz = beta * r3[1];
     const float rpi = 1.0f / rp;
     const float zd = zc * inv_d;
 #pragma unroll
@@ -756,7 +761,7 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_p2_bwd(
     const St* __restrict__ vprev2, const St* __restrict__ vprev, const float* __restrict__ w,
     const float* __restrict__ kg, const float* __restrict__ gamma, int prenorm, float eps,
     const St* __restrict__ dx, float* __restrict__ dpart, St* __restrict__ g_out, float* __restrict__ c_out,
-    float* __restrict__ gh_out, float* __restrict__ part) {
+    float* __restrict__ gp_out, float* __restrict__ part) {
   constexpr int WG = TEAM < 256 ? 256 : TEAM;
   constexpr int TPW = WG / TEAM;
   constexpr int NW = TEAM / kWave;
@@ -792,21 +797,21 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_p2_bwd(
       bissue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(B, tok + step, T, d, C, tl, o1, pin, vprev2, vprev, dx, dpart,
                                                         plane);
       bprocess<St, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, ACC_LDS>(A, tok, T, d, C, tl, wv, lane, lse1, wql, gml, prenorm,
-                                                               eps, inv_d, dpart, g_out, c_out, gh_out, acc,
+                                                               eps, inv_d, dpart, g_out, c_out, gp_out, acc,
                                                                red[team], parity);
       tok += step;
       if (tok - team >= T) break;
       bissue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(A, tok + step, T, d, C, tl, o1, pin, vprev2, vprev, dx, dpart,
                                                         plane);
       bprocess<St, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, ACC_LDS>(B, tok, T, d, C, tl, wv, lane, lse1, wql, gml, prenorm,
-                                                               eps, inv_d, dpart, g_out, c_out, gh_out, acc,
+                                                               eps, inv_d, dpart, g_out, c_out, gp_out, acc,
                                                                red[team], parity);
       tok += step;
     }
   } else {
     while (tok - team < T) {
       bprocess<St, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, ACC_LDS>(A, tok, T, d, C, tl, wv, lane, lse1, wql, gml, prenorm,
-                                                               eps, inv_d, dpart, g_out, c_out, gh_out, acc,
+                                                               eps, inv_d, dpart, g_out, c_out, gp_out, acc,
                                                                red[team], parity);
       tok += step;
       if (tok - team >= T) break;
@@ -872,7 +877,7 @@ int64_t p2_backward_slots(int64_t T, int d) {
 template <typename St, typename Pt, int TEAM, int CPL>
 static hipError_t run_p2b(int64_t T, int d, const void* o1, const float* lse1, const void* pin, const void* vprev2,
                           const void* vprev, const float* w, const float* kg, const float* gamma, int prenorm,
-                          float eps, const void* dx, float* dpart, void* g_out, float* c_out, float* gh_out,
+                          float eps, const void* dx, float* dpart, void* g_out, float* c_out, float* gp_out,
                           float* dw, float* dkg, float* dgamma, float* part, hipStream_t stream) {
   constexpr int WG = TEAM < 256 ? 256 : TEAM;
   constexpr int TPW = WG / TEAM;
@@ -898,7 +903,7 @@ static hipError_t run_p2b(int64_t T, int d, const void* o1, const float* lse1, c
       if (e != hipSuccess) return e;                                                                              \
     }                                                                                                             \
     hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(WG), lds, stream, T, d, o, lse1, pi, v2, v, w, kg, gamma,  \
-                       prenorm, eps, g, dpart, go, c_out, gh_out, part);                                          \
+                       prenorm, eps, g, dpart, go, c_out, gp_out, part);                                          \
   } while (0)
   if (!vprev) {
     ATTNRES_P2B(false, false, false);
@@ -924,14 +929,14 @@ static hipError_t run_p2b(int64_t T, int d, const void* o1, const float* lse1, c
 template <typename St, typename Pt>
 static hipError_t pick_p2b(int64_t T, int d, const void* o1, const float* lse1, const void* pin, const void* vprev2,
                            const void* vprev, const float* w, const float* kg, const float* gamma, int prenorm,
-                           float eps, const void* dx, float* dpart, void* g_out, float* c_out, float* gh_out,
+                           float eps, const void* dx, float* dpart, void* g_out, float* c_out, float* gp_out,
                            float* dw, float* dkg, float* dgamma, float* part, hipStream_t stream) {
   int team, cpl;
   p2b_team(d, team, cpl);
 #define ATTNRES_P2B_RUN(TEAM_, CPL_)                                                                              \
   if (team == TEAM_ && cpl == CPL_)                                                                               \
   return run_p2b<St, Pt, TEAM_, CPL_>(T, d, o1, lse1, pin, vprev2, vprev, w, kg, gamma, prenorm, eps, dx, dpart, \
-                                      g_out, c_out, gh_out, dw, dkg, dgamma, part, stream)
+                                      g_out, c_out, gp_out, dw, dkg, dgamma, part, stream)
   ATTNRES_P2B_RUN(64, 1);
   ATTNRES_P2B_RUN(64, 2);
   ATTNRES_P2B_RUN(256, 1);
@@ -945,18 +950,18 @@ static hipError_t pick_p2b(int64_t T, int d, const void* o1, const float* lse1, 
 hipError_t launch_p2_backward(Dtype dt, int64_t T, int d, const void* o1, const float* lse1, Dtype pdt,
                               const void* pin, const void* vprev2, const void* vprev, const float* w, const float* kg,
                               const float* gamma, int prenorm, float eps, const void* dx, float* dpart, void* g_out,
-                              float* c_out, float* gh_out, float* dw, float* dkg, float* dgamma, float* part,
+                              float* c_out, float* gp_out, float* dw, float* dkg, float* dgamma, float* part,
                               hipStream_t stream) {
 #define ATTNRES_P2B_PIN(St_)                                                                                       \
   do {                                                                                                             \
     if (!pin || pdt == kF32)                                                                                       \
       return pick_p2b<St_, float>(T, d, o1, lse1, pin, vprev2, vprev, w, kg, gamma, prenorm, eps, dx, dpart, g_out, \
-                                  c_out, gh_out, dw, dkg, dgamma, part, stream);                                   \
+                                  c_out, gp_out, dw, dkg, dgamma, part, stream);                                   \
     if (pdt == kP24)                                                                                               \
       return pick_p2b<St_, p24_t>(T, d, o1, lse1, pin, vprev2, vprev, w, kg, gamma, prenorm, eps, dx, dpart, g_out, \
-                                  c_out, gh_out, dw, dkg, dgamma, part, stream);                                   \
+                                  c_out, gp_out, dw, dkg, dgamma, part, stream);                                   \
     return pick_p2b<St_, St_>(T, d, o1, lse1, pin, vprev2, vprev, w, kg, gamma, prenorm, eps, dx, dpart, g_out,     \
-                              c_out, gh_out, dw, dkg, dgamma, part, stream);                                       \
+                              c_out, gp_out, dw, dkg, dgamma, part, stream);                                       \
   } while (0)
   if (dt == kBF16) ATTNRES_P2B_PIN(bf16_t);
   ATTNRES_P2B_PIN(float);
@@ -995,7 +1000,7 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
                                                         int S, const float* __restrict__ q, float eps,
                                                         const St* __restrict__ gin, int64_t gstride,
                                                         const float* __restrict__ c_in,
-                                                        const float* __restrict__ gh_in, float* __restrict__ dsrc,
+                                                        const float* __restrict__ gp_in, float* __restrict__ dsrc,
                                                         int64_t dstride, int accumulate, float* __restrict__ coef) {
   constexpr int QB = P1bPass<St, N, QW>::kQB;
   constexpr int J3 = P1bPass<St, N, QW>::kJ3;
@@ -1089,13 +1094,14 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
         l += a[i];
       }
       const float c = c_in ? c_in[(int64_t)j * T + tok] : 1.f;
-      float gh = 0.f;
+      float go = 0.f;
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         a[i] = a[i] / l;
-        gh = fmaf(a[i], tD[j][i], gh);  // G.h when the phase-1 partition is the whole site
+        go = fmaf(a[i], tD[j][i], go);  // G.o, o the phase-1 partition's output
       }
-      if (gh_in) gh = gh_in[(int64_t)j * T + tok];
+      // G.h = c G.o + (1 - c) G.p, from the same dot products
+      const float gh = gp_in ? fmaf(c, go, (1.0f - c) * gp_in[(int64_t)j * T + tok]) : go;
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         const float ai = c * a[i];
@@ -1240,14 +1246,14 @@ int64_t p1_backward_ranges(int d) {
 
 template <typename St, int N, int QW>
 static hipError_t run_p1b_main(int64_t T, int d, const void* src, int64_t stride, int S, const float* q, float eps,
-                               const void* gin, int64_t gstride, const float* c_in, const float* gh_in, float* dsrc,
+                               const void* gin, int64_t gstride, const float* c_in, const float* gp_in, float* dsrc,
                                int64_t dstride, int accumulate, float* coef, hipStream_t stream) {
   int64_t wgs = T;
   const int64_t cap = (int64_t)device_cu_count() * 2;
   if (wgs > cap) wgs = cap;
   hipLaunchKernelGGL((k_p1_bwd<St, N, QW>), dim3((unsigned)wgs), dim3(kP1bThreads), 0, stream, T, d,
                      static_cast<const St*>(src), stride, S, q, eps, static_cast<const St*>(gin), gstride, c_in,
-                     gh_in, dsrc, dstride, accumulate, coef);
+                     gp_in, dsrc, dstride, accumulate, coef);
   return hipGetLastError();
 }
 
@@ -1265,7 +1271,7 @@ static hipError_t run_p1b_wgrad(int64_t T, int d, const void* src, int64_t strid
 
 template <typename St, int N>
 static hipError_t run_p1b(int64_t T, int d, const void* src, int64_t stride, int S, const float* w, const float* kg,
-                          float eps, const void* gin, int64_t gstride, const float* c_in, const float* gh_in,
+                          float eps, const void* gin, int64_t gstride, const float* c_in, const float* gp_in,
                           float* dsrc, int64_t dstride, int accumulate, float* dw, float* dkg, float* ws,
                           hipStream_t stream) {
   // workspace: coefficients [T][S][N], folded queries [S][d], range sums
@@ -1277,13 +1283,13 @@ static hipError_t run_p1b(int64_t T, int d, const void* src, int64_t stride, int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (S <= 8) {
-    e = run_p1b_main<St, N, 1>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gh_in, dsrc, dstride, accumulate,
+    e = run_p1b_main<St, N, 1>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
                                coef, stream);
   } else if (S <= 16) {
-    e = run_p1b_main<St, N, 2>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gh_in, dsrc, dstride, accumulate,
+    e = run_p1b_main<St, N, 2>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
                                coef, stream);
   } else {
-    e = run_p1b_main<St, N, 4>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gh_in, dsrc, dstride, accumulate,
+    e = run_p1b_main<St, N, 4>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
                                coef, stream);
   }
   if (e != hipSuccess) return e;
@@ -1304,12 +1310,12 @@ static hipError_t run_p1b(int64_t T, int d, const void* src, int64_t stride, int
 template <typename St>
 static hipError_t pick_p1b(int n, int64_t T, int d, const void* src, int64_t stride, int S, const float* w,
                            const float* kg, float eps, const void* gin, int64_t gstride, const float* c_in,
-                           const float* gh_in, float* dsrc, int64_t dstride, int accumulate, float* dw, float* dkg,
+                           const float* gp_in, float* dsrc, int64_t dstride, int accumulate, float* dw, float* dkg,
                            float* ws, hipStream_t stream) {
   switch (n) {
 #define ATTNRES_CASE(N_)                                                                                           \
   case N_:                                                                                                         \
-    return run_p1b<St, N_>(T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gh_in, dsrc, dstride, accumulate, \
+    return run_p1b<St, N_>(T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate, \
                            dw, dkg, ws, stream);
     ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4) ATTNRES_CASE(5) ATTNRES_CASE(6)
     ATTNRES_CASE(7) ATTNRES_CASE(8) ATTNRES_CASE(9) ATTNRES_CASE(10) ATTNRES_CASE(11) ATTNRES_CASE(12)
@@ -1321,12 +1327,12 @@ static hipError_t pick_p1b(int n, int64_t T, int d, const void* src, int64_t str
 
 hipError_t launch_p1_backward(Dtype dt, int64_t T, int d, const void* src, int n, int64_t stride, int S,
                               const float* w, const float* kg, float eps, const void* gin, int64_t gstride,
-                              const float* c_in, const float* gh_in, float* dsrc, int64_t dstride, int accumulate,
+                              const float* c_in, const float* gp_in, float* dsrc, int64_t dstride, int accumulate,
                               float* dw, float* dkg, float* ws, hipStream_t stream) {
   if (dt == kBF16)
-    return pick_p1b<bf16_t>(n, T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gh_in, dsrc, dstride, accumulate,
+    return pick_p1b<bf16_t>(n, T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
                             dw, dkg, ws, stream);
-  return pick_p1b<float>(n, T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gh_in, dsrc, dstride, accumulate, dw,
+  return pick_p1b<float>(n, T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate, dw,
                          dkg, ws, stream);
 }
 

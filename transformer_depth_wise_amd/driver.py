@@ -46,7 +46,7 @@ Sublayer = Callable[[int, torch.Tensor], torch.Tensor]
 
 @dataclasses.dataclass
 class Launch:
-    kind: str       # "phase1", "phase2", "accumulate", "final", "full"
+    kind: str       # "phase1", "phase2", "accumulate", "final", "full", "*_backward"
     bytes: int      # algorithmic bytes moved by this launch
 
 
@@ -278,6 +278,44 @@ class BlockAttnRes:
             mark("final", False)
         return self.h_final
 
+    def plan_backward(self) -> List[Launch]:
+        """Algorithmic bytes of every launch of ``backward``, in launch order
+        (rows counted once; gradients of rows are fp32, read and written).
+        Phase-2 backward of site j: o, dx and the partial source's terms
+        read, G written, and (after the first sublayer) the fp32 running
+        gradient read and written.  Phase-1 backward of a block: the n
+        sources and S rows of G read once, the n fp32 source gradients read
+        and written, plus the per-token coefficients (written and read back).
+        The final site: N+1 sources and dL/dh_final read, N+1 fp32 gradients
+        written."""
+        r = self._row()
+        r32 = self.T * self.d * 4
+        rp = self.T * self.d * (3 if self.partial_format == "p24" else 4)
+        stat = self.T * 4
+        out: List[Launch] = []
+        n_reps = 1 + self.n_given + len(self.block_sizes)
+        if self.final_site:
+            out.append(Launch("final_backward", (n_reps + 1) * r + n_reps * r32 + stat))
+        n = n_reps - 1
+        for S in reversed(self.block_sizes):
+            n -= 1
+            for j in range(S - 1, -1, -1):
+                if j == 0:
+                    b = 2 * r + r + 2 * stat                      # o, dx; G
+                elif j == 1:
+                    b = 3 * r + 2 * r32 + r + 3 * stat            # o, dx, v0; R; G
+                elif j == 2:
+                    b = 4 * r + 2 * r32 + r + 3 * stat            # o, dx, v0, v1; R; G
+                elif j % 2:
+                    b = 3 * r + rp + 2 * r32 + r + 3 * stat       # o, dx, p, v; R; G
+                else:
+                    b = 4 * r + rp + 2 * r32 + r + 3 * stat       # o, dx, p, v, v; R; G
+                out.append(Launch("phase2_backward", b))
+            nsrc = n + 1
+            out.append(Launch("phase1_backward", (nsrc + S) * r + 2 * nsrc * r32 + 2 * S * stat +
+                              2 * self.T * S * nsrc * 4))
+        return out
+
     # --------------------------------------------------------------- backward
     def backward(self, params: Dict[str, torch.Tensor], dx_for: Callable[[int, torch.Tensor], torch.Tensor],
                  dh_final: Optional[torch.Tensor] = None, stream=None,
@@ -301,7 +339,7 @@ class BlockAttnRes:
         dg = torch.zeros((self.L + 1, d), dtype=torch.float32, device=dev)
         dgamma = torch.zeros((max(self.L, 1), d), dtype=torch.float32, device=dev)
         G = torch.empty((smax, T, d), dtype=self.dtype, device=dev)
-        cg = torch.empty((2, smax, T), dtype=torch.float32, device=dev)  # 1 - beta, G.h
+        cg = torch.empty((2, smax, T), dtype=torch.float32, device=dev)  # 1 - beta, G.p
         ws1 = max([_lib.attnres_phase1_backward_workspace_bytes(T, d, n_reps, 1) if self.final_site else 0] +
                   [_lib.attnres_phase1_backward_workspace_bytes(T, d, 1 + self.n_given + b, S)
                    for b, S in enumerate(self.block_sizes)])
@@ -310,12 +348,12 @@ class BlockAttnRes:
         # dL/db_i for b_0 .. b_N: the final site writes them all first
         if self.final_site:
             dB = torch.empty((n_reps, T, d), dtype=torch.float32, device=dev)
-            mark("final", True)
+            mark("final_backward", True)
             attnres_phase1_backward(self.reps, n_reps, w[self.L:self.L + 1],
                                     None if g is None else g[self.L:self.L + 1], eps, dh_final.unsqueeze(0), None,
                                     None, dB, dw[self.L:self.L + 1], None if g is None else dg[self.L:self.L + 1],
                                     ws, accumulate=False, stream=stream)
-            mark("final", False)
+            mark("final_backward", False)
         else:
             dB = torch.zeros((n_reps, T, d), dtype=torch.float32, device=dev)
         l_end = self.L
@@ -330,18 +368,18 @@ class BlockAttnRes:
                 l = l0 + j
                 dx = dx_for(l, R)
                 pin, v2, v = self.recipes[l] if j > 0 else (None, None, None)
-                mark("phase2", True)
+                mark("phase2_backward", True)
                 attnres_phase2_backward(self.o_blocks[b][j], self.lse_blocks[b][j], pin, v, w[l],
                                         None if g is None else g[l], None if gam is None else gam[l], eps, dx,
                                         R if j > 0 else None, G[j], cg[0, j], cg[1, j], dw[l],
                                         None if g is None else dg[l], dgamma[l], ws, sublayer_prev2=v2,
                                         stream=stream)
-                mark("phase2", False)
-            mark("phase1", True)
+                mark("phase2_backward", False)
+            mark("phase1_backward", True)
             attnres_phase1_backward(self.reps, n, w[l0:l0 + S], None if g is None else g[l0:l0 + S], eps, G[:S],
                                     cg[0, :S], cg[1, :S], dB, dw[l0:l0 + S], None if g is None else dg[l0:l0 + S],
                                     ws, accumulate=True, stream=stream)
-            mark("phase1", False)
+            mark("phase1_backward", False)
             l_end = l0
         return {"demb": dB[0], "dgiven": dB[1:1 + self.n_given], "dw": dw, "dg": dg, "dgamma": dgamma[:self.L]}
 
