@@ -837,22 +837,41 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_p2_bwd(
   }
 }
 
-// Add the per-team sums, in slot order: dw += g (.) A, dg += w (.) A,
-// dgamma += the dgamma sum.  One thread per channel.
-__global__ __launch_bounds__(256) void k_p2_bwd_reduce(int64_t slots, int d, const float* __restrict__ part,
-                                                       const float* __restrict__ w, const float* __restrict__ kg,
-                                                       float* __restrict__ dw, float* __restrict__ dkg,
-                                                       float* __restrict__ dgamma) {
-  const int k = blockIdx.x * 256 + threadIdx.x;
-  if (k >= d) return;
+// Add the per-team sums: dw += g (.) A, dg += w (.) A, dgamma += the dgamma
+// sum.  A workgroup takes 64 channels; its 16 waves sum contiguous sixteenths
+// of the slots, and the partial sums are added in wave order through LDS (a
+// fixed order: bitwise reproducible).
+constexpr int kRedWaves = 16;
+
+__global__ __launch_bounds__(64 * kRedWaves) void k_p2_bwd_reduce(int64_t slots, int d,
+                                                                  const float* __restrict__ part,
+                                                                  const float* __restrict__ w,
+                                                                  const float* __restrict__ kg,
+                                                                  float* __restrict__ dw, float* __restrict__ dkg,
+                                                                  float* __restrict__ dgamma) {
+  __shared__ float sums[kRedWaves][2][64];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int k = blockIdx.x * 64 + lane;
+  const int kc = k < d ? k : d - 1;
+  const int64_t s0 = (slots * q) / kRedWaves, s1 = (slots * (q + 1)) / kRedWaves;
   float A = 0.f, G = 0.f;
-  for (int64_t s = 0; s < slots; ++s) {
-    A += part[s * 2 * (int64_t)d + k];
-    G += part[s * 2 * (int64_t)d + d + k];
+  for (int64_t s = s0; s < s1; ++s) {
+    A += part[s * 2 * (int64_t)d + kc];
+    G += part[s * 2 * (int64_t)d + d + kc];
   }
-  if (dw) dw[k] += kg ? kg[k] * A : A;
-  if (dkg) dkg[k] += w[k] * A;
-  if (dgamma) dgamma[k] += G;
+  sums[q][0][lane] = A;
+  sums[q][1][lane] = G;
+  lds_barrier();
+  if (q == 0 && k < d) {
+    A = 0.f, G = 0.f;
+    for (int r = 0; r < kRedWaves; ++r) {
+      A += sums[r][0][lane];
+      G += sums[r][1][lane];
+    }
+    if (dw) dw[k] += kg ? kg[k] * A : A;
+    if (dkg) dkg[k] += w[k] * A;
+    if (dgamma) dgamma[k] += G;
+  }
 }
 
 // Teams of the phase-2 backward by row width (each thread one or two chunks).
@@ -921,7 +940,8 @@ static hipError_t run_p2b(int64_t T, int d, const void* o1, const float* lse1, c
 #undef ATTNRES_P2B
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_p2_bwd_reduce, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, stream, wgs * TPW, d, part, w,
+  hipLaunchKernelGGL(k_p2_bwd_reduce, dim3((unsigned)((d + 63) / 64)), dim3(64 * kRedWaves), 0, stream, wgs * TPW, d,
+                     part, w,
                      kg, vprev ? dw : nullptr, vprev ? dkg : nullptr, prenorm ? dgamma : nullptr);
   return hipGetLastError();
 }
@@ -991,7 +1011,7 @@ __global__ __launch_bounds__(256) void k_fold_queries(int64_t n, const float* __
 // sources; fewer for more sources or fp32 rows (registers).
 template <typename St, int N, int QW>
 struct P1bPass {
-  static constexpr int kQB = N <= 8 ? QW : (sizeof(St) == 4 ? 1 : (QW < 2 ? QW : 2));
+  static constexpr int kQB = N <= 8 ? (QW == 4 ? 2 : QW) : ((sizeof(St) == 4 || QW == 3) ? 1 : (QW < 2 ? QW : 2));
   static constexpr int kJ3 = N <= 8 ? 4 : 2;  // sites per step of part III
 };
 
@@ -1012,7 +1032,8 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
   const int ngroups = (C + 63) >> 6;
   const float inv_d = 1.0f / (float)d;
   for (int64_t tok = blockIdx.x; tok < T; tok += gridDim.x) {
-    // ---- part I: dot products over the row, QB of the wave's sites per pass
+    // ---- part I: dot products over the row, QB of the wave's sites per pass;
+    // the next group's chunks load while the current group is used
 #pragma unroll
     for (int qb = 0; qb < QW; qb += QB) {
       float D[QB][N], Z[QB][N], ss[N];
@@ -1022,20 +1043,28 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
 #pragma unroll
         for (int k = 0; k < QB; ++k) D[k][i] = Z[k][i] = 0.f;
       }
-      for (int g = 0; g < ngroups; ++g) {
+      Chunk<St> ua[N], ub[N], ga[QB], gb[QB];
+      Chunk<float> qa[QB], qbf[QB];
+      auto fetch = [&](Chunk<St>(&u)[N], Chunk<St>(&gq)[QB], Chunk<float>(&qq)[QB], int g) {
         const int c0 = g * 64 + lane;
-        const bool ok = c0 < C;
-        const int c = ok ? c0 : C - 1;
-        Chunk<St> u[N];
+        const int c = c0 < C ? c0 : C - 1;
 #pragma unroll
         for (int i = 0; i < N; ++i) u[i].load(src + i * stride + tok * d + c * 8);
-        float gq[QB][8], qq[QB][8];
 #pragma unroll
         for (int k = 0; k < QB; ++k) {
           const int j0 = wv + 8 * (qb + k);
           const int j = j0 < S ? j0 : S - 1;
-          load8(gin + j * gstride + tok * d + c * 8, gq[k]);
-          load8(q + (int64_t)j * d + c * 8, qq[k]);
+          gq[k].load(gin + j * gstride + tok * d + c * 8);
+          qq[k].load(q + (int64_t)j * d + c * 8);
+        }
+      };
+      auto consume = [&](const Chunk<St>(&u)[N], const Chunk<St>(&gq)[QB], const Chunk<float>(&qq)[QB], int g) {
+        const bool ok = g * 64 + lane < C;
+        float gf[QB][8], qf[QB][8];
+#pragma unroll
+        for (int k = 0; k < QB; ++k) {
+          gq[k].unpack(gf[k]);
+          qq[k].unpack(qf[k]);
         }
 #pragma unroll
         for (int i = 0; i < N; ++i) {
@@ -1050,10 +1079,18 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
           for (int k = 0; k < QB; ++k)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              D[k][i] = fmaf(gq[k][e], ue[e], D[k][i]);
-              Z[k][i] = fmaf(qq[k][e], ue[e], Z[k][i]);
+              D[k][i] = fmaf(gf[k][e], ue[e], D[k][i]);
+              Z[k][i] = fmaf(qf[k][e], ue[e], Z[k][i]);
             }
         }
+      };
+      fetch(ua, ga, qa, 0);
+      for (int g = 0; g < ngroups; g += 2) {
+        fetch(ub, gb, qbf, g + 1 < ngroups ? g + 1 : ngroups - 1);
+        consume(ua, ga, qa, g);
+        if (g + 1 >= ngroups) break;
+        fetch(ua, ga, qa, g + 2 < ngroups ? g + 2 : ngroups - 1);
+        consume(ub, gb, qbf, g + 1);
       }
 #pragma unroll
       for (int k = 0; k < QB; ++k) {
@@ -1122,31 +1159,46 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
       te[i] = e * inv_d * ri * ri;     // coefficient of u_i in the radial term
     }
     lds_barrier();
-    // ---- part III: du_i = sum_j a_ji G_j + sum_j b_ji (w_j (.) g_j) - e_i u_i
+    // ---- part III: du_i = sum_j a_ji G_j + sum_j b_ji (w_j (.) g_j) - e_i u_i;
+    // the next batch of J3 sites loads while the current batch is used
     for (int c = threadIdx.x; c < C; c += kP1bThreads) {
       float du[N][8];
 #pragma unroll
       for (int i = 0; i < N; ++i) zero8(du[i]);
-      for (int j0 = 0; j0 < S; j0 += J3) {
-        float gq[J3][8], qq[J3][8];
+      Chunk<St> ga[J3], gb[J3];
+      Chunk<float> qa[J3], qbf[J3];
+      auto fetch = [&](Chunk<St>(&gq)[J3], Chunk<float>(&qq)[J3], int j0) {
 #pragma unroll
         for (int u = 0; u < J3; ++u) {
           const int j = j0 + u < S ? j0 + u : S - 1;
-          load8(gin + j * gstride + tok * d + c * 8, gq[u]);
-          load8(q + (int64_t)j * d + c * 8, qq[u]);
+          gq[u].load(gin + j * gstride + tok * d + c * 8);
+          qq[u].load(q + (int64_t)j * d + c * 8);
         }
+      };
+      auto consume = [&](const Chunk<St>(&gq)[J3], const Chunk<float>(&qq)[J3], int j0) {
 #pragma unroll
         for (int u = 0; u < J3; ++u) {
           const int j = j0 + u;
           if (j < S) {
+            float gf[8], qf[8];
+            gq[u].unpack(gf);
+            qq[u].unpack(qf);
 #pragma unroll
             for (int i = 0; i < N; ++i) {
               const float ai = ta[j][i], bi = tb[j][i];
 #pragma unroll
-              for (int e = 0; e < 8; ++e) du[i][e] = fmaf(ai, gq[u][e], fmaf(bi, qq[u][e], du[i][e]));
+              for (int e = 0; e < 8; ++e) du[i][e] = fmaf(ai, gf[e], fmaf(bi, qf[e], du[i][e]));
             }
           }
         }
+      };
+      fetch(ga, qa, 0);
+      for (int j0 = 0; j0 < S; j0 += 2 * J3) {
+        fetch(gb, qbf, j0 + J3);
+        consume(ga, qa, j0);
+        if (j0 + J3 >= S) break;
+        fetch(ga, qa, j0 + 2 * J3);
+        consume(gb, qbf, j0 + J3);
       }
 #pragma unroll
       for (int i = 0; i < N; ++i) {
@@ -1174,7 +1226,7 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
 // of (dz_ji / r_i) u_i.  A wave owns one 64-chunk group of channels and a
 // range of tokens; JT sites per launch pass (starting at site j0) keep their
 // sums in registers; the range's sums go to part[range][j][d].
-constexpr int kWgradWaves = 1024;
+constexpr int kWgradWaves = 2048;
 
 template <typename St, int N, int JT>
 __global__ __launch_bounds__(256) void k_p1_bwd_wgrad(int64_t T, int d, const St* __restrict__ src, int64_t stride,
@@ -1193,23 +1245,37 @@ __global__ __launch_bounds__(256) void k_p1_bwd_wgrad(int64_t T, int d, const St
   float acc[JT][8];
 #pragma unroll
   for (int q = 0; q < JT; ++q) zero8(acc[q]);
-  for (int64_t t = t0; t < t1; ++t) {
-    float u[N][8];
+  // the next token's source chunks load while this token's are used
+  Chunk<St> ua[N], ub[N];
+  auto fetch = [&](Chunk<St>(&u)[N], int64_t t) {
+    const int64_t tc = t < T ? t : T - 1;
 #pragma unroll
-    for (int i = 0; i < N; ++i) load8(src + i * stride + t * d + c * 8, u[i]);
+    for (int i = 0; i < N; ++i) u[i].load(src + i * stride + tc * d + c * 8);
+  };
+  auto use = [&](const Chunk<St>(&u)[N], int64_t t) {
     const float* cf = coef + t * S * N;
 #pragma unroll
-    for (int q = 0; q < JT; ++q) {
-      const int j = j0 + q;
-      if (j < S) {
+    for (int i = 0; i < N; ++i) {
+      float ue[8];
+      u[i].unpack(ue);
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
+      for (int q = 0; q < JT; ++q) {
+        const int j = j0 + q;
+        if (j < S) {
           const float b = cf[j * N + i];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(b, u[i][e], acc[q][e]);
+          for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(b, ue[e], acc[q][e]);
         }
       }
     }
+  };
+  if (t0 < t1) fetch(ua, t0);
+  for (int64_t t = t0; t < t1; t += 2) {
+    fetch(ub, t + 1);
+    use(ua, t);
+    if (t + 1 >= t1) break;
+    fetch(ua, t + 2);
+    use(ub, t + 1);
   }
   // every range stores its sums, zeros when it holds no token (the
   // reduction reads all ranges)
@@ -1287,6 +1353,9 @@ static hipError_t run_p1b(int64_t T, int d, const void* src, int64_t stride, int
                                coef, stream);
   } else if (S <= 16) {
     e = run_p1b_main<St, N, 2>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
+                               coef, stream);
+  } else if (S <= 24) {
+    e = run_p1b_main<St, N, 3>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
                                coef, stream);
   } else {
     e = run_p1b_main<St, N, 4>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
