@@ -62,10 +62,12 @@ def cpu_baseline(w, emb, v, prm, target_s: float):
     }
 
 
-def measured_traffic(path, kind, workload):
+def measured_traffic(path, kind, workload, alg_bytes_per_launch=None):
     """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when there is none or
-    the kernel's sources changed since the counters were taken."""
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when there is none,
+    the kernel's sources changed since the counters were taken, or the
+    launch mix differs (the current plan's algorithmic bytes per launch are
+    not the ones the counters were taken with)."""
     import hashlib
     if not os.path.exists(path):
         return None
@@ -82,6 +84,8 @@ def measured_traffic(path, kind, workload):
             return None
         h.update(open(fp, "rb").read())
     if h.hexdigest()[:16] != tr.get("source_sha256_16"):
+        return None
+    if alg_bytes_per_launch is not None and int(alg_bytes_per_launch) != tr.get("algorithmic_bytes_per_launch"):
         return None
     return tr.get("bytes_per_launch")
 
@@ -455,7 +459,7 @@ def main() -> int:
     avg_launch_s = kind_ms[dom] / steps / launches * 1e-3
     avg_bytes = kind_bytes[dom] / launches
     achieved = avg_bytes / avg_launch_s / 1e9
-    traffic = measured_traffic(args.traffic, dom, w.name)
+    traffic = measured_traffic(args.traffic, dom, w.name, int(avg_bytes))
     out = {
         "metric": METRIC,
         "value": round(units * steps / elapsed, 1),
