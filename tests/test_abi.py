@@ -192,10 +192,11 @@ def test_phase1_backward_validation(lib):
     assert p1b(lib, dk=32 * A + 64, kg=48 * A) == EALIAS   # the two weight gradients overlap
     assert p1b(lib, ws=24 * A + 64) == EALIAS
     assert p1b(lib, T=0) == 0
-    # coefficients T x S x n, folded queries S x d, per-range sums (2048 waves over d / 512 groups)
-    assert lib.attnres_phase1_backward_workspace_bytes(1024, 64, 3, 4) == 4 * (1024 * 4 * 3 + 4 * 64 + 2048 * 4 * 64)
+    # coefficients T x (S rounded up to 8) x n, folded queries S x d, per-range sums (2048 waves over
+    # d / 256 groups)
+    assert lib.attnres_phase1_backward_workspace_bytes(1024, 64, 3, 4) == 4 * (1024 * 8 * 3 + 4 * 64 + 2048 * 4 * 64)
     assert lib.attnres_phase1_backward_workspace_bytes(16384, 7168, 8, 24) == \
-        4 * (16384 * 24 * 8 + 24 * 7168 + 147 * 24 * 7168)
+        4 * (16384 * 24 * 8 + 24 * 7168 + 74 * 24 * 7168)
     assert lib.attnres_phase1_backward_workspace_bytes(10, 64, 3, 33) == -1
 
 

@@ -367,8 +367,10 @@ int64_t attnres_phase1_backward_workspace_bytes(int64_t T, int64_t d, int64_t n_
   if (T < 0 || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
   if (n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || S < 1 || S > 32) return -1;
   if (T == 0) return 0;
-  // coefficients [T][S][n], folded queries [S][d], per-range weight sums
-  return (T * S * n_src + S * d + attnres::p1_backward_ranges((int)d) * S * d) * (int64_t)sizeof(float);
+  // coefficients [T][S rounded up to 8][n], folded queries [S][d],
+  // per-range weight sums
+  const int64_t sp = (S + 7) & ~(int64_t)7;
+  return (T * sp * n_src + S * d + attnres::p1_backward_ranges((int)d) * S * d) * (int64_t)sizeof(float);
 }
 
 attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,

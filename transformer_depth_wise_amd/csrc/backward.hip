@@ -1024,6 +1024,7 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
                                                         int64_t dstride, int accumulate, float* __restrict__ coef) {
   constexpr int QB = P1bPass<St, N, QW>::kQB;
   constexpr int J3 = P1bPass<St, N, QW>::kJ3;
+  const int SP = (S + 7) & ~7;  // sites of the coefficient table, padded
   __shared__ float tD[kP1bSites][N], tZ[kP1bSites][N], tss[N];
   __shared__ float ta[kP1bSites][N], tb[kP1bSites][N], tq[kP1bSites][N], te[N];
   const int lane = threadIdx.x & (kWave - 1);
@@ -1147,8 +1148,12 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
         ta[j][i] = ai;
         tb[j][i] = dz * ri;            // dz / r_i: weight of w_j (.) g_j, and of y_i in dw
         tq[j][i] = dz * z[i];
-        coef[(tok * S + j) * N + i] = dz * ri;
+        coef[(tok * SP + j) * N + i] = dz * ri;
       }
+    } else if ((int)threadIdx.x < SP) {
+      // the table is padded to whole groups of 8 sites with zeros
+#pragma unroll
+      for (int i = 0; i < N; ++i) coef[(tok * SP + threadIdx.x) * N + i] = 0.f;
     }
     lds_barrier();
     if ((int)threadIdx.x < N) {
@@ -1223,49 +1228,67 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
 }
 
 // Weight gradients of the block sources: A_j = sum over tokens and sources
-// of (dz_ji / r_i) u_i.  A wave owns one 64-chunk group of channels and a
-// range of tokens; JT sites per launch pass (starting at site j0) keep their
-// sums in registers; the range's sums go to part[range][j][d].
+// of (dz_ji / r_i) u_i.  A wave owns one group of 256 channels (4 per lane,
+// so all JT <= 32 sites keep their sums in registers and the sources are
+// read once) and a range of tokens, with the next token's chunks in flight;
+// the range's sums go to part[range][j][d].
 constexpr int kWgradWaves = 2048;
+
+template <typename St>
+struct Quad;  // 4 consecutive channels
+template <>
+struct Quad<bf16_t> {
+  u32x2_t r;
+  __device__ __forceinline__ void load(const bf16_t* p) { r = ld8(p); }
+  __device__ __forceinline__ void unpack(float (&v)[4]) const {
+    v[0] = __uint_as_float(r.x << 16), v[1] = __uint_as_float(r.x & 0xffff0000u);
+    v[2] = __uint_as_float(r.y << 16), v[3] = __uint_as_float(r.y & 0xffff0000u);
+  }
+};
+template <>
+struct Quad<float> {
+  u32x4_t r;
+  __device__ __forceinline__ void load(const float* p) { r = ld16(p); }
+  __device__ __forceinline__ void unpack(float (&v)[4]) const {
+    v[0] = __uint_as_float(r.x), v[1] = __uint_as_float(r.y), v[2] = __uint_as_float(r.z), v[3] = __uint_as_float(r.w);
+  }
+};
 
 template <typename St, int N, int JT>
 __global__ __launch_bounds__(256) void k_p1_bwd_wgrad(int64_t T, int d, const St* __restrict__ src, int64_t stride,
-                                                      int S, int j0, const float* __restrict__ coef, int64_t tpr,
+                                                      int S, const float* __restrict__ coef, int64_t tpr,
                                                       int64_t ranges, float* __restrict__ part) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int C = d >> 3;
-  const int ngroups = (C + 63) >> 6;
+  const int Q = d >> 2;                 // quads of channels
+  const int ngroups = (Q + 63) >> 6;
   const int grp = wid % ngroups;
   const int64_t range = wid / ngroups;
   const int64_t t0 = range * tpr;
   const int64_t t1 = t0 + tpr < T ? t0 + tpr : T;
   const int c0 = grp * 64 + lane;
-  const int c = c0 < C ? c0 : C - 1;
-  float acc[JT][8];
+  const int c = c0 < Q ? c0 : Q - 1;
+  float acc[JT][4];
 #pragma unroll
-  for (int q = 0; q < JT; ++q) zero8(acc[q]);
-  // the next token's source chunks load while this token's are used
-  Chunk<St> ua[N], ub[N];
-  auto fetch = [&](Chunk<St>(&u)[N], int64_t t) {
+  for (int q = 0; q < JT; ++q) acc[q][0] = acc[q][1] = acc[q][2] = acc[q][3] = 0.f;
+  Quad<St> ua[N], ub[N];
+  auto fetch = [&](Quad<St>(&u)[N], int64_t t) {
     const int64_t tc = t < T ? t : T - 1;
 #pragma unroll
-    for (int i = 0; i < N; ++i) u[i].load(src + i * stride + tc * d + c * 8);
+    for (int i = 0; i < N; ++i) u[i].load(src + i * stride + tc * d + c * 4);
   };
-  auto use = [&](const Chunk<St>(&u)[N], int64_t t) {
-    const float* cf = coef + t * S * N;
+  // the table holds JT (S rounded up to 8) sites per token, zeros past S
+  auto use = [&](const Quad<St>(&u)[N], int64_t t) {
+    const float* cf = coef + t * JT * N;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      float ue[8];
+      float ue[4];
       u[i].unpack(ue);
 #pragma unroll
       for (int q = 0; q < JT; ++q) {
-        const int j = j0 + q;
-        if (j < S) {
-          const float b = cf[j * N + i];
+        const float b = cf[q * N + i];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(b, ue[e], acc[q][e]);
-        }
+        for (int e = 0; e < 4; ++e) acc[q][e] = fmaf(b, ue[e], acc[q][e]);
       }
     }
   };
@@ -1279,11 +1302,13 @@ __global__ __launch_bounds__(256) void k_p1_bwd_wgrad(int64_t T, int d, const St
   }
   // every range stores its sums, zeros when it holds no token (the
   // reduction reads all ranges)
-  if (c0 < C && range < ranges) {
+  if (c0 < Q && range < ranges) {
 #pragma unroll
     for (int q = 0; q < JT; ++q) {
-      const int j = j0 + q;
-      if (j < S) out8(part + (range * S + j) * (int64_t)d + c * 8, acc[q]);
+      if (q < S) {
+        float* o = part + (range * S + q) * (int64_t)d + c * 4;
+        *reinterpret_cast<float4*>(o) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+      }
     }
   }
 }
@@ -1306,7 +1331,7 @@ __global__ __launch_bounds__(256) void k_p1_bwd_wgrad_reduce(int64_t ranges, int
 // Token ranges of the weight-gradient pass (a fixed count, so the
 // workspace size and the summation order do not depend on the device).
 int64_t p1_backward_ranges(int d) {
-  const int ngroups = ((d >> 3) + 63) >> 6;
+  const int ngroups = ((d >> 2) + 63) >> 6;
   return (kWgradWaves + ngroups - 1) / ngroups;
 }
 
@@ -1324,14 +1349,14 @@ static hipError_t run_p1b_main(int64_t T, int d, const void* src, int64_t stride
 }
 
 template <typename St, int N, int JT>
-static hipError_t run_p1b_wgrad(int64_t T, int d, const void* src, int64_t stride, int S, int j0, const float* coef,
+static hipError_t run_p1b_wgrad(int64_t T, int d, const void* src, int64_t stride, int S, const float* coef,
                                 float* part, hipStream_t stream) {
   const int64_t ranges = p1_backward_ranges(d);
-  const int ngroups = ((d >> 3) + 63) >> 6;
+  const int ngroups = ((d >> 2) + 63) >> 6;
   const int64_t tpr = (T + ranges - 1) / ranges;
   const int64_t waves = ranges * ngroups;
   hipLaunchKernelGGL((k_p1_bwd_wgrad<St, N, JT>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, T, d,
-                     static_cast<const St*>(src), stride, S, j0, coef, tpr, ranges, part);
+                     static_cast<const St*>(src), stride, S, coef, tpr, ranges, part);
   return hipGetLastError();
 }
 
@@ -1342,7 +1367,7 @@ static hipError_t run_p1b(int64_t T, int d, const void* src, int64_t stride, int
                           hipStream_t stream) {
   // workspace: coefficients [T][S][N], folded queries [S][d], range sums
   float* coef = ws;
-  float* q = coef + T * (int64_t)S * N;
+  float* q = coef + T * (int64_t)((S + 7) & ~7) * N;
   float* part = q + (int64_t)S * d;
   const int64_t nq = (int64_t)S * d;
   hipLaunchKernelGGL(k_fold_queries, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, stream, nq, w, kg, q);
@@ -1362,13 +1387,15 @@ static hipError_t run_p1b(int64_t T, int d, const void* src, int64_t stride, int
                                coef, stream);
   }
   if (e != hipSuccess) return e;
+  // (the coefficient table has (S rounded up to 8) sites per token)
   if (S <= 8) {
-    e = run_p1b_wgrad<St, N, 8>(T, d, src, stride, S, 0, coef, part, stream);
+    e = run_p1b_wgrad<St, N, 8>(T, d, src, stride, S, coef, part, stream);
   } else if (S <= 16) {
-    e = run_p1b_wgrad<St, N, 16>(T, d, src, stride, S, 0, coef, part, stream);
+    e = run_p1b_wgrad<St, N, 16>(T, d, src, stride, S, coef, part, stream);
+  } else if (S <= 24) {
+    e = run_p1b_wgrad<St, N, 24>(T, d, src, stride, S, coef, part, stream);
   } else {
-    e = run_p1b_wgrad<St, N, 16>(T, d, src, stride, S, 0, coef, part, stream);
-    if (e == hipSuccess) e = run_p1b_wgrad<St, N, 16>(T, d, src, stride, S, 16, coef, part, stream);
+    e = run_p1b_wgrad<St, N, 32>(T, d, src, stride, S, coef, part, stream);
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_p1_bwd_wgrad_reduce, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, stream,
