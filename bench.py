@@ -144,6 +144,61 @@ def _time(fn, steps: int) -> float:
     return (time.perf_counter() - t0) / steps
 
 
+def backward_report(dev, steps: int):
+    """Backward through the whole block structure of the 16K chunk
+    (training): one training forward keeps the phase-1 outputs and partial
+    sums, then ``max(2, steps // 4)`` backward passes are timed.  The
+    synthetic upstream gradient of sublayer l's input is another sublayer's
+    output row (a model's sublayer backward would produce it from dL/dv_l)."""
+    import torch
+    import synth
+    import transformer_depth_wise_amd as tdw
+
+    w = synth.WORKLOADS["prefill_chunk_bf16"]
+    prm = synth.params(w, dev)
+    scales = synth.sublayer_scales(w)
+    st = tdw.BlockAttnRes(w.T, w.d, w.block_sizes, w.torch_dtype, n_given=w.n_given, eps=w.eps, device=dev,
+                          final_site=w.final_site, training=True)
+    st.reps[0].copy_(synth.embedding(w, 0, w.T, dev))
+    v = [synth.sublayer_output(w, l + 1, 0, w.T, dev, scales) for l in range(w.L)]
+    st.forward(prm, lambda l, x: v[l])
+    dx_for = lambda l, dv: v[(l + 1) % w.L]  # noqa: E731
+    recs = []
+    stream = torch.cuda.current_stream()
+
+    def instrument(kind, begin):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        if begin:
+            recs.append([kind, e, None])
+        else:
+            recs[-1][2] = e
+
+    st.backward(prm, dx_for, dh_final=v[0])
+    nb = max(2, steps // 4)
+    sec = _time(lambda k: st.backward(prm, dx_for, dh_final=v[0], instrument=instrument), nb)
+    plan = st.plan_backward()
+    b = sum(x.bytes for x in plan)
+    kinds = {}
+    for kind, e0, e1 in recs:
+        kinds.setdefault(kind, [0.0, 0])
+        kinds[kind][0] += e0.elapsed_time(e1) / nb
+        kinds[kind][1] += 1
+    kb = {}
+    for x in plan:
+        kb[x.kind] = kb.get(x.kind, 0) + x.bytes
+    out = {
+        "config": {"T": w.T, "d": w.d, "blocks": list(w.block_sizes), "final_site": w.final_site},
+        "ms_per_step": round(sec * 1e3, 4), "value": round(w.T * w.L / sec, 1), "unit": "token-sublayers/s",
+        "hbm_gbps": round(b / sec / 1e9, 1), "bytes_per_step": b,
+        "kernels": {k: {"ms_per_step": round(ms, 4), "launches_per_step": c // nb,
+                        "gbps": round(kb[k] / (ms * 1e-3) / 1e9, 1)} for k, (ms, c) in kinds.items()},
+        "note": "backward only (the training forward that keeps its activations is not timed here)"}
+    del st, v
+    torch.cuda.empty_cache()
+    return out
+
+
 def other_workloads(dev, steps: int):
     """Shorter measurements of the other hot-path shapes, each pass over
     resident inputs: the decode-shaped block step (eager launches and one
@@ -275,53 +330,7 @@ def other_workloads(dev, steps: int):
     del sts, subs
     torch.cuda.empty_cache()
 
-    # backward through the whole block structure of the 16K chunk (training):
-    # one training forward keeps the phase-1 outputs and partial sums, then
-    # the backward is timed; the synthetic upstream gradient of sublayer l's
-    # input is another sublayer's output row (a model's sublayer backward
-    # would produce it from dL/dv_l)
-    w = synth.WORKLOADS["prefill_chunk_bf16"]
-    prm = synth.params(w, dev)
-    scales = synth.sublayer_scales(w)
-    st = tdw.BlockAttnRes(w.T, w.d, w.block_sizes, w.torch_dtype, n_given=w.n_given, eps=w.eps, device=dev,
-                          final_site=w.final_site, training=True)
-    st.reps[0].copy_(synth.embedding(w, 0, w.T, dev))
-    v = [synth.sublayer_output(w, l + 1, 0, w.T, dev, scales) for l in range(w.L)]
-    st.forward(prm, lambda l, x: v[l])
-    dx_for = lambda l, dv: v[(l + 1) % w.L]  # noqa: E731
-    recs = []
-    stream = torch.cuda.current_stream()
-
-    def instrument(kind, begin):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)
-        if begin:
-            recs.append([kind, e, None])
-        else:
-            recs[-1][2] = e
-
-    st.backward(prm, dx_for, dh_final=v[0])
-    nb = max(2, steps // 4)
-    sec = _time(lambda k: st.backward(prm, dx_for, dh_final=v[0], instrument=instrument), nb)
-    plan = st.plan_backward()
-    b = sum(x.bytes for x in plan)
-    kinds = {}
-    for kind, e0, e1 in recs:
-        kinds.setdefault(kind, [0.0, 0])
-        kinds[kind][0] += e0.elapsed_time(e1) / nb
-        kinds[kind][1] += 1
-    kb = {}
-    for x in plan:
-        kb[x.kind] = kb.get(x.kind, 0) + x.bytes
-    res["block_backward_prefill_chunk"] = {
-        "config": {"T": w.T, "d": w.d, "blocks": list(w.block_sizes), "final_site": w.final_site},
-        "ms_per_step": round(sec * 1e3, 4), "value": round(w.T * w.L / sec, 1), "unit": "token-sublayers/s",
-        "hbm_gbps": round(b / sec / 1e9, 1), "bytes_per_step": b,
-        "kernels": {k: {"ms_per_step": round(ms, 4), "launches_per_step": c // nb,
-                        "gbps": round(kb[k] / (ms * 1e-3) / 1e9, 1)} for k, (ms, c) in kinds.items()},
-        "note": "backward only (the training forward that keeps its activations is not timed here)"}
-    del st, v
-    torch.cuda.empty_cache()
+    res["block_backward_prefill_chunk"] = backward_report(dev, steps)
     return res
 
 
@@ -334,6 +343,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the decode / Full / per-GPU-share workloads")
+    ap.add_argument("--backward", action="store_true",
+                    help="time only the backward through the 16K chunk's block structure (one JSON line)")
     ap.add_argument("--probe", choices=["copy"], default=None,
                     help="run only a plain device copy of known size (counter calibration)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -364,6 +375,10 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"probe": "copy", "bytes_read_per_dispatch": a.numel() * 2,
                           "bytes_written_per_dispatch": b.numel() * 2, "dispatches": 4}), flush=True)
+        return 0
+    if args.backward:
+        print(json.dumps({"metric": "AttnRes backward token-sublayers/s (block structure, 16K chunk)",
+                          **backward_report(dev, args.steps)}), flush=True)
         return 0
     w = synth.WORKLOADS[args.workload]
     if w.chunk:
