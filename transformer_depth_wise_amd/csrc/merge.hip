@@ -309,10 +309,12 @@ static hipError_t run_merge(int64_t T, int d, const void* o1, const float* lse1,
   constexpr int TPW = 256 / TEAM;
   const int64_t tiles = (T + TPW - 1) / TPW;
   // persistent: 2 workgroups per CU; 1 for the launches that read two
-  // previous outputs and store the partial (two write streams besides four
-  // read streams: fewer concurrent streams kept HBM at 5.4 instead of
-  // 5.1 TB/s there, while the lighter launches were faster with 2)
-  const int64_t cap = (int64_t)device_cu_count() * (vprev2 ? 1 : 2);
+  // previous outputs and store the partial, over long token ranges (two
+  // write streams besides four read streams: fewer concurrent streams kept
+  // HBM at 5.4 instead of 5.1 TB/s at 16K tokens, while the lighter launches,
+  // and every launch at 2K tokens, were faster with 2)
+  const int64_t cus = device_cu_count();
+  const int64_t cap = cus * ((vprev2 && T >= 32 * cus) ? 1 : 2);
   const dim3 grid((unsigned)(tiles < cap ? tiles : cap));
   const size_t lds = x_out ? sizeof(float) * (size_t)d : 0;  // PreNorm gain (at most 64 KiB)
   const St* o = static_cast<const St*>(o1);
