@@ -35,6 +35,9 @@ BWD_CASES = [
     (200, 1032, (3, 5, 2), 1, "bf16", True),  # ragged chunk groups
     (96, 2048, (6,), 3, "bf16", True),
     (40, 7168, (5, 4), 2, "bf16", True),
+    (6, 16384, (3, 2), 1, "bf16", True),      # widest rows: 1024-thread teams
+    (7, 10240, (2, 2), 0, "f32", True),       # fp32 rows past 8192
+    (24, 256, (2, 2, 2, 2), 11, "bf16", True),  # up to 15 block sources
 ]
 
 
