@@ -33,9 +33,10 @@
  *    Parameters (w, key_gain, prenorm_gain) are fp32 [.., d] rows.
  *  - Layout: row-major, token-major rows of d channels.  A row set [T][d] is
  *    contiguous.  Multi-source inputs are slabs src + i*src_stride (elements).
- *  - d must be a multiple of 8 and at most 16384; strides multiples of 8;
- *    row and parameter pointers 16-byte aligned, statistics ([T] / [S][T]
- *    fp32) pointers 4-byte aligned.
+ *  - d must be a multiple of 8 and at most 16384; strides multiples of 8,
+ *    in [0, ATTNRES_MAX_STRIDE]; 0 <= T <= ATTNRES_MAX_T (anything else is
+ *    ATTNRES_EINVAL); row and parameter pointers 16-byte aligned, statistics
+ *    ([T] / [S][T] fp32) pointers 4-byte aligned.
  *  - All pointers except `stream` are device pointers owned by the caller.
  *    The library allocates nothing and keeps no state beyond loaded kernels.
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Calls
@@ -76,6 +77,9 @@ typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1, ATTNRES_P24 = 2 } attnres_dtyp
 #define ATTNRES_MAX_SOURCES 32          /* attnres_full / phase 1 with S == 1 */
 #define ATTNRES_MAX_SOURCES_MULTI 16    /* phase 1 with S >= 2 */
 #define ATTNRES_MAX_GROUP_SOURCES 16    /* attnres_phase2_merge_multi */
+#define ATTNRES_MAX_T 2147483647LL      /* tokens per call */
+#define ATTNRES_MAX_QUERIES 4096        /* S of phase 1 */
+#define ATTNRES_MAX_STRIDE (1LL << 40)  /* slab strides, in elements; strides are >= 0 */
 
 /*
  * Phase 1 of a block ("Attention Residuals" notes, section 10, first phase;
@@ -91,7 +95,7 @@ typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1, ATTNRES_P24 = 2 } attnres_dtyp
  *   source row itself in phase 2).  m_out, lse_out: [S][T] fp32 (m_out may
  *   be NULL).
  * Limits: 1 <= n_src <= ATTNRES_MAX_SOURCES_MULTI when S >= 2, <=
- * ATTNRES_MAX_SOURCES when S == 1; S >= 1 (queries are processed 32 at a
+ * ATTNRES_MAX_SOURCES when S == 1; 1 <= S <= ATTNRES_MAX_QUERIES (queries are processed 32 at a
  * time; each group of 32 reads the sources once for the scores and once for
  * the outputs).
  * workspace: caller-owned device memory of at least

@@ -87,6 +87,11 @@ def test_phase1_validation(lib):
     assert phase1(lib, lse=16 * A + 8) == EALIAS      # stats inside the output
     assert phase1(lib, lse=24 * A + 2) == EALIGN
     assert phase1(lib, eps=-1.0) == EINVAL
+    assert phase1(lib, T=1 << 31) == EINVAL              # more than ATTNRES_MAX_T tokens
+    assert phase1(lib, S=4097) == EINVAL                 # more than ATTNRES_MAX_QUERIES
+    assert phase1(lib, n=1, stride=-8) == EINVAL         # strides are >= 0 even where unused
+    assert phase1(lib, stride=(1 << 40) + 8) == EINVAL   # beyond ATTNRES_MAX_STRIDE
+    assert lib.attnres_phase1_workspace_bytes(1 << 31, 64, 2, 4) == -1
     assert phase1(lib, ws=None) == EINVAL                # S >= 2 needs the workspace
     assert phase1(lib, ws_bytes=100) == EINVAL           # too small
     assert phase1(lib, ws=16 * A + 64) == EALIAS         # workspace inside the output
@@ -192,6 +197,9 @@ def test_phase1_backward_validation(lib):
     assert p1b(lib, dk=32 * A + 64, kg=48 * A) == EALIAS   # the two weight gradients overlap
     assert p1b(lib, ws=24 * A + 64) == EALIAS
     assert p1b(lib, T=0) == 0
+    assert p1b(lib, gstride=1 << 41) == EINVAL
+    assert lib.attnres_phase1_backward_workspace_bytes(1 << 31, 64, 3, 4) == -1
+    assert lib.attnres_phase2_backward_workspace_bytes(1 << 31, 64) == -1
     # coefficients T x (S rounded up to 8) x n, folded queries S x d, per-range sums (2048 waves over
     # d / 256 groups)
     assert lib.attnres_phase1_backward_workspace_bytes(1024, 64, 3, 4) == 4 * (1024 * 8 * 3 + 4 * 64 + 2048 * 4 * 64)
@@ -228,6 +236,8 @@ def test_merge_validation(lib):
     # a P24 partial spans 3 bytes per element: the low-byte plane starts 1024 x 64 x 2 bytes in
     assert merge(lib, v=7 * A + 1024 * 64 * 2, pin=5 * A, pdt=2, pout=7 * A, podt=2) == EALIAS
     assert merge(lib, T=0) == 0
+    assert merge(lib, T=-1) == EINVAL
+    assert merge(lib, T=1 << 31) == EINVAL
     assert merge(lib, T=0, o=None, lse=None, x=None) == 0               # empty: pointers unused
 
 
@@ -241,6 +251,8 @@ def test_full_and_accumulate_validation(lib):
     assert f(h=A + 128) == EALIAS
     assert f(d=4) == EALIGN
     assert f(T=0) == 0
+    assert f(T=1 << 40) == EINVAL
+    assert f(stride=-64) == EINVAL
     acc = lambda **k: checked(lib.attnres_block_accumulate(k.get("dt", 1), k.get("T", 64), k.get("d", 64), k.get("pdt", 0),
                                                    p(k.get("pin")), p(k.get("v2")), p(k.get("v", A)),
                                                    p(k.get("out", 2 * A)), None))
@@ -248,6 +260,7 @@ def test_full_and_accumulate_validation(lib):
     assert acc(out=A) == EALIAS
     assert acc(pin=2 * A, pdt=0) == EALIAS          # in place only with the same dtype
     assert acc(T=0, v=None, out=None) == 0
+    assert acc(T=1 << 31, v=None, out=None) == EINVAL
     assert acc(dt=3) == EDTYPE
     assert acc(dt=2) == EDTYPE                      # P24 only for the partial
     assert acc(T=0, pin=5 * A, pdt=2) == 0
@@ -273,6 +286,7 @@ def test_merge_multi_validation(lib):
     assert mm(dt=2) == EDTYPE
     assert mm(d=12) == EALIGN
     assert mm(T=0) == 0
+    assert mm(stride=1 << 41) == EINVAL
     assert mm(T=0, n=0, src=None, w=None, o=None, lse=None, x=None) == 0
 
 
@@ -299,6 +313,8 @@ def test_site_backward_validation(lib):
     assert sb(stride=64 * 64 + 4) == EALIGN
     assert sb(dt=2) == EDTYPE
     assert sb(T=0, src=None, dx=None, dsrc=None, dw=None, ws=None) == 0
+    assert sb(dstride=-64) == EINVAL
+    assert lib.attnres_site_backward_workspace_bytes(1 << 31, 64) == -1
 
 
 def test_status_strings(lib):

@@ -21,6 +21,9 @@ ATTNRES_MAX_D = 16384
 ATTNRES_MAX_SOURCES = 32
 ATTNRES_MAX_SOURCES_MULTI = 16
 ATTNRES_MAX_GROUP_SOURCES = 16
+ATTNRES_MAX_T = 2147483647
+ATTNRES_MAX_QUERIES = 4096
+ATTNRES_MAX_STRIDE = 1 << 40
 
 EXPORTED = ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_workspace_bytes", "attnres_phase2_merge", "attnres_phase2_merge_multi",
             "attnres_full", "attnres_block_accumulate", "attnres_site_backward", "attnres_site_backward_workspace_bytes",

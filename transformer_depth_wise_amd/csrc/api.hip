@@ -60,6 +60,15 @@ attnres_status_t check_d(int64_t d) {
   return ATTNRES_OK;
 }
 
+// token count and slab strides in range, so that every byte extent below
+// fits in int64 (T * d * 4 < 2^47, S * T * d * 4 < 2^59, strides < 2^45 bytes)
+bool extent_ok(int64_t T, std::initializer_list<int64_t> strides = {}) {
+  if (T < 0 || T > ATTNRES_MAX_T) return false;
+  for (int64_t s : strides)
+    if (s < 0 || s > ATTNRES_MAX_STRIDE) return false;
+  return true;
+}
+
 attnres_status_t hip_status(hipError_t e) { return e == hipSuccess ? ATTNRES_OK : ATTNRES_EHIP; }
 
 // all non-null row pointers 16-byte aligned, statistics pointers 4-byte aligned
@@ -89,7 +98,8 @@ const char* attnres_status_string(attnres_status_t status) {
 }
 
 int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int64_t S) {
-  if (T < 0 || n_src < 1 || S < 1 || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
+  if (!extent_ok(T) || n_src < 1 || S < 1 || S > ATTNRES_MAX_QUERIES || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0)
+    return -1;
   if (n_src > ATTNRES_MAX_SOURCES_MULTI) return S == 1 ? 0 : -1;
   // packed queries (32 rows x 4 bytes x d rounded up to 128) + softmax
   // weights (T x n x min(S, 32) x 4 bytes)
@@ -106,9 +116,9 @@ static attnres_status_t phase1_impl(attnres_dtype_t dt, const void* src, int64_t
   if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
-  if (T < 0 || S < 1 || n_src < 1) return ATTNRES_EINVAL;
+  if (!extent_ok(T, {src_stride}) || S < 1 || S > ATTNRES_MAX_QUERIES || n_src < 1) return ATTNRES_EINVAL;
   if (n_src > (S == 1 && !x0 ? ATTNRES_MAX_SOURCES : ATTNRES_MAX_SOURCES_MULTI)) return ATTNRES_EINVAL;
-  if (T > (int64_t)1 << 40 || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (!(eps >= 0.f)) return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!src || !w || !lse_out) return ATTNRES_EINVAL;
   if (x0 && !out && n_src > 1) return ATTNRES_EINVAL;
@@ -189,7 +199,7 @@ attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, 
   if (partial_out_dt != ATTNRES_F32 && partial_out_dt != ATTNRES_P24) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
-  if (T < 0 || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (!extent_ok(T) || !(eps >= 0.f)) return ATTNRES_EINVAL;
   if (!sublayer_prev && (partial_in || partial_out || sublayer_prev2)) return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!p1_out || !p1_lse || (!h_out && !x_out)) return ATTNRES_EINVAL;
@@ -234,7 +244,8 @@ attnres_status_t attnres_phase2_merge_multi(attnres_dtype_t dt, int64_t T, int64
   if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
-  if (T < 0 || n_src < 0 || n_src > ATTNRES_MAX_GROUP_SOURCES || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (!extent_ok(T, {src_stride}) || n_src < 0 || n_src > ATTNRES_MAX_GROUP_SOURCES || !(eps >= 0.f))
+    return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!p1_out || !p1_lse || (!h_out && !x_out)) return ATTNRES_EINVAL;
   if (n_src > 0 && (!src || !w)) return ATTNRES_EINVAL;
@@ -260,7 +271,7 @@ attnres_status_t attnres_phase2_merge_multi(attnres_dtype_t dt, int64_t T, int64
 }
 
 int64_t attnres_site_backward_workspace_bytes(int64_t T, int64_t d) {
-  if (T < 0 || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
+  if (!extent_ok(T) || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
   if (T == 0) return 0;
   return attnres::backward_slots(T, (int)d) * 2 * d * (int64_t)sizeof(float);
 }
@@ -274,7 +285,8 @@ attnres_status_t attnres_site_backward(attnres_dtype_t dt, const void* src, int6
   if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
-  if (T < 0 || n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (!extent_ok(T, {src_stride, dsrc_stride}) || n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || !(eps >= 0.f))
+    return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!src || !w || !dx || !dsrc || !dw) return ATTNRES_EINVAL;
   if (n_src > 1 && (src_stride < T * d || dsrc_stride < T * d)) return ATTNRES_EINVAL;
@@ -309,7 +321,7 @@ attnres_status_t attnres_site_backward(attnres_dtype_t dt, const void* src, int6
 }
 
 int64_t attnres_phase2_backward_workspace_bytes(int64_t T, int64_t d) {
-  if (T < 0 || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
+  if (!extent_ok(T) || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
   if (T == 0) return 0;
   return attnres::p2_backward_slots(T, (int)d) * 2 * d * (int64_t)sizeof(float);
 }
@@ -324,7 +336,7 @@ attnres_status_t attnres_phase2_backward(attnres_dtype_t dt, int64_t T, int64_t 
   if (!dtype_ok(dt) || !partial_ok(partial_dt, dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
-  if (T < 0 || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (!extent_ok(T) || !(eps >= 0.f)) return ATTNRES_EINVAL;
   if (!sublayer_prev && (partial_in || sublayer_prev2)) return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!p1_out || !dx || !g_out || !c_out || !gp_out || !w) return ATTNRES_EINVAL;
@@ -364,7 +376,7 @@ attnres_status_t attnres_phase2_backward(attnres_dtype_t dt, int64_t T, int64_t 
 }
 
 int64_t attnres_phase1_backward_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int64_t S) {
-  if (T < 0 || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
+  if (!extent_ok(T) || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
   if (n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || S < 1 || S > 32) return -1;
   if (T == 0) return 0;
   // coefficients [T][S rounded up to 8][n], folded queries [S][d],
@@ -382,7 +394,8 @@ attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, const void* src, in
   if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
-  if (T < 0 || n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || S < 1 || S > 32 || !(eps >= 0.f))
+  if (!extent_ok(T, {src_stride, g_stride, dsrc_stride}) || n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || S < 1 ||
+      S > 32 || !(eps >= 0.f))
     return ATTNRES_EINVAL;
   if (gp_in == nullptr && c_in != nullptr) return ATTNRES_EINVAL;  // a partial weight needs its G.p
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
@@ -422,7 +435,8 @@ attnres_status_t attnres_full(attnres_dtype_t dt, const void* src, int64_t n_src
   if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
-  if (T < 0 || n_src < 1 || n_src > ATTNRES_MAX_SOURCES || !(eps >= 0.f)) return ATTNRES_EINVAL;
+  if (!extent_ok(T, {src_stride}) || n_src < 1 || n_src > ATTNRES_MAX_SOURCES || !(eps >= 0.f))
+    return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!src || !w || (!h_out && !x_out)) return ATTNRES_EINVAL;
   if (n_src > 1 && src_stride < T * d) return ATTNRES_EINVAL;
@@ -453,7 +467,7 @@ attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t
   if (!dtype_ok(dt) || !partial_ok(partial_dt, dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
-  if (T < 0) return ATTNRES_EINVAL;
+  if (!extent_ok(T)) return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!v || !out) return ATTNRES_EINVAL;
   st = check_align({partial_in, v2, v, out});
