@@ -54,6 +54,33 @@ def _esize(dt: torch.dtype) -> int:
     return 4 if dt == torch.float32 else 2
 
 
+def _check_params(params: Dict[str, torch.Tensor], d: int, sites: int, norms: int, device: torch.device) -> None:
+    """Checked once per pass, so that the per-launch calls can skip the
+    binding's own checks: w, g fp32 [>= sites, d]; gamma fp32 [>= norms, d];
+    contiguous; on the pass's device, which must be the current one."""
+    for name, rows, required in (("w", sites, True), ("g", sites, False), ("gamma", norms, False)):
+        t = params.get(name)
+        if t is None:
+            if required:
+                raise ValueError("params['%s'] is required" % name)
+            continue
+        if (t.dtype != torch.float32 or t.dim() != 2 or t.shape[0] < rows or t.shape[1] != d or
+                not t.is_contiguous()):
+            raise ValueError("params['%s'] must be a contiguous fp32 [>= %d, %d] tensor, got %s %s"
+                             % (name, rows, d, t.dtype, tuple(t.shape)))
+        _lib._on_device(t)
+    if device.index is not None and torch.cuda.current_device() != device.index:
+        raise ValueError("the pass's buffers live on %s, but the current device is cuda:%d"
+                         % (device, torch.cuda.current_device()))
+
+
+def _checked_rows(t: torch.Tensor, name: str, T: int, d: int, dtype: torch.dtype) -> torch.Tensor:
+    """A caller-supplied [T, d] row set (a sublayer's output or gradient)."""
+    _lib._rows(t, name, T, d, dtype)
+    _lib._on_device(t)
+    return t
+
+
 class BlockAttnRes:
     """Block AttnRes forward over T tokens of width d on the current GPU.
 
@@ -91,6 +118,7 @@ class BlockAttnRes:
                              % _lib.ATTNRES_MAX_SOURCES_MULTI)
         smax = max(self.block_sizes) if self.block_sizes else 1
         self.reps = torch.empty((n_reps, T, d), dtype=dtype, device=dev)
+        self.device = dev = self.reps.device  # with its index
         self.o1 = torch.empty((smax, T, d), dtype=dtype, device=dev)
         self.m1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
         self.lse1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
@@ -196,6 +224,7 @@ class BlockAttnRes:
         the block.  ``hook(site, x=, h=, o1=, lse1=, m1=)`` is called after
         each phase-2 launch.  ``instrument(kind, begin)`` is called just
         before (begin=True) and after (begin=False) every launch."""
+        _check_params(params, self.d, self.L + (1 if self.final_site else 0), self.L, self.device)
         w, g, gam = params["w"], params.get("g"), params.get("gamma")
         eps = self.eps
         n_done = 1 + self.n_given
@@ -215,11 +244,11 @@ class BlockAttnRes:
                 attnres_phase1_first_prenorm(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S],
                                              eps, None if single else self.o1[:S], self.m1[:S], self.lse1[:S],
                                              None if gam is None else gam[l0], self.x[l0 % nx], self.h,
-                                             self.workspace, stream=stream)
+                                             self.workspace, stream=stream, check=False)
             else:
                 attnres_phase1(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S], eps,
                                o1 if (self.training or not single) else None, self.m1[:S], lse1,
-                               self.workspace, stream=stream)
+                               self.workspace, stream=stream, check=False)
             mark("phase1", False)
             # the two latest outputs of the block stay alive (prev2, prev)
             prev2 = prev = None
@@ -252,21 +281,22 @@ class BlockAttnRes:
                 else:
                     mark("phase2", True)
                     attnres_phase2_merge(o, lse1[j], pin, prev, pout, w[site], kg, pg, eps,
-                                         self.h, x, stream=stream, sublayer_prev2=v2)
+                                         self.h, x, stream=stream, sublayer_prev2=v2, check=False)
                     mark("phase2", False)
                 if hook is not None:
                     hook(site, x=x, h=self.h, o1=o, lse1=lse1[j], m1=self.m1[j])
-                prev2, prev = prev, sublayer(site, x)
+                prev2, prev = prev, _checked_rows(sublayer(site, x), "output of sublayer %d" % site, self.T,
+                                                  self.d, self.dtype)
             mark("accumulate", True)
             p_last = self.partial if slots is None else (slots[-1] if slots else None)
             if S == 1:
-                attnres_block_accumulate(None, prev, self.reps[n_done], stream=stream)
+                attnres_block_accumulate(None, prev, self.reps[n_done], stream=stream, check=False)
             elif S == 2:
-                attnres_block_accumulate(None, prev, self.reps[n_done], stream=stream, v2=prev2)
+                attnres_block_accumulate(None, prev, self.reps[n_done], stream=stream, v2=prev2, check=False)
             elif S % 2:
-                attnres_block_accumulate(p_last, prev, self.reps[n_done], stream=stream)
+                attnres_block_accumulate(p_last, prev, self.reps[n_done], stream=stream, check=False)
             else:
-                attnres_block_accumulate(p_last, prev, self.reps[n_done], stream=stream, v2=prev2)
+                attnres_block_accumulate(p_last, prev, self.reps[n_done], stream=stream, v2=prev2, check=False)
             mark("accumulate", False)
             n_done += 1
             l0 += S
@@ -274,7 +304,7 @@ class BlockAttnRes:
             mark("final", True)
             attnres_phase1(self.reps, n_done, w[self.L:self.L + 1], None if g is None else g[self.L:self.L + 1],
                            eps, self.h_final.unsqueeze(0), None, self.lse_final.unsqueeze(0), self.workspace,
-                           stream=stream)
+                           stream=stream, check=False)
             mark("final", False)
         return self.h_final
 
@@ -330,6 +360,9 @@ class BlockAttnRes:
             raise RuntimeError("backward needs a forward built with training=True")
         if self.final_site and dh_final is None:
             raise ValueError("dh_final is required with the final aggregation site")
+        _check_params(params, self.d, self.L + (1 if self.final_site else 0), self.L, self.device)
+        if self.final_site:
+            _checked_rows(dh_final, "dh_final", self.T, self.d, self.dtype)
         w, g, gam = params["w"], params.get("g"), params.get("gamma")
         T, d, eps, dev = self.T, self.d, self.eps, self.device
         mark = instrument if instrument is not None else (lambda kind, begin: None)
@@ -352,7 +385,7 @@ class BlockAttnRes:
             attnres_phase1_backward(self.reps, n_reps, w[self.L:self.L + 1],
                                     None if g is None else g[self.L:self.L + 1], eps, dh_final.unsqueeze(0), None,
                                     None, dB, dw[self.L:self.L + 1], None if g is None else dg[self.L:self.L + 1],
-                                    ws, accumulate=False, stream=stream)
+                                    ws, accumulate=False, stream=stream, check=False)
             mark("final_backward", False)
         else:
             dB = torch.zeros((n_reps, T, d), dtype=torch.float32, device=dev)
@@ -366,19 +399,19 @@ class BlockAttnRes:
             R = dB[n]
             for j in range(S - 1, -1, -1):
                 l = l0 + j
-                dx = dx_for(l, R)
+                dx = _checked_rows(dx_for(l, R), "dL/dx of sublayer %d" % l, T, d, self.dtype)
                 pin, v2, v = self.recipes[l] if j > 0 else (None, None, None)
                 mark("phase2_backward", True)
                 attnres_phase2_backward(self.o_blocks[b][j], self.lse_blocks[b][j], pin, v, w[l],
                                         None if g is None else g[l], None if gam is None else gam[l], eps, dx,
                                         R if j > 0 else None, G[j], cg[0, j], cg[1, j], dw[l],
                                         None if g is None else dg[l], dgamma[l], ws, sublayer_prev2=v2,
-                                        stream=stream)
+                                        stream=stream, check=False)
                 mark("phase2_backward", False)
             mark("phase1_backward", True)
             attnres_phase1_backward(self.reps, n, w[l0:l0 + S], None if g is None else g[l0:l0 + S], eps, G[:S],
                                     cg[0, :S], cg[1, :S], dB, dw[l0:l0 + S], None if g is None else dg[l0:l0 + S],
-                                    ws, accumulate=True, stream=stream)
+                                    ws, accumulate=True, stream=stream, check=False)
             mark("phase1_backward", False)
             l_end = l0
         return {"demb": dB[0], "dgiven": dB[1:1 + self.n_given], "dw": dw, "dg": dg, "dgamma": dgamma[:self.L]}
@@ -447,6 +480,7 @@ class FullAttnRes:
                 instrument: Optional[Callable[[str, bool], None]] = None) -> torch.Tensor:
         """``hist[0]`` must hold the embedding; ``sublayer(l, x_l)`` writes the
         output of sublayer l (0-based) into ``hist[l + 1]``."""
+        _check_params(params, self.d, self.L + (1 if self.final_site else 0), self.L, self.hist.device)
         w, g, gam = params["w"], params.get("g"), params.get("gamma")
         mark = instrument if instrument is not None else (lambda kind, begin: None)
         if self.group is None:
@@ -454,7 +488,8 @@ class FullAttnRes:
                 x = self.x[l % 2]
                 mark("full", True)
                 attnres_full(self.hist, l + 1, w[l], None if g is None else g[l],
-                             None if gam is None else gam[l], self.eps, self.h, x, self.lse, stream=stream)
+                             None if gam is None else gam[l], self.eps, self.h, x, self.lse, stream=stream,
+                             check=False)
                 mark("full", False)
                 if hook is not None:
                     hook(l, x=x, h=self.h, lse=self.lse)
@@ -470,7 +505,7 @@ class FullAttnRes:
                 attnres_phase1_first_prenorm(self.hist, n, w[g0:g0 + S], None if g is None else g[g0:g0 + S],
                                              self.eps, None if single else self.o1[:S], self.m1[:S],
                                              self.lse1[:S], None if gam is None else gam[g0],
-                                             self.x[g0 % 2], self.h, self.workspace, stream=stream)
+                                             self.x[g0 % 2], self.h, self.workspace, stream=stream, check=False)
                 mark("phase1", False)
                 for j in range(S):
                     l = g0 + j
@@ -480,7 +515,7 @@ class FullAttnRes:
                         mark("phase2", True)
                         attnres_phase2_merge_multi(o, self.lse1[j], self.hist[g0 + 1:g0 + 1 + j], j, w[l],
                                                    None if g is None else g[l], None if gam is None else gam[l],
-                                                   self.eps, self.h, x, stream=stream)
+                                                   self.eps, self.h, x, stream=stream, check=False)
                         mark("phase2", False)
                     if hook is not None:
                         hook(l, x=x, h=self.h, lse=None)
@@ -488,7 +523,7 @@ class FullAttnRes:
         if self.final_site:
             mark("final", True)
             attnres_full(self.hist, self.L + 1, w[self.L], None if g is None else g[self.L], None, self.eps,
-                         self.h_final, None, None, stream=stream)
+                         self.h_final, None, None, stream=stream, check=False)
             mark("final", False)
         return self.h_final
 
