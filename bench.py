@@ -354,7 +354,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the AttnRes aggregation never mixes tokens, so it shards by "
-              "token with no communication; multi-GPU runs are not part of this build (--gpus 1).",
+              "token with no communication; a run over several GPUs is not supported (use --gpus 1).",
               file=sys.stderr)
         return 2
 
