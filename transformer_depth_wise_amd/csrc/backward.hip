@@ -1085,14 +1085,24 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
             }
         }
       };
+      // two-stage ring, ua holding group g at the top of every round.  The
+      // rounds have no exit between a load and its use (an exit there lets
+      // the compiler sink the loads to their use, which then waits for every
+      // load before the dot products), and scheduling barriers keep the next
+      // group's loads ahead of the current group's arithmetic.
       fetch(ua, ga, qa, 0);
-      for (int g = 0; g < ngroups; g += 2) {
-        fetch(ub, gb, qbf, g + 1 < ngroups ? g + 1 : ngroups - 1);
+      int g = 0;
+      for (; g + 2 <= ngroups; g += 2) {
+        fetch(ub, gb, qbf, g + 1);
+        __builtin_amdgcn_sched_barrier(0);
         consume(ua, ga, qa, g);
-        if (g + 1 >= ngroups) break;
+        __builtin_amdgcn_sched_barrier(0);
         fetch(ua, ga, qa, g + 2 < ngroups ? g + 2 : ngroups - 1);
+        __builtin_amdgcn_sched_barrier(0);
         consume(ub, gb, qbf, g + 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      if (g < ngroups) consume(ua, ga, qa, g);
 #pragma unroll
       for (int k = 0; k < QB; ++k) {
         const int j = wv + 8 * (qb + k);
