@@ -1135,6 +1135,173 @@ __global__ __launch_bounds__(256) void k_phase1_single(const St* __restrict__ sr
 }
 
 // ---------------------------------------------------------------------------
+// S == 1 with rows of at most 256 chunks (Full AttnRes one-shot sites, the
+// final aggregation without a workspace): one pass over the sources with an
+// online softmax, so every source row is read once.  A wave owns one token at
+// a time; per batch of BS sources it forms each score (w (.) g).u / r(u) from
+// the row held in registers (DPP wave sums for the dot product and the sum
+// of squares), then rescales the running maximum, normaliser and output by
+// the batch's new maximum -- the log-sum-exp merge of the notes' two-phase
+// scheme, applied batch by batch -- and adds the batch's weighted rows.  The
+// next (token, batch) item's loads are in flight while the current one is
+// used (an exit-free two-stage ring; the last batch's missing sources load
+// the last source again and get weight zero).
+template <typename St, int K1>
+__global__ __launch_bounds__(256) void k_site_online(const St* __restrict__ src, int n, int64_t stride, int64_t T,
+                                                     int d, const float* __restrict__ w,
+                                                     const float* __restrict__ kg,
+                                                     const float* __restrict__ gamma, float eps,
+                                                     St* __restrict__ h_out, St* __restrict__ x_out,
+                                                     float* __restrict__ m_out, float* __restrict__ lse_out) {
+  constexpr int BS = (sizeof(St) == 2 ? 8 : 4) / K1 > 0 ? (sizeof(St) == 2 ? 8 : 4) / K1 : 1;
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const int C = d >> 3;
+  const float inv_d = 1.0f / (float)d;
+  // this lane's chunks of the folded query and of the PreNorm gain (zero /
+  // one past the end of the row)
+  float q[K1][8], gm[K1][8];
+#pragma unroll
+  for (int k = 0; k < K1; ++k) {
+    const int c = lane + 64 * k;
+    if (c < C) {
+      load8(w + c * 8, q[k]);
+      if (kg) {
+        float g8[8];
+        load8(kg + c * 8, g8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[k][e] *= g8[e];
+      }
+    } else {
+      zero8(q[k]);
+    }
+    if (gamma && x_out && c < C) {
+      load8(gamma + c * 8, gm[k]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gm[k][e] = 1.f;
+    }
+  }
+  const int64_t ntok = gw < T ? (T - gw + nw - 1) / nw : 0;  // this wave's tokens
+  const int nb = (n + BS - 1) / BS;
+  const int64_t items = ntok * nb;
+  if (items == 0) return;
+  auto issue = [&](Chunk<St>(&u)[BS][K1], int64_t it) {
+    const int64_t itc = it < items ? it : items - 1;
+    const int64_t tq = itc / nb;
+    const int b = (int)(itc - tq * nb);
+    const int64_t tok = gw + tq * nw;
+#pragma unroll
+    for (int j = 0; j < BS; ++j) {
+      const int i = b * BS + j < n ? b * BS + j : n - 1;
+#pragma unroll
+      for (int k = 0; k < K1; ++k) {
+        const int c0 = lane + 64 * k;
+        u[j][k].load(src + (int64_t)i * stride + tok * d + (c0 < C ? c0 : C - 1) * 8);
+      }
+    }
+  };
+  float m = -INFINITY, l = 0.f;
+  float o[K1][8];
+#pragma unroll
+  for (int k = 0; k < K1; ++k) zero8(o[k]);
+  auto consume = [&](const Chunk<St>(&u)[BS][K1], int64_t it) {
+    const int64_t tq = it / nb;
+    const int b = (int)(it - tq * nb);
+    float v[BS][K1][8], z[BS];
+    float zmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < BS; ++j) {
+      float zp = 0.f, sp = 0.f;
+#pragma unroll
+      for (int k = 0; k < K1; ++k) {
+        u[j][k].unpack(v[j][k]);
+        const bool cok = lane + 64 * k < C;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[j][k][e] = cok ? v[j][k][e] : 0.f;
+          zp = fmaf(q[k][e], v[j][k][e], zp);
+          sp = fmaf(v[j][k][e], v[j][k][e], sp);
+        }
+      }
+      const float zs = wave_sum_dpp(zp) / sqrtf(wave_sum_dpp(sp) * inv_d + eps);
+      z[j] = b * BS + j < n ? zs : -INFINITY;
+      zmax = fmaxf(zmax, z[j]);
+    }
+    if (b == 0) {
+      m = -INFINITY;
+      l = 0.f;
+#pragma unroll
+      for (int k = 0; k < K1; ++k) zero8(o[k]);
+    }
+    const float mn = fmaxf(m, zmax);            // finite: every batch has a source
+    const float sc = m == -INFINITY ? 0.f : expf(m - mn);
+    l *= sc;
+#pragma unroll
+    for (int k = 0; k < K1; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[k][e] *= sc;
+#pragma unroll
+    for (int j = 0; j < BS; ++j) {
+      const float p = expf(z[j] - mn);          // 0 for a missing source
+      l += p;
+#pragma unroll
+      for (int k = 0; k < K1; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[k][e] = fmaf(p, v[j][k][e], o[k][e]);
+    }
+    m = mn;
+    if (b == nb - 1) {
+      const int64_t tok = gw + tq * nw;
+      const float il = 1.0f / l;
+      float ssq = 0.f;
+#pragma unroll
+      for (int k = 0; k < K1; ++k) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o[k][e] *= il;
+          ssq = fmaf(o[k][e], o[k][e], ssq);
+        }
+        const int c = lane + 64 * k;
+        if (h_out && c < C) store8(h_out + tok * d + c * 8, o[k]);
+      }
+      if (x_out) {
+        const float rinv = 1.0f / sqrtf(wave_sum_dpp(ssq) * inv_d + eps);
+#pragma unroll
+        for (int k = 0; k < K1; ++k) {
+          const int c = lane + 64 * k;
+          if (c < C) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = gm[k][e] * (o[k][e] * rinv);
+            store8(x_out + tok * d + c * 8, x);
+          }
+        }
+      }
+      if (lane == 0) {
+        if (m_out) m_out[tok] = m;
+        if (lse_out) lse_out[tok] = m + logf(l);
+      }
+    }
+  };
+  Chunk<St> A[BS][K1], B[BS][K1];
+  issue(A, 0);
+  int64_t it = 0;
+  for (; it + 2 <= items; it += 2) {
+    issue(B, it + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(A, it);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(A, it + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(B, it + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (it < items) consume(A, it);
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 
 // Allow `dynamic` bytes of dynamic LDS when a launch needs more than 64 KiB
@@ -1287,9 +1454,19 @@ template <typename St>
 static hipError_t run_single(const void* src, int n, int64_t stride, int64_t T, int d, const float* w,
                              const float* kg, const float* gamma, float eps, void* h_out, void* x_out,
                              float* m_out, float* lse_out, hipStream_t stream) {
-  const size_t lds = sizeof(float) * (2 * Red<1, kGroup>::kSlot + 16 * kSingleNP + 16);
-  // rows of up to 256 chunks take the wave-per-token output loop
   const int C = d >> 3;
+  if (C <= 256) {
+    // one pass with an online softmax, a wave per token
+    auto k = C <= 64 ? k_site_online<St, 1> : C <= 128 ? k_site_online<St, 2> : k_site_online<St, 4>;
+    int64_t waves = T;
+    const int64_t cap = (int64_t)device_cu_count() * 16;
+    if (waves > cap) waves = cap;
+    hipLaunchKernelGGL(k, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, static_cast<const St*>(src), n,
+                       stride, T, d, w, kg, gamma, eps, static_cast<St*>(h_out), static_cast<St*>(x_out), m_out,
+                       lse_out);
+    return hipGetLastError();
+  }
+  const size_t lds = sizeof(float) * (2 * Red<1, kGroup>::kSlot + 16 * kSingleNP + 16);
   auto kern = C <= 64 ? k_phase1_single<St, 1>
               : C <= 128 ? k_phase1_single<St, 2>
               : C <= 256 ? k_phase1_single<St, 4> : k_phase1_single<St, 0>;
