@@ -122,11 +122,20 @@ def test_block_edge_shapes(T, d, blocks, n_given, dt):
     _say("worst", worst)
 
 
-@pytest.mark.parametrize("T,d,L", [(5, 8, 3), (18, 200, 31), (64, 1024, 9)])
-def test_full_edge_shapes(T, d, L):
+@pytest.mark.parametrize("T,d,L,dt", [
+    (5, 8, 3, "bf16"), (18, 200, 31, "bf16"), (64, 1024, 9, "bf16"),
+    (33, 520, 12, "bf16"),    # 65 chunks: two chunks per lane, the second mostly past the row
+    (29, 2048, 31, "bf16"),   # four chunks per lane, 32 sources: batches of two
+    (21, 1544, 10, "f32"),    # fp32, four chunks per lane, batches of one
+    (40, 1032, 7, "f32"),     # fp32, two chunks per lane, ragged last batch
+    (17, 2056, 5, "bf16"),    # widest row past the one-pass kernel: the tile kernel
+])
+def test_full_edge_shapes(T, d, L, dt):
+    """One-shot sites over the row widths and source counts of both site
+    kernels (one pass for rows of <= 256 chunks, the tile kernel beyond)."""
     base = synth.WORKLOADS["full_bf16"]
-    w = synth.scaled(base, name="full_edge", T=T, d=d, block_sizes=(1,) * L, seed=777 + L)
-    _say("case full_edge T=%d d=%d L=%d" % (T, d, L))
+    w = synth.scaled(base, name="full_edge", T=T, d=d, block_sizes=(1,) * L, seed=777 + L + d, dtype=dt)
+    _say("case full_edge T=%d d=%d L=%d %s" % (T, d, L, dt))
     run_full_parity(w)
 
 
