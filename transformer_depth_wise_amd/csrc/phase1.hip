@@ -951,11 +951,13 @@ __global__ __launch_bounds__(256) void k_p1_out_tokens(const St* __restrict__ sr
 
 // ---------------------------------------------------------------------------
 // S == 1: one query, up to 32 sources, optional PreNorm of the output (Full
-// AttnRes sites and the final aggregation).  Part B walks the tile's tokens
-// with the whole workgroup (the PreNorm needs each token's full row).
+// AttnRes sites and the final aggregation without a workspace) for rows of
+// more than 256 chunks.  Part A scores a 16-token tile on the matrix cores;
+// part B walks the tile's tokens with the whole workgroup (the PreNorm needs
+// each token's full row).
 constexpr int kSingleNP = 32;
 
-template <typename St, int KW>
+template <typename St>
 __global__ __launch_bounds__(256) void k_phase1_single(const St* __restrict__ src, int n, int64_t stride,
                                                        int64_t T, int d, const float* __restrict__ w,
                                                        const float* __restrict__ kg,
@@ -992,83 +994,6 @@ __global__ __launch_bounds__(256) void k_phase1_single(const St* __restrict__ sr
 
   const int C = d >> 3;
   const int ntile = (int)((T - tok0) < 16 ? (T - tok0) : 16);
-  if (KW > 0) {
-    // rows of at most 256 chunks: a wave per token, four tokens at a time,
-    // the PreNorm's sum of squares reduced inside the wave
-    constexpr int K1 = KW > 0 ? KW : 1;
-    const int lane = threadIdx.x & 63;
-    for (int t = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); t < ntile; t += 4) {
-      const int64_t tok = tok0 + t;
-      const float* al = zb + t * kSingleNP;
-      float h[K1][8];
-      float ssq = 0.f;
-#pragma unroll
-      for (int k = 0; k < K1; ++k) zero8(h[k]);
-      int i = 0;
-      for (; i + 4 <= n; i += 4) {
-        Chunk<St> u[4][K1];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int k = 0; k < K1; ++k) {
-            const int c0 = lane + 64 * k;
-            u[j][k].load(src + (int64_t)(i + j) * stride + tok * d + (c0 < C ? c0 : C - 1) * 8);
-          }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float a = al[i + j];
-#pragma unroll
-          for (int k = 0; k < K1; ++k) {
-            float v[8];
-            u[j][k].unpack(v);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) h[k][e] = fmaf(a, v[e], h[k][e]);
-          }
-        }
-      }
-      for (; i < n; ++i) {
-        const float a = al[i];
-#pragma unroll
-        for (int k = 0; k < K1; ++k) {
-          const int c0 = lane + 64 * k;
-          float v[8];
-          load8(src + (int64_t)i * stride + tok * d + (c0 < C ? c0 : C - 1) * 8, v);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) h[k][e] = fmaf(a, v[e], h[k][e]);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < K1; ++k) {
-        const int c = lane + 64 * k;
-        if (c < C) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ssq = fmaf(h[k][e], h[k][e], ssq);
-          if (h_out) store8(h_out + tok * d + c * 8, h[k]);
-        }
-      }
-      if (x_out) {
-        const float rinv = 1.0f / sqrtf(wave_sum_dpp(ssq) / (float)d + eps);
-#pragma unroll
-        for (int k = 0; k < K1; ++k) {
-          const int c = lane + 64 * k;
-          if (c < C) {
-            float gm[8];
-            if (gamma) {
-              load8(gamma + c * 8, gm);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) gm[e] = 1.f;
-            }
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = gm[e] * (h[k][e] * rinv);
-            store8(x_out + tok * d + c * 8, x);
-          }
-        }
-      }
-    }
-    return;
-  }
   int parity = 0;
   for (int t = 0; t < ntile; ++t) {
     const int64_t tok = tok0 + t;
@@ -1466,10 +1391,9 @@ static hipError_t run_single(const void* src, int n, int64_t stride, int64_t T, 
                        lse_out);
     return hipGetLastError();
   }
+  // wider rows: scores per 16-token tile on the matrix cores, then the outputs
   const size_t lds = sizeof(float) * (2 * Red<1, kGroup>::kSlot + 16 * kSingleNP + 16);
-  auto kern = C <= 64 ? k_phase1_single<St, 1>
-              : C <= 128 ? k_phase1_single<St, 2>
-              : C <= 256 ? k_phase1_single<St, 4> : k_phase1_single<St, 0>;
+  auto kern = k_phase1_single<St>;
   hipError_t e = set_lds(kern, lds);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((T + 15) / 16));
