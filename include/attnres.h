@@ -102,9 +102,10 @@ typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1, ATTNRES_P24 = 2 } attnres_dtyp
  * attnres_phase1_workspace_bytes(T, d, n_src, S) bytes, 16-byte aligned,
  * used for the queries packed as matrix-core operands and for the softmax
  * weights between the scoring and output kernels (its contents afterwards are
- * unspecified).  Required for S >= 2.  For S == 1 it is optional: without it
- * (or when it is too small) one fused kernel computes the site instead of the
- * streaming pair.
+ * unspecified).  Required for S >= 2.  For S == 1 it is not used (may be
+ * NULL): one pass over the sources computes the site with an online softmax
+ * (the running maximum and normaliser rescaled batch by batch, as in the
+ * notes' log-sum-exp merge), reading every source row once.
  * out must not overlap src; m_out, lse_out and workspace must not overlap
  * anything.
  */

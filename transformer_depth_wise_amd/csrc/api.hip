@@ -125,9 +125,9 @@ static attnres_status_t phase1_impl(attnres_dtype_t dt, const void* src, int64_t
   if (n_src > 1 && (src_stride < T * d)) return ATTNRES_EINVAL;
   if (src_stride % 8 != 0) return ATTNRES_EALIGN;
   int64_t ws_need = attnres_phase1_workspace_bytes(T, d, n_src, S);
-  // S == 1 without the first-query PreNorm: the workspace is optional
-  // (without it, one fused kernel runs)
-  if (S == 1 && !x0 && (!workspace || workspace_bytes < ws_need)) ws_need = 0;
+  // S == 1 without the first-query PreNorm: one pass over the sources with an
+  // online softmax; the workspace is not used
+  if (S == 1 && !x0) ws_need = 0;
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return ATTNRES_EINVAL;
   st = check_align({src, w, key_gain, out, ws_need > 0 ? workspace : nullptr, gamma0, x0, h0}, {m_out, lse_out});
   if (st != ATTNRES_OK) return st;

@@ -1227,6 +1227,203 @@ __global__ __launch_bounds__(256) void k_site_online(const St* __restrict__ src,
 }
 
 // ---------------------------------------------------------------------------
+// S == 1 with wider rows (the final aggregation, Full AttnRes sites of more
+// than 256 chunks): the same one-pass online softmax with a 512-thread
+// workgroup per token, each thread owning CPT chunks of the row.  A batch's
+// 2 x BS partial sums (w (.) g).u and |u|^2 are added over the workgroup in
+// one fixed-order reduction (DPP wave sums, then the 8 waves in index order
+// through LDS; two buffers alternate, so one barrier per reduction).  The
+// next (token, batch) item's loads are in flight meanwhile.
+constexpr int kTeam = 512;
+
+template <typename St, int CPT>
+__global__ __launch_bounds__(kTeam) void k_site_team(const St* __restrict__ src, int n, int64_t stride, int64_t T,
+                                                     int d, const float* __restrict__ w,
+                                                     const float* __restrict__ kg,
+                                                     const float* __restrict__ gamma, float eps,
+                                                     St* __restrict__ h_out, St* __restrict__ x_out,
+                                                     float* __restrict__ m_out, float* __restrict__ lse_out) {
+  constexpr int BS = (sizeof(St) == 2 ? 4 : 2) / (CPT > 2 ? 2 : 1);  // sources per batch (registers)
+  constexpr int NW = kTeam / 64;
+  __shared__ float red[2][NW][2 * BS];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int C = d >> 3;
+  const float inv_d = 1.0f / (float)d;
+  float q[CPT][8], gm[CPT][8];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int c = threadIdx.x + kTeam * k;
+    if (c < C) {
+      load8(w + c * 8, q[k]);
+      if (kg) {
+        float g8[8];
+        load8(kg + c * 8, g8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[k][e] *= g8[e];
+      }
+    } else {
+      zero8(q[k]);
+    }
+    if (gamma && x_out && c < C) {
+      load8(gamma + c * 8, gm[k]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gm[k][e] = 1.f;
+    }
+  }
+  const int64_t ntok = (int64_t)blockIdx.x < T ? (T - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
+  const int nb = (n + BS - 1) / BS;
+  const int64_t items = ntok * nb;
+  if (items == 0) return;  // uniform over the workgroup
+  int parity = 0;
+  // fixed-order workgroup sum of v[0..NV); every thread gets the sums
+  auto team_sum = [&](auto& v) {
+    constexpr int NV = sizeof(v) / sizeof(float);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = wave_sum_dpp(v[i]);
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) red[parity][wv][i] = v[i];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float t = red[parity][0][i];
+#pragma unroll
+      for (int r = 1; r < NW; ++r) t += red[parity][r][i];
+      v[i] = t;
+    }
+    parity ^= 1;
+  };
+  auto issue = [&](Chunk<St>(&u)[BS][CPT], int64_t it) {
+    const int64_t itc = it < items ? it : items - 1;
+    const int64_t tq = itc / nb;
+    const int b = (int)(itc - tq * nb);
+    const int64_t tok = blockIdx.x + tq * gridDim.x;
+#pragma unroll
+    for (int j = 0; j < BS; ++j) {
+      const int i = b * BS + j < n ? b * BS + j : n - 1;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const int c0 = threadIdx.x + kTeam * k;
+        u[j][k].load(src + (int64_t)i * stride + tok * d + (c0 < C ? c0 : C - 1) * 8);
+      }
+    }
+  };
+  float m = -INFINITY, l = 0.f;
+  float o[CPT][8];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) zero8(o[k]);
+  auto consume = [&](const Chunk<St>(&u)[BS][CPT], int64_t it) {
+    const int64_t tq = it / nb;
+    const int b = (int)(it - tq * nb);
+    float part[2 * BS];
+#pragma unroll
+    for (int j = 0; j < BS; ++j) {
+      float zp = 0.f, sp = 0.f;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        float v[8];
+        u[j][k].unpack(v);
+        const bool cok = (int)threadIdx.x + kTeam * k < C;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = cok ? v[e] : 0.f;
+          zp = fmaf(q[k][e], x, zp);
+          sp = fmaf(x, x, sp);
+        }
+      }
+      part[2 * j] = zp;
+      part[2 * j + 1] = sp;
+    }
+    team_sum(part);
+    float z[BS];
+    float zmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < BS; ++j) {
+      z[j] = b * BS + j < n ? part[2 * j] / sqrtf(part[2 * j + 1] * inv_d + eps) : -INFINITY;
+      zmax = fmaxf(zmax, z[j]);
+    }
+    if (b == 0) {
+      m = -INFINITY;
+      l = 0.f;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) zero8(o[k]);
+    }
+    const float mn = fmaxf(m, zmax);  // finite: every batch has a source
+    const float sc = m == -INFINITY ? 0.f : expf(m - mn);
+    l *= sc;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[k][e] *= sc;
+#pragma unroll
+    for (int j = 0; j < BS; ++j) {
+      const float p = expf(z[j] - mn);  // 0 for a missing source
+      l += p;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        float v[8];
+        u[j][k].unpack(v);
+        const bool cok = (int)threadIdx.x + kTeam * k < C;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[k][e] = fmaf(p, cok ? v[e] : 0.f, o[k][e]);
+      }
+    }
+    m = mn;
+    if (b == nb - 1) {
+      const int64_t tok = blockIdx.x + tq * gridDim.x;
+      const float il = 1.0f / l;
+      float ssq = 0.f;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o[k][e] *= il;
+          ssq = fmaf(o[k][e], o[k][e], ssq);
+        }
+        const int c = threadIdx.x + kTeam * k;
+        if (h_out && c < C) store8(h_out + tok * d + c * 8, o[k]);
+      }
+      if (x_out) {
+        float sq[1] = {ssq};
+        team_sum(sq);
+        const float rinv = 1.0f / sqrtf(sq[0] * inv_d + eps);
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          const int c = threadIdx.x + kTeam * k;
+          if (c < C) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = gm[k][e] * (o[k][e] * rinv);
+            store8(x_out + tok * d + c * 8, x);
+          }
+        }
+      }
+      if (threadIdx.x == 0) {
+        if (m_out) m_out[tok] = m;
+        if (lse_out) lse_out[tok] = m + logf(l);
+      }
+    }
+  };
+  Chunk<St> A[BS][CPT], B[BS][CPT];
+  issue(A, 0);
+  int64_t it = 0;
+  for (; it + 2 <= items; it += 2) {
+    issue(B, it + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(A, it);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(A, it + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(B, it + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (it < items) consume(A, it);
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 
 // Allow `dynamic` bytes of dynamic LDS when a launch needs more than 64 KiB
@@ -1389,6 +1586,16 @@ static hipError_t run_single(const void* src, int n, int64_t stride, int64_t T, 
     hipLaunchKernelGGL(k, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, static_cast<const St*>(src), n,
                        stride, T, d, w, kg, gamma, eps, static_cast<St*>(h_out), static_cast<St*>(x_out), m_out,
                        lse_out);
+    return hipGetLastError();
+  }
+  if (C <= 4 * kTeam) {
+    // the same one pass, a 512-thread workgroup per token
+    auto k = C <= 2 * kTeam ? k_site_team<St, 2> : k_site_team<St, 4>;
+    int64_t wgs = T;
+    const int64_t cap = (int64_t)device_cu_count() * 2;
+    if (wgs > cap) wgs = cap;
+    hipLaunchKernelGGL(k, dim3((unsigned)wgs), dim3(kTeam), 0, stream, static_cast<const St*>(src), n, stride, T, d,
+                       w, kg, gamma, eps, static_cast<St*>(h_out), static_cast<St*>(x_out), m_out, lse_out);
     return hipGetLastError();
   }
   // wider rows: scores per 16-token tile on the matrix cores, then the outputs
