@@ -109,6 +109,9 @@ EDGE = [
     (16, 64, (17, 2), 0, "f32"),           # S = 17: second query tile of 16 partly used
     (23, 512, (1,) * 15, 0, "bf16"),      # 16 completed sources at the last blocks
     (31, 16384, (4,), 0, "bf16"),          # widest supported row
+    (9, 4104, (2, 1), 1, "f32"),           # fp32 final site over 513 chunks: workgroup per token, 2 chunks a thread
+    (6, 8200, (2,), 2, "f32"),             # fp32 final site over 1025 chunks: 4 chunks a thread
+    (300, 2048, (3, 3), 0, "bf16"),        # final site over 256 chunks: the widest wave-per-token row
 ]
 
 
