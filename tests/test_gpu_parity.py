@@ -112,6 +112,8 @@ EDGE = [
     (9, 4104, (2, 1), 1, "f32"),           # fp32 final site over 513 chunks: workgroup per token, 2 chunks a thread
     (6, 8200, (2,), 2, "f32"),             # fp32 final site over 1025 chunks: 4 chunks a thread
     (300, 2048, (3, 3), 0, "bf16"),        # final site over 256 chunks: the widest wave-per-token row
+    (5, 8, (2,) + (1,) * 18, 0, "f32"),    # one-query blocks past 16 sources: first merge in phase 2
+    (37, 1032, (1,) * 20, 1, "bf16"),
 ]
 
 

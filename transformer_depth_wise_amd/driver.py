@@ -112,8 +112,8 @@ class BlockAttnRes:
         n_reps = 1 + self.n_given + len(self.block_sizes)
         if n_reps > _lib.ATTNRES_MAX_SOURCES:
             raise ValueError("too many sources for one aggregation site: %d" % n_reps)
-        if any(s > 1 for s in self.block_sizes) and 1 + self.n_given + len(self.block_sizes) - 1 > \
-                _lib.ATTNRES_MAX_SOURCES_MULTI:
+        if any(s > 1 and 1 + self.n_given + b > _lib.ATTNRES_MAX_SOURCES_MULTI
+               for b, s in enumerate(self.block_sizes)):
             raise ValueError("phase 1 with S >= 2 supports at most %d completed sources"
                              % _lib.ATTNRES_MAX_SOURCES_MULTI)
         smax = max(self.block_sizes) if self.block_sizes else 1
@@ -122,10 +122,12 @@ class BlockAttnRes:
         self.o1 = torch.empty((smax, T, d), dtype=dtype, device=dev)
         self.m1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
         self.lse1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
-        n_max = 1 + self.n_given + max(0, len(self.block_sizes) - 1)
-        ws = _lib.attnres_phase1_workspace_bytes(T, d, n_max, smax) if T > 0 else 0
-        if final_site and T > 0:  # the final site runs as a one-query phase 1
-            ws = max(ws, _lib.attnres_phase1_workspace_bytes(T, d, n_reps, 1))
+        # the largest phase-1 workspace over the blocks (a one-query phase 1
+        # without the first sublayer's PreNorm, and the final site, need none)
+        ws = 0
+        for b, S in enumerate(self.block_sizes):
+            if T > 0 and (S > 1 or self._fuse(S, 1 + self.n_given + b)):
+                ws = max(ws, _lib.attnres_phase1_workspace_bytes(T, d, 1 + self.n_given + b, S))
         self.workspace = torch.empty((max(ws, 16) // 4,), dtype=torch.float32, device=dev)
         # running partial sum: P24 (24-bit split) for bf16 rows, fp32 for fp32 rows
         self.partial_format = partial or ("p24" if dtype == torch.bfloat16 else "f32")
@@ -167,6 +169,12 @@ class BlockAttnRes:
         out["total"] = sum(out.values())
         return out
 
+    def _fuse(self, S: int, n_done: int) -> bool:
+        """Whether the block's first sublayer takes its PreNorm output from the
+        phase-1 pass (that pass reads at most ATTNRES_MAX_SOURCES_MULTI
+        sources; a one-query block with more merges its first site in phase 2)."""
+        return self.fuse_first and (S > 1 or n_done <= _lib.ATTNRES_MAX_SOURCES_MULTI)
+
     def _row(self, dt=None) -> int:
         return self.T * self.d * _esize(self.dtype if dt is None else dt)
 
@@ -178,7 +186,8 @@ class BlockAttnRes:
         out: List[Launch] = []
         n_done = 1 + self.n_given
         for S in self.block_sizes:
-            if self.fuse_first:  # + x of the first sublayer (phase 1 writes it instead of o_0)
+            fuse = self._fuse(S, n_done)
+            if fuse:  # + x of the first sublayer (phase 1 writes it instead of o_0)
                 out.append(Launch("phase1", n_done * r + S * r + S * 2 * stat if n_done > 1 else
                                   2 * r + S * 2 * stat))
             elif n_done == 1:  # statistics only; phase 2 reads b_0 as its phase-1 output
@@ -186,7 +195,7 @@ class BlockAttnRes:
             else:
                 out.append(Launch("phase1", n_done * r + S * (r + 2 * stat)))
             for j in range(S):
-                if j == 0 and self.fuse_first:
+                if j == 0 and fuse:
                     continue
                 if j == 0:
                     b = 2 * r + stat                  # o; x
@@ -239,8 +248,9 @@ class BlockAttnRes:
             o1 = self.o_blocks[b] if self.training else self.o1[:S]
             lse1 = self.lse_blocks[b] if self.training else self.lse1[:S]
             slots = self.p_slots[b] if self.training else None
+            fuse = self._fuse(S, n_done)
             mark("phase1", True)
-            if self.fuse_first:
+            if fuse:
                 attnres_phase1_first_prenorm(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S],
                                              eps, None if single else self.o1[:S], self.m1[:S], self.lse1[:S],
                                              None if gam is None else gam[l0], self.x[l0 % nx], self.h,
@@ -275,7 +285,7 @@ class BlockAttnRes:
                 if self.training:
                     self.recipes[site] = (pin, v2, prev)
                 o = self.reps[0] if (single and not self.training) else o1[j]
-                if j == 0 and self.fuse_first:
+                if j == 0 and fuse:
                     # x (and h = o_0) came out of phase 1; slab 0 of o1 is scratch
                     o = self.reps[0] if single else self.h
                 else:
