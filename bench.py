@@ -199,6 +199,22 @@ def backward_report(dev, steps: int):
     return out
 
 
+def io_model(w, rows) -> dict:
+    """The measured path's algorithmic rows per token and sublayer beside the
+    pages' analytic residual I/O per layer (rows of d): at this workload's
+    depth and block count, and at the pages' own L = 128, N = 8, S = 16."""
+    from transformer_depth_wise_amd import costmodel as cm
+    N = len(w.block_sizes)
+    return {"this_path": round(rows, 3),
+            "pages_model_here": cm.model_for(w.L, N),
+            "pages_model_L128_N8_S16": {"standard_residual": cm.io_standard_residual(1),
+                                        "mhc_m4": round(cm.io_mhc(4, w.d) / w.d, 3),
+                                        "full_two_phase": cm.io_full_two_phase(16, 8, 1),
+                                        "block_two_phase": cm.io_block_two_phase(8, 16, 1)},
+            "note": "the pages give no breakdown of the 5 rows of their Block figure; this path counts "
+                    "the write and re-read of the phase-1 outputs and its 24-bit partial sum explicitly"}
+
+
 def other_workloads(dev, steps: int):
     """Shorter measurements of the other hot-path shapes, each pass over
     resident inputs: the decode-shaped block step (eager launches and one
@@ -495,6 +511,7 @@ def main() -> int:
         "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
         "bytes_per_token_sublayer": round(step_bytes / units, 1),
         "rows_per_token_sublayer": round(step_bytes / units / (w.d * w.elem_bytes), 3),
+        "io_model": io_model(w, step_bytes / units / (w.d * w.elem_bytes)),
         "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
