@@ -241,6 +241,39 @@ def test_token_split_invariance():
         assert torch.equal(s2.h_final, whole[a:b])
 
 
+def test_token_permutation_equivariance():
+    """Permuting the tokens permutes every output bitwise: no kernel lets a
+    token's result depend on its position or neighbours (which wave, tile or
+    workgroup computes it)."""
+    _say("case token permutation")
+    dev = torch.device("cuda")
+    w = synth.scaled(synth.WORKLOADS["prefill_chunk_bf16"], T=777, block_sizes=(4, 3, 2), n_given=1,
+                     name="perm")
+    from harness import block_inputs
+    emb, given, v = block_inputs(w, dev)
+    prm = synth.params(w, dev)
+    perm = torch.randperm(w.T, generator=torch.Generator().manual_seed(5)).to(dev)
+
+    def run(e, gs, vs):
+        st = tdw.BlockAttnRes(w.T, w.d, w.block_sizes, w.torch_dtype, n_given=1, keep_h=True, device=dev)
+        st.reps[0].copy_(e)
+        st.reps[1].copy_(gs[0])
+        xs, hs = [], []
+
+        def hook(site, **k):
+            xs.append(k["x"].clone())
+            hs.append(k["h"].clone())
+
+        st.forward(prm, lambda l, x: vs[l], hook=hook)
+        return st.h_final.clone(), st.reps.clone(), torch.stack(xs), torch.stack(hs)
+
+    ref = run(emb, given, v)
+    got = run(emb[perm].contiguous(), [gl[perm].contiguous() for gl in given], [vl[perm].contiguous() for vl in v])
+    assert torch.equal(got[0], ref[0][perm])
+    for a, b in zip(got[1:], ref[1:]):
+        assert torch.equal(a, b[:, perm])
+
+
 # ------------------------------------------------ decode step as a HIP graph
 def test_decode_step_graph_replay_matches_eager():
     """The decode-shaped block step (T=256, one block of 24, 7 given block
