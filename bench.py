@@ -17,6 +17,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -353,8 +354,8 @@ def other_workloads(dev, steps: int):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_chunk_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -449,6 +450,10 @@ def main() -> int:
     kind_ms = {}
     for kind, a, b in recs:
         kind_ms[kind] = kind_ms.get(kind, 0.0) + a.elapsed_time(b)
+    # per-pass span (first launch's start to last launch's end), for the
+    # spread over the timed passes
+    per = len(recs) // args.steps
+    spans = sorted(recs[p * per][1].elapsed_time(recs[p * per + per - 1][2]) for p in range(args.steps))
 
     # ---- cold-cache pass: a 512 MiB scratch write between consecutive
     # launches evicts the 256 MB last-level cache (MALL), as the sublayers of
@@ -499,6 +504,10 @@ def main() -> int:
         "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms": {"median": round(statistics.median(spans), 4),
+                    "p90": round(spans[-(-9 * len(spans) // 10) - 1], 4),  # nearest rank
+                    "min": round(spans[0], 4), "max": round(spans[-1], 4),
+                    "note": "per-pass span between the first and last launch's HIP events"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
