@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from harness import TOL, row_rel_err, run_block_parity, run_full_parity, stat_err, _host
+from harness import TOL, Capture, row_rel_err, run_block_parity, run_full_parity, stat_err, _host
 import transformer_depth_wise_amd as tdw
 
 pytestmark = pytest.mark.gpu
@@ -201,6 +201,51 @@ def test_phase1_single_query_equals_full():
     tdw.attnres_full(src, n, wq[0], g[0], None, 1e-6, h, None, lse2)
     assert torch.equal(out[0], h)
     assert torch.equal(lse[0], lse2)
+
+
+@pytest.mark.parametrize("T,d,L", [(300, 1024, 8), (97, 7168, 5)])
+def test_block_of_single_sublayers_equals_full_and_grouped(T, d, L):
+    """GPU against GPU on the same inputs: Block AttnRes with every block one
+    sublayer long has Full AttnRes's sources at every site (structured notes
+    on arXiv 2603.15031, section 8: N = L recovers Full), and the grouped
+    two-phase Full schedule computes the one-shot sites exactly up to
+    rounding (section 7, two-phase computation).  Each GPU result is within
+    the parity tolerance of the same exact values, so they are compared at it."""
+    _say("case block N=L vs full vs grouped T=%d d=%d L=%d" % (T, d, L))
+    dev = torch.device("cuda")
+    base = synth.WORKLOADS["full_bf16"]
+    w = synth.scaled(base, name="block_vs_full", T=T, d=d, block_sizes=(1,) * L, seed=4242 + d)
+    scales = synth.sublayer_scales(w)
+    prm = synth.params(w, dev)
+    emb = synth.embedding(w, 0, T, dev)
+    v = [synth.sublayer_output(w, l + 1, 0, T, dev, scales) for l in range(L)]
+    idx = torch.arange(T, device=dev)
+
+    def full(group):
+        st = tdw.FullAttnRes(T, d, L, w.torch_dtype, eps=w.eps, device=dev, keep_h=True, group=group)
+        st.hist[0].copy_(emb)
+        for l in range(L):
+            st.hist[l + 1].copy_(v[l])
+        cap = Capture(idx)
+        st.forward(prm, lambda l, x: None, hook=cap)
+        return cap, st.h_final.clone()
+
+    blk = tdw.BlockAttnRes(T, d, w.block_sizes, w.torch_dtype, eps=w.eps, device=dev, keep_h=True)
+    blk.reps[0].copy_(emb)
+    bcap = Capture(idx)
+    blk.forward(prm, lambda l, x: v[l], hook=bcap)
+    torch.cuda.synchronize()
+    one, one_hf = full(None)
+    grp, grp_hf = full(4 if L > 4 else 2)
+    tol = TOL[w.dtype]
+    for other, hf in ((bcap, blk.h_final), (grp, grp_hf)):
+        for k in ("x", "h"):
+            e = float(row_rel_err(other.stacked(k), one.stacked(k)).max())
+            assert e <= tol, (k, e)
+        assert float(row_rel_err(_host(hf), _host(one_hf)).max()) <= tol
+    # Block's one-query sites and Full's one-shot sites compute the same
+    # softmax: their statistics agree to fp32 rounding
+    assert float(stat_err(bcap.stacked("lse1"), one.stacked("lse")).max()) <= 1e-4
 
 
 def test_block_runs_are_bitwise_deterministic():
