@@ -219,7 +219,8 @@ def io_model(w, rows) -> dict:
 def other_workloads(dev, steps: int):
     """Shorter measurements of the other hot-path shapes, each pass over
     resident inputs: the decode-shaped block step (eager launches and one
-    HIP-graph replay per pass), Full AttnRes one-shot sites, and one GPU's
+    HIP-graph replay per pass), Full AttnRes (one-shot sites, the grouped
+    schedule, the backward), one aggregation site's backward, and one GPU's
     token share (2048 tokens) of the 16K chunk.  Working sets that fit the
     256 MB last-level cache rotate over 4 input replicas so that every pass
     reads from HBM."""
@@ -313,6 +314,21 @@ def other_workloads(dev, steps: int):
                                  "ms_per_step": round(sec * 1e3, 4), "value": round(w.T * w.L / sec, 1),
                                  "unit": "token-sublayers/s", "hbm_gbps": round(b / sec / 1e9, 1),
                                  "bytes_per_step": b}
+    # the backward of Full AttnRes over the same outputs (site backward passes
+    # accumulating every representation's gradient in fp32); the synthetic
+    # sublayer backward returns another resident output row as dL/dx_l
+    dxs = [fulls[0].hist[(l + 2) % (w.L + 1)] for l in range(w.L)]
+    dxf = lambda l, dv: dxs[l]  # noqa: E731
+    for f in fulls:
+        f.backward(prm, dxf, dh_final=f.hist[1])
+    sec = _time(lambda k: fulls[k % 4].backward(prm, dxf, dh_final=fulls[k % 4].hist[1]), max(steps, 20))
+    b = sum(x.bytes for x in fulls[0].plan_backward())
+    res[w.name + "_backward"] = {"config": {"T": w.T, "d": w.d, "sublayers": w.L,
+                                            "schedule": "site backward, reverse"},
+                                 "ms_per_step": round(sec * 1e3, 4), "value": round(w.T * w.L / sec, 1),
+                                 "unit": "token-sublayers/s", "hbm_gbps": round(b / sec / 1e9, 1),
+                                 "bytes_per_step": b,
+                                 "note": "includes zeroing the fp32 gradient rows and parameter gradients"}
     del fulls, grouped
 
     # backward of one aggregation site at the 16K chunk's final-site shape

@@ -240,7 +240,7 @@ attnres_status_t attnres_full(attnres_dtype_t dt,
  *     dprenorm_gain = dL/dprenorm_gain (NULL or prenorm == 0: not computed),
  * each [d] fp32, summed over the T tokens in a fixed order (bitwise
  * reproducible).  key_gain, prenorm_gain NULL mean ones.
- * Limits: 1 <= n_src <= ATTNRES_MAX_SOURCES_MULTI.  The dsrc rows must not
+ * Limits: 1 <= n_src <= ATTNRES_MAX_SOURCES.  The dsrc rows must not
  * overlap any input; the [d] outputs must not overlap anything.
  * workspace: at least attnres_site_backward_workspace_bytes(T, d) bytes of
  * caller-owned device memory, 16-byte aligned (per-team partial sums).
@@ -254,6 +254,26 @@ attnres_status_t attnres_site_backward(attnres_dtype_t dt,
                                        const void* dx, void* dsrc, int64_t dsrc_stride,
                                        float* dw, float* dkey_gain, float* dprenorm_gain,
                                        void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * As attnres_site_backward, but dL/du_i is ADDED to fp32 rows:
+ *     dsrc + i*dsrc_stride += dL/du_i  ([T][d] fp32, i < n_src).
+ * A source feeds every later site of Full AttnRes ("Attention Residuals"
+ * notes, section 7: layer l attends over all earlier outputs), so its
+ * gradient is the sum of one contribution per site; the sites' backward
+ * passes accumulate into one fp32 row per source in reverse site order.
+ * dw, dkey_gain, dprenorm_gain are written, not accumulated (each site has
+ * its own parameters).  Same limits, alignment, aliasing rules and
+ * workspace as attnres_site_backward; dsrc_stride counts fp32 elements.
+ */
+attnres_status_t attnres_site_backward_accumulate(attnres_dtype_t dt,
+                                                  const void* src, int64_t n_src, int64_t src_stride,
+                                                  int64_t T, int64_t d,
+                                                  const float* w, const float* key_gain,
+                                                  const float* prenorm_gain, int prenorm, float eps,
+                                                  const void* dx, float* dsrc, int64_t dsrc_stride,
+                                                  float* dw, float* dkey_gain, float* dprenorm_gain,
+                                                  void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * Backward through the block structure, in the two phases of the forward

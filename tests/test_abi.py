@@ -290,8 +290,10 @@ def test_merge_multi_validation(lib):
     assert mm(T=0, n=0, src=None, w=None, o=None, lse=None, x=None) == 0
 
 
-def test_site_backward_validation(lib):
-    sb = lambda **k: checked(lib.attnres_site_backward(
+@pytest.mark.parametrize("entry", ["attnres_site_backward", "attnres_site_backward_accumulate"])
+def test_site_backward_validation(lib, entry):
+    acc = entry.endswith("accumulate")  # fp32 gradient rows
+    sb = lambda **k: checked(getattr(lib, entry)(
         k.get("dt", 1), p(k.get("src", A)), k.get("n", 2), k.get("stride", 64 * 64), k.get("T", 64), k.get("d", 64),
         p(k.get("w", 2 * A)), None, None, k.get("prenorm", 1), 1e-6, p(k.get("dx", 3 * A)), p(k.get("dsrc", 4 * A)),
         k.get("dstride", 64 * 64), p(k.get("dw", 5 * A)), p(k.get("dkg")), p(k.get("dgm")), p(k.get("ws", 6 * A)),
@@ -301,7 +303,7 @@ def test_site_backward_validation(lib):
     assert lib.attnres_site_backward_workspace_bytes(0, 64) == 0
     assert lib.attnres_site_backward_workspace_bytes(64, 12) == -1
     assert sb(n=0) == EINVAL
-    assert sb(n=17) == EINVAL
+    assert sb(n=33) == EINVAL
     assert sb(wsb=16) == EINVAL                     # workspace too small
     assert sb(ws=None) == EINVAL
     assert sb(dw=None) == EINVAL
@@ -310,6 +312,9 @@ def test_site_backward_validation(lib):
     assert sb(dw=3 * A + 256) == EALIAS             # dw over dx
     assert sb(dkg=5 * A + 8) == EALIAS              # two [d] outputs overlap
     assert sb(ws=4 * A + 1024) == EALIAS            # workspace over the gradients
+    if acc:
+        # the fp32 gradient slabs end 2 * 4096 * 4 bytes after dsrc (bf16 ones: half that)
+        assert sb(ws=4 * A + 20000) == EALIAS
     assert sb(stride=64 * 64 + 4) == EALIGN
     assert sb(dt=2) == EDTYPE
     assert sb(T=0, src=None, dx=None, dsrc=None, dw=None, ws=None) == 0

@@ -100,6 +100,11 @@ def test_backward_arguments():
                rows(d, dtype=f32), None, None, ws)
     with pytest.raises(ValueError, match="dw is required"):
         tdw.attnres_site_backward(src, n, w, None, None, False, 1e-6, dx, rows(n, T, d), None, None, None, ws)
+    not_on_gpu(tdw.attnres_site_backward_accumulate, src, n, w, None, None, True, 1e-6, dx,
+               rows(n, T, d, dtype=f32), rows(d, dtype=f32), None, rows(d, dtype=f32), ws)
+    with pytest.raises(TypeError, match="dsrc"):    # the accumulated gradients are fp32 rows
+        tdw.attnres_site_backward_accumulate(src, n, w, None, None, True, 1e-6, dx, rows(n, T, d),
+                                             rows(d, dtype=f32), None, None, ws)
     o, lse, G = rows(T, d), rows(T, dtype=f32), rows(T, d)
     c, gp, R = rows(T, dtype=f32), rows(T, dtype=f32), rows(T, d, dtype=f32)
     not_on_gpu(tdw.attnres_phase2_backward, o, lse, None, rows(T, d), w, None, None, 1e-6, dx, R, G, c, gp,

@@ -492,6 +492,10 @@ BWD = [
     (5, 8, 1, True, "f32", 1.0),            # one source: no score gradient
     (40, 16384, 2, True, "bf16", 0.02),     # widest row
     (2100, 2048, 4, True, "bf16", 0.02),    # many tokens per team
+    (50, 1024, 17, True, "bf16", 0.02),     # more than 16 sources: rows re-read per pass
+    (33, 7168, 32, True, "bf16", 0.02),     # the most sources
+    (20, 16384, 24, False, "bf16", 0.02),   # widest row, many sources
+    (40, 256, 25, True, "f32", 0.05),
 ]
 
 
@@ -532,6 +536,99 @@ def test_site_backward_matches_oracle(T, d, n, prenorm, dt, qs):
     tdw.attnres_site_backward(src, n, w, kg, gm if prenorm else None, prenorm, 1e-6, dx, d2, dw2, None, None, ws)
     torch.cuda.synchronize()
     assert torch.equal(d2, dsrc) and torch.equal(dw2, dw)
+
+
+@pytest.mark.parametrize("T,d,n,prenorm,dt,qs", [BWD[1], BWD[3], BWD[8], BWD[9], BWD[11]])
+def test_site_backward_accumulate_adds_the_gradient(T, d, n, prenorm, dt, qs):
+    """attnres_site_backward_accumulate adds dL/du_i to fp32 rows already
+    holding other contributions; the increment matches the oracle's
+    backward, and dw/dg/dgamma equal the storing entry point's bit for bit."""
+    _say("case site backward accumulate T=%d d=%d n=%d %s" % (T, d, n, dt))
+    dev = torch.device("cuda")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    g = torch.Generator(device=dev).manual_seed(6000 + T + d + n)
+    scales = torch.exp(torch.rand((n, 1, 1), generator=g, device=dev) * 2.0)
+    src = (torch.randn((n, T, d), generator=g, device=dev) * scales).to(tdt)
+    w = torch.randn((d,), generator=g, device=dev) * qs
+    kg = torch.rand((d,), generator=g, device=dev) * 0.4 + 0.8
+    gm = torch.rand((d,), generator=g, device=dev) * 0.4 + 0.8
+    dx = torch.randn((T, d), generator=g, device=dev).to(tdt)
+    ws = torch.empty(tdw.attnres_site_backward_workspace_bytes(T, d) // 4 + 4, device=dev)
+    ref = oracle.site_backward(src, w, kg, gm if prenorm else None, 1e-6, dx, prenorm=prenorm)
+    # other contributions of each row's own size (an offset far above a row
+    # would round its increment away in fp32)
+    row_max = torch.from_numpy(np.abs(ref["du"]).max(axis=-1, keepdims=True)).float().to(dev)
+    start = torch.randn((n, T, d), generator=g, device=dev) * row_max
+    acc = start.clone()
+    dw, dkg, dgm = (torch.empty((d,), device=dev) for _ in range(3))
+    tdw.attnres_site_backward_accumulate(src, n, w, kg, gm if prenorm else None, prenorm, 1e-6, dx, acc, dw, dkg,
+                                         dgm if prenorm else None, ws)
+    dsrc = torch.empty_like(src)
+    dw2, dkg2, dgm2 = (torch.empty((d,), device=dev) for _ in range(3))
+    tdw.attnres_site_backward(src, n, w, kg, gm if prenorm else None, prenorm, 1e-6, dx, dsrc, dw2, dkg2,
+                              dgm2 if prenorm else None, ws)
+    torch.cuda.synchronize()
+    inc = _host(acc) - _host(start)
+    err = row_rel_err(inc.reshape(n * T, d), ref["du"].reshape(n * T, d)).max()
+    _say("worst du increment %.3e" % err)
+    assert err <= TOL[dt]
+    assert torch.equal(dw, dw2) and torch.equal(dkg, dkg2)
+    if prenorm:
+        assert torch.equal(dgm, dgm2)
+    # the increment is the storing entry point's gradient before its rounding
+    assert (acc - start - dsrc.float()).abs().max().item() <= \
+        (2.0 ** -8 if dt == "bf16" else 1e-5) * dsrc.float().abs().max().item()
+
+
+FULL_BWD = [
+    # (T, d, L, dtype, group used by the forward)
+    (64, 256, 4, "f32", None),
+    (256, 1024, 16, "bf16", None),     # the Full workload's depth and width: 17 sources at the final site
+    (256, 1024, 16, "bf16", 4),        # same, forward on the grouped two-phase schedule
+    (33, 7168, 6, "bf16", None),
+    (24, 520, 31, "bf16", None),       # 32 sources at the final site, ragged width
+]
+
+
+@pytest.mark.parametrize("T,d,L,dt,group", FULL_BWD)
+def test_full_backward_matches_oracle(T, d, L, dt, group):
+    """Full AttnRes backward (site backward passes accumulating in fp32) on
+    the GPU against the oracle's backward of Block AttnRes with one sublayer
+    per block, which is Full AttnRes (structured notes on arXiv 2603.15031,
+    section 8): dL/dv_l of every sublayer, dL/db_0, dw, dg, dgamma."""
+    _say("case full backward T=%d d=%d L=%d %s group=%s" % (T, d, L, dt, group))
+    dev = torch.device("cuda")
+    base = synth.WORKLOADS["full_bf16"]
+    w = synth.scaled(base, name="full_bwd", T=T, d=d, block_sizes=(1,) * L, seed=8100 + L + d, dtype=dt)
+    scales = synth.sublayer_scales(w)
+    prm = synth.params(w, dev)
+    emb = synth.embedding(w, 0, T, dev)
+    v = [synth.sublayer_output(w, l + 1, 0, T, dev, scales) for l in range(L)]
+    st = tdw.FullAttnRes(T, d, L, w.torch_dtype, eps=w.eps, device=dev, group=group)
+    st.hist[0].copy_(emb)
+    for l in range(L):
+        st.hist[l + 1].copy_(v[l])
+    st.forward(prm, lambda l, x: None)
+    gen = torch.Generator(device=dev).manual_seed(8200 + T + d)
+    dx = [torch.randn((T, d), generator=gen, device=dev).to(w.torch_dtype) for _ in range(L)]
+    dhf = torch.randn((T, d), generator=gen, device=dev).to(w.torch_dtype)
+    dv = [None] * L
+
+    def dx_for(l, g_v):
+        dv[l] = g_v.clone()
+        return dx[l]
+
+    out = st.backward(prm, dx_for, dh_final=dhf)
+    torch.cuda.synchronize()
+    ref = oracle.block_backward(emb, torch.stack(v), prm["w"], prm["g"], prm["gamma"], w.block_sizes, w.eps,
+                                torch.stack(dx), dhf)
+    gpu = {"dv": _host(torch.stack(dv)), "demb": _host(out["demb"]), "dw": _host(out["dw"]),
+           "dg": _host(out["dg"]), "dgamma": _host(out["dgamma"])}
+    tol = TOL[dt]
+    for k, x in gpu.items():
+        e = float(row_rel_err(x, ref[k]).max())
+        _say("worst %s %.3e" % (k, e))
+        assert e <= tol, (k, e)
 
 
 # --------------------------------------------- long context, chunked prefill

@@ -7,6 +7,7 @@ a C ABI declared in ``include/attnres.h``); ``_lib`` binds it with ctypes and
 from ._lib import (attnres_block_accumulate, attnres_full, attnres_phase1, attnres_phase1_first_prenorm,
                    attnres_phase1_workspace_bytes,
                    attnres_phase2_merge, attnres_phase2_merge_multi, attnres_site_backward,
+                   attnres_site_backward_accumulate,
                    attnres_site_backward_workspace_bytes, attnres_phase2_backward,
                    attnres_phase2_backward_workspace_bytes, attnres_phase1_backward,
                    attnres_phase1_backward_workspace_bytes, AttnResError, load, status_string)
@@ -14,6 +15,6 @@ from .driver import BlockAttnRes, FullAttnRes, prefill_chunked
 
 __all__ = ["attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_workspace_bytes", "attnres_phase2_merge", "attnres_phase2_merge_multi",
            "attnres_full", "attnres_block_accumulate", "attnres_site_backward",
-           "attnres_site_backward_workspace_bytes", "attnres_phase2_backward", "attnres_phase2_backward_workspace_bytes",
+           "attnres_site_backward_accumulate", "attnres_site_backward_workspace_bytes", "attnres_phase2_backward", "attnres_phase2_backward_workspace_bytes",
            "attnres_phase1_backward", "attnres_phase1_backward_workspace_bytes", "AttnResError", "load", "status_string", "BlockAttnRes",
            "FullAttnRes", "prefill_chunked"]

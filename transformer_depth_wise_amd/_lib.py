@@ -25,8 +25,9 @@ ATTNRES_MAX_T = 2147483647
 ATTNRES_MAX_QUERIES = 4096
 ATTNRES_MAX_STRIDE = 1 << 40
 
-EXPORTED = ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_workspace_bytes", "attnres_phase2_merge", "attnres_phase2_merge_multi",
-            "attnres_full", "attnres_block_accumulate", "attnres_site_backward", "attnres_site_backward_workspace_bytes",
+EXPORTED = ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_workspace_bytes",
+            "attnres_phase2_merge", "attnres_phase2_merge_multi", "attnres_full", "attnres_block_accumulate",
+            "attnres_site_backward", "attnres_site_backward_accumulate", "attnres_site_backward_workspace_bytes",
             "attnres_phase2_backward", "attnres_phase2_backward_workspace_bytes", "attnres_phase1_backward",
             "attnres_phase1_backward_workspace_bytes", "attnres_status_string")
 
@@ -59,6 +60,7 @@ def load(path: Optional[str] = None):
     lib.attnres_phase2_merge_multi.argtypes = [E, I, I, V, V, V, I, I, V, V, V, F, V, V, V]
     lib.attnres_full.argtypes = [E, V, I, I, I, I, V, V, V, F, V, V, V, V]
     lib.attnres_site_backward.argtypes = [E, V, I, I, I, I, V, V, V, E, F, V, V, I, V, V, V, V, I, V]
+    lib.attnres_site_backward_accumulate.argtypes = lib.attnres_site_backward.argtypes
     lib.attnres_site_backward_workspace_bytes.argtypes = [I, I]
     lib.attnres_site_backward_workspace_bytes.restype = ctypes.c_int64
     lib.attnres_block_accumulate.argtypes = [E, I, I, E, V, V, V, V, V]
@@ -69,9 +71,9 @@ def load(path: Optional[str] = None):
     lib.attnres_phase1_backward.argtypes = [E, V, I, I, I, I, V, V, I, F, V, I, V, V, V, I, E, V, V, V, I, V]
     lib.attnres_phase1_backward_workspace_bytes.argtypes = [I, I, I, I]
     lib.attnres_phase1_backward_workspace_bytes.restype = ctypes.c_int64
-    for fn in ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase2_merge", "attnres_phase2_merge_multi", "attnres_full",
-               "attnres_block_accumulate", "attnres_site_backward", "attnres_phase2_backward",
-               "attnres_phase1_backward"):
+    for fn in ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase2_merge", "attnres_phase2_merge_multi",
+               "attnres_full", "attnres_block_accumulate", "attnres_site_backward",
+               "attnres_site_backward_accumulate", "attnres_phase2_backward", "attnres_phase1_backward"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.attnres_status_string.argtypes = [ctypes.c_int]
     lib.attnres_status_string.restype = ctypes.c_char_p
@@ -404,6 +406,34 @@ def attnres_site_backward(src: torch.Tensor, n_src: int, w: torch.Tensor, key_ga
                                       _ptr(dprenorm_gain), _ptr(workspace), _workspace(workspace),
                                       _stream(stream))
     _check("attnres_site_backward", rc)
+
+
+def attnres_site_backward_accumulate(src: torch.Tensor, n_src: int, w: torch.Tensor,
+                                     key_gain: Optional[torch.Tensor], prenorm_gain: Optional[torch.Tensor],
+                                     prenorm: bool, eps: float, dx: torch.Tensor, dsrc: torch.Tensor,
+                                     dw: torch.Tensor, dkey_gain: Optional[torch.Tensor],
+                                     dprenorm_gain: Optional[torch.Tensor], workspace: torch.Tensor, stream=None,
+                                     check: bool = True) -> None:
+    """As attnres_site_backward, but dL/du_i is added to dsrc: [>=n_src, T, d]
+    fp32 slabs."""
+    if dx.dim() != 2:
+        raise ValueError("dx must be a [T, d] tensor")
+    T, d = dx.shape
+    if check:
+        dt = _storage(src, "src")
+        _rows(src, "src", T, d, dt, n=n_src)
+        _rows(dx, "dx", T, d, dt)
+        _rows(dsrc, "dsrc", T, d, torch.float32, n=n_src)
+        for t, name in ((w, "w"), (key_gain, "key_gain"), (prenorm_gain, "prenorm_gain"), (dw, "dw"),
+                        (dkey_gain, "dkey_gain"), (dprenorm_gain, "dprenorm_gain")):
+            _fp32(t, name, (d,), optional=name not in ("w", "dw"))
+        _workspace(workspace)
+        _on_device(src, dx, dsrc, w, key_gain, prenorm_gain, dw, dkey_gain, dprenorm_gain, workspace)
+    rc = load().attnres_site_backward_accumulate(
+        dtype_code(src.dtype), _ptr(src), n_src, _slab_stride(src, T, d), T, d, _ptr(w), _ptr(key_gain),
+        _ptr(prenorm_gain), 1 if prenorm else 0, eps, _ptr(dx), _ptr(dsrc), _slab_stride(dsrc, T, d), _ptr(dw),
+        _ptr(dkey_gain), _ptr(dprenorm_gain), _ptr(workspace), _workspace(workspace), _stream(stream))
+    _check("attnres_site_backward_accumulate", rc)
 
 
 def attnres_phase2_backward_workspace_bytes(T: int, d: int) -> int:

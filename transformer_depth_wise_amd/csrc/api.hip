@@ -276,16 +276,18 @@ int64_t attnres_site_backward_workspace_bytes(int64_t T, int64_t d) {
   return attnres::backward_slots(T, (int)d) * 2 * d * (int64_t)sizeof(float);
 }
 
-attnres_status_t attnres_site_backward(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
-                                       int64_t T, int64_t d, const float* w, const float* key_gain,
-                                       const float* prenorm_gain, int prenorm, float eps, const void* dx,
-                                       void* dsrc, int64_t dsrc_stride, float* dw, float* dkey_gain,
-                                       float* dprenorm_gain, void* workspace, int64_t workspace_bytes,
-                                       void* stream) {
+// Shared by the storing and the accumulating entry points: dsrc holds rows
+// of the storage type, or fp32 rows to add to (acc).
+static attnres_status_t site_backward_impl(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
+                                           int64_t T, int64_t d, const float* w, const float* key_gain,
+                                           const float* prenorm_gain, int prenorm, float eps, const void* dx,
+                                           void* dsrc, int64_t dsrc_stride, bool acc, float* dw, float* dkey_gain,
+                                           float* dprenorm_gain, void* workspace, int64_t workspace_bytes,
+                                           void* stream) {
   if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
-  if (!extent_ok(T, {src_stride, dsrc_stride}) || n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || !(eps >= 0.f))
+  if (!extent_ok(T, {src_stride, dsrc_stride}) || n_src < 1 || n_src > ATTNRES_MAX_SOURCES || !(eps >= 0.f))
     return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!src || !w || !dx || !dsrc || !dw) return ATTNRES_EINVAL;
@@ -297,7 +299,7 @@ attnres_status_t attnres_site_backward(attnres_dtype_t dt, const void* src, int6
   if (st != ATTNRES_OK) return st;
   const int64_t es = esize(dt);
   const Range rs = range_of(src, ((n_src - 1) * src_stride + T * d) * es);
-  const Range rds = range_of(dsrc, ((n_src - 1) * dsrc_stride + T * d) * es);
+  const Range rds = range_of(dsrc, ((n_src - 1) * dsrc_stride + T * d) * (acc ? 4 : es));
   const Range rdx = range_of(dx, T * d * es);
   const Range rw = range_of(w, d * 4);
   const Range rg = key_gain ? range_of(key_gain, d * 4) : Range{0, 0};
@@ -315,9 +317,29 @@ attnres_status_t attnres_site_backward(attnres_dtype_t dt, const void* src, int6
       if (overlaps(outs[a], outs[b])) return ATTNRES_EALIAS;
   return hip_status(attnres::launch_site_backward(kind_of(dt), T, (int)d, src, (int)n_src, src_stride, w, key_gain,
                                                   prenorm ? prenorm_gain : nullptr, prenorm ? 1 : 0, eps, dx, dsrc,
-                                                  dsrc_stride, dw, dkey_gain, prenorm ? dprenorm_gain : nullptr,
-                                                  static_cast<float*>(workspace),
+                                                  dsrc_stride, acc ? 1 : 0, dw, dkey_gain,
+                                                  prenorm ? dprenorm_gain : nullptr, static_cast<float*>(workspace),
                                                   static_cast<hipStream_t>(stream)));
+}
+
+attnres_status_t attnres_site_backward(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
+                                       int64_t T, int64_t d, const float* w, const float* key_gain,
+                                       const float* prenorm_gain, int prenorm, float eps, const void* dx,
+                                       void* dsrc, int64_t dsrc_stride, float* dw, float* dkey_gain,
+                                       float* dprenorm_gain, void* workspace, int64_t workspace_bytes,
+                                       void* stream) {
+  return site_backward_impl(dt, src, n_src, src_stride, T, d, w, key_gain, prenorm_gain, prenorm, eps, dx, dsrc,
+                            dsrc_stride, false, dw, dkey_gain, dprenorm_gain, workspace, workspace_bytes, stream);
+}
+
+attnres_status_t attnres_site_backward_accumulate(attnres_dtype_t dt, const void* src, int64_t n_src,
+                                                  int64_t src_stride, int64_t T, int64_t d, const float* w,
+                                                  const float* key_gain, const float* prenorm_gain, int prenorm,
+                                                  float eps, const void* dx, float* dsrc, int64_t dsrc_stride,
+                                                  float* dw, float* dkey_gain, float* dprenorm_gain, void* workspace,
+                                                  int64_t workspace_bytes, void* stream) {
+  return site_backward_impl(dt, src, n_src, src_stride, T, d, w, key_gain, prenorm_gain, prenorm, eps, dx, dsrc,
+                            dsrc_stride, true, dw, dkey_gain, dprenorm_gain, workspace, workspace_bytes, stream);
 }
 
 int64_t attnres_phase2_backward_workspace_bytes(int64_t T, int64_t d) {

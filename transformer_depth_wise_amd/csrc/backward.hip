@@ -26,12 +26,14 @@
 // and the dgamma sums are accumulated per thread over the team's tokens,
 // written per team to the workspace, and summed over teams in a fixed order
 // by a second kernel: no atomics, bitwise reproducible.
+#include <type_traits>
+
 #include "attnres_device.h"
 #include "attnres_launch.h"
 
 namespace attnres {
 
-constexpr int kBwdMax = 16;   // sources per site
+constexpr int kBwdMax = 32;   // sources per site
 constexpr int kBwdBatch = 4;  // rows loaded per batch
 
 // Fixed-order sum of v[0..NV) over the team (NW waves): DPP wave sums, then
@@ -58,11 +60,15 @@ __device__ __forceinline__ void team_reduce(float (&v)[NV], float* buf, int wv, 
   }
 }
 
-template <typename St, int TEAM, int CPL, bool HOLD, int NR>
+// ACC: dsrc holds fp32 rows and dL/du_i is added to them; otherwise dL/du_i
+// is stored in the storage type.
+template <typename St, int TEAM, int CPL, bool HOLD, int NR, bool ACC>
 __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
     int64_t T, int d, const St* __restrict__ src, int n, int64_t stride, const float* __restrict__ w,
     const float* __restrict__ kg, const float* __restrict__ gamma, int prenorm, float eps,
-    const St* __restrict__ dx, St* __restrict__ dsrc, int64_t dstride, float* __restrict__ part) {
+    const St* __restrict__ dx, void* __restrict__ dsrc_v, int64_t dstride, float* __restrict__ part) {
+  using Dt = typename std::conditional<ACC, float, St>::type;
+  Dt* const dsrc = static_cast<Dt*>(dsrc_v);
   constexpr int WG = TEAM < 256 ? 256 : TEAM;
   constexpr int TPW = WG / TEAM;
   constexpr int NW = TEAM / kWave;
@@ -222,8 +228,9 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
         M = fmaxf(M, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(M), 0x4E, 0xF, 0xF, false)));
         M = fmaxf(M, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(M), 0x141, 0xF, 0xF, false)));
         M = fmaxf(M, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(M), 0x140, 0xF, 0xF, false)));
+        if (NR > 16) M = fmaxf(M, __shfl_xor(M, 16));  // rows of 16 lanes: 0-15 with 16-31
         const float e = src_lane ? expf(zi - M) : 0.f;
-        const float den = wave_sum_dpp(e);  // lanes >= 16 hold zeros
+        const float den = wave_sum_dpp(e);  // lanes >= n hold zeros
         if (src_lane) {
           s_ri[lane] = ri;
           s_z[lane] = zi;
@@ -348,6 +355,15 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
           Chunk<St> u[kB];
 #pragma unroll
           for (int r = 0; r < kB; ++r) u[r] = row(b0 + r, c8);
+          // ACC: the batch's earlier contributions, loaded together before
+          // its stores (a load after a store of the same array would wait)
+          float old[ACC ? kB : 1][8];
+          if constexpr (ACC) {
+#pragma unroll
+            for (int r = 0; r < kB; ++r)
+              if (b0 + r < n && live && ok[c8])
+                load8(dsrc + (int64_t)(b0 + r) * dstride + tok * d + cc[c8] * 8, old[r]);
+          }
 #pragma unroll
           for (int r = 0; r < kB; ++r) {
             const int i = b0 + r;
@@ -361,7 +377,13 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
                 o[e] = fmaf(a, gdx[c8][e], g * ri * (q[e] - y * zi * inv_d));
                 tA[e] = fmaf(g, y, tA[e]);
               }
-              if (live && ok[c8]) store8(dsrc + (int64_t)i * dstride + tok * d + cc[c8] * 8, o);
+              if (live && ok[c8]) {
+                if constexpr (ACC) {
+#pragma unroll
+                  for (int e = 0; e < 8; ++e) o[e] += old[r][e];
+                }
+                store8(dsrc + (int64_t)i * dstride + tok * d + cc[c8] * 8, o);
+              }
             }
           }
         }
@@ -397,23 +419,43 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
     }
 }
 
-// Sum the per-team partials in slot order; dw = g (.) A, dg = w (.) A,
-// dgamma = the dgamma sum.  One thread per channel.
-__global__ __launch_bounds__(256) void k_site_backward_reduce(int64_t slots, int d, const float* __restrict__ part,
-                                                              const float* __restrict__ w,
-                                                              const float* __restrict__ kg,
-                                                              float* __restrict__ dw, float* __restrict__ dkg,
-                                                              float* __restrict__ dgamma) {
-  const int k = blockIdx.x * 256 + threadIdx.x;
-  if (k >= d) return;
+// Sum the per-team partials part[slot][0..1][d] in a fixed order: wave q of
+// a workgroup adds a contiguous sixteenth of the slots for 64 channels, then
+// the first wave adds the sixteen partial sums in wave order.  dw = g (.) A,
+// dg = w (.) A, dgamma = G; with `add` they are added to the outputs instead
+// of written.
+constexpr int kRedWaves = 16;
+
+__global__ __launch_bounds__(64 * kRedWaves) void k_wgrad_reduce(int64_t slots, int d,
+                                                                 const float* __restrict__ part,
+                                                                 const float* __restrict__ w,
+                                                                 const float* __restrict__ kg,
+                                                                 float* __restrict__ dw, float* __restrict__ dkg,
+                                                                 float* __restrict__ dgamma, int add) {
+  __shared__ float sums[kRedWaves][2][64];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int k = blockIdx.x * 64 + lane;
+  const int kc = k < d ? k : d - 1;
+  const int64_t s0 = (slots * q) / kRedWaves, s1 = (slots * (q + 1)) / kRedWaves;
   float A = 0.f, G = 0.f;
-  for (int64_t s = 0; s < slots; ++s) {
-    A += part[s * 2 * (int64_t)d + k];
-    G += part[s * 2 * (int64_t)d + d + k];
+  for (int64_t s = s0; s < s1; ++s) {
+    A += part[s * 2 * (int64_t)d + kc];
+    G += part[s * 2 * (int64_t)d + d + kc];
   }
-  dw[k] = kg ? kg[k] * A : A;
-  if (dkg) dkg[k] = w[k] * A;
-  if (dgamma) dgamma[k] = G;
+  sums[q][0][lane] = A;
+  sums[q][1][lane] = G;
+  lds_barrier();
+  if (q == 0 && k < d) {
+    A = 0.f, G = 0.f;
+    for (int r = 0; r < kRedWaves; ++r) {
+      A += sums[r][0][lane];
+      G += sums[r][1][lane];
+    }
+    const float a = kg ? kg[k] * A : A;
+    if (dw) dw[k] = add ? dw[k] + a : a;
+    if (dkg) dkg[k] = add ? dkg[k] + w[k] * A : w[k] * A;
+    if (dgamma) dgamma[k] = add ? dgamma[k] + G : G;
+  }
 }
 
 int backward_team(int d) {
@@ -431,7 +473,7 @@ int64_t backward_slots(int64_t T, int d) {
   return (wgs < 1024 ? wgs : 1024) * tpw;
 }
 
-template <typename St, int TEAM, int CPL, bool HOLD, int NR>
+template <typename St, int TEAM, int CPL, bool HOLD, int NR, bool ACC>
 static hipError_t run_bwd(int64_t T, int d, const void* src, int n, int64_t stride, const float* w,
                           const float* kg, const float* gamma, int prenorm, float eps, const void* dx, void* dsrc,
                           int64_t dstride, float* dw, float* dkg, float* dgamma, float* part, hipStream_t stream) {
@@ -443,39 +485,44 @@ static hipError_t run_bwd(int64_t T, int d, const void* src, int n, int64_t stri
   if (wgs > 1024) wgs = 1024;
   const size_t lds = HOLD ? sizeof(float) * ((size_t)2 * CPL * 8 * WG + (size_t)d) : 0;
   if (lds > 48 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_site_backward<St, TEAM, CPL, HOLD, NR>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(k_site_backward<St, TEAM, CPL, HOLD, NR, ACC>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_site_backward<St, TEAM, CPL, HOLD, NR>), dim3((unsigned)wgs), dim3(WG), lds, stream, T, d,
-                     static_cast<const St*>(src), n, stride, w, kg, gamma, prenorm, eps, static_cast<const St*>(dx),
-                     static_cast<St*>(dsrc), dstride, part);
+  hipLaunchKernelGGL((k_site_backward<St, TEAM, CPL, HOLD, NR, ACC>), dim3((unsigned)wgs), dim3(WG), lds, stream, T,
+                     d, static_cast<const St*>(src), n, stride, w, kg, gamma, prenorm, eps, static_cast<const St*>(dx),
+                     dsrc, dstride, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_site_backward_reduce, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, stream, wgs * TPW, d,
-                     part, w, kg, dw, dkg, prenorm ? dgamma : nullptr);
+  hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((d + 63) / 64)), dim3(64 * kRedWaves), 0, stream, wgs * TPW, d,
+                     part, w, kg, dw, dkg, prenorm ? dgamma : nullptr, 0);
   return hipGetLastError();
 }
 
-template <typename St>
+// More than 16 sources: the rows are re-read from L2 in every pass instead
+// of held in registers.
+template <typename St, bool ACC>
 static hipError_t pick_bwd(int64_t T, int d, const void* src, int n, int64_t stride, const float* w, const float* kg,
                            const float* gamma, int prenorm, float eps, const void* dx, void* dsrc, int64_t dstride,
                            float* dw, float* dkg, float* dgamma, float* part, hipStream_t stream) {
   const int C = d >> 3;
-#define ATTNRES_BWD(TEAM_, CPL_, HOLD_, NR_)                                                                     \
-  return run_bwd<St, TEAM_, CPL_, HOLD_, NR_>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, dstride, \
-                                              dw, dkg, dgamma, part, stream)
-#define ATTNRES_BWD_HOLD(TEAM_, CPL_)       \
-  do {                                      \
-    if (n <= 8) ATTNRES_BWD(TEAM_, CPL_, true, 8);   \
-    if (n <= 12) ATTNRES_BWD(TEAM_, CPL_, true, 12); \
-    ATTNRES_BWD(TEAM_, CPL_, true, 16);             \
+#define ATTNRES_BWD(TEAM_, CPL_, HOLD_, NR_)                                                                  \
+  return run_bwd<St, TEAM_, CPL_, HOLD_, NR_, ACC>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, \
+                                                   dstride, dw, dkg, dgamma, part, stream)
+#define ATTNRES_BWD_HOLD(TEAM_, CPL_)                  \
+  do {                                                 \
+    if (n > 16) ATTNRES_BWD(TEAM_, CPL_, false, 32);   \
+    if (n <= 8) ATTNRES_BWD(TEAM_, CPL_, true, 8);     \
+    if (n <= 12) ATTNRES_BWD(TEAM_, CPL_, true, 12);   \
+    ATTNRES_BWD(TEAM_, CPL_, true, 16);               \
   } while (0)
   if (C <= 64) ATTNRES_BWD_HOLD(64, 1);
   if (C <= 128) ATTNRES_BWD_HOLD(64, 2);
   if (C <= 256) ATTNRES_BWD_HOLD(256, 1);
   if (C <= 512) ATTNRES_BWD_HOLD(512, 1);
   if (C <= 1024) ATTNRES_BWD_HOLD(512, 2);
+  if (n > 16) ATTNRES_BWD(1024, 2, false, 32);
   ATTNRES_BWD(1024, 2, false, 16);
 #undef ATTNRES_BWD_HOLD
 #undef ATTNRES_BWD
@@ -483,13 +530,18 @@ static hipError_t pick_bwd(int64_t T, int d, const void* src, int n, int64_t str
 
 hipError_t launch_site_backward(Dtype dt, int64_t T, int d, const void* src, int n, int64_t stride, const float* w,
                                 const float* kg, const float* gamma, int prenorm, float eps, const void* dx,
-                                void* dsrc, int64_t dstride, float* dw, float* dkg, float* dgamma, float* part,
-                                hipStream_t stream) {
-  if (dt == kBF16)
-    return pick_bwd<bf16_t>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, dstride, dw, dkg, dgamma,
-                            part, stream);
-  return pick_bwd<float>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, dstride, dw, dkg, dgamma, part,
-                         stream);
+                                void* dsrc, int64_t dstride, int accumulate, float* dw, float* dkg, float* dgamma,
+                                float* part, hipStream_t stream) {
+#define ATTNRES_SB(ST_, ACC_)                                                                                      \
+  return pick_bwd<ST_, ACC_>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, dstride, dw, dkg, dgamma, \
+                             part, stream)
+  if (dt == kBF16) {
+    if (accumulate) ATTNRES_SB(bf16_t, true);
+    ATTNRES_SB(bf16_t, false);
+  }
+  if (accumulate) ATTNRES_SB(float, true);
+  ATTNRES_SB(float, false);
+#undef ATTNRES_SB
 }
 
 
@@ -837,43 +889,6 @@ __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_p2_bwd(
   }
 }
 
-// Add the per-team sums: dw += g (.) A, dg += w (.) A, dgamma += the dgamma
-// sum.  A workgroup takes 64 channels; its 16 waves sum contiguous sixteenths
-// of the slots, and the partial sums are added in wave order through LDS (a
-// fixed order: bitwise reproducible).
-constexpr int kRedWaves = 16;
-
-__global__ __launch_bounds__(64 * kRedWaves) void k_p2_bwd_reduce(int64_t slots, int d,
-                                                                  const float* __restrict__ part,
-                                                                  const float* __restrict__ w,
-                                                                  const float* __restrict__ kg,
-                                                                  float* __restrict__ dw, float* __restrict__ dkg,
-                                                                  float* __restrict__ dgamma) {
-  __shared__ float sums[kRedWaves][2][64];
-  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
-  const int k = blockIdx.x * 64 + lane;
-  const int kc = k < d ? k : d - 1;
-  const int64_t s0 = (slots * q) / kRedWaves, s1 = (slots * (q + 1)) / kRedWaves;
-  float A = 0.f, G = 0.f;
-  for (int64_t s = s0; s < s1; ++s) {
-    A += part[s * 2 * (int64_t)d + kc];
-    G += part[s * 2 * (int64_t)d + d + kc];
-  }
-  sums[q][0][lane] = A;
-  sums[q][1][lane] = G;
-  lds_barrier();
-  if (q == 0 && k < d) {
-    A = 0.f, G = 0.f;
-    for (int r = 0; r < kRedWaves; ++r) {
-      A += sums[r][0][lane];
-      G += sums[r][1][lane];
-    }
-    if (dw) dw[k] += kg ? kg[k] * A : A;
-    if (dkg) dkg[k] += w[k] * A;
-    if (dgamma) dgamma[k] += G;
-  }
-}
-
 // Teams of the phase-2 backward by row width (each thread one or two chunks).
 static void p2b_team(int d, int& team, int& cpl) {
   const int C = d >> 3;
@@ -940,9 +955,8 @@ static hipError_t run_p2b(int64_t T, int d, const void* o1, const float* lse1, c
 #undef ATTNRES_P2B
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_p2_bwd_reduce, dim3((unsigned)((d + 63) / 64)), dim3(64 * kRedWaves), 0, stream, wgs * TPW, d,
-                     part, w,
-                     kg, vprev ? dw : nullptr, vprev ? dkg : nullptr, prenorm ? dgamma : nullptr);
+  hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((d + 63) / 64)), dim3(64 * kRedWaves), 0, stream, wgs * TPW, d,
+                     part, w, kg, vprev ? dw : nullptr, vprev ? dkg : nullptr, prenorm ? dgamma : nullptr, 1);
   return hipGetLastError();
 }
 

@@ -37,6 +37,7 @@ import torch
 
 from . import _lib
 from ._lib import (attnres_block_accumulate, attnres_full, attnres_phase1, attnres_phase1_backward,
+                   attnres_site_backward_accumulate,
                    attnres_phase1_first_prenorm, attnres_phase2_backward, attnres_phase2_merge,
                    attnres_phase2_merge_multi)
 
@@ -536,6 +537,63 @@ class FullAttnRes:
                          self.h_final, None, None, stream=stream, check=False)
             mark("final", False)
         return self.h_final
+
+    def plan_backward(self) -> List[Launch]:
+        """Algorithmic bytes of ``backward``: per site its sources and dx
+        (storage type) once, and the sources' fp32 gradient rows read and
+        written once."""
+        r = self.T * self.d * _esize(self.dtype)
+        r32 = self.T * self.d * 4
+        out = []
+        if self.final_site:
+            out.append(Launch("final_backward", (self.L + 1) * (r + 2 * r32) + r))
+        for l in range(self.L - 1, -1, -1):
+            out.append(Launch("site_backward", (l + 1) * (r + 2 * r32) + r))
+        return out
+
+    def backward(self, params: Dict[str, torch.Tensor], dx_for: Callable[[int, torch.Tensor], torch.Tensor],
+                 dh_final: Optional[torch.Tensor] = None, stream=None,
+                 instrument: Optional[Callable[[str, bool], None]] = None) -> Dict[str, torch.Tensor]:
+        """Backward of the last ``forward`` (``hist`` unchanged since), sites
+        in reverse order.  Both schedules compute the same sites, so both have
+        the one-shot sites' gradient.  Every representation feeds all later
+        sites ("Attention Residuals" notes, section 7), so its gradient is a
+        sum over sites, accumulated in one fp32 row per representation.
+        ``dx_for(l, dv_l)`` is the sublayer's backward: it receives dL/dv_l
+        (= dL/dhist[l+1], fp32 [T, d], complete once every later site has run;
+        valid only during the call) and returns dL/dx_l ([T, d], storage
+        dtype).  ``dh_final``: dL/dh_final (needed with the final site).
+        Returns fp32 ``demb`` [T, d], ``dw``, ``dg`` [L+1, d], ``dgamma`` [L, d]."""
+        if self.final_site and dh_final is None:
+            raise ValueError("dh_final is required with the final aggregation site")
+        T, d, L, eps = self.T, self.d, self.L, self.eps
+        dev = self.hist.device
+        _check_params(params, d, L + (1 if self.final_site else 0), L, dev)
+        if self.final_site:
+            _checked_rows(dh_final, "dh_final", T, d, self.dtype)
+        w, g, gam = params["w"], params.get("g"), params.get("gamma")
+        mark = instrument if instrument is not None else (lambda kind, begin: None)
+        dH = torch.zeros((L + 1, T, d), dtype=torch.float32, device=dev)
+        dw = torch.zeros((L + 1, d), dtype=torch.float32, device=dev)
+        dg = torch.zeros((L + 1, d), dtype=torch.float32, device=dev)
+        dgamma = torch.zeros((max(L, 1), d), dtype=torch.float32, device=dev)
+        ws = torch.empty((max(_lib.attnres_site_backward_workspace_bytes(T, d), 16) + 3) // 4,
+                         dtype=torch.float32, device=dev)
+        if self.final_site:
+            mark("final_backward", True)
+            attnres_site_backward_accumulate(self.hist, L + 1, w[L], None if g is None else g[L], None, False, eps,
+                                             dh_final, dH, dw[L], None if g is None else dg[L], None, ws,
+                                             stream=stream, check=False)
+            mark("final_backward", False)
+        for l in range(L - 1, -1, -1):
+            dx = _checked_rows(dx_for(l, dH[l + 1]), "dL/dx of sublayer %d" % l, T, d, self.dtype)
+            mark("site_backward", True)
+            attnres_site_backward_accumulate(self.hist, l + 1, w[l], None if g is None else g[l],
+                                             None if gam is None else gam[l], True, eps, dx, dH, dw[l],
+                                             None if g is None else dg[l], dgamma[l], ws, stream=stream,
+                                             check=False)
+            mark("site_backward", False)
+        return {"demb": dH[0], "dw": dw, "dg": dg, "dgamma": dgamma[:L]}
 
 
 def prefill_chunked(T_total: int, chunk: int, d: int, block_sizes: Sequence[int], dtype: torch.dtype,
