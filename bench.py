@@ -200,6 +200,42 @@ def backward_report(dev, steps: int):
     return out
 
 
+def full_backward_report(fulls, prm, steps: int) -> dict:
+    """Backward of Full AttnRes over resident outputs (site backward passes
+    accumulating every representation's gradient in fp32), rotating over the
+    given FullAttnRes states; the synthetic sublayer backward returns another
+    resident output row as dL/dx_l."""
+    f0 = fulls[0]
+    L = f0.L
+    dxs = [f0.hist[(l + 2) % (L + 1)] for l in range(L)]
+    dxf = lambda l, dv: dxs[l]  # noqa: E731
+    for f in fulls:
+        f.backward(prm, dxf, dh_final=f.hist[1])
+    nf = len(fulls)
+    sec = _time(lambda k: fulls[k % nf].backward(prm, dxf, dh_final=fulls[k % nf].hist[1]), max(steps, 20))
+    b = sum(x.bytes for x in f0.plan_backward())
+    return {"config": {"T": f0.T, "d": f0.d, "sublayers": L, "schedule": "site backward, reverse"},
+            "ms_per_step": round(sec * 1e3, 4), "value": round(f0.T * L / sec, 1),
+            "unit": "token-sublayers/s", "hbm_gbps": round(b / sec / 1e9, 1), "bytes_per_step": b,
+            "note": "includes zeroing the fp32 gradient rows and parameter gradients"}
+
+
+def full_states(w, dev, replicas: int):
+    """FullAttnRes states over resident synthetic outputs of workload w."""
+    import synth
+    import transformer_depth_wise_amd as tdw
+    prm = synth.params(w, dev)
+    scales = synth.sublayer_scales(w)
+    fulls = []
+    for r in range(replicas):
+        f = tdw.FullAttnRes(w.T, w.d, w.L, w.torch_dtype, eps=w.eps, device=dev, final_site=w.final_site)
+        f.hist[0].copy_(synth.embedding(w, 0, w.T, dev))
+        for l in range(w.L):
+            f.hist[l + 1].copy_(synth.sublayer_output(w, l + 1, 0, w.T, dev, scales))
+        fulls.append(f)
+    return fulls, prm
+
+
 def io_model(w, rows) -> dict:
     """The measured path's algorithmic rows per token and sublayer beside the
     pages' analytic residual I/O per layer (rows of d): at this workload's
@@ -280,15 +316,7 @@ def other_workloads(dev, steps: int):
 
     # Full AttnRes: every sublayer output its own source, one-shot per site
     w = synth.WORKLOADS["full_bf16"]
-    prm = synth.params(w, dev)
-    scales = synth.sublayer_scales(w)
-    fulls = []
-    for r in range(4):
-        f = tdw.FullAttnRes(w.T, w.d, w.L, w.torch_dtype, eps=w.eps, device=dev, final_site=w.final_site)
-        f.hist[0].copy_(synth.embedding(w, 0, w.T, dev))
-        for l in range(w.L):
-            f.hist[l + 1].copy_(synth.sublayer_output(w, l + 1, 0, w.T, dev, scales))
-        fulls.append(f)
+    fulls, prm = full_states(w, dev, 4)
     noop = lambda l, x: None  # noqa: E731  (outputs are resident in hist)
     for f in fulls:
         f.forward(prm, noop)
@@ -314,21 +342,7 @@ def other_workloads(dev, steps: int):
                                  "ms_per_step": round(sec * 1e3, 4), "value": round(w.T * w.L / sec, 1),
                                  "unit": "token-sublayers/s", "hbm_gbps": round(b / sec / 1e9, 1),
                                  "bytes_per_step": b}
-    # the backward of Full AttnRes over the same outputs (site backward passes
-    # accumulating every representation's gradient in fp32); the synthetic
-    # sublayer backward returns another resident output row as dL/dx_l
-    dxs = [fulls[0].hist[(l + 2) % (w.L + 1)] for l in range(w.L)]
-    dxf = lambda l, dv: dxs[l]  # noqa: E731
-    for f in fulls:
-        f.backward(prm, dxf, dh_final=f.hist[1])
-    sec = _time(lambda k: fulls[k % 4].backward(prm, dxf, dh_final=fulls[k % 4].hist[1]), max(steps, 20))
-    b = sum(x.bytes for x in fulls[0].plan_backward())
-    res[w.name + "_backward"] = {"config": {"T": w.T, "d": w.d, "sublayers": w.L,
-                                            "schedule": "site backward, reverse"},
-                                 "ms_per_step": round(sec * 1e3, 4), "value": round(w.T * w.L / sec, 1),
-                                 "unit": "token-sublayers/s", "hbm_gbps": round(b / sec / 1e9, 1),
-                                 "bytes_per_step": b,
-                                 "note": "includes zeroing the fp32 gradient rows and parameter gradients"}
+    res[w.name + "_backward"] = full_backward_report(fulls, prm, steps)
     del fulls, grouped
 
     # backward of one aggregation site at the 16K chunk's final-site shape
@@ -377,7 +391,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the decode / Full / per-GPU-share workloads")
     ap.add_argument("--backward", action="store_true",
-                    help="time only the backward through the 16K chunk's block structure (one JSON line)")
+                    help="time only a backward (one JSON line): through the 16K chunk's block structure, or "
+                         "with --workload full_bf16 that of Full AttnRes")
     ap.add_argument("--probe", choices=["copy"], default=None,
                     help="run only a plain device copy of known size (counter calibration)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -409,11 +424,16 @@ def main() -> int:
         print(json.dumps({"probe": "copy", "bytes_read_per_dispatch": a.numel() * 2,
                           "bytes_written_per_dispatch": b.numel() * 2, "dispatches": 4}), flush=True)
         return 0
+    w = synth.WORKLOADS[args.workload]
+    if args.backward and w.full:
+        fulls, prm = full_states(w, dev, 4)
+        print(json.dumps({"metric": "AttnRes backward token-sublayers/s (Full AttnRes, %s)" % w.name,
+                          **full_backward_report(fulls, prm, args.steps)}), flush=True)
+        return 0
     if args.backward:
         print(json.dumps({"metric": "AttnRes backward token-sublayers/s (block structure, 16K chunk)",
                           **backward_report(dev, args.steps)}), flush=True)
         return 0
-    w = synth.WORKLOADS[args.workload]
     if w.chunk:
         print(json.dumps(long_prefill_report(w, dev)), flush=True)
         return 0

@@ -438,6 +438,9 @@ __global__ __launch_bounds__(64 * kRedWaves) void k_wgrad_reduce(int64_t slots, 
   const int kc = k < d ? k : d - 1;
   const int64_t s0 = (slots * q) / kRedWaves, s1 = (slots * (q + 1)) / kRedWaves;
   float A = 0.f, G = 0.f;
+  // unrolled so that eight slots' loads are in flight at once; the adds
+  // keep slot order
+#pragma unroll 8
   for (int64_t s = s0; s < s1; ++s) {
     A += part[s * 2 * (int64_t)d + kc];
     G += part[s * 2 * (int64_t)d + d + kc];
