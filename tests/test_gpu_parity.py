@@ -629,6 +629,18 @@ def test_full_backward_matches_oracle(T, d, L, dt, group):
         e = float(row_rel_err(x, ref[k]).max())
         _say("worst %s %.3e" % (k, e))
         assert e <= tol, (k, e)
+    # a second backward gives the same bits (fixed-order reductions, no atomics)
+    dv2 = [None] * L
+
+    def dx_for2(l, g_v):
+        dv2[l] = g_v.clone()
+        return dx[l]
+
+    out2 = st.backward(prm, dx_for2, dh_final=dhf)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(dv2, dv))
+    for k in ("demb", "dw", "dg", "dgamma"):
+        assert torch.equal(out2[k], out[k]), k
 
 
 # --------------------------------------------- long context, chunked prefill
