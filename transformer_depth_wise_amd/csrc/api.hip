@@ -317,7 +317,7 @@ static attnres_status_t site_backward_impl(attnres_dtype_t dt, const void* src, 
       if (overlaps(outs[a], outs[b])) return ATTNRES_EALIAS;
   return hip_status(attnres::launch_site_backward(kind_of(dt), T, (int)d, src, (int)n_src, src_stride, w, key_gain,
                                                   prenorm ? prenorm_gain : nullptr, prenorm ? 1 : 0, eps, dx, dsrc,
-                                                  dsrc_stride, acc ? 1 : 0, dw, dkey_gain,
+                                                  dsrc_stride, acc ? 1 : 0, 0, dw, dkey_gain,
                                                   prenorm ? dprenorm_gain : nullptr, static_cast<float*>(workspace),
                                                   static_cast<hipStream_t>(stream)));
 }
@@ -402,9 +402,12 @@ int64_t attnres_phase1_backward_workspace_bytes(int64_t T, int64_t d, int64_t n_
   if (n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || S < 1 || S > 32) return -1;
   if (T == 0) return 0;
   // coefficients [T][S rounded up to 8][n], folded queries [S][d],
-  // per-range weight sums
+  // per-range weight sums; one site (S == 1) may run on the site backward,
+  // whose per-team sums need attnres_site_backward_workspace_bytes
   const int64_t sp = (S + 7) & ~(int64_t)7;
-  return (T * sp * n_src + S * d + attnres::p1_backward_ranges((int)d) * S * d) * (int64_t)sizeof(float);
+  const int64_t need = (T * sp * n_src + S * d + attnres::p1_backward_ranges((int)d) * S * d) * (int64_t)sizeof(float);
+  const int64_t site = S == 1 ? attnres_site_backward_workspace_bytes(T, d) : 0;
+  return need > site ? need : site;
 }
 
 attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,

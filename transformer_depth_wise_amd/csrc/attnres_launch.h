@@ -37,8 +37,8 @@ hipError_t launch_merge_multi(Dtype dt, int64_t T, int d, const void* o1, const 
 
 hipError_t launch_site_backward(Dtype dt, int64_t T, int d, const void* src, int n, int64_t stride, const float* w,
                                 const float* kg, const float* gamma, int prenorm, float eps, const void* dx,
-                                void* dsrc, int64_t dstride, int accumulate, float* dw, float* dkg, float* dgamma,
-                                float* part, hipStream_t stream);
+                                void* dsrc, int64_t dstride, int out_mode, int wadd, float* dw, float* dkg,
+                                float* dgamma, float* part, hipStream_t stream);
 int64_t backward_slots(int64_t T, int d);
 
 // Backward through the block structure (training).  Phase-2 backward of one

@@ -60,14 +60,17 @@ __device__ __forceinline__ void team_reduce(float (&v)[NV], float* buf, int wv, 
   }
 }
 
-// ACC: dsrc holds fp32 rows and dL/du_i is added to them; otherwise dL/du_i
-// is stored in the storage type.
-template <typename St, int TEAM, int CPL, bool HOLD, int NR, bool ACC>
+// OUT: how dL/du_i leaves -- stored in the storage type (kOutStore), added to
+// fp32 rows (kOutAdd) or stored as fp32 rows (kOutF32).
+constexpr int kOutStore = 0, kOutAdd = 1, kOutF32 = 2;
+
+template <typename St, int TEAM, int CPL, bool HOLD, int NR, int OUT>
 __global__ __launch_bounds__(TEAM < 256 ? 256 : TEAM) void k_site_backward(
     int64_t T, int d, const St* __restrict__ src, int n, int64_t stride, const float* __restrict__ w,
     const float* __restrict__ kg, const float* __restrict__ gamma, int prenorm, float eps,
     const St* __restrict__ dx, void* __restrict__ dsrc_v, int64_t dstride, float* __restrict__ part) {
-  using Dt = typename std::conditional<ACC, float, St>::type;
+  constexpr bool ACC = OUT == kOutAdd;
+  using Dt = typename std::conditional<OUT == kOutStore, St, float>::type;
   Dt* const dsrc = static_cast<Dt*>(dsrc_v);
   constexpr int WG = TEAM < 256 ? 256 : TEAM;
   constexpr int TPW = WG / TEAM;
@@ -476,10 +479,11 @@ int64_t backward_slots(int64_t T, int d) {
   return (wgs < 1024 ? wgs : 1024) * tpw;
 }
 
-template <typename St, int TEAM, int CPL, bool HOLD, int NR, bool ACC>
+template <typename St, int TEAM, int CPL, bool HOLD, int NR, int OUT>
 static hipError_t run_bwd(int64_t T, int d, const void* src, int n, int64_t stride, const float* w,
                           const float* kg, const float* gamma, int prenorm, float eps, const void* dx, void* dsrc,
-                          int64_t dstride, float* dw, float* dkg, float* dgamma, float* part, hipStream_t stream) {
+                          int64_t dstride, int wadd, float* dw, float* dkg, float* dgamma, float* part,
+                          hipStream_t stream) {
   constexpr int WG = TEAM < 256 ? 256 : TEAM;
   constexpr int TPW = WG / TEAM;
   int64_t wgs = (T + TPW - 1) / TPW;
@@ -489,30 +493,30 @@ static hipError_t run_bwd(int64_t T, int d, const void* src, int n, int64_t stri
   const size_t lds = HOLD ? sizeof(float) * ((size_t)2 * CPL * 8 * WG + (size_t)d) : 0;
   if (lds > 48 * 1024) {
     const hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(k_site_backward<St, TEAM, CPL, HOLD, NR, ACC>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(k_site_backward<St, TEAM, CPL, HOLD, NR, OUT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_site_backward<St, TEAM, CPL, HOLD, NR, ACC>), dim3((unsigned)wgs), dim3(WG), lds, stream, T,
+  hipLaunchKernelGGL((k_site_backward<St, TEAM, CPL, HOLD, NR, OUT>), dim3((unsigned)wgs), dim3(WG), lds, stream, T,
                      d, static_cast<const St*>(src), n, stride, w, kg, gamma, prenorm, eps, static_cast<const St*>(dx),
                      dsrc, dstride, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((d + 63) / 64)), dim3(64 * kRedWaves), 0, stream, wgs * TPW, d,
-                     part, w, kg, dw, dkg, prenorm ? dgamma : nullptr, 0);
+                     part, w, kg, dw, dkg, prenorm ? dgamma : nullptr, wadd);
   return hipGetLastError();
 }
 
 // More than 16 sources: the rows are re-read from L2 in every pass instead
 // of held in registers.
-template <typename St, bool ACC>
+template <typename St, int OUT>
 static hipError_t pick_bwd(int64_t T, int d, const void* src, int n, int64_t stride, const float* w, const float* kg,
                            const float* gamma, int prenorm, float eps, const void* dx, void* dsrc, int64_t dstride,
-                           float* dw, float* dkg, float* dgamma, float* part, hipStream_t stream) {
+                           int wadd, float* dw, float* dkg, float* dgamma, float* part, hipStream_t stream) {
   const int C = d >> 3;
 #define ATTNRES_BWD(TEAM_, CPL_, HOLD_, NR_)                                                                  \
-  return run_bwd<St, TEAM_, CPL_, HOLD_, NR_, ACC>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, \
-                                                   dstride, dw, dkg, dgamma, part, stream)
+  return run_bwd<St, TEAM_, CPL_, HOLD_, NR_, OUT>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, \
+                                                   dstride, wadd, dw, dkg, dgamma, part, stream)
 #define ATTNRES_BWD_HOLD(TEAM_, CPL_)                  \
   do {                                                 \
     if (n > 16) ATTNRES_BWD(TEAM_, CPL_, false, 32);   \
@@ -533,17 +537,19 @@ static hipError_t pick_bwd(int64_t T, int d, const void* src, int n, int64_t str
 
 hipError_t launch_site_backward(Dtype dt, int64_t T, int d, const void* src, int n, int64_t stride, const float* w,
                                 const float* kg, const float* gamma, int prenorm, float eps, const void* dx,
-                                void* dsrc, int64_t dstride, int accumulate, float* dw, float* dkg, float* dgamma,
-                                float* part, hipStream_t stream) {
-#define ATTNRES_SB(ST_, ACC_)                                                                                      \
-  return pick_bwd<ST_, ACC_>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, dstride, dw, dkg, dgamma, \
-                             part, stream)
+                                void* dsrc, int64_t dstride, int out_mode, int wadd, float* dw, float* dkg,
+                                float* dgamma, float* part, hipStream_t stream) {
+#define ATTNRES_SB(ST_, OUT_)                                                                                    \
+  return pick_bwd<ST_, OUT_>(T, d, src, n, stride, w, kg, gamma, prenorm, eps, dx, dsrc, dstride, wadd, dw, dkg, \
+                             dgamma, part, stream)
   if (dt == kBF16) {
-    if (accumulate) ATTNRES_SB(bf16_t, true);
-    ATTNRES_SB(bf16_t, false);
+    if (out_mode == kOutAdd) ATTNRES_SB(bf16_t, kOutAdd);
+    if (out_mode == kOutF32) ATTNRES_SB(bf16_t, kOutF32);
+    ATTNRES_SB(bf16_t, kOutStore);
   }
-  if (accumulate) ATTNRES_SB(float, true);
-  ATTNRES_SB(float, false);
+  // fp32 rows: storing in the storage type is storing fp32
+  if (out_mode == kOutAdd) ATTNRES_SB(float, kOutAdd);
+  ATTNRES_SB(float, kOutStore);
 #undef ATTNRES_SB
 }
 
@@ -1452,6 +1458,12 @@ hipError_t launch_p1_backward(Dtype dt, int64_t T, int d, const void* src, int n
                               const float* w, const float* kg, float eps, const void* gin, int64_t gstride,
                               const float* c_in, const float* gp_in, float* dsrc, int64_t dstride, int accumulate,
                               float* dw, float* dkg, float* ws, hipStream_t stream) {
+  // one site without a partial source (the final aggregation): the site
+  // backward without PreNorm computes the same gradients, with a team per
+  // token instead of one busy wave, into fp32 rows; its weight sums are added
+  if (S == 1 && !c_in && !gp_in)
+    return launch_site_backward(dt, T, d, src, n, stride, w, kg, nullptr, 0, eps, gin, dsrc, dstride,
+                                accumulate ? kOutAdd : kOutF32, 1, dw, dkg, nullptr, ws, stream);
   if (dt == kBF16)
     return pick_p1b<bf16_t>(n, T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
                             dw, dkg, ws, stream);
