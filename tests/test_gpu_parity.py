@@ -596,19 +596,32 @@ def test_full_backward_matches_oracle(T, d, L, dt, group):
     the GPU against the oracle's backward of Block AttnRes with one sublayer
     per block, which is Full AttnRes (structured notes on arXiv 2603.15031,
     section 8): dL/dv_l of every sublayer, dL/db_0, dw, dg, dgamma."""
-    _say("case full backward T=%d d=%d L=%d %s group=%s" % (T, d, L, dt, group))
+    _full_backward_case(T, d, L, dt, group)
+
+
+def test_full_backward_unit_gains_without_final_site():
+    """The same without the final aggregation and with the gains left out
+    (None: ones) on the GPU side."""
+    _full_backward_case(50, 256, 5, "bf16", None, final_site=False, gains=False)
+
+
+def _full_backward_case(T, d, L, dt, group, final_site=True, gains=True):
+    _say("case full backward T=%d d=%d L=%d %s group=%s final=%s gains=%s" % (T, d, L, dt, group, final_site,
+                                                                              gains))
     dev = torch.device("cuda")
     base = synth.WORKLOADS["full_bf16"]
-    w = synth.scaled(base, name="full_bwd", T=T, d=d, block_sizes=(1,) * L, seed=8100 + L + d, dtype=dt)
+    w = synth.scaled(base, name="full_bwd", T=T, d=d, block_sizes=(1,) * L, seed=8100 + L + d, dtype=dt,
+                     final_site=final_site, unit_gains=not gains)
     scales = synth.sublayer_scales(w)
     prm = synth.params(w, dev)
+    gpu_prm = prm if gains else {"w": prm["w"], "g": None, "gamma": None}
     emb = synth.embedding(w, 0, T, dev)
     v = [synth.sublayer_output(w, l + 1, 0, T, dev, scales) for l in range(L)]
-    st = tdw.FullAttnRes(T, d, L, w.torch_dtype, eps=w.eps, device=dev, group=group)
+    st = tdw.FullAttnRes(T, d, L, w.torch_dtype, eps=w.eps, device=dev, group=group, final_site=final_site)
     st.hist[0].copy_(emb)
     for l in range(L):
         st.hist[l + 1].copy_(v[l])
-    st.forward(prm, lambda l, x: None)
+    st.forward(gpu_prm, lambda l, x: None)
     gen = torch.Generator(device=dev).manual_seed(8200 + T + d)
     dx = [torch.randn((T, d), generator=gen, device=dev).to(w.torch_dtype) for _ in range(L)]
     dhf = torch.randn((T, d), generator=gen, device=dev).to(w.torch_dtype)
@@ -618,13 +631,15 @@ def test_full_backward_matches_oracle(T, d, L, dt, group):
         dv[l] = g_v.clone()
         return dx[l]
 
-    out = st.backward(prm, dx_for, dh_final=dhf)
+    out = st.backward(gpu_prm, dx_for, dh_final=dhf if final_site else None)
     torch.cuda.synchronize()
     ref = oracle.block_backward(emb, torch.stack(v), prm["w"], prm["g"], prm["gamma"], w.block_sizes, w.eps,
-                                torch.stack(dx), dhf)
+                                torch.stack(dx), dhf if final_site else None, final_site=final_site)
     gpu = {"dv": _host(torch.stack(dv)), "demb": _host(out["demb"]), "dw": _host(out["dw"]),
            "dg": _host(out["dg"]), "dgamma": _host(out["dgamma"])}
     tol = TOL[dt]
+    if not gains:  # no key gains: their gradient is not computed (stays zero)
+        assert not gpu.pop("dg").any()
     for k, x in gpu.items():
         e = float(row_rel_err(x, ref[k]).max())
         _say("worst %s %.3e" % (k, e))
@@ -636,7 +651,7 @@ def test_full_backward_matches_oracle(T, d, L, dt, group):
         dv2[l] = g_v.clone()
         return dx[l]
 
-    out2 = st.backward(prm, dx_for2, dh_final=dhf)
+    out2 = st.backward(gpu_prm, dx_for2, dh_final=dhf if final_site else None)
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(dv2, dv))
     for k in ("demb", "dw", "dg", "dgamma"):

@@ -563,7 +563,8 @@ class FullAttnRes:
         (= dL/dhist[l+1], fp32 [T, d], complete once every later site has run;
         valid only during the call) and returns dL/dx_l ([T, d], storage
         dtype).  ``dh_final``: dL/dh_final (needed with the final site).
-        Returns fp32 ``demb`` [T, d], ``dw``, ``dg`` [L+1, d], ``dgamma`` [L, d]."""
+        Returns fp32 ``demb`` [T, d], ``dw``, ``dg`` [L+1, d] (``dg`` stays
+        zero without key gains), ``dgamma`` [L, d]."""
         if self.final_site and dh_final is None:
             raise ValueError("dh_final is required with the final aggregation site")
         T, d, L, eps = self.T, self.d, self.L, self.eps
