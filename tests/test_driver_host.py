@@ -77,3 +77,16 @@ def test_workspace_sizes_cover_the_site_backward_for_one_site():
     for T, d, n in ((16384, 7168, 9), (100, 64, 3), (4096, 1024, 17 - 1)):
         assert _lib.attnres_phase1_backward_workspace_bytes(T, d, n, 1) >= \
             _lib.attnres_site_backward_workspace_bytes(T, d)
+
+
+def test_bench_refuses_several_gpus():
+    # one GPU's throughput is the measured value; several GPUs are not run
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "several GPUs is not supported" in r.stderr
+    assert r.stdout == ""
