@@ -57,10 +57,63 @@ def cpu_baseline(w, emb, v, prm, target_s: float):
         "value": round(done * w.L / spent, 1),
         "unit": "token-sublayers/s",
         "cores": oracle.threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": "%d tokens (batches of %d evenly spaced tokens) of the %d-token chunk, all %d sublayers "
                   "+ final site, fp64, %.1f s of oracle time" % (done, batch, w.T, w.L, spent),
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name and logical core count, as the OS reports them."""
+    name = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    import platform
+    return "%s (%d logical cores visible)" % (name or platform.processor() or "unknown", os.cpu_count() or 0)
+
+
+def ceiling(dev, total_bytes: int = 4 << 30, reps: int = 10) -> dict:
+    """Achievable HBM rate of plain streaming kernels (attnres_stream_probe:
+    16-byte accesses, persistent grid-stride loop) with the read/write mixes
+    of the path's kernels: read-only, write-only, copy, and the phase-2
+    merge's two mixes (odd positions read o, the stored partial and v and
+    write x: about 3 reads : 1 write; even positions also read the
+    one-before-last output and store the partial: about 4 : 2).  Each probe
+    moves ``total_bytes`` per dispatch, far beyond the 256 MB last-level
+    cache; the rate is the mean over ``reps`` dispatches timed with HIP
+    events on the launch stream."""
+    import torch
+    import transformer_depth_wise_amd as tdw
+
+    src = torch.empty((total_bytes,), dtype=torch.uint8, device=dev)
+    dst = torch.empty((total_bytes,), dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    stream = torch.cuda.current_stream()
+    out = {"bytes_per_dispatch": total_bytes, "unit": "GB/s",
+           "note": "attnres_stream_probe: the rate a streaming kernel with this read:write mix reaches here"}
+    for name, nr, nw in (("read", 1, 0), ("write", 0, 1), ("copy", 1, 1), ("mix_3r1w", 3, 1),
+                         ("mix_4r2w", 4, 2)):
+        sb = (total_bytes // (nr + nw)) // (1 << 20) * (1 << 20)
+        for _ in range(2):
+            tdw.attnres_stream_probe(nr, nw, src, dst, sb)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            tdw.attnres_stream_probe(nr, nw, src, dst, sb)
+        e1.record(stream)
+        e1.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / reps
+        out[name] = round((nr + nw) * sb / sec / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def measured_traffic(path, kind, workload, alg_bytes_per_launch=None):
@@ -378,6 +431,9 @@ def other_workloads(dev, steps: int):
     torch.cuda.empty_cache()
 
     res["block_backward_prefill_chunk"] = backward_report(dev, steps)
+    torch.cuda.empty_cache()
+    # the long-context workload: 131072 tokens in 16K chunks vs unchunked
+    res["long_prefill_memory"] = long_prefill_report(synth.WORKLOADS["long_prefill_bf16"], dev)
     return res
 
 
@@ -458,6 +514,12 @@ def main() -> int:
     for x in plan:
         kind_bytes[x.kind] = kind_bytes.get(x.kind, 0) + x.bytes
         kind_count[x.kind] = kind_count.get(x.kind, 0) + 1
+    # the scope table's plain row model of the same launches
+    survey = st.plan_survey()
+    survey_bytes = sum(x.bytes for x in survey)
+    survey_kind = {}
+    for x in survey:
+        survey_kind[x.kind] = survey_kind.get(x.kind, 0) + x.bytes
     sub = lambda l, x: v[l]  # noqa: E731
 
     for _ in range(args.warmup):
@@ -524,14 +586,20 @@ def main() -> int:
     for k in kind_ms:
         t_step = kind_ms[k] / steps  # ms per step
         kernels[k] = {"ms_per_step": round(t_step, 4), "launches_per_step": kind_count[k],
-                      "gbps": round(kind_bytes[k] / (t_step * 1e-3) / 1e9, 1),
-                      "bytes_per_step": kind_bytes[k]}
+                      "gbps": round(survey_kind[k] / (t_step * 1e-3) / 1e9, 1),
+                      "bytes_per_step": survey_kind[k],
+                      "path_gbps": round(kind_bytes[k] / (t_step * 1e-3) / 1e9, 1),
+                      "path_bytes_per_step": kind_bytes[k]}
     dom = max(kind_ms, key=lambda k: kind_ms[k])
     launches = kind_count[dom]
     avg_launch_s = kind_ms[dom] / steps / launches * 1e-3
     avg_bytes = kind_bytes[dom] / launches
-    achieved = avg_bytes / avg_launch_s / 1e9
+    avg_survey = survey_kind[dom] / launches
+    achieved = avg_survey / avg_launch_s / 1e9
+    achieved_path = avg_bytes / avg_launch_s / 1e9
     traffic = measured_traffic(args.traffic, dom, w.name, int(avg_bytes))
+    ceil = ceiling(dev)
+    survey_gbps = survey_bytes / (elapsed / steps) / 1e9
     out = {
         "metric": METRIC,
         "value": round(units * steps / elapsed, 1),
@@ -552,22 +620,40 @@ def main() -> int:
         "config": {"workload": w.name, "T": w.T, "d": w.d, "sublayers": w.L,
                    "blocks": list(w.block_sizes), "storage": w.dtype, "partial_sum": st.partial_format,
                    "parallelism": "single GPU"},
-        "hbm_gbps": round(gbps, 1),
-        "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "hbm_gbps": round(survey_gbps, 1),
+        "hbm_frac": round(survey_gbps / PEAK_HBM_GBPS, 4),
+        "bytes_per_step": survey_bytes,
+        "byte_model": "the scope table's rows (phase 1: n + S, merges 2/3/5, block sum 3, final N + 2 rows per "
+                      "token); path_bytes adds what this path really moves beyond it (the 24-bit partial "
+                      "sum's extra byte plane, the stored-every-second-sublayer schedule, statistics)",
+        "path_bytes": {"bytes_per_step": step_bytes, "hbm_gbps": round(gbps, 1),
+                       "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4)},
         "bytes_per_token_sublayer": round(step_bytes / units, 1),
         "rows_per_token_sublayer": round(step_bytes / units / (w.d * w.elem_bytes), 3),
         "io_model": io_model(w, step_bytes / units / (w.d * w.elem_bytes)),
         "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "avg_launch_us": round(avg_launch_s * 1e6, 2), "algorithmic_bytes_per_launch": int(avg_bytes)},
+                     "avg_launch_us": round(avg_launch_s * 1e6, 2),
+                     "algorithmic_bytes_per_launch": int(avg_survey),
+                     "frac_survey_bytes": round(achieved / PEAK_HBM_GBPS, 4),
+                     "path_bytes_per_launch": int(avg_bytes),
+                     "achieved_path_bytes": round(achieved_path, 1),
+                     "frac_path_bytes": round(achieved_path / PEAK_HBM_GBPS, 4),
+                     "frac_of_ceiling": {k: round(achieved_path / ceil[k], 4) for k in ("copy", "mix_3r1w",
+                                                                                         "mix_4r2w")},
+                     "note": "traffic is measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                             "copy-calibrated) and compares with path_bytes_per_launch; frac_of_ceiling "
+                             "divides the path's bytes by the streaming probe's rate at the same mixes"},
+        "ceiling": ceil,
         "cold_cache": {
             "note": "512 MiB scratch write between launches (MALL evicted), AttnRes kernels only",
             "ms_per_step": round(cold_ms, 4),
             "value": round(units / (cold_ms * 1e-3), 1),
-            "hbm_gbps": round(step_bytes / (cold_ms * 1e-3) / 1e9, 1),
-            "kernels_gbps": {k: round(kind_bytes[k] / (cold_kind[k] * 1e-3) / 1e9, 1) for k in cold_kind},
-            "dominant_frac": round(kind_bytes[dom] / (cold_kind[dom] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+            "hbm_gbps": round(survey_bytes / (cold_ms * 1e-3) / 1e9, 1),
+            "path_hbm_gbps": round(step_bytes / (cold_ms * 1e-3) / 1e9, 1),
+            "kernels_path_gbps": {k: round(kind_bytes[k] / (cold_kind[k] * 1e-3) / 1e9, 1) for k in cold_kind},
+            "dominant_frac": round(survey_kind[dom] / (cold_kind[dom] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, emb, v, prm, args.cpu_seconds)

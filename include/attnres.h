@@ -324,7 +324,8 @@ attnres_status_t attnres_site_backward_accumulate(attnres_dtype_t dt,
  *     dw += dL/dw, dkey_gain += dL/dkey_gain ([S][d] fp32) of the block
  *       sources' scores (dkey_gain NULL: not computed),
  *   the [S][d] sums over the tokens in a fixed order.  Limits: 1 <= n_src <=
- *   ATTNRES_MAX_SOURCES_MULTI, 1 <= S <= 32.  Outputs must not overlap any
+ *   ATTNRES_MAX_SOURCES_MULTI (ATTNRES_MAX_SOURCES for one site without
+ *   c_in and gp_in), 1 <= S <= 32.  Outputs must not overlap any
  *   input or each other.  workspace:
  *   attnres_phase1_backward_workspace_bytes(T, d, n_src, S) bytes, 16-byte
  *   aligned (per-token coefficients, w (.) key_gain, per-range sums; for
@@ -366,6 +367,24 @@ attnres_status_t attnres_phase1_backward(attnres_dtype_t dt,
 attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t d,
                                           attnres_dtype_t partial_dt, const void* partial_in,
                                           const void* v2, const void* v, void* out, void* stream);
+
+/*
+ * Streaming-bandwidth probe: a measurement aid that computes nothing of the
+ * aggregation.  It bounds the HBM rate a kernel with a given mix of read and
+ * write streams can reach, the way the aggregation kernels move rows (the
+ * reading notes, "静态 Query 与两阶段计算", ask for the benefit of the
+ * two-phase scheme to be verified against DRAM reads and kernel latency).
+ * Reads n_read streams of stream_bytes each, consecutive from src, and
+ * writes n_write streams, consecutive from dst (16-byte accesses, a wave
+ * covering 1 KiB of consecutive bytes of each stream per instruction).
+ *   0 <= n_read <= 4, 0 <= n_write <= 2, not both zero; stream_bytes a
+ *   positive multiple of 16 (at most 2^40).  With n_write == 0, dst must
+ *   still point at 16 writable bytes (kept as the loads' sink; not written
+ *   for any data these probes read).  The read and written ranges must not
+ *   overlap.  Asynchronous on `stream`, like every other entry point.
+ */
+attnres_status_t attnres_stream_probe(int64_t n_read, int64_t n_write, const void* src, void* dst,
+                                      int64_t stream_bytes, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* attnres_status_string(attnres_status_t status);

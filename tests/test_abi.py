@@ -1,11 +1,19 @@
 """The C-ABI library: it loads, exports every declared symbol, and rejects bad
 arguments before any launch.  Runs without a GPU: every call here fails
-validation (or has T == 0) and returns before touching the HIP runtime."""
+validation (or has T == 0) and returns before touching the HIP runtime.
+
+The calls pass fake device addresses.  With a GPU visible, a validation
+regression would launch kernels on them, so this file refuses to run where a
+device is visible (counting devices does not initialise the runtime)."""
 import ctypes
 import os
 import re
 
 import pytest
+import torch
+
+if torch.cuda.device_count() > 0:
+    pytest.skip("fake-pointer validation tests run only where no GPU is visible", allow_module_level=True)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attnres.h")
@@ -326,3 +334,18 @@ def test_status_strings(lib):
     from transformer_depth_wise_amd import _lib
     for code in range(6):
         assert _lib.status_string(code).startswith("ATTNRES_")
+
+
+def test_stream_probe_validation(lib):
+    def probe(nr=1, nw=1, src=A, dst=64 * A, nbytes=1 << 20):
+        return checked(lib.attnres_stream_probe(nr, nw, p(src), p(dst), nbytes, None))
+    assert probe(nr=5) == EINVAL
+    assert probe(nw=3) == EINVAL
+    assert probe(nr=0, nw=0) == EINVAL
+    assert probe(nbytes=0) == EINVAL
+    assert probe(nbytes=(1 << 20) + 8) == EALIGN
+    assert probe(src=None) == EINVAL
+    assert probe(dst=None) == EINVAL
+    assert probe(src=A + 4) == EALIGN
+    assert probe(dst=A + (1 << 19)) == EALIAS           # written range overlaps the read one
+    assert probe(nr=2, dst=A + (1 << 20)) == EALIAS     # second read stream overlaps the writes

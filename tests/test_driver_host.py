@@ -31,6 +31,22 @@ def test_block_plan_bytes_per_token_sublayer():
     assert sum(x.bytes for x in twice) == 2 * sum(x.bytes for x in plan)
 
 
+def test_block_plan_survey_rows():
+    # the plain row model of the scope table: 1146 rows per token at the 16K
+    # chunk's layout (36 phase-1 reads + 186 phase-1 writes + 890 phase-2 +
+    # 24 block sums + 10 final), 874 of them in the 178 merge launches
+    T, d = 16, 7168
+    st = tdw.BlockAttnRes(T, d, K3, BF, device="cpu")
+    sv = st.plan_survey()
+    r = T * d * 2
+    assert sum(x.bytes for x in sv) == 1146 * r
+    assert sum(x.bytes for x in sv if x.kind == "phase2") == 874 * r
+    assert [x.kind for x in sv] == [x.kind for x in st.plan()]   # the same launches
+    unfused = tdw.BlockAttnRes(T, d, K3, BF, device="cpu", fuse_first=False).plan_survey()
+    assert sum(x.bytes for x in unfused) == 1146 * r
+    assert sum(x.bytes for x in unfused if x.kind == "phase2") == 890 * r
+
+
 def test_block_plan_backward_bytes():
     # the 16K chunk's backward moves 509859266560 bytes (every term is
     # proportional to T): 16 tokens of it move 1/1024 of that
@@ -47,6 +63,23 @@ def test_block_source_limits():
     tdw.BlockAttnRes(4, 64, (1,) * 15 + (2,), BF, device="cpu")      # 16 completed sources for S = 2
 
 
+def test_training_limits_checked_before_any_forward():
+    # the backward's limits are checked when the training state is built,
+    # not after a whole forward: a one-sublayer block with 17 completed
+    # sources runs forward (one query, up to 32 sources) but not backward
+    tdw.BlockAttnRes(4, 64, (1,) * 16, BF, device="cpu")
+    with pytest.raises(ValueError, match="would read 17 completed sources"):
+        tdw.BlockAttnRes(4, 64, (1,) * 17, BF, device="cpu", training=True)
+    with pytest.raises(ValueError, match="at most 32 sublayers per block"):
+        tdw.BlockAttnRes(4, 64, (33,), BF, device="cpu", training=True)
+    tdw.BlockAttnRes(4, 64, (32,) + (1,) * 15, BF, device="cpu", training=True)   # 16 sources, 32 sites
+    # the final site's one-query backward takes up to 32 sources
+    assert _lib.attnres_phase1_backward_workspace_bytes(64, 256, 32, 1) == \
+        _lib.attnres_site_backward_workspace_bytes(64, 256)
+    assert _lib.attnres_phase1_backward_workspace_bytes(64, 256, 17, 2) == -1
+    assert _lib.attnres_phase1_backward_workspace_bytes(64, 256, 33, 1) == -1
+
+
 def test_full_plan_and_limits():
     T, d, L = 8, 64, 16
     f = tdw.FullAttnRes(T, d, L, BF, device="cpu")
@@ -54,6 +87,14 @@ def test_full_plan_and_limits():
     assert sum(x.bytes for x in f.plan_backward()) == \
         sum((l + 1) * (r + 2 * r32) + r for l in range(L + 1))
     assert [x.kind for x in f.plan()].count("full") == L
+    # one-shot sites: site l reads its l sources and writes x; the final site
+    # reads the L + 1 representations and writes h_final.  At the Full
+    # workload's depth (L = 16) that is 152 + 18 = 170 rows per token.
+    rows = sum(x.bytes for x in f.plan() if x.kind in ("full", "final")) / r
+    assert rows == sum(l + 1 for l in range(1, L + 1)) + (L + 2) + (L + 1) * 4 / (d * 2) and \
+        int(rows) == 170
+    kept = tdw.FullAttnRes(T, d, L, BF, device="cpu", keep_h=True)
+    assert sum(x.bytes for x in kept.plan()) == sum(x.bytes for x in f.plan()) + L * r
     with pytest.raises(ValueError, match="at most 32 sources"):
         tdw.FullAttnRes(T, d, 32, BF, device="cpu")
     with pytest.raises(ValueError, match="group size"):

@@ -29,7 +29,7 @@ EXPORTED = ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_wo
             "attnres_phase2_merge", "attnres_phase2_merge_multi", "attnres_full", "attnres_block_accumulate",
             "attnres_site_backward", "attnres_site_backward_accumulate", "attnres_site_backward_workspace_bytes",
             "attnres_phase2_backward", "attnres_phase2_backward_workspace_bytes", "attnres_phase1_backward",
-            "attnres_phase1_backward_workspace_bytes", "attnres_status_string")
+            "attnres_phase1_backward_workspace_bytes", "attnres_stream_probe", "attnres_status_string")
 
 
 class AttnResError(RuntimeError):
@@ -71,7 +71,8 @@ def load(path: Optional[str] = None):
     lib.attnres_phase1_backward.argtypes = [E, V, I, I, I, I, V, V, I, F, V, I, V, V, V, I, E, V, V, V, I, V]
     lib.attnres_phase1_backward_workspace_bytes.argtypes = [I, I, I, I]
     lib.attnres_phase1_backward_workspace_bytes.restype = ctypes.c_int64
-    for fn in ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase2_merge", "attnres_phase2_merge_multi",
+    lib.attnres_stream_probe.argtypes = [I, I, V, V, I, V]
+    for fn in ("attnres_stream_probe", "attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase2_merge", "attnres_phase2_merge_multi",
                "attnres_full", "attnres_block_accumulate", "attnres_site_backward",
                "attnres_site_backward_accumulate", "attnres_phase2_backward", "attnres_phase1_backward"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -534,3 +535,18 @@ def attnres_block_accumulate(partial_in: Optional[torch.Tensor], v: torch.Tensor
     rc = load().attnres_block_accumulate(dtype_code(v.dtype), T, d, _fmt(partial_in), _ptr(partial_in), _ptr(v2),
                                          _ptr(v), _ptr(out), _stream(stream))
     _check("attnres_block_accumulate", rc)
+
+
+def attnres_stream_probe(n_read: int, n_write: int, src: Optional[torch.Tensor], dst: torch.Tensor,
+                         stream_bytes: int, stream=None) -> None:
+    """Streaming-bandwidth probe: read ``n_read`` streams of ``stream_bytes``
+    each from the start of ``src`` and write ``n_write`` streams to ``dst``
+    (which needs at least 16 bytes when nothing is written)."""
+    need_r, need_w = n_read * stream_bytes, max(n_write * stream_bytes, 16)
+    if n_read and (src is None or src.numel() * src.element_size() < need_r or not src.is_contiguous()):
+        raise ValueError("src must be a contiguous tensor of at least %d bytes" % need_r)
+    if dst.numel() * dst.element_size() < need_w or not dst.is_contiguous():
+        raise ValueError("dst must be a contiguous tensor of at least %d bytes" % need_w)
+    _on_device(src, dst)
+    rc = load().attnres_stream_probe(n_read, n_write, _ptr(src), _ptr(dst), stream_bytes, _stream(stream))
+    _check("attnres_stream_probe", rc)

@@ -399,6 +399,10 @@ attnres_status_t attnres_phase2_backward(attnres_dtype_t dt, int64_t T, int64_t 
 
 int64_t attnres_phase1_backward_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int64_t S) {
   if (!extent_ok(T) || d <= 0 || d > ATTNRES_MAX_D || d % 8 != 0) return -1;
+  // one site (S == 1) without c_in / gp_in runs on the site backward, which
+  // takes up to ATTNRES_MAX_SOURCES sources and needs only its per-team sums
+  if (S == 1 && n_src > ATTNRES_MAX_SOURCES_MULTI && n_src <= ATTNRES_MAX_SOURCES)
+    return T == 0 ? 0 : attnres_site_backward_workspace_bytes(T, d);
   if (n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || S < 1 || S > 32) return -1;
   if (T == 0) return 0;
   // coefficients [T][S rounded up to 8][n], folded queries [S][d],
@@ -419,8 +423,12 @@ attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, const void* src, in
   if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
-  if (!extent_ok(T, {src_stride, g_stride, dsrc_stride}) || n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || S < 1 ||
-      S > 32 || !(eps >= 0.f))
+  // one site without c_in / gp_in (the final aggregation) takes as many
+  // sources as the site backward it runs on
+  const bool one_site = S == 1 && !c_in && !gp_in;
+  const int64_t max_src = one_site ? ATTNRES_MAX_SOURCES : ATTNRES_MAX_SOURCES_MULTI;
+  if (!extent_ok(T, {src_stride, g_stride, dsrc_stride}) || n_src < 1 || n_src > max_src || S < 1 || S > 32 ||
+      !(eps >= 0.f))
     return ATTNRES_EINVAL;
   if (gp_in == nullptr && c_in != nullptr) return ATTNRES_EINVAL;  // a partial weight needs its G.p
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
@@ -507,6 +515,21 @@ attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t
   if (!in_place && overlaps(ro, rp)) return ATTNRES_EALIAS;
   return hip_status(attnres::launch_accumulate(kind_of(dt), T, (int)d, kind_of(partial_dt), partial_in, v2, v, out,
                                                static_cast<hipStream_t>(stream)));
+}
+
+attnres_status_t attnres_stream_probe(int64_t n_read, int64_t n_write, const void* src, void* dst,
+                                      int64_t stream_bytes, void* stream) {
+  if (n_read < 0 || n_read > 4 || n_write < 0 || n_write > 2 || n_read + n_write == 0) return ATTNRES_EINVAL;
+  if (stream_bytes <= 0 || stream_bytes > (int64_t)1 << 40) return ATTNRES_EINVAL;
+  if (stream_bytes % 16 != 0) return ATTNRES_EALIGN;
+  if ((n_read > 0 && !src) || !dst) return ATTNRES_EINVAL;
+  attnres_status_t st = check_align({src, dst});
+  if (st != ATTNRES_OK) return st;
+  const Range r = range_of(src, n_read * stream_bytes);
+  const Range w = range_of(dst, (n_write > 0 ? n_write * stream_bytes : 16));
+  if (n_read > 0 && overlaps(r, w)) return ATTNRES_EALIAS;
+  return hip_status(attnres::launch_stream_probe((int)n_read, (int)n_write, src, dst, stream_bytes,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -62,6 +62,12 @@ hipError_t launch_p1_backward(Dtype dt, int64_t T, int d, const void* src, int n
                               float* dw, float* dkg, float* ws, hipStream_t stream);
 int64_t p1_backward_ranges(int d);
 
+// Streaming-bandwidth probe: n_read byte streams of stream_bytes each read
+// from src (consecutive), n_write written to dst (n_write == 0: dst holds 16
+// bytes that are never written in practice).
+hipError_t launch_stream_probe(int n_read, int n_write, const void* src, void* dst, int64_t stream_bytes,
+                               hipStream_t stream);
+
 hipError_t launch_accumulate(Dtype dt, int64_t T, int d, Dtype pdt, const void* pin, const void* v2,
                              const void* v, void* out, hipStream_t stream);
 

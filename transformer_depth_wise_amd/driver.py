@@ -117,6 +117,17 @@ class BlockAttnRes:
                for b, s in enumerate(self.block_sizes)):
             raise ValueError("phase 1 with S >= 2 supports at most %d completed sources"
                              % _lib.ATTNRES_MAX_SOURCES_MULTI)
+        if self.training:
+            # the phase-1 backward of a block takes every site of the block at
+            # once (at most 32) and, with the sites' partial-source terms, at
+            # most ATTNRES_MAX_SOURCES_MULTI block sources, also for one-sublayer
+            # blocks (whose forward could take more)
+            for b, S in enumerate(self.block_sizes):
+                if S > 32:
+                    raise ValueError("the backward supports at most 32 sublayers per block, got %d" % S)
+                if 1 + self.n_given + b > _lib.ATTNRES_MAX_SOURCES_MULTI:
+                    raise ValueError("the backward of block %d would read %d completed sources (at most %d)"
+                                     % (b, 1 + self.n_given + b, _lib.ATTNRES_MAX_SOURCES_MULTI))
         smax = max(self.block_sizes) if self.block_sizes else 1
         self.reps = torch.empty((n_reps, T, d), dtype=dtype, device=dev)
         self.device = dev = self.reps.device  # with its index
@@ -220,6 +231,34 @@ class BlockAttnRes:
             n_done += 1
         if self.final_site:
             out.append(Launch("final", (n_done + 1) * r + stat))
+        return out
+
+    def plan_survey(self) -> List[Launch]:
+        """The same launches priced with the plain row model of the scope
+        table (rows only, no statistics; every partial sum one row of the
+        storage dtype): phase 1 of a block reads its n sources and writes S
+        outputs; the first sublayer's merge reads o and writes x (2 rows; here
+        it happens inside phase 1, so it is booked there); the second reads o
+        and v_1 and writes x (3); every later one reads o, the partial and the
+        previous output and writes the partial and x (5); the block sum reads
+        the partial and the last output and writes b_n (3); the final site
+        reads the N + 1 representations and writes h_final.  At the 16K
+        chunk's layout this is 1146 rows per token, 874 of them in the 178
+        merge launches."""
+        r = self._row()
+        out: List[Launch] = []
+        n_done = 1 + self.n_given
+        for S in self.block_sizes:
+            fuse = self._fuse(S, n_done)
+            out.append(Launch("phase1", (n_done + S + (2 if fuse else 0)) * r))
+            for j in range(S):
+                if j == 0 and fuse:
+                    continue
+                out.append(Launch("phase2", (2 if j == 0 else 3 if j == 1 else 5) * r))
+            out.append(Launch("accumulate", 3 * r))
+            n_done += 1
+        if self.final_site:
+            out.append(Launch("final", (n_done + 1) * r))
         return out
 
     # ---------------------------------------------------------------- forward
@@ -472,7 +511,9 @@ class FullAttnRes:
         r = self.T * self.d * _esize(self.dtype)
         stat = self.T * 4
         if self.group is None:
-            out = [Launch("full", (l + 1) * r + r + stat) for l in range(1, self.L + 1)]
+            # site l reads its l sources and writes x (and h when kept)
+            hr = r if self.h is not None else 0
+            out = [Launch("full", (l + 1) * r + hr + stat) for l in range(1, self.L + 1)]
         else:
             out = []
             for g0 in range(0, self.L, self.group):
@@ -612,7 +653,8 @@ def prefill_chunked(T_total: int, chunk: int, d: int, block_sizes: Sequence[int]
     st = BlockAttnRes(min(chunk, T_total), d, block_sizes, dtype, eps=eps)
     for c0 in range(0, T_total, chunk):
         c1 = min(T_total, c0 + chunk)
-        if c1 - c0 != st.T:  # ragged last chunk
+        if c1 - c0 != st.T:  # ragged last chunk: release the full-size buffers first
+            st = None
             st = BlockAttnRes(c1 - c0, d, block_sizes, dtype, eps=eps)
         fill_embedding(c0, c1, st.reps[0])
         hook = hook_for_chunk(c0, c1) if hook_for_chunk is not None else None
