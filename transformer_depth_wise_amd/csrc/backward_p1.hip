@@ -1,0 +1,466 @@
+#include "backward_common.h"
+
+namespace attnres {
+
+// ---------------------------------------------------------------------------
+// Phase-1 backward: one 512-thread workgroup per token at a time.  Part I:
+// wave w takes the sites j = w, w + 8, ... (QW of them) and walks the row in
+// groups of 64 chunks, accumulating G_j.u_i, (w_j (.) g_j).u_i and |u_i|^2 in
+// registers (every wave reads all n source chunks; the eight waves of the
+// workgroup walk the same groups, so seven of them hit in the caches), then
+// DPP wave sums into LDS.  Part II (one thread per site, then one per source)
+// forms the coefficients.  Part III: each thread owns chunks of 8 channels
+// and writes du_i for all i, re-reading G_j, w_j, g_j and u_i.
+constexpr int kP1bThreads = 512;
+constexpr int kP1bSites = 32;  // S of one launch
+
+// q = w (.) g for the S sites of a launch (gain NULL: ones).
+__global__ __launch_bounds__(256) void k_fold_queries(int64_t n, const float* __restrict__ w,
+                                                      const float* __restrict__ kg, float* __restrict__ q) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k < n) q[k] = kg ? w[k] * kg[k] : w[k];
+}
+
+// Sites per pass of part I: all QW of the wave's sites for up to 8 bf16
+// sources; fewer for more sources or fp32 rows (registers).
+template <typename St, int N, int QW>
+struct P1bPass {
+  static constexpr int kQB = N <= 8 ? (QW == 4 ? 2 : QW) : ((sizeof(St) == 4 || QW == 3) ? 1 : (QW < 2 ? QW : 2));
+  static constexpr int kJ3 = N <= 8 ? 4 : 2;  // sites per step of part III
+};
+
+template <typename St, int N, int QW>
+__global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const St* __restrict__ src, int64_t stride,
+                                                        int S, const float* __restrict__ q, float eps,
+                                                        const St* __restrict__ gin, int64_t gstride,
+                                                        const float* __restrict__ c_in,
+                                                        const float* __restrict__ gp_in, float* __restrict__ dsrc,
+                                                        int64_t dstride, int accumulate, float* __restrict__ coef) {
+  constexpr int QB = P1bPass<St, N, QW>::kQB;
+  constexpr int J3 = P1bPass<St, N, QW>::kJ3;
+  const int SP = (S + 7) & ~7;  // sites of the coefficient table, padded
+  __shared__ float tD[kP1bSites][N], tZ[kP1bSites][N], tss[N];
+  __shared__ float ta[kP1bSites][N], tb[kP1bSites][N], tq[kP1bSites][N], te[N];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int C = d >> 3;
+  const int ngroups = (C + 63) >> 6;
+  const float inv_d = 1.0f / (float)d;
+  for (int64_t tok = blockIdx.x; tok < T; tok += gridDim.x) {
+    // ---- part I: dot products over the row, QB of the wave's sites per pass;
+    // the next group's chunks load while the current group is used
+#pragma unroll
+    for (int qb = 0; qb < QW; qb += QB) {
+      float D[QB][N], Z[QB][N], ss[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        ss[i] = 0.f;
+#pragma unroll
+        for (int k = 0; k < QB; ++k) D[k][i] = Z[k][i] = 0.f;
+      }
+      Chunk<St> ua[N], ub[N], ga[QB], gb[QB];
+      Chunk<float> qa[QB], qbf[QB];
+      auto fetch = [&](Chunk<St>(&u)[N], Chunk<St>(&gq)[QB], Chunk<float>(&qq)[QB], int g) {
+        const int c0 = g * 64 + lane;
+        const int c = c0 < C ? c0 : C - 1;
+#pragma unroll
+        for (int i = 0; i < N; ++i) u[i].load(src + i * stride + tok * d + c * 8);
+#pragma unroll
+        for (int k = 0; k < QB; ++k) {
+          const int j0 = wv + 8 * (qb + k);
+          const int j = j0 < S ? j0 : S - 1;
+          gq[k].load(gin + j * gstride + tok * d + c * 8);
+          qq[k].load(q + (int64_t)j * d + c * 8);
+        }
+      };
+      auto consume = [&](const Chunk<St>(&u)[N], const Chunk<St>(&gq)[QB], const Chunk<float>(&qq)[QB], int g) {
+        const bool ok = g * 64 + lane < C;
+        float gf[QB][8], qf[QB][8];
+#pragma unroll
+        for (int k = 0; k < QB; ++k) {
+          gq[k].unpack(gf[k]);
+          qq[k].unpack(qf[k]);
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          float ue[8];
+          u[i].unpack(ue);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ue[e] = ok ? ue[e] : 0.f;
+            if (qb == 0) ss[i] = fmaf(ue[e], ue[e], ss[i]);
+          }
+#pragma unroll
+          for (int k = 0; k < QB; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              D[k][i] = fmaf(gf[k][e], ue[e], D[k][i]);
+              Z[k][i] = fmaf(qf[k][e], ue[e], Z[k][i]);
+            }
+        }
+      };
+      // two-stage ring, ua holding group g at the top of every round.  The
+      // rounds have no exit between a load and its use (an exit there lets
+      // the compiler sink the loads to their use, which then waits for every
+      // load before the dot products), and scheduling barriers keep the next
+      // group's loads ahead of the current group's arithmetic.
+      fetch(ua, ga, qa, 0);
+      int g = 0;
+      for (; g + 2 <= ngroups; g += 2) {
+        fetch(ub, gb, qbf, g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(ua, ga, qa, g);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(ua, ga, qa, g + 2 < ngroups ? g + 2 : ngroups - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(ub, gb, qbf, g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (g < ngroups) consume(ua, ga, qa, g);
+#pragma unroll
+      for (int k = 0; k < QB; ++k) {
+        const int j = wv + 8 * (qb + k);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const float dv = wave_sum_dpp(D[k][i]);
+          const float zv = wave_sum_dpp(Z[k][i]);
+          if (lane == 0 && j < S) {
+            tD[j][i] = dv;
+            tZ[j][i] = zv;
+          }
+        }
+      }
+      if (qb == 0 && wv == 0) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const float sv = wave_sum_dpp(ss[i]);
+          if (lane == 0) tss[i] = sv;
+        }
+      }
+    }
+    lds_barrier();
+    // ---- part II: coefficients, one thread per site
+    if ((int)threadIdx.x < S) {
+      const int j = threadIdx.x;
+      float z[N], a[N];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        z[i] = tZ[j][i] / sqrtf(tss[i] * inv_d + eps);
+        mx = fmaxf(mx, z[i]);
+      }
+      float l = 0.f;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        a[i] = expf(z[i] - mx);
+        l += a[i];
+      }
+      const float c = c_in ? c_in[(int64_t)j * T + tok] : 1.f;
+      float go = 0.f;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        a[i] = a[i] / l;
+        go = fmaf(a[i], tD[j][i], go);  // G.o, o the phase-1 partition's output
+      }
+      // G.h = c G.o + (1 - c) G.p, from the same dot products
+      const float gh = gp_in ? fmaf(c, go, (1.0f - c) * gp_in[(int64_t)j * T + tok]) : go;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const float ai = c * a[i];
+        const float dz = ai * (tD[j][i] - gh);
+        const float ri = 1.0f / sqrtf(tss[i] * inv_d + eps);
+        ta[j][i] = ai;
+        tb[j][i] = dz * ri;            // dz / r_i: weight of w_j (.) g_j, and of y_i in dw
+        tq[j][i] = dz * z[i];
+        coef[(tok * SP + j) * N + i] = dz * ri;
+      }
+    } else if ((int)threadIdx.x < SP) {
+      // the table is padded to whole groups of 8 sites with zeros
+#pragma unroll
+      for (int i = 0; i < N; ++i) coef[(tok * SP + threadIdx.x) * N + i] = 0.f;
+    }
+    lds_barrier();
+    if ((int)threadIdx.x < N) {
+      const int i = threadIdx.x;
+      float e = 0.f;
+      for (int j = 0; j < S; ++j) e += tq[j][i];
+      const float ri = 1.0f / sqrtf(tss[i] * inv_d + eps);
+      te[i] = e * inv_d * ri * ri;     // coefficient of u_i in the radial term
+    }
+    lds_barrier();
+    // ---- part III: du_i = sum_j a_ji G_j + sum_j b_ji (w_j (.) g_j) - e_i u_i;
+    // the next batch of J3 sites loads while the current batch is used
+    for (int c = threadIdx.x; c < C; c += kP1bThreads) {
+      float du[N][8];
+#pragma unroll
+      for (int i = 0; i < N; ++i) zero8(du[i]);
+      Chunk<St> ga[J3], gb[J3];
+      Chunk<float> qa[J3], qbf[J3];
+      auto fetch = [&](Chunk<St>(&gq)[J3], Chunk<float>(&qq)[J3], int j0) {
+#pragma unroll
+        for (int u = 0; u < J3; ++u) {
+          const int j = j0 + u < S ? j0 + u : S - 1;
+          gq[u].load(gin + j * gstride + tok * d + c * 8);
+          qq[u].load(q + (int64_t)j * d + c * 8);
+        }
+      };
+      auto consume = [&](const Chunk<St>(&gq)[J3], const Chunk<float>(&qq)[J3], int j0) {
+#pragma unroll
+        for (int u = 0; u < J3; ++u) {
+          const int j = j0 + u;
+          if (j < S) {
+            float gf[8], qf[8];
+            gq[u].unpack(gf);
+            qq[u].unpack(qf);
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+              const float ai = ta[j][i], bi = tb[j][i];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) du[i][e] = fmaf(ai, gf[e], fmaf(bi, qf[e], du[i][e]));
+            }
+          }
+        }
+      };
+      fetch(ga, qa, 0);
+      for (int j0 = 0; j0 < S; j0 += 2 * J3) {
+        fetch(gb, qbf, j0 + J3);
+        consume(ga, qa, j0);
+        if (j0 + J3 >= S) break;
+        fetch(ga, qa, j0 + 2 * J3);
+        consume(gb, qbf, j0 + J3);
+      }
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        float u[8];
+        load8(src + i * stride + tok * d + c * 8, u);
+        const float ei = te[i];
+        float* dst = dsrc + i * dstride + tok * d + c * 8;
+        if (accumulate) {
+          float old[8];
+          load8(dst, old);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) du[i][e] = old[e] + (du[i][e] - ei * u[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) du[i][e] = du[i][e] - ei * u[e];
+        }
+        out8(dst, du[i]);
+      }
+    }
+    lds_barrier();  // the next token rewrites the tables
+  }
+}
+
+// Weight gradients of the block sources: A_j = sum over tokens and sources
+// of (dz_ji / r_i) u_i.  A wave owns one group of 256 channels (4 per lane,
+// so all JT <= 32 sites keep their sums in registers and the sources are
+// read once) and a range of tokens, with the next token's chunks in flight;
+// the range's sums go to part[range][j][d].
+constexpr int kWgradWaves = 2048;
+
+template <typename St>
+struct Quad;  // 4 consecutive channels
+template <>
+struct Quad<bf16_t> {
+  u32x2_t r;
+  __device__ __forceinline__ void load(const bf16_t* p) { r = ld8(p); }
+  __device__ __forceinline__ void unpack(float (&v)[4]) const {
+    v[0] = __uint_as_float(r.x << 16), v[1] = __uint_as_float(r.x & 0xffff0000u);
+    v[2] = __uint_as_float(r.y << 16), v[3] = __uint_as_float(r.y & 0xffff0000u);
+  }
+};
+template <>
+struct Quad<float> {
+  u32x4_t r;
+  __device__ __forceinline__ void load(const float* p) { r = ld16(p); }
+  __device__ __forceinline__ void unpack(float (&v)[4]) const {
+    v[0] = __uint_as_float(r.x), v[1] = __uint_as_float(r.y), v[2] = __uint_as_float(r.z), v[3] = __uint_as_float(r.w);
+  }
+};
+
+template <typename St, int N, int JT>
+__global__ __launch_bounds__(256) void k_p1_bwd_wgrad(int64_t T, int d, const St* __restrict__ src, int64_t stride,
+                                                      int S, const float* __restrict__ coef, int64_t tpr,
+                                                      int64_t ranges, float* __restrict__ part) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Q = d >> 2;                 // quads of channels
+  const int ngroups = (Q + 63) >> 6;
+  const int grp = wid % ngroups;
+  const int64_t range = wid / ngroups;
+  const int64_t t0 = range * tpr;
+  const int64_t t1 = t0 + tpr < T ? t0 + tpr : T;
+  const int c0 = grp * 64 + lane;
+  const int c = c0 < Q ? c0 : Q - 1;
+  float acc[JT][4];
+#pragma unroll
+  for (int q = 0; q < JT; ++q) acc[q][0] = acc[q][1] = acc[q][2] = acc[q][3] = 0.f;
+  Quad<St> ua[N], ub[N];
+  auto fetch = [&](Quad<St>(&u)[N], int64_t t) {
+    const int64_t tc = t < T ? t : T - 1;
+#pragma unroll
+    for (int i = 0; i < N; ++i) u[i].load(src + i * stride + tc * d + c * 4);
+  };
+  // the table holds JT (S rounded up to 8) sites per token, zeros past S
+  auto use = [&](const Quad<St>(&u)[N], int64_t t) {
+    const float* cf = coef + t * JT * N;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      float ue[4];
+      u[i].unpack(ue);
+#pragma unroll
+      for (int q = 0; q < JT; ++q) {
+        const float b = cf[q * N + i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[q][e] = fmaf(b, ue[e], acc[q][e]);
+      }
+    }
+  };
+  if (t0 < t1) fetch(ua, t0);
+  for (int64_t t = t0; t < t1; t += 2) {
+    fetch(ub, t + 1);
+    use(ua, t);
+    if (t + 1 >= t1) break;
+    fetch(ua, t + 2);
+    use(ub, t + 1);
+  }
+  // every range stores its sums, zeros when it holds no token (the
+  // reduction reads all ranges)
+  if (c0 < Q && range < ranges) {
+#pragma unroll
+    for (int q = 0; q < JT; ++q) {
+      if (q < S) {
+        float* o = part + (range * S + q) * (int64_t)d + c * 4;
+        *reinterpret_cast<float4*>(o) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+      }
+    }
+  }
+}
+
+// dw_j += g_j (.) A_j, dg_j += w_j (.) A_j, A_j summed over the ranges in
+// order.  One thread per (site, channel).
+__global__ __launch_bounds__(256) void k_p1_bwd_wgrad_reduce(int64_t ranges, int S, int d,
+                                                             const float* __restrict__ part,
+                                                             const float* __restrict__ w,
+                                                             const float* __restrict__ kg, float* __restrict__ dw,
+                                                             float* __restrict__ dkg) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= (int64_t)S * d) return;
+  float A = 0.f;
+  for (int64_t r = 0; r < ranges; ++r) A += part[r * S * (int64_t)d + k];
+  dw[k] += kg ? kg[k] * A : A;
+  if (dkg) dkg[k] += w[k] * A;
+}
+
+// Token ranges of the weight-gradient pass (a fixed count, so the
+// workspace size and the summation order do not depend on the device).
+int64_t p1_backward_ranges(int d) {
+  const int ngroups = ((d >> 2) + 63) >> 6;
+  return (kWgradWaves + ngroups - 1) / ngroups;
+}
+
+template <typename St, int N, int QW>
+static hipError_t run_p1b_main(int64_t T, int d, const void* src, int64_t stride, int S, const float* q, float eps,
+                               const void* gin, int64_t gstride, const float* c_in, const float* gp_in, float* dsrc,
+                               int64_t dstride, int accumulate, float* coef, hipStream_t stream) {
+  int64_t wgs = T;
+  const int64_t cap = (int64_t)device_cu_count() * 2;
+  if (wgs > cap) wgs = cap;
+  hipLaunchKernelGGL((k_p1_bwd<St, N, QW>), dim3((unsigned)wgs), dim3(kP1bThreads), 0, stream, T, d,
+                     static_cast<const St*>(src), stride, S, q, eps, static_cast<const St*>(gin), gstride, c_in,
+                     gp_in, dsrc, dstride, accumulate, coef);
+  return hipGetLastError();
+}
+
+template <typename St, int N, int JT>
+static hipError_t run_p1b_wgrad(int64_t T, int d, const void* src, int64_t stride, int S, const float* coef,
+                                float* part, hipStream_t stream) {
+  const int64_t ranges = p1_backward_ranges(d);
+  const int ngroups = ((d >> 2) + 63) >> 6;
+  const int64_t tpr = (T + ranges - 1) / ranges;
+  const int64_t waves = ranges * ngroups;
+  hipLaunchKernelGGL((k_p1_bwd_wgrad<St, N, JT>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, T, d,
+                     static_cast<const St*>(src), stride, S, coef, tpr, ranges, part);
+  return hipGetLastError();
+}
+
+template <typename St, int N>
+static hipError_t run_p1b(int64_t T, int d, const void* src, int64_t stride, int S, const float* w, const float* kg,
+                          float eps, const void* gin, int64_t gstride, const float* c_in, const float* gp_in,
+                          float* dsrc, int64_t dstride, int accumulate, float* dw, float* dkg, float* ws,
+                          hipStream_t stream) {
+  // workspace: coefficients [T][S][N], folded queries [S][d], range sums
+  float* coef = ws;
+  float* q = coef + T * (int64_t)((S + 7) & ~7) * N;
+  float* part = q + (int64_t)S * d;
+  const int64_t nq = (int64_t)S * d;
+  hipLaunchKernelGGL(k_fold_queries, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, stream, nq, w, kg, q);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (S <= 8) {
+    e = run_p1b_main<St, N, 1>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
+                               coef, stream);
+  } else if (S <= 16) {
+    e = run_p1b_main<St, N, 2>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
+                               coef, stream);
+  } else if (S <= 24) {
+    e = run_p1b_main<St, N, 3>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
+                               coef, stream);
+  } else {
+    e = run_p1b_main<St, N, 4>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
+                               coef, stream);
+  }
+  if (e != hipSuccess) return e;
+  // (the coefficient table has (S rounded up to 8) sites per token)
+  if (S <= 8) {
+    e = run_p1b_wgrad<St, N, 8>(T, d, src, stride, S, coef, part, stream);
+  } else if (S <= 16) {
+    e = run_p1b_wgrad<St, N, 16>(T, d, src, stride, S, coef, part, stream);
+  } else if (S <= 24) {
+    e = run_p1b_wgrad<St, N, 24>(T, d, src, stride, S, coef, part, stream);
+  } else {
+    e = run_p1b_wgrad<St, N, 32>(T, d, src, stride, S, coef, part, stream);
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_p1_bwd_wgrad_reduce, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, stream,
+                     p1_backward_ranges(d), S, d, part, w, kg, dw, dkg);
+  return hipGetLastError();
+}
+
+template <typename St>
+static hipError_t pick_p1b(int n, int64_t T, int d, const void* src, int64_t stride, int S, const float* w,
+                           const float* kg, float eps, const void* gin, int64_t gstride, const float* c_in,
+                           const float* gp_in, float* dsrc, int64_t dstride, int accumulate, float* dw, float* dkg,
+                           float* ws, hipStream_t stream) {
+  switch (n) {
+#define ATTNRES_CASE(N_)                                                                                           \
+  case N_:                                                                                                         \
+    return run_p1b<St, N_>(T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate, \
+                           dw, dkg, ws, stream);
+    ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4) ATTNRES_CASE(5) ATTNRES_CASE(6)
+    ATTNRES_CASE(7) ATTNRES_CASE(8) ATTNRES_CASE(9) ATTNRES_CASE(10) ATTNRES_CASE(11) ATTNRES_CASE(12)
+    ATTNRES_CASE(13) ATTNRES_CASE(14) ATTNRES_CASE(15) ATTNRES_CASE(16)
+#undef ATTNRES_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_p1_backward(Dtype dt, int64_t T, int d, const void* src, int n, int64_t stride, int S,
+                              const float* w, const float* kg, float eps, const void* gin, int64_t gstride,
+                              const float* c_in, const float* gp_in, float* dsrc, int64_t dstride, int accumulate,
+                              float* dw, float* dkg, float* ws, hipStream_t stream) {
+  // one site without a partial source (the final aggregation): the site
+  // backward without PreNorm computes the same gradients, with a team per
+  // token instead of one busy wave, into fp32 rows; its weight sums are added
+  if (S == 1 && !c_in && !gp_in)
+    return launch_site_backward(dt, T, d, src, n, stride, w, kg, nullptr, 0, eps, gin, dsrc, dstride,
+                                accumulate ? kOutAdd : kOutF32, 1, dw, dkg, nullptr, ws, stream);
+  if (dt == kBF16)
+    return pick_p1b<bf16_t>(n, T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
+                            dw, dkg, ws, stream);
+  return pick_p1b<float>(n, T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate, dw,
+                         dkg, ws, stream);
+}
+
+
+}  // namespace attnres
