@@ -62,7 +62,8 @@ typedef enum {
     ATTNRES_EDTYPE = 2,  /* unknown dtype */
     ATTNRES_EALIGN = 3,  /* d or a stride not a multiple of 8, pointer not 16-byte aligned */
     ATTNRES_EALIAS = 4,  /* an output overlaps an input (other than the allowed in-place case) */
-    ATTNRES_EHIP = 5     /* the HIP runtime reported an error at launch */
+    ATTNRES_EHIP = 5,    /* the HIP runtime reported an error at launch */
+    ATTNRES_ESCRATCH = 6 /* more workspace than attnres_phase1_noalloc holds */
 } attnres_status_t;
 
 /* Storage formats.  ATTNRES_P24 is only valid for the running partial sum
@@ -115,6 +116,30 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt,
                                 const float* w, const float* key_gain, int64_t S, float eps,
                                 void* out, float* m_out, float* lse_out,
                                 void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * attnres_phase1 without the caller's workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results (bit for bit),
+ * limits and errors as attnres_phase1, except that the workspace is a device
+ * array of ATTNRES_NOALLOC_SCRATCH_BYTES inside the library: one copy per
+ * GPU, held until the process ends, its address looked up on the first call
+ * on each device.  The call allocates nothing and calls no allocating
+ * routine.  A call whose attnres_phase1_workspace_bytes(T, d, n_src, S)
+ * exceeds ATTNRES_NOALLOC_SCRATCH_BYTES returns ATTNRES_ESCRATCH (64 MiB
+ * covers, e.g., 16384 tokens with up to 16 sources and 32 queries, or 32768
+ * tokens with 8 sources and 24 queries).  Every call on one GPU shares that
+ * GPU's array, which keeps whatever the last call left there (nothing in it
+ * needs to start at zero): calls that overlap in time on one GPU -- on
+ * different streams, or from different host threads -- race on it and must
+ * be serialised by the caller.
+ */
+#define ATTNRES_NOALLOC_SCRATCH_BYTES (64LL << 20)
+attnres_status_t attnres_phase1_noalloc(attnres_dtype_t dt,
+                                        const void* src, int64_t n_src, int64_t src_stride,
+                                        int64_t T, int64_t d,
+                                        const float* w, const float* key_gain, int64_t S, float eps,
+                                        void* out, float* m_out, float* lse_out, void* stream);
 
 /*
  * Phase 1 of a block with the first sublayer's input finished in the same

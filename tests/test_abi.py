@@ -349,3 +349,18 @@ def test_stream_probe_validation(lib):
     assert probe(src=A + 4) == EALIGN
     assert probe(dst=A + (1 << 19)) == EALIAS           # written range overlaps the read one
     assert probe(nr=2, dst=A + (1 << 20)) == EALIAS     # second read stream overlaps the writes
+
+
+def test_phase1_noalloc_validation(lib):
+    # size checks return before the library looks up its scratch on a device
+    def call(dt=1, n=3, T=4096, d=64, S=4, out=16 * A):
+        return checked(lib.attnres_phase1_noalloc(dt, p(A), n, T * d, T, d, p(8 * A), None, S, 1e-6, p(out), None,
+                                                  p(24 * A), None))
+    ESCRATCH = 6
+    assert call(dt=7) == EDTYPE
+    assert call(n=17) == EINVAL                       # more than 16 sources with S >= 2
+    assert call(d=12) == EALIGN
+    assert call(T=200000, n=16, S=32) == ESCRATCH     # 410 MB of workspace > 64 MiB of scratch
+    assert call(T=0) == 0                             # empty token set: nothing touched
+    assert lib.attnres_phase1_workspace_bytes(16384, 7168, 16, 32) <= 64 << 20
+    assert "ESCRATCH" in lib.attnres_status_string(ESCRATCH).decode()

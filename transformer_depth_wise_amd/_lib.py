@@ -24,12 +24,13 @@ ATTNRES_MAX_GROUP_SOURCES = 16
 ATTNRES_MAX_T = 2147483647
 ATTNRES_MAX_QUERIES = 4096
 ATTNRES_MAX_STRIDE = 1 << 40
+ATTNRES_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_workspace_bytes",
             "attnres_phase2_merge", "attnres_phase2_merge_multi", "attnres_full", "attnres_block_accumulate",
             "attnres_site_backward", "attnres_site_backward_accumulate", "attnres_site_backward_workspace_bytes",
             "attnres_phase2_backward", "attnres_phase2_backward_workspace_bytes", "attnres_phase1_backward",
-            "attnres_phase1_backward_workspace_bytes", "attnres_stream_probe", "attnres_status_string")
+            "attnres_phase1_backward_workspace_bytes", "attnres_stream_probe", "attnres_phase1_noalloc", "attnres_status_string")
 
 
 class AttnResError(RuntimeError):
@@ -72,7 +73,8 @@ def load(path: Optional[str] = None):
     lib.attnres_phase1_backward_workspace_bytes.argtypes = [I, I, I, I]
     lib.attnres_phase1_backward_workspace_bytes.restype = ctypes.c_int64
     lib.attnres_stream_probe.argtypes = [I, I, V, V, I, V]
-    for fn in ("attnres_stream_probe", "attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase2_merge", "attnres_phase2_merge_multi",
+    lib.attnres_phase1_noalloc.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V]
+    for fn in ("attnres_phase1_noalloc", "attnres_stream_probe", "attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase2_merge", "attnres_phase2_merge_multi",
                "attnres_full", "attnres_block_accumulate", "attnres_site_backward",
                "attnres_site_backward_accumulate", "attnres_phase2_backward", "attnres_phase1_backward"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -269,6 +271,22 @@ def attnres_phase1(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Opt
                                _ptr(key_gain), S, eps, _ptr(out), _ptr(m_out), _ptr(lse_out), _ptr(workspace),
                                _workspace(workspace), _stream(stream))
     _check("attnres_phase1", rc)
+
+
+def attnres_phase1_noalloc(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],
+                           eps: float, out: Optional[torch.Tensor], m_out: Optional[torch.Tensor],
+                           lse_out: torch.Tensor, stream=None, check: bool = True) -> None:
+    """attnres_phase1 with the library's own device scratch as workspace
+    (allocates nothing; calls overlapping in time on one GPU race on it)."""
+    if check:
+        _phase1_args(src, n_src, w, key_gain, out, m_out, lse_out)
+        _on_device(src, w, key_gain, out, m_out, lse_out)
+    S, T = lse_out.shape
+    d = src.shape[-1]
+    rc = load().attnres_phase1_noalloc(dtype_code(src.dtype), _ptr(src), n_src, _slab_stride(src, T, d), T, d,
+                                       _ptr(w), _ptr(key_gain), S, eps, _ptr(out), _ptr(m_out), _ptr(lse_out),
+                                       _stream(stream))
+    _check("attnres_phase1_noalloc", rc)
 
 
 def attnres_phase1_first_prenorm(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],

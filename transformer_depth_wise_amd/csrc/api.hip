@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/attnres.h"
 #include "attnres_launch.h"
 
@@ -93,6 +95,9 @@ const char* attnres_status_string(attnres_status_t status) {
     case ATTNRES_EALIGN: return "ATTNRES_EALIGN: d or a stride not a multiple of 8, or pointer not 16-byte aligned";
     case ATTNRES_EALIAS: return "ATTNRES_EALIAS: an output overlaps an input";
     case ATTNRES_EHIP: return "ATTNRES_EHIP: the HIP runtime reported an error";
+    case ATTNRES_ESCRATCH:
+      return "ATTNRES_ESCRATCH: the call needs more workspace than the allocation-free entry point's "
+             "ATTNRES_NOALLOC_SCRATCH_BYTES";
   }
   return "ATTNRES_UNKNOWN_STATUS";
 }
@@ -176,6 +181,49 @@ attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_s
                                 int64_t workspace_bytes, void* stream) {
   return phase1_impl(dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, nullptr, nullptr,
                      nullptr, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free phase 1: the workspace is this file's device array instead
+// of caller memory.  Each GPU holds its own copy for the life of the process;
+// its address on the current device is looked up once per device (with that
+// device current) and kept, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[ATTNRES_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[64] = {nullptr};
+
+// The current device's copy of `scratch`, or nullptr if it cannot be found.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+attnres_status_t attnres_phase1_noalloc(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
+                                        int64_t T, int64_t d, const float* w, const float* key_gain, int64_t S,
+                                        float eps, void* out, float* m_out, float* lse_out, void* stream) {
+  // the sizes are checked (and T == 0 returns) before anything touches the device
+  if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
+  const int64_t need = attnres_phase1_workspace_bytes(T, d, n_src, S);
+  if (need < 0) return phase1_impl(dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out,
+                                   nullptr, nullptr, nullptr, nullptr, 0, stream);
+  if (need > ATTNRES_NOALLOC_SCRATCH_BYTES) return ATTNRES_ESCRATCH;
+  if (T == 0)
+    return phase1_impl(dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, nullptr,
+                       nullptr, nullptr, nullptr, 0, stream);
+  void* ws = scratch_on_current_device();
+  if (!ws) return ATTNRES_EHIP;
+  return phase1_impl(dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, nullptr, nullptr,
+                     nullptr, ws, ATTNRES_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 attnres_status_t attnres_phase1_first_prenorm(attnres_dtype_t dt, const void* src, int64_t n_src,
