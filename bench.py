@@ -79,16 +79,22 @@ def cpu_model() -> str:
     return "%s (%d logical cores visible)" % (name or platform.processor() or "unknown", os.cpu_count() or 0)
 
 
-def ceiling(dev, total_bytes: int = 4 << 30, reps: int = 10) -> dict:
+PROBE_SHAPES = [(g, u, nt) for g in (1, 2, 4) for u in (1, 2, 8) for nt in (False, True)]
+
+
+def ceiling(dev, total_bytes: int = 4 << 30, reps: int = 6) -> dict:
     """Achievable HBM rate of plain streaming kernels (attnres_stream_probe:
     16-byte accesses, persistent grid-stride loop) with the read/write mixes
     of the path's kernels: read-only, write-only, copy, and the phase-2
     merge's two mixes (odd positions read o, the stored partial and v and
     write x: about 3 reads : 1 write; even positions also read the
-    one-before-last output and store the partial: about 4 : 2).  Each probe
-    moves ``total_bytes`` per dispatch, far beyond the 256 MB last-level
-    cache; the rate is the mean over ``reps`` dispatches timed with HIP
-    events on the launch stream."""
+    one-before-last output and store the partial: about 4 : 2).  Each mix
+    is run in 18 launch shapes (1, 2 or 4 workgroups per CU; 1, 2 or 8
+    chunks in flight per thread; plain or non-temporal accesses) and the
+    best rate is reported with its shape.  Each dispatch moves
+    ``total_bytes``, far beyond the 256 MB last-level cache; a rate is the
+    mean over ``reps`` dispatches timed with HIP events on the launch
+    stream."""
     import torch
     import transformer_depth_wise_amd as tdw
 
@@ -101,16 +107,20 @@ def ceiling(dev, total_bytes: int = 4 << 30, reps: int = 10) -> dict:
     for name, nr, nw in (("read", 1, 0), ("write", 0, 1), ("copy", 1, 1), ("mix_3r1w", 3, 1),
                          ("mix_4r2w", 4, 2)):
         sb = (total_bytes // (nr + nw)) // (1 << 20) * (1 << 20)
-        for _ in range(2):
-            tdw.attnres_stream_probe(nr, nw, src, dst, sb)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            tdw.attnres_stream_probe(nr, nw, src, dst, sb)
-        e1.record(stream)
-        e1.synchronize()
-        sec = e0.elapsed_time(e1) * 1e-3 / reps
-        out[name] = round((nr + nw) * sb / sec / 1e9, 1)
+        best, shape = 0.0, None
+        for g, u, nt in PROBE_SHAPES:
+            tdw.attnres_stream_probe(nr, nw, src, dst, sb, g, u, nt)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                tdw.attnres_stream_probe(nr, nw, src, dst, sb, g, u, nt)
+            e1.record(stream)
+            e1.synchronize()
+            rate = (nr + nw) * sb / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
+            if rate > best:
+                best, shape = rate, {"workgroups_per_cu": g, "unroll": u, "nontemporal": nt}
+        out[name] = round(best, 1)
+        out[name + "_shape"] = shape
     del src, dst
     torch.cuda.empty_cache()
     return out

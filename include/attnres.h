@@ -401,15 +401,20 @@ attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t
  * two-phase scheme to be verified against DRAM reads and kernel latency).
  * Reads n_read streams of stream_bytes each, consecutive from src, and
  * writes n_write streams, consecutive from dst (16-byte accesses, a wave
- * covering 1 KiB of consecutive bytes of each stream per instruction).
- *   0 <= n_read <= 4, 0 <= n_write <= 2, not both zero; stream_bytes a
+ * covering 1 KiB of consecutive bytes of each stream per instruction), with
+ * workgroups_per_cu 256-thread workgroups per compute unit in a grid-stride
+ * loop, `unroll` chunks of each stream in flight per thread (1, 2, 4 or 8),
+ * and non-temporal loads and stores when `nontemporal` is nonzero.
+ *   0 <= n_read <= 4, 0 <= n_write <= 2, not both zero; 1 <=
+ *   workgroups_per_cu <= 16; stream_bytes a
  *   positive multiple of 16 (at most 2^40).  With n_write == 0, dst must
  *   still point at 16 writable bytes (kept as the loads' sink; not written
  *   for any data these probes read).  The read and written ranges must not
  *   overlap.  Asynchronous on `stream`, like every other entry point.
  */
 attnres_status_t attnres_stream_probe(int64_t n_read, int64_t n_write, const void* src, void* dst,
-                                      int64_t stream_bytes, void* stream);
+                                      int64_t stream_bytes, int64_t workgroups_per_cu, int64_t unroll,
+                                      int64_t nontemporal, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* attnres_status_string(attnres_status_t status);

@@ -337,8 +337,11 @@ def test_status_strings(lib):
 
 
 def test_stream_probe_validation(lib):
-    def probe(nr=1, nw=1, src=A, dst=64 * A, nbytes=1 << 20):
-        return checked(lib.attnres_stream_probe(nr, nw, p(src), p(dst), nbytes, None))
+    def probe(nr=1, nw=1, src=A, dst=64 * A, nbytes=1 << 20, per_cu=2, unroll=2, nt=1):
+        return checked(lib.attnres_stream_probe(nr, nw, p(src), p(dst), nbytes, per_cu, unroll, nt, None))
+    assert probe(per_cu=0) == EINVAL
+    assert probe(per_cu=17) == EINVAL
+    assert probe(unroll=3) == EINVAL
     assert probe(nr=5) == EINVAL
     assert probe(nw=3) == EINVAL
     assert probe(nr=0, nw=0) == EINVAL

@@ -72,7 +72,7 @@ def load(path: Optional[str] = None):
     lib.attnres_phase1_backward.argtypes = [E, V, I, I, I, I, V, V, I, F, V, I, V, V, V, I, E, V, V, V, I, V]
     lib.attnres_phase1_backward_workspace_bytes.argtypes = [I, I, I, I]
     lib.attnres_phase1_backward_workspace_bytes.restype = ctypes.c_int64
-    lib.attnres_stream_probe.argtypes = [I, I, V, V, I, V]
+    lib.attnres_stream_probe.argtypes = [I, I, V, V, I, I, I, I, V]
     lib.attnres_phase1_noalloc.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V]
     for fn in ("attnres_phase1_noalloc", "attnres_stream_probe", "attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase2_merge", "attnres_phase2_merge_multi",
                "attnres_full", "attnres_block_accumulate", "attnres_site_backward",
@@ -556,15 +556,18 @@ def attnres_block_accumulate(partial_in: Optional[torch.Tensor], v: torch.Tensor
 
 
 def attnres_stream_probe(n_read: int, n_write: int, src: Optional[torch.Tensor], dst: torch.Tensor,
-                         stream_bytes: int, stream=None) -> None:
+                         stream_bytes: int, workgroups_per_cu: int = 2, unroll: int = 2, nontemporal: bool = True,
+                         stream=None) -> None:
     """Streaming-bandwidth probe: read ``n_read`` streams of ``stream_bytes``
     each from the start of ``src`` and write ``n_write`` streams to ``dst``
-    (which needs at least 16 bytes when nothing is written)."""
+    (which needs at least 16 bytes when nothing is written), with the given
+    launch shape and access policy."""
     need_r, need_w = n_read * stream_bytes, max(n_write * stream_bytes, 16)
     if n_read and (src is None or src.numel() * src.element_size() < need_r or not src.is_contiguous()):
         raise ValueError("src must be a contiguous tensor of at least %d bytes" % need_r)
     if dst.numel() * dst.element_size() < need_w or not dst.is_contiguous():
         raise ValueError("dst must be a contiguous tensor of at least %d bytes" % need_w)
     _on_device(src, dst)
-    rc = load().attnres_stream_probe(n_read, n_write, _ptr(src), _ptr(dst), stream_bytes, _stream(stream))
+    rc = load().attnres_stream_probe(n_read, n_write, _ptr(src), _ptr(dst), stream_bytes, workgroups_per_cu, unroll,
+                                     1 if nontemporal else 0, _stream(stream))
     _check("attnres_stream_probe", rc)

@@ -64,9 +64,11 @@ int64_t p1_backward_ranges(int d);
 
 // Streaming-bandwidth probe: n_read byte streams of stream_bytes each read
 // from src (consecutive), n_write written to dst (n_write == 0: dst holds 16
-// bytes that are never written in practice).
+// bytes that are never written in practice); per_cu workgroups per compute
+// unit, `unroll` chunks per stream in flight per thread (1, 2, 4 or 8),
+// non-temporal loads and stores when `nontemporal`.
 hipError_t launch_stream_probe(int n_read, int n_write, const void* src, void* dst, int64_t stream_bytes,
-                               hipStream_t stream);
+                               int per_cu, int unroll, bool nontemporal, hipStream_t stream);
 
 hipError_t launch_accumulate(Dtype dt, int64_t T, int d, Dtype pdt, const void* pin, const void* v2,
                              const void* v, void* out, hipStream_t stream);
