@@ -238,9 +238,10 @@ def backward_report(dev, steps: int):
         else:
             recs[-1][2] = e
 
-    st.backward(prm, dx_for, dh_final=v[0])
+    dhf = v[0].to(st.h_final.dtype)   # h_final is fp32 in a bf16 training pass
+    st.backward(prm, dx_for, dh_final=dhf)
     nb = max(2, steps // 4)
-    sec = _time(lambda k: st.backward(prm, dx_for, dh_final=v[0], instrument=instrument), nb)
+    sec = _time(lambda k: st.backward(prm, dx_for, dh_final=dhf, instrument=instrument), nb)
     plan = st.plan_backward()
     b = sum(x.bytes for x in plan)
     kinds = {}

@@ -86,7 +86,7 @@ typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1, ATTNRES_P24 = 2 } attnres_dtyp
  * Phase 1 of a block ("Attention Residuals" notes, section 10, first phase;
  * "Attention Residuals 阅读补充", static-query batching Q K^T).
  * For each token t and each query s < S, over the n_src completed sources
- * u_i = src + i*src_stride (each [T][d], dtype dt):
+ * u_i = src + i*src_stride (each [T][d], dtype src_dt):
  *     z_si = w_s^T (key_gain_s (.) u_i / r(u_i)),  m_s = max_i z_si,
  *     lse_s = m_s + ln sum_i e^{z_si - m_s},
  *     out[s][t][:] = sum_i e^{z_si - lse_s} u_i        (normalised)
@@ -109,8 +109,15 @@ typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1, ATTNRES_P24 = 2 } attnres_dtyp
  * notes' log-sum-exp merge), reading every source row once.
  * out must not overlap src; m_out, lse_out and workspace must not overlap
  * anything.
+ * src_dt: the sources' dtype, dt itself, or ATTNRES_F32 with dt ==
+ * ATTNRES_BF16 (fp32 sources, bf16 outputs; then 1 <= n_src <=
+ * ATTNRES_MAX_SOURCES_MULTI and the workspace is required for S == 1 too).
+ * A training forward keeps the block sums exact this way: the notes'
+ * section 8 defines b_n as the sum of the block's outputs, and storing it in
+ * bf16 would change what the backward differentiates.  Any other pair is
+ * ATTNRES_EDTYPE.
  */
-attnres_status_t attnres_phase1(attnres_dtype_t dt,
+attnres_status_t attnres_phase1(attnres_dtype_t dt, attnres_dtype_t src_dt,
                                 const void* src, int64_t n_src, int64_t src_stride,
                                 int64_t T, int64_t d,
                                 const float* w, const float* key_gain, int64_t S, float eps,
@@ -335,7 +342,10 @@ attnres_status_t attnres_site_backward_accumulate(attnres_dtype_t dt,
  *   aligned (per-team sums).
  *
  * attnres_phase1_backward: the block sources' part of S sites at once.
- *   src, n_src, src_stride: the block sources as for attnres_phase1.
+ *   src, n_src, src_stride: the block sources as for attnres_phase1, of
+ *   dtype src_dt: dt, or ATTNRES_F32 with dt == ATTNRES_BF16 (the exact
+ *   block sums a training forward keeps; then n_src <=
+ *   ATTNRES_MAX_SOURCES_MULTI also for one site).  dt is G's dtype.
  *   w, key_gain: [S][d] fp32 (key_gain NULL = ones).  g_in + j*g_stride:
  *   G_j [T][d] (dt) of site j.  c_in, gp_in: [S][T] fp32 from the sites'
  *   attnres_phase2_backward (both NULL: each site is its phase-1 partition
@@ -371,7 +381,7 @@ attnres_status_t attnres_phase2_backward(attnres_dtype_t dt, int64_t T, int64_t 
                                          void* workspace, int64_t workspace_bytes, void* stream);
 
 int64_t attnres_phase1_backward_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int64_t S);
-attnres_status_t attnres_phase1_backward(attnres_dtype_t dt,
+attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, attnres_dtype_t src_dt,
                                          const void* src, int64_t n_src, int64_t src_stride,
                                          int64_t T, int64_t d,
                                          const float* w, const float* key_gain, int64_t S, float eps,
@@ -386,12 +396,16 @@ attnres_status_t attnres_phase1_backward(attnres_dtype_t dt,
  * the block's sublayer outputs):
  *     out = ((partial_in or 0) + (v2 or 0)) + v      (fp32, in that order)
  *   partial_in: [T][d] in format partial_dt (F32, P24 or dt; NULL = zero);
- *   v2 (NULL = zero), v, out: [T][d] dtype dt.  out may be the same pointer
- *   as partial_in when partial_dt == dt; out must not overlap v or v2.
+ *   v2 (NULL = zero), v: [T][d] dtype dt.  out: [T][d] of dtype out_dt, dt
+ *   itself or ATTNRES_F32 with dt == ATTNRES_BF16 (the exact fp32 sum, kept
+ *   by a training forward; any other pair is ATTNRES_EDTYPE).  out may be
+ *   the same pointer as partial_in when partial_dt == out_dt; out must not
+ *   overlap v or v2.
  */
 attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t d,
                                           attnres_dtype_t partial_dt, const void* partial_in,
-                                          const void* v2, const void* v, void* out, void* stream);
+                                          const void* v2, const void* v, void* out, attnres_dtype_t out_dt,
+                                          void* stream);
 
 /*
  * Streaming-bandwidth probe: a measurement aid that computes nothing of the

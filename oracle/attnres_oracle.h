@@ -145,20 +145,12 @@ int oracle_site_backward_tokens(int64_t n_tok, int64_t n, int64_t d, const float
  * Outputs (fp64): dv [L][n_tok][d]; dreps [1 + n_given][n_tok][d] (the
  * embedding, then the given block sums); dw, dg [L+1][d] and dgamma [L][d],
  * summed over the tokens (overwritten).  dx [L][n_tok][d], dhf [n_tok][d].
- * bf16_sums != 0: every block sum b_n enters the later sites rounded to
- * bfloat16 (oracle_round_bf16), as a bf16 store of the block
- * representations keeps it; the rounding passes gradients through
- * unchanged (dL/dv_l of the block's outputs is dL/db_n of the rounded
- * value).  0: exact fp64 sums. */
+ * Block sums are exact fp64 sums, as the notes define them. */
 int oracle_block_backward(int64_t n_tok, int64_t d, int64_t n_blocks, const int64_t* blocks,
                           int64_t n_given, const float* emb, const float* given, const float* v,
                           const float* w, const float* g, const float* gamma, double eps,
-                          int final_site, int bf16_sums, const float* dx, const float* dhf, double* dv_out,
+                          int final_site, const float* dx, const float* dhf, double* dv_out,
                           double* dreps_out, double* dw_out, double* dg_out, double* dgamma_out);
-
-/* x rounded to fp32 (nearest even), then to bfloat16 (the upper 16 bits of
- * fp32, nearest even); infinities and NaN pass through. */
-double oracle_round_bf16(double x);
 
 /* Number of OpenMP threads the forward functions use (1 without OpenMP). */
 int oracle_threads(void);

@@ -73,15 +73,17 @@ def block_inputs(w: synth.Workload, device, t0: int = 0, t1: Optional[int] = Non
 
 def run_block_parity(w: synth.Workload, samples: Optional[Sequence[int]] = None, device="cuda",
                      keep_h: bool = True, x_ring: int = 4, partial: Optional[str] = None,
-                     fuse_first: bool = True) -> Dict[str, float]:
+                     fuse_first: bool = True, training: bool = False) -> Dict[str, float]:
     """Block AttnRes on the GPU vs the oracle on sampled tokens.  Returns the
-    worst error per output kind (already asserted against the bar)."""
+    worst error per output kind (already asserted against the bar).  With
+    ``training`` the forward that keeps its activations runs (fp32 block
+    representations for bf16 rows)."""
     dev = torch.device(device)
     emb, given, v = block_inputs(w, dev)
     prm = synth.params(w, dev)
     st = BlockAttnRes(w.T, w.d, w.block_sizes, w.torch_dtype, n_given=w.n_given, eps=w.eps, device=dev,
                       keep_h=keep_h, x_ring=x_ring, final_site=w.final_site, partial=partial,
-                      fuse_first=fuse_first)
+                      fuse_first=fuse_first, training=training)
     st.reps[0].copy_(emb)
     for n, b in enumerate(given):
         st.reps[1 + n].copy_(b)
@@ -159,12 +161,10 @@ def run_block_backward_parity(w: synth.Workload, samples: Optional[Sequence[int]
     Upstream gradients dx_l, dh_final are seeded N(0,1) rows (or, with
     ``dx_from_outputs``, the sublayer outputs themselves, to save memory).
 
-    For bf16 storage the forward keeps the block sums in bf16, and the exact
-    gradient is sensitive to that rounding (the logit gradient weighs
-    u_i - h, a difference of nearly equal rows).  The GPU result is held to
-    the bar against the oracle whose block sums are rounded to bf16 the same
-    way (computed by the oracle itself), and against the exact oracle to the
-    bar plus the distance between the two oracle results."""
+    The reference is the oracle's backward of the plain definition (block
+    sums exact).  The training forward keeps the block representations in
+    fp32 for that reason; dL/dh_final enters in h_final's dtype (fp32 there,
+    the same values as the bf16 rows drawn here)."""
     dev = torch.device(device)
     emb, given, v = block_inputs(w, dev)
     prm = synth.params(w, dev)
@@ -189,16 +189,13 @@ def run_block_backward_parity(w: synth.Workload, samples: Optional[Sequence[int]
         dv_rows[l] = dv.index_select(0, idx).clone()
         return dx[l]
 
-    out = st.backward(prm, dx_for, dh_final=dhf if w.final_site else None)
+    out = st.backward(prm, dx_for, dh_final=dhf.to(st.h_final.dtype) if w.final_site else None)
     torch.cuda.synchronize()
     sel = lambda t: t.index_select(0, idx)  # noqa: E731
     args = (sel(emb), torch.stack([sel(t) for t in v]), prm["w"], prm["g"], prm["gamma"], w.block_sizes, w.eps,
             torch.stack([sel(t) for t in dx]), sel(dhf) if w.final_site else None)
     kw = dict(given=torch.stack([sel(t) for t in given]) if given else None, final_site=w.final_site)
-    # two references: exact block sums, and (bf16 storage) the block sums
-    # rounded to bf16 as the forward stores them, gradients passing through
     exact = oracle.block_backward(*args, **kw)
-    stored = oracle.block_backward(*args, bf16_sums=True, **kw) if w.dtype == "bf16" else exact
     gpu = {"dv": _host(torch.stack(dv_rows)), "demb": _host(sel(out["demb"]))}
     if w.n_given:
         gpu["dgiven"] = _host(out["dgiven"].index_select(1, idx))
@@ -209,13 +206,7 @@ def run_block_backward_parity(w: synth.Workload, samples: Optional[Sequence[int]
     bar = TOL[w.dtype] if tol is None else tol
     worst = {}
     for k, x in gpu.items():
-        e = float(row_rel_err(x, stored[k]).max())
-        # what bf16 storage of the block sums alone moves the exact gradient by
-        sens = float(row_rel_err(stored[k], exact[k]).max())
-        e_exact = float(row_rel_err(x, exact[k]).max())
+        e = float(row_rel_err(x, exact[k]).max())
         worst[k] = e
-        worst[k + "_vs_exact"] = e_exact
         assert e <= bar, "%s: %s max-abs-rel %.3e exceeds %.1e" % (w.name, k, e, bar)
-        assert e_exact <= bar + sens, "%s: %s vs exact sums %.3e exceeds %.1e + %.3e" % (w.name, k, e_exact, bar,
-                                                                                          sens)
     return worst

@@ -69,16 +69,22 @@ def checked(rc):
     return rc
 
 
-def phase1(lib, dt=1, src=A, n=3, stride=4096 * 64, T=4096, d=64, w=8 * A, kg=None, S=4, eps=1e-6,
+def phase1(lib, dt=1, sdt=None, src=A, n=3, stride=4096 * 64, T=4096, d=64, w=8 * A, kg=None, S=4, eps=1e-6,
            out=16 * A, m=None, lse=24 * A, ws=32 * A, ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = lib.attnres_phase1_workspace_bytes(T, d, n, S)
-    return checked(lib.attnres_phase1(dt, p(src), n, stride, T, d, p(w), p(kg), S, eps, p(out), p(m), p(lse),
+    sdt = dt if sdt is None else sdt
+    return checked(lib.attnres_phase1(dt, sdt, p(src), n, stride, T, d, p(w), p(kg), S, eps, p(out), p(m), p(lse),
                                       p(ws), ws_bytes, None))
 
 
 def test_phase1_validation(lib):
     assert phase1(lib, dt=7) == EDTYPE
+    assert phase1(lib, sdt=7) == EDTYPE
+    assert phase1(lib, dt=0, sdt=1) == EDTYPE     # bf16 sources, fp32 outputs: not a supported pair
+    assert phase1(lib, dt=1, sdt=2) == EDTYPE     # P24 is a partial-sum format only
+    assert phase1(lib, dt=1, sdt=0, n=17, S=1) == EINVAL   # fp32 sources with bf16 outputs: at most 16
+    assert phase1(lib, dt=1, sdt=0, S=1, ws=None, ws_bytes=0) == EINVAL  # ... and a workspace even for S == 1
     assert phase1(lib, d=12) == EALIGN
     assert phase1(lib, d=0) == EINVAL
     assert phase1(lib, d=16392) == EINVAL
@@ -176,16 +182,23 @@ def test_phase2_backward_validation(lib):
     assert lib.attnres_phase2_backward_workspace_bytes(10, 12) == -1
 
 
-def p1b(lib, dt=1, src=A, n=3, stride=1024 * 64, T=1024, d=64, w=8 * A, kg=None, S=4, g=16 * A, gstride=1024 * 64,
+def p1b(lib, dt=1, sdt=None, src=A, n=3, stride=1024 * 64, T=1024, d=64, w=8 * A, kg=None, S=4, g=16 * A, gstride=1024 * 64,
         c=None, gh=None, ds=24 * A, dstride=1024 * 64, dw=32 * A, dk=None, ws=40 * A, ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = lib.attnres_phase1_backward_workspace_bytes(T, d, n, S)
-    return checked(lib.attnres_phase1_backward(dt, p(src), n, stride, T, d, p(w), p(kg), S, 1e-6, p(g), gstride, p(c),
+    sdt = dt if sdt is None else sdt
+    return checked(lib.attnres_phase1_backward(dt, sdt, p(src), n, stride, T, d, p(w), p(kg), S, 1e-6, p(g), gstride,
+                                               p(c),
                                                p(gh), p(ds), dstride, 1, p(dw), p(dk), p(ws), ws_bytes, None))
 
 
 def test_phase1_backward_validation(lib):
     assert p1b(lib, dt=3) == EDTYPE
+    assert p1b(lib, dt=0, sdt=1) == EDTYPE                 # bf16 sources with fp32 G: not a supported pair
+    assert p1b(lib, sdt=2) == EDTYPE
+    assert p1b(lib, sdt=0, n=17, S=1) == EINVAL            # fp32 sources, bf16 G: at most 16, one site too
+    # fp32 sources are twice as long: the second slab reaches the gradients
+    assert p1b(lib, sdt=0, n=2, stride=1024 * 64, ds=A + 1024 * 64 * 2 * 2) == EALIAS
     assert p1b(lib, d=12) == EALIGN
     assert p1b(lib, n=0) == EINVAL
     assert p1b(lib, n=17) == EINVAL
@@ -263,8 +276,14 @@ def test_full_and_accumulate_validation(lib):
     assert f(stride=-64) == EINVAL
     acc = lambda **k: checked(lib.attnres_block_accumulate(k.get("dt", 1), k.get("T", 64), k.get("d", 64), k.get("pdt", 0),
                                                    p(k.get("pin")), p(k.get("v2")), p(k.get("v", A)),
-                                                   p(k.get("out", 2 * A)), None))
+                                                   p(k.get("out", 2 * A)), k.get("odt", k.get("dt", 1)),
+                                                   None))
     assert acc(v=None) == EINVAL
+    assert acc(odt=2) == EDTYPE                     # the block sum is dt or fp32
+    assert acc(dt=0, odt=1) == EDTYPE               # fp32 rows summed into bf16: not a supported pair
+    # an fp32 sum is twice as long as a bf16 row: ending where v starts as a
+    # bf16 row would, it reaches into v
+    assert acc(odt=0, out=A - 64 * 64 * 2) == EALIAS
     assert acc(out=A) == EALIAS
     assert acc(pin=2 * A, pdt=0) == EALIAS          # in place only with the same dtype
     assert acc(T=0, v=None, out=None) == 0

@@ -26,6 +26,9 @@ SPECIFIED = {
 # Arguments the header adds to a specified call, and why.
 EXTENSIONS = {
     "attnres_phase1": {
+        # fp32 sources with bf16 outputs: a training forward keeps the block
+        # sums exact (they are what the backward differentiates)
+        "src_dt": "dtype of the source rows (dt, or F32 with bf16 outputs)",
         # caller-owned memory for the packed queries and the softmax weights
         # between the scoring and output kernels (the library allocates nothing)
         "workspace": "scratch of attnres_phase1_workspace_bytes()",
@@ -41,6 +44,7 @@ EXTENSIONS = {
     "attnres_full": {},
     "attnres_block_accumulate": {
         "partial_dt": "format of partial_in (F32, P24 or dt)",
+        "out_dt": "dtype of the block sum (dt, or F32: a training forward keeps it exact)",
         "v2": "the block's one-before-last output (partial stored every second sublayer)",
     },
     "attnres_status_string": {},

@@ -48,10 +48,17 @@ def test_block_plan_survey_rows():
 
 
 def test_block_plan_backward_bytes():
-    # the 16K chunk's backward moves 509859266560 bytes (every term is
-    # proportional to T): 16 tokens of it move 1/1024 of that
+    # the 16K chunk's backward moves 520663793664 bytes (every term is
+    # proportional to T): 16 tokens of it move 1/1024 of that.  The block
+    # representations are fp32 in a bf16 training pass: 46 rows per token
+    # more than bf16 ones would move (the final site's 9 representations and
+    # dL/dh_final, and the 1 + 2 + ... + 8 block-source reads of phase 1)
     st = tdw.BlockAttnRes(16, 7168, K3, BF, device="cpu", training=True)
-    assert sum(x.bytes for x in st.plan_backward()) * 1024 == 509859266560
+    assert st.reps.dtype == torch.float32 and st.h_final.dtype == torch.float32
+    assert sum(x.bytes for x in st.plan_backward()) * 1024 == 520663793664
+    assert 520663793664 - 509859266560 == 46 * 16384 * 7168 * 2
+    inf = tdw.BlockAttnRes(16, 7168, K3, BF, device="cpu")
+    assert inf.reps.dtype == BF and inf.h_final.dtype == BF
 
 
 def test_block_source_limits():

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import synth
-from harness import run_block_backward_parity
+from harness import run_block_backward_parity, run_block_parity
 import transformer_depth_wise_amd as tdw
 
 pytestmark = pytest.mark.gpu
@@ -66,3 +66,26 @@ def test_block_backward_prefill_chunk_sampled():
     _say("case block backward prefill_chunk_bf16 T=%d d=%d blocks=%s (8 sampled tokens)" % (w.T, w.d, w.block_sizes))
     worst = run_block_backward_parity(w, samples=synth.sample_tokens(w.T, 8), params_too=False, dx_from_outputs=True)
     _say("worst", worst)
+
+
+TRAIN_FWD_CASES = [
+    # (T, d, blocks, n_given, dtype): the training forward reads fp32 block
+    # representations in phase 1 (bf16 outputs), sums blocks in fp32
+    (64, 256, (4, 4), 0, "bf16"),
+    (200, 1032, (3, 1, 2), 2, "bf16"),      # a one-sublayer block: one query on fp32 sources
+    (33, 7168, (5, 3), 14, "bf16"),         # 16 sources in the last block
+    (5, 8, (1, 2), 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("T,d,blocks,n_given,dt", TRAIN_FWD_CASES)
+def test_training_forward_matches_oracle(T, d, blocks, n_given, dt):
+    base = synth.WORKLOADS["tiny_block_f32"]
+    w = synth.scaled(base, name="trainfwd", T=T, d=d, block_sizes=tuple(blocks), n_given=n_given, dtype=dt,
+                     unit_gains=False, seed=6300 + T + d)
+    _say("case training forward T=%d d=%d blocks=%s given=%d %s" % (T, d, blocks, n_given, dt))
+    worst = run_block_parity(w, training=True)
+    _say("worst", worst)
+    # the block sums are fp32 here: they carry the exact sums to fp32 rounding
+    if dt == "bf16":
+        assert worst["reps"] < 1e-4

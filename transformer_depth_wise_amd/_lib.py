@@ -53,7 +53,7 @@ def load(path: Optional[str] = None):
                            "`python -m transformer_depth_wise_amd.build`" % p)
     lib = ctypes.CDLL(p)
     V, I, F, E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
-    lib.attnres_phase1.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V, I, V]
+    lib.attnres_phase1.argtypes = [E, E, V, I, I, I, I, V, V, I, F, V, V, V, V, I, V]
     lib.attnres_phase1_first_prenorm.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V, V, V, V, I, V]
     lib.attnres_phase1_workspace_bytes.argtypes = [I, I, I, I]
     lib.attnres_phase1_workspace_bytes.restype = ctypes.c_int64
@@ -64,12 +64,12 @@ def load(path: Optional[str] = None):
     lib.attnres_site_backward_accumulate.argtypes = lib.attnres_site_backward.argtypes
     lib.attnres_site_backward_workspace_bytes.argtypes = [I, I]
     lib.attnres_site_backward_workspace_bytes.restype = ctypes.c_int64
-    lib.attnres_block_accumulate.argtypes = [E, I, I, E, V, V, V, V, V]
+    lib.attnres_block_accumulate.argtypes = [E, I, I, E, V, V, V, V, E, V]
     lib.attnres_phase2_backward.argtypes = [E, I, I, V, V, E, V, V, V, V, V, V, E, F, V, V, V, V, V, V, V, V, V, I,
                                             V]
     lib.attnres_phase2_backward_workspace_bytes.argtypes = [I, I]
     lib.attnres_phase2_backward_workspace_bytes.restype = ctypes.c_int64
-    lib.attnres_phase1_backward.argtypes = [E, V, I, I, I, I, V, V, I, F, V, I, V, V, V, I, E, V, V, V, I, V]
+    lib.attnres_phase1_backward.argtypes = [E, E, V, I, I, I, I, V, V, I, F, V, I, V, V, V, I, E, V, V, V, I, V]
     lib.attnres_phase1_backward_workspace_bytes.argtypes = [I, I, I, I]
     lib.attnres_phase1_backward_workspace_bytes.restype = ctypes.c_int64
     lib.attnres_stream_probe.argtypes = [I, I, V, V, I, I, I, I, V]
@@ -247,7 +247,9 @@ def _phase1_args(src, n_src, w, key_gain, out, m_out, lse_out):
     _rows(src, "src", T, d, dt, n=n_src)
     _fp32(w, "w", (S, d), optional=False)
     _fp32(key_gain, "key_gain", (S, d))
-    if out is not None and (out.dtype != dt or tuple(out.shape) != (S, T, d) or not out.is_contiguous()):
+    # outputs of the sources' dtype, or bf16 outputs from fp32 sources
+    odt = torch.bfloat16 if (out is not None and dt == torch.float32 and out.dtype == torch.bfloat16) else dt
+    if out is not None and (out.dtype != odt or tuple(out.shape) != (S, T, d) or not out.is_contiguous()):
         raise ValueError("out: expected a contiguous [%d, %d, %d] %s tensor, got %s %s"
                          % (S, T, d, dt, out.dtype, tuple(out.shape)))
     _fp32(m_out, "m_out", (S, T))
@@ -267,7 +269,9 @@ def attnres_phase1(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Opt
         _on_device(src, w, key_gain, out, m_out, lse_out, workspace)
     S, T = lse_out.shape
     d = src.shape[-1]
-    rc = load().attnres_phase1(dtype_code(src.dtype), _ptr(src), n_src, _slab_stride(src, T, d), T, d, _ptr(w),
+    out_dt = out.dtype if out is not None else src.dtype
+    rc = load().attnres_phase1(dtype_code(out_dt), dtype_code(src.dtype), _ptr(src), n_src, _slab_stride(src, T, d),
+                               T, d, _ptr(w),
                                _ptr(key_gain), S, eps, _ptr(out), _ptr(m_out), _ptr(lse_out), _ptr(workspace),
                                _workspace(workspace), _stream(stream))
     _check("attnres_phase1", rc)
@@ -520,7 +524,9 @@ def attnres_phase1_backward(src: torch.Tensor, n_src: int, w: torch.Tensor, key_
     if check:
         dt = _storage(src, "src")
         _rows(src, "src", T, d, dt, n=n_src)
-        _rows(g_in, "g_in", T, d, dt, n=S)
+        # G of the sources' dtype, or bf16 G with fp32 sources
+        gdt = torch.bfloat16 if (dt == torch.float32 and g_in.dtype == torch.bfloat16) else dt
+        _rows(g_in, "g_in", T, d, gdt, n=S)
         _rows(dsrc, "dsrc", T, d, torch.float32, n=n_src)
         for t, name in ((w, "w"), (key_gain, "key_gain"), (dw, "dw"), (dkey_gain, "dkey_gain")):
             _fp32(t, name, (S, d), optional=name not in ("w", "dw"))
@@ -528,7 +534,8 @@ def attnres_phase1_backward(src: torch.Tensor, n_src: int, w: torch.Tensor, key_
         _fp32(gp_in, "gp_in", (S, T))
         _workspace(workspace)
         _on_device(src, w, key_gain, g_in, c_in, gp_in, dsrc, dw, dkey_gain, workspace)
-    rc = load().attnres_phase1_backward(dtype_code(src.dtype), _ptr(src), n_src, _slab_stride(src, T, d), T, d,
+    rc = load().attnres_phase1_backward(dtype_code(g_in.dtype), dtype_code(src.dtype), _ptr(src), n_src,
+                                        _slab_stride(src, T, d), T, d,
                                         _ptr(w), _ptr(key_gain), S, eps, _ptr(g_in), _slab_stride(g_in, T, d),
                                         _ptr(c_in), _ptr(gp_in), _ptr(dsrc), _slab_stride(dsrc, T, d),
                                         1 if accumulate else 0, _ptr(dw), _ptr(dkey_gain), _ptr(workspace),
@@ -539,7 +546,7 @@ def attnres_phase1_backward(src: torch.Tensor, n_src: int, w: torch.Tensor, key_
 def attnres_block_accumulate(partial_in: Optional[torch.Tensor], v: torch.Tensor, out: torch.Tensor,
                              stream=None, v2: Optional[torch.Tensor] = None, check: bool = True) -> None:
     """out = (partial_in or 0) + (v2 or 0) + v; all [T, d] (partial_in may be
-    a P24 buffer)."""
+    a P24 buffer; out may be fp32 for bf16 rows: the exact sum)."""
     if v.dim() != 2:
         raise ValueError("v must be a [T, d] tensor")
     T, d = v.shape
@@ -547,11 +554,11 @@ def attnres_block_accumulate(partial_in: Optional[torch.Tensor], v: torch.Tensor
         dt = _storage(v, "v")
         _rows(v, "v", T, d, dt)
         _rows(v2, "v2", T, d, dt, optional=True)
-        _rows(out, "out", T, d, dt)
+        _rows(out, "out", T, d, torch.float32 if (out is not None and out.dtype == torch.float32) else dt)
         _partial(partial_in, "partial_in", T, d, dt)
         _on_device(partial_in, v2, v, out)
     rc = load().attnres_block_accumulate(dtype_code(v.dtype), T, d, _fmt(partial_in), _ptr(partial_in), _ptr(v2),
-                                         _ptr(v), _ptr(out), _stream(stream))
+                                         _ptr(v), _ptr(out), dtype_code(out.dtype), _stream(stream))
     _check("attnres_block_accumulate", rc)
 
 

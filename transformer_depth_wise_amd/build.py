@@ -17,8 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libattnres.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "phase1.hip", "merge.hip", "full.hip", "backward.hip", "backward_p2.hip", "backward_p1.hip",
-           "probe.hip"]
+SOURCES = ["api.hip", "phase1.hip", "merge.hip", "full.hip", "backward.hip", "backward_p2.hip",
+           "backward_p1_bf16.hip", "backward_p1_f32.hip", "backward_p1_f32src.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -114,15 +114,20 @@ int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int6
 }
 
 // Shared by attnres_phase1 and attnres_phase1_first_prenorm (x0 != null).
-static attnres_status_t phase1_impl(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
-                                    int64_t T, int64_t d, const float* w, const float* key_gain, int64_t S,
-                                    float eps, void* out, float* m_out, float* lse_out, const float* gamma0,
-                                    void* x0, void* h0, void* workspace, int64_t workspace_bytes, void* stream) {
-  if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
+static attnres_status_t phase1_impl(attnres_dtype_t dt, attnres_dtype_t src_dt, const void* src, int64_t n_src,
+                                    int64_t src_stride, int64_t T, int64_t d, const float* w,
+                                    const float* key_gain, int64_t S, float eps, void* out, float* m_out,
+                                    float* lse_out, const float* gamma0, void* x0, void* h0, void* workspace,
+                                    int64_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dt) || !dtype_ok(src_dt)) return ATTNRES_EDTYPE;
+  // sources of the outputs' type, or fp32 sources with bf16 outputs
+  const bool mixed = src_dt != dt;
+  if (mixed && !(src_dt == ATTNRES_F32 && dt == ATTNRES_BF16)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
   if (!extent_ok(T, {src_stride}) || S < 1 || S > ATTNRES_MAX_QUERIES || n_src < 1) return ATTNRES_EINVAL;
-  if (n_src > (S == 1 && !x0 ? ATTNRES_MAX_SOURCES : ATTNRES_MAX_SOURCES_MULTI)) return ATTNRES_EINVAL;
+  if (n_src > (S == 1 && !x0 && !mixed ? ATTNRES_MAX_SOURCES : ATTNRES_MAX_SOURCES_MULTI)) return ATTNRES_EINVAL;
+  if (mixed && x0) return ATTNRES_EINVAL;  // the first query's PreNorm is fused for equal types only
   if (!(eps >= 0.f)) return ATTNRES_EINVAL;
   if (T == 0) return ATTNRES_OK;  // empty token set: nothing is read or written
   if (!src || !w || !lse_out) return ATTNRES_EINVAL;
@@ -130,14 +135,15 @@ static attnres_status_t phase1_impl(attnres_dtype_t dt, const void* src, int64_t
   if (n_src > 1 && (src_stride < T * d)) return ATTNRES_EINVAL;
   if (src_stride % 8 != 0) return ATTNRES_EALIGN;
   int64_t ws_need = attnres_phase1_workspace_bytes(T, d, n_src, S);
-  // S == 1 without the first-query PreNorm: one pass over the sources with an
-  // online softmax; the workspace is not used
-  if (S == 1 && !x0) ws_need = 0;
+  // S == 1 without the first-query PreNorm (and sources of the outputs'
+  // type): one pass over the sources with an online softmax; the workspace
+  // is not used
+  if (S == 1 && !x0 && !mixed) ws_need = 0;
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return ATTNRES_EINVAL;
   st = check_align({src, w, key_gain, out, ws_need > 0 ? workspace : nullptr, gamma0, x0, h0}, {m_out, lse_out});
   if (st != ATTNRES_OK) return st;
   const int64_t es = esize(dt);
-  const Range rs = range_of(src, ((n_src - 1) * src_stride + T * d) * es);
+  const Range rs = range_of(src, ((n_src - 1) * src_stride + T * d) * esize(src_dt));
   const Range ro = out ? range_of(out, S * T * d * es) : Range{0, 0};
   const Range rl = range_of(lse_out, S * T * 4);
   const Range rm = m_out ? range_of(m_out, S * T * 4) : Range{0, 0};
@@ -165,7 +171,8 @@ static attnres_status_t phase1_impl(attnres_dtype_t dt, const void* src, int64_t
   for (int64_t s0 = 0; s0 < S; s0 += 32) {
     const int64_t sn = (S - s0) < 32 ? (S - s0) : 32;
     char* o = out ? static_cast<char*>(out) + s0 * T * d * es : nullptr;
-    hipError_t e = attnres::launch_phase1_multi(kdt, src, (int)n_src, src_stride, T, (int)d, w + s0 * d,
+    hipError_t e = attnres::launch_phase1_multi(kdt, kind_of(src_dt), src, (int)n_src, src_stride, T, (int)d,
+                                                w + s0 * d,
                                                 key_gain ? key_gain + s0 * d : nullptr, (int)sn, eps, o,
                                                 m_out ? m_out + s0 * T : nullptr, lse_out + s0 * T, gamma0,
                                                 s0 == 0 ? x0 : nullptr, s0 == 0 ? h0 : nullptr,
@@ -175,11 +182,11 @@ static attnres_status_t phase1_impl(attnres_dtype_t dt, const void* src, int64_t
   return ATTNRES_OK;
 }
 
-attnres_status_t attnres_phase1(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
-                                int64_t T, int64_t d, const float* w, const float* key_gain, int64_t S,
-                                float eps, void* out, float* m_out, float* lse_out, void* workspace,
+attnres_status_t attnres_phase1(attnres_dtype_t dt, attnres_dtype_t src_dt, const void* src, int64_t n_src,
+                                int64_t src_stride, int64_t T, int64_t d, const float* w, const float* key_gain,
+                                int64_t S, float eps, void* out, float* m_out, float* lse_out, void* workspace,
                                 int64_t workspace_bytes, void* stream) {
-  return phase1_impl(dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, nullptr, nullptr,
+  return phase1_impl(dt, src_dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, nullptr, nullptr,
                      nullptr, workspace, workspace_bytes, stream);
 }
 
@@ -214,15 +221,15 @@ attnres_status_t attnres_phase1_noalloc(attnres_dtype_t dt, const void* src, int
   // the sizes are checked (and T == 0 returns) before anything touches the device
   if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
   const int64_t need = attnres_phase1_workspace_bytes(T, d, n_src, S);
-  if (need < 0) return phase1_impl(dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out,
+  if (need < 0) return phase1_impl(dt, dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out,
                                    nullptr, nullptr, nullptr, nullptr, 0, stream);
   if (need > ATTNRES_NOALLOC_SCRATCH_BYTES) return ATTNRES_ESCRATCH;
   if (T == 0)
-    return phase1_impl(dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, nullptr,
+    return phase1_impl(dt, dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, nullptr,
                        nullptr, nullptr, nullptr, 0, stream);
   void* ws = scratch_on_current_device();
   if (!ws) return ATTNRES_EHIP;
-  return phase1_impl(dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, nullptr, nullptr,
+  return phase1_impl(dt, dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, nullptr, nullptr,
                      nullptr, ws, ATTNRES_NOALLOC_SCRATCH_BYTES, stream);
 }
 
@@ -233,7 +240,7 @@ attnres_status_t attnres_phase1_first_prenorm(attnres_dtype_t dt, const void* sr
                                               void* x_out, void* h_out, void* workspace, int64_t workspace_bytes,
                                               void* stream) {
   if (!x_out) return ATTNRES_EINVAL;
-  return phase1_impl(dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, prenorm_gain,
+  return phase1_impl(dt, dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, prenorm_gain,
                      x_out, h_out, workspace, workspace_bytes, stream);
 }
 
@@ -462,18 +469,21 @@ int64_t attnres_phase1_backward_workspace_bytes(int64_t T, int64_t d, int64_t n_
   return need > site ? need : site;
 }
 
-attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, const void* src, int64_t n_src, int64_t src_stride,
-                                         int64_t T, int64_t d, const float* w, const float* key_gain, int64_t S,
-                                         float eps, const void* g_in, int64_t g_stride, const float* c_in,
-                                         const float* gp_in, float* dsrc, int64_t dsrc_stride, int accumulate,
-                                         float* dw, float* dkey_gain, void* workspace, int64_t workspace_bytes,
-                                         void* stream) {
-  if (!dtype_ok(dt)) return ATTNRES_EDTYPE;
+attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, attnres_dtype_t src_dt, const void* src,
+                                         int64_t n_src, int64_t src_stride, int64_t T, int64_t d, const float* w,
+                                         const float* key_gain, int64_t S, float eps, const void* g_in,
+                                         int64_t g_stride, const float* c_in, const float* gp_in, float* dsrc,
+                                         int64_t dsrc_stride, int accumulate, float* dw, float* dkey_gain,
+                                         void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dt) || !dtype_ok(src_dt)) return ATTNRES_EDTYPE;
+  // sources of G's type, or fp32 sources with bf16 G
+  const bool mixed = src_dt != dt;
+  if (mixed && !(src_dt == ATTNRES_F32 && dt == ATTNRES_BF16)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
-  // one site without c_in / gp_in (the final aggregation) takes as many
-  // sources as the site backward it runs on
-  const bool one_site = S == 1 && !c_in && !gp_in;
+  // one site without c_in / gp_in (the final aggregation) with rows of one
+  // type takes as many sources as the site backward it runs on
+  const bool one_site = S == 1 && !c_in && !gp_in && !mixed;
   const int64_t max_src = one_site ? ATTNRES_MAX_SOURCES : ATTNRES_MAX_SOURCES_MULTI;
   if (!extent_ok(T, {src_stride, g_stride, dsrc_stride}) || n_src < 1 || n_src > max_src || S < 1 || S > 32 ||
       !(eps >= 0.f))
@@ -489,7 +499,7 @@ attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, const void* src, in
   st = check_align({src, w, key_gain, g_in, dsrc, workspace}, {c_in, gp_in, dw, dkey_gain});
   if (st != ATTNRES_OK) return st;
   const int64_t es = esize(dt);
-  const Range i_s = range_of(src, ((n_src - 1) * src_stride + T * d) * es);
+  const Range i_s = range_of(src, ((n_src - 1) * src_stride + T * d) * esize(src_dt));
   const Range i_w = range_of(w, S * d * 4), i_k = key_gain ? range_of(key_gain, S * d * 4) : Range{0, 0};
   const Range i_g = range_of(g_in, ((S - 1) * g_stride + T * d) * es);
   const Range i_c = c_in ? range_of(c_in, S * T * 4) : Range{0, 0};
@@ -504,7 +514,8 @@ attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, const void* src, in
   for (int a = 0; a < 4; ++a)
     for (int b = a + 1; b < 4; ++b)
       if (overlaps(outs[a], outs[b])) return ATTNRES_EALIAS;
-  return hip_status(attnres::launch_p1_backward(kind_of(dt), T, (int)d, src, (int)n_src, src_stride, (int)S, w,
+  return hip_status(attnres::launch_p1_backward(kind_of(dt), kind_of(src_dt), T, (int)d, src, (int)n_src, src_stride,
+                                                (int)S, w,
                                                 key_gain, eps, g_in, g_stride, c_in, gp_in, dsrc, dsrc_stride,
                                                 accumulate ? 1 : 0, dw, dkey_gain, static_cast<float*>(workspace),
                                                 static_cast<hipStream_t>(stream)));
@@ -544,8 +555,9 @@ attnres_status_t attnres_full(attnres_dtype_t dt, const void* src, int64_t n_src
 
 attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t d, attnres_dtype_t partial_dt,
                                           const void* partial_in, const void* v2, const void* v, void* out,
-                                          void* stream) {
+                                          attnres_dtype_t out_dt, void* stream) {
   if (!dtype_ok(dt) || !partial_ok(partial_dt, dt)) return ATTNRES_EDTYPE;
+  if (out_dt != dt && !(out_dt == ATTNRES_F32 && dt == ATTNRES_BF16)) return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
   if (!extent_ok(T)) return ATTNRES_EINVAL;
@@ -554,15 +566,15 @@ attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t
   st = check_align({partial_in, v2, v, out});
   if (st != ATTNRES_OK) return st;
   const int64_t rows = T * d;
-  const Range ro = range_of(out, rows * esize(dt));
+  const Range ro = range_of(out, rows * esize(out_dt));
   const Range rv = range_of(v, rows * esize(dt));
   const Range rp = partial_in ? range_of(partial_in, rows * esize(partial_dt)) : Range{0, 0};
   const Range rv2 = v2 ? range_of(v2, rows * esize(dt)) : Range{0, 0};
   if (overlaps(ro, rv) || overlaps(ro, rv2)) return ATTNRES_EALIAS;
-  const bool in_place = partial_in == out && partial_dt == dt;
+  const bool in_place = partial_in == out && partial_dt == out_dt;
   if (!in_place && overlaps(ro, rp)) return ATTNRES_EALIAS;
-  return hip_status(attnres::launch_accumulate(kind_of(dt), T, (int)d, kind_of(partial_dt), partial_in, v2, v, out,
-                                               static_cast<hipStream_t>(stream)));
+  return hip_status(attnres::launch_accumulate(kind_of(dt), kind_of(out_dt), T, (int)d, kind_of(partial_dt),
+                                               partial_in, v2, v, out, static_cast<hipStream_t>(stream)));
 }
 
 attnres_status_t attnres_stream_probe(int64_t n_read, int64_t n_write, const void* src, void* dst,

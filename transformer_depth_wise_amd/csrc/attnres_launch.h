@@ -10,13 +10,14 @@ enum Dtype { kF32 = 0, kBF16 = 1, kP24 = 2 };
 
 int device_cu_count();
 
-// Phase 1 of a block, one tile of at most 32 queries (n <= 16); `alpha` is
+// Phase 1 of a block, one tile of at most 32 queries (n <= 16), sources of
+// type sdt (dt, or fp32 sources with bf16 outputs and no x0); `alpha` is
 // workspace for the packed queries and T * S * n fp32 softmax weights.  With
 // x0 != null, query 0's output goes through the PreNorm with gain gamma0
 // into x0 (and as is into h0 when not null) instead of slab 0 of out, which
 // may be used as scratch; out may then be null when n == 1.  Or S == 1 with
 // optional PreNorm (n <= 32).  Return a hipError_t.
-hipError_t launch_phase1_multi(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
+hipError_t launch_phase1_multi(Dtype dt, Dtype sdt, const void* src, int n, int64_t stride, int64_t T, int d,
                                const float* w, const float* kg, int S, float eps, void* out,
                                float* m_out, float* lse_out, const float* gamma0, void* x0, void* h0,
                                float* alpha, hipStream_t stream);
@@ -55,8 +56,9 @@ int64_t p2_backward_slots(int64_t T, int d);
 
 // Phase-1 backward of a block: the block sources' gradients written or added
 // (accumulate) into dsrc (fp32), the block-source part of dw, dkg added.
+// Sources of type sdt (dt, or fp32 with bf16 G rows).
 // ws: T * S * n coefficients + p1_backward_ranges(d) * S * d partial sums.
-hipError_t launch_p1_backward(Dtype dt, int64_t T, int d, const void* src, int n, int64_t stride, int S,
+hipError_t launch_p1_backward(Dtype dt, Dtype sdt, int64_t T, int d, const void* src, int n, int64_t stride, int S,
                               const float* w, const float* kg, float eps, const void* gin, int64_t gstride,
                               const float* c_in, const float* gp_in, float* dsrc, int64_t dstride, int accumulate,
                               float* dw, float* dkg, float* ws, hipStream_t stream);
@@ -70,7 +72,8 @@ int64_t p1_backward_ranges(int d);
 hipError_t launch_stream_probe(int n_read, int n_write, const void* src, void* dst, int64_t stream_bytes,
                                int per_cu, int unroll, bool nontemporal, hipStream_t stream);
 
-hipError_t launch_accumulate(Dtype dt, int64_t T, int d, Dtype pdt, const void* pin, const void* v2,
+// out (of type odt: dt, or fp32 for bf16 rows) = (pin + v2) + v.
+hipError_t launch_accumulate(Dtype dt, Dtype odt, int64_t T, int d, Dtype pdt, const void* pin, const void* v2,
                              const void* v, void* out, hipStream_t stream);
 
 }  // namespace attnres

@@ -527,4 +527,32 @@ hipError_t launch_wgrad_reduce(int64_t slots, int d, const float* part, const fl
   return hipGetLastError();
 }
 
+// Token ranges of the weight-gradient pass (a fixed count, so the
+// workspace size and the summation order do not depend on the device).
+int64_t p1_backward_ranges(int d) {
+  const int ngroups = ((d >> 2) + 63) >> 6;
+  return (kWgradWaves + ngroups - 1) / ngroups;
+}
+
+hipError_t launch_p1_backward(Dtype dt, Dtype sdt, int64_t T, int d, const void* src, int n, int64_t stride, int S,
+                              const float* w, const float* kg, float eps, const void* gin, int64_t gstride,
+                              const float* c_in, const float* gp_in, float* dsrc, int64_t dstride, int accumulate,
+                              float* dw, float* dkg, float* ws, hipStream_t stream) {
+  // one site without a partial source (the final aggregation), rows of one
+  // type: the site backward without PreNorm computes the same gradients, with
+  // a team per token instead of one busy wave, into fp32 rows; its weight
+  // sums are added
+  if (S == 1 && !c_in && !gp_in && sdt == dt)
+    return launch_site_backward(dt, T, d, src, n, stride, w, kg, nullptr, 0, eps, gin, dsrc, dstride,
+                                accumulate ? kOutAdd : kOutF32, 1, dw, dkg, nullptr, ws, stream);
+  if (sdt == kF32 && dt == kBF16)
+    return launch_p1b_f32src(n, T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride,
+                             accumulate, dw, dkg, ws, stream);
+  if (dt == kBF16)
+    return launch_p1b_bf16(n, T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
+                           dw, dkg, ws, stream);
+  return launch_p1b_f32(n, T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate, dw,
+                        dkg, ws, stream);
+}
+
 }  // namespace attnres

@@ -52,4 +52,19 @@ hipError_t launch_wgrad_reduce(int64_t slots, int d, const float* part, const fl
 // Threads per team of the site backward for rows of d channels.
 int backward_team(int d);
 
+// Waves of the phase-1 backward's weight-gradient pass (a fixed count, so the
+// workspace size and the summation order do not depend on the device).
+constexpr int kWgradWaves = 2048;
+
+// The phase-1 backward of a block for one pair of row types: bf16 sources and
+// G, fp32 sources and G, or fp32 sources with bf16 G.
+#define ATTNRES_P1B_ARGS                                                                                        \
+  int n, int64_t T, int d, const void *src, int64_t stride, int S, const float *w, const float *kg, float eps, \
+      const void *gin, int64_t gstride, const float *c_in, const float *gp_in, float *dsrc, int64_t dstride,   \
+      int accumulate, float *dw, float *dkg, float *ws, hipStream_t stream
+hipError_t launch_p1b_bf16(ATTNRES_P1B_ARGS);
+hipError_t launch_p1b_f32(ATTNRES_P1B_ARGS);
+hipError_t launch_p1b_f32src(ATTNRES_P1B_ARGS);
+#undef ATTNRES_P1B_ARGS
+
 }  // namespace attnres

@@ -1,3 +1,7 @@
+#pragma once
+// Private to libattnres: the phase-1 backward kernels as templates over the
+// source rows' type Ut and the type St of the sites' G rows (equal, or fp32
+// sources with bf16 G), instantiated by one translation unit per pair.
 #include "backward_common.h"
 
 namespace attnres {
@@ -15,7 +19,7 @@ constexpr int kP1bThreads = 512;
 constexpr int kP1bSites = 32;  // S of one launch
 
 // q = w (.) g for the S sites of a launch (gain NULL: ones).
-__global__ __launch_bounds__(256) void k_fold_queries(int64_t n, const float* __restrict__ w,
+static __global__ __launch_bounds__(256) void k_fold_queries(int64_t n, const float* __restrict__ w,
                                                       const float* __restrict__ kg, float* __restrict__ q) {
   const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (k < n) q[k] = kg ? w[k] * kg[k] : w[k];
@@ -23,21 +27,21 @@ __global__ __launch_bounds__(256) void k_fold_queries(int64_t n, const float* __
 
 // Sites per pass of part I: all QW of the wave's sites for up to 8 bf16
 // sources; fewer for more sources or fp32 rows (registers).
-template <typename St, int N, int QW>
+template <typename Ut, int N, int QW>
 struct P1bPass {
-  static constexpr int kQB = N <= 8 ? (QW == 4 ? 2 : QW) : ((sizeof(St) == 4 || QW == 3) ? 1 : (QW < 2 ? QW : 2));
+  static constexpr int kQB = N <= 8 ? (QW == 4 ? 2 : QW) : ((sizeof(Ut) == 4 || QW == 3) ? 1 : (QW < 2 ? QW : 2));
   static constexpr int kJ3 = N <= 8 ? 4 : 2;  // sites per step of part III
 };
 
-template <typename St, int N, int QW>
-__global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const St* __restrict__ src, int64_t stride,
+template <typename Ut, typename St, int N, int QW>
+__global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const Ut* __restrict__ src, int64_t stride,
                                                         int S, const float* __restrict__ q, float eps,
                                                         const St* __restrict__ gin, int64_t gstride,
                                                         const float* __restrict__ c_in,
                                                         const float* __restrict__ gp_in, float* __restrict__ dsrc,
                                                         int64_t dstride, int accumulate, float* __restrict__ coef) {
-  constexpr int QB = P1bPass<St, N, QW>::kQB;
-  constexpr int J3 = P1bPass<St, N, QW>::kJ3;
+  constexpr int QB = P1bPass<Ut, N, QW>::kQB;
+  constexpr int J3 = P1bPass<Ut, N, QW>::kJ3;
   const int SP = (S + 7) & ~7;  // sites of the coefficient table, padded
   __shared__ float tD[kP1bSites][N], tZ[kP1bSites][N], tss[N];
   __shared__ float ta[kP1bSites][N], tb[kP1bSites][N], tq[kP1bSites][N], te[N];
@@ -58,9 +62,10 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
 #pragma unroll
         for (int k = 0; k < QB; ++k) D[k][i] = Z[k][i] = 0.f;
       }
-      Chunk<St> ua[N], ub[N], ga[QB], gb[QB];
+      Chunk<Ut> ua[N], ub[N];
+      Chunk<St> ga[QB], gb[QB];
       Chunk<float> qa[QB], qbf[QB];
-      auto fetch = [&](Chunk<St>(&u)[N], Chunk<St>(&gq)[QB], Chunk<float>(&qq)[QB], int g) {
+      auto fetch = [&](Chunk<Ut>(&u)[N], Chunk<St>(&gq)[QB], Chunk<float>(&qq)[QB], int g) {
         const int c0 = g * 64 + lane;
         const int c = c0 < C ? c0 : C - 1;
 #pragma unroll
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
           qq[k].load(q + (int64_t)j * d + c * 8);
         }
       };
-      auto consume = [&](const Chunk<St>(&u)[N], const Chunk<St>(&gq)[QB], const Chunk<float>(&qq)[QB], int g) {
+      auto consume = [&](const Chunk<Ut>(&u)[N], const Chunk<St>(&gq)[QB], const Chunk<float>(&qq)[QB], int g) {
         const bool ok = g * 64 + lane < C;
         float gf[QB][8], qf[QB][8];
 #pragma unroll
@@ -256,7 +261,6 @@ __global__ __launch_bounds__(kP1bThreads) void k_p1_bwd(int64_t T, int d, const 
 // so all JT <= 32 sites keep their sums in registers and the sources are
 // read once) and a range of tokens, with the next token's chunks in flight;
 // the range's sums go to part[range][j][d].
-constexpr int kWgradWaves = 2048;
 
 template <typename St>
 struct Quad;  // 4 consecutive channels
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(256) void k_p1_bwd_wgrad(int64_t T, int d, const St
 
 // dw_j += g_j (.) A_j, dg_j += w_j (.) A_j, A_j summed over the ranges in
 // order.  One thread per (site, channel).
-__global__ __launch_bounds__(256) void k_p1_bwd_wgrad_reduce(int64_t ranges, int S, int d,
+static __global__ __launch_bounds__(256) void k_p1_bwd_wgrad_reduce(int64_t ranges, int S, int d,
                                                              const float* __restrict__ part,
                                                              const float* __restrict__ w,
                                                              const float* __restrict__ kg, float* __restrict__ dw,
@@ -352,22 +356,15 @@ __global__ __launch_bounds__(256) void k_p1_bwd_wgrad_reduce(int64_t ranges, int
   if (dkg) dkg[k] += w[k] * A;
 }
 
-// Token ranges of the weight-gradient pass (a fixed count, so the
-// workspace size and the summation order do not depend on the device).
-int64_t p1_backward_ranges(int d) {
-  const int ngroups = ((d >> 2) + 63) >> 6;
-  return (kWgradWaves + ngroups - 1) / ngroups;
-}
-
-template <typename St, int N, int QW>
+template <typename Ut, typename St, int N, int QW>
 static hipError_t run_p1b_main(int64_t T, int d, const void* src, int64_t stride, int S, const float* q, float eps,
                                const void* gin, int64_t gstride, const float* c_in, const float* gp_in, float* dsrc,
                                int64_t dstride, int accumulate, float* coef, hipStream_t stream) {
   int64_t wgs = T;
   const int64_t cap = (int64_t)device_cu_count() * 2;
   if (wgs > cap) wgs = cap;
-  hipLaunchKernelGGL((k_p1_bwd<St, N, QW>), dim3((unsigned)wgs), dim3(kP1bThreads), 0, stream, T, d,
-                     static_cast<const St*>(src), stride, S, q, eps, static_cast<const St*>(gin), gstride, c_in,
+  hipLaunchKernelGGL((k_p1_bwd<Ut, St, N, QW>), dim3((unsigned)wgs), dim3(kP1bThreads), 0, stream, T, d,
+                     static_cast<const Ut*>(src), stride, S, q, eps, static_cast<const St*>(gin), gstride, c_in,
                      gp_in, dsrc, dstride, accumulate, coef);
   return hipGetLastError();
 }
@@ -384,7 +381,7 @@ static hipError_t run_p1b_wgrad(int64_t T, int d, const void* src, int64_t strid
   return hipGetLastError();
 }
 
-template <typename St, int N>
+template <typename Ut, typename St, int N>
 static hipError_t run_p1b(int64_t T, int d, const void* src, int64_t stride, int S, const float* w, const float* kg,
                           float eps, const void* gin, int64_t gstride, const float* c_in, const float* gp_in,
                           float* dsrc, int64_t dstride, int accumulate, float* dw, float* dkg, float* ws,
@@ -398,28 +395,28 @@ static hipError_t run_p1b(int64_t T, int d, const void* src, int64_t stride, int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (S <= 8) {
-    e = run_p1b_main<St, N, 1>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
+    e = run_p1b_main<Ut, St, N, 1>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
                                coef, stream);
   } else if (S <= 16) {
-    e = run_p1b_main<St, N, 2>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
+    e = run_p1b_main<Ut, St, N, 2>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
                                coef, stream);
   } else if (S <= 24) {
-    e = run_p1b_main<St, N, 3>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
+    e = run_p1b_main<Ut, St, N, 3>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
                                coef, stream);
   } else {
-    e = run_p1b_main<St, N, 4>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
+    e = run_p1b_main<Ut, St, N, 4>(T, d, src, stride, S, q, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
                                coef, stream);
   }
   if (e != hipSuccess) return e;
   // (the coefficient table has (S rounded up to 8) sites per token)
   if (S <= 8) {
-    e = run_p1b_wgrad<St, N, 8>(T, d, src, stride, S, coef, part, stream);
+    e = run_p1b_wgrad<Ut, N, 8>(T, d, src, stride, S, coef, part, stream);
   } else if (S <= 16) {
-    e = run_p1b_wgrad<St, N, 16>(T, d, src, stride, S, coef, part, stream);
+    e = run_p1b_wgrad<Ut, N, 16>(T, d, src, stride, S, coef, part, stream);
   } else if (S <= 24) {
-    e = run_p1b_wgrad<St, N, 24>(T, d, src, stride, S, coef, part, stream);
+    e = run_p1b_wgrad<Ut, N, 24>(T, d, src, stride, S, coef, part, stream);
   } else {
-    e = run_p1b_wgrad<St, N, 32>(T, d, src, stride, S, coef, part, stream);
+    e = run_p1b_wgrad<Ut, N, 32>(T, d, src, stride, S, coef, part, stream);
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_p1_bwd_wgrad_reduce, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, stream,
@@ -427,7 +424,7 @@ static hipError_t run_p1b(int64_t T, int d, const void* src, int64_t stride, int
   return hipGetLastError();
 }
 
-template <typename St>
+template <typename Ut, typename St>
 static hipError_t pick_p1b(int n, int64_t T, int d, const void* src, int64_t stride, int S, const float* w,
                            const float* kg, float eps, const void* gin, int64_t gstride, const float* c_in,
                            const float* gp_in, float* dsrc, int64_t dstride, int accumulate, float* dw, float* dkg,
@@ -435,7 +432,7 @@ static hipError_t pick_p1b(int n, int64_t T, int d, const void* src, int64_t str
   switch (n) {
 #define ATTNRES_CASE(N_)                                                                                           \
   case N_:                                                                                                         \
-    return run_p1b<St, N_>(T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate, \
+    return run_p1b<Ut, St, N_>(T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate, \
                            dw, dkg, ws, stream);
     ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4) ATTNRES_CASE(5) ATTNRES_CASE(6)
     ATTNRES_CASE(7) ATTNRES_CASE(8) ATTNRES_CASE(9) ATTNRES_CASE(10) ATTNRES_CASE(11) ATTNRES_CASE(12)
@@ -444,23 +441,5 @@ static hipError_t pick_p1b(int n, int64_t T, int d, const void* src, int64_t str
   }
   return hipErrorInvalidValue;
 }
-
-hipError_t launch_p1_backward(Dtype dt, int64_t T, int d, const void* src, int n, int64_t stride, int S,
-                              const float* w, const float* kg, float eps, const void* gin, int64_t gstride,
-                              const float* c_in, const float* gp_in, float* dsrc, int64_t dstride, int accumulate,
-                              float* dw, float* dkg, float* ws, hipStream_t stream) {
-  // one site without a partial source (the final aggregation): the site
-  // backward without PreNorm computes the same gradients, with a team per
-  // token instead of one busy wave, into fp32 rows; its weight sums are added
-  if (S == 1 && !c_in && !gp_in)
-    return launch_site_backward(dt, T, d, src, n, stride, w, kg, nullptr, 0, eps, gin, dsrc, dstride,
-                                accumulate ? kOutAdd : kOutF32, 1, dw, dkg, nullptr, ws, stream);
-  if (dt == kBF16)
-    return pick_p1b<bf16_t>(n, T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate,
-                            dw, dkg, ws, stream);
-  return pick_p1b<float>(n, T, d, src, stride, S, w, kg, eps, gin, gstride, c_in, gp_in, dsrc, dstride, accumulate, dw,
-                         dkg, ws, stream);
-}
-
 
 }  // namespace attnres

@@ -265,11 +265,12 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
   }
 }
 
-// out = ((partial or 0) + (v2 or 0)) + v, in that order.
-template <typename St, typename Pt>
+// out = ((partial or 0) + (v2 or 0)) + v, in that order; the sum is stored
+// as Ot (the rows' type, or fp32).
+template <typename St, typename Pt, typename Ot>
 __global__ __launch_bounds__(256) void k_accumulate(int64_t nchunks, const Pt* __restrict__ pin,
                                                     const St* __restrict__ v2, const St* __restrict__ v,
-                                                    St* __restrict__ out) {
+                                                    Ot* __restrict__ out) {
   const int64_t step = (int64_t)gridDim.x * 256;
   const int64_t plane = nchunks * 8;
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks; c += step) {
@@ -399,30 +400,31 @@ hipError_t launch_merge(Dtype dt, int64_t T, int d, const void* o1, const float*
                          stream);
 }
 
-template <typename St, typename Pt>
+template <typename St, typename Pt, typename Ot>
 static hipError_t run_acc(int64_t T, int d, const void* pin, const void* v2, const void* v, void* out,
                           hipStream_t stream) {
   const int64_t nchunks = T * (int64_t)(d >> 3);
   const int64_t blocks = (nchunks + 255) / 256;
   const int64_t cap = (int64_t)device_cu_count() * 16;
   const dim3 grid((unsigned)(blocks < cap ? blocks : cap));
-  hipLaunchKernelGGL((k_accumulate<St, Pt>), grid, dim3(256), 0, stream, nchunks, static_cast<const Pt*>(pin),
-                     static_cast<const St*>(v2), static_cast<const St*>(v), static_cast<St*>(out));
+  hipLaunchKernelGGL((k_accumulate<St, Pt, Ot>), grid, dim3(256), 0, stream, nchunks, static_cast<const Pt*>(pin),
+                     static_cast<const St*>(v2), static_cast<const St*>(v), static_cast<Ot*>(out));
   return hipGetLastError();
 }
 
-template <typename St>
+template <typename St, typename Ot>
 static hipError_t acc_pin(Dtype pdt, int64_t T, int d, const void* pin, const void* v2, const void* v, void* out,
                           hipStream_t stream) {
-  if (!pin || pdt == kF32) return run_acc<St, float>(T, d, pin, v2, v, out, stream);
-  if (pdt == kP24) return run_acc<St, p24_t>(T, d, pin, v2, v, out, stream);
-  return run_acc<St, St>(T, d, pin, v2, v, out, stream);
+  if (!pin || pdt == kF32) return run_acc<St, float, Ot>(T, d, pin, v2, v, out, stream);
+  if (pdt == kP24) return run_acc<St, p24_t, Ot>(T, d, pin, v2, v, out, stream);
+  return run_acc<St, St, Ot>(T, d, pin, v2, v, out, stream);
 }
 
-hipError_t launch_accumulate(Dtype dt, int64_t T, int d, Dtype pdt, const void* pin, const void* v2,
+hipError_t launch_accumulate(Dtype dt, Dtype odt, int64_t T, int d, Dtype pdt, const void* pin, const void* v2,
                              const void* v, void* out, hipStream_t stream) {
-  if (dt == kBF16) return acc_pin<bf16_t>(pdt, T, d, pin, v2, v, out, stream);
-  return acc_pin<float>(pdt, T, d, pin, v2, v, out, stream);
+  if (dt == kBF16 && odt == kF32) return acc_pin<bf16_t, float>(pdt, T, d, pin, v2, v, out, stream);
+  if (dt == kBF16) return acc_pin<bf16_t, bf16_t>(pdt, T, d, pin, v2, v, out, stream);
+  return acc_pin<float, float>(pdt, T, d, pin, v2, v, out, stream);
 }
 
 }  // namespace attnres

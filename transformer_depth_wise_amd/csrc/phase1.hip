@@ -34,6 +34,8 @@
 // clamped, valid address and the value is replaced by zero afterwards.  This
 // keeps loads free of exec-mask branches, so the compiler issues a whole
 // K-block (or the next item) of loads before the first wait.
+#include <type_traits>
+
 #include "attnres_device.h"
 #include "attnres_launch.h"
 
@@ -717,9 +719,9 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
 // current item is computed.  N is the exact number of sources.  The S output
 // rows are written with non-temporal stores: they are read back only by the
 // phase-2 launches, long after this kernel.
-template <typename St, int N>
-__device__ __forceinline__ void p1_issue(Chunk<St> (&s)[N], bool& ok, int64_t item, int64_t items, int ngroups,
-                                         const St* __restrict__ src, int64_t stride, int d, int C, int lane) {
+template <typename Ut, int N>
+__device__ __forceinline__ void p1_issue(Chunk<Ut> (&s)[N], bool& ok, int64_t item, int64_t items, int ngroups,
+                                         const Ut* __restrict__ src, int64_t stride, int d, int C, int lane) {
   const int64_t it = item < items ? item : items - 1;
   const int64_t t = it / ngroups;
   const int c0 = (int)(it - t * ngroups) * 64 + lane;
@@ -729,8 +731,8 @@ __device__ __forceinline__ void p1_issue(Chunk<St> (&s)[N], bool& ok, int64_t it
   for (int i = 0; i < N; ++i) s[i].load(src + (int64_t)i * stride + t * d + c * 8);
 }
 
-template <typename St, int N>
-__device__ __forceinline__ void p1_emit(const Chunk<St> (&s)[N], bool ok, int64_t item, int ngroups, int64_t T,
+template <typename Ut, typename St, int N>
+__device__ __forceinline__ void p1_emit(const Chunk<Ut> (&s)[N], bool ok, int64_t item, int ngroups, int64_t T,
                                         int d, int lane, const float* __restrict__ alpha, int S,
                                         St* __restrict__ out, St* __restrict__ out0) {
   const int64_t t = item / ngroups;
@@ -752,8 +754,8 @@ __device__ __forceinline__ void p1_emit(const Chunk<St> (&s)[N], bool ok, int64_
   }
 }
 
-template <typename St, int N>
-__global__ __launch_bounds__(256) void k_p1_out(const St* __restrict__ src, int64_t stride, int64_t T, int d,
+template <typename Ut, typename St, int N>
+__global__ __launch_bounds__(256) void k_p1_out(const Ut* __restrict__ src, int64_t stride, int64_t T, int d,
                                                 const float* __restrict__ alpha, int S, St* __restrict__ out,
                                                 St* __restrict__ out0) {
   const int C = d >> 3;
@@ -762,16 +764,16 @@ __global__ __launch_bounds__(256) void k_p1_out(const St* __restrict__ src, int6
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * 4;
   int64_t item = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  Chunk<St> A[N], B[N];
+  Chunk<Ut> A[N], B[N];
   bool okA, okB;
-  p1_issue<St, N>(A, okA, item, items, ngroups, src, stride, d, C, lane);
+  p1_issue<Ut, N>(A, okA, item, items, ngroups, src, stride, d, C, lane);
   while (item < items) {
-    p1_issue<St, N>(B, okB, item + nw, items, ngroups, src, stride, d, C, lane);
-    p1_emit<St, N>(A, okA, item, ngroups, T, d, lane, alpha, S, out, out0);
+    p1_issue<Ut, N>(B, okB, item + nw, items, ngroups, src, stride, d, C, lane);
+    p1_emit<Ut, St, N>(A, okA, item, ngroups, T, d, lane, alpha, S, out, out0);
     item += nw;
     if (item >= items) break;
-    p1_issue<St, N>(A, okA, item + nw, items, ngroups, src, stride, d, C, lane);
-    p1_emit<St, N>(B, okB, item, ngroups, T, d, lane, alpha, S, out, out0);
+    p1_issue<Ut, N>(A, okA, item + nw, items, ngroups, src, stride, d, C, lane);
+    p1_emit<Ut, St, N>(B, okB, item, ngroups, T, d, lane, alpha, S, out, out0);
     item += nw;
   }
 }
@@ -832,9 +834,9 @@ static inline size_t first_lds_bytes(int d, bool f32) {
   return 4 * padded * (f32 ? 4 : 2) + padded * 4;
 }
 
-template <typename St, int N>
-__device__ __forceinline__ void p1_issue_tok(Chunk<St> (&s)[N], int64_t t, int g, int64_t T,
-                                             const St* __restrict__ src, int64_t stride, int d, int C, int lane) {
+template <typename Ut, int N>
+__device__ __forceinline__ void p1_issue_tok(Chunk<Ut> (&s)[N], int64_t t, int g, int64_t T,
+                                             const Ut* __restrict__ src, int64_t stride, int d, int C, int lane) {
   const int64_t tc = t < T ? t : T - 1;
   const int c0 = g * 64 + lane;
   const int c = c0 < C ? c0 : C - 1;
@@ -842,8 +844,8 @@ __device__ __forceinline__ void p1_issue_tok(Chunk<St> (&s)[N], int64_t t, int g
   for (int i = 0; i < N; ++i) s[i].load(src + (int64_t)i * stride + tc * d + c * 8);
 }
 
-template <typename St, int N, bool FIRST>
-__global__ __launch_bounds__(256) void k_p1_out_tokens(const St* __restrict__ src, int64_t stride, int64_t T,
+template <typename Ut, typename St, int N, bool FIRST>
+__global__ __launch_bounds__(256) void k_p1_out_tokens(const Ut* __restrict__ src, int64_t stride, int64_t T,
                                                        int d, const float* __restrict__ alpha, int S,
                                                        St* __restrict__ out, const float* __restrict__ gamma0,
                                                        float eps, St* __restrict__ x0, St* __restrict__ h0) {
@@ -874,7 +876,7 @@ __global__ __launch_bounds__(256) void k_p1_out_tokens(const St* __restrict__ sr
   advance(tn, gn);
   float ss = 0.f;
 
-  auto emit = [&](const Chunk<St>(&s)[N], int64_t tok, int grp) {
+  auto emit = [&](const Chunk<Ut>(&s)[N], int64_t tok, int grp) {
     const int c = grp * 64 + lane;
     const bool ok = c < C;
     float b[N][8];
@@ -934,15 +936,15 @@ __global__ __launch_bounds__(256) void k_p1_out_tokens(const St* __restrict__ sr
     }
   };
 
-  Chunk<St> A[N], B[N];
-  p1_issue_tok<St, N>(A, t, g, T, src, stride, d, C, lane);
+  Chunk<Ut> A[N], B[N];
+  p1_issue_tok<Ut, N>(A, t, g, T, src, stride, d, C, lane);
   while (t < T) {
-    p1_issue_tok<St, N>(B, tn, gn, T, src, stride, d, C, lane);
+    p1_issue_tok<Ut, N>(B, tn, gn, T, src, stride, d, C, lane);
     emit(A, t, g);
     t = tn, g = gn;
     advance(tn, gn);
     if (t >= T) break;
-    p1_issue_tok<St, N>(A, tn, gn, T, src, stride, d, C, lane);
+    p1_issue_tok<Ut, N>(A, tn, gn, T, src, stride, d, C, lane);
     emit(B, t, g);
     t = tn, g = gn;
     advance(tn, gn);
@@ -1451,16 +1453,20 @@ static bool token_order(int64_t T) {
 
 constexpr size_t kMaxLds = 160 * 1024;
 
-template <typename St, int N>
+// Ut: source rows, St: outputs (the same type, or fp32 sources with bf16
+// outputs; the first query's PreNorm is only fused for equal types).
+template <typename Ut, typename St, int N>
 static hipError_t run_out(const void* src, int64_t stride, int64_t T, int d, const float* al, int S, void* out,
                           const float* gamma0, float eps, void* x0, void* h0, hipStream_t stream) {
-  const St* sp = static_cast<const St*>(src);
+  constexpr bool kSame = std::is_same<Ut, St>::value;
+  const Ut* sp = static_cast<const Ut*>(src);
   St* op = static_cast<St*>(out);
   const bool tok = token_order(T);
   const dim3 tgrid((unsigned)device_cu_count());
-  if (x0 && tok && first_lds_bytes(d, sizeof(St) == 4) <= kMaxLds) {
+  if (!kSame && x0) return hipErrorInvalidValue;
+  if (kSame && x0 && tok && first_lds_bytes(d, sizeof(St) == 4) <= kMaxLds) {
     const size_t lds = first_lds_bytes(d, sizeof(St) == 4);
-    auto k = k_p1_out_tokens<St, N, true>;
+    auto k = k_p1_out_tokens<Ut, St, N, kSame>;
     hipError_t e = set_lds(k, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, tgrid, dim3(256), lds, stream, sp, stride, T, d, al, S, op, gamma0, eps,
@@ -1472,13 +1478,13 @@ static hipError_t run_out(const void* src, int64_t stride, int64_t T, int d, con
   St* op0 = (x0 && h0) ? static_cast<St*>(h0) : op;
   if (op) {
     if (tok && !x0) {
-      hipLaunchKernelGGL((k_p1_out_tokens<St, N, false>), tgrid, dim3(256), 0, stream, sp, stride, T, d, al, S, op,
-                         nullptr, eps, nullptr, nullptr);
+      hipLaunchKernelGGL((k_p1_out_tokens<Ut, St, N, false>), tgrid, dim3(256), 0, stream, sp, stride, T, d, al, S,
+                         op, nullptr, eps, nullptr, nullptr);
     } else {
       const int64_t items = T * (int64_t)(((d >> 3) + 63) >> 6);
       const int64_t wgs = (items + 3) / 4;
       const int64_t cap = (int64_t)device_cu_count() * 8;
-      hipLaunchKernelGGL((k_p1_out<St, N>), dim3((unsigned)(wgs < cap ? wgs : cap)), dim3(256), 0, stream, sp,
+      hipLaunchKernelGGL((k_p1_out<Ut, St, N>), dim3((unsigned)(wgs < cap ? wgs : cap)), dim3(256), 0, stream, sp,
                          stride, T, d, al, S, op, op0);
     }
     hipError_t e = hipGetLastError();
@@ -1491,13 +1497,13 @@ static hipError_t run_out(const void* src, int64_t stride, int64_t T, int d, con
                       nullptr, nullptr, nullptr, gamma0, eps, hh, x0, stream);
 }
 
-template <typename St>
+template <typename Ut, typename St>
 static hipError_t pick_out(int n, const void* src, int64_t stride, int64_t T, int d, const float* al, int S,
                            void* out, const float* gamma0, float eps, void* x0, void* h0, hipStream_t stream) {
   switch (n) {
 #define ATTNRES_CASE(N_) \
   case N_:               \
-    return run_out<St, N_>(src, stride, T, d, al, S, out, gamma0, eps, x0, h0, stream);
+    return run_out<Ut, St, N_>(src, stride, T, d, al, S, out, gamma0, eps, x0, h0, stream);
     ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4) ATTNRES_CASE(5) ATTNRES_CASE(6)
     ATTNRES_CASE(7) ATTNRES_CASE(8) ATTNRES_CASE(9) ATTNRES_CASE(10) ATTNRES_CASE(11) ATTNRES_CASE(12)
     ATTNRES_CASE(13) ATTNRES_CASE(14) ATTNRES_CASE(15) ATTNRES_CASE(16)
@@ -1506,7 +1512,9 @@ static hipError_t pick_out(int n, const void* src, int64_t stride, int64_t T, in
   return hipErrorInvalidValue;
 }
 
-template <typename St, int MT>
+// The scores (and the query packing for their matrix-core type) follow the
+// source rows' type Ut; the outputs are stored as St.
+template <typename Ut, typename St, int MT>
 static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, int d, const float* w,
                             const float* kg, int S, float eps, void* out, float* m_out, float* lse_out,
                             const float* gamma0, void* x0, void* h0, float* ws, hipStream_t stream) {
@@ -1516,7 +1524,7 @@ static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, i
   u32x4_t* pk = reinterpret_cast<u32x4_t*>(ws);
   float* al = ws + (int64_t)nkb * kPackedKBlockWords * 4;
   const int npk = nkb * MT * 4 * 64;
-  hipLaunchKernelGGL((k_pack_queries<St, MT>), dim3((unsigned)((npk + 255) / 256)), dim3(256), 0, stream, w, kg,
+  hipLaunchKernelGGL((k_pack_queries<Ut, MT>), dim3((unsigned)((npk + 255) / 256)), dim3(256), 0, stream, w, kg,
                      S, d, pk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1524,11 +1532,11 @@ static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, i
   if (wide_groups >= device_cu_count()) {
     // enough 64-token tiles for one workgroup per compute unit
     const size_t zl = sizeof(float) * kWideWaves * 16 * S * n;
-    auto kw = k_p1_scores_wide<St, MT>;
+    auto kw = k_p1_scores_wide<Ut, MT>;
     e = set_lds(kw, zl, zl + sizeof(u32x4_t) * 2 * MT * 512);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kw, dim3((unsigned)wide_groups), dim3(64 * (kWideWaves + 1)), zl, stream,
-                       static_cast<const St*>(src), n, stride, T, d, pk, S, eps, al, m_out, lse_out);
+                       static_cast<const Ut*>(src), n, stride, T, d, pk, S, eps, al, m_out, lse_out);
   } else {
     // one workgroup per (16-token tile, group of G sources), then the
     // softmax per pair; G is the largest of 4, 2, 1 that still gives two
@@ -1537,13 +1545,13 @@ static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, i
     const int64_t want = 2 * (int64_t)device_cu_count();
     const int G = tiles * ((n + 3) / 4) >= want ? 4 : (tiles * ((n + 1) / 2) >= want ? 2 : 1);
     const dim3 grid((unsigned)tiles, (unsigned)((n + G - 1) / G));
-    const St* sp = static_cast<const St*>(src);
+    const Ut* sp = static_cast<const Ut*>(src);
     if (G == 4) {
-      hipLaunchKernelGGL((k_p1_scores<St, MT, 4>), grid, dim3(256), 0, stream, sp, n, stride, T, d, pk, S, eps, al);
+      hipLaunchKernelGGL((k_p1_scores<Ut, MT, 4>), grid, dim3(256), 0, stream, sp, n, stride, T, d, pk, S, eps, al);
     } else if (G == 2) {
-      hipLaunchKernelGGL((k_p1_scores<St, MT, 2>), grid, dim3(256), 0, stream, sp, n, stride, T, d, pk, S, eps, al);
+      hipLaunchKernelGGL((k_p1_scores<Ut, MT, 2>), grid, dim3(256), 0, stream, sp, n, stride, T, d, pk, S, eps, al);
     } else {
-      hipLaunchKernelGGL((k_p1_scores<St, MT, 1>), grid, dim3(256), 0, stream, sp, n, stride, T, d, pk, S, eps, al);
+      hipLaunchKernelGGL((k_p1_scores<Ut, MT, 1>), grid, dim3(256), 0, stream, sp, n, stride, T, d, pk, S, eps, al);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1553,23 +1561,23 @@ static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, i
   }
   e = hipGetLastError();
   if (e != hipSuccess || (out == nullptr && x0 == nullptr)) return e;  // statistics only
-  return pick_out<St>(n, src, stride, T, d, al, S, out, gamma0, eps, x0, h0, stream);
+  return pick_out<Ut, St>(n, src, stride, T, d, al, S, out, gamma0, eps, x0, h0, stream);
 }
 
-hipError_t launch_phase1_multi(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
+hipError_t launch_phase1_multi(Dtype dt, Dtype sdt, const void* src, int n, int64_t stride, int64_t T, int d,
                                const float* w, const float* kg, int S, float eps, void* out,
                                float* m_out, float* lse_out, const float* gamma0, void* x0, void* h0, float* ws,
                                hipStream_t stream) {
-  if (dt == kBF16) {
-    if (S <= 16)
-      return run_multi<bf16_t, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, gamma0, x0, h0, ws,
-                                  stream);
-    return run_multi<bf16_t, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, gamma0, x0, h0, ws,
-                                stream);
-  }
-  if (S <= 16)
-    return run_multi<float, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, gamma0, x0, h0, ws, stream);
-  return run_multi<float, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, gamma0, x0, h0, ws, stream);
+#define ATTNRES_MULTI(UT_, ST_)                                                                                   \
+  return S <= 16 ? run_multi<UT_, ST_, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, gamma0, x0, h0, \
+                                          ws, stream)                                                            \
+                 : run_multi<UT_, ST_, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, gamma0, x0, h0, \
+                                          ws, stream)
+  if (dt == kBF16 && sdt == kBF16) ATTNRES_MULTI(bf16_t, bf16_t);
+  if (dt == kBF16 && sdt == kF32) ATTNRES_MULTI(float, bf16_t);
+  if (dt == kF32 && sdt == kF32) ATTNRES_MULTI(float, float);
+#undef ATTNRES_MULTI
+  return hipErrorInvalidValue;
 }
 
 template <typename St>

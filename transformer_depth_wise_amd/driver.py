@@ -94,7 +94,13 @@ class BlockAttnRes:
     ``training``: keep what ``backward`` needs -- every site's phase-1
     output and statistics, and every stored partial sum (each in its own
     buffer instead of in place); the first sublayer is then merged by a
-    phase-2 launch so that its phase-1 output is stored too.
+    phase-2 launch so that its phase-1 output is stored too.  With bf16
+    rows, training keeps the block representations (``reps``, and
+    ``h_final``) in fp32: the notes' section 8 defines b_n as the sum of the
+    block's outputs, and the backward differentiates the forward that reads
+    those exact sums (phase 1 then reads fp32 sources and writes bf16
+    outputs; the embedding and given block sums are copied in exactly).
+    ``dh_final`` then comes in fp32 too.
     """
 
     def __init__(self, T: int, d: int, block_sizes: Sequence[int], dtype: torch.dtype, n_given: int = 0,
@@ -129,16 +135,19 @@ class BlockAttnRes:
                     raise ValueError("the backward of block %d would read %d completed sources (at most %d)"
                                      % (b, 1 + self.n_given + b, _lib.ATTNRES_MAX_SOURCES_MULTI))
         smax = max(self.block_sizes) if self.block_sizes else 1
-        self.reps = torch.empty((n_reps, T, d), dtype=dtype, device=dev)
+        # the block representations' storage: fp32 in a bf16 training pass
+        self.rep_dtype = torch.float32 if self.training else dtype
+        self.reps = torch.empty((n_reps, T, d), dtype=self.rep_dtype, device=dev)
         self.device = dev = self.reps.device  # with its index
         self.o1 = torch.empty((smax, T, d), dtype=dtype, device=dev)
         self.m1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
         self.lse1 = torch.empty((smax, T), dtype=torch.float32, device=dev)
         # the largest phase-1 workspace over the blocks (a one-query phase 1
-        # without the first sublayer's PreNorm, and the final site, need none)
+        # without the first sublayer's PreNorm and with sources of the output
+        # type, and the final site, need none)
         ws = 0
         for b, S in enumerate(self.block_sizes):
-            if T > 0 and (S > 1 or self._fuse(S, 1 + self.n_given + b)):
+            if T > 0 and (S > 1 or self._fuse(S, 1 + self.n_given + b) or self.rep_dtype != dtype):
                 ws = max(ws, _lib.attnres_phase1_workspace_bytes(T, d, 1 + self.n_given + b, S))
         self.workspace = torch.empty((max(ws, 16) // 4,), dtype=torch.float32, device=dev)
         # running partial sum: P24 (24-bit split) for bf16 rows, fp32 for fp32 rows
@@ -158,7 +167,7 @@ class BlockAttnRes:
             self.recipes: List[Optional[tuple]] = [None] * self.L
         self.x = torch.empty((max(1, x_ring), T, d), dtype=dtype, device=dev)
         self.h = torch.empty((T, d), dtype=dtype, device=dev) if keep_h else None
-        self.h_final = torch.empty((T, d), dtype=dtype, device=dev)
+        self.h_final = torch.empty((T, d), dtype=self.rep_dtype, device=dev)
         self.lse_final = torch.empty((T,), dtype=torch.float32, device=dev)
 
     def _new_partial(self) -> torch.Tensor:
@@ -193,6 +202,7 @@ class BlockAttnRes:
     def plan(self) -> List[Launch]:
         """Algorithmic bytes of every launch of one pass, in launch order."""
         r = self._row()
+        rr = self._row(self.rep_dtype)  # a block representation (fp32 in a bf16 training pass)
         r32 = self.T * self.d * (3 if self.partial_format == "p24" else 4)
         stat = self.T * 4
         out: List[Launch] = []
@@ -200,12 +210,13 @@ class BlockAttnRes:
         for S in self.block_sizes:
             fuse = self._fuse(S, n_done)
             if fuse:  # + x of the first sublayer (phase 1 writes it instead of o_0)
-                out.append(Launch("phase1", n_done * r + S * r + S * 2 * stat if n_done > 1 else
-                                  2 * r + S * 2 * stat))
-            elif n_done == 1:  # statistics only; phase 2 reads b_0 as its phase-1 output
-                out.append(Launch("phase1", r + S * 2 * stat))
+                out.append(Launch("phase1", n_done * rr + S * r + S * 2 * stat if n_done > 1 else
+                                  rr + r + S * 2 * stat))
+            elif n_done == 1 and not self.training:
+                # statistics only; phase 2 reads b_0 as its phase-1 output
+                out.append(Launch("phase1", rr + S * 2 * stat))
             else:
-                out.append(Launch("phase1", n_done * r + S * (r + 2 * stat)))
+                out.append(Launch("phase1", n_done * rr + S * (r + 2 * stat)))
             for j in range(S):
                 if j == 0 and fuse:
                     continue
@@ -221,16 +232,16 @@ class BlockAttnRes:
                     b = 4 * r + 2 * r32 + stat        # o, p, v, v; p, x
                 out.append(Launch("phase2", b))
             if S == 1:
-                out.append(Launch("accumulate", 2 * r))
+                out.append(Launch("accumulate", r + rr))
             elif S == 2:
-                out.append(Launch("accumulate", 3 * r))
+                out.append(Launch("accumulate", 2 * r + rr))
             elif S % 2:
-                out.append(Launch("accumulate", 2 * r + r32))   # p (stored at S-1), v; b
+                out.append(Launch("accumulate", r + r32 + rr))       # p (stored at S-1), v; b
             else:
-                out.append(Launch("accumulate", 3 * r + r32))   # p (stored at S-2), v, v; b
+                out.append(Launch("accumulate", 2 * r + r32 + rr))   # p (stored at S-2), v, v; b
             n_done += 1
         if self.final_site:
-            out.append(Launch("final", (n_done + 1) * r + stat))
+            out.append(Launch("final", (n_done + 1) * rr + stat))
         return out
 
     def plan_survey(self) -> List[Launch]:
@@ -369,13 +380,14 @@ class BlockAttnRes:
         The final site: N+1 sources and dL/dh_final read, N+1 fp32 gradients
         written."""
         r = self._row()
+        rr = self._row(self.rep_dtype)  # a block representation (fp32 in a bf16 training pass)
         r32 = self.T * self.d * 4
         rp = self.T * self.d * (3 if self.partial_format == "p24" else 4)
         stat = self.T * 4
         out: List[Launch] = []
         n_reps = 1 + self.n_given + len(self.block_sizes)
-        if self.final_site:
-            out.append(Launch("final_backward", (n_reps + 1) * r + n_reps * r32 + stat))
+        if self.final_site:   # the representations and dL/dh_final (h_final's dtype) read
+            out.append(Launch("final_backward", (n_reps + 1) * rr + n_reps * r32 + stat))
         n = n_reps - 1
         for S in reversed(self.block_sizes):
             n -= 1
@@ -392,7 +404,7 @@ class BlockAttnRes:
                     b = 4 * r + rp + 2 * r32 + r + 3 * stat       # o, dx, p, v, v; R; G
                 out.append(Launch("phase2_backward", b))
             nsrc = n + 1
-            out.append(Launch("phase1_backward", (nsrc + S) * r + 2 * nsrc * r32 + 2 * S * stat +
+            out.append(Launch("phase1_backward", nsrc * rr + S * r + 2 * nsrc * r32 + 2 * S * stat +
                               2 * self.T * S * nsrc * 4))
         return out
 
@@ -412,7 +424,7 @@ class BlockAttnRes:
             raise ValueError("dh_final is required with the final aggregation site")
         _check_params(params, self.d, self.L + (1 if self.final_site else 0), self.L, self.device)
         if self.final_site:
-            _checked_rows(dh_final, "dh_final", self.T, self.d, self.dtype)
+            _checked_rows(dh_final, "dh_final", self.T, self.d, self.h_final.dtype)
         w, g, gam = params["w"], params.get("g"), params.get("gamma")
         T, d, eps, dev = self.T, self.d, self.eps, self.device
         mark = instrument if instrument is not None else (lambda kind, begin: None)
