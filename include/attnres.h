@@ -66,12 +66,20 @@ typedef enum {
     ATTNRES_ESCRATCH = 6 /* more workspace than attnres_phase1_noalloc holds */
 } attnres_status_t;
 
-/* Storage formats.  ATTNRES_P24 is only valid for the running partial sum
- * of a block (partial_in / partial_out): the fp32 value rounded to nearest
- * even at bit 8 of its encoding and kept as its upper 24 bits, stored as two
- * planes -- T*d 16-bit upper halves followed by T*d bytes holding bits 8..15
- * (3 bytes per element; full fp32 range, relative step 2^-16). */
-typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1, ATTNRES_P24 = 2 } attnres_dtype_t;
+/* Storage formats.  ATTNRES_P24 and ATTNRES_Q16 are only valid for the
+ * running partial sum of a block (partial_in / partial_out).
+ * P24: the fp32 value rounded to nearest even at bit 8 of its encoding and
+ * kept as its upper 24 bits, stored as two planes -- T*d 16-bit upper halves
+ * followed by T*d bytes holding bits 8..15 (3 bytes per element; full fp32
+ * range, relative step 2^-16).
+ * Q16: 16-bit fixed point with one power-of-two scale per row -- T*d int16
+ * values q followed by T int32 row exponents e (2 bytes per element plus 4
+ * per row); element k of row t is q[t][k] * 2^(e[t] - 15), where e[t] is
+ * the smallest exponent with every |value| of the row below 2^e[t], and q is
+ * the value times 2^(15 - e[t]) rounded to nearest even (|q| <= 32767): every
+ * element is kept to within 2^-15 of the row's largest magnitude.  Finite
+ * values only.  The buffer must be 16-byte aligned. */
+typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1, ATTNRES_P24 = 2, ATTNRES_Q16 = 3 } attnres_dtype_t;
 
 /* Largest supported values. */
 #define ATTNRES_MAX_D 16384
@@ -193,12 +201,13 @@ int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int6
  *   Otherwise the partial sum is
  *       p = ((partial_in or 0) + (sublayer_prev2 or 0)) + sublayer_prev
  *   in fp32 arithmetic, in that order.  partial_in: [T][d] in format
- *   partial_dt (F32, P24, or dt itself for a sublayer output; NULL = zero);
+ *   partial_dt (F32, P24, Q16, or dt itself for a sublayer output; NULL =
+ *   zero);
  *   sublayer_prev, sublayer_prev2: [T][d] of dtype dt (the outputs of the
  *   previous and the one-before-previous sublayer; sublayer_prev2 NULL =
  *   zero).  With sublayer_prev2 a caller can store the running partial only
  *   at every second sublayer.  p is written to partial_out in format
- *   partial_out_dt (F32 or P24; NULL = not stored); partial_out may be the
+ *   partial_out_dt (F32, P24 or Q16; NULL = not stored); partial_out may be the
  *   same pointer as partial_in when both formats are the same (in place).
  *   Merge: zc = w^T(key_gain (.) p / r(p)), M = max(lse, zc),
  *       h = (e^{lse-M} o + e^{zc-M} p) / (e^{lse-M} + e^{zc-M}).
@@ -395,7 +404,8 @@ attnres_status_t attnres_phase1_backward(attnres_dtype_t dt, attnres_dtype_t src
  * Block completion ("Attention Residuals" notes, section 8: b_n is the sum of
  * the block's sublayer outputs):
  *     out = ((partial_in or 0) + (v2 or 0)) + v      (fp32, in that order)
- *   partial_in: [T][d] in format partial_dt (F32, P24 or dt; NULL = zero);
+ *   partial_in: [T][d] in format partial_dt (F32, P24, Q16 or dt; NULL =
+ *   zero);
  *   v2 (NULL = zero), v: [T][d] dtype dt.  out: [T][d] of dtype out_dt, dt
  *   itself or ATTNRES_F32 with dt == ATTNRES_BF16 (the exact fp32 sum, kept
  *   by a training forward; any other pair is ATTNRES_EDTYPE).  out may be

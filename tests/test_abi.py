@@ -256,6 +256,12 @@ def test_merge_validation(lib):
     assert merge(lib, dt=0, pdt=1, v=6 * A, pin=5 * A) == EDTYPE        # bf16 partial with fp32 rows
     # a P24 partial spans 3 bytes per element: the low-byte plane starts 1024 x 64 x 2 bytes in
     assert merge(lib, v=7 * A + 1024 * 64 * 2, pin=5 * A, pdt=2, pout=7 * A, podt=2) == EALIAS
+    assert merge(lib, T=0, v=6 * A, pin=5 * A, pout=5 * A, pdt=3, podt=3) == 0  # Q16 in place
+    assert merge(lib, v=6 * A, pin=5 * A, pout=5 * A, pdt=3, podt=2) == EALIAS  # Q16 into P24 in place
+    # a Q16 partial ends with T row exponents behind its 1024 x 64 values:
+    # an output starting there overlaps it
+    assert merge(lib, v=6 * A, pin=5 * A, pdt=3, pout=7 * A, podt=3, x=7 * A + 1024 * 64 * 2) == EALIAS
+    assert merge(lib, pdt=4, v=6 * A, pin=5 * A) == EDTYPE
     assert merge(lib, T=0) == 0
     assert merge(lib, T=-1) == EINVAL
     assert merge(lib, T=1 << 31) == EINVAL

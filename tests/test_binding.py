@@ -66,6 +66,10 @@ def test_merge_arguments():
                rows(T, d))
     with pytest.raises(ValueError, match="P24"):
         tdw.attnres_phase2_merge(o, lse, p24[:-1], v, None, w, None, None, 1e-6, None, rows(T, d))
+    q16 = torch.zeros(T * d + 2 * T, dtype=torch.int16)
+    not_on_gpu(tdw.attnres_phase2_merge, o, lse, q16, v, q16, w, None, None, 1e-6, None, rows(T, d))
+    with pytest.raises(ValueError, match="Q16"):      # the row exponents are missing
+        tdw.attnres_phase2_merge(o, lse, q16[:T * d], v, None, w, None, None, 1e-6, None, rows(T, d))
     with pytest.raises(TypeError, match="partial_out"):
         tdw.attnres_phase2_merge(o, lse, None, v, rows(T, d), w, None, None, 1e-6, None, rows(T, d))  # bf16 out
     with pytest.raises(TypeError, match="sublayer_prev"):

@@ -35,15 +35,15 @@ EXTENSIONS = {
         "workspace_bytes": "its size, checked before any launch",
     },
     "attnres_phase2_merge": {
-        # the running partial sum is never bf16: P24 or fp32 (precision)
-        "partial_dt": "format of partial_in (F32, P24 or a sublayer output's dtype)",
+        # the running partial sum is never bf16: Q16, P24 or fp32 (precision)
+        "partial_dt": "format of partial_in (F32, P24, Q16 or a sublayer output's dtype)",
         # storing the partial only every second sublayer saves bytes
         "sublayer_prev2": "the output before the previous one, added first",
-        "partial_out_dt": "format of partial_out (F32 or P24)",
+        "partial_out_dt": "format of partial_out (F32, P24 or Q16)",
     },
     "attnres_full": {},
     "attnres_block_accumulate": {
-        "partial_dt": "format of partial_in (F32, P24 or dt)",
+        "partial_dt": "format of partial_in (F32, P24, Q16 or dt)",
         "out_dt": "dtype of the block sum (dt, or F32: a training forward keeps it exact)",
         "v2": "the block's one-before-last output (partial stored every second sublayer)",
     },

@@ -17,13 +17,18 @@ def rows_per_token_sublayer(plan, T, d, L, esize=2):
 
 
 def test_block_plan_bytes_per_token_sublayer():
-    # the forward at the prefill chunk's shape moves 6.638 rows of d per token
-    # and sublayer (every term is proportional to T; the per-token statistics
-    # make the ratio depend slightly on d); phase 1 writes S outputs per block
-    # except the first block's (its only source is b_0)
+    # the forward at the prefill chunk's shape moves 5.953 rows of d per token
+    # and sublayer with the Q16 partial (2 bytes per element plus a 4-byte row
+    # exponent), 6.638 with the 24-bit one (every term is proportional to T;
+    # the per-token statistics and exponents make the ratio depend slightly on
+    # d); phase 1 writes S outputs per block except the first block's (its
+    # only source is b_0)
     st = tdw.BlockAttnRes(16, 7168, K3, BF, device="cpu")
+    assert st.partial_format == "q16"
     plan = st.plan()
-    assert abs(rows_per_token_sublayer(plan, 16, 7168, 186) - 6.638) < 5e-4
+    assert abs(rows_per_token_sublayer(plan, 16, 7168, 186) - 5.953) < 5e-4
+    p24 = tdw.BlockAttnRes(16, 7168, K3, BF, device="cpu", partial="p24")
+    assert abs(rows_per_token_sublayer(p24.plan(), 16, 7168, 186) - 6.638) < 5e-4
     kinds = [x.kind for x in plan]
     assert kinds.count("phase1") == 8 and kinds.count("accumulate") == 8 and kinds.count("final") == 1
     assert kinds.count("phase2") == 186 - 8     # the first sublayer of each block leaves phase 1
@@ -48,14 +53,20 @@ def test_block_plan_survey_rows():
 
 
 def test_block_plan_backward_bytes():
-    # the 16K chunk's backward moves 520663793664 bytes (every term is
-    # proportional to T): 16 tokens of it move 1/1024 of that.  The block
+    # the 16K chunk's backward moves 501649047552 bytes with the Q16 partial
+    # (every term is proportional to T): 16 tokens of it move 1/1024 of
+    # that.  With the 24-bit partial: one byte more per element for each of
+    # the 162 partial reads of the phase-2 backward (21 per block of 24, 15
+    # for the block of 18), less their row exponents.  The block
     # representations are fp32 in a bf16 training pass: 46 rows per token
     # more than bf16 ones would move (the final site's 9 representations and
     # dL/dh_final, and the 1 + 2 + ... + 8 block-source reads of phase 1)
     st = tdw.BlockAttnRes(16, 7168, K3, BF, device="cpu", training=True)
     assert st.reps.dtype == torch.float32 and st.h_final.dtype == torch.float32
-    assert sum(x.bytes for x in st.plan_backward()) * 1024 == 520663793664
+    assert sum(x.bytes for x in st.plan_backward()) * 1024 == 501649047552
+    p24 = tdw.BlockAttnRes(16, 7168, K3, BF, device="cpu", training=True, partial="p24")
+    assert sum(x.bytes for x in p24.plan_backward()) * 1024 == 520663793664
+    assert 520663793664 - 501649047552 == 162 * 16384 * (7168 - 4)
     assert 520663793664 - 509859266560 == 46 * 16384 * 7168 * 2
     inf = tdw.BlockAttnRes(16, 7168, K3, BF, device="cpu")
     assert inf.reps.dtype == BF and inf.h_final.dtype == BF

@@ -55,7 +55,7 @@ def test_decode_block_bf16_all_tokens():
     _say("worst", worst)
 
 
-@pytest.mark.parametrize("partial", ["p24", "f32"])
+@pytest.mark.parametrize("partial", ["q16", "p24", "f32"])
 def test_prefill_chunk_bf16_sampled(partial):
     w = synth.WORKLOADS["prefill_chunk_bf16"]
     _say("case prefill_chunk_bf16 T=%d d=%d blocks=%s partial=%s (64 sampled tokens)"
@@ -95,6 +95,51 @@ def test_p24_partial_roundtrip_is_exact():
         bad[:4].tolist(), got[tuple(bad[0])], want[tuple(bad[0])], pin.cpu().numpy()[tuple(bad[0])])
     rel = np.abs(back.cpu().numpy() - pin.cpu().numpy()) / np.maximum(np.abs(pin.cpu().numpy()), 1e-30)
     assert rel.max() <= 2.0 ** -16
+
+
+def _q16_emulate(x: np.ndarray) -> np.ndarray:
+    """The Q16 format's value of fp32 rows x: per row the exponent e of
+    frexp(max |x|) (max |x| < 2^e), q = x * 2^(15 - e) rounded to nearest
+    even and clamped to [-32767, 32767], value q * 2^(e - 15)."""
+    x = x.astype(np.float64)
+    e = np.frexp(np.abs(x).max(axis=1))[1][:, None].astype(np.float64)
+    q = np.clip(np.rint(np.ldexp(x, (15 - e).astype(np.int64))), -32767, 32767)
+    return np.ldexp(q, (e - 15).astype(np.int64))
+
+
+def test_q16_partial_roundtrip_is_exact():
+    _say("case Q16 partial round trip")
+    dev = torch.device("cuda")
+    T, d = 37, 1032
+    row_scale = torch.logspace(-20, 20, T, device=dev)[:, None]
+    pin = (torch.randn((T, d), device=dev) * row_scale).float()
+    pin[0] = 0.0                                          # zero row: exponent 0, all zeros
+    pin[1, :] = 0.25
+    pin[1, 5] = -1.0                                      # largest magnitude exactly a power of two
+    pin[2, :] = 1e-3
+    pin[2, 7] = 1.0 - 2.0 ** -20                          # rounds to 32768 steps: clamped to 32767
+    pin[3, :8] = torch.tensor([3.0, -3.0, 1.5, -0.0, 2.0 ** -16, 2.0 ** -17, 3 * 2.0 ** -17, 5 * 2.0 ** -18])
+    zeros = torch.zeros((T, d), dtype=torch.float32, device=dev)
+    o = torch.randn((T, d), device=dev)
+    lse = torch.zeros((T,), device=dev)
+    q16 = tdw._lib.q16_partial(T, d, dev)
+    x = torch.empty((T, d), device=dev)
+    # p = pin + 0, stored as Q16 (fp32 rows: the partial's format is independent of them)
+    tdw.attnres_phase2_merge(o, lse, pin, zeros, q16, torch.zeros(d, device=dev), None, None, 1e-6, None, x)
+    back = torch.empty((T, d), device=dev)
+    tdw.attnres_block_accumulate(q16, zeros, back)  # Q16 -> fp32 + 0
+    torch.cuda.synchronize()
+    got, want = back.cpu().numpy().astype(np.float64), _q16_emulate(pin.cpu().numpy())
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "Q16 mismatch at %s: got %r want %r (input %r)" % (
+        bad[:4].tolist(), got[tuple(bad[0])], want[tuple(bad[0])], pin.cpu().numpy()[tuple(bad[0])])
+    assert np.all(got[0] == 0.0) and got[2, 7] == 32767 * 2.0 ** -15
+    # every element within 2^-15 of its row's largest magnitude
+    ref = pin.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref).max(axis=1) / np.maximum(np.abs(ref).max(axis=1), 1e-300)
+    assert err.max() <= 2.0 ** -15
+    # the Python-side decoder reads the same values
+    np.testing.assert_array_equal(tdw._lib.q16_decode(q16, T, d).cpu().numpy(), got.astype(np.float32))
 
 
 # -------------------------------------------------- ragged and edge shapes

@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattnres.so")
 
-F32, BF16, P24 = 0, 1, 2
+F32, BF16, P24, Q16 = 0, 1, 2, 3
 ATTNRES_MAX_D = 16384
 ATTNRES_MAX_SOURCES = 32
 ATTNRES_MAX_SOURCES_MULTI = 16
@@ -90,19 +90,42 @@ def status_string(code: int) -> str:
 
 def dtype_code(t: torch.dtype) -> int:
     """float32 -> F32, bfloat16 -> BF16; a uint8 tensor holds a partial sum in
-    the 24-bit split format (P24, 3 bytes per element)."""
+    the 24-bit split format (P24, 3 bytes per element), an int16 tensor one in
+    the 16-bit fixed-point format with row exponents (Q16)."""
     if t == torch.float32:
         return F32
     if t == torch.bfloat16:
         return BF16
     if t == torch.uint8:
         return P24
-    raise TypeError("unsupported storage dtype %s (float32, bfloat16, or uint8 for a P24 partial)" % t)
+    if t == torch.int16:
+        return Q16
+    raise TypeError("unsupported storage dtype %s (float32, bfloat16, or uint8 / int16 for a P24 / Q16 partial)" % t)
 
 
 def p24_partial(T: int, d: int, device) -> torch.Tensor:
     """An uninitialised partial-sum buffer in the P24 format."""
     return torch.empty((3 * T * d,), dtype=torch.uint8, device=device)
+
+
+def q16_partial(T: int, d: int, device) -> torch.Tensor:
+    """An uninitialised partial-sum buffer in the Q16 format: T*d int16 values
+    followed by T int32 row exponents (2 int16 elements each)."""
+    return torch.empty((T * d + 2 * T,), dtype=torch.int16, device=device)
+
+
+def _pow2(k: torch.Tensor) -> torch.Tensor:
+    """Exactly 2^k in fp32 for integer k in [-126, 127] (built from its bits)."""
+    return ((k + 127).to(torch.int32) << 23).view(torch.float32)
+
+
+def q16_decode(buf: torch.Tensor, T: int, d: int) -> torch.Tensor:
+    """The fp32 values of a Q16 partial: q * 2^(e - 15) per row, exact (for
+    inspection and tests; the scale is applied as two exact powers of two)."""
+    q = buf[:T * d].view(T, d).float()
+    k = buf[T * d:T * d + 2 * T].view(torch.int32).view(T, 1) - 15
+    k1 = torch.div(k, 2, rounding_mode="floor")
+    return q * _pow2(k1) * _pow2(k - k1)
 
 
 def _rows(t: Optional[torch.Tensor], name: str, T: int, d: int, dtype: torch.dtype, n: int = 1,
@@ -166,8 +189,15 @@ def _partial(t: Optional[torch.Tensor], name: str, T: int, d: int, dtype: torch.
         if not t.is_contiguous() or t.numel() < 3 * T * d:
             raise ValueError("%s: a P24 partial needs a contiguous uint8 buffer of >= %d bytes" % (name, 3 * T * d))
         return P24
+    if t.dtype == torch.int16:
+        if not t.is_contiguous() or t.numel() < T * d + 2 * T:
+            raise ValueError("%s: a Q16 partial needs a contiguous int16 buffer of >= %d elements"
+                             % (name, T * d + 2 * T))
+        if t.data_ptr() % 16:
+            raise ValueError("%s: a Q16 partial must be 16-byte aligned" % name)
+        return Q16
     if t.dtype != torch.float32 and not (allow_storage and t.dtype == dtype):
-        raise TypeError("%s: dtype %s, expected float32, uint8 (P24)%s"
+        raise TypeError("%s: dtype %s, expected float32, uint8 (P24), int16 (Q16)%s"
                         % (name, t.dtype, (" or %s" % dtype) if allow_storage else ""))
     _rows(t, name, T, d, t.dtype)
     return dtype_code(t.dtype)

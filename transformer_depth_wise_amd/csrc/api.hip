@@ -46,14 +46,23 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 int64_t esize(attnres_dtype_t dt) { return dt == ATTNRES_F32 ? 4 : dt == ATTNRES_P24 ? 3 : 2; }
 
-// row storage: F32 or BF16; a partial sum may also be P24
+// Bytes of a [T][d] partial sum in format pdt (Q16: the values, then T row
+// exponents).
+int64_t partial_bytes(attnres_dtype_t pdt, int64_t T, int64_t d) {
+  return T * d * esize(pdt) + (pdt == ATTNRES_Q16 ? T * 4 : 0);
+}
+
+// row storage: F32 or BF16; a partial sum may also be P24 or Q16
 bool dtype_ok(attnres_dtype_t dt) { return dt == ATTNRES_F32 || dt == ATTNRES_BF16; }
 bool partial_ok(attnres_dtype_t pdt, attnres_dtype_t dt) {
-  return pdt == ATTNRES_F32 || pdt == ATTNRES_P24 || pdt == dt;
+  return pdt == ATTNRES_F32 || pdt == ATTNRES_P24 || pdt == ATTNRES_Q16 || pdt == dt;
 }
 
 Dtype kind_of(attnres_dtype_t dt) {
-  return dt == ATTNRES_F32 ? attnres::kF32 : dt == ATTNRES_P24 ? attnres::kP24 : attnres::kBF16;
+  return dt == ATTNRES_F32   ? attnres::kF32
+         : dt == ATTNRES_P24 ? attnres::kP24
+         : dt == ATTNRES_Q16 ? attnres::kQ16
+                             : attnres::kBF16;
 }
 
 attnres_status_t check_d(int64_t d) {
@@ -251,7 +260,8 @@ attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, 
                                       const float* w, const float* key_gain, const float* prenorm_gain, float eps,
                                       void* h_out, void* x_out, void* stream) {
   if (!dtype_ok(dt) || !partial_ok(partial_dt, dt)) return ATTNRES_EDTYPE;
-  if (partial_out_dt != ATTNRES_F32 && partial_out_dt != ATTNRES_P24) return ATTNRES_EDTYPE;
+  if (partial_out_dt != ATTNRES_F32 && partial_out_dt != ATTNRES_P24 && partial_out_dt != ATTNRES_Q16)
+    return ATTNRES_EDTYPE;
   attnres_status_t st = check_d(d);
   if (st != ATTNRES_OK) return st;
   if (!extent_ok(T) || !(eps >= 0.f)) return ATTNRES_EINVAL;
@@ -266,10 +276,10 @@ attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, 
   const int64_t es = esize(dt);
   const int64_t rows = T * d;
   const Range r_o = range_of(p1_out, rows * es), r_l = range_of(p1_lse, T * 4);
-  const Range r_pi = partial_in ? range_of(partial_in, rows * esize(partial_dt)) : Range{0, 0};
+  const Range r_pi = partial_in ? range_of(partial_in, partial_bytes(partial_dt, T, d)) : Range{0, 0};
   const Range r_v = sublayer_prev ? range_of(sublayer_prev, rows * es) : Range{0, 0};
   const Range r_v2 = sublayer_prev2 ? range_of(sublayer_prev2, rows * es) : Range{0, 0};
-  const Range r_po = partial_out ? range_of(partial_out, rows * esize(partial_out_dt)) : Range{0, 0};
+  const Range r_po = partial_out ? range_of(partial_out, partial_bytes(partial_out_dt, T, d)) : Range{0, 0};
   const Range r_w = w ? range_of(w, d * 4) : Range{0, 0};
   const Range r_g = key_gain ? range_of(key_gain, d * 4) : Range{0, 0};
   const Range r_gm = prenorm_gain ? range_of(prenorm_gain, d * 4) : Range{0, 0};
@@ -426,7 +436,7 @@ attnres_status_t attnres_phase2_backward(attnres_dtype_t dt, int64_t T, int64_t 
   if (st != ATTNRES_OK) return st;
   const int64_t es = esize(dt), rows = T * d;
   const Range i_o = range_of(p1_out, rows * es), i_l = p1_lse ? range_of(p1_lse, T * 4) : Range{0, 0};
-  const Range i_p = partial_in ? range_of(partial_in, rows * esize(partial_dt)) : Range{0, 0};
+  const Range i_p = partial_in ? range_of(partial_in, partial_bytes(partial_dt, T, d)) : Range{0, 0};
   const Range i_v2 = sublayer_prev2 ? range_of(sublayer_prev2, rows * es) : Range{0, 0};
   const Range i_v = sublayer_prev ? range_of(sublayer_prev, rows * es) : Range{0, 0};
   const Range i_w = range_of(w, d * 4), i_g = key_gain ? range_of(key_gain, d * 4) : Range{0, 0};
@@ -568,7 +578,7 @@ attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t
   const int64_t rows = T * d;
   const Range ro = range_of(out, rows * esize(out_dt));
   const Range rv = range_of(v, rows * esize(dt));
-  const Range rp = partial_in ? range_of(partial_in, rows * esize(partial_dt)) : Range{0, 0};
+  const Range rp = partial_in ? range_of(partial_in, partial_bytes(partial_dt, T, d)) : Range{0, 0};
   const Range rv2 = v2 ? range_of(v2, rows * esize(dt)) : Range{0, 0};
   if (overlaps(ro, rv) || overlaps(ro, rv2)) return ATTNRES_EALIAS;
   const bool in_place = partial_in == out && partial_dt == out_dt;

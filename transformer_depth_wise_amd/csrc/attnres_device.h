@@ -19,6 +19,14 @@ struct p24_t {
   unsigned char byte;
 };
 
+// Storage tag for the 16-bit fixed-point format of a block's running partial
+// sum: a plane of T*d int16 values q, then T int32 row exponents e; element
+// k of row t is q[t][k] * 2^(e[t] - 15), with 2^e[t] above the row's largest
+// magnitude (so every element is kept to within 2^-15 of the row's largest).
+struct q16_t {
+  short q;
+};
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -135,6 +143,64 @@ template <> struct Chunk<p24_t> {
   }
 };
 
+template <> struct Chunk<q16_t> {
+  u32x4_t r;  // 8 int16 values
+  __device__ __forceinline__ void load_at(const q16_t* b, int64_t off, int64_t) { r = ld16(b + off); }
+  __device__ __forceinline__ void zero() { r = u32x4_t{0u, 0u, 0u, 0u}; }
+  // the values times 2^(e - 15)
+  __device__ __forceinline__ void unpack(float (&v)[8], int e) const {
+    const unsigned w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = (int)(short)(unsigned short)(w[i >> 1] >> (16 * (i & 1)));
+      v[i] = ldexpf((float)q, e - 15);
+    }
+  }
+};
+
+// The per-row part of a partial-sum format: the row exponent of Q16, nothing
+// for the others.  load(base, tok, plane) reads row tok's exponent from
+// behind the plane of T*d values.
+template <typename Pt> struct RowExp {
+  __device__ __forceinline__ void load(const Pt*, int64_t, int64_t) {}
+};
+template <> struct RowExp<q16_t> {
+  int e;
+  __device__ __forceinline__ void load(const q16_t* b, int64_t tok, int64_t plane) {
+    e = *reinterpret_cast<const int*>(reinterpret_cast<const unsigned char*>(b) + plane * 2 + tok * 4);
+  }
+};
+
+// A partial-sum chunk as fp32 values, whatever its format.
+template <typename Pt>
+__device__ __forceinline__ void unpack_partial(const Chunk<Pt>& c, const RowExp<Pt>&, float (&v)[8]) {
+  c.unpack(v);
+}
+template <>
+__device__ __forceinline__ void unpack_partial(const Chunk<q16_t>& c, const RowExp<q16_t>& x, float (&v)[8]) {
+  c.unpack(v, x.e);
+}
+
+// Q16 row exponent for a row whose largest magnitude is amax: the e with
+// amax < 2^e (frexp's exponent; 0 for a zero row).
+__device__ __forceinline__ int q16_exponent(float amax) {
+  int e = 0;
+  (void)frexpf(amax, &e);
+  return e;
+}
+
+// 8 values of a row with exponent e as Q16 (nearest, ties to even; |q| <= 32767).
+__device__ __forceinline__ u32x4_t q16_pack(const float (&v)[8], int e) {
+  unsigned h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float q = rintf(ldexpf(v[i], 15 - e));
+    q = fminf(fmaxf(q, -32767.f), 32767.f);
+    h[i] = (unsigned)(unsigned short)(short)(int)q;
+  }
+  return u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+}
+
 // fp32 -> upper 24 bits, round to nearest even at bit 8 (finite values).
 __device__ __forceinline__ unsigned round24(float x) {
   const unsigned u = __float_as_uint(x);
@@ -213,6 +279,35 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+
+// Sums of a and b and the maximum of c over the 256 threads of a workgroup,
+// in a fixed order (identical in every thread); `lds` holds 12 floats,
+// alternated by the caller like block_sum2_256's.
+__device__ __forceinline__ float3 block_sum2_max_256(float a, float b, float c, float* lds) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  c = wave_max(c);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    lds[3 * wave + 0] = a;
+    lds[3 * wave + 1] = b;
+    lds[3 * wave + 2] = c;
+  }
+  lds_barrier();
+  float3 r;
+  // the same order as block_sum2_256: (w0 + w1) + (w2 + w3)
+  r.x = (lds[0] + lds[3]) + (lds[6] + lds[9]);
+  r.y = (lds[1] + lds[4]) + (lds[7] + lds[10]);
+  r.z = fmaxf(fmaxf(lds[2], lds[5]), fmaxf(lds[8], lds[11]));
+  return r;
 }
 
 // Sum of (a, b) over the 256 threads of a workgroup, in a fixed order (the

@@ -6,7 +6,7 @@
 
 namespace attnres {
 
-enum Dtype { kF32 = 0, kBF16 = 1, kP24 = 2 };
+enum Dtype { kF32 = 0, kBF16 = 1, kP24 = 2, kQ16 = 3 };
 
 int device_cu_count();
 

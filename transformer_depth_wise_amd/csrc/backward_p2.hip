@@ -43,6 +43,7 @@ template <typename St, typename Pt, int CPL>
 struct BStage {
   Chunk<St> o[CPL], v[CPL], v2[CPL], dx[CPL];
   Chunk<Pt> q[CPL];
+  RowExp<Pt> qe;
   Chunk<float> r[CPL];
   bool ok[CPL];
 };
@@ -53,6 +54,7 @@ __device__ __forceinline__ void bissue(BStage<St, Pt, CPL>& s, int64_t tok, int6
                                        const St* dx, const float* dpart, int64_t plane) {
   const bool live = tok < T;
   const int64_t tc = live ? tok : T - 1;
+  if (HAS_PIN) s.qe.load(pin, tc, plane);
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
     const int c0 = tl + TEAM * k;
@@ -125,7 +127,7 @@ __device__ __forceinline__ void bprocess(const BStage<St, Pt, CPL>& s, int64_t t
       float v[8];
       s.v[k].unpack(v);
       if (HAS_PIN) {
-        s.q[k].unpack(p[k]);
+        unpack_partial(s.q[k], s.qe, p[k]);
         if (HAS_V2) {
           float v2[8];
           s.v2[k].unpack(v2);
@@ -446,6 +448,9 @@ hipError_t launch_p2_backward(Dtype dt, int64_t T, int d, const void* o1, const 
   do {                                                                                                             \
     if (!pin || pdt == kF32)                                                                                       \
       return pick_p2b<St_, float>(T, d, o1, lse1, pin, vprev2, vprev, w, kg, gamma, prenorm, eps, dx, dpart, g_out, \
+                                  c_out, gp_out, dw, dkg, dgamma, part, stream);                                   \
+    if (pdt == kQ16)                                                                                               \
+      return pick_p2b<St_, q16_t>(T, d, o1, lse1, pin, vprev2, vprev, w, kg, gamma, prenorm, eps, dx, dpart, g_out, \
                                   c_out, gp_out, dw, dkg, dgamma, part, stream);                                   \
     if (pdt == kP24)                                                                                               \
       return pick_p2b<St_, p24_t>(T, d, o1, lse1, pin, vprev2, vprev, w, kg, gamma, prenorm, eps, dx, dpart, g_out, \

@@ -34,8 +34,12 @@ template <typename St, typename Pt, int CPL>
 struct Stage {
   Chunk<St> o[CPL], v[CPL], v2[CPL];
   Chunk<Pt> q[CPL];
+  RowExp<Pt> qe;
   bool ok[CPL];
 };
+
+// Formats of the stored partial sum (pfmt).
+constexpr int kPoutF32 = 0, kPoutP24 = 1, kPoutQ16 = 2;
 
 // Loads of one token for the team.  Every load is unconditional (an
 // out-of-range token or chunk reads a clamped valid address and is zeroed
@@ -46,6 +50,7 @@ __device__ __forceinline__ void issue(Stage<St, Pt, CPL>& s, int64_t tok, int64_
                                       int64_t plane) {
   const bool live = tok < T;
   const int64_t tc = live ? tok : T - 1;
+  if (HAS_PIN) s.qe.load(pin, tc, plane);
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
     const int c0 = tl + TEAM * k;
@@ -61,12 +66,14 @@ __device__ __forceinline__ void issue(Stage<St, Pt, CPL>& s, int64_t tok, int64_
 
 template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN, bool HAS_V2>
 __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok, int64_t T, int d, int C, int tl,
-                                        const float* lse1, void* pout, bool pout24, int64_t plane,
+                                        const float* lse1, void* pout, int pfmt, int64_t plane,
                                         const float (&wq)[CPL][8], const float4* gm_lds, float eps, float inv_d,
-                                        St* h_out, St* x_out, float (*red)[8], int& parity) {
+                                        St* h_out, St* x_out, float (*red)[12], int& parity) {
   const bool live = tok < T;
+  // a Q16 partial is stored after the row's largest magnitude is known
+  const bool q16 = pout && pfmt == kPoutQ16;
   float h[CPL][8], p[CPL][8];
-  float ss = 0.f, dot = 0.f;
+  float ss = 0.f, dot = 0.f, amax = 0.f;
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
     s.o[k].unpack(h[k]);
@@ -75,7 +82,7 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
       float v[8];
       s.v[k].unpack(v);
       if (HAS_PIN) {
-        s.q[k].unpack(p[k]);
+        unpack_partial(s.q[k], s.qe, p[k]);
         if (HAS_V2) {
           float v2[8];
           s.v2[k].unpack(v2);
@@ -102,9 +109,9 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
     }
     if (HAS_V) {
       const int c = tl + TEAM * k;
-      if (pout && s.ok[k]) {
+      if (pout && !q16 && s.ok[k]) {
         const int64_t off = tok * d + c * 8;
-        if (pout24) {
+        if (pfmt == kPoutP24) {
           out24(static_cast<p24_t*>(pout), off, plane, p[k]);
         } else {
           out8(static_cast<float*>(pout) + off, p[k]);
@@ -114,12 +121,32 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
       for (int e = 0; e < 8; ++e) {
         ss = fmaf(p[k][e], p[k][e], ss);
         dot = fmaf(wq[k][e], p[k][e], dot);
+        amax = fmaxf(amax, fabsf(p[k][e]));
       }
     }
   }
   if (HAS_V) {
     float2 r;
-    if (TEAM == 256) {
+    if (q16) {
+      // one exchange for both sums and the row's largest magnitude
+      float pmax;
+      if (TEAM == 256) {
+        const float3 r3 = block_sum2_max_256(ss, dot, amax, red[parity]);
+        parity ^= 1;
+        r = make_float2(r3.x, r3.y);
+        pmax = r3.z;
+      } else {
+        r.x = wave_sum(ss);
+        r.y = wave_sum(dot);
+        pmax = wave_max(amax);
+      }
+      const int e = q16_exponent(pmax);
+      unsigned char* pb = static_cast<unsigned char*>(pout);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+        if (s.ok[k]) st16(pb + (tok * d + (tl + TEAM * k) * 8) * 2, q16_pack(p[k], e));
+      if (live && tl == 0) *reinterpret_cast<int*>(pb + plane * 2 + tok * 4) = e;
+    } else if (TEAM == 256) {
       r = block_sum2_256(ss, dot, red[parity]);
       parity ^= 1;
     } else {
@@ -170,13 +197,13 @@ template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN,
 __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __restrict__ o1,
                                                const float* __restrict__ lse1, const Pt* __restrict__ pin,
                                                const St* __restrict__ vprev2, const St* __restrict__ vprev,
-                                               void* __restrict__ pout, int pout24,
+                                               void* __restrict__ pout, int pfmt,
                                                const float* __restrict__ w, const float* __restrict__ kg,
                                                const float* __restrict__ gamma, float eps,
                                                St* __restrict__ h_out, St* __restrict__ x_out) {
   constexpr int TPW = 256 / TEAM;
   const int64_t plane = T * (int64_t)d;
-  __shared__ float red[2][8];
+  __shared__ float red[2][12];
   // the PreNorm gain, used once per token at the very end, waits in LDS; the
   // folded query w (.) g stays in registers
   extern __shared__ float4 gm_lds[];  // [d / 4]
@@ -252,13 +279,13 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
   lds_barrier();
   while (tok - team < T) {
     issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(B, tok + step, T, d, C, tl, o1, pin, vprev2, vprev, plane);
-    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(A, tok, T, d, C, tl, lse1, pout, pout24 != 0, plane, wq, gm_lds, eps,
+    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(A, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq, gm_lds, eps,
                                               inv_d, h_out, x_out,
                                               red, parity);
     tok += step;
     if (tok - team >= T) break;
     issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(A, tok + step, T, d, C, tl, o1, pin, vprev2, vprev, plane);
-    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(B, tok, T, d, C, tl, lse1, pout, pout24 != 0, plane, wq, gm_lds, eps,
+    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(B, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq, gm_lds, eps,
                                               inv_d, h_out, x_out,
                                               red, parity);
     tok += step;
@@ -266,37 +293,43 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
 }
 
 // out = ((partial or 0) + (v2 or 0)) + v, in that order; the sum is stored
-// as Ot (the rows' type, or fp32).
+// as Ot (the rows' type, or fp32).  A workgroup takes whole rows (a partial
+// sum's row exponent is read once per row) and its threads the row's chunks.
 template <typename St, typename Pt, typename Ot>
-__global__ __launch_bounds__(256) void k_accumulate(int64_t nchunks, const Pt* __restrict__ pin,
+__global__ __launch_bounds__(256) void k_accumulate(int64_t T, int d, const Pt* __restrict__ pin,
                                                     const St* __restrict__ v2, const St* __restrict__ v,
                                                     Ot* __restrict__ out) {
-  const int64_t step = (int64_t)gridDim.x * 256;
-  const int64_t plane = nchunks * 8;
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks; c += step) {
-    float a[8], b[8];
-    load8(v + c * 8, b);
-    if (pin) {
-      Chunk<Pt> q;
-      q.load_at(pin, c * 8, plane);
-      q.unpack(a);
-      if (v2) {
-        float t[8];
-        load8(v2 + c * 8, t);
+  const int C = d >> 3;
+  const int64_t plane = T * (int64_t)d;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    RowExp<Pt> qe;
+    if (pin) qe.load(pin, t, plane);
+    for (int c = threadIdx.x; c < C; c += 256) {
+      const int64_t off = t * d + c * 8;
+      float a[8], b[8];
+      load8(v + off, b);
+      if (pin) {
+        Chunk<Pt> q;
+        q.load_at(pin, off, plane);
+        unpack_partial(q, qe, a);
+        if (v2) {
+          float x[8];
+          load8(v2 + off, x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = a[e] + t[e];
+          for (int e = 0; e < 8; ++e) a[e] = a[e] + x[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = a[e] + b[e];
+      } else if (v2) {
+        load8(v2 + off, a);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = a[e] + b[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = b[e];
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = a[e] + b[e];
-    } else if (v2) {
-      load8(v2 + c * 8, a);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = a[e] + b[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = b[e];
+      store8(out + off, a);
     }
-    store8(out + c * 8, a);
   }
 }
 
@@ -304,7 +337,7 @@ __global__ __launch_bounds__(256) void k_accumulate(int64_t nchunks, const Pt* _
 
 template <typename St, typename Pt, int TEAM, int CPL>
 static hipError_t run_merge(int64_t T, int d, const void* o1, const float* lse1, const void* pin,
-                            const void* vprev2, const void* vprev, void* pout, int pout24, const float* w,
+                            const void* vprev2, const void* vprev, void* pout, int pfmt, const float* w,
                             const float* kg, const float* gamma, float eps, void* h_out, void* x_out,
                             hipStream_t stream) {
   constexpr int TPW = 256 / TEAM;
@@ -334,7 +367,7 @@ static hipError_t run_merge(int64_t T, int d, const void* o1, const float* lse1,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);          \
       if (e != hipSuccess) return e;                                                                            \
     }                                                                                                           \
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, T, d, o, lse1, pi, v2, v, pout, pout24, w, kg, gamma, \
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, T, d, o, lse1, pi, v2, v, pout, pfmt, w, kg, gamma, \
                        eps, h, x);                                                                              \
   } while (0)
   if (!vprev) {
@@ -356,12 +389,12 @@ static hipError_t run_merge(int64_t T, int d, const void* o1, const float* lse1,
 
 template <typename St, typename Pt>
 static hipError_t pick_team(int64_t T, int d, const void* o1, const float* lse1, const void* pin,
-                            const void* vprev2, const void* vprev, void* pout, int pout24, const float* w,
+                            const void* vprev2, const void* vprev, void* pout, int pfmt, const float* w,
                             const float* kg, const float* gamma, float eps, void* h_out, void* x_out,
                             hipStream_t stream) {
   const int C = d >> 3;
 #define ATTNRES_RUN_MERGE(TEAM_, CPL_)                                                                             \
-  return run_merge<St, Pt, TEAM_, CPL_>(T, d, o1, lse1, pin, vprev2, vprev, pout, pout24, w, kg, gamma, eps, h_out, \
+  return run_merge<St, Pt, TEAM_, CPL_>(T, d, o1, lse1, pin, vprev2, vprev, pout, pfmt, w, kg, gamma, eps, h_out, \
                                         x_out, stream)
   if (C <= 64) ATTNRES_RUN_MERGE(64, 1);
   if (C <= 128) ATTNRES_RUN_MERGE(64, 2);
@@ -374,17 +407,20 @@ static hipError_t pick_team(int64_t T, int d, const void* o1, const float* lse1,
 
 template <typename St>
 static hipError_t pick_pin(Dtype pdt, int64_t T, int d, const void* o1, const float* lse1, const void* pin,
-                           const void* vprev2, const void* vprev, void* pout, int pout24, const float* w,
+                           const void* vprev2, const void* vprev, void* pout, int pfmt, const float* w,
                            const float* kg, const float* gamma, float eps, void* h_out, void* x_out,
                            hipStream_t stream) {
   // without a partial input the partial type is irrelevant: one instance
   if (!pin || pdt == kF32)
-    return pick_team<St, float>(T, d, o1, lse1, pin, vprev2, vprev, pout, pout24, w, kg, gamma, eps, h_out, x_out,
+    return pick_team<St, float>(T, d, o1, lse1, pin, vprev2, vprev, pout, pfmt, w, kg, gamma, eps, h_out, x_out,
+                                stream);
+  if (pdt == kQ16)
+    return pick_team<St, q16_t>(T, d, o1, lse1, pin, vprev2, vprev, pout, pfmt, w, kg, gamma, eps, h_out, x_out,
                                 stream);
   if (pdt == kP24)
-    return pick_team<St, p24_t>(T, d, o1, lse1, pin, vprev2, vprev, pout, pout24, w, kg, gamma, eps, h_out, x_out,
+    return pick_team<St, p24_t>(T, d, o1, lse1, pin, vprev2, vprev, pout, pfmt, w, kg, gamma, eps, h_out, x_out,
                                 stream);
-  return pick_team<St, St>(T, d, o1, lse1, pin, vprev2, vprev, pout, pout24, w, kg, gamma, eps, h_out, x_out,
+  return pick_team<St, St>(T, d, o1, lse1, pin, vprev2, vprev, pout, pfmt, w, kg, gamma, eps, h_out, x_out,
                            stream);
 }
 
@@ -392,22 +428,20 @@ hipError_t launch_merge(Dtype dt, int64_t T, int d, const void* o1, const float*
                         const void* pin, const void* vprev2, const void* vprev, Dtype podt, void* pout,
                         const float* w, const float* kg, const float* gamma, float eps, void* h_out, void* x_out,
                         hipStream_t stream) {
-  const int pout24 = podt == kP24 ? 1 : 0;
+  const int pfmt = podt == kP24 ? kPoutP24 : podt == kQ16 ? kPoutQ16 : kPoutF32;
   if (dt == kBF16)
-    return pick_pin<bf16_t>(pdt, T, d, o1, lse1, pin, vprev2, vprev, pout, pout24, w, kg, gamma, eps, h_out, x_out,
+    return pick_pin<bf16_t>(pdt, T, d, o1, lse1, pin, vprev2, vprev, pout, pfmt, w, kg, gamma, eps, h_out, x_out,
                             stream);
-  return pick_pin<float>(pdt, T, d, o1, lse1, pin, vprev2, vprev, pout, pout24, w, kg, gamma, eps, h_out, x_out,
+  return pick_pin<float>(pdt, T, d, o1, lse1, pin, vprev2, vprev, pout, pfmt, w, kg, gamma, eps, h_out, x_out,
                          stream);
 }
 
 template <typename St, typename Pt, typename Ot>
 static hipError_t run_acc(int64_t T, int d, const void* pin, const void* v2, const void* v, void* out,
                           hipStream_t stream) {
-  const int64_t nchunks = T * (int64_t)(d >> 3);
-  const int64_t blocks = (nchunks + 255) / 256;
-  const int64_t cap = (int64_t)device_cu_count() * 16;
-  const dim3 grid((unsigned)(blocks < cap ? blocks : cap));
-  hipLaunchKernelGGL((k_accumulate<St, Pt, Ot>), grid, dim3(256), 0, stream, nchunks, static_cast<const Pt*>(pin),
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const dim3 grid((unsigned)(T < cap ? T : cap));
+  hipLaunchKernelGGL((k_accumulate<St, Pt, Ot>), grid, dim3(256), 0, stream, T, d, static_cast<const Pt*>(pin),
                      static_cast<const St*>(v2), static_cast<const St*>(v), static_cast<Ot*>(out));
   return hipGetLastError();
 }
@@ -416,6 +450,7 @@ template <typename St, typename Ot>
 static hipError_t acc_pin(Dtype pdt, int64_t T, int d, const void* pin, const void* v2, const void* v, void* out,
                           hipStream_t stream) {
   if (!pin || pdt == kF32) return run_acc<St, float, Ot>(T, d, pin, v2, v, out, stream);
+  if (pdt == kQ16) return run_acc<St, q16_t, Ot>(T, d, pin, v2, v, out, stream);
   if (pdt == kP24) return run_acc<St, p24_t, Ot>(T, d, pin, v2, v, out, stream);
   return run_acc<St, St, Ot>(T, d, pin, v2, v, out, stream);
 }

@@ -17,10 +17,12 @@ outputs ``o1 [S_max, T, d]`` with their ``lse/m [S_max, T]`` (fp32) and the
 phase-1 workspace (packed queries and softmax weights), the running
 intra-block partial sum ``partial``, and a small ring of PreNorm outputs
 ``x``.  The partial sum is never stored in bf16: a bf16 running sum over a
-24-sublayer block drifts by several percent of the row maximum.  It is kept in
-the 24-bit split format (P24, 3 bytes per element, relative step 2^-16) for
-bf16 rows and in fp32 for fp32 rows; block sums are rounded to the storage
-dtype once, when they are complete.  The partial is stored only at the even
+24-sublayer block drifts by several percent of the row maximum.  For bf16
+rows it is kept in the 16-bit fixed-point format with one power-of-two
+exponent per row (Q16: 2 bytes per element, every element to within 2^-15 of
+its row's largest magnitude; the 24-bit split format P24 remains selectable),
+and in fp32 for fp32 rows; block sums are rounded to the storage dtype once,
+when they are complete.  The partial is stored only at the even
 positions j = 2, 4, ... of a block: sublayer j + 1 reads it with v_j and
 writes nothing, sublayer j + 2 reads it with v_j and v_{j+1} and stores the
 next one, so the two latest sublayer outputs must stay valid.
@@ -151,13 +153,15 @@ class BlockAttnRes:
                 ws = max(ws, _lib.attnres_phase1_workspace_bytes(T, d, 1 + self.n_given + b, S))
         self.workspace = torch.empty((max(ws, 16) // 4,), dtype=torch.float32, device=dev)
         # running partial sum: P24 (24-bit split) for bf16 rows, fp32 for fp32 rows
-        self.partial_format = partial or ("p24" if dtype == torch.bfloat16 else "f32")
-        if self.partial_format == "p24":
+        self.partial_format = partial or ("q16" if dtype == torch.bfloat16 else "f32")
+        if self.partial_format == "q16":
+            self.partial = _lib.q16_partial(T, d, dev)
+        elif self.partial_format == "p24":
             self.partial = _lib.p24_partial(T, d, dev)
         elif self.partial_format == "f32":
             self.partial = torch.empty((T, d), dtype=torch.float32, device=dev)
         else:
-            raise ValueError("partial format must be 'p24' or 'f32'")
+            raise ValueError("partial format must be 'q16', 'p24' or 'f32'")
         if self.training:
             # per block: phase-1 outputs and statistics of every site, and the
             # partial sums stored at positions j = 2, 4, ..., S - 1 (slot j // 2 - 1)
@@ -171,6 +175,8 @@ class BlockAttnRes:
         self.lse_final = torch.empty((T,), dtype=torch.float32, device=dev)
 
     def _new_partial(self) -> torch.Tensor:
+        if self.partial_format == "q16":
+            return _lib.q16_partial(self.T, self.d, self.device)
         if self.partial_format == "p24":
             return _lib.p24_partial(self.T, self.d, self.device)
         return torch.empty((self.T, self.d), dtype=torch.float32, device=self.device)
@@ -196,6 +202,11 @@ class BlockAttnRes:
         sources; a one-query block with more merges its first site in phase 2)."""
         return self.fuse_first and (S > 1 or n_done <= _lib.ATTNRES_MAX_SOURCES_MULTI)
 
+    def _partial_bytes(self) -> int:
+        """Bytes of one stored partial sum (Q16: values and row exponents)."""
+        es = {"q16": 2, "p24": 3, "f32": 4}[self.partial_format]
+        return self.T * self.d * es + (self.T * 4 if self.partial_format == "q16" else 0)
+
     def _row(self, dt=None) -> int:
         return self.T * self.d * _esize(self.dtype if dt is None else dt)
 
@@ -203,7 +214,7 @@ class BlockAttnRes:
         """Algorithmic bytes of every launch of one pass, in launch order."""
         r = self._row()
         rr = self._row(self.rep_dtype)  # a block representation (fp32 in a bf16 training pass)
-        r32 = self.T * self.d * (3 if self.partial_format == "p24" else 4)
+        r32 = self._partial_bytes()
         stat = self.T * 4
         out: List[Launch] = []
         n_done = 1 + self.n_given
@@ -382,7 +393,7 @@ class BlockAttnRes:
         r = self._row()
         rr = self._row(self.rep_dtype)  # a block representation (fp32 in a bf16 training pass)
         r32 = self.T * self.d * 4
-        rp = self.T * self.d * (3 if self.partial_format == "p24" else 4)
+        rp = self._partial_bytes()
         stat = self.T * 4
         out: List[Launch] = []
         n_reps = 1 + self.n_given + len(self.block_sizes)
