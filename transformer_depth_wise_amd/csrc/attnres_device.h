@@ -100,10 +100,21 @@ __device__ __forceinline__ void st8(void* p, u32x2_t v) { *reinterpret_cast<u32x
 // load_at(base, off, plane): the 8 elements at element offset `off` of a
 // [T][d] buffer; `plane` = T*d is used by split formats only.
 template <typename T> struct Chunk;
+// Non-temporal 16- and 8-byte loads: for streams read once (or read again
+// only by a later kernel), so that they do not displace reusable lines.
+__device__ __forceinline__ u32x4_t ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ u32x2_t ld8_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
+
 template <> struct Chunk<bf16_t> {
   u32x4_t r;
   __device__ __forceinline__ void load(const bf16_t* p) { r = ld16(p); }
+  __device__ __forceinline__ void load_nt(const bf16_t* p) { r = ld16_nt(p); }
   __device__ __forceinline__ void load_at(const bf16_t* b, int64_t off, int64_t) { r = ld16(b + off); }
+  __device__ __forceinline__ void load_at_nt(const bf16_t* b, int64_t off, int64_t) { r = ld16_nt(b + off); }
   __device__ __forceinline__ void zero() { r = u32x4_t{0u, 0u, 0u, 0u}; }
   __device__ __forceinline__ void unpack(float (&v)[8]) const {
     unpack_bf16x8(make_uint4(r.x, r.y, r.z, r.w), v);
@@ -112,7 +123,9 @@ template <> struct Chunk<bf16_t> {
 template <> struct Chunk<float> {
   u32x4_t a, b;
   __device__ __forceinline__ void load(const float* p) { a = ld16(p); b = ld16(p + 4); }
+  __device__ __forceinline__ void load_nt(const float* p) { a = ld16_nt(p); b = ld16_nt(p + 4); }
   __device__ __forceinline__ void load_at(const float* p, int64_t off, int64_t) { load(p + off); }
+  __device__ __forceinline__ void load_at_nt(const float* p, int64_t off, int64_t) { load_nt(p + off); }
   __device__ __forceinline__ void zero() { a = u32x4_t{0u, 0u, 0u, 0u}; b = a; }
   __device__ __forceinline__ void unpack(float (&v)[8]) const {
     v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
@@ -126,6 +139,11 @@ template <> struct Chunk<p24_t> {
     const unsigned char* base = reinterpret_cast<const unsigned char*>(b);
     hi = ld16(base + off * 2);
     lo = ld8(base + plane * 2 + off);
+  }
+  __device__ __forceinline__ void load_at_nt(const p24_t* b, int64_t off, int64_t plane) {
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(b);
+    hi = ld16_nt(base + off * 2);
+    lo = ld8_nt(base + plane * 2 + off);
   }
   __device__ __forceinline__ void zero() {
     hi = u32x4_t{0u, 0u, 0u, 0u};
@@ -146,6 +164,7 @@ template <> struct Chunk<p24_t> {
 template <> struct Chunk<q16_t> {
   u32x4_t r;  // 8 int16 values
   __device__ __forceinline__ void load_at(const q16_t* b, int64_t off, int64_t) { r = ld16(b + off); }
+  __device__ __forceinline__ void load_at_nt(const q16_t* b, int64_t off, int64_t) { r = ld16_nt(b + off); }
   __device__ __forceinline__ void zero() { r = u32x4_t{0u, 0u, 0u, 0u}; }
   // the values times 2^(e - 15)
   __device__ __forceinline__ void unpack(float (&v)[8], int e) const {
@@ -225,6 +244,23 @@ __device__ __forceinline__ void out24(p24_t* b, int64_t off, int64_t plane, cons
 // they do not displace reusable lines from the caches.
 __device__ __forceinline__ void st16_nt(void* p, u32x4_t v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void st8_nt(void* p, u32x2_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
+}
+// out24 with non-temporal stores
+__device__ __forceinline__ void out24_nt(p24_t* b, int64_t off, int64_t plane, const float (&v)[8]) {
+  unsigned r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = round24(v[e]);
+  unsigned char* base = reinterpret_cast<unsigned char*>(b);
+  st16_nt(base + off * 2, u32x4_t{(r[0] >> 16) | (r[1] & 0xffff0000u), (r[2] >> 16) | (r[3] & 0xffff0000u),
+                                  (r[4] >> 16) | (r[5] & 0xffff0000u), (r[6] >> 16) | (r[7] & 0xffff0000u)});
+  st8_nt(base + plane * 2 + off,
+         u32x2_t{((r[0] >> 8) & 0xffu) | (((r[1] >> 8) & 0xffu) << 8) | (((r[2] >> 8) & 0xffu) << 16) |
+                     (((r[3] >> 8) & 0xffu) << 24),
+                 ((r[4] >> 8) & 0xffu) | (((r[5] >> 8) & 0xffu) << 8) | (((r[6] >> 8) & 0xffu) << 16) |
+                     (((r[7] >> 8) & 0xffu) << 24)});
 }
 __device__ __forceinline__ void out8_nt(bf16_t* p, const float (&v)[8]) {
   st16_nt(p, u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});

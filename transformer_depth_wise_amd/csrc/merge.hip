@@ -23,7 +23,11 @@
 // two workgroups per CU walks over the tokens; the raw rows of the team's next
 // token are loaded before the current token is reduced, merged and stored, so
 // HBM traffic continues through the reductions and barriers (the loop is
-// unrolled twice over two register stages).
+// unrolled twice over two register stages).  Every row load and store is
+// non-temporal: each row is used once per launch, and what a later launch
+// reads again is far larger than the caches (with non-temporal loads and
+// stores phase 2 of the 16K-token chunk took 37.4 ms instead of 40.0 on one
+// MI355X, measured in one run).
 #include "attnres_device.h"
 #include "attnres_launch.h"
 
@@ -57,10 +61,10 @@ __device__ __forceinline__ void issue(Stage<St, Pt, CPL>& s, int64_t tok, int64_
     s.ok[k] = live && c0 < C;
     const int c = c0 < C ? c0 : C - 1;
     const int64_t off = tc * d + c * 8;
-    s.o[k].load(o1 + off);
-    if (HAS_V) s.v[k].load(vprev + off);
-    if (HAS_V2) s.v2[k].load(vprev2 + off);
-    if (HAS_PIN) s.q[k].load_at(pin, off, plane);
+    s.o[k].load_nt(o1 + off);
+    if (HAS_V) s.v[k].load_nt(vprev + off);
+    if (HAS_V2) s.v2[k].load_nt(vprev2 + off);
+    if (HAS_PIN) s.q[k].load_at_nt(pin, off, plane);
   }
 }
 
@@ -112,9 +116,9 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
       if (pout && !q16 && s.ok[k]) {
         const int64_t off = tok * d + c * 8;
         if (pfmt == kPoutP24) {
-          out24(static_cast<p24_t*>(pout), off, plane, p[k]);
+          out24_nt(static_cast<p24_t*>(pout), off, plane, p[k]);
         } else {
-          out8(static_cast<float*>(pout) + off, p[k]);
+          out8_nt(static_cast<float*>(pout) + off, p[k]);
         }
       }
 #pragma unroll
@@ -144,7 +148,7 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
       unsigned char* pb = static_cast<unsigned char*>(pout);
 #pragma unroll
       for (int k = 0; k < CPL; ++k)
-        if (s.ok[k]) st16(pb + (tok * d + (tl + TEAM * k) * 8) * 2, q16_pack(p[k], e));
+        if (s.ok[k]) st16_nt(pb + (tok * d + (tl + TEAM * k) * 8) * 2, q16_pack(p[k], e));
       if (live && tl == 0) *reinterpret_cast<int*>(pb + plane * 2 + tok * 4) = e;
     } else if (TEAM == 256) {
       r = block_sum2_256(ss, dot, red[parity]);
@@ -180,14 +184,14 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
   for (int k = 0; k < CPL; ++k) {
     if (s.ok[k]) {
       const int64_t off = tok * d + (tl + TEAM * k) * 8;
-      if (h_out) out8(h_out + off, h[k]);
+      if (h_out) out8_nt(h_out + off, h[k]);
       if (x_out) {
         const float4 g0 = gm_lds[2 * (tl + TEAM * k)], g1 = gm_lds[2 * (tl + TEAM * k) + 1];
         const float gk[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = gk[e] * (h[k][e] * rinv);
-        out8(x_out + off, x);
+        out8_nt(x_out + off, x);
       }
     }
   }
@@ -342,13 +346,9 @@ static hipError_t run_merge(int64_t T, int d, const void* o1, const float* lse1,
                             hipStream_t stream) {
   constexpr int TPW = 256 / TEAM;
   const int64_t tiles = (T + TPW - 1) / TPW;
-  // persistent: 2 workgroups per CU; 1 for the launches that read two
-  // previous outputs and store the partial, over long token ranges (two
-  // write streams besides four read streams: fewer concurrent streams kept
-  // HBM at 5.4 instead of 5.1 TB/s at 16K tokens, while the lighter launches,
-  // and every launch at 2K tokens, were faster with 2)
-  const int64_t cus = device_cu_count();
-  const int64_t cap = cus * ((vprev2 && T >= 32 * cus) ? 1 : 2);
+  // persistent: 2 workgroups per CU (with non-temporal accesses every
+  // instance was fastest so; 1 per CU cost 7%)
+  const int64_t cap = (int64_t)device_cu_count() * 2;
   const dim3 grid((unsigned)(tiles < cap ? tiles : cap));
   const size_t lds = x_out ? sizeof(float) * (size_t)d : 0;  // PreNorm gain (at most 64 KiB)
   const St* o = static_cast<const St*>(o1);
