@@ -1235,17 +1235,20 @@ __global__ __launch_bounds__(256) void k_site_online(const St* __restrict__ src,
 // 2 x BS partial sums (w (.) g).u and |u|^2 are added over the workgroup in
 // one fixed-order reduction (DPP wave sums, then the 8 waves in index order
 // through LDS; two buffers alternate, so one barrier per reduction).  The
-// next (token, batch) item's loads are in flight meanwhile.
+// next DEPTH - 1 (token, batch) items' loads are in flight meanwhile; the
+// rows are read once, with non-temporal loads.  One source per batch, two
+// stages and four workgroups per CU took the 16K chunk's final site (9
+// sources, d = 7168) from 0.63 to 0.49 ms on an MI355X; batches of 3 or 4
+// sources, or 3 to 6 stages, were slower in the same run.
 constexpr int kTeam = 512;
 
-template <typename St, int CPT>
+template <typename St, int CPT, int BS, int DEPTH>
 __global__ __launch_bounds__(kTeam) void k_site_team(const St* __restrict__ src, int n, int64_t stride, int64_t T,
                                                      int d, const float* __restrict__ w,
                                                      const float* __restrict__ kg,
                                                      const float* __restrict__ gamma, float eps,
                                                      St* __restrict__ h_out, St* __restrict__ x_out,
                                                      float* __restrict__ m_out, float* __restrict__ lse_out) {
-  constexpr int BS = (sizeof(St) == 2 ? 4 : 2) / (CPT > 2 ? 2 : 1);  // sources per batch (registers)
   constexpr int NW = kTeam / 64;
   __shared__ float red[2][NW][2 * BS];
   const int lane = threadIdx.x & 63;
@@ -1309,7 +1312,7 @@ __global__ __launch_bounds__(kTeam) void k_site_team(const St* __restrict__ src,
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
         const int c0 = threadIdx.x + kTeam * k;
-        u[j][k].load(src + (int64_t)i * stride + tok * d + (c0 < C ? c0 : C - 1) * 8);
+        u[j][k].load_nt(src + (int64_t)i * stride + tok * d + (c0 < C ? c0 : C - 1) * 8);
       }
     }
   };
@@ -1409,20 +1412,24 @@ __global__ __launch_bounds__(kTeam) void k_site_team(const St* __restrict__ src,
       }
     }
   };
-  Chunk<St> A[BS][CPT], B[BS][CPT];
-  issue(A, 0);
+  // a ring of DEPTH stages: DEPTH - 1 (token, batch) items in flight while
+  // the oldest is used
+  Chunk<St> ring[DEPTH][BS][CPT];
+#pragma unroll
+  for (int s = 0; s < DEPTH - 1; ++s) issue(ring[s], s);
   int64_t it = 0;
-  for (; it + 2 <= items; it += 2) {
-    issue(B, it + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    consume(A, it);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(A, it + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    consume(B, it + 1);
-    __builtin_amdgcn_sched_barrier(0);
+  for (; it + DEPTH <= items; it += DEPTH) {
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) {
+      issue(ring[(s + DEPTH - 1) % DEPTH], it + s + DEPTH - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(ring[s], it + s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if (it < items) consume(A, it);
+#pragma unroll
+  for (int s = 0; s < DEPTH - 1; ++s)  // tail: every stage is already loaded
+    if (it + s < items) consume(ring[s], it + s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1598,9 +1605,9 @@ static hipError_t run_single(const void* src, int n, int64_t stride, int64_t T, 
   }
   if (C <= 4 * kTeam) {
     // the same one pass, a 512-thread workgroup per token
-    auto k = C <= 2 * kTeam ? k_site_team<St, 2> : k_site_team<St, 4>;
+    auto k = C <= 2 * kTeam ? k_site_team<St, 2, 1, 2> : k_site_team<St, 4, 1, 2>;
     int64_t wgs = T;
-    const int64_t cap = (int64_t)device_cu_count() * 2;
+    const int64_t cap = (int64_t)device_cu_count() * 4;
     if (wgs > cap) wgs = cap;
     hipLaunchKernelGGL(k, dim3((unsigned)wgs), dim3(kTeam), 0, stream, static_cast<const St*>(src), n, stride, T, d,
                        w, kg, gamma, eps, static_cast<St*>(h_out), static_cast<St*>(x_out), m_out, lse_out);
