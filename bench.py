@@ -408,6 +408,24 @@ def other_workloads(dev, steps: int):
                                  "bytes_per_step": b}
     res[w.name + "_backward"] = full_backward_report(fulls, prm, steps)
     del fulls, grouped
+    torch.cuda.empty_cache()
+
+    # a larger Full AttnRes shape, where the bytes rather than the launches
+    # decide: one-shot sites re-read every earlier output (152 rows per token
+    # at depth 16), the grouped schedule reads each completed source once per
+    # group (groups of 4: 107 rows)
+    wl = synth.scaled(w, name="full_bf16_T16384_d4096", T=16384, d=4096)
+    fl, prm = full_states(wl, dev, 1)
+    gl = tdw.FullAttnRes(wl.T, wl.d, wl.L, wl.torch_dtype, eps=wl.eps, device=dev, final_site=wl.final_site, group=4)
+    gl.hist = fl[0].hist
+    for name, st in (("one_shot", fl[0]), ("grouped4", gl)):
+        st.forward(prm, noop)
+        sec = _time(lambda k: st.forward(prm, noop), max(steps // 2, 10))
+        b = sum(x.bytes for x in st.plan())
+        res.setdefault(wl.name, {"config": {"T": wl.T, "d": wl.d, "sublayers": wl.L}})[name] = {
+            "ms_per_step": round(sec * 1e3, 4), "value": round(wl.T * wl.L / sec, 1), "unit": "token-sublayers/s",
+            "hbm_gbps": round(b / sec / 1e9, 1), "bytes_per_step": b, "launches_per_step": len(st.plan())}
+    del fl, gl
 
     # backward of one aggregation site at the 16K chunk's final-site shape
     # (9 sources), with and without the PreNorm
