@@ -429,8 +429,10 @@ attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t
  * workgroups_per_cu 256-thread workgroups per compute unit in a grid-stride
  * loop, `unroll` chunks of each stream in flight per thread (1, 2, 4 or 8),
  * and non-temporal loads and stores when `nontemporal` is nonzero.
- *   0 <= n_read <= 4, 0 <= n_write <= 2, not both zero; 1 <=
- *   workgroups_per_cu <= 16; stream_bytes a
+ *   0 <= n_read <= 4, 0 <= n_write <= 2, not both zero, or one of the
+ *   many-stream mixes (n_read, n_write) = (8, 0) (the scoring pass over a
+ *   block's sources) and (9, 1) (the final aggregation: nine sources, one
+ *   output); 1 <= workgroups_per_cu <= 16; stream_bytes a
  *   positive multiple of 16 (at most 2^40).  With n_write == 0, dst must
  *   still point at 16 writable bytes (kept as the loads' sink; not written
  *   for any data these probes read).  The read and written ranges must not

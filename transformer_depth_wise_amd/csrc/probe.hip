@@ -100,6 +100,8 @@ hipError_t launch_stream_probe(int n_read, int n_write, const void* src, void* d
   ATTNRES_PROBE(2, 2);
   ATTNRES_PROBE(3, 2);
   ATTNRES_PROBE(4, 2);
+  ATTNRES_PROBE(8, 0);
+  ATTNRES_PROBE(9, 1);
 #undef ATTNRES_PROBE
   return hipErrorInvalidValue;
 }
