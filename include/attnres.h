@@ -185,6 +185,43 @@ attnres_status_t attnres_phase1_first_prenorm(attnres_dtype_t dt,
                                               const float* prenorm_gain, void* x_out, void* h_out,
                                               void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * Phase 1 of a block whose newest source, the previous block's sum, is
+ * formed in the same call ("Attention Residuals" notes, section 8: b_n is the
+ * sum of block n's sublayer outputs; "Attention Residuals 阅读补充", "如何解
+ * 释小于 2% 的延迟": the small overhead rests on fusing such operators).
+ * First
+ *     u_{n_src-1} = ((partial_in or 0) + (sublayer_prev2 or 0)) + sublayer_prev,
+ * summed in fp32 in that order and stored to source slab n_src-1 as src_dt --
+ * the same values attnres_block_accumulate(sublayer_dt, T, d, partial_dt,
+ * partial_in, sublayer_prev2, sublayer_prev, that slab, src_dt) stores -- then
+ * everything attnres_phase1_first_prenorm does (x_out != NULL; src_dt must
+ * equal dt) or attnres_phase1 does (x_out == NULL; prenorm_gain and h_out
+ * must be NULL too), bit for bit, reading sources 0..n_src-2 from src.
+ *   src: the n_src source slabs as for attnres_phase1; slab n_src-1 is
+ *   written (its previous contents are not read).
+ *   partial_in (format partial_dt, NULL = none), sublayer_prev2 (NULL =
+ *   none), sublayer_prev (required): [T][d] pieces, the outputs of dtype
+ *   sublayer_dt, as for attnres_block_accumulate; src_dt is sublayer_dt, or
+ *   ATTNRES_F32 with bf16 outputs (exact block sums).  dt and src_dt pair as
+ *   for attnres_phase1 (a training forward's final site: fp32 sources and
+ *   outputs, bf16 pieces).
+ * Over long token ranges (at least 64 tokens per compute unit) with a
+ * partial_in in ATTNRES_Q16 or ATTNRES_F32 the sum is formed inside the
+ * scoring pass, which reads the pieces instead of the slab and writes the
+ * slab once; otherwise the call runs the block-sum kernel first.
+ * Limits and workspace as the call it stands for, with 2 <= n_src.  No piece
+ * may overlap slab n_src-1 or any output; the outputs follow the rules of
+ * attnres_phase1 / attnres_phase1_first_prenorm against all of src.
+ */
+attnres_status_t attnres_phase1_accumulate(attnres_dtype_t dt, attnres_dtype_t src_dt, void* src, int64_t n_src,
+                                           int64_t src_stride, int64_t T, int64_t d, const float* w,
+                                           const float* key_gain, int64_t S, float eps, attnres_dtype_t partial_dt,
+                                           const void* partial_in, attnres_dtype_t sublayer_dt,
+                                           const void* sublayer_prev2, const void* sublayer_prev, void* out,
+                                           float* m_out, float* lse_out, const float* prenorm_gain, void* x_out,
+                                           void* h_out, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Workspace bytes attnres_phase1 uses: 16384 * ceil(d / 128) (packed
  * queries) + T * n_src * min(S, 32) * 4 (softmax weights); 0 for S == 1 with
  * more than ATTNRES_MAX_SOURCES_MULTI sources; -1 for invalid sizes. */

@@ -36,6 +36,7 @@ def declared_functions():
 def test_header_declares_every_entry_point():
     names = declared_functions()
     for n in ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_workspace_bytes", "attnres_phase2_merge",
+              "attnres_phase1_accumulate",
               "attnres_phase2_backward", "attnres_phase1_backward",
               "attnres_phase2_merge_multi", "attnres_full", "attnres_block_accumulate", "attnres_status_string"):
         assert n in names
@@ -147,6 +148,46 @@ def test_phase1_first_prenorm_validation(lib):
     assert first_prenorm(lib, dt=9) == EDTYPE
     assert first_prenorm(lib, T=0) == 0
     assert first_prenorm(lib, T=0, x=None) == EINVAL
+
+
+def p1acc(lib, dt=1, sdt=None, vdt=None, src=A, n=3, stride=4096 * 64, T=4096, d=64, w=8 * A, kg=None, S=4, pdt=3,
+          pin=54 * A, v2=52 * A, v=50 * A, out=16 * A, m=None, lse=24 * A, gm=None, x=None, h=None, ws=32 * A,
+          ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attnres_phase1_workspace_bytes(T, d, n, S)
+    sdt = dt if sdt is None else sdt
+    vdt = dt if vdt is None else vdt
+    return checked(lib.attnres_phase1_accumulate(dt, sdt, p(src), n, stride, T, d, p(w), p(kg), S, 1e-6, pdt, p(pin),
+                                                 vdt, p(v2), p(v), p(out), p(m), p(lse), p(gm), p(x), p(h), p(ws),
+                                                 ws_bytes, None))
+
+
+def test_phase1_accumulate_validation(lib):
+    slab2 = A + 2 * 4096 * 64 * 2                      # byte address of source slab n-1 = 2
+    assert p1acc(lib, n=1) == EINVAL                   # the newest source is a block sum: n_src >= 2
+    assert p1acc(lib, n=17) == EINVAL
+    assert p1acc(lib, v=None) == EINVAL                # the block's last output is required
+    assert p1acc(lib, pdt=9) == EDTYPE
+    assert p1acc(lib, dt=0, pdt=0, sdt=1) == EDTYPE    # bf16 sources, fp32 outputs
+    assert p1acc(lib, vdt=0, pdt=0) == EDTYPE          # fp32 pieces summed into bf16 sources
+    assert p1acc(lib, vdt=9) == EDTYPE
+    assert p1acc(lib, dt=0, sdt=0, vdt=1, pdt=3, T=0) == 0   # fp32 sources and outputs, bf16 pieces
+    assert p1acc(lib, sdt=0, x=40 * A) == EINVAL       # the PreNorm of query 0 needs equal types
+    assert p1acc(lib, gm=48 * A) == EINVAL             # a PreNorm gain without x_out
+    assert p1acc(lib, h=44 * A) == EINVAL              # h_out without x_out
+    assert p1acc(lib, v=slab2) == EALIAS               # a piece over the slab being written
+    assert p1acc(lib, pin=slab2 + 4096) == EALIAS
+    assert p1acc(lib, v2=16 * A + 64) == EALIAS        # a piece inside an output
+    assert p1acc(lib, pin=24 * A) == EALIAS            # ... inside the statistics
+    assert p1acc(lib, v=50 * A + 2) == EALIGN
+    assert p1acc(lib, out=slab2) == EALIAS             # an output over the sources (as attnres_phase1)
+    assert p1acc(lib, x=40 * A, out=None) == EINVAL    # as attnres_phase1_first_prenorm
+    assert p1acc(lib, ws=None) == EINVAL
+    assert p1acc(lib, d=12) == EALIGN
+    assert p1acc(lib, S=0) == EINVAL
+    assert p1acc(lib, T=1 << 31) == EINVAL
+    assert p1acc(lib, T=0) == 0
+    assert p1acc(lib, T=0, v=None, src=None) == 0
 
 
 def p2b(lib, dt=1, T=1024, d=64, o=A, lse=2 * A, pdt=0, pin=None, v2=None, v=3 * A, w=4 * A, kg=None, gm=None,

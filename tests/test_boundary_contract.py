@@ -80,3 +80,15 @@ def test_stream_is_an_opaque_pointer():
         if name != "attnres_status_string":
             m = re.search(r"\b%s\s*\(([^;{]*)\)\s*;" % name, text, re.S)
             assert re.search(r"void\s*\*\s*stream\s*$", m.group(1).strip()), name
+
+
+def test_phase1_accumulate_is_phase1_plus_the_block_sum():
+    # the fused call takes the phase-1 call's specified arguments and the
+    # block sum's pieces (its `v` is the block's last output, sublayer_prev)
+    params = header_params("attnres_phase1_accumulate")
+    for a in SPECIFIED["attnres_phase1"]:
+        assert a in params, a
+    for a in ("partial_in", "sublayer_prev"):
+        assert a in params, a
+    pos = [params.index(a) for a in SPECIFIED["attnres_phase1"]]
+    assert pos == sorted(pos), "the phase-1 arguments keep their order"

@@ -30,10 +30,18 @@ def test_block_plan_bytes_per_token_sublayer():
     p24 = tdw.BlockAttnRes(16, 7168, K3, BF, device="cpu", partial="p24")
     assert abs(rows_per_token_sublayer(p24.plan(), 16, 7168, 186) - 6.638) < 5e-4
     kinds = [x.kind for x in plan]
-    assert kinds.count("phase1") == 8 and kinds.count("accumulate") == 8 and kinds.count("final") == 1
+    # every block's sum is formed by the next phase-1 call, the last one by the final site's
+    assert kinds.count("phase1") == 8 and kinds.count("accumulate") == 0 and kinds.count("final") == 1
     assert kinds.count("phase2") == 186 - 8     # the first sublayer of each block leaves phase 1
     twice = tdw.BlockAttnRes(32, 7168, K3, BF, device="cpu").plan()
     assert sum(x.bytes for x in twice) == 2 * sum(x.bytes for x in plan)
+    # the same bytes with a block-sum launch per block; without a final site
+    # the last block's sum still needs one
+    sep = tdw.BlockAttnRes(16, 7168, K3, BF, device="cpu", fuse_sum=False).plan()
+    assert [x.kind for x in sep].count("accumulate") == 8
+    assert sum(x.bytes for x in sep) == sum(x.bytes for x in plan)
+    nofinal = [x.kind for x in tdw.BlockAttnRes(16, 7168, K3, BF, device="cpu", final_site=False).plan()]
+    assert nofinal.count("accumulate") == 1 and nofinal[-1] == "accumulate" and "final" not in nofinal
 
 
 def test_block_plan_survey_rows():
@@ -47,6 +55,9 @@ def test_block_plan_survey_rows():
     assert sum(x.bytes for x in sv) == 1146 * r
     assert sum(x.bytes for x in sv if x.kind == "phase2") == 874 * r
     assert [x.kind for x in sv] == [x.kind for x in st.plan()]   # the same launches
+    sep = tdw.BlockAttnRes(T, d, K3, BF, device="cpu", fuse_sum=False)
+    assert [x.kind for x in sep.plan_survey()] == [x.kind for x in sep.plan()]
+    assert sum(x.bytes for x in sep.plan_survey()) == 1146 * r
     unfused = tdw.BlockAttnRes(T, d, K3, BF, device="cpu", fuse_first=False).plan_survey()
     assert sum(x.bytes for x in unfused) == 1146 * r
     assert sum(x.bytes for x in unfused if x.kind == "phase2") == 890 * r

@@ -30,7 +30,8 @@ EXPORTED = ("attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase1_wo
             "attnres_phase2_merge", "attnres_phase2_merge_multi", "attnres_full", "attnres_block_accumulate",
             "attnres_site_backward", "attnres_site_backward_accumulate", "attnres_site_backward_workspace_bytes",
             "attnres_phase2_backward", "attnres_phase2_backward_workspace_bytes", "attnres_phase1_backward",
-            "attnres_phase1_backward_workspace_bytes", "attnres_stream_probe", "attnres_phase1_noalloc", "attnres_status_string")
+            "attnres_phase1_backward_workspace_bytes", "attnres_stream_probe", "attnres_phase1_noalloc",
+            "attnres_phase1_accumulate", "attnres_status_string")
 
 
 class AttnResError(RuntimeError):
@@ -55,6 +56,8 @@ def load(path: Optional[str] = None):
     V, I, F, E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
     lib.attnres_phase1.argtypes = [E, E, V, I, I, I, I, V, V, I, F, V, V, V, V, I, V]
     lib.attnres_phase1_first_prenorm.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V, V, V, V, I, V]
+    lib.attnres_phase1_accumulate.argtypes = [E, E, V, I, I, I, I, V, V, I, F, E, V, E, V, V, V, V, V, V, V, V, V,
+                                              I, V]
     lib.attnres_phase1_workspace_bytes.argtypes = [I, I, I, I]
     lib.attnres_phase1_workspace_bytes.restype = ctypes.c_int64
     lib.attnres_phase2_merge.argtypes = [E, I, I, V, V, E, V, V, V, E, V, V, V, V, F, V, V, V]
@@ -74,7 +77,8 @@ def load(path: Optional[str] = None):
     lib.attnres_phase1_backward_workspace_bytes.restype = ctypes.c_int64
     lib.attnres_stream_probe.argtypes = [I, I, V, V, I, I, I, I, V]
     lib.attnres_phase1_noalloc.argtypes = [E, V, I, I, I, I, V, V, I, F, V, V, V, V]
-    for fn in ("attnres_phase1_noalloc", "attnres_stream_probe", "attnres_phase1", "attnres_phase1_first_prenorm", "attnres_phase2_merge", "attnres_phase2_merge_multi",
+    for fn in ("attnres_phase1_noalloc", "attnres_stream_probe", "attnres_phase1", "attnres_phase1_first_prenorm",
+               "attnres_phase1_accumulate", "attnres_phase2_merge", "attnres_phase2_merge_multi",
                "attnres_full", "attnres_block_accumulate", "attnres_site_backward",
                "attnres_site_backward_accumulate", "attnres_phase2_backward", "attnres_phase1_backward"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -346,6 +350,43 @@ def attnres_phase1_first_prenorm(src: torch.Tensor, n_src: int, w: torch.Tensor,
                                              _ptr(lse_out), _ptr(prenorm_gain), _ptr(x_out), _ptr(h_out),
                                              _ptr(workspace), _workspace(workspace), _stream(stream))
     _check("attnres_phase1_first_prenorm", rc)
+
+
+def attnres_phase1_accumulate(src: torch.Tensor, n_src: int, w: torch.Tensor, key_gain: Optional[torch.Tensor],
+                              eps: float, partial_in: Optional[torch.Tensor], v2: Optional[torch.Tensor],
+                              v: torch.Tensor, out: Optional[torch.Tensor], m_out: Optional[torch.Tensor],
+                              lse_out: torch.Tensor, prenorm_gain: Optional[torch.Tensor] = None,
+                              x_out: Optional[torch.Tensor] = None, h_out: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None, stream=None, check: bool = True) -> None:
+    """attnres_phase1 (x_out None) or attnres_phase1_first_prenorm (x_out
+    given) whose newest source src[n_src - 1] is first formed as
+    (partial_in or 0) + (v2 or 0) + v and written there: v, v2 [T, d] sublayer
+    outputs, partial_in a running partial (fp32, Q16 or P24 buffer, or v's
+    dtype).  The outputs' dtype is out's (else the sources')."""
+    if v is None or v.dim() != 2:
+        raise ValueError("v must be a [T, d] tensor")
+    odt = out.dtype if out is not None else src.dtype
+    if check:
+        _phase1_args(src, n_src, w, key_gain, out, m_out, lse_out)
+        T, d = lse_out.shape[1], src.shape[-1]
+        vdt = _storage(v, "v")
+        _rows(v, "v", T, d, vdt)
+        _rows(v2, "v2", T, d, vdt, optional=True)
+        _partial(partial_in, "partial_in", T, d, vdt)
+        _fp32(prenorm_gain, "prenorm_gain", (d,))
+        _rows(x_out, "x_out", T, d, odt, optional=True)
+        _rows(h_out, "h_out", T, d, odt, optional=True)
+        _workspace(workspace)
+        _on_device(src, w, key_gain, partial_in, v2, v, out, m_out, lse_out, prenorm_gain, x_out, h_out, workspace)
+    S, T = lse_out.shape
+    d = src.shape[-1]
+    rc = load().attnres_phase1_accumulate(dtype_code(odt), dtype_code(src.dtype), _ptr(src), n_src,
+                                          _slab_stride(src, T, d), T, d, _ptr(w), _ptr(key_gain), S, eps,
+                                          _fmt(partial_in), _ptr(partial_in), dtype_code(v.dtype), _ptr(v2), _ptr(v),
+                                          _ptr(out),
+                                          _ptr(m_out), _ptr(lse_out), _ptr(prenorm_gain), _ptr(x_out), _ptr(h_out),
+                                          _ptr(workspace), _workspace(workspace), _stream(stream))
+    _check("attnres_phase1_accumulate", rc)
 
 
 def attnres_phase2_merge(p1_out: torch.Tensor, p1_lse: torch.Tensor, partial_in: Optional[torch.Tensor],

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/attnres.h"
@@ -123,11 +124,13 @@ int64_t attnres_phase1_workspace_bytes(int64_t T, int64_t d, int64_t n_src, int6
 }
 
 // Shared by attnres_phase1 and attnres_phase1_first_prenorm (x0 != null).
+// With nw != null (attnres_phase1_accumulate, validated there), source
+// n_src-1 is first formed from the pieces of a block sum.
 static attnres_status_t phase1_impl(attnres_dtype_t dt, attnres_dtype_t src_dt, const void* src, int64_t n_src,
                                     int64_t src_stride, int64_t T, int64_t d, const float* w,
                                     const float* key_gain, int64_t S, float eps, void* out, float* m_out,
                                     float* lse_out, const float* gamma0, void* x0, void* h0, void* workspace,
-                                    int64_t workspace_bytes, void* stream) {
+                                    int64_t workspace_bytes, void* stream, const attnres::Newest* nw = nullptr) {
   if (!dtype_ok(dt) || !dtype_ok(src_dt)) return ATTNRES_EDTYPE;
   // sources of the outputs' type, or fp32 sources with bf16 outputs
   const bool mixed = src_dt != dt;
@@ -174,9 +177,16 @@ static attnres_status_t phase1_impl(attnres_dtype_t dt, attnres_dtype_t src_dt, 
 
   const Dtype kdt = kind_of(dt);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (S == 1 && ws_need == 0)
+  if (S == 1 && ws_need == 0) {
+    if (nw) {
+      void* newest = static_cast<char*>(const_cast<void*>(src)) + (n_src - 1) * src_stride * esize(src_dt);
+      if (attnres::launch_accumulate(nw->vdt, kind_of(src_dt), T, (int)d, nw->pdt, nw->pin, nw->v2, nw->v, newest, s) !=
+          hipSuccess)
+        return ATTNRES_EHIP;
+    }
     return hip_status(attnres::launch_phase1_single(kdt, src, (int)n_src, src_stride, T, (int)d, w, key_gain,
                                                     nullptr, eps, out, nullptr, m_out, lse_out, s));
+  }
   for (int64_t s0 = 0; s0 < S; s0 += 32) {
     const int64_t sn = (S - s0) < 32 ? (S - s0) : 32;
     char* o = out ? static_cast<char*>(out) + s0 * T * d * es : nullptr;
@@ -185,7 +195,7 @@ static attnres_status_t phase1_impl(attnres_dtype_t dt, attnres_dtype_t src_dt, 
                                                 key_gain ? key_gain + s0 * d : nullptr, (int)sn, eps, o,
                                                 m_out ? m_out + s0 * T : nullptr, lse_out + s0 * T, gamma0,
                                                 s0 == 0 ? x0 : nullptr, s0 == 0 ? h0 : nullptr,
-                                                static_cast<float*>(workspace), s);
+                                                static_cast<float*>(workspace), s0 == 0 ? nw : nullptr, s);
     if (e != hipSuccess) return ATTNRES_EHIP;
   }
   return ATTNRES_OK;
@@ -251,6 +261,55 @@ attnres_status_t attnres_phase1_first_prenorm(attnres_dtype_t dt, const void* sr
   if (!x_out) return ATTNRES_EINVAL;
   return phase1_impl(dt, dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out, prenorm_gain,
                      x_out, h_out, workspace, workspace_bytes, stream);
+}
+
+attnres_status_t attnres_phase1_accumulate(attnres_dtype_t dt, attnres_dtype_t src_dt, void* src, int64_t n_src,
+                                           int64_t src_stride, int64_t T, int64_t d, const float* w,
+                                           const float* key_gain, int64_t S, float eps, attnres_dtype_t partial_dt,
+                                           const void* partial_in, attnres_dtype_t sublayer_dt,
+                                           const void* sublayer_prev2, const void* sublayer_prev, void* out,
+                                           float* m_out, float* lse_out, const float* prenorm_gain, void* x_out,
+                                           void* h_out, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dt) || !dtype_ok(src_dt) || !dtype_ok(sublayer_dt) || !partial_ok(partial_dt, sublayer_dt))
+    return ATTNRES_EDTYPE;
+  // the phase-1 pair, and the block sum's (pieces of sublayer_dt stored as src_dt)
+  if (src_dt != dt && !(src_dt == ATTNRES_F32 && dt == ATTNRES_BF16)) return ATTNRES_EDTYPE;
+  if (src_dt != sublayer_dt && !(src_dt == ATTNRES_F32 && sublayer_dt == ATTNRES_BF16)) return ATTNRES_EDTYPE;
+  if (x_out && src_dt != dt) return ATTNRES_EINVAL;  // as attnres_phase1_first_prenorm
+  if (!x_out && (prenorm_gain || h_out)) return ATTNRES_EINVAL;
+  attnres_status_t st = check_d(d);
+  if (st != ATTNRES_OK) return st;
+  if (!extent_ok(T, {src_stride}) || S < 1 || S > ATTNRES_MAX_QUERIES) return ATTNRES_EINVAL;
+  const int64_t max_src = (S == 1 && !x_out && src_dt == dt) ? ATTNRES_MAX_SOURCES : ATTNRES_MAX_SOURCES_MULTI;
+  if (n_src < 2 || n_src > max_src) return ATTNRES_EINVAL;
+  if (T > 0) {
+    if (!src || !sublayer_prev || !lse_out) return ATTNRES_EINVAL;
+    st = check_align({partial_in, sublayer_prev2, sublayer_prev});
+    if (st != ATTNRES_OK) return st;
+    // the newest slab is written: no piece may overlap it, and no output
+    // may overlap a piece (the outputs are checked against src below)
+    const int64_t rows = T * d;
+    const Range rn = range_of(static_cast<char*>(src) + (n_src - 1) * src_stride * esize(src_dt), rows * esize(src_dt));
+    const Range pieces[] = {range_of(sublayer_prev, rows * esize(sublayer_dt)),
+                            sublayer_prev2 ? range_of(sublayer_prev2, rows * esize(sublayer_dt)) : Range{0, 0},
+                            partial_in ? range_of(partial_in, partial_bytes(partial_dt, T, d)) : Range{0, 0}};
+    const int64_t es = esize(dt);
+    const Range outs[] = {out ? range_of(out, S * rows * es) : Range{0, 0}, range_of(lse_out, S * T * 4),
+                          m_out ? range_of(m_out, S * T * 4) : Range{0, 0},
+                          x_out ? range_of(x_out, rows * es) : Range{0, 0},
+                          h_out ? range_of(h_out, rows * es) : Range{0, 0},
+                          workspace ? range_of(workspace, std::max<int64_t>(0, attnres_phase1_workspace_bytes(
+                                                                     T, d, n_src, S)))
+                                    : Range{0, 0}};
+    for (Range pr : pieces) {
+      if (overlaps(pr, rn)) return ATTNRES_EALIAS;
+      for (Range o : outs)
+        if (overlaps(pr, o)) return ATTNRES_EALIAS;
+    }
+  }
+  const attnres::Newest nw{partial_in, kind_of(partial_dt), kind_of(sublayer_dt), sublayer_prev2, sublayer_prev};
+  return phase1_impl(dt, src_dt, src, n_src, src_stride, T, d, w, key_gain, S, eps, out, m_out, lse_out,
+                     x_out ? prenorm_gain : nullptr, x_out, h_out, workspace, workspace_bytes, stream, &nw);
 }
 
 attnres_status_t attnres_phase2_merge(attnres_dtype_t dt, int64_t T, int64_t d, const void* p1_out,

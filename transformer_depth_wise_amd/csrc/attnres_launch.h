@@ -16,11 +16,24 @@ int device_cu_count();
 // x0 != null, query 0's output goes through the PreNorm with gain gamma0
 // into x0 (and as is into h0 when not null) instead of slab 0 of out, which
 // may be used as scratch; out may then be null when n == 1.  Or S == 1 with
-// optional PreNorm (n <= 32).  Return a hipError_t.
+// optional PreNorm (n <= 32).  With nw != null, source n-1 is first formed
+// from the pieces nw describes (fused into the scoring kernel for long
+// token ranges).  Return a hipError_t.
+// The newest source of a phase-1 call as the pieces of a block sum:
+// ((pin or 0) + (v2 or 0)) + v, the outputs v2, v of type vdt, the partial in
+// format pdt; the sum is written to source slab n-1 (of the sources' type).
+struct Newest {
+  const void* pin;
+  Dtype pdt;
+  Dtype vdt;
+  const void* v2;
+  const void* v;
+};
+
 hipError_t launch_phase1_multi(Dtype dt, Dtype sdt, const void* src, int n, int64_t stride, int64_t T, int d,
                                const float* w, const float* kg, int S, float eps, void* out,
                                float* m_out, float* lse_out, const float* gamma0, void* x0, void* h0,
-                               float* alpha, hipStream_t stream);
+                               float* alpha, const Newest* nw, hipStream_t stream);
 
 hipError_t launch_phase1_single(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
                                 const float* w, const float* kg, const float* gamma, float eps,

@@ -168,6 +168,44 @@ struct Mfma<float> {
   }
 };
 
+// The newest source of a phase-1 call formed from the pieces of the previous
+// block's sum ("Attention Residuals" notes, section 8: b_n is the sum of the
+// block's outputs): u = (partial + (v2 or 0)) + v in fp32, in that order,
+// rounded to the sources' type exactly as the block-sum kernel stores it.
+// `round_store` rounds 8 such values, stores them (when `st`) and returns the
+// matrix-core operand of the rounded chunk.
+template <typename St>
+struct RoundB;
+template <>
+struct RoundB<bf16_t> {
+  static __device__ __forceinline__ Mfma<bf16_t>::B round_store(const float (&x)[8], bf16_t* p, bool st) {
+    const u32x4_t u{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                    pack_bf16x2(x[6], x[7])};
+    if (st) st16(p, u);
+    return __builtin_bit_cast(bf16x8_t, u);
+  }
+};
+template <>
+struct RoundB<float> {
+  static __device__ __forceinline__ Mfma<float>::B round_store(const float (&x)[8], float* p, bool st) {
+    if (st) {
+      st16(p, u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])});
+      st16(p + 4, u32x4_t{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])});
+    }
+    Mfma<float>::B b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b.v[e] = x[e];
+    return b;
+  }
+};
+
+// One K-block of the newest source's pieces for one lane (4 chunks).
+template <typename Vt, typename Pt>
+struct PieceStage {
+  Chunk<Pt> p[4];
+  Chunk<Vt> a[4], b[4];
+};
+
 // Packed query operands.  Channels are grouped into K-blocks of 128 (16
 // chunks of 8); K-block kb of a tile of 16*MT queries is a contiguous run of
 // MT*4*2*64 16-byte words ordered [m][step][half][lane], where lane
@@ -529,10 +567,18 @@ struct WideDepth<float, MT> {
   static constexpr int value = 2;
 };
 
-template <typename St, int MT>
+//
+// FUSED: source n-1 is not read from src but formed from the pieces of the
+// previous block's sum (npin: the stored partial, nv2: the one-before-last
+// output or null, nv: the last output) and stored to ndst, the slab that
+// later kernels read as source n-1; it is scored from the rounded values, so
+// the results equal those of summing first and scoring afterwards, bit for
+// bit.  Its K-blocks come last, through a ring of two stages of pieces.
+template <typename St, int MT, typename Vt = St, typename Pt = float, bool FUSED = false>
 __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
     const St* __restrict__ src, int n, int64_t stride, int64_t T, int d, const u32x4_t* __restrict__ pk, int S,
-    float eps, float* __restrict__ alpha, float* __restrict__ m_out, float* __restrict__ lse_out) {
+    float eps, float* __restrict__ alpha, float* __restrict__ m_out, float* __restrict__ lse_out,
+    const Pt* __restrict__ npin, const Vt* __restrict__ nv2, const Vt* __restrict__ nv, St* __restrict__ ndst) {
   constexpr int D = WideDepth<St, MT>::value;
   constexpr int QW = MT * 512;  // 16-byte words per packed K-block
   static_assert(D % 2 == 0, "the LDS slot of a ring stage must be a constant");
@@ -543,6 +589,7 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
   const int C = d >> 3;
   const int nkb = (C + kKBlock - 1) / kKBlock;
   const int nit = n * nkb;  // (source, K-block) iterations, source-major
+  const int nitr = FUSED ? nit - nkb : nit;  // iterations that read src
   const KOrder ko(nkb);
   // Global memory is touched only by loads until the last loop ends, and
   // every load below is unconditional (indices clamped), so the compiler
@@ -587,7 +634,7 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
   float* zw = zs + wave * (16 * S * n);
   B b[D][4];
   auto issue = [&](B(&bs)[4], int it) {
-    it = it < nit ? it : nit - 1;
+    it = it < nitr ? it : nitr - 1;
     const int i = it / nkb;
     const int kb = it - i * nkb;
     const St* base = row + (int64_t)i * stride;
@@ -678,23 +725,81 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
     }
   };
 
+  if (nitr > 0) {  // uniform
 #pragma unroll
-  for (int s = 0; s < D - 1; ++s) issue(b[s], s);
-  int it0 = 0;
-  for (; it0 + D <= nit; it0 += D) {
+    for (int s = 0; s < D - 1; ++s) issue(b[s], s);
+    int it0 = 0;
+    for (; it0 + D <= nitr; it0 += D) {
 #pragma unroll
-    for (int s = 0; s < D; ++s) {
-      issue(b[(s + D - 1) % D], it0 + s + D - 1);
-      lds_barrier();  // the queries of this K-block are in slot s & 1
-      step(b[s], qs[s & 1], it0 + s);
+      for (int s = 0; s < D; ++s) {
+        issue(b[(s + D - 1) % D], it0 + s + D - 1);
+        lds_barrier();  // the queries of this K-block are in slot s & 1
+        step(b[s], qs[s & 1], it0 + s);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < D - 1; ++s)  // tail: every stage is already loaded
+      if (it0 + s < nitr) {
+        lds_barrier();
+        step(b[s], qs[s & 1], it0 + s);
+      }
+  }
+  if constexpr (FUSED) {
+    // source n-1 from its pieces (loads unconditional: a missing v2 is
+    // replaced by v and not added)
+    const int64_t plane = T * (int64_t)d;
+    const bool live = tok0 + col < T;
+    RowExp<Pt> qe;
+    qe.load(npin, tokc, plane);
+    const Vt* v2p = nv2 ? nv2 : nv;
+    PieceStage<Vt, Pt> ps[2];
+    auto pissue = [&](PieceStage<Vt, Pt>& st, int kb) {
+      kb = kb < nkb ? kb : nkb - 1;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int c0 = kb * kKBlock + s4 * 4 + grp;
+        const int64_t off = tokc * d + (c0 < C ? c0 : C - 1) * 8;
+        st.p[s4].load_at(npin, off, plane);
+        st.a[s4].load(v2p + off);
+        st.b[s4].load(nv + off);
+      }
+    };
+    auto pstep = [&](const PieceStage<Vt, Pt>& st, int kb) {
+      B bs[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int c0 = kb * kKBlock + s4 * 4 + grp;
+        float x[8], y[8];
+        unpack_partial(st.p[s4], qe, x);
+        if (nv2) {
+          st.a[s4].unpack(y);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = x[e] + y[e];
+        }
+        st.b[s4].unpack(y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = x[e] + y[e];
+        bs[s4] = RoundB<St>::round_store(x, ndst + tokc * d + (c0 < C ? c0 : C - 1) * 8, live && c0 < C);
+      }
+      const int it = nitr + kb;
+      step(bs, qs[it & 1], it);
+    };
+    pissue(ps[0], 0);
+    for (int kb = 0; kb < nkb; kb += 2) {
+      pissue(ps[1], kb + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      pstep(ps[0], kb);
+      __builtin_amdgcn_sched_barrier(0);
+      pissue(ps[0], kb + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb + 1 < nkb) {  // uniform
+        lds_barrier();
+        pstep(ps[1], kb + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-#pragma unroll
-  for (int s = 0; s < D - 1; ++s)  // tail: every stage is already loaded
-    if (it0 + s < nit) {
-      lds_barrier();
-      step(b[s], qs[s & 1], it0 + s);
-    }
 
   // softmax over the n sources of every (token, query) pair of the tile (the
   // wave reads back only what it wrote, in program order)
@@ -1522,31 +1627,78 @@ static hipError_t pick_out(int n, const void* src, int64_t stride, int64_t T, in
   return hipErrorInvalidValue;
 }
 
+// The wide scoring kernel on sources of type Ut; Vt and Pt are the types of
+// the newest source's pieces when FUSED.
+template <typename Ut, int MT, typename Vt, typename Pt, bool FUSED>
+static hipError_t launch_wide(const void* src, int n, int64_t stride, int64_t T, int d, const u32x4_t* pk, int S,
+                              float eps, float* al, float* m_out, float* lse_out, const Newest* nw,
+                              hipStream_t stream) {
+  const int64_t wide_groups = (T + 16 * kWideWaves - 1) / (16 * kWideWaves);
+  const size_t zl = sizeof(float) * kWideWaves * 16 * S * n;
+  auto kw = k_p1_scores_wide<Ut, MT, Vt, Pt, FUSED>;
+  hipError_t e = set_lds(kw, zl, zl + sizeof(u32x4_t) * 2 * MT * 512);
+  if (e != hipSuccess) return e;
+  Ut* dst = FUSED ? static_cast<Ut*>(const_cast<void*>(src)) + (int64_t)(n - 1) * stride : nullptr;
+  hipLaunchKernelGGL(kw, dim3((unsigned)wide_groups), dim3(64 * (kWideWaves + 1)), zl, stream,
+                     static_cast<const Ut*>(src), n, stride, T, d, pk, S, eps, al, m_out, lse_out,
+                     static_cast<const Pt*>(FUSED ? nw->pin : nullptr), static_cast<const Vt*>(FUSED ? nw->v2 : nullptr),
+                     static_cast<const Vt*>(FUSED ? nw->v : nullptr), dst);
+  return hipGetLastError();
+}
+
+static constexpr Dtype kind_of_type(bool f32) { return f32 ? kF32 : kBF16; }
+
 // The scores (and the query packing for their matrix-core type) follow the
 // source rows' type Ut; the outputs are stored as St.
 template <typename Ut, typename St, int MT>
 static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, int d, const float* w,
                             const float* kg, int S, float eps, void* out, float* m_out, float* lse_out,
-                            const float* gamma0, void* x0, void* h0, float* ws, hipStream_t stream) {
+                            const float* gamma0, void* x0, void* h0, float* ws, const Newest* nw,
+                            hipStream_t stream) {
   // workspace: packed queries first (room for 32 queries), then the softmax
   // weights
   const int nkb = ((d >> 3) + kKBlock - 1) / kKBlock;
   u32x4_t* pk = reinterpret_cast<u32x4_t*>(ws);
   float* al = ws + (int64_t)nkb * kPackedKBlockWords * 4;
   const int npk = nkb * MT * 4 * 64;
+  const int64_t wide_groups = (T + 16 * kWideWaves - 1) / (16 * kWideWaves);
+  const bool wide = wide_groups >= device_cu_count();
+  // the newest source from the pieces of a block sum: summed inside the wide
+  // scoring kernel (a stored partial in Q16 or fp32), else by the block-sum
+  // kernel first
+  const bool fused = nw && wide && nw->pin && (nw->pdt == kQ16 || nw->pdt == kF32);
+  hipError_t e;
+  if (nw && !fused) {
+    e = launch_accumulate(nw->vdt, kind_of_type(sizeof(Ut) == 4), T, d, nw->pdt, nw->pin, nw->v2, nw->v,
+                          static_cast<Ut*>(const_cast<void*>(src)) + (int64_t)(n - 1) * stride, stream);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((k_pack_queries<Ut, MT>), dim3((unsigned)((npk + 255) / 256)), dim3(256), 0, stream, w, kg,
                      S, d, pk);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t wide_groups = (T + 16 * kWideWaves - 1) / (16 * kWideWaves);
-  if (wide_groups >= device_cu_count()) {
+  if (wide) {
     // enough 64-token tiles for one workgroup per compute unit
-    const size_t zl = sizeof(float) * kWideWaves * 16 * S * n;
-    auto kw = k_p1_scores_wide<Ut, MT>;
-    e = set_lds(kw, zl, zl + sizeof(u32x4_t) * 2 * MT * 512);
+    if (!fused) {
+      e = launch_wide<Ut, MT, St, float, false>(src, n, stride, T, d, pk, S, eps, al, m_out, lse_out, nw, stream);
+    } else {
+      // the pieces' type: bf16 (the only one bf16 sources take) or fp32
+      bool bf16_pieces = true;
+      if constexpr (sizeof(Ut) == 4) {
+        bf16_pieces = nw->vdt == kBF16;
+        if (!bf16_pieces)
+          e = nw->pdt == kQ16 ? launch_wide<Ut, MT, float, q16_t, true>(src, n, stride, T, d, pk, S, eps, al, m_out,
+                                                                       lse_out, nw, stream)
+                              : launch_wide<Ut, MT, float, float, true>(src, n, stride, T, d, pk, S, eps, al, m_out,
+                                                                       lse_out, nw, stream);
+      }
+      if (bf16_pieces)
+        e = nw->pdt == kQ16 ? launch_wide<Ut, MT, bf16_t, q16_t, true>(src, n, stride, T, d, pk, S, eps, al, m_out,
+                                                                      lse_out, nw, stream)
+                            : launch_wide<Ut, MT, bf16_t, float, true>(src, n, stride, T, d, pk, S, eps, al, m_out,
+                                                                      lse_out, nw, stream);
+    }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kw, dim3((unsigned)wide_groups), dim3(64 * (kWideWaves + 1)), zl, stream,
-                       static_cast<const Ut*>(src), n, stride, T, d, pk, S, eps, al, m_out, lse_out);
   } else {
     // one workgroup per (16-token tile, group of G sources), then the
     // softmax per pair; G is the largest of 4, 2, 1 that still gives two
@@ -1577,12 +1729,12 @@ static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, i
 hipError_t launch_phase1_multi(Dtype dt, Dtype sdt, const void* src, int n, int64_t stride, int64_t T, int d,
                                const float* w, const float* kg, int S, float eps, void* out,
                                float* m_out, float* lse_out, const float* gamma0, void* x0, void* h0, float* ws,
-                               hipStream_t stream) {
+                               const Newest* nw, hipStream_t stream) {
 #define ATTNRES_MULTI(UT_, ST_)                                                                                   \
   return S <= 16 ? run_multi<UT_, ST_, 1>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, gamma0, x0, h0, \
-                                          ws, stream)                                                            \
+                                          ws, nw, stream)                                                        \
                  : run_multi<UT_, ST_, 2>(src, n, stride, T, d, w, kg, S, eps, out, m_out, lse_out, gamma0, x0, h0, \
-                                          ws, stream)
+                                          ws, nw, stream)
   if (dt == kBF16 && sdt == kBF16) ATTNRES_MULTI(bf16_t, bf16_t);
   if (dt == kBF16 && sdt == kF32) ATTNRES_MULTI(float, bf16_t);
   if (dt == kF32 && sdt == kF32) ATTNRES_MULTI(float, float);

@@ -40,7 +40,8 @@ import torch
 from . import _lib
 from ._lib import (attnres_block_accumulate, attnres_full, attnres_phase1, attnres_phase1_backward,
                    attnres_site_backward_accumulate,
-                   attnres_phase1_first_prenorm, attnres_phase2_backward, attnres_phase2_merge,
+                   attnres_phase1_accumulate, attnres_phase1_first_prenorm, attnres_phase2_backward,
+                   attnres_phase2_merge,
                    attnres_phase2_merge_multi)
 
 SiteHook = Callable[..., None]
@@ -103,13 +104,19 @@ class BlockAttnRes:
     those exact sums (phase 1 then reads fp32 sources and writes bf16
     outputs; the embedding and given block sums are copied in exactly).
     ``dh_final`` then comes in fp32 too.
+    ``fuse_sum``: a block's sum b_n is formed by the next phase-1 call
+    (attnres_phase1_accumulate, which sums inside the scoring pass over long
+    token ranges) or by the final site's call, instead of by a block-sum
+    launch at the end of the block (False); after the last block without a
+    final site, a block-sum launch forms it either way.
     """
 
     def __init__(self, T: int, d: int, block_sizes: Sequence[int], dtype: torch.dtype, n_given: int = 0,
                  eps: float = 1e-6, device=None, x_ring: int = 4, keep_h: bool = False,
                  final_site: bool = True, partial: Optional[str] = None, fuse_first: bool = True,
-                 training: bool = False):
+                 training: bool = False, fuse_sum: bool = True):
         self.training = bool(training)
+        self.fuse_sum = bool(fuse_sum)
         self.fuse_first = bool(fuse_first) and not self.training
         self.T, self.d, self.dtype = int(T), int(d), dtype
         self.block_sizes = [int(s) for s in block_sizes]
@@ -218,16 +225,17 @@ class BlockAttnRes:
         stat = self.T * 4
         out: List[Launch] = []
         n_done = 1 + self.n_given
+        pend = 0  # bytes of the previous block's sum still to be formed (its pieces read, b_n written)
         for S in self.block_sizes:
             fuse = self._fuse(S, n_done)
             if fuse:  # + x of the first sublayer (phase 1 writes it instead of o_0)
-                out.append(Launch("phase1", n_done * rr + S * r + S * 2 * stat if n_done > 1 else
-                                  rr + r + S * 2 * stat))
+                out.append(Launch("phase1", pend + (n_done * rr + S * r + S * 2 * stat if n_done > 1 else
+                                                    rr + r + S * 2 * stat)))
             elif n_done == 1 and not self.training:
                 # statistics only; phase 2 reads b_0 as its phase-1 output
-                out.append(Launch("phase1", rr + S * 2 * stat))
+                out.append(Launch("phase1", pend + rr + S * 2 * stat))
             else:
-                out.append(Launch("phase1", n_done * rr + S * (r + 2 * stat)))
+                out.append(Launch("phase1", pend + n_done * rr + S * (r + 2 * stat)))
             for j in range(S):
                 if j == 0 and fuse:
                     continue
@@ -243,16 +251,22 @@ class BlockAttnRes:
                     b = 4 * r + 2 * r32 + stat        # o, p, v, v; p, x
                 out.append(Launch("phase2", b))
             if S == 1:
-                out.append(Launch("accumulate", r + rr))
+                acc = r + rr
             elif S == 2:
-                out.append(Launch("accumulate", 2 * r + rr))
+                acc = 2 * r + rr
             elif S % 2:
-                out.append(Launch("accumulate", r + r32 + rr))       # p (stored at S-1), v; b
+                acc = r + r32 + rr           # p (stored at S-1), v; b
             else:
-                out.append(Launch("accumulate", 2 * r + r32 + rr))   # p (stored at S-2), v, v; b
+                acc = 2 * r + r32 + rr       # p (stored at S-2), v, v; b
+            if self.fuse_sum:
+                pend = acc                   # formed by the next phase-1 (or the final site's) call
+            else:
+                out.append(Launch("accumulate", acc))
             n_done += 1
         if self.final_site:
-            out.append(Launch("final", (n_done + 1) * rr + stat))
+            out.append(Launch("final", pend + (n_done + 1) * rr + stat))
+        elif pend:
+            out.append(Launch("accumulate", pend))
         return out
 
     def plan_survey(self) -> List[Launch]:
@@ -270,17 +284,23 @@ class BlockAttnRes:
         r = self._row()
         out: List[Launch] = []
         n_done = 1 + self.n_given
+        pend = 0  # a block sum formed inside the next call is booked there
         for S in self.block_sizes:
             fuse = self._fuse(S, n_done)
-            out.append(Launch("phase1", (n_done + S + (2 if fuse else 0)) * r))
+            out.append(Launch("phase1", pend + (n_done + S + (2 if fuse else 0)) * r))
             for j in range(S):
                 if j == 0 and fuse:
                     continue
                 out.append(Launch("phase2", (2 if j == 0 else 3 if j == 1 else 5) * r))
-            out.append(Launch("accumulate", 3 * r))
+            if self.fuse_sum:
+                pend = 3 * r
+            else:
+                out.append(Launch("accumulate", 3 * r))
             n_done += 1
         if self.final_site:
-            out.append(Launch("final", (n_done + 1) * r))
+            out.append(Launch("final", pend + (n_done + 1) * r))
+        elif pend:
+            out.append(Launch("accumulate", pend))
         return out
 
     # ---------------------------------------------------------------- forward
@@ -292,9 +312,12 @@ class BlockAttnRes:
         fp32 ``w``, ``g`` [L+1, d] and ``gamma`` [L, d] (``g``/``gamma`` may be
         None for unit gains).  ``sublayer(l, x_l)`` returns the output v_l of
         sublayer l (0-based), a [T, d] tensor that stays valid for the rest of
-        the block.  ``hook(site, x=, h=, o1=, lse1=, m1=)`` is called after
-        each phase-2 launch.  ``instrument(kind, begin)`` is called just
-        before (begin=True) and after (begin=False) every launch."""
+        the block (the last two of a block until the next block's phase-1
+        call, or the final site's, has been issued: with ``fuse_sum`` that
+        call forms the block's sum from them).  ``hook(site, x=, h=, o1=,
+        lse1=, m1=)`` is called after each phase-2 launch.
+        ``instrument(kind, begin)`` is called just before (begin=True) and
+        after (begin=False) every launch."""
         _check_params(params, self.d, self.L + (1 if self.final_site else 0), self.L, self.device)
         w, g, gam = params["w"], params.get("g"), params.get("gamma")
         eps = self.eps
@@ -302,6 +325,7 @@ class BlockAttnRes:
         mark = instrument if instrument is not None else (lambda kind, begin: None)
         l0 = 0
         nx = self.x.shape[0]
+        pending = None  # (partial, v_{S-2}, v_{S-1}) of the previous block, its sum not yet formed
         for b, S in enumerate(self.block_sizes):
             # with a single completed source (the embedding) every phase-1
             # output is that source: compute the statistics only and let
@@ -312,7 +336,15 @@ class BlockAttnRes:
             slots = self.p_slots[b] if self.training else None
             fuse = self._fuse(S, n_done)
             mark("phase1", True)
-            if fuse:
+            if pending is not None:
+                # b_{n_done-1}, the previous block's sum, is formed by this call
+                attnres_phase1_accumulate(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S],
+                                          eps, *pending, o1, self.m1[:S], lse1,
+                                          prenorm_gain=None if (gam is None or not fuse) else gam[l0],
+                                          x_out=self.x[l0 % nx] if fuse else None, h_out=self.h if fuse else None,
+                                          workspace=self.workspace, stream=stream, check=False)
+                pending = None
+            elif fuse:
                 attnres_phase1_first_prenorm(self.reps, n_done, w[l0:l0 + S], None if g is None else g[l0:l0 + S],
                                              eps, None if single else self.o1[:S], self.m1[:S], self.lse1[:S],
                                              None if gam is None else gam[l0], self.x[l0 % nx], self.h,
@@ -359,24 +391,28 @@ class BlockAttnRes:
                     hook(site, x=x, h=self.h, o1=o, lse1=lse1[j], m1=self.m1[j])
                 prev2, prev = prev, _checked_rows(sublayer(site, x), "output of sublayer %d" % site, self.T,
                                                   self.d, self.dtype)
-            mark("accumulate", True)
+            # b_n = ((p or 0) + (v_{S-2} or 0)) + v_{S-1}: the partial stored at
+            # S-2 (S even) or S-1 (S odd), none for S <= 2
             p_last = self.partial if slots is None else (slots[-1] if slots else None)
-            if S == 1:
-                attnres_block_accumulate(None, prev, self.reps[n_done], stream=stream, check=False)
-            elif S == 2:
-                attnres_block_accumulate(None, prev, self.reps[n_done], stream=stream, v2=prev2, check=False)
-            elif S % 2:
-                attnres_block_accumulate(p_last, prev, self.reps[n_done], stream=stream, check=False)
-            else:
-                attnres_block_accumulate(p_last, prev, self.reps[n_done], stream=stream, v2=prev2, check=False)
-            mark("accumulate", False)
+            pending = (None if S <= 2 else p_last, prev2 if S % 2 == 0 else None, prev)
+            if not self.fuse_sum or (b == len(self.block_sizes) - 1 and not self.final_site):
+                mark("accumulate", True)
+                attnres_block_accumulate(pending[0], pending[2], self.reps[n_done], stream=stream, v2=pending[1],
+                                         check=False)
+                mark("accumulate", False)
+                pending = None
             n_done += 1
             l0 += S
         if self.final_site:
             mark("final", True)
-            attnres_phase1(self.reps, n_done, w[self.L:self.L + 1], None if g is None else g[self.L:self.L + 1],
-                           eps, self.h_final.unsqueeze(0), None, self.lse_final.unsqueeze(0), self.workspace,
-                           stream=stream, check=False)
+            wf, gf = w[self.L:self.L + 1], None if g is None else g[self.L:self.L + 1]
+            if pending is not None:
+                attnres_phase1_accumulate(self.reps, n_done, wf, gf, eps, *pending, self.h_final.unsqueeze(0), None,
+                                          self.lse_final.unsqueeze(0), workspace=self.workspace, stream=stream,
+                                          check=False)
+            else:
+                attnres_phase1(self.reps, n_done, wf, gf, eps, self.h_final.unsqueeze(0), None,
+                               self.lse_final.unsqueeze(0), self.workspace, stream=stream, check=False)
             mark("final", False)
         return self.h_final
 
