@@ -213,9 +213,12 @@ def _time(fn, steps: int) -> float:
 def backward_report(dev, steps: int):
     """Backward through the whole block structure of the 16K chunk
     (training): one training forward keeps the phase-1 outputs and partial
-    sums, then ``max(2, steps // 4)`` backward passes are timed.  The
-    synthetic upstream gradient of sublayer l's input is another sublayer's
-    output row (a model's sublayer backward would produce it from dL/dv_l)."""
+    sums, then ``max(2, steps // 4)`` backward passes are timed, and one more
+    with HIP events around every launch gives the per-kernel times (such
+    events cost a few microseconds each, so the timed passes carry none).
+    The synthetic upstream gradient of sublayer l's input is another
+    sublayer's output row (a model's sublayer backward would produce it from
+    dL/dv_l)."""
     import torch
     import synth
     import transformer_depth_wise_amd as tdw
@@ -243,13 +246,15 @@ def backward_report(dev, steps: int):
     dhf = v[0].to(st.h_final.dtype)   # h_final is fp32 in a bf16 training pass
     st.backward(prm, dx_for, dh_final=dhf)
     nb = max(2, steps // 4)
-    sec = _time(lambda k: st.backward(prm, dx_for, dh_final=dhf, instrument=instrument), nb)
+    sec = _time(lambda k: st.backward(prm, dx_for, dh_final=dhf), nb)
+    st.backward(prm, dx_for, dh_final=dhf, instrument=instrument)
+    torch.cuda.synchronize()
     plan = st.plan_backward()
     b = sum(x.bytes for x in plan)
     kinds = {}
     for kind, e0, e1 in recs:
         kinds.setdefault(kind, [0.0, 0])
-        kinds[kind][0] += e0.elapsed_time(e1) / nb
+        kinds[kind][0] += e0.elapsed_time(e1)
         kinds[kind][1] += 1
     kb = {}
     for x in plan:
@@ -258,7 +263,7 @@ def backward_report(dev, steps: int):
         "config": {"T": w.T, "d": w.d, "blocks": list(w.block_sizes), "final_site": w.final_site},
         "ms_per_step": round(sec * 1e3, 4), "value": round(w.T * w.L / sec, 1), "unit": "token-sublayers/s",
         "hbm_gbps": round(b / sec / 1e9, 1), "bytes_per_step": b,
-        "kernels": {k: {"ms_per_step": round(ms, 4), "launches_per_step": c // nb,
+        "kernels": {k: {"ms_per_step": round(ms, 4), "launches_per_step": c,
                         "gbps": round(kb[k] / (ms * 1e-3) / 1e9, 1)} for k, (ms, c) in kinds.items()},
         "note": "backward only (the training forward that keeps its activations is not timed here)"}
     del st, v
