@@ -746,6 +746,27 @@ def _long_prefill(w, chunked: bool, samples, dev):
     return h_final, xs, peak
 
 
+def test_long_prefill_ragged_last_chunk():
+    """A context that is not a whole number of chunks: the last, shorter
+    chunk gets buffers of its own size after the full-size ones are released,
+    so the peak stays that of whole chunks, and the output still equals the
+    unchunked pass bit for bit."""
+    base = synth.WORKLOADS["long_prefill_bf16"]
+    dev = torch.device("cuda")
+    w = synth.scaled(base, name="ragged_prefill", T=3 * 4096 + 1000, d=1024, chunk=4096, block_sizes=(4, 4, 3))
+    whole = synth.scaled(w, T=3 * 4096)
+    samples = synth.sample_tokens(w.T, 8)
+    _say("case long_prefill ragged T=%d chunk=%d" % (w.T, w.chunk))
+    hc, xc, peak_ragged = _long_prefill(w, True, samples, dev)
+    hu, xu, _ = _long_prefill(w, False, samples, dev)
+    _, _, peak_whole = _long_prefill(whole, True, synth.sample_tokens(whole.T, 8), dev)
+    _say("peak: ragged %.3f GB, whole chunks %.3f GB" % (peak_ragged / 1e9, peak_whole / 1e9))
+    assert torch.equal(hc, hu)
+    for t in samples:
+        assert torch.equal(xc[t], xu[t]), t
+    assert peak_ragged <= peak_whole * 1.02
+
+
 def test_long_prefill_chunked_equals_unchunked_and_oracle():
     w = synth.WORKLOADS["long_prefill_bf16"]
     dev = torch.device("cuda")
