@@ -409,7 +409,8 @@ attnres_status_t attnres_site_backward_accumulate(attnres_dtype_t dt,
  *   c_in and gp_in), 1 <= S <= 32.  Outputs must not overlap any
  *   input or each other.  workspace:
  *   attnres_phase1_backward_workspace_bytes(T, d, n_src, S) bytes, 16-byte
- *   aligned (per-token coefficients, w (.) key_gain, per-range sums; for
+ *   aligned (per-token coefficients, w (.) key_gain, per-range sums, the
+ *   queries packed as matrix-core operands; for
  *   S == 1 at least the site backward's per-team sums, since one site
  *   without c_in and gp_in -- the final aggregation -- is computed as
  *   attnres_site_backward without PreNorm would, into the fp32 rows).

@@ -263,10 +263,12 @@ def test_phase1_backward_validation(lib):
     assert lib.attnres_phase1_backward_workspace_bytes(1 << 31, 64, 3, 4) == -1
     assert lib.attnres_phase2_backward_workspace_bytes(1 << 31, 64) == -1
     # coefficients T x (S rounded up to 8) x n, folded queries S x d, per-range sums (2048 waves over
-    # d / 256 groups)
-    assert lib.attnres_phase1_backward_workspace_bytes(1024, 64, 3, 4) == 4 * (1024 * 8 * 3 + 4 * 64 + 2048 * 4 * 64)
+    # d / 256 groups), the queries packed as matrix-core operands (4096 bytes per 32 channels)
+    assert lib.attnres_phase1_backward_workspace_bytes(1024, 64, 3, 4) == \
+        4 * (1024 * 8 * 3 + 4 * 64 + 2048 * 4 * 64) + 2 * 4096
     assert lib.attnres_phase1_backward_workspace_bytes(16384, 7168, 8, 24) == \
-        4 * (16384 * 24 * 8 + 24 * 7168 + 74 * 24 * 7168)
+        4 * (16384 * 24 * 8 + 24 * 7168 + 74 * 24 * 7168) + 224 * 4096
+    assert lib.attnres_phase1_backward_workspace_bytes(8, 1000, 3, 4) % 16 == 0   # 1000 channels: 32 k-steps
     assert lib.attnres_phase1_backward_workspace_bytes(10, 64, 3, 33) == -1
 
 

@@ -530,10 +530,12 @@ int64_t attnres_phase1_backward_workspace_bytes(int64_t T, int64_t d, int64_t n_
   if (n_src < 1 || n_src > ATTNRES_MAX_SOURCES_MULTI || S < 1 || S > 32) return -1;
   if (T == 0) return 0;
   // coefficients [T][S rounded up to 8][n], folded queries [S][d],
-  // per-range weight sums; one site (S == 1) may run on the site backward,
-  // whose per-team sums need attnres_site_backward_workspace_bytes
+  // per-range weight sums, the queries packed as matrix-core operands
+  // (4096 bytes per 32 channels); one site (S == 1) may run on the site
+  // backward, whose per-team sums need attnres_site_backward_workspace_bytes
   const int64_t sp = (S + 7) & ~(int64_t)7;
-  const int64_t need = (T * sp * n_src + S * d + attnres::p1_backward_ranges((int)d) * S * d) * (int64_t)sizeof(float);
+  const int64_t need = (T * sp * n_src + S * d + attnres::p1_backward_ranges((int)d) * S * d) * (int64_t)sizeof(float) +
+                       ((d + 31) / 32) * 4096;
   const int64_t site = S == 1 ? attnres_site_backward_workspace_bytes(T, d) : 0;
   return need > site ? need : site;
 }
