@@ -43,6 +43,9 @@ constexpr int kP1bGE = 256;                // channels per staged group (8 k-ste
 constexpr int kP1bRow = kP1bGE + 8;        // staged row length in bf16 (16-byte pad)
 constexpr int kP1bStage = 64 * kP1bRow;    // bf16 per LDS buffer: G [32], U_hi [16], U_lo [16]
 constexpr int kP1bPieces = 4;              // 16-byte loads per thread per group
+// register stages of groups (kP1bRing - 1 in flight; 3, 4 or 6 stages made
+// the 16K chunk's phase-1 backward 1-2.5 ms slower on an MI355X)
+constexpr int kP1bRing = 2;
 
 static __global__ __launch_bounds__(256) void k_pack_bwd_queries(int S, int d, const float* __restrict__ q,
                                                                u32x4_t* __restrict__ pk) {
@@ -98,7 +101,7 @@ __device__ __forceinline__ void p1b_part1_mfma(int64_t tok, int64_t T, int d, co
   const int t = threadIdx.x;
   const int col = lane & 15, grp = lane >> 4;
   // the thread's pieces: p = t + kP1bThreads * k
-  u32x4_t ra[kP1bPieces], rb[kP1bPieces];
+  u32x4_t rs[kP1bRing][kP1bPieces];
   float ssa[kP1bPieces];
 #pragma unroll
   for (int k = 0; k < kP1bPieces; ++k) ssa[k] = 0.f;
@@ -185,22 +188,23 @@ __device__ __forceinline__ void p1b_part1_mfma(int64_t tok, int64_t T, int d, co
       }
     }
   };
-  issue(ra, 0);
-  for (int g = 0; g < ngr; g += 2) {
-    issue(rb, g + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    stage(ra, g);
-    lds_barrier();
-    mfma(g);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(ra, g + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    if (g + 1 < ngr) {  // uniform
-      stage(rb, g + 1);
-      lds_barrier();
-      mfma(g + 1);
+  // a ring of kP1bRing register stages: kP1bRing - 1 groups in flight while
+  // the oldest is staged and used
+#pragma unroll
+  for (int s = 0; s < kP1bRing - 1; ++s) issue(rs[s], s);
+  for (int g0 = 0; g0 < ngr; g0 += kP1bRing) {
+#pragma unroll
+    for (int s = 0; s < kP1bRing; ++s) {
+      const int g = g0 + s;
+      issue(rs[(s + kP1bRing - 1) % kP1bRing], g + kP1bRing - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (g < ngr) {  // uniform
+        stage(rs[s], g);
+        lds_barrier();
+        mfma(g);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
   lds_barrier();  // every wave is done with the staging buffers
   // wave partials [wave][lane][16], then the sums of squares per piece
