@@ -525,10 +525,7 @@ __global__ __launch_bounds__(256) void k_p1_softmax(int64_t pairs, int n, int S,
 }
 
 // Wide-tile variant of the scoring kernel for long token ranges, with the
-// same results bit for bit.  (A vector-ALU-only scoring kernel for the same
-// work, fp32 queries staged in LDS and 4-8 tokens x 12 queries per thread,
-// took 673 us per launch at 16384 tokens, d = 7168, 8 sources, 24 queries on
-// an MI355X, against 254 us for this one.)  A workgroup holds kWideWaves compute waves, each
+// same results bit for bit.  A workgroup holds kWideWaves compute waves, each
 // owning a 16-token tile over all of d, plus one loader wave.  A compute wave
 // streams its source rows through a ring of D register stages (one K-block of
 // one source per stage), so D-1 K-blocks are in flight while the matrix cores
@@ -536,7 +533,10 @@ __global__ __launch_bounds__(256) void k_p1_softmax(int64_t pairs, int n, int S,
 // K-block into one of two LDS slots one K-block ahead; the workgroup meets at
 // one barrier per K-block.  The loader waits only on its own query loads, so
 // the source stream never waits behind a query load, and every packed query
-// byte leaves L2 once per 64 tokens instead of once per 16.
+// byte leaves L2 once per 64 tokens instead of once per 16.  (A vector-ALU-only
+// scoring kernel for the same work, fp32 queries staged in LDS and 4-8 tokens
+// x 12 queries per thread, took 673 us per launch at 16384 tokens, d = 7168,
+// 8 sources, 24 queries on an MI355X, against 254 us for this one.)
 //
 // Summation order.  Per source, the K-blocks are visited in order; they form
 // four contiguous classes [w*nkb/4, (w+1)*nkb/4), each summed from zero, the
@@ -567,9 +567,8 @@ struct WideDepth<float, MT> {
   static constexpr int value = 2;
 };
 
-//
-// FUSED: source n-1 is not read from src but formed from the pieces of the
-// previous block's sum (npin: the stored partial, nv2: the one-before-last
+// The wide scoring kernel.  FUSED: source n-1 is not read from src but
+// formed from the pieces of the previous block's sum (npin: the stored partial, nv2: the one-before-last
 // output or null, nv: the last output) and stored to ndst, the slab that
 // later kernels read as source n-1; it is scored from the rounded values, so
 // the results equal those of summing first and scoring afterwards, bit for
