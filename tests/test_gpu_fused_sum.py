@@ -66,6 +66,8 @@ CASES = [
     (37, 7168, 3, 1, "q16", True, "bf16", "bf16", "bf16", False),      # one query without PreNorm: single pass
     (1000, 7168, 9, 1, "q16", True, "f32", "f32", "bf16", False),      # a training pass's final site
     (16384, 7168, 8, 18, "q16", True, "bf16", "bf16", "bf16", True),   # the 16K chunk's last block
+    (16384, 256, 3, 40, "q16", True, "bf16", "bf16", "bf16", True),    # 40 queries: two query tiles
+    (16384, 16384, 2, 3, "q16", True, "bf16", "bf16", "bf16", True),   # the widest rows
 ]
 DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
