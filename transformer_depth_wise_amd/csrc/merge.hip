@@ -281,14 +281,19 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
     }
   }
   lds_barrier();
+  // (the workgroup's next tokens are fetched only if it has any: at short
+  // token ranges a dead prefetch would share the compute unit's load path
+  // with the live rows and hold the wave until it returns)
   while (tok - team < T) {
-    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(B, tok + step, T, d, C, tl, o1, pin, vprev2, vprev, plane);
+    if (tok + step - team < T)  // uniform over the workgroup
+      issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(B, tok + step, T, d, C, tl, o1, pin, vprev2, vprev, plane);
     process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(A, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq, gm_lds, eps,
                                               inv_d, h_out, x_out,
                                               red, parity);
     tok += step;
     if (tok - team >= T) break;
-    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(A, tok + step, T, d, C, tl, o1, pin, vprev2, vprev, plane);
+    if (tok + step - team < T)
+      issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(A, tok + step, T, d, C, tl, o1, pin, vprev2, vprev, plane);
     process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(B, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq, gm_lds, eps,
                                               inv_d, h_out, x_out,
                                               red, parity);
@@ -297,18 +302,24 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
 }
 
 // out = ((partial or 0) + (v2 or 0)) + v, in that order; the sum is stored
-// as Ot (the rows' type, or fp32).  A workgroup takes whole rows (a partial
-// sum's row exponent is read once per row) and its threads the row's chunks.
+// as Ot (the rows' type, or fp32).  A workgroup item is a segment of 256
+// chunks of one row (a partial sum's row exponent is read once per item), a
+// thread one chunk, so at short token ranges every load of the launch is in
+// flight at once.
 template <typename St, typename Pt, typename Ot>
 __global__ __launch_bounds__(256) void k_accumulate(int64_t T, int d, const Pt* __restrict__ pin,
                                                     const St* __restrict__ v2, const St* __restrict__ v,
                                                     Ot* __restrict__ out) {
   const int C = d >> 3;
+  const int nseg = (C + 255) >> 8;
   const int64_t plane = T * (int64_t)d;
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+  const int64_t items = T * nseg;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t t = it / nseg;
+    const int c = (int)(it - t * nseg) * 256 + (int)threadIdx.x;
     RowExp<Pt> qe;
     if (pin) qe.load(pin, t, plane);
-    for (int c = threadIdx.x; c < C; c += 256) {
+    if (c < C) {
       const int64_t off = t * d + c * 8;
       float a[8], b[8];
       load8(v + off, b);
@@ -440,7 +451,8 @@ template <typename St, typename Pt, typename Ot>
 static hipError_t run_acc(int64_t T, int d, const void* pin, const void* v2, const void* v, void* out,
                           hipStream_t stream) {
   const int64_t cap = (int64_t)device_cu_count() * 8;
-  const dim3 grid((unsigned)(T < cap ? T : cap));
+  const int64_t items = T * (((d >> 3) + 255) >> 8);
+  const dim3 grid((unsigned)(items < cap ? items : cap));
   hipLaunchKernelGGL((k_accumulate<St, Pt, Ot>), grid, dim3(256), 0, stream, T, d, static_cast<const Pt*>(pin),
                      static_cast<const St*>(v2), static_cast<const St*>(v), static_cast<Ot*>(out));
   return hipGetLastError();
