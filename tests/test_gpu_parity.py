@@ -423,8 +423,10 @@ WIDE = [
 def test_phase1_long_range_equals_slices_and_oracle(dt, d, n, S):
     """Phase 1 over a token range long enough for the wide scoring kernel (64
     tokens per workgroup, one workgroup per compute unit) gives, bit for bit,
-    what calls over shorter slices (16-token tiles) give, and matches the
-    oracle on sampled tokens."""
+    what calls over shorter slices (16-token tiles) give, also slices short
+    enough for the softmax to run inside the output kernel and for the query
+    tiles to be split over workgroups, and matches the oracle on sampled
+    tokens."""
     dev = torch.device("cuda")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     T = 64 * cus + 40                   # ragged last workgroup
@@ -449,6 +451,10 @@ def test_phase1_long_range_equals_slices_and_oracle(dt, d, n, S):
     torch.cuda.synchronize()
     for k in range(3):
         assert torch.equal(whole[k], torch.cat([parts[0][k], parts[1][k]], dim=-2 if k == 0 else -1)), k
+    for t0, t1 in ((0, 300), (T - 1000, T)):
+        short = call(t0, t1)
+        for k in range(3):
+            assert torch.equal(short[k], whole[k][:, t0:t1]), (t0, t1, k)
     tol = TOL[dt]
     for t in synth.sample_tokens(T, 6):
         rows = [src[i, t].double().cpu().numpy() for i in range(n)]

@@ -323,13 +323,44 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// The largest value over the 64 lanes with the same DPP steps as
+// wave_sum_dpp (a maximum does not depend on the order).
+template <int CTRL>
+__device__ __forceinline__ float dpp_max_step(float x) {
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = dpp_max_step<0xB1>(x);
+  x = dpp_max_step<0x4E>(x);
+  x = dpp_max_step<0x141>(x);
+  x = dpp_max_step<0x140>(x);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Wave-level sum and maximum: the shuffle butterfly, or (DPP) the DPP row
+// steps and scalar reads, which take a fraction of the shuffles' latency.
+template <bool DPP>
+__device__ __forceinline__ float wsum(float x) {
+  return DPP ? wave_sum_dpp(x) : wave_sum(x);
+}
+template <bool DPP>
+__device__ __forceinline__ float wmax(float x) {
+  return DPP ? wave_max_dpp(x) : wave_max(x);
+}
+
 // Sums of a and b and the maximum of c over the 256 threads of a workgroup,
 // in a fixed order (identical in every thread); `lds` holds 12 floats,
-// alternated by the caller like block_sum2_256's.
+// alternated by the caller like block_sum2_256's.  DPP: the wave-level steps
+// of wave_sum_dpp.
+template <bool DPP = false>
 __device__ __forceinline__ float3 block_sum2_max_256(float a, float b, float c, float* lds) {
-  a = wave_sum(a);
-  b = wave_sum(b);
-  c = wave_max(c);
+  a = wsum<DPP>(a);
+  b = wsum<DPP>(b);
+  c = wmax<DPP>(c);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   if (lane == 0) {
@@ -349,10 +380,11 @@ __device__ __forceinline__ float3 block_sum2_max_256(float a, float b, float c, 
 // Sum of (a, b) over the 256 threads of a workgroup, in a fixed order (the
 // result is identical in every thread and from run to run).  `lds` holds 8
 // floats; callers alternate between two such buffers so that one barrier per
-// reduction suffices.
+// reduction suffices.  DPP: the wave-level steps of wave_sum_dpp.
+template <bool DPP = false>
 __device__ __forceinline__ float2 block_sum2_256(float a, float b, float* lds) {
-  a = wave_sum(a);
-  b = wave_sum(b);
+  a = wsum<DPP>(a);
+  b = wsum<DPP>(b);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   if (lane == 0) {

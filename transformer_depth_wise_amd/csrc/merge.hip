@@ -17,17 +17,20 @@
 //
 // Each token row is processed by one team of threads (a wave for d <= 2048,
 // the whole 256-thread workgroup above that).  A thread owns CPL chunks of 8
-// channels; the row's two reductions (|p|^2 with w.p, then |h|^2) use wave
-// shuffles and, for 256-thread teams, one LDS exchange each.  The per-channel
-// parameters (w (.) g and gamma) stay in registers while a persistent grid of
-// two workgroups per CU walks over the tokens; the raw rows of the team's next
-// token are loaded before the current token is reduced, merged and stored, so
-// HBM traffic continues through the reductions and barriers (the loop is
-// unrolled twice over two register stages).  Every row load and store is
-// non-temporal: each row is used once per launch, and what a later launch
-// reads again is far larger than the caches (with non-temporal loads and
-// stores phase 2 of the 16K-token chunk took 37.4 ms instead of 40.0 on one
-// MI355X, measured in one run).
+// channels; the row's two reductions (|p|^2 with w.p, then |h|^2) use DPP
+// row steps with scalar lane reads inside a wave (a few tens of cycles, where
+// a shuffle butterfly waits on six LDS round trips) and, for 256-thread
+// teams, one LDS exchange each.  The per-channel parameters stay on chip (w
+// (.) g in registers, gamma in LDS) while a persistent grid of two
+// workgroups per CU walks over the tokens; the raw rows of the team's next
+// token are loaded before the current token is reduced, merged and stored,
+// so HBM traffic continues through the reductions and barriers (the loop is
+// unrolled twice over two register stages).  When every workgroup has a
+// single token (short token ranges) nothing is prefetched.  Every row load
+// and store is non-temporal: each row is used once per launch, and what a
+// later launch reads again is far larger than the caches (with non-temporal
+// loads and stores phase 2 of the 16K-token chunk took 37.4 ms instead of
+// 40.0 on one MI355X, measured in one run).
 #include "attnres_device.h"
 #include "attnres_launch.h"
 
@@ -39,6 +42,7 @@ struct Stage {
   Chunk<St> o[CPL], v[CPL], v2[CPL];
   Chunk<Pt> q[CPL];
   RowExp<Pt> qe;
+  float lse;  // the phase-1 log-sum-exp of the token (with a partial-sum source)
   bool ok[CPL];
 };
 
@@ -47,14 +51,17 @@ constexpr int kPoutF32 = 0, kPoutP24 = 1, kPoutQ16 = 2;
 
 // Loads of one token for the team.  Every load is unconditional (an
 // out-of-range token or chunk reads a clamped valid address and is zeroed
-// when used), so the loads of a stage issue back to back.
-template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN, bool HAS_V2>
+// when used), so the loads of a stage issue back to back.  LSE: the token's
+// phase-1 log-sum-exp comes with them (a workgroup's only token); otherwise
+// it is loaded where it is used.
+template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN, bool HAS_V2, bool LSE>
 __device__ __forceinline__ void issue(Stage<St, Pt, CPL>& s, int64_t tok, int64_t T, int d, int C, int tl,
-                                      const St* o1, const Pt* pin, const St* vprev2, const St* vprev,
-                                      int64_t plane) {
+                                      const St* o1, const float* lse1, const Pt* pin, const St* vprev2,
+                                      const St* vprev, int64_t plane) {
   const bool live = tok < T;
   const int64_t tc = live ? tok : T - 1;
   if (HAS_PIN) s.qe.load(pin, tc, plane);
+  if (HAS_V && LSE) s.lse = lse1[tc];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
     const int c0 = tl + TEAM * k;
@@ -68,7 +75,7 @@ __device__ __forceinline__ void issue(Stage<St, Pt, CPL>& s, int64_t tok, int64_
   }
 }
 
-template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN, bool HAS_V2>
+template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN, bool HAS_V2, bool LSE>
 __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok, int64_t T, int d, int C, int tl,
                                         const float* lse1, void* pout, int pfmt, int64_t plane,
                                         const float (&wq)[CPL][8], const float4* gm_lds, float eps, float inv_d,
@@ -135,14 +142,14 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
       // one exchange for both sums and the row's largest magnitude
       float pmax;
       if (TEAM == 256) {
-        const float3 r3 = block_sum2_max_256(ss, dot, amax, red[parity]);
+        const float3 r3 = block_sum2_max_256<true>(ss, dot, amax, red[parity]);
         parity ^= 1;
         r = make_float2(r3.x, r3.y);
         pmax = r3.z;
       } else {
-        r.x = wave_sum(ss);
-        r.y = wave_sum(dot);
-        pmax = wave_max(amax);
+        r.x = wave_sum_dpp(ss);
+        r.y = wave_sum_dpp(dot);
+        pmax = wave_max_dpp(amax);
       }
       const int e = q16_exponent(pmax);
       unsigned char* pb = static_cast<unsigned char*>(pout);
@@ -151,14 +158,14 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
         if (s.ok[k]) st16_nt(pb + (tok * d + (tl + TEAM * k) * 8) * 2, q16_pack(p[k], e));
       if (live && tl == 0) *reinterpret_cast<int*>(pb + plane * 2 + tok * 4) = e;
     } else if (TEAM == 256) {
-      r = block_sum2_256(ss, dot, red[parity]);
+      r = block_sum2_256<true>(ss, dot, red[parity]);
       parity ^= 1;
     } else {
-      r.x = wave_sum(ss);
-      r.y = wave_sum(dot);
+      r.x = wave_sum_dpp(ss);
+      r.y = wave_sum_dpp(dot);
     }
     const float zc = r.y / sqrtf(r.x * inv_d + eps);
-    const float lse = lse1[live ? tok : T - 1];
+    const float lse = LSE ? s.lse : lse1[live ? tok : T - 1];
     const float beta = 1.0f / (1.0f + expf(lse - zc));
 #pragma unroll
     for (int k = 0; k < CPL; ++k)
@@ -173,10 +180,10 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
   float r2 = 0.f;
   if (x_out) {
     if (TEAM == 256) {
-      r2 = block_sum2_256(sh, 0.f, red[parity]).x;
+      r2 = block_sum2_256<true>(sh, 0.f, red[parity]).x;
       parity ^= 1;
     } else {
-      r2 = wave_sum(sh);
+      r2 = wave_sum_dpp(sh);
     }
   }
   const float rinv = x_out ? 1.0f / sqrtf(r2 * inv_d + eps) : 1.f;
@@ -262,7 +269,13 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
   const int64_t step = (int64_t)gridDim.x * TPW;
   int64_t tok = (int64_t)blockIdx.x * TPW + team;
   Stage<St, Pt, CPL> A, B;
-  issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(A, tok, T, d, C, tl, o1, pin, vprev2, vprev, plane);
+  // every workgroup has one token (short token ranges)
+  const bool one = (int64_t)gridDim.x * TPW >= T;
+  if (one) {
+    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, true>(A, tok, T, d, C, tl, o1, lse1, pin, vprev2, vprev, plane);
+  } else {
+    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(A, tok, T, d, C, tl, o1, lse1, pin, vprev2, vprev, plane);
+  }
   // w (.) g, with chunks past the end of d zeroed (x 1.0 exactly without g)
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
@@ -281,22 +294,31 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
     }
   }
   lds_barrier();
-  // (the workgroup's next tokens are fetched only if it has any: at short
-  // token ranges a dead prefetch would share the compute unit's load path
-  // with the live rows and hold the wave until it returns)
+  if (one) {
+    // no prefetch (it would share the compute unit's load path with the live
+    // rows and hold the wave until it returned); the log-sum-exp came with
+    // the rows
+    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, true>(A, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq, gm_lds,
+                                                              eps, inv_d, h_out, x_out, red, parity);
+    return;
+  }
+  // The loads of a workgroup's next token are unconditional (a token past
+  // the end reads a clamped row), so the waits for the current token's rows
+  // leave them in flight.  The log-sum-exp is loaded where it is used: the
+  // wait for it then also drains the next token's rows before this token's
+  // stores, which measured 2% faster at 16K tokens than loading it with the
+  // rows.
   while (tok - team < T) {
-    if (tok + step - team < T)  // uniform over the workgroup
-      issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(B, tok + step, T, d, C, tl, o1, pin, vprev2, vprev, plane);
-    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(A, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq, gm_lds, eps,
-                                              inv_d, h_out, x_out,
-                                              red, parity);
+    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(B, tok + step, T, d, C, tl, o1, lse1, pin, vprev2, vprev,
+                                                            plane);
+    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(A, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq,
+                                                               gm_lds, eps, inv_d, h_out, x_out, red, parity);
     tok += step;
     if (tok - team >= T) break;
-    if (tok + step - team < T)
-      issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(A, tok + step, T, d, C, tl, o1, pin, vprev2, vprev, plane);
-    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2>(B, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq, gm_lds, eps,
-                                              inv_d, h_out, x_out,
-                                              red, parity);
+    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(A, tok + step, T, d, C, tl, o1, lse1, pin, vprev2, vprev,
+                                                            plane);
+    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(B, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq,
+                                                               gm_lds, eps, inv_d, h_out, x_out, red, parity);
     tok += step;
   }
 }

@@ -227,14 +227,15 @@ __device__ __forceinline__ int64_t packed_index(int kb, int m, int s4, int lane)
 // wave streams through its part of every row; within a K-block, step s4 reads
 // chunk 4*s4 + grp, so the 4 lane groups read 64 contiguous bytes of each
 // token row per instruction.
-// With PACKED, the queries come from `pk` (packed layout above) written by
+// With PACKED, the queries come from `pk` (packed layout above, for MP tiles
+// of 16, of which this pass takes tiles [m0, m0 + MT)) written by
 // k_pack_queries; otherwise w (.) g is formed and split per chunk from the
 // fp32 parameters.
-template <typename St, int MT, int G, bool PACKED, int KB = 1>
+template <typename St, int MT, int G, bool PACKED, int KB = 1, int MP = MT>
 __device__ __forceinline__ void score_pass(const St* __restrict__ src, int64_t stride, int64_t T, int d,
                                            const float* __restrict__ w, const float* __restrict__ kg,
                                            const u32x4_t* __restrict__ pk, int S, int64_t tok0, int g0,
-                                           f32x4_t (&acc)[MT][G], float (&ss)[G]) {
+                                           f32x4_t (&acc)[MT][G], float (&ss)[G], int m0 = 0) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
@@ -272,9 +273,9 @@ __device__ __forceinline__ void score_pass(const St* __restrict__ src, int64_t s
         const int c = cok ? c0 : C - 1;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const int q = m * 16 + col;
+          const int q = (m0 + m) * 16 + col;
           if (PACKED) {
-            const u32x4_t* qp = pk + packed_index<MT>(kb, m, s4, lane);
+            const u32x4_t* qp = pk + packed_index<MP>(kb, m0 + m, s4, lane);
             a[u][s4][m] = Mfma<St>::from_halves(ld16(qp), ld16(qp + 64));
           } else {
             const bool qok = cok && q < S;
@@ -452,20 +453,23 @@ __global__ __launch_bounds__(256) void k_pack_queries(const float* __restrict__ 
 
 // First kernel of the streaming pair for short and mid-sized token ranges:
 // the scores of sources [G*blockIdx.y, +G) (fewer in the last group) for a
-// 16-token tile (blockIdx.x) and up to 32 queries.  The 4 waves take
+// 16-token tile (blockIdx.x) and the query tiles [MT*blockIdx.z, +MT) of the
+// MP packed ones (splitting the query tiles over workgroups doubles the
+// workgroups of a short range and halves the packed-query bytes each one
+// streams; every score is summed exactly as without the split).  The 4 waves take
 // contiguous quarters of d (several K-blocks of loads in flight per wave),
 // their partials are added in the fixed order (w0 + w2) + (w1 + w3) through
 // LDS, and z = Z / r(u) goes to the weight slots alpha[t][q][i] of the
 // workspace; k_p1_softmax turns them into weights.  G trades parallelism
 // (workgroups) against re-reading the packed queries once per group.
-template <typename St, int MT, int G>
+template <typename St, int MT, int G, int MP>
 __device__ __forceinline__ void score_sources(const St* src, int n, int64_t stride, int64_t T, int d,
                                               const u32x4_t* pk, int S, float eps, int64_t tok0, int g0,
-                                              float* red, float* alpha) {
+                                              int m0, float* red, float* alpha) {
   constexpr int KB = G == 1 ? (MT == 1 ? 4 : 3) : (G == 2 ? 2 : 1);
   f32x4_t acc[MT][G];
   float ss[G];
-  score_pass<St, MT, G, true, KB>(src, stride, T, d, nullptr, nullptr, pk, S, tok0, g0, acc, ss);
+  score_pass<St, MT, G, true, KB, MP>(src, stride, T, d, nullptr, nullptr, pk, S, tok0, g0, acc, ss, m0);
   Red<MT, G>::reduce(red, acc, ss);
   if ((threadIdx.x >> 6) == 0) {
     const int lane = threadIdx.x & 63;
@@ -479,29 +483,30 @@ __device__ __forceinline__ void score_sources(const St* src, int n, int64_t stri
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int q = m * 16 + grp * 4 + rr;
+          const int q = (m0 + m) * 16 + grp * 4 + rr;
           if (q < S && tok < T) alpha[(tok * S + q) * n + g0 + i] = acc[m][i][rr] / r;
         }
     }
   }
 }
 
-template <typename St, int MT, int G>
+template <typename St, int MT, int G, int MP = MT>
 __global__ __launch_bounds__(256) void k_p1_scores(const St* __restrict__ src, int n, int64_t stride,
                                                    int64_t T, int d, const u32x4_t* __restrict__ pk, int S,
                                                    float eps, float* __restrict__ alpha) {
   __shared__ float red[2 * Red<MT, G>::kSlot];
   const int64_t tok0 = (int64_t)blockIdx.x * 16;
   const int g0 = blockIdx.y * G;
+  const int m0 = blockIdx.z * MT;
   const int r = n - g0 < G ? n - g0 : G;  // uniform
   if (r == G) {
-    score_sources<St, MT, G>(src, n, stride, T, d, pk, S, eps, tok0, g0, red, alpha);
+    score_sources<St, MT, G, MP>(src, n, stride, T, d, pk, S, eps, tok0, g0, m0, red, alpha);
   } else if (G > 1 && r == 1) {
-    score_sources<St, MT, 1>(src, n, stride, T, d, pk, S, eps, tok0, g0, red, alpha);
+    score_sources<St, MT, 1, MP>(src, n, stride, T, d, pk, S, eps, tok0, g0, m0, red, alpha);
   } else if (G > 2 && r == 2) {
-    score_sources<St, MT, (G > 2 ? 2 : 1)>(src, n, stride, T, d, pk, S, eps, tok0, g0, red, alpha);
+    score_sources<St, MT, (G > 2 ? 2 : 1), MP>(src, n, stride, T, d, pk, S, eps, tok0, g0, m0, red, alpha);
   } else if (G > 3 && r == 3) {
-    score_sources<St, MT, (G > 3 ? 3 : 1)>(src, n, stride, T, d, pk, S, eps, tok0, g0, red, alpha);
+    score_sources<St, MT, (G > 3 ? 3 : 1), MP>(src, n, stride, T, d, pk, S, eps, tok0, g0, m0, red, alpha);
   }
 }
 
@@ -821,14 +826,23 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
 // S >= 2, second kernel: out[q][t] = sum_i alpha[t][q][i] u_i[t] (query 0 to
 // out0, which is out itself unless the first query is redirected).  A wave owns
 // one (token, group of 64 chunks) item at a time, so the weights are
-// wave-uniform and come in through scalar loads; every source chunk is used
-// by all S queries; the next item's source chunks are loaded before the
-// current item is computed.  N is the exact number of sources.  The S output
+// wave-uniform; every source chunk is used by all S queries; the next item's
+// source chunks are loaded before the current item is computed (when the
+// wave has a next item).  N is the exact number of sources.  The S output
 // rows are written with non-temporal stores: they are read back only by the
 // phase-2 launches, long after this kernel.
-template <typename Ut, int N>
-__device__ __forceinline__ void p1_issue(Chunk<Ut> (&s)[N], bool& ok, int64_t item, int64_t items, int ngroups,
-                                         const Ut* __restrict__ src, int64_t stride, int d, int C, int lane) {
+//
+// SM: alpha holds the scores z rather than the weights, and the softmax over
+// the n sources runs here: lane q loads and normalises query q's n scores
+// with the operations of k_p1_softmax in the same order (the same weights bit
+// for bit), the loop over the queries takes each weight from that lane, and
+// the items of chunk group 0 store the statistics.  It saves the softmax
+// launch of a short token range.  Without SM the weights come in through
+// scalar loads.
+template <typename Ut, int N, bool SM>
+__device__ __forceinline__ void p1_issue(Chunk<Ut> (&s)[N], float (&z)[N], bool& ok, int64_t item, int64_t items,
+                                         int ngroups, const Ut* __restrict__ src, int64_t stride, int d, int C,
+                                         int lane, const float* __restrict__ alpha, int S) {
   const int64_t it = item < items ? item : items - 1;
   const int64_t t = it / ngroups;
   const int c0 = (int)(it - t * ngroups) * 64 + lane;
@@ -836,14 +850,36 @@ __device__ __forceinline__ void p1_issue(Chunk<Ut> (&s)[N], bool& ok, int64_t it
   const int c = ok ? c0 : C - 1;
 #pragma unroll
   for (int i = 0; i < N; ++i) s[i].load(src + (int64_t)i * stride + t * d + c * 8);
+  if (SM) {
+    const float* zr = alpha + (t * S + (lane < S ? lane : 0)) * N;
+#pragma unroll
+    for (int i = 0; i < N; ++i) z[i] = zr[i];
+  }
 }
 
-template <typename Ut, typename St, int N>
-__device__ __forceinline__ void p1_emit(const Chunk<Ut> (&s)[N], bool ok, int64_t item, int ngroups, int64_t T,
-                                        int d, int lane, const float* __restrict__ alpha, int S,
-                                        St* __restrict__ out, St* __restrict__ out0) {
+template <typename Ut, typename St, int N, bool SM>
+__device__ __forceinline__ void p1_emit(const Chunk<Ut> (&s)[N], const float (&z)[N], bool ok, int64_t item,
+                                        int ngroups, int64_t T, int d, int lane, const float* __restrict__ alpha,
+                                        int S, St* __restrict__ out, St* __restrict__ out0,
+                                        float* __restrict__ m_out, float* __restrict__ lse_out) {
   const int64_t t = item / ngroups;
-  const int c = (int)(item - t * ngroups) * 64 + lane;
+  const int g = (int)(item - t * ngroups);
+  const int c = g * 64 + lane;
+  float wt[N];
+  if (SM) {
+    float mx = z[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) mx = fmaxf(mx, z[i]);
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) l += expf(z[i] - mx);
+#pragma unroll
+    for (int i = 0; i < N; ++i) wt[i] = expf(z[i] - mx) / l;
+    if (g == 0 && lane < S) {
+      if (m_out) m_out[(int64_t)lane * T + t] = mx;
+      lse_out[(int64_t)lane * T + t] = mx + logf(l);
+    }
+  }
   float b[N][8];
 #pragma unroll
   for (int i = 0; i < N; ++i) s[i].unpack(b[i]);
@@ -853,7 +889,7 @@ __device__ __forceinline__ void p1_emit(const Chunk<Ut> (&s)[N], bool ok, int64_
     zero8(o);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const float a = al[q * N + i];
+      const float a = SM ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt[i]), q)) : al[q * N + i];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = fmaf(a, b[i][e], o[e]);
     }
@@ -861,10 +897,11 @@ __device__ __forceinline__ void p1_emit(const Chunk<Ut> (&s)[N], bool ok, int64_
   }
 }
 
-template <typename Ut, typename St, int N>
+template <typename Ut, typename St, int N, bool SM>
 __global__ __launch_bounds__(256) void k_p1_out(const Ut* __restrict__ src, int64_t stride, int64_t T, int d,
                                                 const float* __restrict__ alpha, int S, St* __restrict__ out,
-                                                St* __restrict__ out0) {
+                                                St* __restrict__ out0, float* __restrict__ m_out,
+                                                float* __restrict__ lse_out) {
   const int C = d >> 3;
   const int ngroups = (C + 63) >> 6;
   const int64_t items = T * ngroups;
@@ -872,15 +909,27 @@ __global__ __launch_bounds__(256) void k_p1_out(const Ut* __restrict__ src, int6
   const int64_t nw = (int64_t)gridDim.x * 4;
   int64_t item = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Chunk<Ut> A[N], B[N];
+  float zA[N], zB[N];
   bool okA, okB;
-  p1_issue<Ut, N>(A, okA, item, items, ngroups, src, stride, d, C, lane);
-  while (item < items) {
-    p1_issue<Ut, N>(B, okB, item + nw, items, ngroups, src, stride, d, C, lane);
-    p1_emit<Ut, St, N>(A, okA, item, ngroups, T, d, lane, alpha, S, out, out0);
+  if (item >= items) return;  // uniform over the wave
+  p1_issue<Ut, N, SM>(A, zA, okA, item, items, ngroups, src, stride, d, C, lane, alpha, S);
+  // the wave's last item has a branch of its own, so that the next item's
+  // loads are unconditional in every other step (and stay in flight across
+  // the wait for the current item's)
+  while (true) {
+    if (item + nw >= items) {
+      p1_emit<Ut, St, N, SM>(A, zA, okA, item, ngroups, T, d, lane, alpha, S, out, out0, m_out, lse_out);
+      break;
+    }
+    p1_issue<Ut, N, SM>(B, zB, okB, item + nw, items, ngroups, src, stride, d, C, lane, alpha, S);
+    p1_emit<Ut, St, N, SM>(A, zA, okA, item, ngroups, T, d, lane, alpha, S, out, out0, m_out, lse_out);
     item += nw;
-    if (item >= items) break;
-    p1_issue<Ut, N>(A, okA, item + nw, items, ngroups, src, stride, d, C, lane);
-    p1_emit<Ut, St, N>(B, okB, item, ngroups, T, d, lane, alpha, S, out, out0);
+    if (item + nw >= items) {
+      p1_emit<Ut, St, N, SM>(B, zB, okB, item, ngroups, T, d, lane, alpha, S, out, out0, m_out, lse_out);
+      break;
+    }
+    p1_issue<Ut, N, SM>(A, zA, okA, item + nw, items, ngroups, src, stride, d, C, lane, alpha, S);
+    p1_emit<Ut, St, N, SM>(B, zB, okB, item, ngroups, T, d, lane, alpha, S, out, out0, m_out, lse_out);
     item += nw;
   }
 }
@@ -1567,11 +1616,17 @@ static bool token_order(int64_t T) {
 
 constexpr size_t kMaxLds = 160 * 1024;
 
+// Whether k_p1_out has the variant with the softmax inside: its two register
+// stages of source chunks and scores must fit (not for 9-16 fp32 sources).
+template <typename Ut, int N>
+constexpr bool kFuseSoftmax = sizeof(Ut) == 2 || N <= 8;
+
 // Ut: source rows, St: outputs (the same type, or fp32 sources with bf16
 // outputs; the first query's PreNorm is only fused for equal types).
 template <typename Ut, typename St, int N>
 static hipError_t run_out(const void* src, int64_t stride, int64_t T, int d, const float* al, int S, void* out,
-                          const float* gamma0, float eps, void* x0, void* h0, hipStream_t stream) {
+                          const float* gamma0, float eps, void* x0, void* h0, float* m_out, float* lse_out,
+                          bool sm, hipStream_t stream) {
   constexpr bool kSame = std::is_same<Ut, St>::value;
   const Ut* sp = static_cast<const Ut*>(src);
   St* op = static_cast<St*>(out);
@@ -1598,8 +1653,20 @@ static hipError_t run_out(const void* src, int64_t stride, int64_t T, int d, con
       const int64_t items = T * (int64_t)(((d >> 3) + 63) >> 6);
       const int64_t wgs = (items + 3) / 4;
       const int64_t cap = (int64_t)device_cu_count() * 8;
-      hipLaunchKernelGGL((k_p1_out<Ut, St, N>), dim3((unsigned)(wgs < cap ? wgs : cap)), dim3(256), 0, stream, sp,
-                         stride, T, d, al, S, op, op0);
+      const dim3 grid((unsigned)(wgs < cap ? wgs : cap));
+      if constexpr (kFuseSoftmax<Ut, N>) {
+        if (sm) {
+          hipLaunchKernelGGL((k_p1_out<Ut, St, N, true>), grid, dim3(256), 0, stream, sp, stride, T, d, al, S, op, op0,
+                             m_out, lse_out);
+        } else {
+          hipLaunchKernelGGL((k_p1_out<Ut, St, N, false>), grid, dim3(256), 0, stream, sp, stride, T, d, al, S, op,
+                             op0, nullptr, nullptr);
+        }
+      } else {
+        if (sm) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_p1_out<Ut, St, N, false>), grid, dim3(256), 0, stream, sp, stride, T, d, al, S, op, op0,
+                           nullptr, nullptr);
+      }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !x0) return e;
@@ -1613,11 +1680,12 @@ static hipError_t run_out(const void* src, int64_t stride, int64_t T, int d, con
 
 template <typename Ut, typename St>
 static hipError_t pick_out(int n, const void* src, int64_t stride, int64_t T, int d, const float* al, int S,
-                           void* out, const float* gamma0, float eps, void* x0, void* h0, hipStream_t stream) {
+                           void* out, const float* gamma0, float eps, void* x0, void* h0, float* m_out,
+                           float* lse_out, bool sm, hipStream_t stream) {
   switch (n) {
 #define ATTNRES_CASE(N_) \
   case N_:               \
-    return run_out<Ut, St, N_>(src, stride, T, d, al, S, out, gamma0, eps, x0, h0, stream);
+    return run_out<Ut, St, N_>(src, stride, T, d, al, S, out, gamma0, eps, x0, h0, m_out, lse_out, sm, stream);
     ATTNRES_CASE(1) ATTNRES_CASE(2) ATTNRES_CASE(3) ATTNRES_CASE(4) ATTNRES_CASE(5) ATTNRES_CASE(6)
     ATTNRES_CASE(7) ATTNRES_CASE(8) ATTNRES_CASE(9) ATTNRES_CASE(10) ATTNRES_CASE(11) ATTNRES_CASE(12)
     ATTNRES_CASE(13) ATTNRES_CASE(14) ATTNRES_CASE(15) ATTNRES_CASE(16)
@@ -1666,6 +1734,7 @@ static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, i
   // scoring kernel (a stored partial in Q16 or fp32), else by the block-sum
   // kernel first
   const bool fused = nw && wide && nw->pin && (nw->pdt == kQ16 || nw->pdt == kF32);
+  bool sm = false;  // softmax inside the output kernel
   hipError_t e;
   if (nw && !fused) {
     e = launch_accumulate(nw->vdt, kind_of_type(sizeof(Ut) == 4), T, d, nw->pdt, nw->pin, nw->v2, nw->v,
@@ -1707,7 +1776,11 @@ static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, i
     const int G = tiles * ((n + 3) / 4) >= want ? 4 : (tiles * ((n + 1) / 2) >= want ? 2 : 1);
     const dim3 grid((unsigned)tiles, (unsigned)((n + G - 1) / G));
     const Ut* sp = static_cast<const Ut*>(src);
-    if (G == 4) {
+    if (MT == 2 && tiles * n < want) {
+      // still short of two workgroups per compute unit: one query tile each
+      hipLaunchKernelGGL((k_p1_scores<Ut, 1, 1, MT>), dim3((unsigned)tiles, (unsigned)n, 2u), dim3(256), 0, stream,
+                         sp, n, stride, T, d, pk, S, eps, al);
+    } else if (G == 4) {
       hipLaunchKernelGGL((k_p1_scores<Ut, MT, 4>), grid, dim3(256), 0, stream, sp, n, stride, T, d, pk, S, eps, al);
     } else if (G == 2) {
       hipLaunchKernelGGL((k_p1_scores<Ut, MT, 2>), grid, dim3(256), 0, stream, sp, n, stride, T, d, pk, S, eps, al);
@@ -1716,13 +1789,18 @@ static hipError_t run_multi(const void* src, int n, int64_t stride, int64_t T, i
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t pairs = T * S;
-    hipLaunchKernelGGL(k_p1_softmax, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, stream, pairs, n, S, T,
-                       al, m_out, lse_out);
+    // the softmax runs inside the output kernel when that is k_p1_out (short
+    // ranges with outputs), else as a launch of its own
+    sm = out != nullptr && !token_order(T) && (sizeof(Ut) == 2 || n <= 8);
+    if (!sm) {
+      const int64_t pairs = T * S;
+      hipLaunchKernelGGL(k_p1_softmax, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, stream, pairs, n, S, T,
+                         al, m_out, lse_out);
+    }
   }
   e = hipGetLastError();
   if (e != hipSuccess || (out == nullptr && x0 == nullptr)) return e;  // statistics only
-  return pick_out<Ut, St>(n, src, stride, T, d, al, S, out, gamma0, eps, x0, h0, stream);
+  return pick_out<Ut, St>(n, src, stride, T, d, al, S, out, gamma0, eps, x0, h0, m_out, lse_out, sm, stream);
 }
 
 hipError_t launch_phase1_multi(Dtype dt, Dtype sdt, const void* src, int n, int64_t stride, int64_t T, int d,
