@@ -312,23 +312,34 @@ def test_block_runs_are_bitwise_deterministic():
         assert torch.equal(a, b)
 
 
-def test_token_split_invariance():
-    """Tokens never interact: one call over T tokens equals calls over slices."""
-    _say("case token split invariance")
+@pytest.mark.parametrize("T,d,cut", [(1000, 7168, 333), (3000, 1024, 1500)])
+def test_token_split_invariance(T, d, cut):
+    """Tokens never interact: one call over T tokens equals calls over slices,
+    every sublayer input and the final output bit for bit.  The slices are
+    short enough for the merge's one-token-per-team path, the whole range
+    takes its persistent loop (256-thread teams at d = 7168, 64-thread teams
+    at d = 1024)."""
+    _say("case token split invariance T=%d d=%d" % (T, d))
     dev = torch.device("cuda")
-    w = synth.scaled(synth.WORKLOADS["prefill_chunk_bf16"], T=1000, block_sizes=(5, 7), name="split")
+    w = synth.scaled(synth.WORKLOADS["prefill_chunk_bf16"], T=T, d=d, block_sizes=(5, 7), name="split")
     from harness import block_inputs
     emb, given, v = block_inputs(w, dev)
     prm = synth.params(w, dev)
-    st = tdw.BlockAttnRes(w.T, w.d, w.block_sizes, w.torch_dtype, device=dev)
-    st.reps[0].copy_(emb)
-    st.forward(prm, lambda l, x: v[l])
-    whole = st.h_final.clone()
-    for a, b in ((0, 333), (333, 1000)):
-        s2 = tdw.BlockAttnRes(b - a, w.d, w.block_sizes, w.torch_dtype, device=dev)
-        s2.reps[0].copy_(emb[a:b])
-        s2.forward(prm, lambda l, x: v[l][a:b].contiguous())
-        assert torch.equal(s2.h_final, whole[a:b])
+
+    def run(a, b):
+        st = tdw.BlockAttnRes(b - a, w.d, w.block_sizes, w.torch_dtype, device=dev)
+        st.reps[0].copy_(emb[a:b])
+        xs = []
+        st.forward(prm, lambda l, x: v[l][a:b].contiguous(), hook=lambda site, x, **k: xs.append(x.clone()))
+        return st.h_final.clone(), xs
+
+    whole, xw = run(0, T)
+    for a, b in ((0, cut), (cut, T)):
+        h, xs = run(a, b)
+        assert torch.equal(h, whole[a:b]), (a, b)
+        assert len(xs) == len(xw)
+        for site, (x, y) in enumerate(zip(xs, xw)):
+            assert torch.equal(x, y[a:b]), (a, b, site)
 
 
 def test_token_permutation_equivariance():

@@ -51,17 +51,17 @@ constexpr int kPoutF32 = 0, kPoutP24 = 1, kPoutQ16 = 2;
 
 // Loads of one token for the team.  Every load is unconditional (an
 // out-of-range token or chunk reads a clamped valid address and is zeroed
-// when used), so the loads of a stage issue back to back.  LSE: the token's
-// phase-1 log-sum-exp comes with them (a workgroup's only token); otherwise
-// it is loaded where it is used.
-template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN, bool HAS_V2, bool LSE>
+// when used), so the loads of a stage issue back to back.  ONE (the team's
+// only token): the token's phase-1 log-sum-exp comes with them; otherwise it
+// is loaded where it is used.
+template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN, bool HAS_V2, bool ONE>
 __device__ __forceinline__ void issue(Stage<St, Pt, CPL>& s, int64_t tok, int64_t T, int d, int C, int tl,
                                       const St* o1, const float* lse1, const Pt* pin, const St* vprev2,
                                       const St* vprev, int64_t plane) {
   const bool live = tok < T;
   const int64_t tc = live ? tok : T - 1;
   if (HAS_PIN) s.qe.load(pin, tc, plane);
-  if (HAS_V && LSE) s.lse = lse1[tc];
+  if (HAS_V && ONE) s.lse = lse1[tc];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
     const int c0 = tl + TEAM * k;
@@ -75,11 +75,14 @@ __device__ __forceinline__ void issue(Stage<St, Pt, CPL>& s, int64_t tok, int64_
   }
 }
 
-template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN, bool HAS_V2, bool LSE>
+// ONE: the log-sum-exp is in the stage and the PreNorm gain of the thread's
+// chunks in gg (else the gain is read from LDS).
+template <typename St, typename Pt, int TEAM, int CPL, bool HAS_V, bool HAS_PIN, bool HAS_V2, bool ONE>
 __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok, int64_t T, int d, int C, int tl,
                                         const float* lse1, void* pout, int pfmt, int64_t plane,
-                                        const float (&wq)[CPL][8], const float4* gm_lds, float eps, float inv_d,
-                                        St* h_out, St* x_out, float (*red)[12], int& parity) {
+                                        const float (&wq)[CPL][8], const float4* gm_lds,
+                                        const float (&gg)[CPL][8], float eps, float inv_d, St* h_out, St* x_out,
+                                        float (*red)[12], int& parity) {
   const bool live = tok < T;
   // a Q16 partial is stored after the row's largest magnitude is known
   const bool q16 = pout && pfmt == kPoutQ16;
@@ -165,7 +168,7 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
       r.y = wave_sum_dpp(dot);
     }
     const float zc = r.y / sqrtf(r.x * inv_d + eps);
-    const float lse = LSE ? s.lse : lse1[live ? tok : T - 1];
+    const float lse = ONE ? s.lse : lse1[live ? tok : T - 1];
     const float beta = 1.0f / (1.0f + expf(lse - zc));
 #pragma unroll
     for (int k = 0; k < CPL; ++k)
@@ -193,8 +196,15 @@ __device__ __forceinline__ void process(const Stage<St, Pt, CPL>& s, int64_t tok
       const int64_t off = tok * d + (tl + TEAM * k) * 8;
       if (h_out) out8_nt(h_out + off, h[k]);
       if (x_out) {
-        const float4 g0 = gm_lds[2 * (tl + TEAM * k)], g1 = gm_lds[2 * (tl + TEAM * k) + 1];
-        const float gk[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        float gk[8];
+        if (ONE) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gk[e] = gg[k][e];
+        } else {
+          const float4 g0 = gm_lds[2 * (tl + TEAM * k)], g1 = gm_lds[2 * (tl + TEAM * k) + 1];
+          gk[0] = g0.x, gk[1] = g0.y, gk[2] = g0.z, gk[3] = g0.w;
+          gk[4] = g1.x, gk[5] = g1.y, gk[6] = g1.z, gk[7] = g1.w;
+        }
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = gk[e] * (h[k][e] * rinv);
@@ -222,6 +232,48 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
   const int tl = threadIdx.x % TEAM;
   const int C = d >> 3;
   const float inv_d = 1.0f / (float)d;
+  int parity = 0;
+  const int64_t step = (int64_t)gridDim.x * TPW;
+  int64_t tok = (int64_t)blockIdx.x * TPW + team;
+  if (step >= T) {
+    // Every team has one token (short token ranges): its rows and phase-1
+    // log-sum-exp are loaded first, then the parameters of the thread's own
+    // chunks (the PreNorm gain too, kept in registers), with no prefetch
+    // (which would share the compute unit's load path with the live rows)
+    // and no barrier before the first reduction.  The arithmetic is that of
+    // the persistent path below, so results do not depend on the path.
+    Stage<St, Pt, CPL> A;
+    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, true>(A, tok, T, d, C, tl, o1, lse1, pin, vprev2, vprev, plane);
+    float wq[CPL][8], gg[CPL][8];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int c0 = tl + TEAM * k;
+      const int c = c0 < C ? c0 : C - 1;
+      if (HAS_V) {
+        load8(w + c * 8, wq[k]);
+        float gq[8];
+        if (kg) {
+          load8(kg + c * 8, gq);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gq[e] = 1.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wq[k][e] = c0 < C ? wq[k][e] * gq[e] : 0.f;
+      } else {
+        zero8(wq[k]);
+      }
+      if (x_out && gamma) {
+        load8(gamma + c * 8, gg[k]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gg[k][e] = 1.f;
+      }
+    }
+    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, true>(A, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq, gm_lds,
+                                                              gg, eps, inv_d, h_out, x_out, red, parity);
+    return;
+  }
   // Prologue, ordered so that nothing waits before the first token's rows
   // are in flight: the parameter loads (clamped, unconditional), then the
   // first token's loads, then the LDS stores of gamma (which wait for gamma
@@ -265,17 +317,8 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
       }
     }
   }
-  int parity = 0;
-  const int64_t step = (int64_t)gridDim.x * TPW;
-  int64_t tok = (int64_t)blockIdx.x * TPW + team;
   Stage<St, Pt, CPL> A, B;
-  // every workgroup has one token (short token ranges)
-  const bool one = (int64_t)gridDim.x * TPW >= T;
-  if (one) {
-    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, true>(A, tok, T, d, C, tl, o1, lse1, pin, vprev2, vprev, plane);
-  } else {
-    issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(A, tok, T, d, C, tl, o1, lse1, pin, vprev2, vprev, plane);
-  }
+  issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(A, tok, T, d, C, tl, o1, lse1, pin, vprev2, vprev, plane);
   // w (.) g, with chunks past the end of d zeroed (x 1.0 exactly without g)
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
@@ -294,14 +337,6 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
     }
   }
   lds_barrier();
-  if (one) {
-    // no prefetch (it would share the compute unit's load path with the live
-    // rows and hold the wave until it returned); the log-sum-exp came with
-    // the rows
-    process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, true>(A, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq, gm_lds,
-                                                              eps, inv_d, h_out, x_out, red, parity);
-    return;
-  }
   // The loads of a workgroup's next token are unconditional (a token past
   // the end reads a clamped row), so the waits for the current token's rows
   // leave them in flight.  The log-sum-exp is loaded where it is used: the
@@ -312,13 +347,13 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
     issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(B, tok + step, T, d, C, tl, o1, lse1, pin, vprev2, vprev,
                                                             plane);
     process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(A, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq,
-                                                               gm_lds, eps, inv_d, h_out, x_out, red, parity);
+                                                               gm_lds, wq, eps, inv_d, h_out, x_out, red, parity);
     tok += step;
     if (tok - team >= T) break;
     issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(A, tok + step, T, d, C, tl, o1, lse1, pin, vprev2, vprev,
                                                             plane);
     process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(B, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq,
-                                                               gm_lds, eps, inv_d, h_out, x_out, red, parity);
+                                                               gm_lds, wq, eps, inv_d, h_out, x_out, red, parity);
     tok += step;
   }
 }
