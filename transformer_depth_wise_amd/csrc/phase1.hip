@@ -1030,7 +1030,14 @@ __global__ __launch_bounds__(256) void k_p1_out_tokens(const Ut* __restrict__ sr
     }
   };
   advance(tn, gn);
-  float ss = 0.f;
+  // |o_0|^2 in the order of the merge kernel's PreNorm, so that x_0 is the
+  // same bits whichever path forms it: rows of at most 256 chunks (a wave per
+  // token there) in one lane sum over the lane's chunks; wider rows (a
+  // 256-thread team there, thread t holding chunks t, t + 256, ...) in four
+  // sums by chunk group modulo 4, added as (s0 + s1) + (s2 + s3) after the
+  // lane reductions
+  const bool wide_row = C > 256;  // uniform
+  float ss0 = 0.f, ss1 = 0.f, ss2 = 0.f, ss3 = 0.f;
 
   auto emit = [&](const Chunk<Ut>(&s)[N], int64_t tok, int grp) {
     const int c = grp * 64 + lane;
@@ -1052,8 +1059,9 @@ __global__ __launch_bounds__(256) void k_p1_out_tokens(const Ut* __restrict__ sr
       float r[8];
       FirstSlot<St>::put(mine + (size_t)c * kW, o, r);
       if (ok) {
+        float& acc = (!wide_row || (grp & 3) == 0) ? ss0 : (grp & 3) == 1 ? ss1 : (grp & 3) == 2 ? ss2 : ss3;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(r[e], r[e], ss);
+        for (int e = 0; e < 8; ++e) acc = fmaf(r[e], r[e], acc);
         if (h0) out8(h0 + tok * d + c * 8, o);
       }
       q = 1;
@@ -1072,8 +1080,9 @@ __global__ __launch_bounds__(256) void k_p1_out_tokens(const Ut* __restrict__ sr
     }
     if (FIRST && grp == ngroups - 1) {
       // the token's last group: PreNorm of o_0 from the wave's LDS copy
-      const float tot = wave_sum_dpp(ss);
-      ss = 0.f;
+      const float tot = wide_row ? (wave_sum_dpp(ss0) + wave_sum_dpp(ss1)) + (wave_sum_dpp(ss2) + wave_sum_dpp(ss3))
+                                 : wave_sum_dpp(ss0);
+      ss0 = ss1 = ss2 = ss3 = 0.f;
       const float rinv = 1.0f / sqrtf(tot * (1.0f / (float)d) + eps);
 #pragma unroll 2
       for (int gg = 0; gg < ngroups; ++gg) {
