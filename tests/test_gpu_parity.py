@@ -491,6 +491,11 @@ FIRST = [
     (None, 8192, 1, 4, "f32", False),      # one source: out may be NULL
     (37, 1032, 3, 4, "bf16", True),        # short range: item-order kernel + PreNorm launch
     (37, 64, 1, 3, "f32", True),           # short range, one source
+    # short ranges, rows over 256 chunks: a workgroup per token with the PreNorm inside
+    (37, 7168, 8, 24, "bf16", True),       # the decode step's shape
+    (300, 4104, 3, 20, "bf16", False),     # ragged last chunk group (9 groups, the last of one chunk)
+    (37, 2056, 4, 5, "f32", True),         # 257 chunks: 5 groups
+    (200, 7168, 16, 24, "bf16", False),    # 16 sources
 ]
 
 

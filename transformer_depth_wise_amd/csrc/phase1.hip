@@ -1116,6 +1116,134 @@ __global__ __launch_bounds__(256) void k_p1_out_tokens(const Ut* __restrict__ sr
   }
 }
 
+// Short token ranges with the first sublayer's PreNorm, rows of more than
+// 256 chunks: a workgroup per token (persistent over tokens), wave w taking
+// the chunk groups w, w + 4, w + 8, ...  Those are exactly the chunks of the
+// merge kernel's wave w for such rows (its 256-thread team gives thread t
+// the chunks t, t + 256, ...), so |o_0|^2 is summed in the merge's order (a
+// lane sum in chunk order, the DPP wave sum, then (w0 + w1) + (w2 + w3)) and
+// x_0 has the bits of phase 1 followed by the merge launch that this kernel
+// replaces.  alpha holds the scores; the softmax runs here as in k_p1_out's
+// SM variant (the same weights bit for bit) and wave 0 stores the
+// statistics.  o_0 is rounded to the storage type and kept in LDS until the
+// row's sum is known; slab 0 of out is not written.
+template <typename Ut, typename St, int N>
+__global__ __launch_bounds__(256) void k_p1_out_wg(const Ut* __restrict__ src, int64_t stride, int64_t T, int d,
+                                                   const float* __restrict__ alpha, int S, St* __restrict__ out,
+                                                   const float* __restrict__ gamma0, float eps, St* __restrict__ x0,
+                                                   St* __restrict__ h0, float* __restrict__ m_out,
+                                                   float* __restrict__ lse_out) {
+  extern __shared__ u32x4_t wg_lds[];  // o_0 of the token, kW words per chunk
+  __shared__ float red[4];
+  constexpr int kW = FirstSlot<St>::kWords;
+  const int C = d >> 3;
+  const int ngroups = (C + 63) >> 6;  // at least 5 here
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const float inv_d = 1.0f / (float)d;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    // the token's weights: lane q normalises query q's scores
+    float z[N], wt[N];
+    {
+      const float* zr = alpha + (t * S + (lane < S ? lane : 0)) * N;
+#pragma unroll
+      for (int i = 0; i < N; ++i) z[i] = zr[i];
+    }
+    Chunk<Ut> A[N], B[N];
+    int g = wave;
+    p1_issue_tok<Ut, N>(A, t, g, T, src, stride, d, C, lane);
+    {
+      float mx = z[0];
+#pragma unroll
+      for (int i = 1; i < N; ++i) mx = fmaxf(mx, z[i]);
+      float l = 0.f;
+#pragma unroll
+      for (int i = 0; i < N; ++i) l += expf(z[i] - mx);
+#pragma unroll
+      for (int i = 0; i < N; ++i) wt[i] = expf(z[i] - mx) / l;
+      if (wave == 0 && lane < S) {
+        if (m_out) m_out[(int64_t)lane * T + t] = mx;
+        lse_out[(int64_t)lane * T + t] = mx + logf(l);
+      }
+    }
+    float ss = 0.f;
+    auto emit = [&](const Chunk<Ut>(&s)[N], int grp) {
+      const int c = grp * 64 + lane;
+      const bool ok = c < C;
+      float b[N][8];
+#pragma unroll
+      for (int i = 0; i < N; ++i) s[i].unpack(b[i]);
+      {
+        float o[8], r[8];
+        zero8(o);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt[i]), 0));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = fmaf(a, b[i][e], o[e]);
+        }
+        if (ok) {
+          FirstSlot<St>::put(wg_lds + (size_t)c * kW, o, r);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = fmaf(r[e], r[e], ss);
+          if (h0) out8(h0 + t * d + c * 8, o);
+        }
+      }
+      for (int q = 1; q < S; ++q) {
+        float o[8];
+        zero8(o);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt[i]), q));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = fmaf(a, b[i][e], o[e]);
+        }
+        if (ok) out8_nt(out + ((int64_t)q * T + t) * d + c * 8, o);
+      }
+    };
+    // the wave's last group has a branch of its own, so that the next
+    // group's loads are unconditional in every other step
+    while (true) {
+      if (g + 4 >= ngroups) {
+        emit(A, g);
+        break;
+      }
+      p1_issue_tok<Ut, N>(B, t, g + 4, T, src, stride, d, C, lane);
+      emit(A, g);
+      g += 4;
+      if (g + 4 >= ngroups) {
+        emit(B, g);
+        break;
+      }
+      p1_issue_tok<Ut, N>(A, t, g + 4, T, src, stride, d, C, lane);
+      emit(B, g);
+      g += 4;
+    }
+    const float ws = wave_sum_dpp(ss);
+    if (lane == 0) red[wave] = ws;
+    lds_barrier();
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const float rinv = 1.0f / sqrtf(tot * inv_d + eps);
+    for (int gg = wave; gg < ngroups; gg += 4) {
+      const int cc = gg * 64 + lane;
+      if (cc < C) {
+        float o[8], gm[8], x[8];
+        FirstSlot<St>::get(wg_lds + (size_t)cc * kW, o);
+        if (gamma0) {
+          load8(gamma0 + cc * 8, gm);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gm[e] = 1.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = gm[e] * (o[e] * rinv);
+        out8(x0 + t * d + cc * 8, x);
+      }
+    }
+    lds_barrier();  // the next token rewrites red and the copy of o_0
+  }
+}
+
 // ---------------------------------------------------------------------------
 // S == 1: one query, up to 32 sources, optional PreNorm of the output (Full
 // AttnRes sites and the final aggregation without a workspace) for rows of
@@ -1650,6 +1778,20 @@ static hipError_t run_out(const void* src, int64_t stride, int64_t T, int d, con
     hipLaunchKernelGGL(k, tgrid, dim3(256), lds, stream, sp, stride, T, d, al, S, op, gamma0, eps,
                        static_cast<St*>(x0), static_cast<St*>(h0));
     return hipGetLastError();
+  }
+  if constexpr (kSame && kFuseSoftmax<Ut, N>) {
+    if (x0 && sm && op && (d >> 3) > 256) {
+      // short range, wide rows: a workgroup per token with the softmax and
+      // the first sublayer's PreNorm inside
+      const size_t lds = (size_t)(d >> 3) * FirstSlot<St>::kWords * sizeof(u32x4_t);
+      auto k = k_p1_out_wg<Ut, St, N>;
+      hipError_t e = set_lds(k, lds, lds + 64);  // + the static reduction slots
+      if (e != hipSuccess) return e;
+      const int64_t cap = (int64_t)device_cu_count() * 4;
+      hipLaunchKernelGGL(k, dim3((unsigned)(T < cap ? T : cap)), dim3(256), lds, stream, sp, stride, T, d, al, S, op,
+                         gamma0, eps, static_cast<St*>(x0), static_cast<St*>(h0), m_out, lse_out);
+      return hipGetLastError();
+    }
   }
   // query 0 goes to h0 when the first sublayer's PreNorm follows in a second
   // launch and h0 is wanted (else to slab 0 of out, used as scratch)
