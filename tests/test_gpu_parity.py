@@ -178,11 +178,17 @@ def test_block_edge_shapes(T, d, blocks, n_given, dt):
     (29, 2048, 31, "bf16"),   # four chunks per lane, 32 sources: batches of two
     (21, 1544, 10, "f32"),    # fp32, four chunks per lane, batches of one
     (40, 1032, 7, "f32"),     # fp32, two chunks per lane, ragged last batch
-    (17, 2056, 5, "bf16"),    # widest row past the one-pass kernel: the tile kernel
+    (17, 2056, 5, "bf16"),    # 257 chunks: the 512-thread one-pass kernel, one chunk per thread
+    (23, 4096, 9, "bf16"),    # 512 chunks, the widest with one chunk per thread
+    (19, 4096, 17, "f32"),    # the same in fp32, 17 sources
+    (11, 4104, 6, "bf16"),    # 513 chunks: two chunks per thread
+    (7, 16384, 3, "bf16"),    # 2048 chunks, the widest row: four chunks per thread
 ])
 def test_full_edge_shapes(T, d, L, dt):
-    """One-shot sites over the row widths and source counts of both site
-    kernels (one pass for rows of <= 256 chunks, the tile kernel beyond)."""
+    """One-shot sites over the row widths and source counts of the site
+    kernels (one pass with a wave per token for rows of <= 256 chunks, one
+    pass with a 512-thread workgroup per token up to the 2048 chunks of the
+    widest row)."""
     base = synth.WORKLOADS["full_bf16"]
     w = synth.scaled(base, name="full_edge", T=T, d=d, block_sizes=(1,) * L, seed=777 + L + d, dtype=dt)
     _say("case full_edge T=%d d=%d L=%d %s" % (T, d, L, dt))

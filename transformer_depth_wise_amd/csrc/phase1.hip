@@ -227,15 +227,12 @@ __device__ __forceinline__ int64_t packed_index(int kb, int m, int s4, int lane)
 // wave streams through its part of every row; within a K-block, step s4 reads
 // chunk 4*s4 + grp, so the 4 lane groups read 64 contiguous bytes of each
 // token row per instruction.
-// With PACKED, the queries come from `pk` (packed layout above, for MP tiles
-// of 16, of which this pass takes tiles [m0, m0 + MT)) written by
-// k_pack_queries; otherwise w (.) g is formed and split per chunk from the
-// fp32 parameters.
-template <typename St, int MT, int G, bool PACKED, int KB = 1, int MP = MT>
+// The queries come from `pk` (packed layout above, for MP tiles of 16, of
+// which this pass takes tiles [m0, m0 + MT)) written by k_pack_queries.
+template <typename St, int MT, int G, int KB, int MP>
 __device__ __forceinline__ void score_pass(const St* __restrict__ src, int64_t stride, int64_t T, int d,
-                                           const float* __restrict__ w, const float* __restrict__ kg,
-                                           const u32x4_t* __restrict__ pk, int S, int64_t tok0, int g0,
-                                           f32x4_t (&acc)[MT][G], float (&ss)[G], int m0 = 0) {
+                                           const u32x4_t* __restrict__ pk, int64_t tok0, int g0,
+                                           f32x4_t (&acc)[MT][G], float (&ss)[G], int m0) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
@@ -273,29 +270,8 @@ __device__ __forceinline__ void score_pass(const St* __restrict__ src, int64_t s
         const int c = cok ? c0 : C - 1;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const int q = (m0 + m) * 16 + col;
-          if (PACKED) {
-            const u32x4_t* qp = pk + packed_index<MP>(kb, m0 + m, s4, lane);
-            a[u][s4][m] = Mfma<St>::from_halves(ld16(qp), ld16(qp + 64));
-          } else {
-            const bool qok = cok && q < S;
-            const int qc = q < S ? q : 0;
-            float qv[8];
-            const u32x4_t w0 = sel16(qok, ld16(w + (int64_t)qc * d + c * 8));
-            const u32x4_t w1 = sel16(qok, ld16(w + (int64_t)qc * d + c * 8 + 4));
-            qv[0] = __uint_as_float(w0.x); qv[1] = __uint_as_float(w0.y); qv[2] = __uint_as_float(w0.z);
-            qv[3] = __uint_as_float(w0.w); qv[4] = __uint_as_float(w1.x); qv[5] = __uint_as_float(w1.y);
-            qv[6] = __uint_as_float(w1.z); qv[7] = __uint_as_float(w1.w);
-            if (kg) {
-              const u32x4_t g0v = ld16(kg + (int64_t)qc * d + c * 8);
-              const u32x4_t g1v = ld16(kg + (int64_t)qc * d + c * 8 + 4);
-              qv[0] *= __uint_as_float(g0v.x); qv[1] *= __uint_as_float(g0v.y);
-              qv[2] *= __uint_as_float(g0v.z); qv[3] *= __uint_as_float(g0v.w);
-              qv[4] *= __uint_as_float(g1v.x); qv[5] *= __uint_as_float(g1v.y);
-              qv[6] *= __uint_as_float(g1v.z); qv[7] *= __uint_as_float(g1v.w);
-            }
-            a[u][s4][m] = Mfma<St>::make_a(qv);
-          }
+          const u32x4_t* qp = pk + packed_index<MP>(kb, m0 + m, s4, lane);
+          a[u][s4][m] = Mfma<St>::from_halves(ld16(qp), ld16(qp + 64));
         }
 #pragma unroll
         for (int i = 0; i < G; ++i) b[u][s4][i] = Mfma<St>::load_b(base[i] + c * 8, cok && tok_ok);
@@ -368,56 +344,6 @@ struct Red {
   }
 };
 
-constexpr int kGroup = 4;  // sources scored per pass over the channels
-
-// One pass of part A for sources [g0, g0+G) followed by the fixed-order
-// reduction; wave 0 then stores z = Z / r(u) into zb[(t * QP + q) * np + i]
-// (ONEQ: only query 0, zb[t * np + i]).
-template <typename St, int MT, int G, bool PACKED, bool ONEQ>
-__device__ __forceinline__ void score_group(const St* src, int64_t stride, int64_t T, int d, const float* w,
-                                            const float* kg, const u32x4_t* pk, int S, float eps, int64_t tok0,
-                                            int g0, float* red, float* zb, int np) {
-  constexpr int QP = 16 * MT;
-  f32x4_t acc[MT][G];
-  float ss[G];
-  score_pass<St, MT, G, PACKED>(src, stride, T, d, w, kg, pk, S, tok0, g0, acc, ss);
-  Red<MT, G>::reduce(red, acc, ss);
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  if ((threadIdx.x >> 6) == 0) {
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const float r = sqrtf(ss[i] / (float)d + eps);
-      if (ONEQ) {
-        if (grp == 0) zb[col * np + g0 + i] = acc[0][i][0] / r;  // row 0 of the MFMA output
-      } else {
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int q = m * 16 + grp * 4 + rr;
-            zb[(col * QP + q) * np + g0 + i] = acc[m][i][rr] / r;
-          }
-      }
-    }
-  }
-}
-
-// All n sources: full groups of kGroup, then one remainder group.
-template <typename St, int MT, bool PACKED, bool ONEQ>
-__device__ __forceinline__ void score_all(const St* src, int n, int64_t stride, int64_t T, int d, const float* w,
-                                          const float* kg, const u32x4_t* pk, int S, float eps, int64_t tok0,
-                                          float* red, float* zb, int np) {
-  int g0 = 0;
-  for (; g0 + kGroup <= n; g0 += kGroup)
-    score_group<St, MT, kGroup, PACKED, ONEQ>(src, stride, T, d, w, kg, pk, S, eps, tok0, g0, red, zb, np);
-  const int r = n - g0;
-  if (r == 1) score_group<St, MT, 1, PACKED, ONEQ>(src, stride, T, d, w, kg, pk, S, eps, tok0, g0, red, zb, np);
-  if (r == 2) score_group<St, MT, 2, PACKED, ONEQ>(src, stride, T, d, w, kg, pk, S, eps, tok0, g0, red, zb, np);
-  if (r == 3) score_group<St, MT, 3, PACKED, ONEQ>(src, stride, T, d, w, kg, pk, S, eps, tok0, g0, red, zb, np);
-}
-
 // ---------------------------------------------------------------------------
 // Prologue of the streaming pair: pack the tile's queries w (.) g once per
 // call into matrix-core operands (layout above).  One thread per (K-block,
@@ -469,7 +395,7 @@ __device__ __forceinline__ void score_sources(const St* src, int n, int64_t stri
   constexpr int KB = G == 1 ? (MT == 1 ? 4 : 3) : (G == 2 ? 2 : 1);
   f32x4_t acc[MT][G];
   float ss[G];
-  score_pass<St, MT, G, true, KB, MP>(src, stride, T, d, nullptr, nullptr, pk, S, tok0, g0, acc, ss, m0);
+  score_pass<St, MT, G, KB, MP>(src, stride, T, d, pk, tok0, g0, acc, ss, m0);
   Red<MT, G>::reduce(red, acc, ss);
   if ((threadIdx.x >> 6) == 0) {
     const int lane = threadIdx.x & 63;
@@ -1245,116 +1171,6 @@ __global__ __launch_bounds__(256) void k_p1_out_wg(const Ut* __restrict__ src, i
 }
 
 // ---------------------------------------------------------------------------
-// S == 1: one query, up to 32 sources, optional PreNorm of the output (Full
-// AttnRes sites and the final aggregation without a workspace) for rows of
-// more than 256 chunks.  Part A scores a 16-token tile on the matrix cores;
-// part B walks the tile's tokens with the whole workgroup (the PreNorm needs
-// each token's full row).
-constexpr int kSingleNP = 32;
-
-template <typename St>
-__global__ __launch_bounds__(256) void k_phase1_single(const St* __restrict__ src, int n, int64_t stride,
-                                                       int64_t T, int d, const float* __restrict__ w,
-                                                       const float* __restrict__ kg,
-                                                       const float* __restrict__ gamma, float eps,
-                                                       St* __restrict__ h_out, St* __restrict__ x_out,
-                                                       float* __restrict__ m_out,
-                                                       float* __restrict__ lse_out) {
-  extern __shared__ float lds[];
-  float* red = lds;
-  float* zb = lds + 2 * Red<1, kGroup>::kSlot;  // [16 tokens][kSingleNP sources]
-  float* red2 = zb + 16 * kSingleNP;             // 2 x 8 floats for the PreNorm reduction
-  const int64_t tok0 = (int64_t)blockIdx.x * 16;
-  score_all<St, 1, false, true>(src, n, stride, T, d, w, kg, nullptr, 1, eps, tok0, red, zb, kSingleNP);
-  lds_barrier();
-  if (threadIdx.x < 16) {
-    float* row = zb + threadIdx.x * kSingleNP;
-    float mx = row[0];
-    for (int i = 1; i < n; ++i) mx = fmaxf(mx, row[i]);
-    float l = 0.f;
-    for (int i = 0; i < n; ++i) {
-      const float e = expf(row[i] - mx);
-      row[i] = e;
-      l += e;
-    }
-    for (int i = 0; i < n; ++i) row[i] = row[i] / l;
-    const int64_t tok = tok0 + threadIdx.x;
-    if (tok < T) {
-      if (m_out) m_out[tok] = mx;
-      if (lse_out) lse_out[tok] = mx + logf(l);
-    }
-  }
-  lds_barrier();
-  if (!h_out && !x_out) return;  // statistics only (uniform)
-
-  const int C = d >> 3;
-  const int ntile = (int)((T - tok0) < 16 ? (T - tok0) : 16);
-  int parity = 0;
-  for (int t = 0; t < ntile; ++t) {
-    const int64_t tok = tok0 + t;
-    const float* al = zb + t * kSingleNP;
-    float h[8][8];
-    float ssq = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = threadIdx.x + 256 * k;
-      zero8(h[k]);
-      if (c < C) {
-        const St* base = src + tok * d + c * 8;
-        int i = 0;
-        for (; i + 4 <= n; i += 4) {
-          float u0[8], u1[8], u2[8], u3[8];
-          load8(base + (int64_t)(i + 0) * stride, u0);
-          load8(base + (int64_t)(i + 1) * stride, u1);
-          load8(base + (int64_t)(i + 2) * stride, u2);
-          load8(base + (int64_t)(i + 3) * stride, u3);
-          const float a0 = al[i], a1 = al[i + 1], a2 = al[i + 2], a3 = al[i + 3];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            h[k][e] = fmaf(a0, u0[e], h[k][e]);
-            h[k][e] = fmaf(a1, u1[e], h[k][e]);
-            h[k][e] = fmaf(a2, u2[e], h[k][e]);
-            h[k][e] = fmaf(a3, u3[e], h[k][e]);
-          }
-        }
-        for (; i < n; ++i) {
-          float u[8];
-          load8(base + (int64_t)i * stride, u);
-          const float a = al[i];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) h[k][e] = fmaf(a, u[e], h[k][e]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ssq = fmaf(h[k][e], h[k][e], ssq);
-        if (h_out) store8(h_out + tok * d + c * 8, h[k]);
-      }
-    }
-    if (x_out) {
-      const float2 tot = block_sum2_256(ssq, 0.f, red2 + 8 * parity);
-      parity ^= 1;
-      const float rinv = 1.0f / sqrtf(tot.x / (float)d + eps);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int c = threadIdx.x + 256 * k;
-        if (c < C) {
-          float gm[8];
-          if (gamma) {
-            load8(gamma + c * 8, gm);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) gm[e] = 1.f;
-          }
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = gm[e] * (h[k][e] * rinv);
-          store8(x_out + tok * d + c * 8, x);
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // S == 1 with rows of at most 256 chunks (Full AttnRes one-shot sites, the
 // final aggregation without a workspace): one pass over the sources with an
 // online softmax, so every source row is read once.  A wave owns one token at
@@ -1532,7 +1348,12 @@ __global__ __launch_bounds__(256) void k_site_online(const St* __restrict__ src,
 // rows are read once, with non-temporal loads.  One source per batch, two
 // stages and four workgroups per CU took the 16K chunk's final site (9
 // sources, d = 7168) from 0.63 to 0.49 ms on an MI355X; batches of 3 or 4
-// sources, or 3 to 6 stages, were slower in the same run.
+// sources, or 3 to 6 stages, were slower in the same run.  Rows of at most
+// 512 chunks take one chunk per thread (with two, every second load was a
+// clamped duplicate) and three stages: 16384 tokens at d = 4096 with 17
+// sources in 0.70-0.72 ms instead of 0.88-0.90 (9 sources 0.44 instead of
+// 0.53); batches of two sources were 5% faster at 17 sources but 40% slower
+// at one.
 constexpr int kTeam = 512;
 
 template <typename St, int CPT, int BS, int DEPTH>
@@ -1988,7 +1809,9 @@ static hipError_t run_single(const void* src, int n, int64_t stride, int64_t T, 
   }
   if (C <= 4 * kTeam) {
     // the same one pass, a 512-thread workgroup per token
-    auto k = C <= 2 * kTeam ? k_site_team<St, 2, 1, 2> : k_site_team<St, 4, 1, 2>;
+    auto k = C <= kTeam       ? k_site_team<St, 1, 1, 3>
+             : C <= 2 * kTeam ? k_site_team<St, 2, 1, 2>
+                              : k_site_team<St, 4, 1, 2>;
     int64_t wgs = T;
     const int64_t cap = (int64_t)device_cu_count() * 4;
     if (wgs > cap) wgs = cap;
@@ -1996,15 +1819,8 @@ static hipError_t run_single(const void* src, int n, int64_t stride, int64_t T, 
                        w, kg, gamma, eps, static_cast<St*>(h_out), static_cast<St*>(x_out), m_out, lse_out);
     return hipGetLastError();
   }
-  // wider rows: scores per 16-token tile on the matrix cores, then the outputs
-  const size_t lds = sizeof(float) * (2 * Red<1, kGroup>::kSlot + 16 * kSingleNP + 16);
-  auto kern = k_phase1_single<St>;
-  hipError_t e = set_lds(kern, lds);
-  if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((T + 15) / 16));
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, static_cast<const St*>(src), n, stride, T, d, w,
-                     kg, gamma, eps, static_cast<St*>(h_out), static_cast<St*>(x_out), m_out, lse_out);
-  return hipGetLastError();
+  // d <= ATTNRES_MAX_D = 16384 (validated by the C ABI): at most 2048 chunks
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_phase1_single(Dtype dt, const void* src, int n, int64_t stride, int64_t T, int d,
