@@ -318,16 +318,16 @@ def test_block_runs_are_bitwise_deterministic():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("T,d,cut", [(1000, 7168, 333), (3001, 1024, 1499), (5000, 7168, 1000)])
+@pytest.mark.parametrize("T,d,cut", [(1000, 7168, 333), (9001, 1024, 4001), (5000, 7168, 1000)])
 def test_token_split_invariance(T, d, cut):
     """Tokens never interact: one call over T tokens equals calls over slices,
-    every sublayer input and the final output bit for bit.  The slices are
-    short enough for the merge's one-token-per-team path, the whole range
-    takes its persistent loop (256-thread teams at d = 7168, 64-thread teams
-    at d = 1024, where 1499 and 1502 tokens leave teams without a token in
-    the last workgroup); at 5000 tokens the whole range forms the first sublayer's
-    input inside phase 1's token-order output kernel, the slices in the
-    short-range kernels and a merge launch."""
+    every sublayer input and the final output bit for bit.  At 9001 tokens
+    (64-thread teams, d = 1024) and 5000 tokens (256-thread teams, d = 7168)
+    the whole range takes the merge's persistent loop and the slices its
+    one-token-per-team path (4001 and 5000 tokens leave teams without a
+    token in the last workgroup); at 5000 tokens the whole range also forms
+    the first sublayer's input inside phase 1's token-order output kernel,
+    the slices in the short-range kernels."""
     _say("case token split invariance T=%d d=%d" % (T, d))
     dev = torch.device("cuda")
     w = synth.scaled(synth.WORKLOADS["prefill_chunk_bf16"], T=T, d=d, block_sizes=(5, 7), name="split")

@@ -414,11 +414,15 @@ static hipError_t run_merge(int64_t T, int d, const void* o1, const float* lse1,
                             hipStream_t stream) {
   constexpr int TPW = 256 / TEAM;
   const int64_t tiles = (T + TPW - 1) / TPW;
+  // Up to 8 tiles per CU, a workgroup per tile (the kernel's one-token path,
+  // which keeps the PreNorm gain in registers: no dynamic LDS).  Beyond,
   // persistent: 2 workgroups per CU (with non-temporal accesses every
-  // instance was fastest so; 1 per CU cost 7%)
-  const int64_t cap = (int64_t)device_cu_count() * 2;
+  // instance was fastest so; 1 per CU cost 7%).
+  const int64_t cu = device_cu_count();
+  const bool one = tiles <= 8 * cu;
+  const int64_t cap = one ? tiles : cu * 2;
   const dim3 grid((unsigned)(tiles < cap ? tiles : cap));
-  const size_t lds = x_out ? sizeof(float) * (size_t)d : 0;  // PreNorm gain (at most 64 KiB)
+  const size_t lds = (x_out && !one) ? sizeof(float) * (size_t)d : 0;  // PreNorm gain (at most 64 KiB)
   const St* o = static_cast<const St*>(o1);
   const Pt* pi = static_cast<const Pt*>(pin);
   const St* v2 = static_cast<const St*>(vprev2);
