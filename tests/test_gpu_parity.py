@@ -503,6 +503,7 @@ FIRST = [
     (300, 4104, 3, 20, "bf16", False),     # ragged last chunk group (9 groups, the last of one chunk)
     (37, 2056, 4, 5, "f32", True),         # 257 chunks: 5 groups
     (200, 7168, 16, 24, "bf16", False),    # 16 sources
+    (1500, 4104, 3, 20, "bf16", False),    # more tokens than workgroups: two tokens on some
 ]
 
 
