@@ -6,10 +6,12 @@
 // products into one Q K^T product, and each source row is read once per
 // block instead of once per sublayer).
 //
-// Work decomposition.  With a workspace (always for S >= 2, and for the
-// final aggregation) phase 1 is a streaming pair: pack the queries, score,
-// then stream the outputs.  Without one (S == 1: Full AttnRes one-shot sites)
-// a single kernel does both parts per 16-token tile.
+// Work decomposition.  For S >= 2 phase 1 is a streaming pair: pack the
+// queries, score, then stream the outputs (the softmax over the sources in
+// the scoring kernel for long token ranges, in its own launch or inside the
+// output kernel for short ones).  S == 1 (Full AttnRes one-shot sites, the
+// final aggregation) is one pass per token with an online softmax
+// (k_site_online, k_site_team).
 //  part A  scores.  Z[q][t][i] = sum_k (w_q g_q)[k] * u_i[t][k] is a dense
 //          contraction over d, computed on the matrix cores with
 //          v_mfma_f32_16x16x32_bf16 (bf16 rows; the fp32 query is split into
@@ -20,15 +22,18 @@
 //          channels.  The sum of squares of every source row (for its RMS) is
 //          accumulated on the vector ALUs from the same registers.  Two
 //          kernels with the same summation order (bitwise equal results):
-//          k_p1_scores gives each (16-token tile, source) pair a workgroup
-//          whose 4 waves take contiguous quarters of d (short token ranges);
+//          k_p1_scores gives each (16-token tile, source group, query tile)
+//          a workgroup whose 4 waves take contiguous quarters of d (short
+//          token ranges);
 //          k_p1_scores_wide gives each wave 16 tokens over all of d and shares
 //          the queries of 4 waves through LDS (long token ranges).  The
 //          queries are packed once per call into MFMA operand blocks; scores,
 //          then softmax weights, go to the caller's workspace.
 //  part B  outputs.  out[s][t] = sum_i alpha[t][s][i] u_i[t]: the source rows
 //          are streamed again (16-byte loads, a wave reads 1 KiB of one row)
-//          and each row chunk serves all S queries.
+//          and each row chunk serves all S queries; with the first
+//          sublayer's PreNorm, x_0 replaces out[0] (k_p1_out_tokens for long
+//          ranges, k_p1_out_wg for short ones with rows over 256 chunks).
 //
 // Every global load is unconditional: an out-of-range token or chunk loads a
 // clamped, valid address and the value is replaced by zero afterwards.  This
