@@ -109,9 +109,9 @@ typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1, ATTNRES_P24 = 2, ATTNRES_Q16 =
  * the outputs).
  * workspace: caller-owned device memory of at least
  * attnres_phase1_workspace_bytes(T, d, n_src, S) bytes, 16-byte aligned,
- * used for the queries packed as matrix-core operands and for the softmax
- * weights between the scoring and output kernels (its contents afterwards are
- * unspecified).  Required for S >= 2.  For S == 1 it is not used (may be
+ * used for the queries packed as matrix-core operands and for the scores or
+ * softmax weights between the scoring and output kernels (its contents
+ * afterwards are unspecified).  Required for S >= 2.  For S == 1 it is not used (may be
  * NULL): one pass over the sources computes the site with an online softmax
  * (the running maximum and normaliser rescaled batch by batch, as in the
  * notes' log-sum-exp merge), reading every source row once.
