@@ -990,9 +990,18 @@ __global__ __launch_bounds__(256) void k_p1_out_tokens(const Ut* __restrict__ sr
       float r[8];
       FirstSlot<St>::put(mine + (size_t)c * kW, o, r);
       if (ok) {
-        float& acc = (!wide_row || (grp & 3) == 0) ? ss0 : (grp & 3) == 1 ? ss1 : (grp & 3) == 2 ? ss2 : ss3;
+        // the chunk group's sum: all four read and written back as values
+        // (selecting among the captured variables themselves selects their
+        // addresses, which keeps them in scratch memory)
+        const int sel = wide_row ? (grp & 3) : 0;
+        const float a0 = ss0, a1 = ss1, a2 = ss2, a3 = ss3;
+        float acc = sel == 0 ? a0 : sel == 1 ? a1 : sel == 2 ? a2 : a3;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fmaf(r[e], r[e], acc);
+        ss0 = sel == 0 ? acc : a0;
+        ss1 = sel == 1 ? acc : a1;
+        ss2 = sel == 2 ? acc : a2;
+        ss3 = sel == 3 ? acc : a3;
         if (h0) out8(h0 + tok * d + c * 8, o);
       }
       q = 1;
