@@ -25,8 +25,10 @@
 //          k_p1_scores gives each (16-token tile, source group, query tile)
 //          a workgroup whose 4 waves take contiguous quarters of d (short
 //          token ranges);
-//          k_p1_scores_wide gives each wave 16 tokens over all of d and shares
-//          the queries of 4 waves through LDS (long token ranges).  The
+//          k_p1_scores_wide gives each 16-token tile over all of d one wave
+//          (fp32 rows) or two that share its sources (bf16 rows) and shares
+//          the queries of a workgroup's 4 tiles through LDS (long token
+//          ranges).  The
 //          queries are packed once per call into MFMA operand blocks; scores,
 //          then softmax weights, go to the caller's workspace.
 //  part B  outputs.  out[s][t] = sum_i alpha[t][s][i] u_i[t]: the source rows
@@ -461,18 +463,23 @@ __global__ __launch_bounds__(256) void k_p1_softmax(int64_t pairs, int n, int S,
 }
 
 // Wide-tile variant of the scoring kernel for long token ranges, with the
-// same results bit for bit.  A workgroup holds kWideWaves compute waves, each
-// owning a 16-token tile over all of d, plus one loader wave.  A compute wave
-// streams its source rows through a ring of D register stages (one K-block of
-// one source per stage), so D-1 K-blocks are in flight while the matrix cores
-// work on the oldest.  The loader wave copies the packed queries of each
-// K-block into one of two LDS slots one K-block ahead; the workgroup meets at
-// one barrier per K-block.  The loader waits only on its own query loads, so
-// the source stream never waits behind a query load, and every packed query
-// byte leaves L2 once per 64 tokens instead of once per 16.  (A vector-ALU-only
-// scoring kernel for the same work, fp32 queries staged in LDS and 4-8 tokens
-// x 12 queries per thread, took 673 us per launch at 16384 tokens, d = 7168,
-// 8 sources, 24 queries on an MI355X, against 254 us for this one.)
+// same results bit for bit.  A workgroup holds kWideWaves 16-token tiles over
+// all of d, H compute waves per tile (bf16 sources: two, each scoring half of
+// the sources, so that a compute unit has eight source streams in flight;
+// fp32 sources: one), plus one loader wave.  A compute wave streams its source
+// rows through a ring of D register stages (one K-block of one source per
+// stage), so D-1 K-blocks are in flight while the matrix cores work on the
+// oldest.  The loader wave copies the packed queries of each K-block straight
+// from global memory into one of two or three LDS slots, one or two K-blocks
+// ahead; the workgroup meets at one barrier per K-block.  The loader waits only
+// on its own copies, so the source stream never waits behind a query load, and
+// every packed query byte leaves L2 once per 64 tokens instead of once per 16.
+// (Two waves per tile took phase 1 of an 8-source, 18-query block at 16384
+// tokens, d = 7168, from 1.64-1.67 to 1.59-1.60 ms on an MI355X.  A
+// vector-ALU-only scoring kernel for the same work, fp32 queries staged in LDS
+// and 4-8 tokens x 12 queries per thread, took 673 us per launch at 16384
+// tokens, d = 7168, 8 sources, 24 queries, against 254 us for the one-wave
+// version of this one.)
 //
 // Summation order.  Per source, the K-blocks are visited in order; they form
 // four contiguous classes [w*nkb/4, (w+1)*nkb/4), each summed from zero, the
@@ -490,13 +497,21 @@ struct KOrder {
   }
 };
 
-constexpr int kWideWaves = 4;  // compute waves (16 tokens each) per workgroup
+constexpr int kWideWaves = 4;  // 16-token tiles per workgroup
 
 // Ring depth (stages of one K-block): 16 VGPRs per bf16 stage, 32 per fp32
 // stage, within the 256 VGPRs a wave may hold (two waves share one SIMD).
+// H: compute waves per tile.  bf16 sources take two (each scoring a share of
+// the sources), at most 168 VGPRs per wave (three waves on one SIMD with the
+// loader) and two stages each; fp32 sources one, with the whole register
+// budget of a single wave per SIMD.
+template <typename St>
+struct WideHalves {
+  static constexpr int value = sizeof(St) == 2 ? 2 : 1;
+};
 template <typename St, int MT>
 struct WideDepth {
-  static constexpr int value = MT == 1 ? 6 : 4;
+  static constexpr int value = WideHalves<St>::value == 2 ? 2 : (MT == 1 ? 6 : 4);
 };
 template <int MT>
 struct WideDepth<float, MT> {
@@ -509,53 +524,58 @@ struct WideDepth<float, MT> {
 // later kernels read as source n-1; it is scored from the rounded values, so
 // the results equal those of summing first and scoring afterwards, bit for
 // bit.  Its K-blocks come last, through a ring of two stages of pieces.
-template <typename St, int MT, typename Vt = St, typename Pt = float, bool FUSED = false>
-__global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
+template <typename St, int MT, typename Vt = St, typename Pt = float, bool FUSED = false,
+          int kWideHalves = WideHalves<St>::value>
+__global__ __launch_bounds__(64 * (kWideWaves * kWideHalves + 1)) void k_p1_scores_wide(
     const St* __restrict__ src, int n, int64_t stride, int64_t T, int d, const u32x4_t* __restrict__ pk, int S,
     float eps, float* __restrict__ alpha, float* __restrict__ m_out, float* __restrict__ lse_out,
-    const Pt* __restrict__ npin, const Vt* __restrict__ nv2, const Vt* __restrict__ nv, St* __restrict__ ndst) {
+    const Pt* __restrict__ npin, const Vt* __restrict__ nv2, const Vt* __restrict__ nv, St* __restrict__ ndst,
+    int nslot) {
   constexpr int D = WideDepth<St, MT>::value;
   constexpr int QW = MT * 512;  // 16-byte words per packed K-block
-  static_assert(D % 2 == 0, "the LDS slot of a ring stage must be a constant");
-  __shared__ u32x4_t qs[2][QW];
-  extern __shared__ float zs[];  // per compute wave: z[16 tokens][S][n]
+  // nslot (2 or 3) LDS slots of packed queries, then per tile z[16 tokens][S][n]
+  extern __shared__ u32x4_t wide_lds[];
+  u32x4_t* const qs = wide_lds;
+  float* const zs = reinterpret_cast<float*>(wide_lds + nslot * QW);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int C = d >> 3;
   const int nkb = (C + kKBlock - 1) / kKBlock;
-  const int nit = n * nkb;  // (source, K-block) iterations, source-major
-  const int nitr = FUSED ? nit - nkb : nit;  // iterations that read src
+  // With two waves per tile they score the sources [0, n0) and [n0, n); the
+  // newest source (formed from its pieces when FUSED) is the last of its
+  // half.  Both take one K-block step per barrier, the shorter half idling
+  // through the longer one's extra steps.
+  const int n0 = kWideHalves == 2 ? (n + 1) >> 1 : n;
+  const int nsteps = n0 * nkb;  // K-block steps of the longer half
   const KOrder ko(nkb);
   // Global memory is touched only by loads until the last loop ends, and
   // every load below is unconditional (indices clamped), so the compiler
   // counts the loads in flight exactly and never waits for a younger stage.
 
-  if (wave == kWideWaves) {
-    // loader: the queries of iteration `it` go to slot it & 1
-    u32x4_t r0[MT * 8], r1[MT * 8];
-    auto fetch = [&](u32x4_t(&r)[MT * 8], int it) {
-      const int kb = (it < nit ? it : nit - 1) % nkb;
-      const u32x4_t* p = pk + (int64_t)kb * QW + lane;
+  if (wave == kWideWaves * kWideHalves) {
+    // loader: the queries of step `it` are copied from global memory
+    // straight into LDS slot it % nslot (no registers), nslot - 1 steps
+    // ahead; at the barrier of step it only the copies of later steps may
+    // be in flight
+    const int nit = nsteps;
+    const int ahead = nslot - 1;
+    auto fetch = [&](int it) {
+      const u32x4_t* p = pk + (int64_t)(it % nkb) * QW + lane;
+      u32x4_t* q = qs + (it % nslot) * QW;
 #pragma unroll
-      for (int j = 0; j < MT * 8; ++j) r[j] = ld16(p + j * 64);
+      for (int j = 0; j < MT * 8; ++j) __builtin_amdgcn_global_load_lds(p + j * 64, q + j * 64, 16, 0, 0);
     };
-    fetch(r0, 0);
-    fetch(r1, 1);
-    int it = 0;
-    for (; it + 2 <= nit; it += 2) {
-#pragma unroll
-      for (int j = 0; j < MT * 8; ++j) qs[0][j * 64 + lane] = r0[j];
-      fetch(r0, it + 2);
-      lds_barrier();
-#pragma unroll
-      for (int j = 0; j < MT * 8; ++j) qs[1][j * 64 + lane] = r1[j];
-      fetch(r1, it + 3);
-      lds_barrier();
-    }
-    if (it < nit) {
-#pragma unroll
-      for (int j = 0; j < MT * 8; ++j) qs[0][j * 64 + lane] = r0[j];
-      lds_barrier();
+    for (int k = 0; k < ahead && k < nit; ++k) fetch(k);
+    for (int it = 0; it < nit; ++it) {
+      if (ahead == 2 && it + 1 < nit) {
+        wait_vmcnt<MT * 8>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      // a bare barrier: the wait above already covers the copies that the
+      // compute waves read after it (a fence would drain every copy)
+      __builtin_amdgcn_s_barrier();
+      if (it + ahead < nit) fetch(it + ahead);
     }
     return;
   }
@@ -563,16 +583,21 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
   typedef typename Mfma<St>::B B;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int64_t tok0 = (int64_t)blockIdx.x * (16 * kWideWaves) + wave * 16;
+  const int tile = wave % kWideWaves;
+  const int half = wave / kWideWaves;
+  const int sb = half ? n0 : 0, se = half ? n : n0;  // this wave's sources (all of them for one wave per tile)
+  const bool own_fused = FUSED && se == n && se > sb;  // the newest source is this wave's
+  const int nitr = (se - sb - (own_fused ? 1 : 0)) * nkb;  // steps that read src
+  const int64_t tok0 = (int64_t)blockIdx.x * (16 * kWideWaves) + tile * 16;
   const int64_t tokc = tok0 + col < T ? tok0 + col : T - 1;  // clamped row; results of such lanes are dropped
   const St* row = src + tokc * d;
-  float* zw = zs + wave * (16 * S * n);
+  float* zw = zs + tile * (16 * S * n);
   B b[D][4];
   auto issue = [&](B(&bs)[4], int it) {
     it = it < nitr ? it : nitr - 1;
     const int i = it / nkb;
     const int kb = it - i * nkb;
-    const St* base = row + (int64_t)i * stride;
+    const St* base = row + (int64_t)(sb + i) * stride;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       // raw load: chunks past the end of d are zeroed when the stage is used,
@@ -591,8 +616,8 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
   // one iteration: wait for the queries, then the matrix-core work on the
   // oldest ring stage, then the per-class / per-source bookkeeping
   auto step = [&](B(&bs)[4], const u32x4_t* slot, int it) {
-    const int i = it / nkb;
-    const int kb = it - i * nkb;
+    const int kb = it % nkb;
+    const int i = sb + it / nkb;  // the source
     int w;
     bool last;
     ko.at(kb, w, last);
@@ -601,23 +626,25 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
       for (int s4 = 0; s4 < 4; ++s4)
         if (kb * kKBlock + s4 * 4 + grp >= C) bs[s4] = Mfma<St>::zero_b();
     }
-    // all query fragments of the K-block first: the LDS latency is paid once
-    // per K-block, not once per matrix-core step
-    typename Mfma<St>::A a[4][MT];
+    // the query fragments of the next matrix-core step are read from LDS
+    // while the current one runs (two waves share a SIMD, so the register
+    // file holds two fragment sets per wave, not a whole K-block's)
+    typename Mfma<St>::A a[2][MT];
     const u32x4_t* q = slot + lane;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
+    auto frag = [&](typename Mfma<St>::A(&fa)[MT], int s4) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const u32x4_t* qp = q + ((m * 4 + s4) * 2) * 64;
-        a[s4][m] = Mfma<St>::from_halves(qp[0], qp[64]);
+        fa[m] = Mfma<St>::from_halves(qp[0], qp[64]);
       }
-    __builtin_amdgcn_sched_barrier(0);
+    };
+    frag(a[0], 0);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
+      if (s4 < 3) frag(a[(s4 + 1) & 1], s4 + 1);
       Mfma<St>::sumsq(bs[s4], ss);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) Mfma<St>::mma(acc[m], a[s4][m], bs[s4]);
+      for (int m = 0; m < MT; ++m) Mfma<St>::mma(acc[m], a[s4 & 1][m], bs[s4]);
     }
     if (last) {
       float sw = ss;
@@ -668,18 +695,18 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
 #pragma unroll
       for (int s = 0; s < D; ++s) {
         issue(b[(s + D - 1) % D], it0 + s + D - 1);
-        lds_barrier();  // the queries of this K-block are in slot s & 1
-        step(b[s], qs[s & 1], it0 + s);
+        lds_barrier();  // the queries of this K-block are in slot (it0 + s) % nslot
+        step(b[s], qs + ((it0 + s) % nslot) * QW, it0 + s);
       }
     }
 #pragma unroll
     for (int s = 0; s < D - 1; ++s)  // tail: every stage is already loaded
       if (it0 + s < nitr) {
         lds_barrier();
-        step(b[s], qs[s & 1], it0 + s);
+        step(b[s], qs + ((it0 + s) % nslot) * QW, it0 + s);
       }
   }
-  if constexpr (FUSED) {
+  if (FUSED && own_fused) {
     // source n-1 from its pieces (loads unconditional: a missing v2 is
     // replaced by v and not added)
     const int64_t plane = T * (int64_t)d;
@@ -717,7 +744,7 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
         bs[s4] = RoundB<St>::round_store(x, ndst + tokc * d + (c0 < C ? c0 : C - 1) * 8, live && c0 < C);
       }
       const int it = nitr + kb;
-      step(bs, qs[it & 1], it);
+      step(bs, qs + (it % nslot) * QW, it);
     };
     pissue(ps[0], 0);
     for (int kb = 0; kb < nkb; kb += 2) {
@@ -736,9 +763,12 @@ __global__ __launch_bounds__(64 * (kWideWaves + 1)) void k_p1_scores_wide(
     }
   }
 
-  // softmax over the n sources of every (token, query) pair of the tile (the
-  // wave reads back only what it wrote, in program order)
-  for (int pidx = lane; pidx < 16 * S; pidx += 64) {
+  // the shorter half's idle steps, then every score of the tile is in LDS
+  for (int k = (se - sb) * nkb; k < nsteps; ++k) lds_barrier();
+  lds_barrier();
+  // softmax over the n sources of every (token, query) pair of the tile, the
+  // pairs shared by the tile's two waves
+  for (int pidx = half * 64 + lane; pidx < 16 * S; pidx += 64 * kWideHalves) {
     const int t = pidx / S, qi = pidx - t * S;
     const int64_t tok = tok0 + t;
     if (tok >= T) continue;
@@ -1687,15 +1717,19 @@ static hipError_t launch_wide(const void* src, int n, int64_t stride, int64_t T,
                               float eps, float* al, float* m_out, float* lse_out, const Newest* nw,
                               hipStream_t stream) {
   const int64_t wide_groups = (T + 16 * kWideWaves - 1) / (16 * kWideWaves);
+  // three query slots (copies two steps ahead) where the LDS has room, else two
   const size_t zl = sizeof(float) * kWideWaves * 16 * S * n;
+  const size_t slot = sizeof(u32x4_t) * MT * 512;
+  const int nslot = zl + 3 * slot <= kMaxLds ? 3 : 2;
+  const size_t lds = zl + nslot * slot;
   auto kw = k_p1_scores_wide<Ut, MT, Vt, Pt, FUSED>;
-  hipError_t e = set_lds(kw, zl, zl + sizeof(u32x4_t) * 2 * MT * 512);
+  hipError_t e = set_lds(kw, lds);
   if (e != hipSuccess) return e;
   Ut* dst = FUSED ? static_cast<Ut*>(const_cast<void*>(src)) + (int64_t)(n - 1) * stride : nullptr;
-  hipLaunchKernelGGL(kw, dim3((unsigned)wide_groups), dim3(64 * (kWideWaves + 1)), zl, stream,
+  hipLaunchKernelGGL(kw, dim3((unsigned)wide_groups), dim3(64 * (kWideWaves * WideHalves<Ut>::value + 1)), lds, stream,
                      static_cast<const Ut*>(src), n, stride, T, d, pk, S, eps, al, m_out, lse_out,
                      static_cast<const Pt*>(FUSED ? nw->pin : nullptr), static_cast<const Vt*>(FUSED ? nw->v2 : nullptr),
-                     static_cast<const Vt*>(FUSED ? nw->v : nullptr), dst);
+                     static_cast<const Vt*>(FUSED ? nw->v : nullptr), dst, nslot);
   return hipGetLastError();
 }
 
