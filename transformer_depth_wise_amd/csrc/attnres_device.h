@@ -311,14 +311,6 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
 // orders global memory, which makes every wave wait for all of its global
 // loads and stores in flight (the prefetched next item included); here those
 // stay in flight across the barrier.
-// Wait until at most N vector-memory operations of this wave are in flight
-// (they complete in issue order), e.g. copies straight into LDS.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();

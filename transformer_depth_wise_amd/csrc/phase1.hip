@@ -499,6 +499,14 @@ struct KOrder {
 
 constexpr int kWideWaves = 4;  // 16-token tiles per workgroup
 
+// Wait until at most N vector-memory operations of this wave are in flight
+// (they complete in issue order), e.g. copies straight into LDS.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Ring depth (stages of one K-block): 16 VGPRs per bf16 stage, 32 per fp32
 // stage, within the 256 VGPRs a wave may hold (two waves share one SIMD).
 // H: compute waves per tile.  bf16 sources take two (each scoring a share of
