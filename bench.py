@@ -90,7 +90,9 @@ def ceiling(dev, total_bytes: int = 4 << 30, reps: int = 6) -> dict:
     write x: about 3 reads : 1 write; even positions also read the
     one-before-last output and store the partial: about 4 : 2), eight
     concurrent read streams (the scoring pass over the last blocks'
-    sources) and nine reads with one write (the final aggregation).  Each mix
+    sources), nine reads with one write (the final aggregation) and seven
+    reads with 24 writes (the phase-1 output pass of a 7-source, 24-sublayer
+    block).  Each mix
     is run in 18 launch shapes (1, 2 or 4 workgroups per CU; 1, 2 or 8
     chunks in flight per thread; plain or non-temporal accesses) and the
     best rate is reported with its shape.  Each dispatch moves
@@ -107,7 +109,7 @@ def ceiling(dev, total_bytes: int = 4 << 30, reps: int = 6) -> dict:
     out = {"bytes_per_dispatch": total_bytes, "unit": "GB/s",
            "note": "attnres_stream_probe: the rate a streaming kernel with this read:write mix reaches here"}
     for name, nr, nw in (("read", 1, 0), ("write", 0, 1), ("copy", 1, 1), ("mix_3r1w", 3, 1),
-                         ("mix_4r2w", 4, 2), ("read_8", 8, 0), ("mix_9r1w", 9, 1)):
+                         ("mix_4r2w", 4, 2), ("read_8", 8, 0), ("mix_9r1w", 9, 1), ("mix_7r24w", 7, 24)):
         sb = (total_bytes // (nr + nw)) // (1 << 20) * (1 << 20)
         best, shape = 0.0, None
         for g, u, nt in PROBE_SHAPES:

@@ -469,8 +469,9 @@ attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t
  * and non-temporal loads and stores when `nontemporal` is nonzero.
  *   0 <= n_read <= 4, 0 <= n_write <= 2, not both zero, or one of the
  *   many-stream mixes (n_read, n_write) = (8, 0) (the scoring pass over a
- *   block's sources) and (9, 1) (the final aggregation: nine sources, one
- *   output); 1 <= workgroups_per_cu <= 16; stream_bytes a
+ *   block's sources), (9, 1) (the final aggregation: nine sources, one
+ *   output) and (7, 24) (the phase-1 output pass of a block with seven
+ *   sources and 24 sublayers); 1 <= workgroups_per_cu <= 16; stream_bytes a
  *   positive multiple of 16 (at most 2^40).  With n_write == 0, dst must
  *   still point at 16 writable bytes (kept as the loads' sink; not written
  *   for any data these probes read).  The read and written ranges must not

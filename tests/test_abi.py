@@ -411,8 +411,10 @@ def test_stream_probe_validation(lib):
     assert probe(per_cu=17) == EINVAL
     assert probe(unroll=3) == EINVAL
     assert probe(nr=5) == EINVAL
-    assert probe(nr=8, nw=1) == EINVAL     # the many-stream mixes are (8, 0) and (9, 1) only
+    assert probe(nr=8, nw=1) == EINVAL     # the many-stream mixes are (8, 0), (9, 1) and (7, 24) only
     assert probe(nr=9, nw=0) == EINVAL
+    assert probe(nr=7, nw=23) == EINVAL
+    assert probe(nr=6, nw=24) == EINVAL
     assert probe(nr=10, nw=1) == EINVAL
     assert probe(nw=3) == EINVAL
     assert probe(nr=0, nw=0) == EINVAL

@@ -651,7 +651,7 @@ attnres_status_t attnres_block_accumulate(attnres_dtype_t dt, int64_t T, int64_t
 attnres_status_t attnres_stream_probe(int64_t n_read, int64_t n_write, const void* src, void* dst,
                                       int64_t stream_bytes, int64_t workgroups_per_cu, int64_t unroll,
                                       int64_t nontemporal, void* stream) {
-  const bool many = (n_read == 8 && n_write == 0) || (n_read == 9 && n_write == 1);
+  const bool many = (n_read == 8 && n_write == 0) || (n_read == 9 && n_write == 1) || (n_read == 7 && n_write == 24);
   if (!many && (n_read < 0 || n_read > 4 || n_write < 0 || n_write > 2 || n_read + n_write == 0))
     return ATTNRES_EINVAL;
   if (workgroups_per_cu < 1 || workgroups_per_cu > 16) return ATTNRES_EINVAL;

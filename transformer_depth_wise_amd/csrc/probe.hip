@@ -102,6 +102,7 @@ hipError_t launch_stream_probe(int n_read, int n_write, const void* src, void* d
   ATTNRES_PROBE(4, 2);
   ATTNRES_PROBE(8, 0);
   ATTNRES_PROBE(9, 1);
+  ATTNRES_PROBE(7, 24);
 #undef ATTNRES_PROBE
   return hipErrorInvalidValue;
 }
