@@ -436,6 +436,11 @@ WIDE = [
     ("bf16", 7168, 9, 1),
     ("f32", 1032, 3, 20),
     ("bf16", 1024, 16, 32),
+    # bf16 tiles take two scoring waves, each with a share of the sources: an
+    # odd count (3 + 2, ragged K-blocks) and a single source (the second wave
+    # only keeps the barriers)
+    ("bf16", 2056, 5, 24),
+    ("bf16", 1024, 1, 20),
 ]
 
 
