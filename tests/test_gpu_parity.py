@@ -501,6 +501,7 @@ FIRST = [
     (None, 16384, 2, 2, "bf16", True),     # wider: phase 1 + a separate PreNorm launch
     (None, 4096, 4, 3, "f32", True),
     (None, 8192, 1, 4, "f32", False),      # one source: out may be NULL
+    (None, 7168, 1, 24, "bf16", True),     # one source, the 16K chunk's first block (PreNorm-only merge launch)
     (37, 1032, 3, 4, "bf16", True),        # short range: item-order kernel + PreNorm launch
     (37, 64, 1, 3, "f32", True),           # short range, one source
     # short ranges, rows over 256 chunks: a workgroup per token with the PreNorm inside

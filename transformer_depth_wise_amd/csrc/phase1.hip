@@ -1643,7 +1643,11 @@ static hipError_t run_out(const void* src, int64_t stride, int64_t T, int d, con
   const bool tok = token_order(T);
   const dim3 tgrid((unsigned)device_cu_count());
   if (!kSame && x0) return hipErrorInvalidValue;
-  if (kSame && x0 && tok && first_lds_bytes(d, sizeof(St) == 4) <= kMaxLds) {
+  // (one source and no outputs: only x_0 = PreNorm(u_0) is wanted, which the
+  // merge kernel's PreNorm-only launch below forms with the same bits at its
+  // streaming rate; the token-order kernel's four waves per CU took 158 us
+  // for it at 16384 tokens, d = 7168)
+  if (kSame && x0 && tok && (N > 1 || op) && first_lds_bytes(d, sizeof(St) == 4) <= kMaxLds) {
     const size_t lds = first_lds_bytes(d, sizeof(St) == 4);
     auto k = k_p1_out_tokens<Ut, St, N, kSame>;
     hipError_t e = set_lds(k, lds);
