@@ -498,6 +498,10 @@ struct KOrder {
 };
 
 constexpr int kWideWaves = 4;  // 16-token tiles per workgroup
+// Bytes per token row of a compute wave's 16-row staging buffer: a 256-byte
+// K-block plus 16, so that the operand-layout reads (16 tokens x 16 bytes
+// per group of four lanes) fall on distinct banks.
+constexpr int kRowPitch = 272;
 
 // Wait until at most N vector-memory operations of this wave are in flight
 // (they complete in issue order), e.g. copies straight into LDS.
@@ -533,7 +537,7 @@ struct WideDepth<float, MT> {
 // the results equal those of summing first and scoring afterwards, bit for
 // bit.  Its K-blocks come last, through a ring of two stages of pieces.
 template <typename St, int MT, typename Vt = St, typename Pt = float, bool FUSED = false,
-          int kWideHalves = WideHalves<St>::value>
+          int kWideHalves = WideHalves<St>::value, bool ROWS = false>
 __global__ __launch_bounds__(64 * (kWideWaves * kWideHalves + 1)) void k_p1_scores_wide(
     const St* __restrict__ src, int n, int64_t stride, int64_t T, int d, const u32x4_t* __restrict__ pk, int S,
     float eps, float* __restrict__ alpha, float* __restrict__ m_out, float* __restrict__ lse_out,
@@ -541,10 +545,12 @@ __global__ __launch_bounds__(64 * (kWideWaves * kWideHalves + 1)) void k_p1_scor
     int nslot) {
   constexpr int D = WideDepth<St, MT>::value;
   constexpr int QW = MT * 512;  // 16-byte words per packed K-block
-  // nslot (2 or 3) LDS slots of packed queries, then per tile z[16 tokens][S][n]
+  // nslot (2 or 3) LDS slots of packed queries, then per tile z[16 tokens][S][n],
+  // then (ROWS) a 16-row staging buffer per compute wave
   extern __shared__ u32x4_t wide_lds[];
   u32x4_t* const qs = wide_lds;
   float* const zs = reinterpret_cast<float*>(wide_lds + nslot * QW);
+  unsigned char* const rowbuf = reinterpret_cast<unsigned char*>(zs + kWideWaves * 16 * S * n);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int C = d >> 3;
@@ -600,18 +606,32 @@ __global__ __launch_bounds__(64 * (kWideWaves * kWideHalves + 1)) void k_p1_scor
   const int64_t tokc = tok0 + col < T ? tok0 + col : T - 1;  // clamped row; results of such lanes are dropped
   const St* row = src + tokc * d;
   float* zw = zs + tile * (16 * S * n);
+  unsigned char* const wb = rowbuf + wave * (16 * kRowPitch);  // ROWS: this wave's staging rows
   B b[D][4];
   auto issue = [&](B(&bs)[4], int it) {
     it = it < nitr ? it : nitr - 1;
     const int i = it / nkb;
     const int kb = it - i * nkb;
-    const St* base = row + (int64_t)(sb + i) * stride;
+    if constexpr (ROWS) {
+      // whole-row pieces: load s4 covers tokens 4 s4 .. 4 s4 + 3 of the
+      // tile, 16 lanes (the K-block's 256 contiguous bytes) per token
+      const St* sbase = src + (int64_t)(sb + i) * stride;
+      const int c0 = kb * kKBlock + (lane & 15);
+      const int cc = c0 < C ? c0 : C - 1;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      // raw load: chunks past the end of d are zeroed when the stage is used,
-      // so that nothing here waits for the data
-      const int c0 = kb * kKBlock + s4 * 4 + grp;
-      bs[s4] = Mfma<St>::load_b(base + (c0 < C ? c0 : C - 1) * 8, true);
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int64_t tk = tok0 + s4 * 4 + (lane >> 4);
+        bs[s4] = Mfma<St>::load_b(sbase + (tk < T ? tk : T - 1) * d + cc * 8, true);
+      }
+    } else {
+      const St* base = row + (int64_t)(sb + i) * stride;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        // raw load: chunks past the end of d are zeroed when the stage is used,
+        // so that nothing here waits for the data
+        const int c0 = kb * kKBlock + s4 * 4 + grp;
+        bs[s4] = Mfma<St>::load_b(base + (c0 < C ? c0 : C - 1) * 8, true);
+      }
     }
   };
 
@@ -623,9 +643,22 @@ __global__ __launch_bounds__(64 * (kWideWaves * kWideHalves + 1)) void k_p1_scor
 
   // one iteration: wait for the queries, then the matrix-core work on the
   // oldest ring stage, then the per-class / per-source bookkeeping
-  auto step = [&](B(&bs)[4], const u32x4_t* slot, int it) {
+  auto step = [&](B(&bs)[4], const u32x4_t* slot, int it, auto rows) {
     const int kb = it % nkb;
     const int i = sb + it / nkb;  // the source
+    if constexpr (decltype(rows)::value) {
+      // whole-row pieces to the operand layout through the wave's own LDS
+      // rows (a wave's LDS accesses complete in order: no wait or barrier)
+      static_assert(!decltype(rows)::value || sizeof(B) == 16, "whole-row staging is for bf16 rows");
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        *reinterpret_cast<u32x4_t*>(wb + (s4 * 4 + (lane >> 4)) * kRowPitch + (lane & 15) * 16) =
+            *reinterpret_cast<const u32x4_t*>(&bs[s4]);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        *reinterpret_cast<u32x4_t*>(&bs[s4]) =
+            *reinterpret_cast<const u32x4_t*>(wb + col * kRowPitch + (s4 * 4 + grp) * 16);
+    }
     int w;
     bool last;
     ko.at(kb, w, last);
@@ -704,14 +737,14 @@ __global__ __launch_bounds__(64 * (kWideWaves * kWideHalves + 1)) void k_p1_scor
       for (int s = 0; s < D; ++s) {
         issue(b[(s + D - 1) % D], it0 + s + D - 1);
         lds_barrier();  // the queries of this K-block are in slot (it0 + s) % nslot
-        step(b[s], qs + ((it0 + s) % nslot) * QW, it0 + s);
+        step(b[s], qs + ((it0 + s) % nslot) * QW, it0 + s, std::integral_constant<bool, ROWS>{});
       }
     }
 #pragma unroll
     for (int s = 0; s < D - 1; ++s)  // tail: every stage is already loaded
       if (it0 + s < nitr) {
         lds_barrier();
-        step(b[s], qs + ((it0 + s) % nslot) * QW, it0 + s);
+        step(b[s], qs + ((it0 + s) % nslot) * QW, it0 + s, std::integral_constant<bool, ROWS>{});
       }
   }
   if (FUSED && own_fused) {
@@ -752,7 +785,7 @@ __global__ __launch_bounds__(64 * (kWideWaves * kWideHalves + 1)) void k_p1_scor
         bs[s4] = RoundB<St>::round_store(x, ndst + tokc * d + (c0 < C ? c0 : C - 1) * 8, live && c0 < C);
       }
       const int it = nitr + kb;
-      step(bs, qs + (it % nslot) * QW, it);
+      step(bs, qs + (it % nslot) * QW, it, std::false_type{});
     };
     pissue(ps[0], 0);
     for (int kb = 0; kb < nkb; kb += 2) {
@@ -1724,17 +1757,18 @@ static hipError_t pick_out(int n, const void* src, int64_t stride, int64_t T, in
 
 // The wide scoring kernel on sources of type Ut; Vt and Pt are the types of
 // the newest source's pieces when FUSED.
-template <typename Ut, int MT, typename Vt, typename Pt, bool FUSED>
-static hipError_t launch_wide(const void* src, int n, int64_t stride, int64_t T, int d, const u32x4_t* pk, int S,
-                              float eps, float* al, float* m_out, float* lse_out, const Newest* nw,
-                              hipStream_t stream) {
+template <typename Ut, int MT, typename Vt, typename Pt, bool FUSED, bool ROWS>
+static hipError_t launch_wide_r(const void* src, int n, int64_t stride, int64_t T, int d, const u32x4_t* pk, int S,
+                                float eps, float* al, float* m_out, float* lse_out, const Newest* nw,
+                                hipStream_t stream) {
   const int64_t wide_groups = (T + 16 * kWideWaves - 1) / (16 * kWideWaves);
   // three query slots (copies two steps ahead) where the LDS has room, else two
   const size_t zl = sizeof(float) * kWideWaves * 16 * S * n;
   const size_t slot = sizeof(u32x4_t) * MT * 512;
-  const int nslot = zl + 3 * slot <= kMaxLds ? 3 : 2;
-  const size_t lds = zl + nslot * slot;
-  auto kw = k_p1_scores_wide<Ut, MT, Vt, Pt, FUSED>;
+  const size_t rb = ROWS ? (size_t)kWideWaves * WideHalves<Ut>::value * 16 * kRowPitch : 0;
+  const int nslot = zl + 3 * slot + rb <= kMaxLds ? 3 : 2;
+  const size_t lds = zl + nslot * slot + rb;
+  auto kw = k_p1_scores_wide<Ut, MT, Vt, Pt, FUSED, WideHalves<Ut>::value, ROWS>;
   hipError_t e = set_lds(kw, lds);
   if (e != hipSuccess) return e;
   Ut* dst = FUSED ? static_cast<Ut*>(const_cast<void*>(src)) + (int64_t)(n - 1) * stride : nullptr;
@@ -1743,6 +1777,26 @@ static hipError_t launch_wide(const void* src, int n, int64_t stride, int64_t T,
                      static_cast<const Pt*>(FUSED ? nw->pin : nullptr), static_cast<const Vt*>(FUSED ? nw->v2 : nullptr),
                      static_cast<const Vt*>(FUSED ? nw->v : nullptr), dst, nslot);
   return hipGetLastError();
+}
+
+// bf16 rows are loaded as whole-row pieces and staged through LDS into the
+// matrix-core operand layout where the LDS has room for the staging rows
+// (16 tokens x 64 bytes per load instruction, the operand layout itself,
+// streamed at 5.5 TB/s on an MI355X in a load-only probe of this kernel's
+// pattern; 4 tokens x 256 bytes at 7.0-7.1)
+template <typename Ut, int MT, typename Vt, typename Pt, bool FUSED>
+static hipError_t launch_wide(const void* src, int n, int64_t stride, int64_t T, int d, const u32x4_t* pk, int S,
+                              float eps, float* al, float* m_out, float* lse_out, const Newest* nw,
+                              hipStream_t stream) {
+  if constexpr (sizeof(Ut) == 2) {
+    const size_t need = sizeof(float) * kWideWaves * 16 * S * n + 2 * sizeof(u32x4_t) * MT * 512 +
+                        (size_t)kWideWaves * WideHalves<Ut>::value * 16 * kRowPitch;
+    if (need <= kMaxLds)
+      return launch_wide_r<Ut, MT, Vt, Pt, FUSED, true>(src, n, stride, T, d, pk, S, eps, al, m_out, lse_out, nw,
+                                                        stream);
+  }
+  return launch_wide_r<Ut, MT, Vt, Pt, FUSED, false>(src, n, stride, T, d, pk, S, eps, al, m_out, lse_out, nw,
+                                                     stream);
 }
 
 static constexpr Dtype kind_of_type(bool f32) { return f32 ? kF32 : kBF16; }
