@@ -344,14 +344,21 @@ __global__ __launch_bounds__(256) void k_merge(int64_t T, int d, const St* __res
   // stores, which measured 2% faster at 16K tokens than loading it with the
   // rows.
   while (tok - team < T) {
+    // the next token's loads are issued at a raised wave priority, so that
+    // they leave the SIMD ahead of the arithmetic of the other workgroup's
+    // waves (3.5-6.5% faster merges at the 16K chunk than at equal priority)
+    __builtin_amdgcn_s_setprio(2);
     issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(B, tok + step, T, d, C, tl, o1, lse1, pin, vprev2, vprev,
                                                             plane);
+    __builtin_amdgcn_s_setprio(0);
     process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(A, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq,
                                                                gm_lds, wq, eps, inv_d, h_out, x_out, red, parity);
     tok += step;
     if (tok - team >= T) break;
+    __builtin_amdgcn_s_setprio(2);
     issue<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(A, tok + step, T, d, C, tl, o1, lse1, pin, vprev2, vprev,
                                                             plane);
+    __builtin_amdgcn_s_setprio(0);
     process<St, Pt, TEAM, CPL, HAS_V, HAS_PIN, HAS_V2, false>(B, tok, T, d, C, tl, lse1, pout, pfmt, plane, wq,
                                                                gm_lds, wq, eps, inv_d, h_out, x_out, red, parity);
     tok += step;
