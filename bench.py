@@ -328,8 +328,8 @@ def io_model(w, rows) -> dict:
 def other_workloads(dev, steps: int):
     """Shorter measurements of the other hot-path shapes, each pass over
     resident inputs: the decode-shaped block step (eager launches and one
-    HIP-graph replay per pass), Full AttnRes (one-shot sites, the grouped
-    schedule, the backward), one aggregation site's backward, and one GPU's
+    HIP-graph replay per pass), Full AttnRes (one-shot sites and the grouped
+    schedule, each eager and as a graph replay; the backward), one aggregation site's backward, and one GPU's
     token share (2048 tokens) of the 16K chunk.  Working sets that fit the
     256 MB last-level cache rotate over 4 input replicas so that every pass
     reads from HBM."""
@@ -415,6 +415,25 @@ def other_workloads(dev, steps: int):
                                  "ms_per_step": round(sec * 1e3, 4), "value": round(w.T * w.L / sec, 1),
                                  "unit": "token-sublayers/s", "hbm_gbps": round(b / sec / 1e9, 1),
                                  "bytes_per_step": b}
+    # both schedules as one HIP-graph replay per pass (at 8 MB per row set the
+    # launches, 17 one-shot against 32 grouped, weigh as much as the bytes)
+    for key, states in ((w.name, fulls), (w.name + "_grouped4", grouped)):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for st in states:
+                st.forward(prm, noop)
+        torch.cuda.current_stream().wait_stream(side)
+        gs = []
+        for st in states:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                st.forward(prm, noop)
+            gs.append(g)
+        sec = _time(lambda k: gs[k % len(gs)].replay(), max(steps, 20))
+        res[key]["graph_replay"] = {"ms_per_step": round(sec * 1e3, 4), "value": round(w.T * w.L / sec, 1),
+                                    "hbm_gbps": round(res[key]["bytes_per_step"] / sec / 1e9, 1)}
+        del gs
     res[w.name + "_backward"] = full_backward_report(fulls, prm, steps)
     del fulls, grouped
     torch.cuda.empty_cache()
